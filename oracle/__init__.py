@@ -1,0 +1,197 @@
+"""fp64 CPU oracle for paged Top-K decode attention (ctypes binding of oracle.c).
+
+TEST INFRASTRUCTURE ONLY: the test suite, the smoke check and the benchmark's
+CPU-baseline leg use it; the library never imports it.  It shares no code with
+the HIP path: inputs come from the seeded workload generator as numpy arrays,
+are copied exactly to float64 here, and everything after that is oracle.c.
+
+Functions (each computed as oracle.c states it):
+
+* ``block_meta``      channel-wise min/max key per (page, KV head)   (KVDrive §2.2, §2.3)
+* ``head_scores``     Quest score per (sequence, query head, block)  (KVDrive §2.2)
+* ``group_scores``    max of the head scores over each GQA group
+* ``topk``            rank-count Top-K, lower index wins ties, ascending output
+* ``attention``       softmax decode attention, dense or over selected blocks
+                      (Dual-Blade background; KVDrive §2.3 step 3)
+* ``attention_splits``  the same on each contiguous chunk of the block list
+* ``combine``         log-sum-exp merge of split partials
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(_HERE, "liboracle.so")
+# The pin tests' mutation check points this at a deliberately broken build of
+# oracle.c to show that the pins catch the mistake.
+_LIB_ENV = "KVD_ORACLE_LIB"
+_lib = None
+
+_D = ctypes.POINTER(ctypes.c_double)
+_I = ctypes.POINTER(ctypes.c_int32)
+_int = ctypes.c_int
+
+
+def _load():
+    global _lib
+    if _lib is not None:
+        return _lib
+    path = os.environ.get(_LIB_ENV) or _LIB_PATH
+    if path == _LIB_PATH and not os.path.exists(_LIB_PATH):
+        from . import build as _b
+        _b.build()
+    lib = ctypes.CDLL(path)
+    lib.oracle_num_threads.restype = _int
+    lib.oracle_block_meta.argtypes = [_D, _int, _int, _int, _I, _I, _int, _D]
+    lib.oracle_head_scores.argtypes = [_D, _D, _I, _I, _int, _int, _int, _int, _int, _int, _D]
+    lib.oracle_group_scores.argtypes = [_D, _int, _int, _int, _int, _D]
+    lib.oracle_topk.argtypes = [_D, _I, _int, _int, _int, _int, _int, _I, _I]
+    lib.oracle_attention.argtypes = [_D, _D, _D, _I, _I, _I, _I, _int, _int, _int, _int, _int,
+                                     _int, _int, ctypes.c_double, _D, _D]
+    lib.oracle_attention_splits.argtypes = [_D, _D, _D, _I, _I, _I, _I, _int, _int, _int, _int,
+                                            _int, _int, _int, ctypes.c_double, _int, _D, _D, _D]
+    lib.oracle_combine.argtypes = [_int, _int, _int, _int, _D, _D, _D, _D, _D]
+    for f in ("oracle_block_meta", "oracle_head_scores", "oracle_group_scores", "oracle_topk",
+              "oracle_attention", "oracle_attention_splits", "oracle_combine"):
+        getattr(lib, f).restype = None
+    _lib = lib
+    return lib
+
+
+def num_threads() -> int:
+    return int(_load().oracle_num_threads())
+
+
+def _f64(a) -> np.ndarray:
+    return np.ascontiguousarray(a, dtype=np.float64)
+
+
+def _i32(a) -> np.ndarray:
+    return np.ascontiguousarray(a, dtype=np.int32)
+
+
+def _pd(a: Optional[np.ndarray]):
+    return None if a is None else a.ctypes.data_as(_D)
+
+
+def _pi(a: Optional[np.ndarray]):
+    return None if a is None else a.ctypes.data_as(_I)
+
+
+def block_meta(k_pool, page_ids, valid_tokens, kmeta: Optional[np.ndarray] = None) -> np.ndarray:
+    """kmeta [P, Hkv, 2, D] (0 = channel min, 1 = channel max) over each listed page's
+    first ``valid_tokens`` slots.  Pages not listed keep the values of ``kmeta``
+    (zeros if it is not given)."""
+    k = _f64(k_pool)
+    P, Hkv, bs, D = k.shape
+    ids, val = _i32(page_ids), _i32(valid_tokens)
+    out = np.zeros((P, Hkv, 2, D)) if kmeta is None else _f64(kmeta).copy()
+    _load().oracle_block_meta(_pd(k), Hkv, bs, D, _pi(ids), _pi(val), len(ids), _pd(out))
+    return out
+
+
+def head_scores(q, kmeta, block_table, seq_lens, block_size: int) -> np.ndarray:
+    """Quest score per (b, query head, logical block) [B, Hq, maxN]; -inf past N_b."""
+    q, km = _f64(q), _f64(kmeta)
+    bt, sl = _i32(block_table), _i32(seq_lens)
+    B, Hq, D = q.shape
+    Hkv = km.shape[1]
+    maxN = bt.shape[1]
+    out = np.empty((B, Hq, maxN))
+    _load().oracle_head_scores(_pd(q), _pd(km), _pi(bt), _pi(sl), B, Hq, Hkv, D, block_size,
+                               maxN, _pd(out))
+    return out
+
+
+def group_scores(head_scores_, num_kv_heads: int) -> np.ndarray:
+    """Group score [B, Hkv, maxN]: max over the query heads of each KV head."""
+    hs = _f64(head_scores_)
+    B, Hq, maxN = hs.shape
+    out = np.empty((B, num_kv_heads, maxN))
+    _load().oracle_group_scores(_pd(hs), B, Hq, num_kv_heads, maxN, _pd(out))
+    return out
+
+
+def topk(group_scores_, seq_lens, block_size: int, k: int):
+    """(sel int32 [B, Hkv, k] ascending, -1 padded;  sel_count int32 [B, Hkv])."""
+    gs = _f64(group_scores_)
+    sl = _i32(seq_lens)
+    B, Hkv, maxN = gs.shape
+    sel = np.empty((B, Hkv, k), dtype=np.int32)
+    cnt = np.empty((B, Hkv), dtype=np.int32)
+    _load().oracle_topk(_pd(gs), _pi(sl), B, Hkv, maxN, block_size, k, _pi(sel), _pi(cnt))
+    return sel, cnt
+
+
+def attention(q, k_pool, v_pool, block_table, seq_lens, scale: float,
+              sel=None, sel_count=None):
+    """(out [B, Hq, D], lse [B, Hq]) of decode attention; dense when ``sel`` is None."""
+    q, k, v = _f64(q), _f64(k_pool), _f64(v_pool)
+    bt, sl = _i32(block_table), _i32(seq_lens)
+    B, Hq, D = q.shape
+    _, Hkv, bs, _ = k.shape
+    maxN = bt.shape[1]
+    s = None if sel is None else _i32(sel)
+    c = None if sel_count is None else _i32(sel_count)
+    stride = 0 if s is None else s.shape[-1]
+    out = np.empty((B, Hq, D))
+    lse = np.empty((B, Hq))
+    _load().oracle_attention(_pd(q), _pd(k), _pd(v), _pi(bt), _pi(sl), _pi(s), _pi(c), stride,
+                             B, Hq, Hkv, D, bs, maxN, float(scale), _pd(out), _pd(lse))
+    return out, lse
+
+
+def attention_splits(q, k_pool, v_pool, block_table, seq_lens, scale: float, num_splits: int,
+                     sel=None, sel_count=None):
+    """(part_o [B, Hq, S, D], part_m [B, Hq, S], part_l [B, Hq, S]) split partials."""
+    q, k, v = _f64(q), _f64(k_pool), _f64(v_pool)
+    bt, sl = _i32(block_table), _i32(seq_lens)
+    B, Hq, D = q.shape
+    _, Hkv, bs, _ = k.shape
+    maxN = bt.shape[1]
+    s = None if sel is None else _i32(sel)
+    c = None if sel_count is None else _i32(sel_count)
+    stride = 0 if s is None else s.shape[-1]
+    S = int(num_splits)
+    po = np.empty((B, Hq, S, D))
+    pm = np.empty((B, Hq, S))
+    pl = np.empty((B, Hq, S))
+    _load().oracle_attention_splits(_pd(q), _pd(k), _pd(v), _pi(bt), _pi(sl), _pi(s), _pi(c),
+                                    stride, B, Hq, Hkv, D, bs, maxN, float(scale), S,
+                                    _pd(po), _pd(pm), _pd(pl))
+    return po, pm, pl
+
+
+def combine(part_o, part_m, part_l):
+    """(out [B, Hq, D], lse [B, Hq]) from split partials."""
+    po, pm, pl = _f64(part_o), _f64(part_m), _f64(part_l)
+    B, Hq, S, D = po.shape
+    out = np.empty((B, Hq, D))
+    lse = np.empty((B, Hq))
+    _load().oracle_combine(B, Hq, D, S, _pd(po), _pd(pm), _pd(pl), _pd(out), _pd(lse))
+    return out, lse
+
+
+def sparse_step(q, k_pool, block_table, seq_lens, block_size: int, k: int, kmeta=None):
+    """Convenience: meta (if not given) -> head scores -> group scores -> Top-K.
+
+    Returns (kmeta, head_scores, group_scores, sel, sel_count)."""
+    qa = _f64(q)
+    Hkv = np.asarray(k_pool).shape[1]
+    if kmeta is None:
+        bt, sl = _i32(block_table), _i32(seq_lens)
+        ids, val = [], []
+        for b in range(bt.shape[0]):
+            nb = -(-int(sl[b]) // block_size)
+            for n in range(nb):
+                ids.append(bt[b, n])
+                val.append(min(block_size, int(sl[b]) - n * block_size))
+        kmeta = block_meta(k_pool, ids, val)
+    hs = head_scores(qa, kmeta, block_table, seq_lens, block_size)
+    gs = group_scores(hs, Hkv)
+    sel, cnt = topk(gs, seq_lens, block_size, k)
+    return kmeta, hs, gs, sel, cnt

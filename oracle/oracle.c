@@ -1,0 +1,342 @@
+/*
+ * fp64 CPU oracle for paged Top-K decode attention.
+ *
+ * TEST INFRASTRUCTURE ONLY.  This file is the slow, plain reference that the
+ * HIP path is checked against.  Only the test suite, the smoke check and the
+ * CPU-baseline leg of the benchmark may load it; the library never does.  It
+ * shares no code, header, table or helper with the HIP path.
+ *
+ * Every quantity is computed in double precision from exact float64 copies of
+ * the (fp32 / fp16 / bf16) inputs, with plain loops in the order the
+ * definitions state them.  OpenMP only splits independent rows
+ * (a sequence, a head, a page) across threads; it never changes the order of
+ * a sum.
+ *
+ * Sources (cited by page and section):
+ *  - KVDrive paper (Chinese translation page), §2.2 "Sparse attention": Quest
+ *    cuts the keys into blocks, estimates a block's importance by multiplying
+ *    the query with the channel-wise minimum and maximum of its keys, and
+ *    keeps only the Top-K blocks for each query.
+ *  - KVDrive, §2.3 "KV cache offloading": spatial chunking uses min/max/mean
+ *    keys of adjacent tokens as block representatives; a decode step selects
+ *    critical entries through a GPU-resident index, fetches them, and runs
+ *    sparse attention over them.
+ *  - KVDrive, §4 "System overview": the index is built at prefill.
+ *  - Dual-Blade page, "Background and key observations": every decode step
+ *    loads all previous K/V pairs to compute the current token's attention.
+ *  - DirectKV review page, "Core method" 3: the fused decode kernel computes
+ *    scores and a streaming softmax in one pass over the KV.
+ *
+ * Readings where the pages are silent (also listed in the design notes):
+ *  - block score  sigma = sum_c max(q_c*kmin_c, q_c*kmax_c), unscaled;
+ *  - GQA: one selection per (sequence, KV head); its score is the max of the
+ *    per-query-head scores of that group; query head h uses KV head h / G;
+ *  - K_eff = min(K, N_b); ties go to the lower block index; the selected list
+ *    is emitted in ascending block order;
+ *  - attention logit z_t = scale * (q . k_t), softmax over the token set;
+ *  - split s of a list of n blocks covers list positions
+ *    [s*c, min((s+1)*c, n)) with c = ceil(n / S); an empty split has
+ *    m = -inf, l = 0, o = 0.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+typedef int64_t i64;
+
+int oracle_num_threads(void) {
+#ifdef _OPENMP
+  return omp_get_max_threads();
+#else
+  return 1;
+#endif
+}
+
+static i64 ceil_div(i64 a, i64 b) { return (a + b - 1) / b; }
+
+/* Element (page p, KV head j, slot s, channel c) of a [P, Hkv, bs, D] pool. */
+static const double* pool_row(const double* pool, i64 p, i64 j, i64 s, int Hkv, int bs, int D) {
+  return pool + (((p * Hkv + j) * bs + s) * (i64)D);
+}
+
+/*
+ * O1 block meta (KVDrive §2.2 / §2.3: channel-wise min and max key of a block).
+ * kmeta layout [P, Hkv, 2, D]; index 0 = min, 1 = max; only the listed pages
+ * are written, over their first valid_tokens[i] slots.
+ */
+void oracle_block_meta(const double* k_pool, int Hkv, int bs, int D,
+                       const int32_t* page_ids, const int32_t* valid_tokens, int n_ids,
+                       double* kmeta) {
+#pragma omp parallel for schedule(static)
+  for (int i = 0; i < n_ids; ++i) {
+    const i64 p = page_ids[i];
+    const int nv = valid_tokens[i];
+    for (int j = 0; j < Hkv; ++j) {
+      double* mn = kmeta + ((p * Hkv + j) * 2 + 0) * (i64)D;
+      double* mx = kmeta + ((p * Hkv + j) * 2 + 1) * (i64)D;
+      for (int c = 0; c < D; ++c) {
+        double lo = INFINITY, hi = -INFINITY;
+        for (int s = 0; s < nv; ++s) {
+          const double x = pool_row(k_pool, p, j, s, Hkv, bs, D)[c];
+          if (x < lo) lo = x;
+          if (x > hi) hi = x;
+        }
+        mn[c] = lo;
+        mx[c] = hi;
+      }
+    }
+  }
+}
+
+/*
+ * O2 per-query-head Quest score of every logical block (KVDrive §2.2):
+ *   sigma[b,h,n] = sum_c max(q[b,h,c]*kmin[p,j,c], q[b,h,c]*kmax[p,j,c])
+ * with p = block_table[b,n] and j = h / G.  -inf for n >= N_b.
+ */
+void oracle_head_scores(const double* q, const double* kmeta, const int32_t* block_table,
+                        const int32_t* seq_lens, int B, int Hq, int Hkv, int D, int bs, int maxN,
+                        double* head_scores) {
+  const int G = Hq / Hkv;
+#pragma omp parallel for collapse(2) schedule(static)
+  for (int b = 0; b < B; ++b) {
+    for (int h = 0; h < Hq; ++h) {
+      const i64 nb = ceil_div(seq_lens[b], bs);
+      const int j = h / G;
+      const double* qh = q + ((i64)b * Hq + h) * D;
+      double* out = head_scores + ((i64)b * Hq + h) * maxN;
+      for (i64 n = 0; n < maxN; ++n) {
+        if (n >= nb) { out[n] = -INFINITY; continue; }
+        const i64 p = block_table[(i64)b * maxN + n];
+        const double* mn = kmeta + ((p * Hkv + j) * 2 + 0) * (i64)D;
+        const double* mx = kmeta + ((p * Hkv + j) * 2 + 1) * (i64)D;
+        double acc = 0.0;
+        for (int c = 0; c < D; ++c) {
+          const double a = qh[c] * mn[c];
+          const double e = qh[c] * mx[c];
+          acc += (a > e) ? a : e;
+        }
+        out[n] = acc;
+      }
+    }
+  }
+}
+
+/*
+ * O3 group score: Sigma[b,j,n] = max over the G query heads h with h / G == j
+ * of sigma[b,h,n].
+ */
+void oracle_group_scores(const double* head_scores, int B, int Hq, int Hkv, int maxN,
+                         double* group_scores) {
+  const int G = Hq / Hkv;
+  for (int b = 0; b < B; ++b)
+    for (int j = 0; j < Hkv; ++j)
+      for (i64 n = 0; n < maxN; ++n) {
+        double best = -INFINITY;
+        for (int g = 0; g < G; ++g) {
+          const double s = head_scores[((i64)b * Hq + j * G + g) * maxN + n];
+          if (s > best) best = s;
+        }
+        group_scores[((i64)b * Hkv + j) * maxN + n] = best;
+      }
+}
+
+/*
+ * O4 Top-K selection by rank count (KVDrive §2.2: keep the Top-K blocks):
+ * block n < N_b is selected iff
+ *   #{ m < N_b : S_m > S_n  or  (S_m == S_n and m < n) }  <  K_eff,
+ * K_eff = min(K, N_b).  The selected blocks are written in ascending order,
+ * the rest of the row is -1.
+ */
+void oracle_topk(const double* group_scores, const int32_t* seq_lens, int B, int Hkv, int maxN,
+                 int bs, int K, int32_t* sel, int32_t* sel_count) {
+#pragma omp parallel for collapse(2) schedule(dynamic)
+  for (int b = 0; b < B; ++b) {
+    for (int j = 0; j < Hkv; ++j) {
+      const i64 nb = ceil_div(seq_lens[b], bs);
+      const i64 keff = (K < nb) ? K : nb;
+      const double* s = group_scores + ((i64)b * Hkv + j) * maxN;
+      int32_t* out = sel + ((i64)b * Hkv + j) * K;
+      i64 w = 0;
+      for (i64 n = 0; n < nb; ++n) {
+        i64 rank = 0;
+        for (i64 m = 0; m < nb; ++m)
+          if (s[m] > s[n] || (s[m] == s[n] && m < n)) ++rank;
+        if (rank < keff) out[w++] = (int32_t)n;
+      }
+      for (i64 r = w; r < K; ++r) out[r] = -1;
+      sel_count[(i64)b * Hkv + j] = (int32_t)w;
+    }
+  }
+}
+
+/*
+ * The logical block list of (b, kv head j): all blocks 0..N_b-1 when sel is
+ * NULL (dense decode, Dual-Blade background), else the selected list.
+ */
+static i64 block_list(const int32_t* sel, int sel_stride, int b, int j, int Hkv, i64 pos) {
+  if (!sel) return pos;
+  return sel[((i64)b * Hkv + j) * sel_stride + pos];
+}
+
+static i64 list_len(const int32_t* sel_count, int b, int j, int Hkv, i64 nb) {
+  return sel_count ? sel_count[(i64)b * Hkv + j] : nb;
+}
+
+/*
+ * Softmax attention of query (b, h) over the tokens of list positions
+ * [pos0, pos1): z_t = scale * (q . k_t); m = max z; l = sum exp(z - m);
+ * o = sum exp(z - m) v_t / l.  Token t of logical block n lives at page
+ * block_table[b, n], slot t - n*bs, and only t < L_b count.
+ * Writes o[D] and returns (m, l) through the pointers.  An empty range gives
+ * m = -inf, l = 0, o = 0.
+ */
+static void attend_range(const double* q, const double* k_pool, const double* v_pool,
+                         const int32_t* block_table, const int32_t* seq_lens,
+                         const int32_t* sel, int sel_stride,
+                         int Hq, int Hkv, int D, int bs, int maxN, double scale,
+                         int b, int h, i64 pos0, i64 pos1,
+                         double* z_buf, double* o, double* m_out, double* l_out) {
+  const int G = Hq / Hkv;
+  const int j = h / G;
+  const i64 L = seq_lens[b];
+  const double* qh = q + ((i64)b * Hq + h) * D;
+
+  /* pass 1: logits of every token in the range */
+  i64 nt = 0;
+  double m = -INFINITY;
+  for (i64 pos = pos0; pos < pos1; ++pos) {
+    const i64 n = block_list(sel, sel_stride, b, j, Hkv, pos);
+    const i64 p = block_table[(i64)b * maxN + n];
+    for (int s = 0; s < bs; ++s) {
+      const i64 t = n * bs + s;
+      if (t >= L) break;
+      const double* k = pool_row(k_pool, p, j, s, Hkv, bs, D);
+      double dot = 0.0;
+      for (int c = 0; c < D; ++c) dot += qh[c] * k[c];
+      const double z = scale * dot;
+      z_buf[nt++] = z;
+      if (z > m) m = z;
+    }
+  }
+  for (int c = 0; c < D; ++c) o[c] = 0.0;
+  if (nt == 0) { *m_out = -INFINITY; *l_out = 0.0; return; }
+
+  /* pass 2: l = sum exp(z - m), o = sum exp(z - m) v */
+  double l = 0.0;
+  i64 it = 0;
+  for (i64 pos = pos0; pos < pos1; ++pos) {
+    const i64 n = block_list(sel, sel_stride, b, j, Hkv, pos);
+    const i64 p = block_table[(i64)b * maxN + n];
+    for (int s = 0; s < bs; ++s) {
+      const i64 t = n * bs + s;
+      if (t >= L) break;
+      const double e = exp(z_buf[it++] - m);
+      const double* v = pool_row(v_pool, p, j, s, Hkv, bs, D);
+      l += e;
+      for (int c = 0; c < D; ++c) o[c] += e * v[c];
+    }
+  }
+  for (int c = 0; c < D; ++c) o[c] /= l;
+  *m_out = m;
+  *l_out = l;
+}
+
+/*
+ * O5 decode attention for every (b, h): dense over t < L_b when sel is NULL,
+ * else over the tokens of the selected blocks of (b, h / G).
+ * out [B, Hq, D]; lse [B, Hq] = m + ln l (may be NULL).
+ */
+void oracle_attention(const double* q, const double* k_pool, const double* v_pool,
+                      const int32_t* block_table, const int32_t* seq_lens,
+                      const int32_t* sel, const int32_t* sel_count, int sel_stride,
+                      int B, int Hq, int Hkv, int D, int bs, int maxN, double scale,
+                      double* out, double* lse) {
+  const int G = Hq / Hkv;
+#pragma omp parallel
+  {
+    i64 maxL = 0;
+    for (int b = 0; b < B; ++b) if (seq_lens[b] > maxL) maxL = seq_lens[b];
+    double* z_buf = (double*)malloc(sizeof(double) * (size_t)(maxL > 0 ? maxL : 1));
+#pragma omp for collapse(2) schedule(dynamic)
+    for (int b = 0; b < B; ++b) {
+      for (int h = 0; h < Hq; ++h) {
+        const i64 nb = ceil_div(seq_lens[b], bs);
+        const i64 n_list = list_len(sel_count, b, h / G, Hkv, nb);
+        double m, l;
+        double* o = out + ((i64)b * Hq + h) * D;
+        attend_range(q, k_pool, v_pool, block_table, seq_lens, sel, sel_stride,
+                     Hq, Hkv, D, bs, maxN, scale, b, h, 0, n_list, z_buf, o, &m, &l);
+        if (lse) lse[(i64)b * Hq + h] = m + log(l);
+      }
+    }
+    free(z_buf);
+  }
+}
+
+/*
+ * O6 split partials: O5 restricted to each contiguous chunk of the block list.
+ * part_o [B, Hq, S, D] (normalised per split), part_m / part_l [B, Hq, S].
+ */
+void oracle_attention_splits(const double* q, const double* k_pool, const double* v_pool,
+                             const int32_t* block_table, const int32_t* seq_lens,
+                             const int32_t* sel, const int32_t* sel_count, int sel_stride,
+                             int B, int Hq, int Hkv, int D, int bs, int maxN, double scale,
+                             int num_splits, double* part_o, double* part_m, double* part_l) {
+  const int G = Hq / Hkv;
+  const int S = num_splits;
+#pragma omp parallel
+  {
+    i64 maxL = 0;
+    for (int b = 0; b < B; ++b) if (seq_lens[b] > maxL) maxL = seq_lens[b];
+    double* z_buf = (double*)malloc(sizeof(double) * (size_t)(maxL > 0 ? maxL : 1));
+#pragma omp for collapse(2) schedule(dynamic)
+    for (int b = 0; b < B; ++b) {
+      for (int h = 0; h < Hq; ++h) {
+        const i64 nb = ceil_div(seq_lens[b], bs);
+        const i64 n_list = list_len(sel_count, b, h / G, Hkv, nb);
+        const i64 chunk = ceil_div(n_list, S);
+        for (int s = 0; s < S; ++s) {
+          i64 p0 = (i64)s * chunk, p1 = p0 + chunk;
+          if (p0 > n_list) p0 = n_list;
+          if (p1 > n_list) p1 = n_list;
+          const i64 row = ((i64)b * Hq + h) * S + s;
+          attend_range(q, k_pool, v_pool, block_table, seq_lens, sel, sel_stride,
+                       Hq, Hkv, D, bs, maxN, scale, b, h, p0, p1, z_buf,
+                       part_o + row * D, part_m + row, part_l + row);
+        }
+      }
+    }
+    free(z_buf);
+  }
+}
+
+/*
+ * Log-sum-exp merge of split partials:
+ *   M = max_s m_s;  w_s = l_s * exp(m_s - M)  (0 for an empty split);
+ *   out = sum_s w_s o_s / sum_s w_s;  lse = M + ln(sum_s w_s).
+ */
+void oracle_combine(int B, int Hq, int D, int num_splits, const double* part_o,
+                    const double* part_m, const double* part_l, double* out, double* lse) {
+  const int S = num_splits;
+  for (i64 r = 0; r < (i64)B * Hq; ++r) {
+    double M = -INFINITY;
+    for (int s = 0; s < S; ++s)
+      if (part_m[r * S + s] > M) M = part_m[r * S + s];
+    double wsum = 0.0;
+    double* o = out + r * D;
+    for (int c = 0; c < D; ++c) o[c] = 0.0;
+    for (int s = 0; s < S; ++s) {
+      const double ms = part_m[r * S + s];
+      if (ms == -INFINITY) continue;
+      const double w = part_l[r * S + s] * exp(ms - M);
+      wsum += w;
+      for (int c = 0; c < D; ++c) o[c] += w * part_o[(r * S + s) * D + c];
+    }
+    for (int c = 0; c < D; ++c) o[c] /= wsum;
+    if (lse) lse[r] = M + log(wsum);
+  }
+}

@@ -1,0 +1,65 @@
+"""The oracle's pins catch plausible mistakes (CPU only).
+
+Each case copies oracle.c, plants one slip in the copy, builds it with gcc
+into a temporary library, and runs tests/test_oracle_pins.py against that
+library (through the oracle's KVD_ORACLE_LIB override) in a subprocess.  The
+pin suite must fail for every planted slip.  The committed oracle is never
+modified.
+"""
+import os
+import subprocess
+import sys
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+SRC = os.path.join(ROOT, "oracle", "oracle.c")
+
+# (name, text in oracle.c, replacement, occurrence to replace: 0-based index)
+MUTANTS = [
+    ("meta_max_is_min", "if (x > hi) hi = x;", "if (x < hi) hi = x;", 0),
+    ("meta_ignores_valid_count", "for (int s = 0; s < nv; ++s)", "for (int s = 0; s < bs; ++s)", 0),
+    ("score_min_not_max", "acc += (a > e) ? a : e;", "acc += (a < e) ? a : e;", 0),
+    ("score_kmax_only", "acc += (a > e) ? a : e;", "acc += e;", 0),
+    ("score_wrong_head_map", "const int j = h / G;", "const int j = h % Hkv;", 0),
+    ("group_min_not_max", "if (s > best) best = s;", "if (s < best || best == -INFINITY) best = s;", 0),
+    ("topk_ties_to_higher_index", "(s[m] == s[n] && m < n)", "(s[m] == s[n] && m > n)", 0),
+    ("topk_keeps_one_too_many", "if (rank < keff) out[w++]", "if (rank <= keff && w < K) out[w++]", 0),
+    ("attn_drops_scale", "const double z = scale * dot;", "const double z = dot;", 0),
+    ("attn_token_off_by_one", "if (t >= L) break;", "if (t > L) break;", 0),
+    ("attn_value_is_key", "const double* v = pool_row(v_pool", "const double* v = pool_row(k_pool", 0),
+    ("attn_wrong_kv_head", "const int j = h / G;", "const int j = h % Hkv;", 1),
+    ("attn_unnormalised", "for (int c = 0; c < D; ++c) o[c] /= l;", "", 0),
+    ("split_chunks_overlap", "i64 p0 = (i64)s * chunk, p1 = p0 + chunk;",
+     "i64 p0 = (i64)s * chunk, p1 = p0 + chunk + 1;", 0),
+    ("combine_drops_l", "const double w = part_l[r * S + s] * exp(ms - M);",
+     "const double w = exp(ms - M);", 0),
+    ("combine_lse_drops_max", "if (lse) lse[r] = M + log(wsum);", "if (lse) lse[r] = log(wsum);", 0),
+]
+
+
+def _replace_nth(text, old, new, n):
+    start = -1
+    for _ in range(n + 1):
+        start = text.find(old, start + 1)
+        if start < 0:
+            raise AssertionError(f"pattern not found ({n}): {old!r}")
+    return text[:start] + new + text[start + len(old):]
+
+
+@pytest.mark.parametrize("name,old,new,nth", MUTANTS, ids=[m[0] for m in MUTANTS])
+def test_pins_catch_planted_mistake(tmp_path, name, old, new, nth):
+    with open(SRC) as f:
+        text = f.read()
+    mutated = _replace_nth(text, old, new, nth)
+    assert mutated != text
+    src = tmp_path / "oracle_mut.c"
+    lib = tmp_path / "liboracle_mut.so"
+    src.write_text(mutated)
+    subprocess.run(["gcc", "-std=c11", "-O2", "-ffp-contract=off", "-fopenmp", "-fPIC",
+                    "-shared", "-o", str(lib), str(src), "-lm"], check=True)
+    env = dict(os.environ, KVD_ORACLE_LIB=str(lib), OMP_NUM_THREADS="2")
+    r = subprocess.run([sys.executable, "-m", "pytest", "-x", "-q", "-p", "no:cacheprovider",
+                        os.path.join(ROOT, "tests", "test_oracle_pins.py")],
+                       cwd=ROOT, env=env, capture_output=True, text=True, timeout=600)
+    assert r.returncode != 0, f"mutant {name} survived the pins:\n{r.stdout[-2000:]}"

@@ -1,0 +1,462 @@
+"""Pins of the fp64 oracle against things other than itself (no GPU).
+
+Each oracle function is checked against at least one of: a hand-derived golden
+fixture (tests/golden), a library routine (numpy reductions, Python's sort,
+torch's scaled_dot_product_attention, scipy's softmax / logsumexp), brute force
+on tiny inputs (box corners, subset enumeration), closed-form special cases and
+invariants of the method.  The pins are chosen so that a plausible slip in the
+oracle (a swapped min/max, a dropped scale, a wrong head map, a reversed tie
+rule, an off-by-one token mask, K used for V, a dropped l in the merge) fails
+at least one of them; tests/test_oracle_mutants.py plants exactly those slips.
+"""
+import itertools
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+import scipy.special
+import torch
+
+import oracle
+from kv_cache_decode_amd import workload as wl
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "quest_tiny.json")
+
+
+def mk(B=2, Hq=4, Hkv=2, D=8, lens=(37, 16), dtype="f32", seed=0, **kw):
+    spec = wl.Workload(name="pin", num_seqs=B, num_q_heads=Hq, num_kv_heads=Hkv, head_dim=D,
+                       seq_lens=tuple(lens), dtype=dtype, seed=seed, **kw)
+    return wl.generate(spec)
+
+
+def page_lists(data):
+    """All (page id, valid tokens) pairs referenced by the block table."""
+    spec = data.spec
+    ids, val = [], []
+    for b in range(spec.num_seqs):
+        for n in range(spec.blocks(b)):
+            ids.append(int(data.block_table[b, n]))
+            val.append(min(spec.block_size, spec.seq_lens[b] - n * spec.block_size))
+    return np.array(ids, np.int32), np.array(val, np.int32)
+
+
+def gather(pool, data, b, j, blocks):
+    """Valid token rows of (sequence b, KV head j) over the logical ``blocks``, in order."""
+    spec = data.spec
+    bs, L = spec.block_size, spec.seq_lens[b]
+    rows = []
+    for n in blocks:
+        p = data.block_table[b, n]
+        nv = min(bs, L - n * bs)
+        rows.append(pool[p, j, :nv, :])
+    return np.concatenate(rows, axis=0)
+
+
+def sdpa(qv, K, V, scale):
+    """torch's fused attention in float64 on the CPU for one query row."""
+    q = torch.from_numpy(np.asarray(qv, np.float64)).reshape(1, 1, 1, -1)
+    k = torch.from_numpy(np.ascontiguousarray(K, np.float64))[None, None]
+    v = torch.from_numpy(np.ascontiguousarray(V, np.float64))[None, None]
+    out = torch.nn.functional.scaled_dot_product_attention(q, k, v, scale=scale)
+    return out.reshape(-1).numpy()
+
+
+def full_meta(data):
+    ids, val = page_lists(data)
+    return oracle.block_meta(data.k64(), ids, val)
+
+
+@pytest.fixture(scope="module")
+def golden():
+    with open(GOLDEN) as f:
+        return json.load(f)
+
+
+# ---------------------------------------------------------------- O1 block meta
+
+def test_meta_golden(golden):
+    g = golden["meta_score"]
+    k = np.array(g["k_slots"], np.float64).reshape(1, 1, g["block_size"], g["head_dim"])
+    km = oracle.block_meta(k, [0], [g["valid_tokens"]])
+    assert km[0, 0, 0].tolist() == g["kmin"]
+    assert km[0, 0, 1].tolist() == g["kmax"]
+
+
+@pytest.mark.parametrize("dtype", ["f32", "f16", "bf16"])
+def test_meta_matches_numpy_reduction(dtype):
+    data = mk(B=3, Hq=6, Hkv=3, D=16, lens=(45, 16, 3), dtype=dtype, seed=11, extra_pages=2)
+    k64 = data.k64()
+    ids, val = page_lists(data)
+    km = oracle.block_meta(k64, ids, val)
+    for p, nv in zip(ids, val):
+        np.testing.assert_array_equal(km[p, :, 0], k64[p, :, :nv].min(axis=1))
+        np.testing.assert_array_equal(km[p, :, 1], k64[p, :, :nv].max(axis=1))
+
+
+def test_meta_brackets_and_attains_every_valid_key():
+    data = mk(B=2, Hq=2, Hkv=2, D=8, lens=(50, 7), seed=12)
+    k64 = data.k64()
+    ids, val = page_lists(data)
+    km = oracle.block_meta(k64, ids, val)
+    for p, nv in zip(ids, val):
+        ks = k64[p, :, :nv]                          # [Hkv, nv, D]
+        assert np.all(km[p, :, 0][:, None] <= ks) and np.all(ks <= km[p, :, 1][:, None])
+        assert np.all(np.any(ks == km[p, :, 0][:, None], axis=1))
+        assert np.all(np.any(ks == km[p, :, 1][:, None], axis=1))
+
+
+# ---------------------------------------------------------------- O2 / O3 scores
+
+def test_score_golden(golden):
+    g = golden["meta_score"]
+    kmeta = np.array([[[g["kmin"], g["kmax"]]]], np.float64)          # [1, 1, 2, D]
+    for qv, want, tok_max in zip(g["queries"], g["scores"], g["token_max_dot"]):
+        q = np.array(qv, np.float64).reshape(1, 1, -1)
+        s = oracle.head_scores(q, kmeta, np.zeros((1, 1), np.int32), np.array([3], np.int32),
+                               g["block_size"])
+        assert s[0, 0, 0] == want
+        assert s[0, 0, 0] >= tok_max
+
+
+def test_score_is_support_function_of_the_key_box():
+    """Brute force: the Quest score equals max over the 2^D corners of the
+    [kmin, kmax] box of q . x -- the largest q . k any key inside the block's
+    bounding box can reach.  D = 6 keeps the enumeration at 64 corners."""
+    data = mk(B=2, Hq=4, Hkv=2, D=6, lens=(40, 21), seed=13)
+    q64 = data.q64()
+    km = full_meta(data)
+    hs = oracle.head_scores(q64, km, data.block_table, data.seq_lens, 16)
+    G = data.spec.group
+    corners = np.array(list(itertools.product([0, 1], repeat=6)))         # [64, 6]
+    for b in range(2):
+        for h in range(4):
+            j = h // G
+            for n in range(data.spec.blocks(b)):
+                p = data.block_table[b, n]
+                box = np.where(corners == 0, km[p, j, 0], km[p, j, 1])   # [64, 6]
+                want = max(float(np.dot(q64[b, h], x)) for x in box)
+                assert hs[b, h, n] == pytest.approx(want, rel=1e-13, abs=1e-13)
+
+
+def test_score_upper_bounds_every_token_dot():
+    data = mk(B=2, Hq=8, Hkv=2, D=16, lens=(70, 33), dtype="bf16", seed=14)
+    q64, k64 = data.q64(), data.k64()
+    km = full_meta(data)
+    hs = oracle.head_scores(q64, km, data.block_table, data.seq_lens, 16)
+    gs = oracle.group_scores(hs, 2)
+    G = data.spec.group
+    for b in range(2):
+        for j in range(2):
+            for n in range(data.spec.blocks(b)):
+                K = gather(k64, data, b, j, [n])
+                dots = q64[b, j * G:(j + 1) * G] @ K.T                  # [G, tokens]
+                for g in range(G):
+                    assert hs[b, j * G + g, n] >= dots[g].max() - 1e-12
+                assert gs[b, j, n] >= dots.max() - 1e-12
+
+
+def test_score_block_size_one_is_the_dot_product():
+    data = mk(B=1, Hq=2, Hkv=1, D=16, lens=(9,), block_size=1, seed=15)
+    q64, k64 = data.q64(), data.k64()
+    ids, val = page_lists(data)
+    km = oracle.block_meta(k64, ids, val)
+    hs = oracle.head_scores(q64, km, data.block_table, data.seq_lens, 1)
+    for h in range(2):
+        for n in range(9):
+            p = data.block_table[0, n]
+            assert hs[0, h, n] == pytest.approx(float(q64[0, h] @ k64[p, 0, 0]), rel=1e-13)
+
+
+def test_score_shift_adds_q_dot_u():
+    """K += u for every key shifts kmin and kmax by u, so every score moves by q . u."""
+    data = mk(B=1, Hq=2, Hkv=1, D=8, lens=(64,), seed=16)
+    q64, k64 = data.q64(), data.k64()
+    ids, val = page_lists(data)
+    u = np.linspace(-1.5, 2.0, 8)
+    hs0 = oracle.head_scores(q64, oracle.block_meta(k64, ids, val), data.block_table,
+                             data.seq_lens, 16)
+    hs1 = oracle.head_scores(q64, oracle.block_meta(k64 + u, ids, val), data.block_table,
+                             data.seq_lens, 16)
+    for h in range(2):
+        np.testing.assert_allclose(hs1[0, h], hs0[0, h] + q64[0, h] @ u, rtol=1e-12, atol=1e-12)
+
+
+def test_score_is_minus_inf_past_the_sequence():
+    data = mk(B=2, Hq=2, Hkv=1, D=8, lens=(50, 17), seed=17)
+    hs = oracle.head_scores(data.q64(), full_meta(data), data.block_table, data.seq_lens, 16)
+    assert np.all(np.isneginf(hs[1, :, 2:]))
+    assert np.all(np.isfinite(hs[1, :, :2]))
+
+
+def test_group_score_is_max_over_the_group_and_reduces_for_g1():
+    data = mk(B=2, Hq=8, Hkv=2, D=8, lens=(48, 20), seed=18)
+    hs = oracle.head_scores(data.q64(), full_meta(data), data.block_table, data.seq_lens, 16)
+    gs = oracle.group_scores(hs, 2)
+    np.testing.assert_array_equal(gs, hs.reshape(2, 2, 4, -1).max(axis=2))
+    gs1 = oracle.group_scores(hs, 8)
+    np.testing.assert_array_equal(gs1, hs)
+
+
+def test_scores_invariant_under_page_permutation():
+    data = mk(B=2, Hq=4, Hkv=2, D=8, lens=(40, 30), seed=19)
+    hs0 = oracle.head_scores(data.q64(), full_meta(data), data.block_table, data.seq_lens, 16)
+    rng = np.random.default_rng(5)
+    P = data.spec.num_pages
+    perm = rng.permutation(P)                    # new page of old page p is perm[p]
+    k_new = np.empty_like(data.k_raw)
+    k_new[perm] = data.k_raw
+    data2 = wl.WorkloadData(spec=data.spec, q_raw=data.q_raw, k_raw=k_new, v_raw=data.v_raw,
+                            block_table=perm[data.block_table].astype(np.int32),
+                            seq_lens=data.seq_lens, planted=data.planted)
+    hs1 = oracle.head_scores(data2.q64(), full_meta(data2), data2.block_table, data2.seq_lens, 16)
+    np.testing.assert_array_equal(hs0, hs1)
+
+
+# ---------------------------------------------------------------- O4 Top-K
+
+def test_topk_golden(golden):
+    g = golden["topk"]
+    s = np.array(g["scores"], np.float64).reshape(1, 1, -1)
+    for case in g["cases"]:
+        sel, cnt = oracle.topk(s, np.array([6 * 16], np.int32), 16, case["k"])
+        want = case["selected"]
+        assert cnt[0, 0] == len(want)
+        assert sel[0, 0, :len(want)].tolist() == want
+        assert np.all(sel[0, 0, len(want):] == -1)
+
+
+def _sorted_topk(scores, k):
+    order = sorted(range(len(scores)), key=lambda i: (-scores[i], i))
+    return sorted(order[:k])
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_topk_matches_a_library_sort_with_heavy_ties(seed):
+    rng = np.random.default_rng(100 + seed)
+    B, Hkv = 3, 2
+    lens = rng.integers(1, 40 * 16, size=B).astype(np.int32)
+    maxN = int(max(-(-lens // 16)))
+    gs = rng.integers(-4, 5, size=(B, Hkv, maxN)).astype(np.float64)   # many ties
+    for k in (1, 3, 7, 50):
+        sel, cnt = oracle.topk(gs, lens, 16, k)
+        for b in range(B):
+            nb = -(-int(lens[b]) // 16)
+            for j in range(Hkv):
+                want = _sorted_topk(list(gs[b, j, :nb]), k)
+                assert cnt[b, j] == len(want) == min(k, nb)
+                assert sel[b, j, :cnt[b, j]].tolist() == want
+                assert np.all(sel[b, j, cnt[b, j]:] == -1)
+
+
+def test_topk_is_the_best_subset_by_enumeration():
+    """Brute force: among all K-subsets, the selection has the largest score sum,
+    and among the subsets with that sum it is the lexicographically smallest
+    (lower indices win ties).  Integer scores keep the sums exact."""
+    rng = np.random.default_rng(7)
+    for trial in range(40):
+        n = int(rng.integers(1, 10))
+        scores = rng.integers(-3, 4, size=n).astype(np.float64)
+        for k in range(1, n + 1):
+            best = max(itertools.combinations(range(n), k),
+                       key=lambda c: (sum(scores[list(c)]), [-i for i in c]))
+            sel, cnt = oracle.topk(scores.reshape(1, 1, n), np.array([n * 16], np.int32), 16, k)
+            assert sel[0, 0, :cnt[0, 0]].tolist() == list(best)
+
+
+def test_topk_duplicate_page_tie_goes_to_lower_block():
+    data = mk(B=1, Hq=1, Hkv=1, D=8, lens=(64,), seed=20)
+    bt = data.block_table.copy()
+    bt[0, 3] = bt[0, 1]                              # blocks 1 and 3 read the same page
+    q64 = data.q64()
+    km = full_meta(data)
+    hs = oracle.head_scores(q64, km, bt, data.seq_lens, 16)
+    gs = oracle.group_scores(hs, 1)
+    assert gs[0, 0, 1] == gs[0, 0, 3]
+    # K such that exactly one of the twins fits: rank of the tied value
+    rank = int(np.sum(gs[0, 0, :4] > gs[0, 0, 1]))
+    sel, cnt = oracle.topk(gs, data.seq_lens, 16, rank + 1)
+    chosen = set(sel[0, 0, :cnt[0, 0]].tolist())
+    assert 1 in chosen and 3 not in chosen
+
+
+def test_topk_k_at_least_n_keeps_all_blocks():
+    gs = np.random.default_rng(3).standard_normal((1, 2, 5))
+    sel, cnt = oracle.topk(gs, np.array([70], np.int32), 16, 9)
+    assert cnt.tolist() == [[5, 5]]
+    assert sel[0, 0].tolist() == [0, 1, 2, 3, 4, -1, -1, -1, -1]
+
+
+# ---------------------------------------------------------------- O5 attention
+
+def test_attention_golden(golden):
+    g = golden["attention"]
+    q = np.array(g["q"], np.float64).reshape(1, 1, -1)
+    k = np.array(g["k"], np.float64).reshape(1, 1, 2, 2)
+    v = np.array(g["v"], np.float64).reshape(1, 1, 2, 2)
+    out, lse = oracle.attention(q, k, v, np.zeros((1, 1), np.int32), np.array([2], np.int32),
+                                g["scale"])
+    np.testing.assert_allclose(out[0, 0], g["out"], rtol=1e-14, atol=1e-14)
+    assert lse[0, 0] == pytest.approx(g["lse"], rel=1e-14)
+
+
+@pytest.mark.parametrize("dtype,Hq,Hkv", [("f32", 4, 2), ("f16", 3, 3), ("bf16", 8, 2)])
+def test_dense_attention_matches_torch_sdpa(dtype, Hq, Hkv):
+    data = mk(B=3, Hq=Hq, Hkv=Hkv, D=16, lens=(70, 16, 5), dtype=dtype, seed=21)
+    q64, k64, v64 = data.q64(), data.k64(), data.v64()
+    scale = 1 / math.sqrt(16)
+    out, lse = oracle.attention(q64, k64, v64, data.block_table, data.seq_lens, scale)
+    G = data.spec.group
+    for b in range(3):
+        blocks = range(data.spec.blocks(b))
+        for h in range(Hq):
+            K = gather(k64, data, b, h // G, blocks)
+            V = gather(v64, data, b, h // G, blocks)
+            np.testing.assert_allclose(out[b, h], sdpa(q64[b, h], K, V, scale),
+                                       rtol=1e-12, atol=1e-14)
+            z = scale * (K @ q64[b, h])
+            assert lse[b, h] == pytest.approx(scipy.special.logsumexp(z), rel=1e-13)
+
+
+def test_sparse_attention_matches_softmax_over_selected_tokens():
+    data = mk(B=2, Hq=4, Hkv=2, D=16, lens=(150, 91), dtype="bf16", seed=22)
+    q64, k64, v64 = data.q64(), data.k64(), data.v64()
+    sel, cnt = wl.random_selection(data, 4, seed=3)
+    scale = 0.3
+    out, _ = oracle.attention(q64, k64, v64, data.block_table, data.seq_lens, scale, sel, cnt)
+    G = data.spec.group
+    for b in range(2):
+        for h in range(4):
+            j = h // G
+            blocks = sel[b, j, :cnt[b, j]]
+            K = gather(k64, data, b, j, blocks)
+            V = gather(v64, data, b, j, blocks)
+            w = scipy.special.softmax(scale * (K @ q64[b, h]))
+            np.testing.assert_allclose(out[b, h], w @ V, rtol=1e-12, atol=1e-14)
+
+
+def test_attention_single_token_returns_its_value():
+    data = mk(B=1, Hq=2, Hkv=1, D=8, lens=(1,), seed=23)
+    out, lse = oracle.attention(data.q64(), data.k64(), data.v64(), data.block_table,
+                                data.seq_lens, 0.5)
+    p = data.block_table[0, 0]
+    for h in range(2):
+        np.testing.assert_array_equal(out[0, h], data.v64()[p, 0, 0])
+        assert lse[0, h] == pytest.approx(0.5 * data.q64()[0, h] @ data.k64()[p, 0, 0], rel=1e-14)
+
+
+def test_attention_equal_keys_give_the_mean_value():
+    data = mk(B=1, Hq=1, Hkv=1, D=8, lens=(29,), seed=24)
+    k = data.k64()
+    k[:] = k[0, 0, 0]                                 # every key identical
+    out, lse = oracle.attention(data.q64(), k, data.v64(), data.block_table, data.seq_lens, 0.7)
+    V = gather(data.v64(), data, 0, 0, range(2))
+    np.testing.assert_allclose(out[0, 0], V.mean(axis=0), rtol=1e-13, atol=1e-15)
+    z0 = 0.7 * data.q64()[0, 0] @ k[0, 0, 0]
+    assert lse[0, 0] == pytest.approx(z0 + math.log(29), rel=1e-13)
+
+
+def test_attention_dominant_logit_returns_that_value():
+    data = mk(B=1, Hq=1, Hkv=1, D=8, lens=(40,), seed=25)
+    q = np.zeros((1, 1, 8)); q[0, 0, 0] = 1.0
+    k = np.zeros_like(data.k64())
+    p = data.block_table[0, 1]
+    k[p, 0, 5, 0] = 60.0                               # token 21 dominates by e^60
+    out, _ = oracle.attention(q, k, data.v64(), data.block_table, data.seq_lens, 1.0)
+    np.testing.assert_allclose(out[0, 0], data.v64()[p, 0, 5], rtol=1e-20, atol=1e-23)
+
+
+def test_attention_invariant_under_a_common_key_shift():
+    data = mk(B=2, Hq=4, Hkv=2, D=8, lens=(55, 30), seed=26)
+    q64, k64, v64 = data.q64(), data.k64(), data.v64()
+    u = np.linspace(2.0, -1.0, 8)
+    o0, _ = oracle.attention(q64, k64, v64, data.block_table, data.seq_lens, 0.35)
+    o1, _ = oracle.attention(q64, k64 + u, v64, data.block_table, data.seq_lens, 0.35)
+    np.testing.assert_allclose(o1, o0, rtol=1e-11, atol=1e-13)
+
+
+def test_attention_invariant_under_page_permutation():
+    data = mk(B=2, Hq=2, Hkv=2, D=8, lens=(45, 17), seed=27, extra_pages=3)
+    q64, k64, v64 = data.q64(), data.k64(), data.v64()
+    o0, l0 = oracle.attention(q64, k64, v64, data.block_table, data.seq_lens, 0.35)
+    perm = np.random.default_rng(1).permutation(data.spec.num_pages)
+    k2, v2 = np.empty_like(k64), np.empty_like(v64)
+    k2[perm], v2[perm] = k64, v64
+    o1, l1 = oracle.attention(q64, k2, v2, perm[data.block_table].astype(np.int32),
+                              data.seq_lens, 0.35)
+    np.testing.assert_array_equal(o0, o1)
+    np.testing.assert_array_equal(l0, l1)
+
+
+def test_topk_all_blocks_equals_dense():
+    data = mk(B=2, Hq=4, Hkv=2, D=16, lens=(83, 40), dtype="bf16", seed=28)
+    q64, k64, v64 = data.q64(), data.k64(), data.v64()
+    _, _, _, sel, cnt = oracle.sparse_step(q64, k64, data.block_table, data.seq_lens, 16,
+                                           k=data.spec.max_blocks)
+    od, ld = oracle.attention(q64, k64, v64, data.block_table, data.seq_lens, 0.25)
+    os_, ls = oracle.attention(q64, k64, v64, data.block_table, data.seq_lens, 0.25, sel, cnt)
+    np.testing.assert_array_equal(od, os_)
+    np.testing.assert_array_equal(ld, ls)
+
+
+def test_mha_is_gqa_with_one_head_per_group():
+    """G=1: each query head attends only to its own KV head, so running head h
+    alone (as a 1-head problem) gives the same row."""
+    data = mk(B=1, Hq=3, Hkv=3, D=8, lens=(35,), seed=29)
+    q64, k64, v64 = data.q64(), data.k64(), data.v64()
+    full, _ = oracle.attention(q64, k64, v64, data.block_table, data.seq_lens, 0.4)
+    for h in range(3):
+        one, _ = oracle.attention(q64[:, h:h + 1], k64[:, h:h + 1], v64[:, h:h + 1],
+                                  data.block_table, data.seq_lens, 0.4)
+        np.testing.assert_array_equal(one[0, 0], full[0, h])
+
+
+# ---------------------------------------------------------------- O6 splits + merge
+
+def test_combine_golden(golden):
+    g = golden["combine"]
+    po = np.array(g["part_o"], np.float64).reshape(1, 1, 3, 1)
+    pm = np.array([float(x) for x in g["part_m"]]).reshape(1, 1, 3)
+    pl = np.array(g["part_l"], np.float64).reshape(1, 1, 3)
+    out, lse = oracle.combine(po, pm, pl)
+    assert out[0, 0, 0] == pytest.approx(g["out"][0], rel=1e-15)
+    assert lse[0, 0] == pytest.approx(g["lse"], rel=1e-15)
+
+
+def test_each_split_is_attention_over_its_chunk():
+    data = mk(B=2, Hq=2, Hkv=1, D=8, lens=(150, 40), seed=30)
+    q64, k64, v64 = data.q64(), data.k64(), data.v64()
+    S = 3
+    po, pm, pl = oracle.attention_splits(q64, k64, v64, data.block_table, data.seq_lens, 0.5, S)
+    for b in range(2):
+        nb = data.spec.blocks(b)
+        c = -(-nb // S)
+        for h in range(2):
+            for s in range(S):
+                blocks = range(min(s * c, nb), min((s + 1) * c, nb))
+                if len(blocks) == 0:
+                    assert pm[b, h, s] == -np.inf and pl[b, h, s] == 0
+                    assert np.all(po[b, h, s] == 0)
+                    continue
+                K = gather(k64, data, b, 0, blocks)
+                V = gather(v64, data, b, 0, blocks)
+                z = 0.5 * (K @ q64[b, h])
+                assert pm[b, h, s] == pytest.approx(z.max(), rel=1e-14)
+                assert pl[b, h, s] == pytest.approx(np.exp(z - z.max()).sum(), rel=1e-13)
+                np.testing.assert_allclose(po[b, h, s], sdpa(q64[b, h], K, V, 0.5),
+                                           rtol=1e-12, atol=1e-14)
+
+
+@pytest.mark.parametrize("S", [1, 2, 3, 7, 40])
+@pytest.mark.parametrize("sparse", [False, True])
+def test_split_then_combine_equals_unsplit(S, sparse):
+    data = mk(B=2, Hq=4, Hkv=2, D=16, lens=(190, 33), dtype="f16", seed=31)
+    q64, k64, v64 = data.q64(), data.k64(), data.v64()
+    sel, cnt = wl.random_selection(data, 5, seed=4) if sparse else (None, None)
+    ref, lref = oracle.attention(q64, k64, v64, data.block_table, data.seq_lens, 0.25, sel, cnt)
+    parts = oracle.attention_splits(q64, k64, v64, data.block_table, data.seq_lens, 0.25, S,
+                                    sel, cnt)
+    out, lse = oracle.combine(*parts)
+    np.testing.assert_allclose(out, ref, rtol=1e-12, atol=1e-14)
+    np.testing.assert_allclose(lse, lref, rtol=1e-13)
