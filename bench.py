@@ -1,0 +1,388 @@
+"""Benchmark of the paged Top-K decode step on one MI355X.
+
+Workload: Llama-3.1-8B-shaped GQA decode of one layer at 128k context (batch 1,
+32 query / 8 KV heads, head_dim 128, bf16 KV in 16-token pages, shuffled page
+table, 5% planted blocks, Top-K 256 blocks), synthetic seeded data.
+
+One step = one pass over every stage of the path on that input:
+  block meta build over all 8192 pages -> Quest scores + Top-K 256 ->
+  sparse split-K attention -> merge -> dense split-K attention -> merge.
+The metric is KV GB/s (algorithmic bytes of the step / step time, and the same
+per stage) and decode steps/s; the dominant kernel (dense attention) is also
+reported against the 8 TB/s HBM peak.  Inputs are resident in HBM before the
+timed region.  Four copies of the workload are rotated so that no step can be
+served from the 256 MB last-level cache by the step before it.
+
+Also in the same run: the zero-copy variant (K/V pools in mapped pinned host
+memory; its roofline is the measured host-to-device copy bandwidth), and the
+fp64 oracle timed on the host cores on the same workload (cpu_baseline).
+
+Usage: python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-cpu-baseline]
+       python bench.py --copy-calibration    (a plain 1 GiB device copy, for counter scaling)
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import re
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0
+WORKLOAD = "llama3.1_8b_gqa_b1_128k_bf16"
+HOSTKV_WORKLOAD = "llama3.1_8b_gqa_b1_128k_bf16_hostkv"
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "paged_attn_dense_gqa128k_pmc.md")
+ATTN_SOURCE = os.path.join(ROOT, "kv_cache_decode_amd", "csrc", "kvd_kernels.hip")
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+# ---------------------------------------------------------------- algorithmic bytes
+#
+# Per (block, KV head) unit: K and V tiles of bs x D elements, meta rows of 2 x D.
+
+def stage_bytes(spec, topk: int, s_sparse: int, s_dense: int) -> dict:
+    eb = spec.elem_bytes
+    bs, D, B, Hq, Hkv = spec.block_size, spec.head_dim, spec.num_seqs, spec.num_q_heads, spec.num_kv_heads
+    blocks = spec.used_pages                       # sum_b N_b
+    maxN = spec.max_blocks
+    tile = bs * D * eb                             # one K (or V) tile
+    meta_row = 2 * D * eb
+    q_bytes = B * Hq * D * eb
+    keff = sum(min(topk, spec.blocks(b)) for b in range(B))
+    part = lambda S: B * Hq * S * (D + 2) * 4
+    out = B * Hq * (D + 1) * 4
+    return {
+        "meta_build": blocks * Hkv * (tile + meta_row) + blocks * 8,
+        "score_topk": blocks * Hkv * meta_row + q_bytes + blocks * Hkv * 4      # meta + q + table
+                      + 2 * B * Hkv * maxN * 4                                   # scores out + in
+                      + B * Hkv * (topk + 1) * 4,                                # selection
+        "sparse_attn": keff * Hkv * 2 * tile + q_bytes + keff * Hkv * 8 + part(s_sparse),
+        "sparse_combine": part(s_sparse) + out,
+        "dense_attn": blocks * Hkv * 2 * tile + q_bytes + blocks * Hkv * 4 + part(s_dense),
+        "dense_combine": part(s_dense) + out,
+    }
+
+
+# ---------------------------------------------------------------- HBM traffic from counters
+
+def source_digest() -> str:
+    with open(ATTN_SOURCE, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def measured_traffic():
+    """Counter-derived HBM bytes per dense-attention launch, if the committed
+    profile was taken on the current kernel source (else None)."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            text = f.read()
+    except OSError:
+        return None
+    m_sha = re.search(r"kernel_source_sha256_16:\s*([0-9a-f]+)", text)
+    m_b = re.search(r"hbm_bytes_per_launch:\s*([0-9.eE+]+)", text)
+    if not (m_sha and m_b) or m_sha.group(1) != source_digest():
+        return None
+    return float(m_b.group(1))
+
+
+# ---------------------------------------------------------------- GPU part
+
+def run_gpu(args, spec, data):
+    import torch
+    from kv_cache_decode_amd.step import DeviceWorkload
+
+    dev = torch.device("cuda:0")
+    k = spec.topk_blocks
+    copies = [DeviceWorkload(data, device=dev) for _ in range(args.copies)]
+    for c in copies:                       # the index exists before decoding starts
+        c.meta_build()
+    torch.cuda.synchronize()
+    from kv_cache_decode_amd import kvdecode as kd
+    s_sparse = kd.kv_auto_num_splits(copies[0].shape, k)
+    s_dense = kd.kv_auto_num_splits(copies[0].shape, spec.max_blocks)
+    stages = ["meta_build", "score_topk", "sparse_attn", "sparse_combine", "dense_attn",
+              "dense_combine"]
+
+    def step(c, ev=None):
+        if ev is not None:
+            ev[0].record()
+        c.meta_build()
+        if ev is not None:
+            ev[1].record()
+        c.score_topk(k)
+        if ev is not None:
+            ev[2].record()
+        c.attention(sparse=True, num_splits=s_sparse)
+        if ev is not None:
+            ev[3].record()
+        c.combine(s_sparse)
+        if ev is not None:
+            ev[4].record()
+        c.attention(sparse=False, num_splits=s_dense)
+        if ev is not None:
+            ev[5].record()
+        c.combine(s_dense)
+        if ev is not None:
+            ev[6].record()
+
+    for i in range(args.warmup):
+        step(copies[i % len(copies)])
+    torch.cuda.synchronize()
+
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(7)] for _ in range(args.steps)]
+    t_start, t_end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    t_start.record()
+    for i in range(args.steps):
+        step(copies[i % len(copies)], evs[i])
+    t_end.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    total_ms = t_start.elapsed_time(t_end)
+    per_stage_ms = {s: float(np.mean([e[i].elapsed_time(e[i + 1]) for e in evs]))
+                    for i, s in enumerate(stages)}
+    for c in copies:
+        c.close()
+    del copies
+    torch.cuda.empty_cache()
+    return {
+        "total_ms": total_ms, "wall_s": wall, "stage_ms": per_stage_ms,
+        "s_sparse": s_sparse, "s_dense": s_dense,
+    }
+
+
+def run_zero_copy(args):
+    """Sparse decode with K/V read directly from mapped pinned host memory."""
+    import torch
+    from kv_cache_decode_amd import workload as wl
+    from kv_cache_decode_amd.step import DeviceWorkload
+
+    spec = wl.WORKLOADS[HOSTKV_WORKLOAD]
+    data = wl.generate(spec)
+    dev = torch.device("cuda:0")
+    dw = DeviceWorkload(data, device=dev, host_kv=True)
+    dw.meta_build()                  # the index (kmeta) is built once and lives in HBM
+    k = spec.topk_blocks
+    dw.score_topk(k)
+    S = dw.auto_splits(sparse=True)
+    for _ in range(3):
+        dw.decode(sparse=True, num_splits=S)
+    torch.cuda.synchronize()
+    reps = args.zc_reps
+    e = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+    attn_ms, comb_ms = [], []
+    for _ in range(reps):
+        e[0].record()
+        dw.attention(sparse=True, num_splits=S)
+        e[1].record()
+        dw.combine(S)
+        e[2].record()
+        torch.cuda.synchronize()
+        attn_ms.append(e[0].elapsed_time(e[1]))
+        comb_ms.append(e[1].elapsed_time(e[2]))
+    # dense over the host link once, for scale
+    e[0].record()
+    S_d = dw.attention(sparse=False)
+    e[1].record()
+    torch.cuda.synchronize()
+    dense_ms = e[0].elapsed_time(e[1])
+    dw.close()
+
+    # measured host-to-device copy bandwidth: 256 MiB from pinned memory, best of 10
+    n = 256 << 20
+    src = torch.empty(n, dtype=torch.uint8, pin_memory=True)
+    src.fill_(1)
+    dst = torch.empty(n, dtype=torch.uint8, device=dev)
+    best = float("inf")
+    for _ in range(10):
+        e[0].record()
+        dst.copy_(src, non_blocking=True)
+        e[1].record()
+        torch.cuda.synchronize()
+        best = min(best, e[0].elapsed_time(e[1]))
+    h2d_gbps = n / (best * 1e-3) / 1e9
+
+    eb = spec.elem_bytes
+    keff = sum(min(k, spec.blocks(b)) for b in range(spec.num_seqs))
+    link_bytes = keff * spec.num_kv_heads * 2 * spec.block_size * spec.head_dim * eb
+    dense_link_bytes = spec.used_pages * spec.num_kv_heads * 2 * spec.block_size * spec.head_dim * eb
+    attn = float(np.median(attn_ms))
+    host_gbps = link_bytes / (attn * 1e-3) / 1e9
+    return {
+        "workload": HOSTKV_WORKLOAD,
+        "sparse_attn_us": attn * 1e3,
+        "sparse_combine_us": float(np.median(comb_ms)) * 1e3,
+        "host_link_bytes": link_bytes,
+        "host_link_gbps": host_gbps,
+        "dense_attn_us": dense_ms * 1e3,
+        "dense_host_link_gbps": dense_link_bytes / (dense_ms * 1e-3) / 1e9,
+        "h2d_memcpy_gbps": h2d_gbps,
+        "frac_of_h2d": host_gbps / h2d_gbps,
+        "splits": S,
+    }
+
+
+# ---------------------------------------------------------------- CPU baseline (oracle)
+
+def run_cpu_baseline(spec, data, step_bytes: int, reps: int):
+    import oracle
+
+    q, kp, vp = data.q64(), data.k64(), data.v64()
+    bt, sl = data.block_table, data.seq_lens
+    bs, k = spec.block_size, spec.topk_blocks
+    ids, val = [], []
+    for b in range(spec.num_seqs):
+        for n in range(spec.blocks(b)):
+            ids.append(int(bt[b, n]))
+            val.append(min(bs, spec.seq_lens[b] - n * bs))
+    ids, val = np.array(ids, np.int32), np.array(val, np.int32)
+    scale = 1.0 / np.sqrt(spec.head_dim)
+    times = []
+    for _ in range(reps):
+        t0 = time.perf_counter()
+        km = oracle.block_meta(kp, ids, val)
+        hs = oracle.head_scores(q, km, bt, sl, bs)
+        gs = oracle.group_scores(hs, spec.num_kv_heads)
+        sel, cnt = oracle.topk(gs, sl, bs, k)
+        oracle.attention(q, kp, vp, bt, sl, scale, sel, cnt)
+        oracle.attention(q, kp, vp, bt, sl, scale)
+        times.append(time.perf_counter() - t0)
+    t = float(np.median(times))
+    return {
+        "value": step_bytes / t / 1e9,
+        "unit": "GB/s",
+        "cores": oracle.num_threads(),
+        "kind": "oracle",
+        "sample": f"{reps} full steps of {spec.name} (meta build, scores, Top-K, sparse and "
+                  f"dense attention) in fp64; median step {t:.2f} s",
+        "step_s": t,
+        "steps_per_s": 1.0 / t,
+    }
+
+
+# ---------------------------------------------------------------- main
+
+def copy_calibration():
+    import torch
+    n = 1 << 30
+    a = torch.empty(n, dtype=torch.uint8, device="cuda:0")
+    b = torch.empty_like(a)
+    a.fill_(3)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes_read": n, "copy_bytes_written": n}), flush=True)
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--copies", type=int, default=4)
+    ap.add_argument("--zc-reps", type=int, default=5)
+    ap.add_argument("--cpu-reps", type=int, default=3)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-zero-copy", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}, WORLD_SIZE "
+              f"{world}); this build has no multi-GPU path.", file=sys.stderr)
+        sys.exit(2)
+    if args.copy_calibration:
+        copy_calibration()
+        return
+
+    import torch
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    from kv_cache_decode_amd import workload as wl
+
+    spec = wl.WORKLOADS[WORKLOAD]
+    log(f"[bench] generating {spec.name}")
+    data = wl.generate(spec)
+    log("[bench] timing GPU steps")
+    g = run_gpu(args, spec, data)
+    sb = stage_bytes(spec, spec.topk_blocks, g["s_sparse"], g["s_dense"])
+    step_bytes = int(sum(sb.values()))
+    ms = g["total_ms"] / args.steps
+    st = g["stage_ms"]
+    stage_us = {s: st[s] * 1e3 for s in st}
+    stage_gbps = {s: sb[s] / (st[s] * 1e-3) / 1e9 for s in st}
+    sparse_ms = st["score_topk"] + st["sparse_attn"] + st["sparse_combine"]
+    dense_ms = st["dense_attn"] + st["dense_combine"]
+    dense_gbps = stage_gbps["dense_attn"]
+    traffic = measured_traffic()
+
+    zc = None
+    if not args.no_zero_copy:
+        log("[bench] zero-copy host-KV variant")
+        zc = run_zero_copy(args)
+    cpu = None
+    if not args.no_cpu_baseline:
+        log("[bench] CPU baseline (oracle)")
+        cpu = run_cpu_baseline(spec, data, step_bytes, args.cpu_reps)
+
+    rec = {
+        "metric": "KV GB/s streamed by decode attention (% of HBM peak) + decode steps/sec",
+        "value": step_bytes / (ms * 1e-3) / 1e9,
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {
+            "workload": spec.name, "batch": spec.num_seqs, "context": spec.seq_lens[0],
+            "q_heads": spec.num_q_heads, "kv_heads": spec.num_kv_heads,
+            "head_dim": spec.head_dim, "block_size": spec.block_size,
+            "kv_storage": spec.dtype, "topk_blocks": spec.topk_blocks,
+            "splits_sparse": g["s_sparse"], "splits_dense": g["s_dense"],
+            "step": "meta_build(all pages) + score_topk + sparse attn + combine + dense attn + combine",
+        },
+        "frac_of_hbm_peak": step_bytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBPS,
+        "decode_steps_per_s": {"sparse": 1e3 / sparse_ms, "dense": 1e3 / dense_ms,
+                               "full_step": 1e3 / ms},
+        "step_bytes": step_bytes,
+        "stage_bytes": sb,
+        "stage_us": stage_us,
+        "stage_gbps": stage_gbps,
+        "roofline": {
+            "kernel": "paged_attn_kernel (dense)",
+            "bound": "hbm",
+            "achieved": dense_gbps,
+            "peak": HBM_PEAK_GBPS,
+            "unit": "GB/s",
+            "frac": dense_gbps / HBM_PEAK_GBPS,
+            "traffic": traffic,
+            "algorithmic_bytes_per_launch": sb["dense_attn"],
+            "avg_launch_us": stage_us["dense_attn"],
+        },
+        "zero_copy": zc,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(rec), flush=True)
+
+
+if __name__ == "__main__":
+    main()

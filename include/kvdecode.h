@@ -1,0 +1,186 @@
+/*
+ * kvdecode.h -- C ABI of the MI355X (gfx950) paged Top-K decode-attention library.
+ *
+ * One decode step of one layer over a block-paged KV cache:
+ *
+ *   kv_block_meta_build   channel-wise min/max key of every KV page (the block index)
+ *   kv_block_score_topk   Quest block score of every logical block, then Top-K blocks
+ *   kv_paged_decode_attn  split-K softmax decode attention, dense or over selected blocks
+ *   kv_decode_combine     log-sum-exp merge of the split partials
+ *
+ * The method is the select -> fetch -> compute decode step of the KVDrive paper
+ * (§2.3, §4): a GPU-resident index picks the critical KV blocks, only those are
+ * read, and attention runs over them.  The block index is Quest's (KVDrive
+ * §2.2): per block the channel-wise minimum and maximum of the keys, and a
+ * block score obtained by multiplying the query with them.  Dense decode (every
+ * step reads all previous KV, Dual-Blade page, background section) is the same
+ * attention call without a selection.  A KV pool may live in mapped pinned host
+ * memory that the kernels read directly (the zero-copy KV manager of the
+ * DirectKV review page, core method 4), so only the pages a call touches cross
+ * the host link.
+ *
+ * Conventions shared by every call
+ * --------------------------------
+ * - Pointers are device addresses (or device-mapped host addresses from
+ *   kv_host_alloc) unless stated otherwise; the caller owns every buffer.  No
+ *   call allocates device memory; scratch comes in as a caller workspace.
+ * - Every call is asynchronous and stream-ordered on `stream` (a hipStream_t;
+ *   NULL = the default stream).  Nothing synchronises.
+ * - Host-side validation runs before any launch and returns a status; the
+ *   device is not touched when a call returns an error.  kv_last_error_message()
+ *   gives the reason (thread-local).
+ * - Device-side integer data (page ids, block tables, sequence lengths,
+ *   selections) is trusted: it must satisfy the ranges stated below.
+ * - Head mapping: query head h reads KV head h / G, G = num_q_heads / num_kv_heads.
+ * - Layouts (row-major, innermost last):
+ *     q        [B, Hq, D]            dtype
+ *     K, V     [P, Hkv, bs, D]       dtype   (page p, KV head j, slot s, channel c)
+ *     kmeta    [P, Hkv, 2, D]        dtype   (index 0 = channel min, 1 = channel max)
+ *     block_table int32 [B, maxN]    logical block n of sequence b -> page
+ *     seq_lens    int32 [B]          L_b >= 1 tokens, current token included,
+ *                                    N_b = ceil(L_b / bs) <= maxN
+ *     scores   fp32 [B, Hkv, maxN]   (-inf for n >= N_b)
+ *     sel      int32 [B, Hkv, sel_stride] ascending logical block ids, -1 padded
+ *     sel_count int32 [B, Hkv]
+ *     part_o   fp32 [B, Hq, S, D]    per-split normalised output
+ *     part_m, part_l fp32 [B, Hq, S] per-split max logit and sum of exp(logit - max)
+ *     out      fp32 [B, Hq, D];  lse fp32 [B, Hq]
+ * - Alignment: q, K, V and kmeta 16 bytes; part_o and out 16 bytes; the rest 4.
+ */
+#ifndef KVDECODE_H
+#define KVDECODE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  KV_OK = 0,
+  KV_ERR_INVALID_ARG = 1, /* null pointer, non-positive size, inconsistent shape */
+  KV_ERR_UNSUPPORTED = 2, /* valid but not built: head_dim, block_size, group size, dtype */
+  KV_ERR_ALIGNMENT = 3,   /* a pointer misses the alignment stated above */
+  KV_ERR_WORKSPACE = 4,   /* workspace missing or smaller than the size query returned */
+  KV_ERR_HIP = 5          /* the HIP runtime reported an error at launch */
+} kv_status;
+
+typedef enum { KV_F32 = 0, KV_F16 = 1, KV_BF16 = 2 } kv_dtype;
+
+/* kv_shape.flags */
+#define KV_FLAG_HOST_KV 0x1u /* K/V pools are device-mapped pinned host memory */
+
+/* kv_host_alloc flags */
+#define KV_HOST_COHERENT 0x0u    /* default mapped pinned memory */
+#define KV_HOST_NONCOHERENT 0x1u /* mapped pinned memory the GPU may cache */
+
+typedef struct {
+  int32_t num_seqs;           /* B >= 1 */
+  int32_t num_q_heads;        /* Hq, a multiple of Hkv */
+  int32_t num_kv_heads;       /* Hkv >= 1; G = Hq / Hkv in {1, 2, 4, 8} */
+  int32_t head_dim;           /* D in {64, 128} */
+  int32_t block_size;         /* bs: tokens per page, 16 */
+  int32_t max_blocks_per_seq; /* maxN >= 1: row length of block_table and scores */
+  int32_t num_pages;          /* P >= 1: pages in the K/V pools */
+  int32_t dtype;              /* kv_dtype of q, K, V and kmeta */
+  uint32_t flags;             /* KV_FLAG_* */
+} kv_shape;
+
+/*
+ * Block index build (KVDrive §2.2 and §2.3: a block is represented by the
+ * channel-wise min and max of its keys; KVDrive §4: built at prefill).
+ * For i < num_page_ids and every KV head j, writes
+ *   kmeta[p, j, 0, c] = min_{s < v} K[p, j, s, c],  kmeta[p, j, 1, c] = max_{s < v} K[p, j, s, c]
+ * with p = page_ids[i], v = page_valid_tokens[i] in [1, bs].  Exact (min and max
+ * of representable values), so results are bit-identical to any exact reference
+ * up to the sign of zero.  Pages not listed are not touched.  Page ids must be
+ * distinct and in [0, P).
+ */
+kv_status kv_block_meta_build(const kv_shape* shape, const void* k_cache, const int32_t* page_ids,
+                              const int32_t* page_valid_tokens, int32_t num_page_ids, void* kmeta,
+                              void* stream);
+
+/* Workspace bytes kv_block_score_topk needs when scores_out is NULL (0 otherwise). */
+size_t kv_score_topk_workspace_size(const kv_shape* shape, int32_t topk_blocks);
+
+/*
+ * Quest block scoring and Top-K selection (KVDrive §2.2).
+ * For every sequence b, query head h and logical block n < N_b:
+ *   sigma[b,h,n] = sum_c max(q[b,h,c] * kmin[p,j,c], q[b,h,c] * kmax[p,j,c]),
+ *   p = block_table[b,n], j = h / G   (fp32 accumulation; products are exact for
+ *   fp16/bf16 inputs),
+ * the group score S[b,j,n] = max over the G query heads of KV head j, and the
+ * selection: the K_eff = min(topk_blocks, N_b) blocks of largest S (ties: lower
+ * block index first), written ascending to sel_blocks[b, j, 0..K_eff) with -1
+ * after, and K_eff to sel_count[b, j].  sel_blocks has row stride topk_blocks.
+ * scores_out (nullable) receives S ([B, Hkv, maxN], -inf for n >= N_b); when it
+ * is NULL the scores go to `workspace`, which must hold
+ * kv_score_topk_workspace_size() bytes.  topk_blocks >= 1; maxN <= 32768.
+ */
+kv_status kv_block_score_topk(const kv_shape* shape, const void* q, const void* kmeta,
+                              const int32_t* block_table, const int32_t* seq_lens,
+                              int32_t topk_blocks, float* scores_out, int32_t* sel_blocks,
+                              int32_t* sel_count, void* workspace, size_t workspace_bytes,
+                              void* stream);
+
+/*
+ * Number of splits the library would pick for `blocks_per_unit` blocks per
+ * (sequence, KV head) (maxN for dense calls, the selection length for sparse
+ * ones): enough waves to fill the GPU, at least 8 blocks per split.  Always >= 1.
+ */
+int32_t kv_auto_num_splits(const kv_shape* shape, int32_t blocks_per_unit);
+
+/*
+ * Split-K decode attention (Dual-Blade background: a decode step attends over
+ * all previous KV; KVDrive §2.3 step 3: sparse attention over the selected
+ * blocks; DirectKV review, core method 2/3: the query and the running output
+ * stay in registers and each KV tile is read once, with a streaming softmax).
+ * For query head h of sequence b, the block list is 0..N_b-1 when sel_blocks is
+ * NULL, else sel_blocks[b, h/G, 0..sel_count[b, h/G]) (ascending, distinct,
+ * < N_b; row stride sel_stride).  Split s covers list positions
+ * [s*c, min((s+1)*c, n)) with c = ceil(n / num_splits); over its tokens t < L_b:
+ *   z_t = scale * (q . k_t),  m = max z_t,  l = sum exp(z_t - m),
+ *   part_o = sum exp(z_t - m) v_t / l,  part_m = m,  part_l = l
+ * (fp32 accumulation).  An empty split writes m = -inf, l = 0, o = 0.
+ * num_splits >= 1 (see kv_auto_num_splits).  With KV_FLAG_HOST_KV the K/V
+ * pointers may be device pointers of kv_host_alloc memory.
+ */
+kv_status kv_paged_decode_attn(const kv_shape* shape, const void* q, const void* k_cache,
+                               const void* v_cache, const int32_t* block_table,
+                               const int32_t* seq_lens, const int32_t* sel_blocks,
+                               const int32_t* sel_count, int32_t sel_stride, float scale,
+                               int32_t num_splits, float* part_o, float* part_m, float* part_l,
+                               void* stream);
+
+/*
+ * Exact log-sum-exp merge of split partials (the streaming-softmax rescale of
+ * the DirectKV review, core method 3, applied across splits):
+ *   M = max_s m_s,  w_s = l_s * exp(m_s - M) (0 for an empty split),
+ *   out = sum_s w_s o_s / sum_s w_s,  lse = M + ln(sum_s w_s).
+ * lse_out is nullable.  Every row needs at least one non-empty split.
+ */
+kv_status kv_decode_combine(const kv_shape* shape, int32_t num_splits, const float* part_o,
+                            const float* part_m, const float* part_l, float* out, float* lse_out,
+                            void* stream);
+
+/*
+ * Pinned, device-mapped host memory for a zero-copy K/V pool (DirectKV review,
+ * core method 4: KV kept in pinned host memory behind a device-visible pointer).
+ * *host_ptr is the CPU address, *dev_ptr the address to pass to the kernels.
+ * flags: KV_HOST_COHERENT or KV_HOST_NONCOHERENT.  Free with kv_host_free.
+ */
+kv_status kv_host_alloc(size_t bytes, uint32_t flags, void** host_ptr, void** dev_ptr);
+kv_status kv_host_free(void* host_ptr);
+
+/* Static description of a status code. */
+const char* kv_status_string(kv_status status);
+
+/* Message of the last failing call on this thread ("" if none). */
+const char* kv_last_error_message(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* KVDECODE_H */

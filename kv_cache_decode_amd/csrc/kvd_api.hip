@@ -1,0 +1,248 @@
+// C ABI of the paged Top-K decode library: host-side validation, then one
+// launcher call per entry point.  Every check runs before any device work, so
+// an error status means the device was not touched.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cstdarg>
+#include <cstdio>
+#include <string>
+
+#include "../../include/kvdecode.h"
+#include "kvd_launch.hpp"
+
+namespace kvd {
+int device_cu_count();
+}
+
+namespace {
+
+thread_local std::string g_last_error;
+
+kv_status fail(kv_status st, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return st;
+}
+
+kv_status ok() {
+  g_last_error.clear();
+  return KV_OK;
+}
+
+kv_status hip_status(hipError_t e, const char* where) {
+  if (e == hipSuccess) return ok();
+  return fail(KV_ERR_HIP, "%s: %s", where, hipGetErrorString(e));
+}
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+size_t dtype_bytes(int dt) { return dt == KV_F32 ? 4 : 2; }
+
+// Checks shared by every call that takes a shape.
+kv_status check_shape(const kv_shape* s) {
+  if (!s) return fail(KV_ERR_INVALID_ARG, "shape is NULL");
+  if (s->num_seqs < 1 || s->num_seqs > 65535)
+    return fail(KV_ERR_INVALID_ARG, "num_seqs=%d must be in [1, 65535]", s->num_seqs);
+  if (s->num_kv_heads < 1 || s->num_kv_heads > 65535)
+    return fail(KV_ERR_INVALID_ARG, "num_kv_heads=%d must be in [1, 65535]", s->num_kv_heads);
+  if (s->num_q_heads < 1 || s->num_q_heads % s->num_kv_heads != 0)
+    return fail(KV_ERR_INVALID_ARG, "num_q_heads=%d must be a positive multiple of num_kv_heads=%d",
+                s->num_q_heads, s->num_kv_heads);
+  const int G = s->num_q_heads / s->num_kv_heads;
+  if (G != 1 && G != 2 && G != 4 && G != 8)
+    return fail(KV_ERR_UNSUPPORTED, "group size %d not built (1, 2, 4, 8)", G);
+  if (s->head_dim != 64 && s->head_dim != 128)
+    return fail(KV_ERR_UNSUPPORTED, "head_dim=%d not built (64, 128)", s->head_dim);
+  if (s->block_size != 16)
+    return fail(KV_ERR_UNSUPPORTED, "block_size=%d not built (16)", s->block_size);
+  if (s->max_blocks_per_seq < 1)
+    return fail(KV_ERR_INVALID_ARG, "max_blocks_per_seq=%d must be >= 1", s->max_blocks_per_seq);
+  if (s->num_pages < 1) return fail(KV_ERR_INVALID_ARG, "num_pages=%d must be >= 1", s->num_pages);
+  if (s->dtype != KV_F32 && s->dtype != KV_F16 && s->dtype != KV_BF16)
+    return fail(KV_ERR_UNSUPPORTED, "dtype=%d unknown", s->dtype);
+  if (s->flags & ~KV_FLAG_HOST_KV) return fail(KV_ERR_INVALID_ARG, "unknown flags 0x%x", s->flags);
+  return KV_OK;
+}
+
+size_t scores_bytes(const kv_shape* s) {
+  return (size_t)s->num_seqs * s->num_kv_heads * s->max_blocks_per_seq * sizeof(float);
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* kv_status_string(kv_status st) {
+  switch (st) {
+    case KV_OK: return "KV_OK";
+    case KV_ERR_INVALID_ARG: return "KV_ERR_INVALID_ARG";
+    case KV_ERR_UNSUPPORTED: return "KV_ERR_UNSUPPORTED";
+    case KV_ERR_ALIGNMENT: return "KV_ERR_ALIGNMENT";
+    case KV_ERR_WORKSPACE: return "KV_ERR_WORKSPACE";
+    case KV_ERR_HIP: return "KV_ERR_HIP";
+  }
+  return "unknown kv_status";
+}
+
+const char* kv_last_error_message(void) { return g_last_error.c_str(); }
+
+kv_status kv_block_meta_build(const kv_shape* shape, const void* k_cache, const int32_t* page_ids,
+                              const int32_t* page_valid_tokens, int32_t num_page_ids, void* kmeta,
+                              void* stream) {
+  kv_status st = check_shape(shape);
+  if (st != KV_OK) return st;
+  if (num_page_ids < 0) return fail(KV_ERR_INVALID_ARG, "num_page_ids=%d < 0", num_page_ids);
+  if (num_page_ids == 0) return ok();
+  if (!k_cache || !page_ids || !page_valid_tokens || !kmeta)
+    return fail(KV_ERR_INVALID_ARG, "k_cache, page_ids, page_valid_tokens and kmeta are required");
+  if ((long)num_page_ids * shape->num_kv_heads > 0x7fffffffL)
+    return fail(KV_ERR_INVALID_ARG, "num_page_ids * num_kv_heads overflows int32");
+  if (!aligned(k_cache, 16) || !aligned(kmeta, 16))
+    return fail(KV_ERR_ALIGNMENT, "k_cache and kmeta must be 16-byte aligned");
+  if (!aligned(page_ids, 4) || !aligned(page_valid_tokens, 4))
+    return fail(KV_ERR_ALIGNMENT, "page_ids and page_valid_tokens must be 4-byte aligned");
+  return hip_status(kvd::launch_block_meta(shape->dtype, shape->head_dim, k_cache, page_ids,
+                                           page_valid_tokens, num_page_ids, shape->num_kv_heads,
+                                           kmeta, (hipStream_t)stream),
+                    "kv_block_meta_build launch");
+}
+
+size_t kv_score_topk_workspace_size(const kv_shape* shape, int32_t topk_blocks) {
+  (void)topk_blocks;
+  if (check_shape(shape) != KV_OK) return 0;
+  return (scores_bytes(shape) + 255) & ~(size_t)255;
+}
+
+kv_status kv_block_score_topk(const kv_shape* shape, const void* q, const void* kmeta,
+                              const int32_t* block_table, const int32_t* seq_lens,
+                              int32_t topk_blocks, float* scores_out, int32_t* sel_blocks,
+                              int32_t* sel_count, void* workspace, size_t workspace_bytes,
+                              void* stream) {
+  kv_status st = check_shape(shape);
+  if (st != KV_OK) return st;
+  if (topk_blocks < 1) return fail(KV_ERR_INVALID_ARG, "topk_blocks=%d must be >= 1", topk_blocks);
+  if (shape->max_blocks_per_seq > kvd::kTopkMaxBlocks)
+    return fail(KV_ERR_UNSUPPORTED, "max_blocks_per_seq=%d above the Top-K limit %d",
+                shape->max_blocks_per_seq, kvd::kTopkMaxBlocks);
+  if (!q || !kmeta || !block_table || !seq_lens || !sel_blocks || !sel_count)
+    return fail(KV_ERR_INVALID_ARG, "q, kmeta, block_table, seq_lens, sel_blocks, sel_count are required");
+  if (!aligned(q, 16) || !aligned(kmeta, 16))
+    return fail(KV_ERR_ALIGNMENT, "q and kmeta must be 16-byte aligned");
+  if (!aligned(block_table, 4) || !aligned(seq_lens, 4) || !aligned(sel_blocks, 4) ||
+      !aligned(sel_count, 4) || (scores_out && !aligned(scores_out, 4)))
+    return fail(KV_ERR_ALIGNMENT, "integer and score arrays must be 4-byte aligned");
+  float* scores = scores_out;
+  if (!scores) {
+    const size_t need = kv_score_topk_workspace_size(shape, topk_blocks);
+    if (!workspace || workspace_bytes < need)
+      return fail(KV_ERR_WORKSPACE, "workspace of %zu bytes needed (got %zu)", need,
+                  workspace ? workspace_bytes : (size_t)0);
+    if (!aligned(workspace, 4)) return fail(KV_ERR_ALIGNMENT, "workspace must be 4-byte aligned");
+    scores = static_cast<float*>(workspace);
+  }
+  const int G = shape->num_q_heads / shape->num_kv_heads;
+  hipStream_t s = (hipStream_t)stream;
+  hipError_t e = kvd::launch_block_score(shape->dtype, shape->head_dim, G, q, kmeta, block_table,
+                                         seq_lens, shape->num_seqs, shape->num_q_heads,
+                                         shape->num_kv_heads, shape->max_blocks_per_seq, scores, s);
+  if (e != hipSuccess) return hip_status(e, "kv_block_score_topk score launch");
+  return hip_status(kvd::launch_topk(scores, seq_lens, shape->num_seqs, shape->num_kv_heads,
+                                     shape->max_blocks_per_seq, topk_blocks, sel_blocks, sel_count,
+                                     s),
+                    "kv_block_score_topk top-k launch");
+}
+
+int32_t kv_auto_num_splits(const kv_shape* shape, int32_t blocks_per_unit) {
+  if (check_shape(shape) != KV_OK || blocks_per_unit < 1) return 1;
+  const long units = (long)shape->num_seqs * shape->num_kv_heads;
+  // about 8 waves per compute unit in flight, each over >= 8 pages
+  const long target_waves = (long)kvd::device_cu_count() * 8;
+  long s = (target_waves + units - 1) / units;
+  s = std::min<long>(s, (blocks_per_unit + 7) / 8);
+  return (int32_t)std::max<long>(1, std::min<long>(s, 65535L * 4));
+}
+
+kv_status kv_paged_decode_attn(const kv_shape* shape, const void* q, const void* k_cache,
+                               const void* v_cache, const int32_t* block_table,
+                               const int32_t* seq_lens, const int32_t* sel_blocks,
+                               const int32_t* sel_count, int32_t sel_stride, float scale,
+                               int32_t num_splits, float* part_o, float* part_m, float* part_l,
+                               void* stream) {
+  kv_status st = check_shape(shape);
+  if (st != KV_OK) return st;
+  if (num_splits < 1 || num_splits > 65535 * 4)
+    return fail(KV_ERR_INVALID_ARG, "num_splits=%d must be in [1, 262140]", num_splits);
+  if (!q || !k_cache || !v_cache || !block_table || !seq_lens || !part_o || !part_m || !part_l)
+    return fail(KV_ERR_INVALID_ARG, "q, k_cache, v_cache, block_table, seq_lens and partials are required");
+  if ((sel_blocks == nullptr) != (sel_count == nullptr))
+    return fail(KV_ERR_INVALID_ARG, "sel_blocks and sel_count go together");
+  if (sel_blocks && sel_stride < 1)
+    return fail(KV_ERR_INVALID_ARG, "sel_stride=%d must be >= 1", sel_stride);
+  if (!(scale > 0.0f) || !(scale < INFINITY))
+    return fail(KV_ERR_INVALID_ARG, "scale must be finite and positive");
+  if (!aligned(q, 16) || !aligned(k_cache, 16) || !aligned(v_cache, 16) || !aligned(part_o, 16))
+    return fail(KV_ERR_ALIGNMENT, "q, k_cache, v_cache and part_o must be 16-byte aligned");
+  if (!aligned(block_table, 4) || !aligned(seq_lens, 4) || !aligned(part_m, 4) ||
+      !aligned(part_l, 4) || (sel_blocks && (!aligned(sel_blocks, 4) || !aligned(sel_count, 4))))
+    return fail(KV_ERR_ALIGNMENT, "integer and partial arrays must be 4-byte aligned");
+  const int G = shape->num_q_heads / shape->num_kv_heads;
+  return hip_status(
+      kvd::launch_paged_attn(shape->dtype, shape->head_dim, G, q, k_cache, v_cache, block_table,
+                             seq_lens, sel_blocks, sel_count, sel_stride, shape->num_seqs,
+                             shape->num_q_heads, shape->num_kv_heads, shape->max_blocks_per_seq,
+                             num_splits, scale, part_o, part_m, part_l, (hipStream_t)stream),
+      "kv_paged_decode_attn launch");
+}
+
+kv_status kv_decode_combine(const kv_shape* shape, int32_t num_splits, const float* part_o,
+                            const float* part_m, const float* part_l, float* out, float* lse_out,
+                            void* stream) {
+  kv_status st = check_shape(shape);
+  if (st != KV_OK) return st;
+  if (num_splits < 1) return fail(KV_ERR_INVALID_ARG, "num_splits=%d must be >= 1", num_splits);
+  if (!part_o || !part_m || !part_l || !out)
+    return fail(KV_ERR_INVALID_ARG, "partials and out are required");
+  if (!aligned(part_o, 16) || !aligned(out, 16))
+    return fail(KV_ERR_ALIGNMENT, "part_o and out must be 16-byte aligned");
+  if (!aligned(part_m, 4) || !aligned(part_l, 4) || (lse_out && !aligned(lse_out, 4)))
+    return fail(KV_ERR_ALIGNMENT, "part_m, part_l and lse must be 4-byte aligned");
+  const long rows = (long)shape->num_seqs * shape->num_q_heads;
+  if (rows > 0x7fffffffL) return fail(KV_ERR_INVALID_ARG, "too many rows");
+  return hip_status(kvd::launch_combine(shape->head_dim, part_o, part_m, part_l, (int)rows,
+                                        num_splits, out, lse_out, (hipStream_t)stream),
+                    "kv_decode_combine launch");
+}
+
+kv_status kv_host_alloc(size_t bytes, uint32_t flags, void** host_ptr, void** dev_ptr) {
+  if (!host_ptr || !dev_ptr) return fail(KV_ERR_INVALID_ARG, "host_ptr and dev_ptr are required");
+  *host_ptr = nullptr;
+  *dev_ptr = nullptr;
+  if (bytes == 0) return fail(KV_ERR_INVALID_ARG, "bytes must be > 0");
+  if (flags & ~KV_HOST_NONCOHERENT) return fail(KV_ERR_INVALID_ARG, "unknown flags 0x%x", flags);
+  unsigned hf = hipHostMallocMapped;
+  hf |= (flags & KV_HOST_NONCOHERENT) ? hipHostMallocNonCoherent : hipHostMallocCoherent;
+  void* h = nullptr;
+  hipError_t e = hipHostMalloc(&h, bytes, hf);
+  if (e != hipSuccess) return hip_status(e, "kv_host_alloc hipHostMalloc");
+  void* d = nullptr;
+  e = hipHostGetDevicePointer(&d, h, 0);
+  if (e != hipSuccess) {
+    (void)hipHostFree(h);
+    return hip_status(e, "kv_host_alloc hipHostGetDevicePointer");
+  }
+  *host_ptr = h;
+  *dev_ptr = d;
+  return ok();
+}
+
+kv_status kv_host_free(void* host_ptr) {
+  if (!host_ptr) return ok();
+  return hip_status(hipHostFree(host_ptr), "kv_host_free");
+}
+
+}  // extern "C"

@@ -1,0 +1,151 @@
+// Device helpers shared by the gfx950 kernels: storage-dtype traits (16-byte
+// chunk loads and exact widening to fp32) and wave64 cross-lane reductions
+// built from DPP row operations.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace kvd {
+
+constexpr int kWave = 64;
+constexpr int kBlockSize = 16;  // tokens per KV page
+
+// ---------------------------------------------------------------- dtypes
+//
+// Every kernel moves K/V/meta in 16-byte chunks (global_load_dwordx4), so a
+// chunk holds E = 16 / sizeof(element) channels.
+
+struct F32 {
+  using storage = float;
+  static constexpr int E = 4;
+  __device__ static inline void widen(const uint4& w, float* f) {
+    f[0] = __uint_as_float(w.x);
+    f[1] = __uint_as_float(w.y);
+    f[2] = __uint_as_float(w.z);
+    f[3] = __uint_as_float(w.w);
+  }
+  __device__ static inline uint4 narrow_exact(const float* f) {
+    return make_uint4(__float_as_uint(f[0]), __float_as_uint(f[1]), __float_as_uint(f[2]),
+                      __float_as_uint(f[3]));
+  }
+};
+
+struct BF16 {
+  using storage = uint16_t;
+  static constexpr int E = 8;
+  __device__ static inline void widen2(uint32_t w, float& lo, float& hi) {
+    lo = __uint_as_float(w << 16);
+    hi = __uint_as_float(w & 0xffff0000u);
+  }
+  __device__ static inline void widen(const uint4& w, float* f) {
+    widen2(w.x, f[0], f[1]);
+    widen2(w.y, f[2], f[3]);
+    widen2(w.z, f[4], f[5]);
+    widen2(w.w, f[6], f[7]);
+  }
+  // Only for values that are exactly representable in bf16 (a min or max of
+  // bf16 inputs): the low 16 bits of the fp32 pattern are zero.
+  __device__ static inline uint32_t pack2(float lo, float hi) {
+    return (__float_as_uint(lo) >> 16) | (__float_as_uint(hi) & 0xffff0000u);
+  }
+  __device__ static inline uint4 narrow_exact(const float* f) {
+    return make_uint4(pack2(f[0], f[1]), pack2(f[2], f[3]), pack2(f[4], f[5]), pack2(f[6], f[7]));
+  }
+};
+
+struct F16 {
+  using storage = _Float16;
+  static constexpr int E = 8;
+  __device__ static inline void widen2(uint32_t w, float& lo, float& hi) {
+    _Float16 a = __builtin_bit_cast(_Float16, (uint16_t)(w & 0xffffu));
+    _Float16 b = __builtin_bit_cast(_Float16, (uint16_t)(w >> 16));
+    lo = (float)a;
+    hi = (float)b;
+  }
+  __device__ static inline void widen(const uint4& w, float* f) {
+    widen2(w.x, f[0], f[1]);
+    widen2(w.y, f[2], f[3]);
+    widen2(w.z, f[4], f[5]);
+    widen2(w.w, f[6], f[7]);
+  }
+  __device__ static inline uint32_t pack2(float lo, float hi) {
+    uint16_t a = __builtin_bit_cast(uint16_t, (_Float16)lo);
+    uint16_t b = __builtin_bit_cast(uint16_t, (_Float16)hi);
+    return (uint32_t)a | ((uint32_t)b << 16);
+  }
+  __device__ static inline uint4 narrow_exact(const float* f) {
+    return make_uint4(pack2(f[0], f[1]), pack2(f[2], f[3]), pack2(f[4], f[5]), pack2(f[6], f[7]));
+  }
+};
+
+__device__ inline uint4 load16(const void* p) { return *reinterpret_cast<const uint4*>(p); }
+__device__ inline void store16(void* p, const uint4& v) { *reinterpret_cast<uint4*>(p) = v; }
+
+// ---------------------------------------------------------------- lane shuffles
+//
+// DPP controls (gfx9 encoding): quad_perm, row_mirror (lane i <-> 15-i in a
+// 16-lane row), row_half_mirror (i <-> 7-i in each 8-lane half row).
+
+enum : int {
+  kDppXor1 = 0xB1,        // quad_perm [1,0,3,2]
+  kDppXor2 = 0x4E,        // quad_perm [2,3,0,1]
+  kDppHalfMirror = 0x141,
+  kDppMirror = 0x140,
+};
+
+template <int CTRL>
+__device__ inline float dpp(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
+}
+
+__device__ inline float xor16(float v) {
+  // ds_swizzle bit mode inside each 32-lane half: and 0x1F, or 0, xor 0x10.
+  return __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(v), 0x401F));
+}
+__device__ inline float xor32(float v) { return __shfl_xor(v, 32, kWave); }
+
+struct OpSum {
+  __device__ static inline float apply(float a, float b) { return a + b; }
+};
+struct OpMax {
+  __device__ static inline float apply(float a, float b) { return fmaxf(a, b); }
+};
+struct OpMin {
+  __device__ static inline float apply(float a, float b) { return fminf(a, b); }
+};
+
+// All-reduce over aligned groups of N lanes (N = 1..64, a power of two); every
+// lane of a group ends with the group's result.  Each step pairs a lane with a
+// lane of the other half of its current group, which is enough for sum, min
+// and max once the lower levels are uniform.
+template <int N, typename Op>
+__device__ inline float group_reduce(float v) {
+  if constexpr (N >= 2) v = Op::apply(v, dpp<kDppXor1>(v));
+  if constexpr (N >= 4) v = Op::apply(v, dpp<kDppXor2>(v));
+  if constexpr (N >= 8) v = Op::apply(v, dpp<kDppHalfMirror>(v));
+  if constexpr (N >= 16) v = Op::apply(v, dpp<kDppMirror>(v));
+  if constexpr (N >= 32) v = Op::apply(v, xor16(v));
+  if constexpr (N >= 64) v = Op::apply(v, xor32(v));
+  return v;
+}
+
+// Reduce across the row groups of a wave: lanes l and l ^ k for k = N .. 32,
+// i.e. over all lanes with the same position inside their N-lane group.  The
+// pairing is a true xor so values that differ inside a group stay apart.
+template <int N, typename Op>
+__device__ inline float cross_group_reduce(float v) {
+  static_assert(N >= 8 && N <= 64, "row groups are 8..64 lanes wide");
+  if constexpr (N <= 8) v = Op::apply(v, __shfl_xor(v, 8, kWave));
+  if constexpr (N <= 16) v = Op::apply(v, xor16(v));
+  if constexpr (N <= 32) v = Op::apply(v, xor32(v));
+  return v;
+}
+
+__device__ inline float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+__device__ inline int lane_id() { return __lane_id(); }
+
+__device__ inline int readlane(int v, int lane) { return __builtin_amdgcn_readlane(v, lane); }
+
+}  // namespace kvd

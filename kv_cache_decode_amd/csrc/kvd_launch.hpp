@@ -1,0 +1,35 @@
+// Internal launchers: one per kernel family, dispatching on (dtype, head_dim,
+// group size) to the template instances.  Shapes are validated by the C ABI
+// layer before these run; the launchers only size grids.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace kvd {
+
+hipError_t launch_block_meta(int dtype, int D, const void* k_cache, const int32_t* page_ids,
+                             const int32_t* valid_tokens, int n_ids, int Hkv, void* kmeta,
+                             hipStream_t stream);
+
+hipError_t launch_block_score(int dtype, int D, int G, const void* q, const void* kmeta,
+                              const int32_t* block_table, const int32_t* seq_lens, int B, int Hq,
+                              int Hkv, int maxN, float* scores, hipStream_t stream);
+
+hipError_t launch_topk(const float* scores, const int32_t* seq_lens, int B, int Hkv, int maxN,
+                       int K, int32_t* sel, int32_t* sel_count, hipStream_t stream);
+
+hipError_t launch_paged_attn(int dtype, int D, int G, const void* q, const void* k_cache,
+                             const void* v_cache, const int32_t* block_table,
+                             const int32_t* seq_lens, const int32_t* sel,
+                             const int32_t* sel_count, int sel_stride, int B, int Hq, int Hkv,
+                             int maxN, int S, float scale, float* part_o, float* part_m,
+                             float* part_l, hipStream_t stream);
+
+hipError_t launch_combine(int D, const float* part_o, const float* part_m, const float* part_l,
+                          int rows, int S, float* out, float* lse, hipStream_t stream);
+
+// Largest maxN the Top-K kernel keeps in registers (1024 threads x 32 keys).
+constexpr int kTopkMaxBlocks = 32768;
+
+}  // namespace kvd

@@ -1,0 +1,168 @@
+"""Thin Python binding of the C ABI in include/kvdecode.h (ctypes).
+
+Argument marshalling only: every function takes the same arguments as its C
+counterpart, with device buffers given as torch tensors (their data_ptr is
+passed) or as raw integer addresses, and raises :class:`KVError` when the
+library returns a status other than KV_OK.  All compute runs in
+``libkvdecode.so``; importing this module without the built library raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Union
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libkvdecode.so")
+
+KV_OK, KV_ERR_INVALID_ARG, KV_ERR_UNSUPPORTED, KV_ERR_ALIGNMENT, KV_ERR_WORKSPACE, KV_ERR_HIP = range(6)
+KV_F32, KV_F16, KV_BF16 = 0, 1, 2
+KV_FLAG_HOST_KV = 0x1
+KV_HOST_COHERENT, KV_HOST_NONCOHERENT = 0x0, 0x1
+DTYPE_CODES = {"f32": KV_F32, "f16": KV_F16, "bf16": KV_BF16}
+
+# every symbol the header declares
+EXPORTS = (
+    "kv_block_meta_build", "kv_score_topk_workspace_size", "kv_block_score_topk",
+    "kv_auto_num_splits", "kv_paged_decode_attn", "kv_decode_combine", "kv_host_alloc",
+    "kv_host_free", "kv_status_string", "kv_last_error_message",
+)
+
+
+class KVError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"{status_string(status)}: {message}")
+        self.status = status
+
+
+class KVShape(ctypes.Structure):
+    _fields_ = [
+        ("num_seqs", ctypes.c_int32),
+        ("num_q_heads", ctypes.c_int32),
+        ("num_kv_heads", ctypes.c_int32),
+        ("head_dim", ctypes.c_int32),
+        ("block_size", ctypes.c_int32),
+        ("max_blocks_per_seq", ctypes.c_int32),
+        ("num_pages", ctypes.c_int32),
+        ("dtype", ctypes.c_int32),
+        ("flags", ctypes.c_uint32),
+    ]
+
+
+def make_shape(num_seqs, num_q_heads, num_kv_heads, head_dim, max_blocks_per_seq, num_pages,
+               dtype, block_size=16, flags=0) -> KVShape:
+    code = DTYPE_CODES.get(dtype, dtype)
+    return KVShape(num_seqs, num_q_heads, num_kv_heads, head_dim, block_size, max_blocks_per_seq,
+                   num_pages, code, flags)
+
+
+def _load() -> ctypes.CDLL:
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is not built: run kv_cache_decode_amd/build.py "
+                          "(or __graft_entry__.build()) first")
+    lib = ctypes.CDLL(LIB_PATH)
+    P, I32, U32, SZ, F = ctypes.c_void_p, ctypes.c_int32, ctypes.c_uint32, ctypes.c_size_t, ctypes.c_float
+    S = ctypes.POINTER(KVShape)
+    sig = {
+        "kv_block_meta_build": (I32, [S, P, P, P, I32, P, P]),
+        "kv_score_topk_workspace_size": (SZ, [S, I32]),
+        "kv_block_score_topk": (I32, [S, P, P, P, P, I32, P, P, P, P, SZ, P]),
+        "kv_auto_num_splits": (I32, [S, I32]),
+        "kv_paged_decode_attn": (I32, [S, P, P, P, P, P, P, P, I32, F, I32, P, P, P, P]),
+        "kv_decode_combine": (I32, [S, I32, P, P, P, P, P, P]),
+        "kv_host_alloc": (I32, [SZ, U32, ctypes.POINTER(P), ctypes.POINTER(P)]),
+        "kv_host_free": (I32, [P]),
+        "kv_status_string": (ctypes.c_char_p, [I32]),
+        "kv_last_error_message": (ctypes.c_char_p, []),
+    }
+    for name, (res, args) in sig.items():
+        fn = getattr(lib, name)
+        fn.restype, fn.argtypes = res, args
+    return lib
+
+
+_lib = _load()
+
+
+def status_string(status: int) -> str:
+    return _lib.kv_status_string(status).decode()
+
+
+def last_error_message() -> str:
+    return _lib.kv_last_error_message().decode()
+
+
+def _check(status: int) -> None:
+    if status != KV_OK:
+        raise KVError(status, last_error_message())
+
+
+Buf = Union[None, int, "torch.Tensor"]  # noqa: F821
+
+
+def _p(x: Buf) -> Optional[int]:
+    if x is None:
+        return None
+    if isinstance(x, int):
+        return x
+    return x.data_ptr()
+
+
+def _stream(stream) -> Optional[int]:
+    if stream is None:
+        import torch
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+def kv_block_meta_build(shape: KVShape, k_cache: Buf, page_ids: Buf, page_valid_tokens: Buf,
+                        num_page_ids: int, kmeta: Buf, stream=None) -> None:
+    _check(_lib.kv_block_meta_build(ctypes.byref(shape), _p(k_cache), _p(page_ids),
+                                    _p(page_valid_tokens), num_page_ids, _p(kmeta),
+                                    _stream(stream)))
+
+
+def kv_score_topk_workspace_size(shape: KVShape, topk_blocks: int) -> int:
+    return int(_lib.kv_score_topk_workspace_size(ctypes.byref(shape), topk_blocks))
+
+
+def kv_block_score_topk(shape: KVShape, q: Buf, kmeta: Buf, block_table: Buf, seq_lens: Buf,
+                        topk_blocks: int, scores_out: Buf, sel_blocks: Buf, sel_count: Buf,
+                        workspace: Buf = None, workspace_bytes: int = 0, stream=None) -> None:
+    _check(_lib.kv_block_score_topk(ctypes.byref(shape), _p(q), _p(kmeta), _p(block_table),
+                                    _p(seq_lens), topk_blocks, _p(scores_out), _p(sel_blocks),
+                                    _p(sel_count), _p(workspace), workspace_bytes,
+                                    _stream(stream)))
+
+
+def kv_auto_num_splits(shape: KVShape, blocks_per_unit: int) -> int:
+    return int(_lib.kv_auto_num_splits(ctypes.byref(shape), blocks_per_unit))
+
+
+def kv_paged_decode_attn(shape: KVShape, q: Buf, k_cache: Buf, v_cache: Buf, block_table: Buf,
+                         seq_lens: Buf, sel_blocks: Buf, sel_count: Buf, sel_stride: int,
+                         scale: float, num_splits: int, part_o: Buf, part_m: Buf, part_l: Buf,
+                         stream=None) -> None:
+    _check(_lib.kv_paged_decode_attn(ctypes.byref(shape), _p(q), _p(k_cache), _p(v_cache),
+                                     _p(block_table), _p(seq_lens), _p(sel_blocks),
+                                     _p(sel_count), sel_stride, scale, num_splits, _p(part_o),
+                                     _p(part_m), _p(part_l), _stream(stream)))
+
+
+def kv_decode_combine(shape: KVShape, num_splits: int, part_o: Buf, part_m: Buf, part_l: Buf,
+                      out: Buf, lse_out: Buf = None, stream=None) -> None:
+    _check(_lib.kv_decode_combine(ctypes.byref(shape), num_splits, _p(part_o), _p(part_m),
+                                  _p(part_l), _p(out), _p(lse_out), _stream(stream)))
+
+
+def kv_host_alloc(nbytes: int, flags: int = KV_HOST_COHERENT):
+    """Returns (host_ptr, dev_ptr) as integers."""
+    h, d = ctypes.c_void_p(), ctypes.c_void_p()
+    _check(_lib.kv_host_alloc(nbytes, flags, ctypes.byref(h), ctypes.byref(d)))
+    return h.value, d.value
+
+
+def kv_host_free(host_ptr: int) -> None:
+    _check(_lib.kv_host_free(host_ptr))

@@ -1,0 +1,154 @@
+"""A decode step of one layer on the device, driven through the C ABI.
+
+:class:`DeviceWorkload` puts a generated workload in device memory (torch
+tensors; the K/V pools optionally in mapped pinned host memory from
+``kv_host_alloc``) and owns the output buffers.  Its methods call the C-ABI
+entry points in the order of the select -> fetch -> compute step (KVDrive §2.3
+and §4): block meta, score + Top-K, split-K attention, merge.  Nothing here
+computes; it only allocates and passes pointers.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+from typing import Optional
+
+import numpy as np
+import torch
+
+from . import kvdecode as kd
+from .workload import WorkloadData
+
+TORCH_DTYPES = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16}
+
+
+def storage_tensor(raw: np.ndarray, dtype: str) -> torch.Tensor:
+    """CPU torch tensor of the storage dtype sharing the bytes of ``raw``."""
+    if dtype == "bf16":
+        return torch.from_numpy(raw.view(np.int16)).view(torch.bfloat16)
+    return torch.from_numpy(raw)
+
+
+class HostBuffer:
+    """Pinned, device-mapped host memory holding a copy of a numpy array."""
+
+    def __init__(self, arr: np.ndarray, flags: int = kd.KV_HOST_COHERENT):
+        arr = np.ascontiguousarray(arr)
+        self.nbytes = arr.nbytes
+        self.host, self.dev = kd.kv_host_alloc(self.nbytes, flags)
+        ctypes.memmove(self.host, arr.ctypes.data, self.nbytes)
+
+    def free(self):
+        if self.host:
+            kd.kv_host_free(self.host)
+            self.host = self.dev = None
+
+    def __del__(self):  # pragma: no cover - best effort
+        try:
+            self.free()
+        except Exception:
+            pass
+
+
+class DeviceWorkload:
+    def __init__(self, data: WorkloadData, device="cuda:0", host_kv: Optional[bool] = None,
+                 host_flags: int = kd.KV_HOST_COHERENT):
+        spec = data.spec
+        self.data, self.spec = data, spec
+        self.device = torch.device(device)
+        self.host_kv = spec.host_kv if host_kv is None else host_kv
+        dt = spec.dtype
+        dev = self.device
+        self.q = storage_tensor(data.q_raw, dt).to(dev)
+        self.block_table = torch.from_numpy(data.block_table).to(dev)
+        self.seq_lens = torch.from_numpy(data.seq_lens).to(dev)
+        self._host = []
+        if self.host_kv:
+            hk, hv = HostBuffer(data.k_raw, host_flags), HostBuffer(data.v_raw, host_flags)
+            self._host = [hk, hv]
+            self.k_cache, self.v_cache = hk.dev, hv.dev
+        else:
+            self.k_cache = storage_tensor(data.k_raw, dt).to(dev)
+            self.v_cache = storage_tensor(data.v_raw, dt).to(dev)
+        P, Hkv, bs, D = data.k_raw.shape
+        self.kmeta = torch.zeros((P, Hkv, 2, D), dtype=TORCH_DTYPES[dt], device=dev)
+        ids, val = [], []
+        for b in range(spec.num_seqs):
+            for n in range(spec.blocks(b)):
+                ids.append(int(data.block_table[b, n]))
+                val.append(min(bs, spec.seq_lens[b] - n * bs))
+        self.page_ids = torch.tensor(ids, dtype=torch.int32, device=dev)
+        self.page_valid = torch.tensor(val, dtype=torch.int32, device=dev)
+        self.shape = kd.make_shape(spec.num_seqs, spec.num_q_heads, spec.num_kv_heads, D,
+                                   spec.max_blocks, P, dt, block_size=bs,
+                                   flags=kd.KV_FLAG_HOST_KV if self.host_kv else 0)
+        self.scale = 1.0 / math.sqrt(D)
+        B, Hq = spec.num_seqs, spec.num_q_heads
+        self.out = torch.empty((B, Hq, D), dtype=torch.float32, device=dev)
+        self.lse = torch.empty((B, Hq), dtype=torch.float32, device=dev)
+        self.scores = torch.empty((B, Hkv, spec.max_blocks), dtype=torch.float32, device=dev)
+        self._parts = {}
+        self.sel = self.sel_count = None
+        self.topk = None
+
+    # ------------------------------------------------------------ buffers
+    def partials(self, num_splits: int):
+        if num_splits not in self._parts:
+            B, Hq, D = self.spec.num_seqs, self.spec.num_q_heads, self.spec.head_dim
+            dev = self.device
+            self._parts[num_splits] = (
+                torch.empty((B, Hq, num_splits, D), dtype=torch.float32, device=dev),
+                torch.empty((B, Hq, num_splits), dtype=torch.float32, device=dev),
+                torch.empty((B, Hq, num_splits), dtype=torch.float32, device=dev),
+            )
+        return self._parts[num_splits]
+
+    def set_selection(self, sel: np.ndarray, sel_count: np.ndarray):
+        self.sel = torch.from_numpy(np.ascontiguousarray(sel, np.int32)).to(self.device)
+        self.sel_count = torch.from_numpy(np.ascontiguousarray(sel_count, np.int32)).to(self.device)
+        self.topk = int(sel.shape[-1])
+
+    def auto_splits(self, sparse: bool) -> int:
+        per_unit = self.topk if sparse else self.spec.max_blocks
+        return kd.kv_auto_num_splits(self.shape, per_unit)
+
+    # ------------------------------------------------------------ steps
+    def meta_build(self, stream=None):
+        kd.kv_block_meta_build(self.shape, self.k_cache, self.page_ids, self.page_valid,
+                               int(self.page_ids.numel()), self.kmeta, stream)
+
+    def score_topk(self, k: int, stream=None):
+        if self.topk != k or self.sel is None:
+            B, Hkv = self.spec.num_seqs, self.spec.num_kv_heads
+            self.sel = torch.empty((B, Hkv, k), dtype=torch.int32, device=self.device)
+            self.sel_count = torch.empty((B, Hkv), dtype=torch.int32, device=self.device)
+            self.topk = k
+        kd.kv_block_score_topk(self.shape, self.q, self.kmeta, self.block_table, self.seq_lens, k,
+                               self.scores, self.sel, self.sel_count, None, 0, stream)
+
+    def attention(self, sparse: bool, num_splits: Optional[int] = None, stream=None):
+        S = num_splits or self.auto_splits(sparse)
+        po, pm, pl = self.partials(S)
+        if sparse:
+            kd.kv_paged_decode_attn(self.shape, self.q, self.k_cache, self.v_cache,
+                                    self.block_table, self.seq_lens, self.sel, self.sel_count,
+                                    self.topk, self.scale, S, po, pm, pl, stream)
+        else:
+            kd.kv_paged_decode_attn(self.shape, self.q, self.k_cache, self.v_cache,
+                                    self.block_table, self.seq_lens, None, None, 0, self.scale, S,
+                                    po, pm, pl, stream)
+        return S
+
+    def combine(self, num_splits: int, stream=None):
+        po, pm, pl = self.partials(num_splits)
+        kd.kv_decode_combine(self.shape, num_splits, po, pm, pl, self.out, self.lse, stream)
+
+    def decode(self, sparse: bool, num_splits: Optional[int] = None, stream=None):
+        S = self.attention(sparse, num_splits, stream)
+        self.combine(S, stream)
+        return S
+
+    def close(self):
+        for h in self._host:
+            h.free()
+        self._host = []

@@ -1,0 +1,164 @@
+"""Comparison helpers for the GPU-vs-oracle parity tests.
+
+Tolerances:
+* attention outputs, per (sequence, head) row: ||o - ref||_2 / ||ref||_2 <= 1e-5
+  for fp32 inputs and 2e-3 for fp16/bf16 inputs (fp32 accumulation);
+* block meta: bit-exact (compared by value, so -0 == +0);
+* scores: |gpu - ref| <= 1e-6 * sum_c |max(q_c kmin_c, q_c kmax_c)| (an fp32 sum
+  of D terms is accurate relative to the sum of the terms' magnitudes, not to
+  the result, which can cancel; the bound is taken from the oracle's score of
+  |q| against |kmin|, |kmax|, which is >= that sum);
+* selection: the GPU set equals the oracle set, except for blocks whose oracle
+  score lies within 1e-6 * |S_K| of the K-th largest oracle score S_K; the GPU
+  list must also be a valid Top-K of the GPU's own scores (ascending, unique,
+  lower index first on equal scores).
+"""
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+import oracle
+from kv_cache_decode_amd import workload as wl
+
+ROW_TOL = {"f32": 1e-5, "f16": 2e-3, "bf16": 2e-3}
+SCORE_RTOL = 1e-6
+TIE_BAND = 1e-6
+
+
+def to_f64(t: torch.Tensor) -> np.ndarray:
+    return t.detach().to("cpu").to(torch.float64).numpy()
+
+
+def assert_rows_close(got: np.ndarray, ref: np.ndarray, tol: float, what: str = "out"):
+    got = got.reshape(-1, got.shape[-1])
+    ref = ref.reshape(-1, ref.shape[-1])
+    assert np.all(np.isfinite(got)), f"{what}: non-finite values"
+    err = np.linalg.norm(got - ref, axis=1)
+    nrm = np.linalg.norm(ref, axis=1)
+    rel = err / np.maximum(nrm, 1e-300)
+    worst = int(np.argmax(rel))
+    assert rel.max() <= tol, (f"{what}: row rel-err {rel.max():.3e} > {tol:.1e} at row {worst} "
+                              f"(max abs err {np.abs(got - ref).max():.3e})")
+    return float(rel.max())
+
+
+def page_lists(data: wl.WorkloadData):
+    spec = data.spec
+    ids, val = [], []
+    for b in range(spec.num_seqs):
+        for n in range(spec.blocks(b)):
+            ids.append(int(data.block_table[b, n]))
+            val.append(min(spec.block_size, spec.seq_lens[b] - n * spec.block_size))
+    return np.array(ids, np.int32), np.array(val, np.int32)
+
+
+class OracleRun:
+    """Lazily computed oracle results for one workload."""
+
+    def __init__(self, data: wl.WorkloadData):
+        self.data = data
+        self.spec = data.spec
+        self.scale = 1.0 / np.sqrt(self.spec.head_dim)
+        self._q = self._k = self._v = None
+        self._meta = None
+
+    @property
+    def q(self):
+        if self._q is None:
+            self._q = self.data.q64()
+        return self._q
+
+    @property
+    def k(self):
+        if self._k is None:
+            self._k = self.data.k64()
+        return self._k
+
+    @property
+    def v(self):
+        if self._v is None:
+            self._v = self.data.v64()
+        return self._v
+
+    def meta(self):
+        if self._meta is None:
+            ids, val = page_lists(self.data)
+            self._meta = oracle.block_meta(self.k, ids, val)
+        return self._meta
+
+    def scores(self):
+        hs = oracle.head_scores(self.q, self.meta(), self.data.block_table, self.data.seq_lens,
+                                self.spec.block_size)
+        return oracle.group_scores(hs, self.spec.num_kv_heads)
+
+    def score_bound(self):
+        """Per (b, KV head, block): an upper bound of sum_c |term_c| over the group's heads."""
+        hs = oracle.head_scores(np.abs(self.q), np.abs(self.meta()), self.data.block_table,
+                                self.data.seq_lens, self.spec.block_size)
+        return oracle.group_scores(hs, self.spec.num_kv_heads)
+
+    def topk(self, k: int, group_scores=None):
+        gs = self.scores() if group_scores is None else group_scores
+        return oracle.topk(gs, self.data.seq_lens, self.spec.block_size, k)
+
+    def attention(self, sel=None, cnt=None):
+        return oracle.attention(self.q, self.k, self.v, self.data.block_table, self.data.seq_lens,
+                                self.scale, sel, cnt)
+
+    def splits(self, S: int, sel=None, cnt=None):
+        return oracle.attention_splits(self.q, self.k, self.v, self.data.block_table,
+                                       self.data.seq_lens, self.scale, S, sel, cnt)
+
+
+def check_scores(gpu_scores: np.ndarray, ref: np.ndarray, nblocks: np.ndarray, bound: np.ndarray):
+    B, Hkv, maxN = ref.shape
+    for b in range(B):
+        nb = int(nblocks[b])
+        assert np.all(np.isneginf(gpu_scores[b, :, nb:])), "scores past N_b must be -inf"
+        r, g, m = ref[b, :, :nb], gpu_scores[b, :, :nb], bound[b, :, :nb]
+        bad = np.abs(g - r) > SCORE_RTOL * np.maximum(m, 1e-30)
+        assert not bad.any(), (f"score mismatch b={b}: max |err| / bound "
+                               f"{(np.abs(g - r) / np.maximum(m, 1e-30)).max():.3e}")
+
+
+def check_selection_valid(sel: np.ndarray, cnt: np.ndarray, scores: np.ndarray,
+                          nblocks: np.ndarray, k: int):
+    """The GPU list is a Top-K of the GPU's own scores with the lower-index tie rule."""
+    B, Hkv, _ = sel.shape
+    for b in range(B):
+        nb = int(nblocks[b])
+        keff = min(k, nb)
+        for j in range(Hkv):
+            c = int(cnt[b, j])
+            assert c == keff, f"sel_count {c} != K_eff {keff}"
+            s = sel[b, j, :c]
+            assert np.all(sel[b, j, c:] == -1), "padding must be -1"
+            assert np.all(np.diff(s) > 0) and s.min() >= 0 and s.max() < nb, "ascending, in range"
+            sc = scores[b, j, :nb].astype(np.float64)
+            order = sorted(range(nb), key=lambda i: (-sc[i], i))
+            assert sorted(order[:keff]) == s.tolist(), "not the Top-K of the GPU's own scores"
+
+
+def check_selection_vs_oracle(sel: np.ndarray, cnt: np.ndarray, ref_sel: np.ndarray,
+                              ref_cnt: np.ndarray, ref_scores: np.ndarray, nblocks: np.ndarray):
+    """Same set as the oracle except inside the tie band around the K-th score.
+    Returns the number of rows whose sets differ (inside the band)."""
+    B, Hkv, _ = sel.shape
+    differing = 0
+    for b in range(B):
+        nb = int(nblocks[b])
+        for j in range(Hkv):
+            assert cnt[b, j] == ref_cnt[b, j]
+            got = set(sel[b, j, :cnt[b, j]].tolist())
+            want = set(ref_sel[b, j, :ref_cnt[b, j]].tolist())
+            if got == want:
+                continue
+            differing += 1
+            sc = ref_scores[b, j, :nb]
+            kth = np.sort(sc)[::-1][ref_cnt[b, j] - 1]
+            for n in got ^ want:
+                assert abs(sc[n] - kth) <= TIE_BAND * abs(kth), (
+                    f"block {n} (b={b}, j={j}) differs outside the tie band: "
+                    f"score {sc[n]!r}, K-th {kth!r}")
+    return differing

@@ -1,0 +1,221 @@
+"""HIP path vs the fp64 oracle, element by element, through the C ABI (GPU)."""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from kv_cache_decode_amd import workload as wl
+from parity import (ROW_TOL, OracleRun, assert_rows_close, check_scores,
+                    check_selection_valid, check_selection_vs_oracle, to_f64)
+
+pytestmark = pytest.mark.gpu
+
+
+def run_device(data, **kw):
+    from kv_cache_decode_amd.step import DeviceWorkload
+    return DeviceWorkload(data, **kw)
+
+
+def mk(B, Hq, Hkv, D, lens, dtype, seed, **kw):
+    spec = wl.Workload(name=f"case{seed}", num_seqs=B, num_q_heads=Hq, num_kv_heads=Hkv,
+                       head_dim=D, seq_lens=tuple(lens), dtype=dtype, seed=seed, **kw)
+    return wl.generate(spec)
+
+
+def gpu_meta_f64(dw):
+    return to_f64(dw.kmeta)
+
+
+# ------------------------------------------------------------------ the grid
+
+GRID = []
+_seed = 1000
+for dtype in ("f32", "f16", "bf16"):
+    for D in (64, 128):
+        for G in (1, 2, 4, 8):
+            _seed += 1
+            GRID.append((dtype, D, G, _seed))
+
+
+@pytest.mark.parametrize("dtype,D,G,seed", GRID, ids=[f"{d}-D{D}-G{G}" for d, D, G, _ in GRID])
+def test_full_step_grid(gpu, dtype, D, G, seed):
+    """Meta, scores, Top-K, dense and sparse attention with splits, ragged lengths
+    (1, 15, 16, 17 and 543 tokens), a shuffled page table and unused pages."""
+    Hkv = 2
+    data = mk(5, Hkv * G, Hkv, D, (543, 1, 15, 16, 17), dtype, seed, extra_pages=3,
+              planted_frac=0.1)
+    o = OracleRun(data)
+    dw = run_device(data, device=gpu)
+    nb = data.num_blocks()
+    tol = ROW_TOL[dtype]
+
+    dw.meta_build()
+    ref_meta = o.meta()
+    got_meta = gpu_meta_f64(dw)
+    for b in range(5):
+        pages = data.block_table[b, :nb[b]]
+        np.testing.assert_array_equal(got_meta[pages], ref_meta[pages])
+    unused = np.setdiff1d(np.arange(data.spec.num_pages), data.block_table[:, :].ravel())
+    unused = [p for p in unused if p >= data.spec.used_pages]
+    assert len(unused) == 3 and np.all(got_meta[unused] == 0), "unlisted pages must stay untouched"
+
+    ref_gs = o.scores()
+    for k in (1, 5, 34, 40):
+        dw.score_topk(k)
+        torch.cuda.synchronize()
+        gs = to_f64(dw.scores)
+        check_scores(gs, ref_gs, nb, o.score_bound())
+        sel, cnt = dw.sel.cpu().numpy(), dw.sel_count.cpu().numpy()
+        check_selection_valid(sel, cnt, dw.scores.cpu().numpy(), nb, k)
+        rsel, rcnt = o.topk(k, ref_gs)
+        check_selection_vs_oracle(sel, cnt, rsel, rcnt, ref_gs, nb)
+
+    ref_dense, ref_lse = o.attention()
+    for S in (1, 3, 7):
+        dw.decode(sparse=False, num_splits=S)
+        assert_rows_close(to_f64(dw.out), ref_dense, tol, f"dense S={S}")
+        np.testing.assert_allclose(to_f64(dw.lse), ref_lse, rtol=tol, atol=tol)
+
+    sel, cnt = wl.random_selection(data, 6, seed=seed)
+    dw.set_selection(sel, cnt)
+    ref_sparse, _ = o.attention(sel, cnt)
+    for S in (1, 2, 5):
+        dw.decode(sparse=True, num_splits=S)
+        assert_rows_close(to_f64(dw.out), ref_sparse, tol, f"sparse S={S}")
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("sparse", [False, True])
+def test_split_partials_match_oracle_including_empty_splits(gpu, dtype, sparse):
+    data = mk(3, 8, 2, 128, (160, 33, 1), dtype, seed=77)
+    o = OracleRun(data)
+    dw = run_device(data, device=gpu)
+    sel = cnt = None
+    if sparse:
+        sel, cnt = wl.random_selection(data, 4, seed=5)
+        dw.set_selection(sel, cnt)
+    S = 12                                    # more splits than blocks for every sequence
+    dw.attention(sparse=sparse, num_splits=S)
+    po, pm, pl = (to_f64(t) for t in dw.partials(S))
+    ro, rm, rl = o.splits(S, sel, cnt)
+    empty = np.isneginf(rm)
+    assert empty.any()
+    assert np.array_equal(np.isneginf(pm), empty)
+    assert np.all(pl[empty] == 0) and np.all(po[empty] == 0)
+    live = ~empty
+    tol = ROW_TOL[dtype]
+    np.testing.assert_allclose(pm[live], rm[live], rtol=tol, atol=tol)
+    np.testing.assert_allclose(pl[live], rl[live], rtol=tol * 10)
+    assert_rows_close(po[live], ro[live], tol, "partial o")
+    dw.combine(S)
+    ref, _ = o.attention(sel, cnt)
+    assert_rows_close(to_f64(dw.out), ref, tol, "combined")
+
+
+def test_topk_ties_go_to_the_lower_block(gpu):
+    """q = 0 makes every score exactly 0: the selection must be blocks 0..K-1."""
+    data = mk(2, 4, 2, 128, (300, 77), "bf16", seed=5)
+    data.q_raw[:] = 0
+    dw = run_device(data, device=gpu)
+    dw.meta_build()
+    for k in (1, 3, 5, 19, 30):
+        dw.score_topk(k)
+        sel, cnt = dw.sel.cpu().numpy(), dw.sel_count.cpu().numpy()
+        for b, nb in enumerate(data.num_blocks()):
+            keff = min(k, int(nb))
+            for j in range(2):
+                assert sel[b, j, :keff].tolist() == list(range(keff))
+                assert cnt[b, j] == keff
+
+
+def test_duplicate_pages_tie_to_the_lower_block(gpu):
+    data = mk(1, 4, 1, 64, (40 * 16,), "f16", seed=6)
+    data.block_table[0, 7] = data.block_table[0, 2]       # blocks 2 and 7 share a page
+    o = OracleRun(data)
+    gs = o.scores()
+    rank = int(np.sum(gs[0, 0, :40] > gs[0, 0, 2]))
+    dw = run_device(data, device=gpu)
+    dw.meta_build()
+    dw.score_topk(rank + 1)
+    chosen = set(dw.sel.cpu().numpy()[0, 0, :rank + 1].tolist())
+    assert 2 in chosen and 7 not in chosen
+
+
+def test_topk_all_blocks_equals_dense(gpu):
+    data = mk(2, 8, 2, 128, (400, 130), "bf16", seed=8)
+    dw = run_device(data, device=gpu)
+    dw.meta_build()
+    dw.score_topk(data.spec.max_blocks)
+    dw.decode(sparse=True, num_splits=3)
+    sparse = to_f64(dw.out)
+    dw.decode(sparse=False, num_splits=3)
+    dense = to_f64(dw.out)
+    np.testing.assert_array_equal(sparse, dense)
+
+
+def test_deterministic_and_page_permutation_invariant(gpu):
+    data = mk(2, 8, 2, 128, (700, 230), "bf16", seed=9, extra_pages=4)
+    dw = run_device(data, device=gpu)
+    dw.meta_build()
+    dw.score_topk(9)
+    runs = []
+    for _ in range(2):
+        dw.meta_build()
+        dw.score_topk(9)
+        dw.decode(sparse=True, num_splits=4)
+        a = dw.out.clone()
+        dw.decode(sparse=False, num_splits=5)
+        runs.append((to_f64(dw.kmeta), dw.scores.cpu().numpy(), dw.sel.cpu().numpy(),
+                     to_f64(a), to_f64(dw.out)))
+    for x, y in zip(*runs):
+        assert x.tobytes() == y.tobytes()
+    perm = np.random.default_rng(2).permutation(data.spec.num_pages)
+    k2, v2 = np.empty_like(data.k_raw), np.empty_like(data.v_raw)
+    k2[perm], v2[perm] = data.k_raw, data.v_raw
+    data2 = wl.WorkloadData(spec=data.spec, q_raw=data.q_raw, k_raw=k2, v_raw=v2,
+                            block_table=perm[data.block_table].astype(np.int32),
+                            seq_lens=data.seq_lens, planted=data.planted)
+    dw2 = run_device(data2, device=gpu)
+    dw2.meta_build()
+    dw2.score_topk(9)
+    dw2.decode(sparse=True, num_splits=4)
+    a2 = to_f64(dw2.out)
+    dw2.decode(sparse=False, num_splits=5)
+    assert dw2.scores.cpu().numpy().tobytes() == runs[0][1].tobytes()
+    assert a2.tobytes() == runs[0][3].tobytes()
+    assert to_f64(dw2.out).tobytes() == runs[0][4].tobytes()
+
+
+def test_canary_guard_bytes_untouched(gpu):
+    """Outputs are written inside their bounds only: canaries around every
+    output buffer survive a full step."""
+    data = mk(2, 8, 2, 128, (333, 64), "bf16", seed=10)
+    dw = run_device(data, device=gpu)
+    CANARY = 0x7FC0DEAD
+
+    def guarded(shape, dtype):
+        n = int(np.prod(shape))
+        buf = torch.empty((n + 128,), dtype=dtype, device=gpu)
+        buf.view(torch.int32).fill_(CANARY)
+        return buf, buf[64:64 + n].view(shape)
+
+    B, Hq, Hkv, D, S, K = 2, 8, 2, 128, 3, 7
+    sbuf, dw.scores = guarded((B, Hkv, data.spec.max_blocks), torch.float32)
+    selbuf, dw.sel = guarded((B, Hkv, K), torch.int32)
+    cbuf, dw.sel_count = guarded((B, Hkv), torch.int32)
+    dw.topk = K
+    obuf, dw.out = guarded((B, Hq, D), torch.float32)
+    lbuf, dw.lse = guarded((B, Hq), torch.float32)
+    pob, po = guarded((B, Hq, S, D), torch.float32)
+    pmb, pm = guarded((B, Hq, S), torch.float32)
+    plb, pl = guarded((B, Hq, S), torch.float32)
+    dw._parts[S] = (po, pm, pl)
+    dw.meta_build()
+    dw.score_topk(K)
+    dw.decode(sparse=True, num_splits=S)
+    torch.cuda.synchronize()
+    for buf in (sbuf, selbuf, cbuf, obuf, lbuf, pob, pmb, plb):
+        words = buf.view(torch.int32).cpu().numpy()
+        assert np.all(words[:64] == CANARY) and np.all(words[-64:] == CANARY)
