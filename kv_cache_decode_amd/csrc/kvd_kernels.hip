@@ -173,13 +173,16 @@ __global__ __launch_bounds__(WAVES * kWave) void block_score_kernel(
 // ============================================================== Top-K
 //
 // One 1024-thread workgroup per (sequence, KV head).  Scores become monotone
-// uint32 keys (larger score -> larger key, -0 folded onto +0 so equal scores
-// give equal keys); thread t keeps keys of blocks [t*EPT, t*EPT+EPT) in
-// registers.  The K_eff-th largest key T is found bit by bit from the top
-// (the largest T with #{key >= T} >= K_eff), counting with wave ballots.  A
-// block is selected if its key is above T, or equal to T and among the first
-// K_eff - #{key > T} equal keys in index order; output positions come from an
-// exclusive scan in index order, so the list is ascending.
+// uint32 keys (larger score -> larger key; -0 folded onto +0 so equal scores
+// give equal keys); thread t keeps the keys of blocks [t*EPT, t*EPT+EPT) in
+// registers.  The K_eff-th largest key T is found by a radix select: the bits
+// above the highest bit where the smallest and largest valid keys differ are
+// fixed at once, then 8-bit digits below them are resolved from the top, each
+// pass building one private LDS histogram per wave (no atomic traffic between
+// waves) that wave 0 merges and scans.  A block is selected if its key is
+// above T, or equal to T and among the first K_eff - #{key > T} equal keys in
+// index order; one exclusive scan of packed (#greater, #equal) counts gives
+// every selected block its output position, so the list comes out ascending.
 
 __device__ inline uint32_t score_key(float f) {
   if (f == 0.0f) f = 0.0f;
@@ -187,32 +190,34 @@ __device__ inline uint32_t score_key(float f) {
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
-template <int NWAVES>
-__device__ inline uint32_t block_sum_uniform(uint32_t wave_value, uint32_t (*buf)[NWAVES],
-                                             int parity) {
-  // wave_value is wave-uniform; returns the workgroup total to every thread.
-  if ((threadIdx.x & (kWave - 1)) == 0) buf[parity][threadIdx.x >> 6] = wave_value;
-  __syncthreads();
-  uint32_t t = 0;
+__device__ inline uint32_t wave_min_u32(uint32_t v) {
 #pragma unroll
-  for (int w = 0; w < NWAVES; ++w) t += buf[parity][w];
-  return t;
+  for (int off = 1; off < kWave; off <<= 1) v = min(v, (uint32_t)__shfl_xor((int)v, off, kWave));
+  return v;
+}
+__device__ inline uint32_t wave_max_u32(uint32_t v) {
+#pragma unroll
+  for (int off = 1; off < kWave; off <<= 1) v = max(v, (uint32_t)__shfl_xor((int)v, off, kWave));
+  return v;
+}
+__device__ inline uint32_t wave_inclusive_scan(uint32_t v) {
+  const int lane = threadIdx.x & (kWave - 1);
+#pragma unroll
+  for (int off = 1; off < kWave; off <<= 1) {
+    const uint32_t o = __shfl_up(v, off, kWave);
+    if (lane >= off) v += o;
+  }
+  return v;
 }
 
 template <int NWAVES>
 __device__ inline uint32_t block_exclusive_scan(uint32_t v, uint32_t* buf) {
   const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x >> 6;
-  uint32_t inc = v;
-#pragma unroll
-  for (int off = 1; off < kWave; off <<= 1) {
-    const uint32_t o = __shfl_up(inc, off, kWave);
-    if (lane >= off) inc += o;
-  }
+  const uint32_t inc = wave_inclusive_scan(v);
   if (lane == kWave - 1) buf[wave] = inc;
   __syncthreads();
   uint32_t before = 0;
   for (int w = 0; w < wave; ++w) before += buf[w];
-  __syncthreads();
   return before + inc - v;
 }
 
@@ -223,57 +228,104 @@ __global__ __launch_bounds__(1024) void topk_kernel(const float* __restrict__ sc
                                                     int32_t* __restrict__ sel,
                                                     int32_t* __restrict__ sel_count) {
   constexpr int NW = 1024 / kWave;
-  __shared__ uint32_t cnt_buf[2][NW];
-  __shared__ uint32_t scan_buf[NW];
+  __shared__ __align__(16) uint32_t hist[NW][256];
+  __shared__ uint32_t buf_a[NW], buf_b[NW], buf_c[NW];
+  __shared__ uint32_t state[2];
   const int j = blockIdx.x, b = blockIdx.y;
-  const int tid = threadIdx.x;
+  const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid >> 6;
   const int nb = (seq_lens[b] + kBlockSize - 1) / kBlockSize;
   const int keff = min(K, nb);
+  int32_t* out = sel + ((size_t)b * Hkv + j) * K;
+  if (tid == 0) sel_count[(size_t)b * Hkv + j] = max(keff, 0);
+  for (int i = max(keff, 0) + tid; i < K; i += 1024) out[i] = -1;
+  if (keff <= 0) return;  // workgroup-uniform
   const float* row = scores + ((size_t)b * Hkv + j) * maxN;
 
   uint32_t key[EPT];
+  uint32_t kmn = 0xFFFFFFFFu, kmx = 0u;
 #pragma unroll
   for (int r = 0; r < EPT; ++r) {
     const int n = tid * EPT + r;
-    key[r] = (n < nb) ? score_key(row[n]) : 0u;  // valid keys are >= key(-inf) > 0
+    key[r] = 0u;
+    if (n < nb) {
+      key[r] = score_key(row[n]);  // valid keys are >= key(-inf) > 0
+      kmn = min(kmn, key[r]);
+      kmx = max(kmx, key[r]);
+    }
   }
-
-  uint32_t T = 0;
-  for (int bit = 31; bit >= 0; --bit) {
-    const uint32_t cand = T | (1u << bit);
-    uint32_t wc = 0;
+  kmn = wave_min_u32(kmn);
+  kmx = wave_max_u32(kmx);
+  if (lane == 0) { buf_a[wave] = kmn; buf_b[wave] = kmx; }
+  __syncthreads();
 #pragma unroll
-    for (int r = 0; r < EPT; ++r) wc += __popcll(__ballot(key[r] >= cand));
-    if (block_sum_uniform<NW>(wc, cnt_buf, bit & 1) >= (uint32_t)keff) T = cand;
+  for (int w = 0; w < NW; ++w) { kmn = min(kmn, buf_a[w]); kmx = max(kmx, buf_b[w]); }
+
+  // bits [lo, 32) of T are known; resolve the rest 8 bits at a time
+  const uint32_t diff = kmn ^ kmx;
+  int lo = diff ? 32 - __clz(diff) : 0;
+  uint32_t prefix = (lo >= 32) ? 0u : (kmx >> lo) << lo;
+  uint32_t krem = (uint32_t)keff;
+  while (lo > 0) {
+    const int width = min(8, lo);
+    const int shift = lo - width;
+    const uint32_t dmask = (1u << width) - 1u;
+    uint32_t* h = hist[wave];
+#pragma unroll
+    for (int i = lane; i < 256; i += kWave) h[i] = 0u;
+#pragma unroll
+    for (int r = 0; r < EPT; ++r) {
+      const bool match = key[r] != 0u && (lo >= 32 || (key[r] >> lo) == (prefix >> lo));
+      if (match) atomicAdd(&h[(key[r] >> shift) & dmask], 1u);
+    }
+    __syncthreads();
+    if (wave == 0) {
+      // lane L owns digits 255-4L .. 252-4L (descending)
+      const int base = 252 - 4 * lane;
+      uint32_t c3 = 0, c2 = 0, c1 = 0, c0 = 0;  // c3 = digit base+3 (largest)
+#pragma unroll
+      for (int w = 0; w < NW; ++w) {
+        const uint4 v = *reinterpret_cast<const uint4*>(&hist[w][base]);
+        c0 += v.x; c1 += v.y; c2 += v.z; c3 += v.w;
+      }
+      const uint32_t mine = c0 + c1 + c2 + c3;
+      uint32_t above = wave_inclusive_scan(mine) - mine;   // keys in larger digits
+      const uint32_t cs[4] = {c3, c2, c1, c0};
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        if (above < krem && above + cs[q] >= krem) {
+          state[0] = (uint32_t)(base + 3 - q);
+          state[1] = krem - above;
+        }
+        above += cs[q];
+      }
+    }
+    __syncthreads();
+    prefix |= state[0] << shift;
+    krem = state[1];
+    lo = shift;
   }
-  uint32_t wgt = 0;
-#pragma unroll
-  for (int r = 0; r < EPT; ++r) wgt += __popcll(__ballot(key[r] > T));
-  // parity 1: the last search step read parity 0, and a barrier separates
-  // this write from the previous reads of parity 1
-  const uint32_t n_gt = block_sum_uniform<NW>(wgt, cnt_buf, 1);
-  const uint32_t need_eq = (uint32_t)keff - n_gt;
+  const uint32_t T = prefix;   // the K_eff-th largest key; krem of its copies are taken
 
-  uint32_t n_eq = 0;
-#pragma unroll
-  for (int r = 0; r < EPT; ++r) n_eq += (key[r] == T);
-  uint32_t eq_rank = block_exclusive_scan<NW>(n_eq, scan_buf);
-  uint32_t take = 0;
-  bool pick[EPT];
+  uint32_t n_gt = 0, n_eq = 0;
 #pragma unroll
   for (int r = 0; r < EPT; ++r) {
-    bool p = key[r] > T;
-    if (key[r] == T) { p = eq_rank < need_eq; ++eq_rank; }
-    pick[r] = p;
-    take += p;
+    n_gt += key[r] > T;
+    n_eq += key[r] == T;
   }
-  uint32_t pos = block_exclusive_scan<NW>(take, scan_buf);
-  int32_t* out = sel + ((size_t)b * Hkv + j) * K;
+  // own buffer: with no radix pass, slower waves may still read buf_a / buf_b
+  const uint32_t ex = block_exclusive_scan<NW>((n_gt << 16) | n_eq, buf_c);
+  uint32_t gt_before = ex >> 16, eq_before = ex & 0xFFFFu;
 #pragma unroll
-  for (int r = 0; r < EPT; ++r)
-    if (pick[r]) out[pos++] = tid * EPT + r;
-  for (int i = keff + tid; i < K; i += 1024) out[i] = -1;
-  if (tid == 0) sel_count[(size_t)b * Hkv + j] = keff;
+  for (int r = 0; r < EPT; ++r) {
+    const int n = tid * EPT + r;
+    if (key[r] > T) {
+      out[gt_before + min(eq_before, krem)] = n;
+      ++gt_before;
+    } else if (key[r] == T) {
+      if (eq_before < krem) out[gt_before + eq_before] = n;
+      ++eq_before;
+    }
+  }
 }
 
 // ============================================================== decode attention
@@ -452,23 +504,27 @@ __global__ __launch_bounds__(WAVES * kWave) void paged_attn_kernel(
 
 // ============================================================== combine
 //
-// One 256-thread workgroup per (sequence, query head) row.  Pass 1: the max of
-// the split maxima.  Pass 2: SPI splits at a time, each handled by D/4 threads
-// holding a float4 of its output, accumulate w_s o_s and w_s with
-// w_s = l_s exp(m_s - M); then the SPI slots are summed through LDS.
+// One 256-thread workgroup per (row, 32-channel chunk), row = (sequence, query
+// head).  Pass 1: the max M of the split maxima.  Pass 2: 32 split slots of 8
+// threads (a float4 each) walk the splits with stride 32 and accumulate
+// w_s * o_s and w_s, w_s = l_s exp(m_s - M) (0 for an empty split, whose o is
+// 0); the loop body has no branch, so the loads of several splits are in
+// flight together.  The 32 slots are then summed through LDS.
 
-template <int D>
+constexpr int kCombineChunk = 32;
+
 __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ part_o,
                                                       const float* __restrict__ part_m,
                                                       const float* __restrict__ part_l, int S,
-                                                      float* __restrict__ out,
+                                                      int D, float* __restrict__ out,
                                                       float* __restrict__ lse) {
-  constexpr int TPS = D / 4;
-  constexpr int SPI = 256 / TPS;
+  constexpr int TPS = kCombineChunk / 4;   // threads per split slot
+  constexpr int SLOTS = 256 / TPS;
   __shared__ float red[256 / kWave];
-  __shared__ float4 acc_s[SPI][TPS];
-  __shared__ float w_s[SPI];
+  __shared__ float4 acc_s[SLOTS][TPS];
+  __shared__ float w_s[SLOTS];
   const size_t row = blockIdx.x;
+  const int d0 = blockIdx.y * kCombineChunk;
   const int tid = threadIdx.x;
   const float* pm = part_m + row * S;
   const float* pl = part_l + row * S;
@@ -481,13 +537,14 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
   M = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
 
   const int slot = tid / TPS, q4 = tid % TPS;
+  const float* po = part_o + (row * S) * D + d0 + q4 * 4;
   float4 a = make_float4(0.f, 0.f, 0.f, 0.f);
   float W = 0.0f;
-  for (int s = slot; s < S; s += SPI) {
+#pragma unroll 4
+  for (int s = slot; s < S; s += SLOTS) {
     const float ms = pm[s];
-    if (ms == -INFINITY) continue;
-    const float w = pl[s] * expf(ms - M);
-    const float4 o = *reinterpret_cast<const float4*>(part_o + (row * S + s) * D + q4 * 4);
+    const float w = (ms == -INFINITY) ? 0.0f : pl[s] * expf(ms - M);
+    const float4 o = *reinterpret_cast<const float4*>(po + (size_t)s * D);
     W += w;
     a.x = fmaf(w, o.x, a.x);
     a.y = fmaf(w, o.y, a.y);
@@ -501,15 +558,15 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
     float4 t = acc_s[0][tid];
     float wt = w_s[0];
 #pragma unroll
-    for (int k = 1; k < SPI; ++k) {
+    for (int k = 1; k < SLOTS; ++k) {
       const float4 u = acc_s[k][tid];
       t.x += u.x; t.y += u.y; t.z += u.z; t.w += u.w;
       wt += w_s[k];
     }
     const float inv = 1.0f / wt;
-    *reinterpret_cast<float4*>(out + row * D + tid * 4) =
+    *reinterpret_cast<float4*>(out + row * D + d0 + tid * 4) =
         make_float4(t.x * inv, t.y * inv, t.z * inv, t.w * inv);
-    if (lse && tid == 0) lse[row] = M + logf(wt);
+    if (lse && tid == 0 && blockIdx.y == 0) lse[row] = M + logf(wt);
   }
 }
 
@@ -642,11 +699,10 @@ hipError_t launch_paged_attn(int dtype, int D, int G, const void* q, const void*
 
 hipError_t launch_combine(int D, const float* part_o, const float* part_m, const float* part_l,
                           int rows, int S, float* out, float* lse, hipStream_t stream) {
-  return with_dim(D, [&](auto d) {
-    hipLaunchKernelGGL((combine_kernel<decltype(d)::value>), dim3(rows), dim3(256), 0, stream,
-                       part_o, part_m, part_l, S, out, lse);
-    return hipGetLastError();
-  });
+  if (D % kCombineChunk) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(combine_kernel, dim3(rows, D / kCombineChunk), dim3(256), 0, stream, part_o,
+                     part_m, part_l, S, D, out, lse);
+  return hipGetLastError();
 }
 
 int device_cu_count() { return cu_count(); }
