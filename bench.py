@@ -39,7 +39,10 @@ HBM_PEAK_GBPS = 8000.0
 WORKLOAD = "llama3.1_8b_gqa_b1_128k_bf16"
 HOSTKV_WORKLOAD = "llama3.1_8b_gqa_b1_128k_bf16_hostkv"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "paged_attn_dense_gqa128k_pmc.md")
-ATTN_SOURCE = os.path.join(ROOT, "kv_cache_decode_amd", "csrc", "kvd_kernels.hip")
+# sources that define the dense attention kernel: the counter-derived traffic
+# is only reported while they are unchanged since the counters were taken
+ATTN_SOURCES = [os.path.join(ROOT, "kv_cache_decode_amd", "csrc", f)
+                for f in ("kvd_attn.hip", "kvd_device.hpp")]
 
 
 def log(*a):
@@ -76,8 +79,11 @@ def stage_bytes(spec, topk: int, s_sparse: int, s_dense: int) -> dict:
 # ---------------------------------------------------------------- HBM traffic from counters
 
 def source_digest() -> str:
-    with open(ATTN_SOURCE, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+    h = hashlib.sha256()
+    for p in ATTN_SOURCES:
+        with open(p, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
 
 
 def measured_traffic():

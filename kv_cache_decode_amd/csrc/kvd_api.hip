@@ -11,10 +11,6 @@
 #include "../../include/kvdecode.h"
 #include "kvd_launch.hpp"
 
-namespace kvd {
-int device_cu_count();
-}
-
 namespace {
 
 thread_local std::string g_last_error;

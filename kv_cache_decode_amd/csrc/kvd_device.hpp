@@ -148,4 +148,17 @@ __device__ inline int lane_id() { return __lane_id(); }
 
 __device__ inline int readlane(int v, int lane) { return __builtin_amdgcn_readlane(v, lane); }
 
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+// Lane geometry of a row of D channels in 16-byte chunks.
+template <typename DT, int D>
+struct RowGeom {
+  static constexpr int E = DT::E;                  // channels per chunk
+  static constexpr int LPR = D / E;                // lanes per row
+  static constexpr int TPI = kWave / LPR;          // rows per load instruction
+  static constexpr int NI = kBlockSize / TPI;      // instructions per 16-row page
+  static_assert(LPR >= 8 && LPR <= 32 && TPI * LPR == kWave && NI >= 1, "row geometry");
+};
+
 }  // namespace kvd

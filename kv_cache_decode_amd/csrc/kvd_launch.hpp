@@ -6,6 +6,7 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+
 namespace kvd {
 
 hipError_t launch_block_meta(int dtype, int D, const void* k_cache, const int32_t* page_ids,
@@ -28,6 +29,21 @@ hipError_t launch_paged_attn(int dtype, int D, int G, const void* q, const void*
 
 hipError_t launch_combine(int D, const float* part_o, const float* part_m, const float* part_l,
                           int rows, int S, float* out, float* lse, hipStream_t stream);
+
+// Compute units of the current device (queried once).
+inline int cu_count() {
+  static int n = 0;
+  if (n == 0) {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        n <= 0)
+      n = 256;
+  }
+  return n;
+}
+
+inline int device_cu_count() { return cu_count(); }
 
 // Largest maxN the Top-K kernel keeps in registers (1024 threads x 32 keys).
 constexpr int kTopkMaxBlocks = 32768;
