@@ -147,6 +147,10 @@ __global__ __launch_bounds__(WAVES * kWave) void paged_attn_kernel(
       for (int it = 0; it < NI; ++it) {
         float vf[E];
         DT::widen(vc[it], vf);
+        if (it * TPI + rg >= valid) {  // slots past the sequence end may hold anything
+#pragma unroll
+          for (int e = 0; e < E; ++e) vf[e] = 0.0f;
+        }
 #pragma unroll
         for (int g = 0; g < G; ++g) {
           const float p = fast_exp2(z[it][g] - m[g]);
@@ -185,6 +189,253 @@ __global__ __launch_bounds__(WAVES * kWave) void paged_attn_kernel(
       part_m[(row0 + g) * S + s] = m[g] * kLn2;
       part_l[(row0 + g) * S + s] = lsum[g];
     }
+  }
+}
+
+// ============================================================== decode attention, MFMA path
+//
+// For 16-bit K/V and a GQA group of G = 2..8 query heads the two contractions
+// of a page are small dense products, so they run on the matrix cores:
+//
+//   S^T[16 tok x 16] = K[16 tok x D] . Q^T[D x 16]       v_mfma_f32_16x16x32 (D/32 steps)
+//   O[16 x D]       += P[16 x 16 tok] . V[16 tok x D]     v_mfma_f32_16x16x16 (D/16 tiles)
+//
+// with the G heads padded to the 16 MFMA rows (rows >= G are zero queries and
+// are never written out).  Lane l = 16*grp + col:
+//   * K is the A operand read straight from the page: lane l holds token col,
+//     channels 8*(4*st + grp) .. +8 of step st;
+//   * Q^T is the B operand, loaded once: head col, the same channels;
+//   * the S^T result gives lane l the logits of head col for tokens 4*grp + i,
+//     i = 0..3 -- exactly the A-operand layout of P for the second product, so
+//     P never moves between lanes;
+//   * V rows load coalesced (lane l: token 4*grp + i, channels D/16*col ..),
+//     and v_perm repacks them into the B operand (4 tokens x 1 channel per
+//     lane and tile);
+//   * lane l accumulates O[4*grp + i][D/16*col + n] in tile n.
+// The softmax state of head col lives in every lane of that column; the rows
+// of O are rescaled only when some head's running max grows.  P is fed to the
+// 16-bit product as a hi + lo pair (p = hi + lo exactly up to 2^-17 relative),
+// so the weights keep close to fp32 precision.
+
+typedef __bf16 bf16x8_v __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x8_v __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x4_v __attribute__((ext_vector_type(4)));
+typedef short s16x4_v __attribute__((ext_vector_type(4)));
+typedef float f32x4_v __attribute__((ext_vector_type(4)));
+
+template <typename DT>
+struct MfmaOps;
+
+template <>
+struct MfmaOps<BF16> {
+  __device__ static inline f32x4_v qk(const uint4& a, const uint4& b, f32x4_v c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_v, a),
+                                                   __builtin_bit_cast(bf16x8_v, b), c, 0, 0, 0);
+  }
+  __device__ static inline f32x4_v pv(const uint2& a, const uint2& b, f32x4_v c) {
+    return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(s16x4_v, a),
+                                                     __builtin_bit_cast(s16x4_v, b), c, 0, 0, 0);
+  }
+  __device__ static inline uint32_t pack(float lo, float hi) {  // round to nearest even
+    return (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)lo) |
+           ((uint32_t)__builtin_bit_cast(uint16_t, (__bf16)hi) << 16);
+  }
+  __device__ static inline float lo(uint32_t w) { return __uint_as_float(w << 16); }
+  __device__ static inline float hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+};
+
+template <>
+struct MfmaOps<F16> {
+  __device__ static inline f32x4_v qk(const uint4& a, const uint4& b, f32x4_v c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8_v, a),
+                                                  __builtin_bit_cast(f16x8_v, b), c, 0, 0, 0);
+  }
+  __device__ static inline f32x4_v pv(const uint2& a, const uint2& b, f32x4_v c) {
+    return __builtin_amdgcn_mfma_f32_16x16x16f16(__builtin_bit_cast(f16x4_v, a),
+                                                 __builtin_bit_cast(f16x4_v, b), c, 0, 0, 0);
+  }
+  __device__ static inline uint32_t pack(float lo, float hi) {
+    return (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)lo) |
+           ((uint32_t)__builtin_bit_cast(uint16_t, (_Float16)hi) << 16);
+  }
+  __device__ static inline float lo(uint32_t w) {
+    return (float)__builtin_bit_cast(_Float16, (uint16_t)(w & 0xffffu));
+  }
+  __device__ static inline float hi(uint32_t w) {
+    return (float)__builtin_bit_cast(_Float16, (uint16_t)(w >> 16));
+  }
+};
+
+// NDW dwords (2*NDW 16-bit channels) of one token row, as one vector load.
+template <int NDW>
+struct RowWords {
+  uint32_t w[NDW];
+  __device__ inline void load(const void* p) {
+    if constexpr (NDW == 4) {
+      const uint4 v = *reinterpret_cast<const uint4*>(p);
+      w[0] = v.x; w[1] = v.y; w[2] = v.z; w[3] = v.w;
+    } else {
+      static_assert(NDW == 2, "64 or 128 channels");
+      const uint2 v = *reinterpret_cast<const uint2*>(p);
+      w[0] = v.x; w[1] = v.y;
+    }
+  }
+};
+
+template <typename DT, int D, int G, int WAVES>
+__global__ __launch_bounds__(WAVES * kWave) void paged_attn_mfma_kernel(
+    const void* __restrict__ q, const void* __restrict__ k_cache, const void* __restrict__ v_cache,
+    const int32_t* __restrict__ block_table, const int32_t* __restrict__ seq_lens,
+    const int32_t* __restrict__ sel, const int32_t* __restrict__ sel_count, int sel_stride,
+    int Hq, int Hkv, int maxN, int S, float qscale, float* __restrict__ part_o,
+    float* __restrict__ part_m, float* __restrict__ part_l) {
+  static_assert(G >= 2 && G <= 8, "the group fills 2..8 of the 16 MFMA rows");
+  using St = typename DT::storage;
+  using Ops = MfmaOps<DT>;
+  constexpr int KS = D / 32;   // QK steps of 32 channels
+  constexpr int NT = D / 16;   // PV tiles of 16 output channels
+  constexpr int NDW = D / 32;  // dwords of V per lane and token (D/16 channels)
+  const int lane = threadIdx.x & (kWave - 1);
+  const int s = blockIdx.x * WAVES + (threadIdx.x >> 6);
+  if (s >= S) return;
+  const int j = blockIdx.y, b = blockIdx.z;
+  const int col = lane & 15, grp = lane >> 4;
+
+  const int L = seq_lens[b];
+  const int nb = (L + kBlockSize - 1) / kBlockSize;
+  const int n_list = sel ? sel_count[(size_t)b * Hkv + j] : nb;
+  const int chunk = (n_list + S - 1) / S;
+  const int p0 = min(s * chunk, n_list);
+  const int p1 = min(p0 + chunk, n_list);
+  const size_t row0 = (size_t)b * Hq + (size_t)j * G;
+
+  uint4 qB[KS];
+#pragma unroll
+  for (int st = 0; st < KS; ++st)
+    qB[st] = col < G ? load16(static_cast<const St*>(q) + (row0 + col) * D + 8 * (4 * st + grp))
+                     : make_uint4(0, 0, 0, 0);
+
+  f32x4_v o[NT];
+#pragma unroll
+  for (int n = 0; n < NT; ++n) o[n] = f32x4_v{0.f, 0.f, 0.f, 0.f};
+  float m = -INFINITY, lsum = 0.0f;
+
+  const size_t page_stride = (size_t)Hkv * kBlockSize * D;
+  const St* kb = static_cast<const St*>(k_cache) + (size_t)j * kBlockSize * D + (size_t)col * D +
+                 8 * grp;
+  const St* vb = static_cast<const St*>(v_cache) + (size_t)j * kBlockSize * D +
+                 (size_t)(4 * grp) * D + 2 * NDW * col;
+  const int32_t* sel_row = sel ? sel + ((size_t)b * Hkv + j) * sel_stride : nullptr;
+  const int32_t* bt_row = block_table + (size_t)b * maxN;
+
+  for (int base = p0; base < p1; base += kWave) {
+    const int cnt = min(kWave, p1 - base);
+    int my_page = 0, my_valid = 0;
+    if (lane < cnt) {
+      const int n = sel_row ? sel_row[base + lane] : base + lane;
+      my_page = bt_row[n];
+      my_valid = min(kBlockSize, L - n * kBlockSize);
+    }
+    uint4 ka[KS];
+    RowWords<NDW> vw[4];
+    {
+      const size_t off = (size_t)readlane(my_page, 0) * page_stride;
+#pragma unroll
+      for (int st = 0; st < KS; ++st) ka[st] = load16(kb + off + 32 * st);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) vw[i].load(vb + off + (size_t)i * D);
+    }
+    for (int it = 0; it < cnt; ++it) {
+      uint4 kn[KS];
+      RowWords<NDW> vn[4];
+      if (it + 1 < cnt) {
+        const size_t off = (size_t)readlane(my_page, it + 1) * page_stride;
+#pragma unroll
+        for (int st = 0; st < KS; ++st) kn[st] = load16(kb + off + 32 * st);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) vn[i].load(vb + off + (size_t)i * D);
+      }
+      const int valid = readlane(my_valid, it);
+
+      f32x4_v sacc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int st = 0; st < KS; ++st) sacc = Ops::qk(ka[st], qB[st], sacc);
+      float z[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) z[i] = (4 * grp + i < valid) ? sacc[i] * qscale : -INFINITY;
+      float bm = fmaxf(fmaxf(z[0], z[1]), fmaxf(z[2], z[3]));
+      bm = fmaxf(bm, xor16(bm));
+      bm = fmaxf(bm, xor32(bm));
+      if (__ballot(col < G && bm > m)) {  // wave-uniform
+        const float mn = fmaxf(m, bm);
+        const float alpha = fast_exp2(m - mn);
+        m = mn;
+        lsum *= alpha;
+        float ar[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) ar[i] = __shfl(alpha, 4 * grp + i, kWave);
+#pragma unroll
+        for (int n = 0; n < NT; ++n)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) o[n][i] *= ar[i];
+      }
+      float p[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) p[i] = fast_exp2(z[i] - m);
+      lsum += (p[0] + p[1]) + (p[2] + p[3]);
+      uint2 phi, plo;
+      phi.x = Ops::pack(p[0], p[1]);
+      phi.y = Ops::pack(p[2], p[3]);
+      plo.x = Ops::pack(p[0] - Ops::lo(phi.x), p[1] - Ops::hi(phi.x));
+      plo.y = Ops::pack(p[2] - Ops::lo(phi.y), p[3] - Ops::hi(phi.y));
+
+      if (valid < kBlockSize) {  // slots past the sequence end may hold anything
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          if (4 * grp + i >= valid)
+#pragma unroll
+            for (int k = 0; k < NDW; ++k) vw[i].w[k] = 0u;
+      }
+      uint2 vB[NT];
+#pragma unroll
+      for (int k = 0; k < NDW; ++k) {
+        vB[2 * k].x = __builtin_amdgcn_perm(vw[1].w[k], vw[0].w[k], 0x05040100u);
+        vB[2 * k].y = __builtin_amdgcn_perm(vw[3].w[k], vw[2].w[k], 0x05040100u);
+        vB[2 * k + 1].x = __builtin_amdgcn_perm(vw[1].w[k], vw[0].w[k], 0x07060302u);
+        vB[2 * k + 1].y = __builtin_amdgcn_perm(vw[3].w[k], vw[2].w[k], 0x07060302u);
+      }
+#pragma unroll
+      for (int n = 0; n < NT; ++n) o[n] = Ops::pv(phi, vB[n], o[n]);
+#pragma unroll
+      for (int n = 0; n < NT; ++n) o[n] = Ops::pv(plo, vB[n], o[n]);
+
+#pragma unroll
+      for (int st = 0; st < KS; ++st) ka[st] = kn[st];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) vw[i] = vn[i];
+    }
+  }
+
+  // totals per head (the four k-groups of a column saw disjoint tokens)
+  lsum += xor16(lsum);
+  lsum += xor32(lsum);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int g = 4 * grp + i;                  // output row held in o[.][i]
+    const float lt = __shfl(lsum, g & 15, kWave);
+    if (g < G) {
+      const float inv = lt > 0.0f ? 1.0f / lt : 0.0f;
+      float* dst = part_o + ((row0 + g) * S + s) * D + 2 * NDW * col;
+#pragma unroll
+      for (int n4 = 0; n4 < NT; n4 += 4)
+        *reinterpret_cast<float4*>(dst + n4) =
+            make_float4(o[n4][i] * inv, o[n4 + 1][i] * inv, o[n4 + 2][i] * inv,
+                        o[n4 + 3][i] * inv);
+    }
+  }
+  if (grp == 0 && col < G) {
+    part_m[(row0 + col) * S + s] = m * kLn2;
+    part_l[(row0 + col) * S + s] = lsum;
   }
 }
 
@@ -265,16 +516,24 @@ hipError_t launch_paged_attn(int dtype, int D, int G, const void* q, const void*
                              const int32_t* sel_count, int sel_stride, int B, int Hq, int Hkv,
                              int maxN, int S, float scale, float* part_o, float* part_m,
                              float* part_l, hipStream_t stream) {
+  constexpr int WAVES = 4;
+  const dim3 grid((S + WAVES - 1) / WAVES, Hkv, B);
+  const float qscale = scale * kLog2e;
   return with_dtype(dtype, [&](auto dt) {
     return with_dim(D, [&](auto d) {
       return with_group(G, [&](auto g) {
         using DT = decltype(dt);
-        constexpr int WAVES = 4;
-        const dim3 grid((S + WAVES - 1) / WAVES, Hkv, B);
-        hipLaunchKernelGGL(
-            (paged_attn_kernel<DT, decltype(d)::value, decltype(g)::value, WAVES>), grid,
-            dim3(WAVES * kWave), 0, stream, q, k_cache, v_cache, block_table, seq_lens, sel,
-            sel_count, sel_stride, Hq, Hkv, maxN, S, scale * kLog2e, part_o, part_m, part_l);
+        constexpr int DD = decltype(d)::value, GG = decltype(g)::value;
+        if constexpr (!std::is_same_v<DT, F32> && GG >= 2) {
+          hipLaunchKernelGGL((paged_attn_mfma_kernel<DT, DD, GG, WAVES>), grid,
+                             dim3(WAVES * kWave), 0, stream, q, k_cache, v_cache, block_table,
+                             seq_lens, sel, sel_count, sel_stride, Hq, Hkv, maxN, S, qscale,
+                             part_o, part_m, part_l);
+        } else {
+          hipLaunchKernelGGL((paged_attn_kernel<DT, DD, GG, WAVES>), grid, dim3(WAVES * kWave), 0,
+                             stream, q, k_cache, v_cache, block_table, seq_lens, sel, sel_count,
+                             sel_stride, Hq, Hkv, maxN, S, qscale, part_o, part_m, part_l);
+        }
         return hipGetLastError();
       });
     });

@@ -219,3 +219,35 @@ def test_canary_guard_bytes_untouched(gpu):
     for buf in (sbuf, selbuf, cbuf, obuf, lbuf, pob, pmb, plb):
         words = buf.view(torch.int32).cpu().numpy()
         assert np.all(words[:64] == CANARY) and np.all(words[-64:] == CANARY)
+
+
+@pytest.mark.parametrize("dtype,G", [("f32", 1), ("f16", 1), ("bf16", 4), ("f16", 8), ("bf16", 2)])
+def test_slots_past_the_sequence_end_never_leak(gpu, dtype, G):
+    """Unused slots of the last page (and whole unused pages) hold NaN: every
+    output must still match the oracle, which never reads them."""
+    data = mk(3, 2 * G, 2, 128, (100, 17, 1), dtype, seed=40 + G, extra_pages=2)
+    nan_bits = {"f32": np.float32(np.nan), "f16": np.float16(np.nan), "bf16": np.uint16(0x7FC0)}[dtype]
+    for b, L in enumerate(data.spec.seq_lens):
+        nb = -(-L // 16)
+        p = data.block_table[b, nb - 1]
+        data.k_raw[p, :, L - 16 * (nb - 1):] = nan_bits
+        data.v_raw[p, :, L - 16 * (nb - 1):] = nan_bits
+    data.k_raw[data.spec.used_pages:] = nan_bits
+    data.v_raw[data.spec.used_pages:] = nan_bits
+    o = OracleRun(data)
+    dw = run_device(data, device=gpu)
+    tol = ROW_TOL[dtype]
+    dw.meta_build()
+    dw.score_topk(3)
+    torch.cuda.synchronize()
+    gs = to_f64(dw.scores)
+    for b, nb in enumerate(data.num_blocks()):
+        assert np.all(np.isfinite(gs[b, :, :nb]))
+        pages = data.block_table[b, :nb]
+        np.testing.assert_array_equal(to_f64(dw.kmeta)[pages], o.meta()[pages])
+    for S in (1, 2):
+        dw.decode(sparse=False, num_splits=S)
+        assert_rows_close(to_f64(dw.out), o.attention()[0], tol, "dense")
+        dw.decode(sparse=True, num_splits=S)
+        sel, cnt = dw.sel.cpu().numpy(), dw.sel_count.cpu().numpy()
+        assert_rows_close(to_f64(dw.out), o.attention(sel, cnt)[0], tol, "sparse")
