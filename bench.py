@@ -145,26 +145,65 @@ def run_gpu(args, spec, data):
         step(copies[i % len(copies)])
     torch.cuda.synchronize()
 
+    # per-stage timing: eager launches bracketed by events on the launch stream
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(7)] for _ in range(args.steps)]
-    t_start, t_end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
-    wall0 = time.perf_counter()
-    t_start.record()
     for i in range(args.steps):
         step(copies[i % len(copies)], evs[i])
-    t_end.record()
     torch.cuda.synchronize()
-    wall = time.perf_counter() - wall0
-    total_ms = t_start.elapsed_time(t_end)
     per_stage_ms = {s: float(np.mean([e[i].elapsed_time(e[i + 1]) for e in evs]))
                     for i, s in enumerate(stages)}
+
+    def time_loop(run_one):
+        t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        wall0 = time.perf_counter()
+        t0.record()
+        for i in range(args.steps):
+            run_one(i)
+        t1.record()
+        torch.cuda.synchronize()
+        return t0.elapsed_time(t1), time.perf_counter() - wall0
+
+    # whole-step timing, eager launches without stage events
+    eager_ms, _ = time_loop(lambda i: step(copies[i % len(copies)]))
+
+    # the dominant kernel alone: back-to-back dense launches over the rotated
+    # copies, so per-launch event overhead does not enter its average
+    dense_loop_ms, _ = time_loop(
+        lambda i: copies[i % len(copies)].attention(sparse=False, num_splits=s_dense))
+
+    # whole-step timing, one HIP graph per workload copy
+    launch = "hip_graph"
+    try:
+        graphs = []
+        side = torch.cuda.Stream()
+        for c in copies:
+            side.wait_stream(torch.cuda.current_stream())
+            with torch.cuda.stream(side):
+                step(c)
+            torch.cuda.current_stream().wait_stream(side)
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                step(c)
+            graphs.append(g)
+        for i in range(args.warmup):
+            graphs[i % len(graphs)].replay()
+        total_ms, wall = time_loop(lambda i: graphs[i % len(graphs)].replay())
+        del graphs
+    except RuntimeError as e:          # capture unavailable: report eager launches
+        log(f"[bench] graph capture failed ({e}); timing eager launches")
+        launch = "eager"
+        total_ms, wall = time_loop(lambda i: step(copies[i % len(copies)]))
     for c in copies:
         c.close()
     del copies
     torch.cuda.empty_cache()
     return {
         "total_ms": total_ms, "wall_s": wall, "stage_ms": per_stage_ms,
-        "s_sparse": s_sparse, "s_dense": s_dense,
+        "s_sparse": s_sparse, "s_dense": s_dense, "launch": launch,
+        "dense_attn_loop_us": dense_loop_ms * 1e3 / args.steps,
+        "eager_ms_per_step": eager_ms / args.steps,
     }
 
 
@@ -303,6 +342,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-zero-copy", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true")
+    ap.add_argument("--only-zero-copy", action="store_true",
+                    help="run only the host-KV variant (for profiling it)")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -320,6 +361,9 @@ def main():
         sys.exit(1)
     from kv_cache_decode_amd import workload as wl
 
+    if args.only_zero_copy:
+        print(json.dumps({"zero_copy": run_zero_copy(args)}), flush=True)
+        return
     spec = wl.WORKLOADS[WORKLOAD]
     log(f"[bench] generating {spec.name}")
     data = wl.generate(spec)
@@ -333,7 +377,8 @@ def main():
     stage_gbps = {s: sb[s] / (st[s] * 1e-3) / 1e9 for s in st}
     sparse_ms = st["score_topk"] + st["sparse_attn"] + st["sparse_combine"]
     dense_ms = st["dense_attn"] + st["dense_combine"]
-    dense_gbps = stage_gbps["dense_attn"]
+    dense_us = g["dense_attn_loop_us"]
+    dense_gbps = sb["dense_attn"] / (dense_us * 1e-6) / 1e9
     traffic = measured_traffic()
 
     zc = None
@@ -365,7 +410,9 @@ def main():
             "kv_storage": spec.dtype, "topk_blocks": spec.topk_blocks,
             "splits_sparse": g["s_sparse"], "splits_dense": g["s_dense"],
             "step": "meta_build(all pages) + score_topk + sparse attn + combine + dense attn + combine",
+            "launch": g["launch"],
         },
+        "eager_ms_per_step": g["eager_ms_per_step"],
         "frac_of_hbm_peak": step_bytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBPS,
         "decode_steps_per_s": {"sparse": 1e3 / sparse_ms, "dense": 1e3 / dense_ms,
                                "full_step": 1e3 / ms},
@@ -382,7 +429,8 @@ def main():
             "frac": dense_gbps / HBM_PEAK_GBPS,
             "traffic": traffic,
             "algorithmic_bytes_per_launch": sb["dense_attn"],
-            "avg_launch_us": stage_us["dense_attn"],
+            "avg_launch_us": dense_us,
+            "timing": f"{args.steps} back-to-back launches between two HIP events",
         },
         "zero_copy": zc,
         "cpu_baseline": cpu,

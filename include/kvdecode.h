@@ -95,7 +95,8 @@ typedef struct {
  * with p = page_ids[i], v = page_valid_tokens[i] in [1, bs].  Exact (min and max
  * of representable values), so results are bit-identical to any exact reference
  * up to the sign of zero.  Pages not listed are not touched.  Page ids must be
- * distinct and in [0, P).
+ * distinct and in [0, P); any order is valid, and ascending page order reads
+ * K and writes kmeta as sequential streams (the fastest order for a full build).
  */
 kv_status kv_block_meta_build(const kv_shape* shape, const void* k_cache, const int32_t* page_ids,
                               const int32_t* page_valid_tokens, int32_t num_page_ids, void* kmeta,
@@ -127,7 +128,8 @@ kv_status kv_block_score_topk(const kv_shape* shape, const void* q, const void* 
 /*
  * Number of splits the library would pick for `blocks_per_unit` blocks per
  * (sequence, KV head) (maxN for dense calls, the selection length for sparse
- * ones): enough waves to fill the GPU, at least 8 blocks per split.  Always >= 1.
+ * ones): about 8 waves per compute unit, at least 2 blocks per split (8 with
+ * KV_FLAG_HOST_KV).  Always >= 1.
  */
 int32_t kv_auto_num_splits(const kv_shape* shape, int32_t blocks_per_unit);
 

@@ -11,6 +11,15 @@
 #include "../../include/kvdecode.h"
 #include "kvd_launch.hpp"
 
+// Split heuristic knobs (build macros): target waves per compute unit and the
+// fewest pages a split should own.
+#ifndef KVD_SPLIT_WAVES_PER_CU
+#define KVD_SPLIT_WAVES_PER_CU 8
+#endif
+#ifndef KVD_SPLIT_MIN_BLOCKS
+#define KVD_SPLIT_MIN_BLOCKS 2
+#endif
+
 namespace {
 
 thread_local std::string g_last_error;
@@ -59,6 +68,8 @@ kv_status check_shape(const kv_shape* s) {
   if (s->max_blocks_per_seq < 1)
     return fail(KV_ERR_INVALID_ARG, "max_blocks_per_seq=%d must be >= 1", s->max_blocks_per_seq);
   if (s->num_pages < 1) return fail(KV_ERR_INVALID_ARG, "num_pages=%d must be >= 1", s->num_pages);
+  if ((long)s->num_pages * s->num_kv_heads > 0x7fffffffL)
+    return fail(KV_ERR_INVALID_ARG, "num_pages * num_kv_heads must fit in int32");
   if (s->dtype != KV_F32 && s->dtype != KV_F16 && s->dtype != KV_BF16)
     return fail(KV_ERR_UNSUPPORTED, "dtype=%d unknown", s->dtype);
   if (s->flags & ~KV_FLAG_HOST_KV) return fail(KV_ERR_INVALID_ARG, "unknown flags 0x%x", s->flags);
@@ -156,10 +167,13 @@ kv_status kv_block_score_topk(const kv_shape* shape, const void* q, const void* 
 int32_t kv_auto_num_splits(const kv_shape* shape, int32_t blocks_per_unit) {
   if (check_shape(shape) != KV_OK || blocks_per_unit < 1) return 1;
   const long units = (long)shape->num_seqs * shape->num_kv_heads;
-  // about 8 waves per compute unit in flight, each over >= 8 pages
-  const long target_waves = (long)kvd::device_cu_count() * 8;
+  // about KVD_SPLIT_WAVES_PER_CU waves per compute unit, each over at least
+  // KVD_SPLIT_MIN_BLOCKS pages
+  const long target_waves = (long)kvd::device_cu_count() * KVD_SPLIT_WAVES_PER_CU;
   long s = (target_waves + units - 1) / units;
-  s = std::min<long>(s, (blocks_per_unit + 7) / 8);
+  // pages read over the host link favour fewer, longer splits
+  const long min_blocks = (shape->flags & KV_FLAG_HOST_KV) ? 8 : KVD_SPLIT_MIN_BLOCKS;
+  s = std::min<long>(s, (blocks_per_unit + min_blocks - 1) / min_blocks);
   return (int32_t)std::max<long>(1, std::min<long>(s, 65535L * 4));
 }
 

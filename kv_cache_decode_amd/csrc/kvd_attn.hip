@@ -12,6 +12,22 @@
 #include "kvd_dispatch.hpp"
 #include "kvd_launch.hpp"
 
+// Launch-shape knobs (build macros): waves (= splits) per workgroup, and a
+// lower bound on waves per SIMD for the MFMA kernel (0 = the compiler's
+// choice), which caps its register allocation: 3 fits in 142 VGPRs without
+// spilling, where the unconstrained allocation gave 180 registers (2 waves).
+#ifndef KVD_ATTN_WAVES
+#define KVD_ATTN_WAVES 4
+#endif
+#ifndef KVD_MFMA_WAVES_PER_EU
+#define KVD_MFMA_WAVES_PER_EU 3
+#endif
+#if KVD_MFMA_WAVES_PER_EU > 0
+#define KVD_MFMA_OCCUPANCY __attribute__((amdgpu_waves_per_eu(KVD_MFMA_WAVES_PER_EU)))
+#else
+#define KVD_MFMA_OCCUPANCY
+#endif
+
 namespace kvd {
 
 // ============================================================== decode attention
@@ -27,7 +43,7 @@ namespace kvd {
 // split are fetched once (one per lane) and broadcast with readlane, so the
 // K/V loads never wait on a table lookup.
 
-template <typename DT, int D, int G, int WAVES>
+template <typename DT, int D, int G, int WAVES, bool SPARSE>
 __global__ __launch_bounds__(WAVES * kWave) void paged_attn_kernel(
     const void* __restrict__ q, const void* __restrict__ k_cache, const void* __restrict__ v_cache,
     const int32_t* __restrict__ block_table, const int32_t* __restrict__ seq_lens,
@@ -45,7 +61,7 @@ __global__ __launch_bounds__(WAVES * kWave) void paged_attn_kernel(
 
   const int L = seq_lens[b];
   const int nb = (L + kBlockSize - 1) / kBlockSize;
-  const int n_list = sel ? sel_count[(size_t)b * Hkv + j] : nb;
+  const int n_list = SPARSE ? sel_count[(size_t)b * Hkv + j] : nb;
   const int chunk = (n_list + S - 1) / S;
   const int p0 = min(s * chunk, n_list);
   const int p1 = min(p0 + chunk, n_list);
@@ -71,14 +87,14 @@ __global__ __launch_bounds__(WAVES * kWave) void paged_attn_kernel(
   const size_t lane_off = ((size_t)j * kBlockSize + rg) * D + (size_t)c * E;
   const St* kb = static_cast<const St*>(k_cache) + lane_off;
   const St* vb = static_cast<const St*>(v_cache) + lane_off;
-  const int32_t* sel_row = sel ? sel + ((size_t)b * Hkv + j) * sel_stride : nullptr;
+  const int32_t* sel_row = SPARSE ? sel + ((size_t)b * Hkv + j) * sel_stride : nullptr;
   const int32_t* bt_row = block_table + (size_t)b * maxN;
 
   for (int base = p0; base < p1; base += kWave) {
     const int cnt = min(kWave, p1 - base);
     int my_page = 0, my_valid = 0;
     if (lane < cnt) {
-      const int n = sel_row ? sel_row[base + lane] : base + lane;
+      const int n = SPARSE ? sel_row[base + lane] : base + lane;
       my_page = bt_row[n];
       my_valid = min(kBlockSize, L - n * kBlockSize);
     }
@@ -282,8 +298,8 @@ struct RowWords {
   }
 };
 
-template <typename DT, int D, int G, int WAVES>
-__global__ __launch_bounds__(WAVES * kWave) void paged_attn_mfma_kernel(
+template <typename DT, int D, int G, int WAVES, bool SPARSE>
+__global__ __launch_bounds__(WAVES * kWave) KVD_MFMA_OCCUPANCY void paged_attn_mfma_kernel(
     const void* __restrict__ q, const void* __restrict__ k_cache, const void* __restrict__ v_cache,
     const int32_t* __restrict__ block_table, const int32_t* __restrict__ seq_lens,
     const int32_t* __restrict__ sel, const int32_t* __restrict__ sel_count, int sel_stride,
@@ -303,7 +319,7 @@ __global__ __launch_bounds__(WAVES * kWave) void paged_attn_mfma_kernel(
 
   const int L = seq_lens[b];
   const int nb = (L + kBlockSize - 1) / kBlockSize;
-  const int n_list = sel ? sel_count[(size_t)b * Hkv + j] : nb;
+  const int n_list = SPARSE ? sel_count[(size_t)b * Hkv + j] : nb;
   const int chunk = (n_list + S - 1) / S;
   const int p0 = min(s * chunk, n_list);
   const int p1 = min(p0 + chunk, n_list);
@@ -325,14 +341,14 @@ __global__ __launch_bounds__(WAVES * kWave) void paged_attn_mfma_kernel(
                  8 * grp;
   const St* vb = static_cast<const St*>(v_cache) + (size_t)j * kBlockSize * D +
                  (size_t)(4 * grp) * D + 2 * NDW * col;
-  const int32_t* sel_row = sel ? sel + ((size_t)b * Hkv + j) * sel_stride : nullptr;
+  const int32_t* sel_row = SPARSE ? sel + ((size_t)b * Hkv + j) * sel_stride : nullptr;
   const int32_t* bt_row = block_table + (size_t)b * maxN;
 
   for (int base = p0; base < p1; base += kWave) {
     const int cnt = min(kWave, p1 - base);
     int my_page = 0, my_valid = 0;
     if (lane < cnt) {
-      const int n = sel_row ? sel_row[base + lane] : base + lane;
+      const int n = SPARSE ? sel_row[base + lane] : base + lane;
       my_page = bt_row[n];
       my_valid = min(kBlockSize, L - n * kBlockSize);
     }
@@ -516,7 +532,7 @@ hipError_t launch_paged_attn(int dtype, int D, int G, const void* q, const void*
                              const int32_t* sel_count, int sel_stride, int B, int Hq, int Hkv,
                              int maxN, int S, float scale, float* part_o, float* part_m,
                              float* part_l, hipStream_t stream) {
-  constexpr int WAVES = 4;
+  constexpr int WAVES = KVD_ATTN_WAVES;
   const dim3 grid((S + WAVES - 1) / WAVES, Hkv, B);
   const float qscale = scale * kLog2e;
   return with_dtype(dtype, [&](auto dt) {
@@ -524,16 +540,22 @@ hipError_t launch_paged_attn(int dtype, int D, int G, const void* q, const void*
       return with_group(G, [&](auto g) {
         using DT = decltype(dt);
         constexpr int DD = decltype(d)::value, GG = decltype(g)::value;
-        if constexpr (!std::is_same_v<DT, F32> && GG >= 2) {
-          hipLaunchKernelGGL((paged_attn_mfma_kernel<DT, DD, GG, WAVES>), grid,
-                             dim3(WAVES * kWave), 0, stream, q, k_cache, v_cache, block_table,
-                             seq_lens, sel, sel_count, sel_stride, Hq, Hkv, maxN, S, qscale,
-                             part_o, part_m, part_l);
-        } else {
-          hipLaunchKernelGGL((paged_attn_kernel<DT, DD, GG, WAVES>), grid, dim3(WAVES * kWave), 0,
-                             stream, q, k_cache, v_cache, block_table, seq_lens, sel, sel_count,
-                             sel_stride, Hq, Hkv, maxN, S, qscale, part_o, part_m, part_l);
-        }
+        auto go = [&](auto sparse) {
+          constexpr bool SP = decltype(sparse)::value;
+          if constexpr (!std::is_same_v<DT, F32> && GG >= 2) {
+            hipLaunchKernelGGL((paged_attn_mfma_kernel<DT, DD, GG, WAVES, SP>), grid,
+                               dim3(WAVES * kWave), 0, stream, q, k_cache, v_cache, block_table,
+                               seq_lens, sel, sel_count, sel_stride, Hq, Hkv, maxN, S, qscale,
+                               part_o, part_m, part_l);
+          } else {
+            hipLaunchKernelGGL((paged_attn_kernel<DT, DD, GG, WAVES, SP>), grid,
+                               dim3(WAVES * kWave), 0, stream, q, k_cache, v_cache, block_table,
+                               seq_lens, sel, sel_count, sel_stride, Hq, Hkv, maxN, S, qscale,
+                               part_o, part_m, part_l);
+          }
+        };
+        if (sel) go(std::true_type{});
+        else go(std::false_type{});
         return hipGetLastError();
       });
     });

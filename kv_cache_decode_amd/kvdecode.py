@@ -13,7 +13,9 @@ import os
 from typing import Optional, Union
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libkvdecode.so")
+# KVD_LIBRARY_PATH selects another build of the same library (for example one
+# compiled with different launch-shape macros)
+LIB_PATH = os.environ.get("KVD_LIBRARY_PATH") or os.path.join(_HERE, "libkvdecode.so")
 
 KV_OK, KV_ERR_INVALID_ARG, KV_ERR_UNSUPPORTED, KV_ERR_ALIGNMENT, KV_ERR_WORKSPACE, KV_ERR_HIP = range(6)
 KV_F32, KV_F16, KV_BF16 = 0, 1, 2

@@ -77,8 +77,11 @@ class DeviceWorkload:
             for n in range(spec.blocks(b)):
                 ids.append(int(data.block_table[b, n]))
                 val.append(min(bs, spec.seq_lens[b] - n * bs))
-        self.page_ids = torch.tensor(ids, dtype=torch.int32, device=dev)
-        self.page_valid = torch.tensor(val, dtype=torch.int32, device=dev)
+        # the index build may list pages in any order; physical order turns its
+        # K reads and meta writes into sequential streams
+        order = np.argsort(np.asarray(ids, dtype=np.int64), kind="stable")
+        self.page_ids = torch.tensor(np.asarray(ids, np.int32)[order], device=dev)
+        self.page_valid = torch.tensor(np.asarray(val, np.int32)[order], device=dev)
         self.shape = kd.make_shape(spec.num_seqs, spec.num_q_heads, spec.num_kv_heads, D,
                                    spec.max_blocks, P, dt, block_size=bs,
                                    flags=kd.KV_FLAG_HOST_KV if self.host_kv else 0)

@@ -1,0 +1,174 @@
+"""The C ABI as a library: symbols and host-side validation (no GPU work).
+
+Every call here is built to fail host validation, so it returns before any
+launch; the pointer values passed are never dereferenced.
+"""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+from kv_cache_decode_amd import kvdecode as kd
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "kvdecode.h")
+
+A16 = 0x10000          # 16-byte aligned stand-in address (never dereferenced)
+A4 = 0x10004           # 4-byte aligned, not 16
+ODD = 0x10002          # 2-byte aligned
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(kv_[a-z_]+)\s*\(", text)))
+
+
+def test_header_declares_exactly_the_binding_exports():
+    assert declared_functions() == sorted(kd.EXPORTS)
+
+
+def test_library_exports_every_declared_symbol():
+    out = subprocess.run(["nm", "-D", "--defined-only", kd.LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    exported = set(line.split()[-1] for line in out.splitlines() if line.strip())
+    for name in declared_functions():
+        assert name in exported, name
+        assert getattr(ctypes.CDLL(kd.LIB_PATH), name)
+
+
+@pytest.mark.parametrize("lang", ["c", "c++"])
+def test_header_compiles_standalone(lang, tmp_path):
+    src = tmp_path / ("t.c" if lang == "c" else "t.cpp")
+    src.write_text('#include "kvdecode.h"\nint main(void) { kv_shape s; (void)s; return KV_OK; }\n')
+    cc = "gcc" if lang == "c" else "g++"
+    subprocess.run([cc, "-Wall", "-Werror", "-fsyntax-only", "-I", os.path.dirname(HEADER),
+                    str(src)], check=True)
+
+
+def shape(**kw):
+    base = dict(num_seqs=2, num_q_heads=8, num_kv_heads=2, head_dim=128, max_blocks_per_seq=4,
+                num_pages=8, dtype="bf16")
+    base.update(kw)
+    return kd.make_shape(**base)
+
+
+def expect(status, fn, *args, **kw):
+    with pytest.raises(kd.KVError) as e:
+        fn(*args, **kw, stream=0)
+    assert e.value.status == status, str(e.value)
+    assert kd.last_error_message()
+
+
+def attn(s, **kw):
+    args = dict(q=A16, k_cache=A16, v_cache=A16, block_table=A16, seq_lens=A16, sel_blocks=None,
+                sel_count=None, sel_stride=0, scale=0.1, num_splits=2, part_o=A16, part_m=A16,
+                part_l=A16)
+    args.update(kw)
+    return lambda stream: kd.kv_paged_decode_attn(s, stream=stream, **args)
+
+
+@pytest.mark.parametrize("bad,status", [
+    (dict(num_q_heads=7), kd.KV_ERR_INVALID_ARG),        # not a multiple of Hkv
+    (dict(num_q_heads=6), kd.KV_ERR_UNSUPPORTED),        # G = 3
+    (dict(num_q_heads=32), kd.KV_ERR_UNSUPPORTED),       # G = 16
+    (dict(head_dim=96), kd.KV_ERR_UNSUPPORTED),
+    (dict(block_size=8), kd.KV_ERR_UNSUPPORTED),
+    (dict(dtype=7), kd.KV_ERR_UNSUPPORTED),
+    (dict(num_seqs=0), kd.KV_ERR_INVALID_ARG),
+    (dict(num_kv_heads=0), kd.KV_ERR_INVALID_ARG),
+    (dict(max_blocks_per_seq=0), kd.KV_ERR_INVALID_ARG),
+    (dict(num_pages=0), kd.KV_ERR_INVALID_ARG),
+    (dict(flags=0x8), kd.KV_ERR_INVALID_ARG),
+    (dict(num_pages=2**30, num_kv_heads=4, num_q_heads=4), kd.KV_ERR_INVALID_ARG),
+])
+def test_shape_validation_in_every_call(bad, status):
+    s = shape(**bad)
+    expect(status, attn(s))
+    expect(status, lambda stream: kd.kv_block_meta_build(s, A16, A16, A16, 4, A16, stream=stream))
+    expect(status, lambda stream: kd.kv_block_score_topk(s, A16, A16, A16, A16, 2, A16, A16, A16,
+                                                         stream=stream))
+    expect(status, lambda stream: kd.kv_decode_combine(s, 2, A16, A16, A16, A16, None,
+                                                       stream=stream))
+    assert kd.kv_auto_num_splits(s, 100) == 1
+    assert kd.kv_score_topk_workspace_size(s, 2) == 0
+
+
+def test_null_shape_is_rejected():
+    lib = ctypes.CDLL(kd.LIB_PATH)
+    lib.kv_paged_decode_attn.restype = ctypes.c_int
+    assert lib.kv_decode_combine(None, 1, None, None, None, None, None, None) == kd.KV_ERR_INVALID_ARG
+    assert lib.kv_block_meta_build(None, None, None, None, 1, None, None) == kd.KV_ERR_INVALID_ARG
+
+
+def test_attention_argument_checks():
+    s = shape()
+    expect(kd.KV_ERR_INVALID_ARG, attn(s, num_splits=0))
+    expect(kd.KV_ERR_INVALID_ARG, attn(s, q=None))
+    expect(kd.KV_ERR_INVALID_ARG, attn(s, part_l=None))
+    expect(kd.KV_ERR_INVALID_ARG, attn(s, sel_blocks=A16))                  # count missing
+    expect(kd.KV_ERR_INVALID_ARG, attn(s, sel_blocks=A16, sel_count=A16))   # stride 0
+    expect(kd.KV_ERR_INVALID_ARG, attn(s, scale=0.0))
+    expect(kd.KV_ERR_INVALID_ARG, attn(s, scale=float("inf")))
+    expect(kd.KV_ERR_INVALID_ARG, attn(s, scale=float("nan")))
+    expect(kd.KV_ERR_ALIGNMENT, attn(s, k_cache=A4))
+    expect(kd.KV_ERR_ALIGNMENT, attn(s, part_o=A4))
+    expect(kd.KV_ERR_ALIGNMENT, attn(s, block_table=ODD))
+    expect(kd.KV_ERR_ALIGNMENT, attn(s, sel_blocks=ODD, sel_count=A16, sel_stride=4))
+
+
+def test_score_topk_argument_checks():
+    s = shape()
+    f = kd.kv_block_score_topk
+    expect(kd.KV_ERR_INVALID_ARG, lambda stream: f(s, A16, A16, A16, A16, 0, A16, A16, A16, stream=stream))
+    expect(kd.KV_ERR_INVALID_ARG, lambda stream: f(s, None, A16, A16, A16, 2, A16, A16, A16, stream=stream))
+    expect(kd.KV_ERR_ALIGNMENT, lambda stream: f(s, A4, A16, A16, A16, 2, A16, A16, A16, stream=stream))
+    need = kd.kv_score_topk_workspace_size(s, 2)
+    assert need >= 2 * 2 * 4 * 4 and need % 256 == 0
+    expect(kd.KV_ERR_WORKSPACE, lambda stream: f(s, A16, A16, A16, A16, 2, None, A16, A16, None, 0,
+                                                 stream=stream))
+    expect(kd.KV_ERR_WORKSPACE, lambda stream: f(s, A16, A16, A16, A16, 2, None, A16, A16, A16,
+                                                 need - 4, stream=stream))
+    big = shape(max_blocks_per_seq=32769)
+    expect(kd.KV_ERR_UNSUPPORTED, lambda stream: f(big, A16, A16, A16, A16, 2, A16, A16, A16,
+                                                   stream=stream))
+
+
+def test_meta_and_combine_argument_checks():
+    s = shape()
+    m = kd.kv_block_meta_build
+    expect(kd.KV_ERR_INVALID_ARG, lambda stream: m(s, A16, A16, A16, -1, A16, stream=stream))
+    expect(kd.KV_ERR_INVALID_ARG, lambda stream: m(s, None, A16, A16, 3, A16, stream=stream))
+    expect(kd.KV_ERR_ALIGNMENT, lambda stream: m(s, A4, A16, A16, 3, A16, stream=stream))
+    m(s, None, None, None, 0, None, stream=0)            # nothing to do: OK, no launch
+    c = kd.kv_decode_combine
+    expect(kd.KV_ERR_INVALID_ARG, lambda stream: c(s, 0, A16, A16, A16, A16, None, stream=stream))
+    expect(kd.KV_ERR_INVALID_ARG, lambda stream: c(s, 2, A16, A16, A16, None, None, stream=stream))
+    expect(kd.KV_ERR_ALIGNMENT, lambda stream: c(s, 2, A16, A16, A16, A4, None, stream=stream))
+
+
+def test_host_alloc_argument_checks_and_status_strings():
+    with pytest.raises(kd.KVError) as e:
+        kd.kv_host_alloc(0)
+    assert e.value.status == kd.KV_ERR_INVALID_ARG
+    with pytest.raises(kd.KVError) as e:
+        kd.kv_host_alloc(64, flags=0x10)
+    assert e.value.status == kd.KV_ERR_INVALID_ARG
+    kd.kv_host_free(0)                                   # NULL is a no-op
+    names = [kd.status_string(i) for i in range(6)]
+    assert names == ["KV_OK", "KV_ERR_INVALID_ARG", "KV_ERR_UNSUPPORTED", "KV_ERR_ALIGNMENT",
+                     "KV_ERR_WORKSPACE", "KV_ERR_HIP"]
+    assert kd.status_string(99) == "unknown kv_status"
+
+
+def test_auto_splits_bounds():
+    s = shape(num_seqs=1, num_kv_heads=8, num_q_heads=32, max_blocks_per_seq=8192, num_pages=8192)
+    for blocks in (1, 2, 7, 256, 8192):
+        S = kd.kv_auto_num_splits(s, blocks)
+        assert 1 <= S <= max(1, blocks)
+    assert kd.kv_auto_num_splits(s, 0) == 1
+    host = shape(num_seqs=1, num_kv_heads=8, num_q_heads=32, max_blocks_per_seq=8192,
+                 num_pages=8192, flags=kd.KV_FLAG_HOST_KV)
+    assert kd.kv_auto_num_splits(host, 256) <= 256 // 8
