@@ -38,6 +38,8 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBPS = 8000.0
 WORKLOAD = "llama3.1_8b_gqa_b1_128k_bf16"
 HOSTKV_WORKLOAD = "llama3.1_8b_gqa_b1_128k_bf16_hostkv"
+# measured beside the headline step at kernel level (not part of `value`)
+OTHER_WORKLOADS = ("llama3.1_8b_gqa_b4_32k_bf16", "opt6.7b_mha_b32_544_f16")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "paged_attn_dense_gqa128k_pmc.md")
 # sources that define the dense attention kernel: the counter-derived traffic
 # is only reported while they are unchanged since the counters were taken
@@ -207,6 +209,57 @@ def run_gpu(args, spec, data):
     }
 
 
+def run_other_workload(args, name):
+    """Kernel-level figures of another named workload (back-to-back launches
+    over rotated copies): dense attention GB/s, and the sparse decode path."""
+    import torch
+    from kv_cache_decode_amd import kvdecode as kd
+    from kv_cache_decode_amd import workload as wl
+    from kv_cache_decode_amd.step import DeviceWorkload
+
+    spec = wl.WORKLOADS[name]
+    data = wl.generate(spec)
+    copies = [DeviceWorkload(data) for _ in range(args.copies)]
+    reps = max(20, args.steps // 2)
+
+    def loop(fn):
+        for i in range(4):
+            fn(copies[i % len(copies)])
+        torch.cuda.synchronize()
+        t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        t0.record()
+        for i in range(reps):
+            fn(copies[i % len(copies)])
+        t1.record()
+        torch.cuda.synchronize()
+        return t0.elapsed_time(t1) * 1e3 / reps
+
+    s_dense = kd.kv_auto_num_splits(copies[0].shape, spec.max_blocks)
+    dense_us = loop(lambda c: c.attention(sparse=False, num_splits=s_dense))
+    sb = stage_bytes(spec, spec.topk_blocks or 1, 1, s_dense)
+    res = {"dense_attn_us": dense_us, "dense_attn_gbps": sb["dense_attn"] / (dense_us * 1e-6) / 1e9,
+           "dense_frac_of_hbm_peak": sb["dense_attn"] / (dense_us * 1e-6) / 1e9 / HBM_PEAK_GBPS,
+           "splits_dense": s_dense, "dtype": spec.dtype, "group": spec.group}
+    if spec.topk_blocks:
+        k = spec.topk_blocks
+        for c in copies:
+            c.meta_build()
+            c.score_topk(k)
+        s_sp = kd.kv_auto_num_splits(copies[0].shape, k)
+        res["meta_build_us"] = loop(lambda c: c.meta_build())
+        res["score_topk_us"] = loop(lambda c: c.score_topk(k))
+        res["sparse_attn_us"] = loop(lambda c: c.attention(sparse=True, num_splits=s_sp))
+        res["sparse_decode_us"] = loop(lambda c: (c.score_topk(k), c.decode(sparse=True,
+                                                                           num_splits=s_sp)))
+        res["sparse_decode_steps_per_s"] = 1e6 / res["sparse_decode_us"]
+        res["splits_sparse"] = s_sp
+    for c in copies:
+        c.close()
+    del copies
+    torch.cuda.empty_cache()
+    return res
+
+
 def run_zero_copy(args):
     """Sparse decode with K/V read directly from mapped pinned host memory."""
     import torch
@@ -341,6 +394,7 @@ def main():
     ap.add_argument("--cpu-reps", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-zero-copy", action="store_true")
+    ap.add_argument("--no-other-workloads", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true")
     ap.add_argument("--only-zero-copy", action="store_true",
                     help="run only the host-KV variant (for profiling it)")
@@ -380,6 +434,12 @@ def main():
     dense_us = g["dense_attn_loop_us"]
     dense_gbps = sb["dense_attn"] / (dense_us * 1e-6) / 1e9
     traffic = measured_traffic()
+
+    others = {}
+    if not args.no_other_workloads:
+        for name in OTHER_WORKLOADS:
+            log(f"[bench] {name}")
+            others[name] = run_other_workload(args, name)
 
     zc = None
     if not args.no_zero_copy:
@@ -432,6 +492,7 @@ def main():
             "avg_launch_us": dense_us,
             "timing": f"{args.steps} back-to-back launches between two HIP events",
         },
+        "other_workloads": others,
         "zero_copy": zc,
         "cpu_baseline": cpu,
     }
