@@ -19,6 +19,9 @@
 #ifndef KVD_ATTN_WAVES
 #define KVD_ATTN_WAVES 4
 #endif
+#ifndef KVD_ATTN_PREFETCH
+#define KVD_ATTN_PREFETCH 1   // pages of K/V loaded ahead by the MFMA kernel
+#endif
 #ifndef KVD_MFMA_WAVES_PER_EU
 #define KVD_MFMA_WAVES_PER_EU 3
 #endif
@@ -103,8 +106,8 @@ __global__ __launch_bounds__(WAVES * kWave) void paged_attn_kernel(
       const size_t off = (size_t)readlane(my_page, 0) * page_stride;
 #pragma unroll
       for (int it = 0; it < NI; ++it) {
-        kc[it] = load16(kb + off + (size_t)it * TPI * D);
-        vc[it] = load16(vb + off + (size_t)it * TPI * D);
+        kc[it] = load16_stream(kb + off + (size_t)it * TPI * D);
+        vc[it] = load16_stream(vb + off + (size_t)it * TPI * D);
       }
     }
     for (int i = 0; i < cnt; ++i) {
@@ -113,8 +116,8 @@ __global__ __launch_bounds__(WAVES * kWave) void paged_attn_kernel(
         const size_t off = (size_t)readlane(my_page, i + 1) * page_stride;
 #pragma unroll
         for (int it = 0; it < NI; ++it) {
-          kn[it] = load16(kb + off + (size_t)it * TPI * D);
-          vn[it] = load16(vb + off + (size_t)it * TPI * D);
+          kn[it] = load16_stream(kb + off + (size_t)it * TPI * D);
+          vn[it] = load16_stream(vb + off + (size_t)it * TPI * D);
         }
       }
       const int valid = readlane(my_valid, i);
@@ -288,11 +291,11 @@ struct RowWords {
   uint32_t w[NDW];
   __device__ inline void load(const void* p) {
     if constexpr (NDW == 4) {
-      const uint4 v = *reinterpret_cast<const uint4*>(p);
+      const uint4 v = load16_stream(p);
       w[0] = v.x; w[1] = v.y; w[2] = v.z; w[3] = v.w;
     } else {
       static_assert(NDW == 2, "64 or 128 channels");
-      const uint2 v = *reinterpret_cast<const uint2*>(p);
+      const uint2 v = load8_stream(p);
       w[0] = v.x; w[1] = v.y;
     }
   }
@@ -352,30 +355,34 @@ __global__ __launch_bounds__(WAVES * kWave) KVD_MFMA_OCCUPANCY void paged_attn_m
       my_page = bt_row[n];
       my_valid = min(kBlockSize, L - n * kBlockSize);
     }
-    uint4 ka[KS];
-    RowWords<NDW> vw[4];
-    {
-      const size_t off = (size_t)readlane(my_page, 0) * page_stride;
+    struct PageRegs {
+      uint4 k[KS];
+      RowWords<NDW> v[4];
+    };
+    auto load_page = [&](PageRegs& r, int idx) {
+      const size_t off = (size_t)readlane(my_page, idx) * page_stride;
 #pragma unroll
-      for (int st = 0; st < KS; ++st) ka[st] = load16(kb + off + 32 * st);
+      for (int st = 0; st < KS; ++st) r.k[st] = load16_stream(kb + off + 32 * st);
 #pragma unroll
-      for (int i = 0; i < 4; ++i) vw[i].load(vb + off + (size_t)i * D);
-    }
+      for (int i = 0; i < 4; ++i) r.v[i].load(vb + off + (size_t)i * D);
+    };
+    PageRegs cur, nxt;
+    load_page(cur, 0);
+#if KVD_ATTN_PREFETCH >= 2
+    if (cnt > 1) load_page(nxt, 1);
+#endif
     for (int it = 0; it < cnt; ++it) {
-      uint4 kn[KS];
-      RowWords<NDW> vn[4];
-      if (it + 1 < cnt) {
-        const size_t off = (size_t)readlane(my_page, it + 1) * page_stride;
-#pragma unroll
-        for (int st = 0; st < KS; ++st) kn[st] = load16(kb + off + 32 * st);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) vn[i].load(vb + off + (size_t)i * D);
-      }
+#if KVD_ATTN_PREFETCH >= 2
+      PageRegs nx2;
+      if (it + 2 < cnt) load_page(nx2, it + 2);
+#else
+      if (it + 1 < cnt) load_page(nxt, it + 1);
+#endif
       const int valid = readlane(my_valid, it);
 
       f32x4_v sacc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int st = 0; st < KS; ++st) sacc = Ops::qk(ka[st], qB[st], sacc);
+      for (int st = 0; st < KS; ++st) sacc = Ops::qk(cur.k[st], qB[st], sacc);
       float z[4];
 #pragma unroll
       for (int i = 0; i < 4; ++i) z[i] = (4 * grp + i < valid) ? sacc[i] * qscale : -INFINITY;
@@ -410,25 +417,27 @@ __global__ __launch_bounds__(WAVES * kWave) KVD_MFMA_OCCUPANCY void paged_attn_m
         for (int i = 0; i < 4; ++i)
           if (4 * grp + i >= valid)
 #pragma unroll
-            for (int k = 0; k < NDW; ++k) vw[i].w[k] = 0u;
+            for (int k = 0; k < NDW; ++k) cur.v[i].w[k] = 0u;
       }
       uint2 vB[NT];
 #pragma unroll
       for (int k = 0; k < NDW; ++k) {
-        vB[2 * k].x = __builtin_amdgcn_perm(vw[1].w[k], vw[0].w[k], 0x05040100u);
-        vB[2 * k].y = __builtin_amdgcn_perm(vw[3].w[k], vw[2].w[k], 0x05040100u);
-        vB[2 * k + 1].x = __builtin_amdgcn_perm(vw[1].w[k], vw[0].w[k], 0x07060302u);
-        vB[2 * k + 1].y = __builtin_amdgcn_perm(vw[3].w[k], vw[2].w[k], 0x07060302u);
+        vB[2 * k].x = __builtin_amdgcn_perm(cur.v[1].w[k], cur.v[0].w[k], 0x05040100u);
+        vB[2 * k].y = __builtin_amdgcn_perm(cur.v[3].w[k], cur.v[2].w[k], 0x05040100u);
+        vB[2 * k + 1].x = __builtin_amdgcn_perm(cur.v[1].w[k], cur.v[0].w[k], 0x07060302u);
+        vB[2 * k + 1].y = __builtin_amdgcn_perm(cur.v[3].w[k], cur.v[2].w[k], 0x07060302u);
       }
 #pragma unroll
       for (int n = 0; n < NT; ++n) o[n] = Ops::pv(phi, vB[n], o[n]);
 #pragma unroll
       for (int n = 0; n < NT; ++n) o[n] = Ops::pv(plo, vB[n], o[n]);
 
-#pragma unroll
-      for (int st = 0; st < KS; ++st) ka[st] = kn[st];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) vw[i] = vn[i];
+#if KVD_ATTN_PREFETCH >= 2
+      cur = nxt;
+      nxt = nx2;
+#else
+      cur = nxt;
+#endif
     }
   }
 

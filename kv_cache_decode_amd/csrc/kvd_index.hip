@@ -12,70 +12,72 @@
 #include "kvd_dispatch.hpp"
 #include "kvd_launch.hpp"
 
+// Launch-shape knobs (build macros): most workgroups per compute unit of the
+// meta build (the grid strides over wave steps beyond that); 16-byte steps per
+// wave of the scorer.
+#ifndef KVD_META_WGS_PER_CU
+#define KVD_META_WGS_PER_CU 16
+#endif
+#ifndef KVD_SCORE_STEPS
+#define KVD_SCORE_STEPS 8
+#endif
+
 namespace kvd {
 
 // ============================================================== block meta
 //
-// One wave per (page, KV head) unit: NI loads cover the 16 x D key tile, each
-// lane folds the slots it holds (slot it*TPI + rg) into a running min and max,
-// the row groups are merged across lanes, and row group 0 writes the min row,
-// row group 1 the max row.  min/max of representable values is exact, so the
-// narrowing back to the storage dtype is exact too.
+// Lane (us, c) of a wave owns channel chunk c (E channels, 16 bytes) of unit
+// slot us: a wave step covers UPS = 64 / LPR consecutive (page, KV head) units
+// u = i*Hkv + j (i indexes page_ids).  Each lane walks the 16 token rows of
+// its unit with one 16-byte load per row -- a load instruction reads UPS full
+// row segments of D*eb bytes -- and keeps the running min and max of its
+// chunk in registers, so no cross-lane reduction is needed.  It then writes
+// its chunk of the min row and of the max row.  min/max of representable
+// values is exact, so the narrowing back to the storage dtype is exact too.
+// Wave steps are spread grid-stride; with page_ids in ascending order a step
+// reads UPS*16*D*eb contiguous bytes.
 
-template <typename DT, int D, int WAVES, int UNROLL>
+template <typename DT, int D, int WAVES>
 __global__ __launch_bounds__(WAVES * kWave) void block_meta_kernel(
     const void* __restrict__ k_cache, const int32_t* __restrict__ page_ids,
     const int32_t* __restrict__ valid_tokens, int n_ids, int Hkv, void* __restrict__ kmeta) {
   using G_ = RowGeom<DT, D>;
   using St = typename DT::storage;
-  constexpr int E = G_::E, LPR = G_::LPR, TPI = G_::TPI, NI = G_::NI;
+  constexpr int E = G_::E, LPR = G_::LPR;
+  constexpr int UPS = kWave / LPR;  // units per wave step
   const int lane = threadIdx.x & (kWave - 1);
-  const int rg = lane / LPR, c = lane % LPR;
-  const int nwaves = gridDim.x * WAVES;
-  const int units = n_ids * Hkv;
+  const int us = lane / LPR, c = lane % LPR;
+  const long units = (long)n_ids * Hkv;
+  const long steps = (units + UPS - 1) / UPS;
+  const long nwaves = (long)gridDim.x * WAVES;
 
-  for (int u0 = blockIdx.x * WAVES + (threadIdx.x >> 6); u0 < units; u0 += nwaves * UNROLL) {
-    uint4 w[UNROLL][NI];
-    int page[UNROLL], nv[UNROLL], head[UNROLL];
+  for (long step = (long)blockIdx.x * WAVES + (threadIdx.x >> 6); step < steps; step += nwaves) {
+    const long u = step * UPS + us;
+    if (u >= units) continue;                      // tail lanes of the last step
+    const int i = (int)(u / Hkv);
+    const int j = (int)(u - (long)i * Hkv);
+    const size_t tile = (size_t)page_ids[i] * Hkv + j;
+    const int nv = valid_tokens[i];
+    const St* src = static_cast<const St*>(k_cache) + tile * kBlockSize * D + (size_t)c * E;
+    uint4 w[kBlockSize];
 #pragma unroll
-    for (int x = 0; x < UNROLL; ++x) {
-      const int u = u0 + x * nwaves;
-      page[x] = -1;
-      if (u < units) {
-        const int i = u / Hkv;
-        head[x] = u - i * Hkv;
-        page[x] = page_ids[i];
-        nv[x] = valid_tokens[i];
-        const St* src = static_cast<const St*>(k_cache) +
-                        (((size_t)page[x] * Hkv + head[x]) * kBlockSize + rg) * D + c * E;
+    for (int t = 0; t < kBlockSize; ++t) w[t] = load16_stream(src + (size_t)t * D);
+    float mn[E], mx[E];
+    DT::widen(w[0], mn);                           // slot 0 is always valid
 #pragma unroll
-        for (int it = 0; it < NI; ++it) w[x][it] = load16(src + (size_t)it * TPI * D);
+    for (int e = 0; e < E; ++e) mx[e] = mn[e];
+#pragma unroll
+    for (int t = 1; t < kBlockSize; ++t) {
+      if (t < nv) {
+        float f[E];
+        DT::widen(w[t], f);
+#pragma unroll
+        for (int e = 0; e < E; ++e) { mn[e] = fminf(mn[e], f[e]); mx[e] = fmaxf(mx[e], f[e]); }
       }
     }
-#pragma unroll
-    for (int x = 0; x < UNROLL; ++x) {
-      if (page[x] < 0) break;  // wave-uniform
-      float mn[E], mx[E];
-#pragma unroll
-      for (int e = 0; e < E; ++e) { mn[e] = INFINITY; mx[e] = -INFINITY; }
-#pragma unroll
-      for (int it = 0; it < NI; ++it) {
-        if (it * TPI + rg < nv[x]) {
-          float f[E];
-          DT::widen(w[x][it], f);
-#pragma unroll
-          for (int e = 0; e < E; ++e) { mn[e] = fminf(mn[e], f[e]); mx[e] = fmaxf(mx[e], f[e]); }
-        }
-      }
-#pragma unroll
-      for (int e = 0; e < E; ++e) {
-        mn[e] = cross_group_reduce<LPR, OpMin>(mn[e]);
-        mx[e] = cross_group_reduce<LPR, OpMax>(mx[e]);
-      }
-      St* dst = static_cast<St*>(kmeta) + ((size_t)page[x] * Hkv + head[x]) * 2 * D + c * E;
-      if (rg == 0) store16(dst, DT::narrow_exact(mn));
-      if (rg == 1) store16(dst + D, DT::narrow_exact(mx));
-    }
+    St* dst = static_cast<St*>(kmeta) + tile * 2 * D + (size_t)c * E;
+    store16(dst, DT::narrow_exact(mn));
+    store16(dst + D, DT::narrow_exact(mx));
   }
 }
 
@@ -319,13 +321,14 @@ hipError_t launch_block_meta(int dtype, int D, const void* k_cache, const int32_
   return with_dtype(dtype, [&](auto dt) {
     return with_dim(D, [&](auto d) {
       using DT = decltype(dt);
-      constexpr int WAVES = 4, UNROLL = 2;
-      const long units = (long)n_ids * Hkv;
-      const long want = (units + WAVES * UNROLL - 1) / (WAVES * UNROLL);
-      const int grid = (int)std::min<long>(want, (long)cu_count() * 16);
-      hipLaunchKernelGGL((block_meta_kernel<DT, decltype(d)::value, WAVES, UNROLL>), dim3(grid),
-                         dim3(WAVES * kWave), 0, stream, k_cache, page_ids, valid_tokens, n_ids,
-                         Hkv, kmeta);
+      constexpr int DD = decltype(d)::value;
+      constexpr int WAVES = 4;
+      constexpr int UPS = kWave / RowGeom<DT, DD>::LPR;
+      const long steps = ((long)n_ids * Hkv + UPS - 1) / UPS;
+      const long want = (steps + WAVES - 1) / WAVES;
+      const int grid = (int)std::min<long>(want, (long)cu_count() * KVD_META_WGS_PER_CU);
+      hipLaunchKernelGGL((block_meta_kernel<DT, DD, WAVES>), dim3(grid), dim3(WAVES * kWave), 0,
+                         stream, k_cache, page_ids, valid_tokens, n_ids, Hkv, kmeta);
       return hipGetLastError();
     });
   });
@@ -339,7 +342,7 @@ hipError_t launch_block_score(int dtype, int D, int G, const void* q, const void
       return with_group(G, [&](auto g) {
         using DT = decltype(dt);
         constexpr int DD = decltype(d)::value;
-        constexpr int WAVES = 4, STEPS = 8;
+        constexpr int WAVES = 4, STEPS = KVD_SCORE_STEPS;
         constexpr int per_wg = WAVES * STEPS * RowGeom<DT, DD>::TPI;
         const dim3 grid((maxN + per_wg - 1) / per_wg, Hkv, B);
         hipLaunchKernelGGL((block_score_kernel<DT, DD, decltype(g)::value, WAVES, STEPS>), grid,

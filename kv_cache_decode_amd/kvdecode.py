@@ -62,6 +62,14 @@ def _load() -> ctypes.CDLL:
     if not os.path.exists(LIB_PATH):
         raise ImportError(f"{LIB_PATH} is not built: run kv_cache_decode_amd/build.py "
                           "(or __graft_entry__.build()) first")
+    # One HIP runtime per process: torch ships its own libamdhip64 under the
+    # same soname, so loading torch first makes the library bind to that
+    # runtime instead of pulling in a second copy from the ROCm install (two
+    # runtimes in one process do not share devices, streams or allocations).
+    try:
+        import torch  # noqa: F401
+    except ImportError:
+        pass
     lib = ctypes.CDLL(LIB_PATH)
     P, I32, U32, SZ, F = ctypes.c_void_p, ctypes.c_int32, ctypes.c_uint32, ctypes.c_size_t, ctypes.c_float
     S = ctypes.POINTER(KVShape)

@@ -172,3 +172,11 @@ def test_auto_splits_bounds():
     host = shape(num_seqs=1, num_kv_heads=8, num_q_heads=32, max_blocks_per_seq=8192,
                  num_pages=8192, flags=kd.KV_FLAG_HOST_KV)
     assert kd.kv_auto_num_splits(host, 256) <= 256 // 8
+
+
+def test_one_hip_runtime_per_process():
+    """The binding loads after torch, so only torch's HIP runtime is mapped."""
+    import torch  # noqa: F401
+    maps = open("/proc/self/maps").read()
+    libs = set(line.split()[-1] for line in maps.splitlines() if "libamdhip64" in line)
+    assert len(libs) == 1, libs
