@@ -5,7 +5,7 @@ Workload: Llama-3.1-8B-shaped GQA decode of one layer at 128k context (batch 1,
 table, 5% planted blocks, Top-K 256 blocks), synthetic seeded data.
 
 One step = one pass over every stage of the path on that input:
-  block meta build over all 8192 pages -> Quest scores + Top-K 256 ->
+  block meta build over all 8192 pages -> append of the newest token -> Quest scores + Top-K 256 ->
   sparse split-K attention -> merge -> dense split-K attention -> merge.
 The metric is KV GB/s (algorithmic bytes of the step / step time, and the same
 per stage) and decode steps/s; the dominant kernel (dense attention) is also
@@ -68,6 +68,8 @@ def stage_bytes(spec, topk: int, s_sparse: int, s_dense: int) -> dict:
     out = B * Hq * (D + 1) * 4
     return {
         "meta_build": blocks * Hkv * (tile + meta_row) + blocks * 8,
+        # new K and V rows in and out, the meta rows of their pages read and written
+        "append": B * Hkv * (4 * D * eb + 2 * meta_row) + 2 * B * 4,
         "score_topk": blocks * Hkv * meta_row + q_bytes + blocks * Hkv * 4      # meta + q + table
                       + 2 * B * Hkv * maxN * 4                                   # scores out + in
                       + B * Hkv * (topk + 1) * 4,                                # selection
@@ -118,37 +120,33 @@ def run_gpu(args, spec, data):
     from kv_cache_decode_amd import kvdecode as kd
     s_sparse = kd.kv_auto_num_splits(copies[0].shape, k)
     s_dense = kd.kv_auto_num_splits(copies[0].shape, spec.max_blocks)
-    stages = ["meta_build", "score_topk", "sparse_attn", "sparse_combine", "dense_attn",
-              "dense_combine"]
+    stages = ["meta_build", "append", "score_topk", "sparse_attn", "sparse_combine",
+              "dense_attn", "dense_combine"]
+    actions = [
+        lambda c: c.meta_build(),
+        lambda c: c.append(),            # the newest token again: state is unchanged
+        lambda c: c.score_topk(k),
+        lambda c: c.attention(sparse=True, num_splits=s_sparse),
+        lambda c: c.combine(s_sparse),
+        lambda c: c.attention(sparse=False, num_splits=s_dense),
+        lambda c: c.combine(s_dense),
+    ]
 
     def step(c, ev=None):
+        for i, act in enumerate(actions):
+            if ev is not None:
+                ev[i].record()
+            act(c)
         if ev is not None:
-            ev[0].record()
-        c.meta_build()
-        if ev is not None:
-            ev[1].record()
-        c.score_topk(k)
-        if ev is not None:
-            ev[2].record()
-        c.attention(sparse=True, num_splits=s_sparse)
-        if ev is not None:
-            ev[3].record()
-        c.combine(s_sparse)
-        if ev is not None:
-            ev[4].record()
-        c.attention(sparse=False, num_splits=s_dense)
-        if ev is not None:
-            ev[5].record()
-        c.combine(s_dense)
-        if ev is not None:
-            ev[6].record()
+            ev[len(actions)].record()
 
     for i in range(args.warmup):
         step(copies[i % len(copies)])
     torch.cuda.synchronize()
 
     # per-stage timing: eager launches bracketed by events on the launch stream
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(7)] for _ in range(args.steps)]
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(len(stages) + 1)]
+           for _ in range(args.steps)]
     torch.cuda.synchronize()
     for i in range(args.steps):
         step(copies[i % len(copies)], evs[i])
@@ -429,8 +427,10 @@ def main():
     st = g["stage_ms"]
     stage_us = {s: st[s] * 1e3 for s in st}
     stage_gbps = {s: sb[s] / (st[s] * 1e-3) / 1e9 for s in st}
-    sparse_ms = st["score_topk"] + st["sparse_attn"] + st["sparse_combine"]
-    dense_ms = st["dense_attn"] + st["dense_combine"]
+    # a decode step: append the new token, then (sparse) score + Top-K + attention +
+    # merge, or (dense) attention + merge
+    sparse_ms = st["append"] + st["score_topk"] + st["sparse_attn"] + st["sparse_combine"]
+    dense_ms = st["append"] + st["dense_attn"] + st["dense_combine"]
     dense_us = g["dense_attn_loop_us"]
     dense_gbps = sb["dense_attn"] / (dense_us * 1e-6) / 1e9
     traffic = measured_traffic()
@@ -469,7 +469,8 @@ def main():
             "head_dim": spec.head_dim, "block_size": spec.block_size,
             "kv_storage": spec.dtype, "topk_blocks": spec.topk_blocks,
             "splits_sparse": g["s_sparse"], "splits_dense": g["s_dense"],
-            "step": "meta_build(all pages) + score_topk + sparse attn + combine + dense attn + combine",
+            "step": "meta_build(all pages) + append + score_topk + sparse attn + combine + "
+                    "dense attn + combine",
             "launch": g["launch"],
         },
         "eager_ms_per_step": g["eager_ms_per_step"],

@@ -7,6 +7,7 @@
  *   kv_block_score_topk   Quest block score of every logical block, then Top-K blocks
  *   kv_paged_decode_attn  split-K softmax decode attention, dense or over selected blocks
  *   kv_decode_combine     log-sum-exp merge of the split partials
+ *   kv_append_token       store the new token's K/V and fold it into its page's meta
  *
  * The method is the select -> fetch -> compute decode step of the KVDrive paper
  * (§2.3, §4): a GPU-resident index picks the critical KV blocks, only those are
@@ -101,6 +102,24 @@ typedef struct {
 kv_status kv_block_meta_build(const kv_shape* shape, const void* k_cache, const int32_t* page_ids,
                               const int32_t* page_valid_tokens, int32_t num_page_ids, void* kmeta,
                               void* stream);
+
+/*
+ * Decode-step append (Dual-Blade background: a decode step stores the new K/V
+ * pair after attending; DirectKV review, core method 4: the KV manager appends
+ * at decode).  For every sequence b and KV head j, the new token sits at
+ * position t = seq_lens[b] - 1 (seq_lens already counts it): page
+ * p = block_table[b, t / bs], slot s = t mod bs.  Writes
+ *   K[p, j, s, :] = k_new[b, j, :],  V[p, j, s, :] = v_new[b, j, :]
+ * (k_new, v_new: [B, Hkv, D] in the storage dtype), and, when kmeta is not
+ * NULL, folds the key into the page's block meta: for s == 0 the min and max
+ * rows become k_new (a fresh page), otherwise they become the element-wise
+ * min / max with k_new.  If kmeta held the exact meta of slots 0..s-1, it then
+ * holds exactly what kv_block_meta_build computes for slots 0..s.  Distinct
+ * sequences must own distinct pages.
+ */
+kv_status kv_append_token(const kv_shape* shape, const void* k_new, const void* v_new,
+                          const int32_t* block_table, const int32_t* seq_lens, void* k_cache,
+                          void* v_cache, void* kmeta, void* stream);
 
 /* Workspace bytes kv_block_score_topk needs when scores_out is NULL (0 otherwise). */
 size_t kv_score_topk_workspace_size(const kv_shape* shape, int32_t topk_blocks);

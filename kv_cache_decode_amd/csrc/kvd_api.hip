@@ -119,6 +119,25 @@ kv_status kv_block_meta_build(const kv_shape* shape, const void* k_cache, const 
                     "kv_block_meta_build launch");
 }
 
+kv_status kv_append_token(const kv_shape* shape, const void* k_new, const void* v_new,
+                          const int32_t* block_table, const int32_t* seq_lens, void* k_cache,
+                          void* v_cache, void* kmeta, void* stream) {
+  kv_status st = check_shape(shape);
+  if (st != KV_OK) return st;
+  if (!k_new || !v_new || !block_table || !seq_lens || !k_cache || !v_cache)
+    return fail(KV_ERR_INVALID_ARG, "k_new, v_new, block_table, seq_lens, k_cache and v_cache are required");
+  if (!aligned(k_new, 16) || !aligned(v_new, 16) || !aligned(k_cache, 16) || !aligned(v_cache, 16) ||
+      (kmeta && !aligned(kmeta, 16)))
+    return fail(KV_ERR_ALIGNMENT, "k_new, v_new, k_cache, v_cache and kmeta must be 16-byte aligned");
+  if (!aligned(block_table, 4) || !aligned(seq_lens, 4))
+    return fail(KV_ERR_ALIGNMENT, "block_table and seq_lens must be 4-byte aligned");
+  return hip_status(kvd::launch_append_token(shape->dtype, shape->head_dim, k_new, v_new,
+                                             block_table, seq_lens, shape->num_seqs,
+                                             shape->num_kv_heads, shape->max_blocks_per_seq,
+                                             k_cache, v_cache, kmeta, (hipStream_t)stream),
+                    "kv_append_token launch");
+}
+
 size_t kv_score_topk_workspace_size(const kv_shape* shape, int32_t topk_blocks) {
   (void)topk_blocks;
   if (check_shape(shape) != KV_OK) return 0;

@@ -81,6 +81,49 @@ __global__ __launch_bounds__(WAVES * kWave) void block_meta_kernel(
   }
 }
 
+// ============================================================== decode-step append
+//
+// One wave per (sequence, KV head); lane c < LPR owns channel chunk c.  The
+// new key and value rows are stored into their slot, and the key is folded
+// into the page's min/max rows (a fresh page, slot 0, starts them over).
+
+template <typename DT, int D>
+__global__ __launch_bounds__(kWave) void append_token_kernel(
+    const void* __restrict__ k_new, const void* __restrict__ v_new,
+    const int32_t* __restrict__ block_table, const int32_t* __restrict__ seq_lens, int Hkv,
+    int maxN, void* __restrict__ k_cache, void* __restrict__ v_cache, void* __restrict__ kmeta) {
+  using G_ = RowGeom<DT, D>;
+  using St = typename DT::storage;
+  constexpr int E = G_::E, LPR = G_::LPR;
+  const int c = threadIdx.x;
+  if (c >= LPR) return;
+  const int j = blockIdx.x, b = blockIdx.y;
+  const int t = seq_lens[b] - 1;
+  const int s = t % kBlockSize;
+  const size_t tile = (size_t)block_table[(size_t)b * maxN + t / kBlockSize] * Hkv + j;
+  const size_t src = ((size_t)b * Hkv + j) * D + (size_t)c * E;
+  const size_t dst = (tile * kBlockSize + s) * D + (size_t)c * E;
+  const uint4 kw = load16(static_cast<const St*>(k_new) + src);
+  store16(static_cast<St*>(k_cache) + dst, kw);
+  store16(static_cast<St*>(v_cache) + dst, load16(static_cast<const St*>(v_new) + src));
+  if (kmeta) {
+    St* m = static_cast<St*>(kmeta) + tile * 2 * D + (size_t)c * E;
+    if (s == 0) {
+      store16(m, kw);
+      store16(m + D, kw);
+    } else {
+      float f[E], mn[E], mx[E];
+      DT::widen(kw, f);
+      DT::widen(load16(m), mn);
+      DT::widen(load16(m + D), mx);
+#pragma unroll
+      for (int e = 0; e < E; ++e) { mn[e] = fminf(mn[e], f[e]); mx[e] = fmaxf(mx[e], f[e]); }
+      store16(m, DT::narrow_exact(mn));
+      store16(m + D, DT::narrow_exact(mx));
+    }
+  }
+}
+
 // ============================================================== block score
 //
 // sigma_h = sum_c max(q_hc kmin_c, q_hc kmax_c) = sum_c (q+_hc kmax_c + q-_hc kmin_c)
@@ -226,12 +269,29 @@ __global__ __launch_bounds__(1024) void topk_kernel(const float* __restrict__ sc
 
   uint32_t key[EPT];
   uint32_t kmn = 0xFFFFFFFFu, kmx = 0u;
+  float sc[EPT];
+  const int n0 = tid * EPT;
+  if constexpr (EPT % 4 == 0) {
+    // 16-byte loads of the thread's contiguous scores when the row allows it
+    if ((reinterpret_cast<uintptr_t>(row) & 15u) == 0 && n0 + EPT <= maxN) {
+#pragma unroll
+      for (int r = 0; r < EPT; r += 4) {
+        const float4 v = *reinterpret_cast<const float4*>(row + n0 + r);
+        sc[r] = v.x; sc[r + 1] = v.y; sc[r + 2] = v.z; sc[r + 3] = v.w;
+      }
+    } else {
+#pragma unroll
+      for (int r = 0; r < EPT; ++r) sc[r] = (n0 + r < maxN) ? row[n0 + r] : 0.0f;
+    }
+  } else {
+#pragma unroll
+    for (int r = 0; r < EPT; ++r) sc[r] = (n0 + r < maxN) ? row[n0 + r] : 0.0f;
+  }
 #pragma unroll
   for (int r = 0; r < EPT; ++r) {
-    const int n = tid * EPT + r;
     key[r] = 0u;
-    if (n < nb) {
-      key[r] = score_key(row[n]);  // valid keys are >= key(-inf) > 0
+    if (n0 + r < nb) {
+      key[r] = score_key(sc[r]);  // valid keys are >= key(-inf) > 0
       kmn = min(kmn, key[r]);
       kmx = max(kmx, key[r]);
     }
@@ -329,6 +389,20 @@ hipError_t launch_block_meta(int dtype, int D, const void* k_cache, const int32_
       const int grid = (int)std::min<long>(want, (long)cu_count() * KVD_META_WGS_PER_CU);
       hipLaunchKernelGGL((block_meta_kernel<DT, DD, WAVES>), dim3(grid), dim3(WAVES * kWave), 0,
                          stream, k_cache, page_ids, valid_tokens, n_ids, Hkv, kmeta);
+      return hipGetLastError();
+    });
+  });
+}
+
+hipError_t launch_append_token(int dtype, int D, const void* k_new, const void* v_new,
+                               const int32_t* block_table, const int32_t* seq_lens, int B,
+                               int Hkv, int maxN, void* k_cache, void* v_cache, void* kmeta,
+                               hipStream_t stream) {
+  return with_dtype(dtype, [&](auto dt) {
+    return with_dim(D, [&](auto d) {
+      hipLaunchKernelGGL((append_token_kernel<decltype(dt), decltype(d)::value>), dim3(Hkv, B),
+                         dim3(kWave), 0, stream, k_new, v_new, block_table, seq_lens, Hkv, maxN,
+                         k_cache, v_cache, kmeta);
       return hipGetLastError();
     });
   });

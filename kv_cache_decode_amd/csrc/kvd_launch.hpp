@@ -13,6 +13,11 @@ hipError_t launch_block_meta(int dtype, int D, const void* k_cache, const int32_
                              const int32_t* valid_tokens, int n_ids, int Hkv, void* kmeta,
                              hipStream_t stream);
 
+hipError_t launch_append_token(int dtype, int D, const void* k_new, const void* v_new,
+                               const int32_t* block_table, const int32_t* seq_lens, int B,
+                               int Hkv, int maxN, void* k_cache, void* v_cache, void* kmeta,
+                               hipStream_t stream);
+
 hipError_t launch_block_score(int dtype, int D, int G, const void* q, const void* kmeta,
                               const int32_t* block_table, const int32_t* seq_lens, int B, int Hq,
                               int Hkv, int maxN, float* scores, hipStream_t stream);

@@ -25,7 +25,7 @@ DTYPE_CODES = {"f32": KV_F32, "f16": KV_F16, "bf16": KV_BF16}
 
 # every symbol the header declares
 EXPORTS = (
-    "kv_block_meta_build", "kv_score_topk_workspace_size", "kv_block_score_topk",
+    "kv_block_meta_build", "kv_append_token", "kv_score_topk_workspace_size", "kv_block_score_topk",
     "kv_auto_num_splits", "kv_paged_decode_attn", "kv_decode_combine", "kv_host_alloc",
     "kv_host_free", "kv_status_string", "kv_last_error_message",
 )
@@ -75,6 +75,7 @@ def _load() -> ctypes.CDLL:
     S = ctypes.POINTER(KVShape)
     sig = {
         "kv_block_meta_build": (I32, [S, P, P, P, I32, P, P]),
+        "kv_append_token": (I32, [S, P, P, P, P, P, P, P, P]),
         "kv_score_topk_workspace_size": (SZ, [S, I32]),
         "kv_block_score_topk": (I32, [S, P, P, P, P, I32, P, P, P, P, SZ, P]),
         "kv_auto_num_splits": (I32, [S, I32]),
@@ -132,6 +133,13 @@ def kv_block_meta_build(shape: KVShape, k_cache: Buf, page_ids: Buf, page_valid_
     _check(_lib.kv_block_meta_build(ctypes.byref(shape), _p(k_cache), _p(page_ids),
                                     _p(page_valid_tokens), num_page_ids, _p(kmeta),
                                     _stream(stream)))
+
+
+def kv_append_token(shape: KVShape, k_new: Buf, v_new: Buf, block_table: Buf, seq_lens: Buf,
+                    k_cache: Buf, v_cache: Buf, kmeta: Buf = None, stream=None) -> None:
+    _check(_lib.kv_append_token(ctypes.byref(shape), _p(k_new), _p(v_new), _p(block_table),
+                                _p(seq_lens), _p(k_cache), _p(v_cache), _p(kmeta),
+                                _stream(stream)))
 
 
 def kv_score_topk_workspace_size(shape: KVShape, topk_blocks: int) -> int:

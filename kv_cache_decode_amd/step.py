@@ -93,6 +93,16 @@ class DeviceWorkload:
         self._parts = {}
         self.sel = self.sel_count = None
         self.topk = None
+        # the K/V rows of each sequence's newest token (position L_b - 1):
+        # appending them again leaves the cache and its index unchanged
+        last_k = np.empty((spec.num_seqs, Hkv, D), dtype=data.k_raw.dtype)
+        last_v = np.empty_like(last_k)
+        for b in range(spec.num_seqs):
+            t = spec.seq_lens[b] - 1
+            p = data.block_table[b, t // bs]
+            last_k[b], last_v[b] = data.k_raw[p, :, t % bs], data.v_raw[p, :, t % bs]
+        self.last_k = storage_tensor(last_k, dt).to(dev)
+        self.last_v = storage_tensor(last_v, dt).to(dev)
 
     # ------------------------------------------------------------ buffers
     def partials(self, num_splits: int):
@@ -119,6 +129,12 @@ class DeviceWorkload:
     def meta_build(self, stream=None):
         kd.kv_block_meta_build(self.shape, self.k_cache, self.page_ids, self.page_valid,
                                int(self.page_ids.numel()), self.kmeta, stream)
+
+    def append(self, k_new=None, v_new=None, stream=None):
+        """Store one new token per sequence at position seq_lens - 1 and fold it into the meta."""
+        kd.kv_append_token(self.shape, self.last_k if k_new is None else k_new,
+                           self.last_v if v_new is None else v_new, self.block_table,
+                           self.seq_lens, self.k_cache, self.v_cache, self.kmeta, stream)
 
     def score_topk(self, k: int, stream=None):
         if self.topk != k or self.sel is None:

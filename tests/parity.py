@@ -44,12 +44,14 @@ def assert_rows_close(got: np.ndarray, ref: np.ndarray, tol: float, what: str = 
 
 
 def page_lists(data: wl.WorkloadData):
-    spec = data.spec
+    """(page ids, valid slot counts) of every page the sequences' current lengths use."""
+    bs = data.spec.block_size
     ids, val = [], []
-    for b in range(spec.num_seqs):
-        for n in range(spec.blocks(b)):
+    for b in range(data.spec.num_seqs):
+        L = int(data.seq_lens[b])
+        for n in range(-(-L // bs)):
             ids.append(int(data.block_table[b, n]))
-            val.append(min(spec.block_size, spec.seq_lens[b] - n * spec.block_size))
+            val.append(min(bs, L - n * bs))
     return np.array(ids, np.int32), np.array(val, np.int32)
 
 

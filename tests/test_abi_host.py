@@ -180,3 +180,15 @@ def test_one_hip_runtime_per_process():
     maps = open("/proc/self/maps").read()
     libs = set(line.split()[-1] for line in maps.splitlines() if "libamdhip64" in line)
     assert len(libs) == 1, libs
+
+
+def test_append_argument_checks():
+    s = shape()
+    f = kd.kv_append_token
+    expect(kd.KV_ERR_INVALID_ARG, lambda stream: f(s, None, A16, A16, A16, A16, A16, A16, stream=stream))
+    expect(kd.KV_ERR_INVALID_ARG, lambda stream: f(s, A16, A16, A16, A16, A16, None, A16, stream=stream))
+    expect(kd.KV_ERR_ALIGNMENT, lambda stream: f(s, A4, A16, A16, A16, A16, A16, A16, stream=stream))
+    expect(kd.KV_ERR_ALIGNMENT, lambda stream: f(s, A16, A16, A16, A16, A16, A16, A4, stream=stream))
+    expect(kd.KV_ERR_ALIGNMENT, lambda stream: f(s, A16, A16, ODD, A16, A16, A16, None, stream=stream))
+    expect(kd.KV_ERR_UNSUPPORTED, lambda stream: f(shape(head_dim=80), A16, A16, A16, A16, A16, A16,
+                                                   None, stream=stream))
