@@ -195,12 +195,49 @@ def run_gpu(args, spec, data):
         log(f"[bench] graph capture failed ({e}); timing eager launches")
         launch = "eager"
         total_ms, wall = time_loop(lambda i: step(copies[i % len(copies)]))
+    # the per-token decode steps on their own, each one HIP graph per copy:
+    # sparse = append + score/Top-K + sparse attention + merge,
+    # dense  = append + dense attention + merge
+    def decode_sparse(c):
+        c.append()
+        c.score_topk(k)
+        c.attention(sparse=True, num_splits=s_sparse)
+        c.combine(s_sparse)
+
+    def decode_dense(c):
+        c.append()
+        c.attention(sparse=False, num_splits=s_dense)
+        c.combine(s_dense)
+
+    decode_us = {}
+    for name, fn in (("sparse", decode_sparse), ("dense", decode_dense)):
+        try:
+            gs = []
+            side = torch.cuda.Stream()
+            for c in copies:
+                side.wait_stream(torch.cuda.current_stream())
+                with torch.cuda.stream(side):
+                    fn(c)
+                torch.cuda.current_stream().wait_stream(side)
+                g_ = torch.cuda.CUDAGraph()
+                with torch.cuda.graph(g_):
+                    fn(c)
+                gs.append(g_)
+            for i in range(args.warmup):
+                gs[i % len(gs)].replay()
+            ms_, _ = time_loop(lambda i: gs[i % len(gs)].replay())
+            del gs
+        except RuntimeError:
+            ms_, _ = time_loop(lambda i: fn(copies[i % len(copies)]))
+        decode_us[name] = ms_ * 1e3 / args.steps
+
     for c in copies:
         c.close()
     del copies
     torch.cuda.empty_cache()
     return {
         "total_ms": total_ms, "wall_s": wall, "stage_ms": per_stage_ms,
+        "decode_us": decode_us,
         "s_sparse": s_sparse, "s_dense": s_dense, "launch": launch,
         "dense_attn_loop_us": dense_loop_ms * 1e3 / args.steps,
         "eager_ms_per_step": eager_ms / args.steps,
@@ -427,10 +464,6 @@ def main():
     st = g["stage_ms"]
     stage_us = {s: st[s] * 1e3 for s in st}
     stage_gbps = {s: sb[s] / (st[s] * 1e-3) / 1e9 for s in st}
-    # a decode step: append the new token, then (sparse) score + Top-K + attention +
-    # merge, or (dense) attention + merge
-    sparse_ms = st["append"] + st["score_topk"] + st["sparse_attn"] + st["sparse_combine"]
-    dense_ms = st["append"] + st["dense_attn"] + st["dense_combine"]
     dense_us = g["dense_attn_loop_us"]
     dense_gbps = sb["dense_attn"] / (dense_us * 1e-6) / 1e9
     traffic = measured_traffic()
@@ -475,8 +508,16 @@ def main():
         },
         "eager_ms_per_step": g["eager_ms_per_step"],
         "frac_of_hbm_peak": step_bytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBPS,
-        "decode_steps_per_s": {"sparse": 1e3 / sparse_ms, "dense": 1e3 / dense_ms,
+        # one decode step of this layer, timed on its own as a HIP graph replay
+        "decode_steps_per_s": {"sparse": 1e6 / g["decode_us"]["sparse"],
+                               "dense": 1e6 / g["decode_us"]["dense"],
                                "full_step": 1e3 / ms},
+        "decode_step_us": g["decode_us"],
+        "decode_step_gbps": {
+            "sparse": (sb["append"] + sb["score_topk"] + sb["sparse_attn"] + sb["sparse_combine"])
+                      / (g["decode_us"]["sparse"] * 1e-6) / 1e9,
+            "dense": (sb["append"] + sb["dense_attn"] + sb["dense_combine"])
+                     / (g["decode_us"]["dense"] * 1e-6) / 1e9},
         "step_bytes": step_bytes,
         "stage_bytes": sb,
         "stage_us": stage_us,
