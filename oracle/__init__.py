@@ -11,6 +11,9 @@ Functions (each computed as oracle.c states it):
 * ``head_scores``     Quest score per (sequence, query head, block)  (KVDrive §2.2)
 * ``group_scores``    max of the head scores over each GQA group
 * ``topk``            rank-count Top-K, lower index wins ties, ascending output
+* ``block_mean``      mean key per (page, KV head)             (KVDrive §2.3, §4)
+* ``head_scores_mean``  q . mean key per (sequence, query head, block)
+* ``select``          Top-K with the first / last tokens' blocks forced in  (KVDrive §9.1)
 * ``attention``       softmax decode attention, dense or over selected blocks
                       (Dual-Blade background; KVDrive §2.3 step 3)
 * ``attention_splits``  the same on each contiguous chunk of the block list
@@ -49,6 +52,9 @@ def _load():
     lib.oracle_block_meta.argtypes = [_D, _int, _int, _int, _I, _I, _int, _D]
     lib.oracle_head_scores.argtypes = [_D, _D, _I, _I, _int, _int, _int, _int, _int, _int, _D]
     lib.oracle_group_scores.argtypes = [_D, _int, _int, _int, _int, _D]
+    lib.oracle_block_mean.argtypes = [_D, _int, _int, _int, _I, _I, _int, _D]
+    lib.oracle_head_scores_mean.argtypes = [_D, _D, _I, _I, _int, _int, _int, _int, _int, _int, _D]
+    lib.oracle_select.argtypes = [_D, _I, _int, _int, _int, _int, _int, _int, _int, _I, _I]
     lib.oracle_topk.argtypes = [_D, _I, _int, _int, _int, _int, _int, _I, _I]
     lib.oracle_attention.argtypes = [_D, _D, _D, _I, _I, _I, _I, _int, _int, _int, _int, _int,
                                      _int, _int, ctypes.c_double, _D, _D]
@@ -56,6 +62,7 @@ def _load():
                                             _int, _int, _int, ctypes.c_double, _int, _D, _D, _D]
     lib.oracle_combine.argtypes = [_int, _int, _int, _int, _D, _D, _D, _D, _D]
     for f in ("oracle_block_meta", "oracle_head_scores", "oracle_group_scores", "oracle_topk",
+              "oracle_block_mean", "oracle_head_scores_mean", "oracle_select",
               "oracle_attention", "oracle_attention_splits", "oracle_combine"):
         getattr(lib, f).restype = None
     _lib = lib
@@ -105,6 +112,43 @@ def head_scores(q, kmeta, block_table, seq_lens, block_size: int) -> np.ndarray:
     _load().oracle_head_scores(_pd(q), _pd(km), _pi(bt), _pi(sl), B, Hq, Hkv, D, block_size,
                                maxN, _pd(out))
     return out
+
+
+def block_mean(k_pool, page_ids, valid_tokens, kmean: Optional[np.ndarray] = None) -> np.ndarray:
+    """kmean [P, Hkv, D]: the average key of each listed page's first ``valid_tokens`` slots."""
+    k = _f64(k_pool)
+    P, Hkv, bs, D = k.shape
+    ids, val = _i32(page_ids), _i32(valid_tokens)
+    out = np.zeros((P, Hkv, D)) if kmean is None else _f64(kmean).copy()
+    _load().oracle_block_mean(_pd(k), Hkv, bs, D, _pi(ids), _pi(val), len(ids), _pd(out))
+    return out
+
+
+def head_scores_mean(q, kmean, block_table, seq_lens, block_size: int) -> np.ndarray:
+    """q . kmean per (b, query head, logical block) [B, Hq, maxN]; -inf past N_b."""
+    q, km = _f64(q), _f64(kmean)
+    bt, sl = _i32(block_table), _i32(seq_lens)
+    B, Hq, D = q.shape
+    Hkv = km.shape[1]
+    maxN = bt.shape[1]
+    out = np.empty((B, Hq, maxN))
+    _load().oracle_head_scores_mean(_pd(q), _pd(km), _pi(bt), _pi(sl), B, Hq, Hkv, D, block_size,
+                                    maxN, _pd(out))
+    return out
+
+
+def select(group_scores_, seq_lens, block_size: int, k: int, sink: int = 0, local: int = 0):
+    """Selection with every block that holds one of the first ``sink`` or the last
+    ``local`` tokens forced in:
+    (sel int32 [B, Hkv, k] ascending, -1 padded;  sel_count int32 [B, Hkv])."""
+    gs = _f64(group_scores_)
+    sl = _i32(seq_lens)
+    B, Hkv, maxN = gs.shape
+    sel = np.empty((B, Hkv, k), dtype=np.int32)
+    cnt = np.empty((B, Hkv), dtype=np.int32)
+    _load().oracle_select(_pd(gs), _pi(sl), B, Hkv, maxN, block_size, k, sink, local, _pi(sel),
+                          _pi(cnt))
+    return sel, cnt
 
 
 def group_scores(head_scores_, num_kv_heads: int) -> np.ndarray:

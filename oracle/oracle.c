@@ -36,7 +36,15 @@
  *  - attention logit z_t = scale * (q . k_t), softmax over the token set;
  *  - split s of a list of n blocks covers list positions
  *    [s*c, min((s+1)*c, n)) with c = ceil(n / S); an empty split has
- *    m = -inf, l = 0, o = 0.
+ *    m = -inf, l = 0, o = 0;
+ *  - mean-key index (KVDrive §2.3 spatial blocking, §4 overview: a page's
+ *    average key as its representative): kmean = average of the valid keys,
+ *    block score q . kmean, then the same group max and Top-K;
+ *  - forced tokens (KVDrive §9.1 setup: the sparse systems always keep the
+ *    first tokens and the most recent tokens): every block holding one of the
+ *    first `sink` or the last `local` tokens of a sequence is selected and
+ *    counts against the budget K; the other K_eff - |forced| places go to the
+ *    best of the remaining blocks.
  */
 #include <math.h>
 #include <stdint.h>
@@ -126,6 +134,56 @@ void oracle_head_scores(const double* q, const double* kmeta, const int32_t* blo
 }
 
 /*
+ * Mean-key representative (KVDrive §2.3, §4): kmean[p, j, c] is the average of
+ * K[p, j, s, c] over the first valid_tokens[i] slots of each listed page.
+ * kmean layout [P, Hkv, D].
+ */
+void oracle_block_mean(const double* k_pool, int Hkv, int bs, int D,
+                       const int32_t* page_ids, const int32_t* valid_tokens, int n_ids,
+                       double* kmean) {
+#pragma omp parallel for schedule(static)
+  for (int i = 0; i < n_ids; ++i) {
+    const i64 p = page_ids[i];
+    const int nv = valid_tokens[i];
+    for (int j = 0; j < Hkv; ++j) {
+      double* out = kmean + (p * Hkv + j) * (i64)D;
+      for (int c = 0; c < D; ++c) {
+        double sum = 0.0;
+        for (int s = 0; s < nv; ++s) sum += pool_row(k_pool, p, j, s, Hkv, bs, D)[c];
+        out[c] = sum / nv;
+      }
+    }
+  }
+}
+
+/*
+ * Per-query-head score against the mean-key index: sigma[b,h,n] = q[b,h] . kmean[p,j]
+ * with p = block_table[b,n], j = h / G; -inf for n >= N_b.
+ */
+void oracle_head_scores_mean(const double* q, const double* kmean, const int32_t* block_table,
+                             const int32_t* seq_lens, int B, int Hq, int Hkv, int D, int bs,
+                             int maxN, double* head_scores) {
+  const int G = Hq / Hkv;
+#pragma omp parallel for collapse(2) schedule(static)
+  for (int b = 0; b < B; ++b) {
+    for (int h = 0; h < Hq; ++h) {
+      const i64 nb = ceil_div(seq_lens[b], bs);
+      const int j = h / G;
+      const double* qh = q + ((i64)b * Hq + h) * D;
+      double* out = head_scores + ((i64)b * Hq + h) * maxN;
+      for (i64 n = 0; n < maxN; ++n) {
+        if (n >= nb) { out[n] = -INFINITY; continue; }
+        const i64 p = block_table[(i64)b * maxN + n];
+        const double* km = kmean + (p * Hkv + j) * (i64)D;
+        double acc = 0.0;
+        for (int c = 0; c < D; ++c) acc += qh[c] * km[c];
+        out[n] = acc;
+      }
+    }
+  }
+}
+
+/*
  * O3 group score: Sigma[b,j,n] = max over the G query heads h with h / G == j
  * of sigma[b,h,n].
  */
@@ -166,6 +224,54 @@ void oracle_topk(const double* group_scores, const int32_t* seq_lens, int B, int
         for (i64 m = 0; m < nb; ++m)
           if (s[m] > s[n] || (s[m] == s[n] && m < n)) ++rank;
         if (rank < keff) out[w++] = (int32_t)n;
+      }
+      for (i64 r = w; r < K; ++r) out[r] = -1;
+      sel_count[(i64)b * Hkv + j] = (int32_t)w;
+    }
+  }
+}
+
+/*
+ * Selection with forced tokens (KVDrive §9.1).  Block n < N_b covers tokens
+ * [n*bs, min((n+1)*bs, L)); it is forced when it holds one of the first `sink`
+ * tokens (n*bs < sink) or one of the last `local` tokens (local > 0 and
+ * (n+1)*bs > L - local).  All forced blocks are selected; of the other blocks,
+ * those whose rank among the non-forced blocks (score descending, lower index
+ * first on ties) is below K_eff - #forced are selected too, K_eff = min(K, N_b).
+ * Output ascending, -1 padded.  The caller keeps #forced <= K.  With
+ * sink = local = 0 this is oracle_topk.
+ */
+static int is_forced(i64 n, i64 L, int bs, int sink, int local) {
+  return n * bs < sink || (local > 0 && (n + 1) * bs > L - local);
+}
+
+void oracle_select(const double* group_scores, const int32_t* seq_lens, int B, int Hkv, int maxN,
+                   int bs, int K, int sink, int local, int32_t* sel, int32_t* sel_count) {
+#pragma omp parallel for collapse(2) schedule(dynamic)
+  for (int b = 0; b < B; ++b) {
+    for (int j = 0; j < Hkv; ++j) {
+      const i64 L = seq_lens[b];
+      const i64 nb = ceil_div(L, bs);
+      const i64 keff = (K < nb) ? K : nb;
+      const double* s = group_scores + ((i64)b * Hkv + j) * maxN;
+      int32_t* out = sel + ((i64)b * Hkv + j) * K;
+      i64 n_forced = 0;
+      for (i64 n = 0; n < nb; ++n) n_forced += is_forced(n, L, bs, sink, local);
+      const i64 free_slots = keff - n_forced;
+      i64 w = 0;
+      for (i64 n = 0; n < nb; ++n) {
+        int take;
+        if (is_forced(n, L, bs, sink, local)) {
+          take = 1;
+        } else {
+          i64 rank = 0;
+          for (i64 m = 0; m < nb; ++m) {
+            if (is_forced(m, L, bs, sink, local)) continue;
+            if (s[m] > s[n] || (s[m] == s[n] && m < n)) ++rank;
+          }
+          take = rank < free_slots;
+        }
+        if (take) out[w++] = (int32_t)n;
       }
       for (i64 r = w; r < K; ++r) out[r] = -1;
       sel_count[(i64)b * Hkv + j] = (int32_t)w;

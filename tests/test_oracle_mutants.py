@@ -28,12 +28,22 @@ MUTANTS = [
     ("attn_drops_scale", "const double z = scale * dot;", "const double z = dot;", 0),
     ("attn_token_off_by_one", "if (t >= L) break;", "if (t > L) break;", 0),
     ("attn_value_is_key", "const double* v = pool_row(v_pool", "const double* v = pool_row(k_pool", 0),
-    ("attn_wrong_kv_head", "const int j = h / G;", "const int j = h % Hkv;", 1),
+    ("attn_wrong_kv_head", "const int j = h / G;", "const int j = h % Hkv;", 2),
     ("attn_unnormalised", "for (int c = 0; c < D; ++c) o[c] /= l;", "", 0),
     ("split_chunks_overlap", "i64 p0 = (i64)s * chunk, p1 = p0 + chunk;",
      "i64 p0 = (i64)s * chunk, p1 = p0 + chunk + 1;", 0),
     ("combine_drops_l", "const double w = part_l[r * S + s] * exp(ms - M);",
      "const double w = exp(ms - M);", 0),
+    ("mean_divides_by_block_size", "out[c] = sum / nv;", "out[c] = sum / bs;", 0),
+    ("mean_counts_every_slot", "for (int s = 0; s < nv; ++s) sum +=", "for (int s = 0; s < bs; ++s) sum +=", 0),
+    ("mean_score_wrong_head_map", "const int j = h / G;", "const int j = h % Hkv;", 1),
+    ("mean_score_uses_the_first_page", "const i64 p = block_table[(i64)b * maxN + n];\n        const double* km",
+     "const i64 p = block_table[(i64)b * maxN];\n        const double* km", 0),
+    ("forced_local_off_by_one", "(n + 1) * bs > L - local", "(n + 1) * bs >= L - local", 0),
+    ("forced_sink_inclusive", "n * bs < sink", "n * bs <= sink", 0),
+    ("forced_not_counted_against_k", "const i64 free_slots = keff - n_forced;",
+     "const i64 free_slots = keff;", 0),
+    ("forced_blocks_compete_for_rank", "if (is_forced(m, L, bs, sink, local)) continue;", "", 0),
     ("combine_lse_drops_max", "if (lse) lse[r] = M + log(wsum);", "if (lse) lse[r] = log(wsum);", 0),
 ]
 

@@ -460,3 +460,153 @@ def test_split_then_combine_equals_unsplit(S, sparse):
     out, lse = oracle.combine(*parts)
     np.testing.assert_allclose(out, ref, rtol=1e-12, atol=1e-14)
     np.testing.assert_allclose(lse, lref, rtol=1e-13)
+
+
+# ---------------------------------------------------------------- selection variants
+# mean-key index (KVDrive §2.3 spatial blocking, §4) and forced sink / local
+# tokens (KVDrive §9.1)
+
+VARIANTS = os.path.join(os.path.dirname(__file__), "golden", "selection_variants.json")
+
+
+@pytest.fixture(scope="module")
+def variants():
+    with open(VARIANTS) as f:
+        return json.load(f)
+
+
+def full_mean(data):
+    ids, val = page_lists(data)
+    return oracle.block_mean(data.k64(), ids, val)
+
+
+def test_mean_golden(variants):
+    g = variants["mean_score"]
+    k = np.array(g["k_slots"], np.float64).reshape(1, 1, g["block_size"], g["head_dim"])
+    km = oracle.block_mean(k, [0], [g["valid_tokens"]])
+    assert km[0, 0].tolist() == g["kmean"]
+    for qv, want in zip(g["queries"], g["scores"]):
+        s = oracle.head_scores_mean(np.array(qv, np.float64).reshape(1, 1, -1), km,
+                                    np.zeros((1, 1), np.int32), np.array([3], np.int32),
+                                    g["block_size"])
+        assert s[0, 0, 0] == want
+
+
+@pytest.mark.parametrize("dtype", ["f32", "f16", "bf16"])
+def test_mean_matches_numpy_reduction(dtype):
+    data = mk(B=3, Hq=6, Hkv=3, D=16, lens=(45, 16, 3), dtype=dtype, seed=31, extra_pages=2)
+    k64 = data.k64()
+    ids, val = page_lists(data)
+    km = oracle.block_mean(k64, ids, val)
+    for p, nv in zip(ids, val):
+        np.testing.assert_allclose(km[p], k64[p, :, :nv].mean(axis=1), rtol=1e-15, atol=1e-15)
+    untouched = np.setdiff1d(np.arange(k64.shape[0]), ids)
+    assert untouched.size and np.all(km[untouched] == 0)
+
+
+def test_mean_score_is_the_average_token_dot():
+    """Linearity: q . mean(k_t) = mean_t (q . k_t), with the dots taken directly
+    from the token rows through the block table (GQA head map h // G)."""
+    data = mk(B=2, Hq=6, Hkv=2, D=8, lens=(53, 20), seed=32)
+    q64, k64 = data.q64(), data.k64()
+    hs = oracle.head_scores_mean(q64, full_mean(data), data.block_table, data.seq_lens, 16)
+    G = 3
+    for b in range(2):
+        nb = data.spec.blocks(b)
+        for h in range(6):
+            for n in range(nb):
+                rows = gather(k64, data, b, h // G, [n])
+                want = float(np.mean(rows @ q64[b, h]))
+                assert abs(hs[b, h, n] - want) <= 1e-13 * (1 + np.abs(rows @ q64[b, h]).sum())
+            assert np.all(np.isneginf(hs[b, h, nb:]))
+
+
+def test_mean_score_single_token_block_is_the_dot_product():
+    data = mk(B=1, Hq=2, Hkv=1, D=8, lens=(48,), seed=33, block_size=1)
+    q64, k64 = data.q64(), data.k64()
+    ids, val = page_lists(data)
+    km = oracle.block_mean(k64, ids, val)
+    hs = oracle.head_scores_mean(q64, km, data.block_table, data.seq_lens, 1)
+    for h in range(2):
+        for n in range(48):
+            p = data.block_table[0, n]
+            assert hs[0, h, n] == pytest.approx(float(q64[0, h] @ k64[p, 0, 0]), rel=1e-14,
+                                                abs=1e-14)
+
+
+def test_mean_score_is_bounded_by_the_quest_score():
+    """The average of q . k_t never exceeds the largest q . k_t, which the
+    Quest score bounds from above."""
+    data = mk(B=2, Hq=4, Hkv=2, D=16, lens=(70, 33), seed=34)
+    mean_s = oracle.head_scores_mean(data.q64(), full_mean(data), data.block_table,
+                                     data.seq_lens, 16)
+    quest = oracle.head_scores(data.q64(), full_meta(data), data.block_table, data.seq_lens, 16)
+    fin = np.isfinite(quest)
+    assert np.all(mean_s[fin] <= quest[fin] + 1e-12)
+
+
+def test_forced_sets_golden(variants):
+    g = variants["forced"]
+    bs = g["block_size"]
+    for case in g["cases"]:
+        L = case["seq_len"]
+        nb = -(-L // bs)
+        # the scores put every block at -1 except none: K = 1 leaves only forced blocks
+        sel, cnt = oracle.select(np.full((1, 1, nb), -1.0), np.array([L], np.int32), bs,
+                                 len(case["forced"]), g["sink_tokens"], g["local_tokens"])
+        assert sel[0, 0, :cnt[0, 0]].tolist() == case["forced"]
+
+
+def test_select_golden(variants):
+    for case in variants["forced"]["select_cases"]:
+        s = np.array(case["scores"], np.float64).reshape(1, 1, -1)
+        sel, cnt = oracle.select(s, np.array([case["seq_len"]], np.int32), 16, case["k"],
+                                 case["sink_tokens"], case["local_tokens"])
+        want = case["selected"]
+        assert cnt[0, 0] == len(want)
+        assert sel[0, 0, :len(want)].tolist() == want
+        assert np.all(sel[0, 0, len(want):] == -1)
+
+
+def _forced_blocks(L, bs, sink, local):
+    """Blocks holding any of the first ``sink`` or the last ``local`` token indices."""
+    toks = set(range(min(sink, L))) | set(range(max(L - local, 0), L))
+    return {t // bs for t in toks}
+
+
+@pytest.mark.parametrize("seed", range(4))
+def test_select_matches_a_library_sort(seed):
+    """Forced blocks by token enumeration, the rest by Python's sort (score
+    descending, index ascending); heavy ties from integer scores."""
+    rng = np.random.default_rng(200 + seed)
+    B, Hkv, bs = 4, 2, 16
+    lens = rng.integers(1, 30 * bs, size=B).astype(np.int32)
+    maxN = int(max(-(-lens // bs)))
+    gs = rng.integers(-3, 4, size=(B, Hkv, maxN)).astype(np.float64)
+    for sink, local in ((4, 64), (0, 17), (33, 0), (1, 1)):
+        k_min = -(-sink // bs) + -(-local // bs) + 1
+        for k in (k_min, k_min + 3, 40):
+            sel, cnt = oracle.select(gs, lens, bs, k, sink, local)
+            for b in range(B):
+                L = int(lens[b])
+                nb = -(-L // bs)
+                forced = _forced_blocks(L, bs, sink, local)
+                rest = [n for n in range(nb) if n not in forced]
+                free = min(k, nb) - len(forced)
+                assert free >= 0
+                for j in range(Hkv):
+                    best = sorted(rest, key=lambda n: (-gs[b, j, n], n))[:free]
+                    want = sorted(forced | set(best))
+                    assert cnt[b, j] == len(want) == min(k, nb)
+                    assert sel[b, j, :cnt[b, j]].tolist() == want
+                    assert np.all(sel[b, j, cnt[b, j]:] == -1)
+
+
+def test_select_without_forcing_is_topk():
+    rng = np.random.default_rng(9)
+    gs = rng.standard_normal((2, 3, 40))
+    lens = np.array([640, 333], np.int32)
+    for k in (1, 5, 40, 64):
+        a = oracle.select(gs, lens, 16, k)
+        b = oracle.topk(gs, lens, 16, k)
+        assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
