@@ -80,6 +80,23 @@ def stage_bytes(spec, topk: int, s_sparse: int, s_dense: int) -> dict:
     }
 
 
+def variant_bytes(spec, topk: int) -> dict:
+    """Algorithmic bytes of the selection variants: the mean-key index holds one
+    fp32 row of D per (page, KV head)."""
+    eb = spec.elem_bytes
+    bs, D, B, Hq, Hkv = spec.block_size, spec.head_dim, spec.num_seqs, spec.num_q_heads, spec.num_kv_heads
+    blocks, maxN = spec.used_pages, spec.max_blocks
+    mean_row, meta_row = 4 * D, 2 * D * eb
+    rest = B * Hq * D * eb + blocks * Hkv * 4 + 2 * B * Hkv * maxN * 4 + B * Hkv * (topk + 1) * 4
+    return {
+        "mean_build": blocks * Hkv * (bs * D * eb + mean_row) + blocks * 8,
+        "meta_build": blocks * Hkv * (bs * D * eb + meta_row) + blocks * 8,
+        "mean_select_forced": blocks * Hkv * mean_row + rest,
+        "minmax_select_forced": blocks * Hkv * meta_row + rest,
+        "minmax_select": blocks * Hkv * meta_row + rest,
+    }
+
+
 # ---------------------------------------------------------------- HBM traffic from counters
 
 def source_digest() -> str:
@@ -209,8 +226,8 @@ def run_gpu(args, spec, data):
         c.attention(sparse=False, num_splits=s_dense)
         c.combine(s_dense)
 
-    decode_us = {}
-    for name, fn in (("sparse", decode_sparse), ("dense", decode_dense)):
+    def graph_us(fn):
+        """Average replay time of one HIP graph per copy holding fn(copy)."""
         try:
             gs = []
             side = torch.cuda.Stream()
@@ -229,7 +246,36 @@ def run_gpu(args, spec, data):
             del gs
         except RuntimeError:
             ms_, _ = time_loop(lambda i: fn(copies[i % len(copies)]))
-        decode_us[name] = ms_ * 1e3 / args.steps
+        return ms_ * 1e3 / args.steps
+
+    decode_us = {"sparse": graph_us(decode_sparse), "dense": graph_us(decode_dense)}
+
+    # selection variants, kernel level (not part of the step): the mean-key
+    # index, and either index with the first 4 / last 64 tokens forced in
+    def kernel_us(fn):
+        for i in range(args.warmup):
+            fn(copies[i % len(copies)])
+        ms_, _ = time_loop(lambda i: fn(copies[i % len(copies)]))
+        return ms_ * 1e3 / args.steps
+
+    for c in copies:
+        c.mean_build()            # from here on append() refreshes the mean rows too
+    torch.cuda.synchronize()
+    variants = {
+        "mean_build_us": kernel_us(lambda c: c.mean_build()),
+        "meta_build_us": kernel_us(lambda c: c.meta_build()),
+        "mean_select_forced_us": kernel_us(lambda c: c.select(k, "mean", 4, 64)),
+        "minmax_select_forced_us": kernel_us(lambda c: c.select(k, "minmax", 4, 64)),
+        "minmax_select_us": kernel_us(lambda c: c.select(k, "minmax", 0, 0)),
+    }
+
+    def decode_sparse_mean(c):
+        c.append()
+        c.select(k, "mean", 4, 64)
+        c.attention(sparse=True, num_splits=s_sparse)
+        c.combine(s_sparse)
+
+    variants["decode_sparse_mean_forced_us"] = graph_us(decode_sparse_mean)
 
     for c in copies:
         c.close()
@@ -237,7 +283,7 @@ def run_gpu(args, spec, data):
     torch.cuda.empty_cache()
     return {
         "total_ms": total_ms, "wall_s": wall, "stage_ms": per_stage_ms,
-        "decode_us": decode_us,
+        "decode_us": decode_us, "variants": variants,
         "s_sparse": s_sparse, "s_dense": s_dense, "launch": launch,
         "dense_attn_loop_us": dense_loop_ms * 1e3 / args.steps,
         "eager_ms_per_step": eager_ms / args.steps,
@@ -419,6 +465,17 @@ def copy_calibration():
     print(json.dumps({"copy_bytes_read": n, "copy_bytes_written": n}), flush=True)
 
 
+def variants_record(spec, v: dict) -> dict:
+    vb = variant_bytes(spec, spec.topk_blocks)
+    rec = {"forced_tokens": {"sink": 4, "local": 64}}
+    for name, b in vb.items():
+        us = v[f"{name}_us"]
+        rec[name] = {"us": us, "gbps": b / (us * 1e-6) / 1e9, "bytes": b}
+    rec["decode_sparse_mean_forced"] = {"us": v["decode_sparse_mean_forced_us"],
+                                        "steps_per_s": 1e6 / v["decode_sparse_mean_forced_us"]}
+    return rec
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -534,6 +591,7 @@ def main():
             "avg_launch_us": dense_us,
             "timing": f"{args.steps} back-to-back launches between two HIP events",
         },
+        "selection_variants": variants_record(spec, g["variants"]),
         "other_workloads": others,
         "zero_copy": zc,
         "cpu_baseline": cpu,

@@ -5,6 +5,9 @@
  *
  *   kv_block_meta_build   channel-wise min/max key of every KV page (the block index)
  *   kv_block_score_topk   Quest block score of every logical block, then Top-K blocks
+ *   kv_block_mean_build   mean key of every KV page (the mean-key block index)
+ *   kv_block_select       block scores from either index, then Top-K with the
+ *                         blocks of the first / last tokens forced in
  *   kv_paged_decode_attn  split-K softmax decode attention, dense or over selected blocks
  *   kv_decode_combine     log-sum-exp merge of the split partials
  *   kv_append_token       store the new token's K/V and fold it into its page's meta
@@ -37,6 +40,7 @@
  *     q        [B, Hq, D]            dtype
  *     K, V     [P, Hkv, bs, D]       dtype   (page p, KV head j, slot s, channel c)
  *     kmeta    [P, Hkv, 2, D]        dtype   (index 0 = channel min, 1 = channel max)
+ *     kmean    [P, Hkv, D]           fp32    (mean key of the page's valid slots)
  *     block_table int32 [B, maxN]    logical block n of sequence b -> page
  *     seq_lens    int32 [B]          L_b >= 1 tokens, current token included,
  *                                    N_b = ceil(L_b / bs) <= maxN
@@ -46,7 +50,7 @@
  *     part_o   fp32 [B, Hq, S, D]    per-split normalised output
  *     part_m, part_l fp32 [B, Hq, S] per-split max logit and sum of exp(logit - max)
  *     out      fp32 [B, Hq, D];  lse fp32 [B, Hq]
- * - Alignment: q, K, V and kmeta 16 bytes; part_o and out 16 bytes; the rest 4.
+ * - Alignment: q, K, V, kmeta and kmean 16 bytes; part_o and out 16 bytes; the rest 4.
  */
 #ifndef KVDECODE_H
 #define KVDECODE_H
@@ -68,6 +72,12 @@ typedef enum {
 } kv_status;
 
 typedef enum { KV_F32 = 0, KV_F16 = 1, KV_BF16 = 2 } kv_dtype;
+
+/* Block index kinds of kv_block_select. */
+typedef enum {
+  KV_INDEX_MINMAX = 0, /* kmeta: channel-wise min and max keys (Quest) */
+  KV_INDEX_MEAN = 1    /* kmean: the mean key */
+} kv_index_kind;
 
 /* kv_shape.flags */
 #define KV_FLAG_HOST_KV 0x1u /* K/V pools are device-mapped pinned host memory */
@@ -104,22 +114,38 @@ kv_status kv_block_meta_build(const kv_shape* shape, const void* k_cache, const 
                               void* stream);
 
 /*
+ * Mean-key block index (KVDrive §2.3: spatial blocking may represent a block by
+ * the mean of its keys; §4: a page's mean key is its representative).
+ * For i < num_page_ids and every KV head j, writes
+ *   kmean[p, j, c] = (sum_{s < v} K[p, j, s, c]) / v     (fp32 [P, Hkv, D])
+ * with p = page_ids[i], v = page_valid_tokens[i] in [1, bs].  The sum is taken
+ * in fp64 in slot order and the quotient is rounded once to fp32; for fp16 and
+ * bf16 keys the fp64 sum is exact, so kmean is the exact mean rounded to the
+ * nearest fp32.  Pages not listed are not touched; ids as in kv_block_meta_build.
+ */
+kv_status kv_block_mean_build(const kv_shape* shape, const void* k_cache, const int32_t* page_ids,
+                              const int32_t* page_valid_tokens, int32_t num_page_ids, float* kmean,
+                              void* stream);
+
+/*
  * Decode-step append (Dual-Blade background: a decode step stores the new K/V
  * pair after attending; DirectKV review, core method 4: the KV manager appends
  * at decode).  For every sequence b and KV head j, the new token sits at
  * position t = seq_lens[b] - 1 (seq_lens already counts it): page
  * p = block_table[b, t / bs], slot s = t mod bs.  Writes
  *   K[p, j, s, :] = k_new[b, j, :],  V[p, j, s, :] = v_new[b, j, :]
- * (k_new, v_new: [B, Hkv, D] in the storage dtype), and, when kmeta is not
- * NULL, folds the key into the page's block meta: for s == 0 the min and max
- * rows become k_new (a fresh page), otherwise they become the element-wise
- * min / max with k_new.  If kmeta held the exact meta of slots 0..s-1, it then
- * holds exactly what kv_block_meta_build computes for slots 0..s.  Distinct
- * sequences must own distinct pages.
+ * (k_new, v_new: [B, Hkv, D] in the storage dtype).  When kmeta is not NULL the
+ * key is folded into the page's min/max rows: for s == 0 they become k_new (a
+ * fresh page), otherwise the element-wise min / max with k_new; if kmeta held
+ * the exact meta of slots 0..s-1, it then holds exactly what
+ * kv_block_meta_build computes for slots 0..s.  When kmean is not NULL the
+ * page's mean row is recomputed from slots 0..s with kv_block_mean_build's
+ * arithmetic, so it equals a rebuild bit for bit.  Distinct sequences must own
+ * distinct pages.
  */
 kv_status kv_append_token(const kv_shape* shape, const void* k_new, const void* v_new,
                           const int32_t* block_table, const int32_t* seq_lens, void* k_cache,
-                          void* v_cache, void* kmeta, void* stream);
+                          void* v_cache, void* kmeta, float* kmean, void* stream);
 
 /* Workspace bytes kv_block_score_topk needs when scores_out is NULL (0 otherwise). */
 size_t kv_score_topk_workspace_size(const kv_shape* shape, int32_t topk_blocks);
@@ -143,6 +169,34 @@ kv_status kv_block_score_topk(const kv_shape* shape, const void* q, const void* 
                               int32_t topk_blocks, float* scores_out, int32_t* sel_blocks,
                               int32_t* sel_count, void* workspace, size_t workspace_bytes,
                               void* stream);
+
+/*
+ * Upper bound of the blocks kv_block_select forces in for any sequence length:
+ * ceil(sink / bs) + (local > 0 ? ceil((local - 1) / bs) + 1 : 0).  -1 for an
+ * invalid shape or a negative count.
+ */
+int32_t kv_max_forced_blocks(const kv_shape* shape, int32_t sink_tokens, int32_t local_tokens);
+
+/*
+ * Block scoring from either index, then Top-K with forced tokens.
+ * index_kind KV_INDEX_MINMAX: `index` is kmeta and the head score is Quest's,
+ * as in kv_block_score_topk.  KV_INDEX_MEAN: `index` is kmean and the head
+ * score is sigma[b,h,n] = q[b,h] . kmean[p, j] (fp32 accumulation).  Group score
+ * and ranking as in kv_block_score_topk, except that every block holding one of
+ * the first sink_tokens tokens (n * bs < sink_tokens) or one of the last
+ * local_tokens tokens ((n + 1) * bs > L_b - local_tokens) is always selected
+ * and counts against the budget (KVDrive §9.1: the sparse systems keep the
+ * first 4 and the last 64 tokens); the other min(topk_blocks, N_b) - #forced
+ * places go to the best of the remaining blocks (ties: lower index).  scores_out
+ * holds the unforced scores.  Requires kv_max_forced_blocks() <= topk_blocks;
+ * workspace as in kv_block_score_topk.  With KV_INDEX_MINMAX and
+ * sink_tokens = local_tokens = 0 this is kv_block_score_topk.
+ */
+kv_status kv_block_select(const kv_shape* shape, int32_t index_kind, const void* q,
+                          const void* index, const int32_t* block_table, const int32_t* seq_lens,
+                          int32_t topk_blocks, int32_t sink_tokens, int32_t local_tokens,
+                          float* scores_out, int32_t* sel_blocks, int32_t* sel_count,
+                          void* workspace, size_t workspace_bytes, void* stream);
 
 /*
  * Number of splits the library would pick for `blocks_per_unit` blocks per

@@ -119,22 +119,44 @@ kv_status kv_block_meta_build(const kv_shape* shape, const void* k_cache, const 
                     "kv_block_meta_build launch");
 }
 
+kv_status kv_block_mean_build(const kv_shape* shape, const void* k_cache, const int32_t* page_ids,
+                              const int32_t* page_valid_tokens, int32_t num_page_ids, float* kmean,
+                              void* stream) {
+  kv_status st = check_shape(shape);
+  if (st != KV_OK) return st;
+  if (num_page_ids < 0) return fail(KV_ERR_INVALID_ARG, "num_page_ids=%d < 0", num_page_ids);
+  if (num_page_ids == 0) return ok();
+  if (!k_cache || !page_ids || !page_valid_tokens || !kmean)
+    return fail(KV_ERR_INVALID_ARG, "k_cache, page_ids, page_valid_tokens and kmean are required");
+  if ((long)num_page_ids * shape->num_kv_heads > 0x7fffffffL)
+    return fail(KV_ERR_INVALID_ARG, "num_page_ids * num_kv_heads overflows int32");
+  if (!aligned(k_cache, 16) || !aligned(kmean, 16))
+    return fail(KV_ERR_ALIGNMENT, "k_cache and kmean must be 16-byte aligned");
+  if (!aligned(page_ids, 4) || !aligned(page_valid_tokens, 4))
+    return fail(KV_ERR_ALIGNMENT, "page_ids and page_valid_tokens must be 4-byte aligned");
+  return hip_status(kvd::launch_block_mean(shape->dtype, shape->head_dim, k_cache, page_ids,
+                                           page_valid_tokens, num_page_ids, shape->num_kv_heads,
+                                           kmean, (hipStream_t)stream),
+                    "kv_block_mean_build launch");
+}
+
 kv_status kv_append_token(const kv_shape* shape, const void* k_new, const void* v_new,
                           const int32_t* block_table, const int32_t* seq_lens, void* k_cache,
-                          void* v_cache, void* kmeta, void* stream) {
+                          void* v_cache, void* kmeta, float* kmean, void* stream) {
   kv_status st = check_shape(shape);
   if (st != KV_OK) return st;
   if (!k_new || !v_new || !block_table || !seq_lens || !k_cache || !v_cache)
     return fail(KV_ERR_INVALID_ARG, "k_new, v_new, block_table, seq_lens, k_cache and v_cache are required");
   if (!aligned(k_new, 16) || !aligned(v_new, 16) || !aligned(k_cache, 16) || !aligned(v_cache, 16) ||
-      (kmeta && !aligned(kmeta, 16)))
-    return fail(KV_ERR_ALIGNMENT, "k_new, v_new, k_cache, v_cache and kmeta must be 16-byte aligned");
+      (kmeta && !aligned(kmeta, 16)) || (kmean && !aligned(kmean, 16)))
+    return fail(KV_ERR_ALIGNMENT,
+                "k_new, v_new, k_cache, v_cache, kmeta and kmean must be 16-byte aligned");
   if (!aligned(block_table, 4) || !aligned(seq_lens, 4))
     return fail(KV_ERR_ALIGNMENT, "block_table and seq_lens must be 4-byte aligned");
   return hip_status(kvd::launch_append_token(shape->dtype, shape->head_dim, k_new, v_new,
                                              block_table, seq_lens, shape->num_seqs,
                                              shape->num_kv_heads, shape->max_blocks_per_seq,
-                                             k_cache, v_cache, kmeta, (hipStream_t)stream),
+                                             k_cache, v_cache, kmeta, kmean, (hipStream_t)stream),
                     "kv_append_token launch");
 }
 
@@ -144,21 +166,41 @@ size_t kv_score_topk_workspace_size(const kv_shape* shape, int32_t topk_blocks) 
   return (scores_bytes(shape) + 255) & ~(size_t)255;
 }
 
-kv_status kv_block_score_topk(const kv_shape* shape, const void* q, const void* kmeta,
-                              const int32_t* block_table, const int32_t* seq_lens,
-                              int32_t topk_blocks, float* scores_out, int32_t* sel_blocks,
-                              int32_t* sel_count, void* workspace, size_t workspace_bytes,
-                              void* stream) {
+int32_t kv_max_forced_blocks(const kv_shape* shape, int32_t sink_tokens, int32_t local_tokens) {
+  if (check_shape(shape) != KV_OK || sink_tokens < 0 || local_tokens < 0) return -1;
+  const long bs = shape->block_size;
+  // the first sink tokens fill ceil(sink / bs) blocks; local consecutive tokens
+  // touch at most ceil((local - 1) / bs) + 1 blocks
+  long n = (sink_tokens + bs - 1) / bs;
+  if (local_tokens > 0) n += (local_tokens - 1 + bs - 1) / bs + 1;
+  return (int32_t)std::min<long>(n, 0x7fffffffL);
+}
+
+kv_status kv_block_select(const kv_shape* shape, int32_t index_kind, const void* q,
+                          const void* index, const int32_t* block_table, const int32_t* seq_lens,
+                          int32_t topk_blocks, int32_t sink_tokens, int32_t local_tokens,
+                          float* scores_out, int32_t* sel_blocks, int32_t* sel_count,
+                          void* workspace, size_t workspace_bytes, void* stream) {
   kv_status st = check_shape(shape);
   if (st != KV_OK) return st;
+  if (index_kind != KV_INDEX_MINMAX && index_kind != KV_INDEX_MEAN)
+    return fail(KV_ERR_INVALID_ARG, "index_kind=%d unknown", index_kind);
   if (topk_blocks < 1) return fail(KV_ERR_INVALID_ARG, "topk_blocks=%d must be >= 1", topk_blocks);
+  if (sink_tokens < 0 || local_tokens < 0)
+    return fail(KV_ERR_INVALID_ARG, "sink_tokens=%d and local_tokens=%d must be >= 0", sink_tokens,
+                local_tokens);
+  const int32_t forced = kv_max_forced_blocks(shape, sink_tokens, local_tokens);
+  if (forced > topk_blocks)
+    return fail(KV_ERR_INVALID_ARG,
+                "sink_tokens=%d and local_tokens=%d can force %d blocks, more than topk_blocks=%d",
+                sink_tokens, local_tokens, forced, topk_blocks);
   if (shape->max_blocks_per_seq > kvd::kTopkMaxBlocks)
     return fail(KV_ERR_UNSUPPORTED, "max_blocks_per_seq=%d above the Top-K limit %d",
                 shape->max_blocks_per_seq, kvd::kTopkMaxBlocks);
-  if (!q || !kmeta || !block_table || !seq_lens || !sel_blocks || !sel_count)
-    return fail(KV_ERR_INVALID_ARG, "q, kmeta, block_table, seq_lens, sel_blocks, sel_count are required");
-  if (!aligned(q, 16) || !aligned(kmeta, 16))
-    return fail(KV_ERR_ALIGNMENT, "q and kmeta must be 16-byte aligned");
+  if (!q || !index || !block_table || !seq_lens || !sel_blocks || !sel_count)
+    return fail(KV_ERR_INVALID_ARG, "q, index, block_table, seq_lens, sel_blocks, sel_count are required");
+  if (!aligned(q, 16) || !aligned(index, 16))
+    return fail(KV_ERR_ALIGNMENT, "q and the index must be 16-byte aligned");
   if (!aligned(block_table, 4) || !aligned(seq_lens, 4) || !aligned(sel_blocks, 4) ||
       !aligned(sel_count, 4) || (scores_out && !aligned(scores_out, 4)))
     return fail(KV_ERR_ALIGNMENT, "integer and score arrays must be 4-byte aligned");
@@ -173,14 +215,24 @@ kv_status kv_block_score_topk(const kv_shape* shape, const void* q, const void* 
   }
   const int G = shape->num_q_heads / shape->num_kv_heads;
   hipStream_t s = (hipStream_t)stream;
-  hipError_t e = kvd::launch_block_score(shape->dtype, shape->head_dim, G, q, kmeta, block_table,
-                                         seq_lens, shape->num_seqs, shape->num_q_heads,
-                                         shape->num_kv_heads, shape->max_blocks_per_seq, scores, s);
-  if (e != hipSuccess) return hip_status(e, "kv_block_score_topk score launch");
+  hipError_t e = kvd::launch_block_score(shape->dtype, shape->head_dim, G, index_kind, q, index,
+                                         block_table, seq_lens, shape->num_seqs,
+                                         shape->num_q_heads, shape->num_kv_heads,
+                                         shape->max_blocks_per_seq, scores, s);
+  if (e != hipSuccess) return hip_status(e, "block score launch");
   return hip_status(kvd::launch_topk(scores, seq_lens, shape->num_seqs, shape->num_kv_heads,
-                                     shape->max_blocks_per_seq, topk_blocks, sel_blocks, sel_count,
-                                     s),
-                    "kv_block_score_topk top-k launch");
+                                     shape->max_blocks_per_seq, topk_blocks, sink_tokens,
+                                     local_tokens, sel_blocks, sel_count, s),
+                    "top-k launch");
+}
+
+kv_status kv_block_score_topk(const kv_shape* shape, const void* q, const void* kmeta,
+                              const int32_t* block_table, const int32_t* seq_lens,
+                              int32_t topk_blocks, float* scores_out, int32_t* sel_blocks,
+                              int32_t* sel_count, void* workspace, size_t workspace_bytes,
+                              void* stream) {
+  return kv_block_select(shape, KV_INDEX_MINMAX, q, kmeta, block_table, seq_lens, topk_blocks, 0,
+                         0, scores_out, sel_blocks, sel_count, workspace, workspace_bytes, stream);
 }
 
 int32_t kv_auto_num_splits(const kv_shape* shape, int32_t blocks_per_unit) {

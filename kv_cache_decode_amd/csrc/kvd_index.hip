@@ -1,8 +1,12 @@
 // gfx950 kernels that build and query the block index of the paged KV cache.
 //
 //   block_meta_kernel   channel-wise min/max key per (page, KV head)      KVDrive §2.2, §2.3
-//   block_score_kernel  Quest score per logical block, max over the GQA group   KVDrive §2.2
-//   topk_kernel         exact Top-K of the block scores, ascending output
+//   block_mean_kernel   mean key per (page, KV head)                      KVDrive §2.3, §4
+//   append_token_kernel store a decode token's K/V and refresh its page's index rows
+//   block_score_kernel  Quest (or mean-key) score per logical block, max over
+//                       the GQA group                                     KVDrive §2.2, §2.3
+//   topk_kernel         exact Top-K of the block scores, ascending output, with
+//                       the blocks of the first / last tokens forced in    KVDrive §9.1
 //
 // All three are HBM- or latency-bound; rows of D channels move as coalesced
 // 16-byte chunks (RowGeom in kvd_device.hpp).
@@ -81,17 +85,80 @@ __global__ __launch_bounds__(WAVES * kWave) void block_meta_kernel(
   }
 }
 
+// ============================================================== block mean
+//
+// Same lane layout and wave steps as the meta build.  Each lane sums its chunk
+// of the valid token rows in fp64, in slot order, divides by the valid count
+// in fp64 and rounds once to fp32: for fp16 / bf16 keys (and fp32 keys whose
+// exponents lie within 29 binades of each other) the fp64 sum is exact, so the
+// stored row is the exact mean rounded to nearest fp32.
+
+template <int E>
+__device__ inline void store_f32_chunk(float* dst, const float (&v)[E]) {
+#pragma unroll
+  for (int i = 0; i < E; i += 4)
+    store16(dst + i, make_uint4(__float_as_uint(v[i]), __float_as_uint(v[i + 1]),
+                                __float_as_uint(v[i + 2]), __float_as_uint(v[i + 3])));
+}
+
+template <typename DT, int D, int WAVES>
+__global__ __launch_bounds__(WAVES * kWave) void block_mean_kernel(
+    const void* __restrict__ k_cache, const int32_t* __restrict__ page_ids,
+    const int32_t* __restrict__ valid_tokens, int n_ids, int Hkv, float* __restrict__ kmean) {
+  using G_ = RowGeom<DT, D>;
+  using St = typename DT::storage;
+  constexpr int E = G_::E, LPR = G_::LPR;
+  constexpr int UPS = kWave / LPR;
+  const int lane = threadIdx.x & (kWave - 1);
+  const int us = lane / LPR, c = lane % LPR;
+  const long units = (long)n_ids * Hkv;
+  const long steps = (units + UPS - 1) / UPS;
+  const long nwaves = (long)gridDim.x * WAVES;
+
+  for (long step = (long)blockIdx.x * WAVES + (threadIdx.x >> 6); step < steps; step += nwaves) {
+    const long u = step * UPS + us;
+    if (u >= units) continue;
+    const int i = (int)(u / Hkv);
+    const int j = (int)(u - (long)i * Hkv);
+    const size_t tile = (size_t)page_ids[i] * Hkv + j;
+    const int nv = valid_tokens[i];
+    const St* src = static_cast<const St*>(k_cache) + tile * kBlockSize * D + (size_t)c * E;
+    uint4 w[kBlockSize];
+#pragma unroll
+    for (int t = 0; t < kBlockSize; ++t) w[t] = load16_stream(src + (size_t)t * D);
+    double acc[E];
+#pragma unroll
+    for (int e = 0; e < E; ++e) acc[e] = 0.0;
+#pragma unroll
+    for (int t = 0; t < kBlockSize; ++t) {
+      if (t < nv) {
+        float f[E];
+        DT::widen(w[t], f);
+#pragma unroll
+        for (int e = 0; e < E; ++e) acc[e] += (double)f[e];
+      }
+    }
+    float m[E];
+#pragma unroll
+    for (int e = 0; e < E; ++e) m[e] = (float)(acc[e] / (double)nv);
+    store_f32_chunk<E>(kmean + tile * D + (size_t)c * E, m);
+  }
+}
+
 // ============================================================== decode-step append
 //
 // One wave per (sequence, KV head); lane c < LPR owns channel chunk c.  The
 // new key and value rows are stored into their slot, and the key is folded
-// into the page's min/max rows (a fresh page, slot 0, starts them over).
+// into the page's min/max rows (a fresh page, slot 0, starts them over).  The
+// page's mean row is recomputed from slots 0..s with the mean build's exact
+// arithmetic (fp64 sum in slot order, one rounding), so it equals a rebuild.
 
 template <typename DT, int D>
 __global__ __launch_bounds__(kWave) void append_token_kernel(
     const void* __restrict__ k_new, const void* __restrict__ v_new,
     const int32_t* __restrict__ block_table, const int32_t* __restrict__ seq_lens, int Hkv,
-    int maxN, void* __restrict__ k_cache, void* __restrict__ v_cache, void* __restrict__ kmeta) {
+    int maxN, void* __restrict__ k_cache, void* __restrict__ v_cache, void* __restrict__ kmeta,
+    float* __restrict__ kmean) {
   using G_ = RowGeom<DT, D>;
   using St = typename DT::storage;
   constexpr int E = G_::E, LPR = G_::LPR;
@@ -122,6 +189,23 @@ __global__ __launch_bounds__(kWave) void append_token_kernel(
       store16(m + D, DT::narrow_exact(mx));
     }
   }
+  if (kmean) {
+    // slots before s come from the cache; this lane wrote none of them
+    const St* rows = static_cast<const St*>(k_cache) + tile * kBlockSize * D + (size_t)c * E;
+    double acc[E];
+#pragma unroll
+    for (int e = 0; e < E; ++e) acc[e] = 0.0;
+    for (int t = 0; t <= s; ++t) {
+      float f[E];
+      DT::widen(t < s ? load16(rows + (size_t)t * D) : kw, f);
+#pragma unroll
+      for (int e = 0; e < E; ++e) acc[e] += (double)f[e];
+    }
+    float mv[E];
+#pragma unroll
+    for (int e = 0; e < E; ++e) mv[e] = (float)(acc[e] / (double)(s + 1));
+    store_f32_chunk<E>(kmean + tile * D + (size_t)c * E, mv);
+  }
 }
 
 // ============================================================== block score
@@ -129,11 +213,15 @@ __global__ __launch_bounds__(kWave) void append_token_kernel(
 // sigma_h = sum_c max(q_hc kmin_c, q_hc kmax_c) = sum_c (q+_hc kmax_c + q-_hc kmin_c)
 // with q+ = max(q, 0), q- = min(q, 0): for each channel one of the two products
 // is an exact zero, so the fused multiply-adds accumulate exactly the max term.
+// With the mean-key index (IDX = kIndexMean) the score is q_h . kmean, the
+// fp32 mean row read as E floats per lane.
 // A wave owns STEPS * TPI consecutive logical blocks of one (sequence, KV
 // head); lane (rg, c) handles channels [c*E, c*E+E) of block n0 + step*TPI + rg.
-// All meta loads of the wave are issued before any arithmetic.
+// All index loads of the wave are issued before any arithmetic.
 
-template <typename DT, int D, int G, int WAVES, int STEPS>
+constexpr int kIndexMinMax = 0, kIndexMean = 1;
+
+template <typename DT, int D, int G, int WAVES, int STEPS, int IDX>
 __global__ __launch_bounds__(WAVES * kWave) void block_score_kernel(
     const void* __restrict__ q, const void* __restrict__ kmeta,
     const int32_t* __restrict__ block_table, const int32_t* __restrict__ seq_lens, int Hq,
@@ -149,18 +237,27 @@ __global__ __launch_bounds__(WAVES * kWave) void block_score_kernel(
   const int nb = (seq_lens[b] + kBlockSize - 1) / kBlockSize;
 
   const int32_t* bt_row = block_table + (size_t)b * maxN;
-  uint4 wmin[STEPS], wmax[STEPS];
+  // 16-byte index loads per block and lane: the min and max chunks, or the
+  // E floats of the mean chunk
+  constexpr int NL = (IDX == kIndexMinMax) ? 2 : E / 4;
+  uint4 w[STEPS][NL];
 #pragma unroll
   for (int st = 0; st < STEPS; ++st) {
     const int n = n0 + st * TPI + rg;
     if (n < nb) {
       const size_t p = (size_t)bt_row[n];
-      const St* src = static_cast<const St*>(kmeta) + (p * Hkv + j) * 2 * D + c * E;
-      wmin[st] = load16(src);
-      wmax[st] = load16(src + D);
+      if constexpr (IDX == kIndexMinMax) {
+        const St* src = static_cast<const St*>(kmeta) + (p * Hkv + j) * 2 * D + c * E;
+        w[st][0] = load16(src);
+        w[st][1] = load16(src + D);
+      } else {
+        const float* src = static_cast<const float*>(kmeta) + (p * Hkv + j) * D + c * E;
+#pragma unroll
+        for (int i = 0; i < NL; ++i) w[st][i] = load16(src + 4 * i);
+      }
     } else {
-      wmin[st] = make_uint4(0, 0, 0, 0);
-      wmax[st] = make_uint4(0, 0, 0, 0);
+#pragma unroll
+      for (int i = 0; i < NL; ++i) w[st][i] = make_uint4(0, 0, 0, 0);
     }
   }
 
@@ -170,24 +267,46 @@ __global__ __launch_bounds__(WAVES * kWave) void block_score_kernel(
     float f[E];
     DT::widen(load16(static_cast<const St*>(q) + ((size_t)b * Hq + j * G + g) * D + c * E), f);
 #pragma unroll
-    for (int e = 0; e < E; ++e) { qp[g][e] = fmaxf(f[e], 0.0f); qn[g][e] = fminf(f[e], 0.0f); }
+    for (int e = 0; e < E; ++e) {
+      if constexpr (IDX == kIndexMinMax) {
+        qp[g][e] = fmaxf(f[e], 0.0f);
+        qn[g][e] = fminf(f[e], 0.0f);
+      } else {
+        qp[g][e] = f[e];
+        qn[g][e] = 0.0f;
+      }
+    }
   }
 
   float* out = scores + ((size_t)b * Hkv + j) * maxN;
 #pragma unroll
   for (int st = 0; st < STEPS; ++st) {
     const int n = n0 + st * TPI + rg;
-    float kmn[E], kmx[E];
-    DT::widen(wmin[st], kmn);
-    DT::widen(wmax[st], kmx);
+    float ka[E], kb[E];   // minmax: kmin, kmax; mean: the mean row
+    if constexpr (IDX == kIndexMinMax) {
+      DT::widen(w[st][0], ka);
+      DT::widen(w[st][1], kb);
+    } else {
+#pragma unroll
+      for (int i = 0; i < NL; ++i) {
+        ka[4 * i + 0] = __uint_as_float(w[st][i].x);
+        ka[4 * i + 1] = __uint_as_float(w[st][i].y);
+        ka[4 * i + 2] = __uint_as_float(w[st][i].z);
+        ka[4 * i + 3] = __uint_as_float(w[st][i].w);
+      }
+    }
     float best = -INFINITY;
 #pragma unroll
     for (int g = 0; g < G; ++g) {
       float acc = 0.0f;
 #pragma unroll
       for (int e = 0; e < E; ++e) {
-        acc = fmaf(qp[g][e], kmx[e], acc);
-        acc = fmaf(qn[g][e], kmn[e], acc);
+        if constexpr (IDX == kIndexMinMax) {
+          acc = fmaf(qp[g][e], kb[e], acc);
+          acc = fmaf(qn[g][e], ka[e], acc);
+        } else {
+          acc = fmaf(qp[g][e], ka[e], acc);
+        }
       }
       acc = group_reduce<LPR, OpSum>(acc);
       best = fmaxf(best, acc);
@@ -209,6 +328,9 @@ __global__ __launch_bounds__(WAVES * kWave) void block_score_kernel(
 // above T, or equal to T and among the first K_eff - #{key > T} equal keys in
 // index order; one exclusive scan of packed (#greater, #equal) counts gives
 // every selected block its output position, so the list comes out ascending.
+// A block holding one of the first `sink` or the last `local` tokens takes the
+// key 0xFFFFFFFF, above every score's key: forced blocks are always selected
+// (the caller keeps their count <= K) and the others compete for the rest.
 
 __device__ inline uint32_t score_key(float f) {
   if (f == 0.0f) f = 0.0f;
@@ -250,8 +372,8 @@ __device__ inline uint32_t block_exclusive_scan(uint32_t v, uint32_t* buf) {
 template <int EPT>
 __global__ __launch_bounds__(1024) void topk_kernel(const float* __restrict__ scores,
                                                     const int32_t* __restrict__ seq_lens,
-                                                    int Hkv, int maxN, int K,
-                                                    int32_t* __restrict__ sel,
+                                                    int Hkv, int maxN, int K, int sink,
+                                                    int local, int32_t* __restrict__ sel,
                                                     int32_t* __restrict__ sel_count) {
   constexpr int NW = 1024 / kWave;
   __shared__ __align__(16) uint32_t hist[NW][256];
@@ -259,8 +381,10 @@ __global__ __launch_bounds__(1024) void topk_kernel(const float* __restrict__ sc
   __shared__ uint32_t state[2];
   const int j = blockIdx.x, b = blockIdx.y;
   const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid >> 6;
-  const int nb = (seq_lens[b] + kBlockSize - 1) / kBlockSize;
+  const int L = seq_lens[b];
+  const int nb = (L + kBlockSize - 1) / kBlockSize;
   const int keff = min(K, nb);
+  const int local_from = local > 0 ? L - local : 0x7fffffff;  // first forced local token
   int32_t* out = sel + ((size_t)b * Hkv + j) * K;
   if (tid == 0) sel_count[(size_t)b * Hkv + j] = max(keff, 0);
   for (int i = max(keff, 0) + tid; i < K; i += 1024) out[i] = -1;
@@ -291,7 +415,9 @@ __global__ __launch_bounds__(1024) void topk_kernel(const float* __restrict__ sc
   for (int r = 0; r < EPT; ++r) {
     key[r] = 0u;
     if (n0 + r < nb) {
-      key[r] = score_key(sc[r]);  // valid keys are >= key(-inf) > 0
+      const int n = n0 + r;
+      const bool forced = n * kBlockSize < sink || (n + 1) * kBlockSize > local_from;
+      key[r] = forced ? 0xFFFFFFFFu : score_key(sc[r]);  // valid keys are >= key(-inf) > 0
       kmn = min(kmn, key[r]);
       kmx = max(kmx, key[r]);
     }
@@ -394,34 +520,61 @@ hipError_t launch_block_meta(int dtype, int D, const void* k_cache, const int32_
   });
 }
 
-hipError_t launch_append_token(int dtype, int D, const void* k_new, const void* v_new,
-                               const int32_t* block_table, const int32_t* seq_lens, int B,
-                               int Hkv, int maxN, void* k_cache, void* v_cache, void* kmeta,
-                               hipStream_t stream) {
+hipError_t launch_block_mean(int dtype, int D, const void* k_cache, const int32_t* page_ids,
+                             const int32_t* valid_tokens, int n_ids, int Hkv, float* kmean,
+                             hipStream_t stream) {
+  if (n_ids <= 0) return hipSuccess;
   return with_dtype(dtype, [&](auto dt) {
     return with_dim(D, [&](auto d) {
-      hipLaunchKernelGGL((append_token_kernel<decltype(dt), decltype(d)::value>), dim3(Hkv, B),
-                         dim3(kWave), 0, stream, k_new, v_new, block_table, seq_lens, Hkv, maxN,
-                         k_cache, v_cache, kmeta);
+      using DT = decltype(dt);
+      constexpr int DD = decltype(d)::value;
+      constexpr int WAVES = 4;
+      constexpr int UPS = kWave / RowGeom<DT, DD>::LPR;
+      const long steps = ((long)n_ids * Hkv + UPS - 1) / UPS;
+      const long want = (steps + WAVES - 1) / WAVES;
+      const int grid = (int)std::min<long>(want, (long)cu_count() * KVD_META_WGS_PER_CU);
+      hipLaunchKernelGGL((block_mean_kernel<DT, DD, WAVES>), dim3(grid), dim3(WAVES * kWave), 0,
+                         stream, k_cache, page_ids, valid_tokens, n_ids, Hkv, kmean);
       return hipGetLastError();
     });
   });
 }
 
-hipError_t launch_block_score(int dtype, int D, int G, const void* q, const void* kmeta,
-                              const int32_t* block_table, const int32_t* seq_lens, int B, int Hq,
-                              int Hkv, int maxN, float* scores, hipStream_t stream) {
+hipError_t launch_append_token(int dtype, int D, const void* k_new, const void* v_new,
+                               const int32_t* block_table, const int32_t* seq_lens, int B,
+                               int Hkv, int maxN, void* k_cache, void* v_cache, void* kmeta,
+                               float* kmean, hipStream_t stream) {
+  return with_dtype(dtype, [&](auto dt) {
+    return with_dim(D, [&](auto d) {
+      hipLaunchKernelGGL((append_token_kernel<decltype(dt), decltype(d)::value>), dim3(Hkv, B),
+                         dim3(kWave), 0, stream, k_new, v_new, block_table, seq_lens, Hkv, maxN,
+                         k_cache, v_cache, kmeta, kmean);
+      return hipGetLastError();
+    });
+  });
+}
+
+hipError_t launch_block_score(int dtype, int D, int G, int index_kind, const void* q,
+                              const void* index, const int32_t* block_table,
+                              const int32_t* seq_lens, int B, int Hq, int Hkv, int maxN,
+                              float* scores, hipStream_t stream) {
   return with_dtype(dtype, [&](auto dt) {
     return with_dim(D, [&](auto d) {
       return with_group(G, [&](auto g) {
         using DT = decltype(dt);
         constexpr int DD = decltype(d)::value;
+        constexpr int GG = decltype(g)::value;
         constexpr int WAVES = 4, STEPS = KVD_SCORE_STEPS;
         constexpr int per_wg = WAVES * STEPS * RowGeom<DT, DD>::TPI;
         const dim3 grid((maxN + per_wg - 1) / per_wg, Hkv, B);
-        hipLaunchKernelGGL((block_score_kernel<DT, DD, decltype(g)::value, WAVES, STEPS>), grid,
-                           dim3(WAVES * kWave), 0, stream, q, kmeta, block_table, seq_lens, Hq,
-                           Hkv, maxN, scores);
+        if (index_kind == kIndexMean)
+          hipLaunchKernelGGL((block_score_kernel<DT, DD, GG, WAVES, STEPS, kIndexMean>), grid,
+                             dim3(WAVES * kWave), 0, stream, q, index, block_table, seq_lens, Hq,
+                             Hkv, maxN, scores);
+        else
+          hipLaunchKernelGGL((block_score_kernel<DT, DD, GG, WAVES, STEPS, kIndexMinMax>), grid,
+                             dim3(WAVES * kWave), 0, stream, q, index, block_table, seq_lens, Hq,
+                             Hkv, maxN, scores);
         return hipGetLastError();
       });
     });
@@ -429,12 +582,13 @@ hipError_t launch_block_score(int dtype, int D, int G, const void* q, const void
 }
 
 hipError_t launch_topk(const float* scores, const int32_t* seq_lens, int B, int Hkv, int maxN,
-                       int K, int32_t* sel, int32_t* sel_count, hipStream_t stream) {
+                       int K, int sink, int local, int32_t* sel, int32_t* sel_count,
+                       hipStream_t stream) {
   const dim3 grid(Hkv, B);
   const int ept = (maxN + 1023) / 1024;
 #define KVD_TOPK(N)                                                                          \
   hipLaunchKernelGGL((topk_kernel<N>), grid, dim3(1024), 0, stream, scores, seq_lens, Hkv, \
-                     maxN, K, sel, sel_count)
+                     maxN, K, sink, local, sel, sel_count)
   if (ept <= 1) KVD_TOPK(1);
   else if (ept <= 2) KVD_TOPK(2);
   else if (ept <= 4) KVD_TOPK(4);

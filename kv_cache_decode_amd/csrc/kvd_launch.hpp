@@ -13,17 +13,24 @@ hipError_t launch_block_meta(int dtype, int D, const void* k_cache, const int32_
                              const int32_t* valid_tokens, int n_ids, int Hkv, void* kmeta,
                              hipStream_t stream);
 
+hipError_t launch_block_mean(int dtype, int D, const void* k_cache, const int32_t* page_ids,
+                             const int32_t* valid_tokens, int n_ids, int Hkv, float* kmean,
+                             hipStream_t stream);
+
 hipError_t launch_append_token(int dtype, int D, const void* k_new, const void* v_new,
                                const int32_t* block_table, const int32_t* seq_lens, int B,
                                int Hkv, int maxN, void* k_cache, void* v_cache, void* kmeta,
-                               hipStream_t stream);
+                               float* kmean, hipStream_t stream);
 
-hipError_t launch_block_score(int dtype, int D, int G, const void* q, const void* kmeta,
-                              const int32_t* block_table, const int32_t* seq_lens, int B, int Hq,
-                              int Hkv, int maxN, float* scores, hipStream_t stream);
+// index_kind: 0 = channel min/max rows in the K dtype, 1 = fp32 mean rows
+hipError_t launch_block_score(int dtype, int D, int G, int index_kind, const void* q,
+                              const void* index, const int32_t* block_table,
+                              const int32_t* seq_lens, int B, int Hq, int Hkv, int maxN,
+                              float* scores, hipStream_t stream);
 
 hipError_t launch_topk(const float* scores, const int32_t* seq_lens, int B, int Hkv, int maxN,
-                       int K, int32_t* sel, int32_t* sel_count, hipStream_t stream);
+                       int K, int sink, int local, int32_t* sel, int32_t* sel_count,
+                       hipStream_t stream);
 
 hipError_t launch_paged_attn(int dtype, int D, int G, const void* q, const void* k_cache,
                              const void* v_cache, const int32_t* block_table,

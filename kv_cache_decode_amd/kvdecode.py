@@ -19,14 +19,16 @@ LIB_PATH = os.environ.get("KVD_LIBRARY_PATH") or os.path.join(_HERE, "libkvdecod
 
 KV_OK, KV_ERR_INVALID_ARG, KV_ERR_UNSUPPORTED, KV_ERR_ALIGNMENT, KV_ERR_WORKSPACE, KV_ERR_HIP = range(6)
 KV_F32, KV_F16, KV_BF16 = 0, 1, 2
+KV_INDEX_MINMAX, KV_INDEX_MEAN = 0, 1
 KV_FLAG_HOST_KV = 0x1
 KV_HOST_COHERENT, KV_HOST_NONCOHERENT = 0x0, 0x1
 DTYPE_CODES = {"f32": KV_F32, "f16": KV_F16, "bf16": KV_BF16}
 
 # every symbol the header declares
 EXPORTS = (
-    "kv_block_meta_build", "kv_append_token", "kv_score_topk_workspace_size", "kv_block_score_topk",
-    "kv_auto_num_splits", "kv_paged_decode_attn", "kv_decode_combine", "kv_host_alloc",
+    "kv_block_meta_build", "kv_block_mean_build", "kv_append_token",
+    "kv_score_topk_workspace_size", "kv_block_score_topk", "kv_max_forced_blocks",
+    "kv_block_select", "kv_auto_num_splits", "kv_paged_decode_attn", "kv_decode_combine", "kv_host_alloc",
     "kv_host_free", "kv_status_string", "kv_last_error_message",
 )
 
@@ -75,7 +77,10 @@ def _load() -> ctypes.CDLL:
     S = ctypes.POINTER(KVShape)
     sig = {
         "kv_block_meta_build": (I32, [S, P, P, P, I32, P, P]),
-        "kv_append_token": (I32, [S, P, P, P, P, P, P, P, P]),
+        "kv_block_mean_build": (I32, [S, P, P, P, I32, P, P]),
+        "kv_append_token": (I32, [S, P, P, P, P, P, P, P, P, P]),
+        "kv_max_forced_blocks": (I32, [S, I32, I32]),
+        "kv_block_select": (I32, [S, I32, P, P, P, P, I32, I32, I32, P, P, P, P, SZ, P]),
         "kv_score_topk_workspace_size": (SZ, [S, I32]),
         "kv_block_score_topk": (I32, [S, P, P, P, P, I32, P, P, P, P, SZ, P]),
         "kv_auto_num_splits": (I32, [S, I32]),
@@ -135,10 +140,18 @@ def kv_block_meta_build(shape: KVShape, k_cache: Buf, page_ids: Buf, page_valid_
                                     _stream(stream)))
 
 
+def kv_block_mean_build(shape: KVShape, k_cache: Buf, page_ids: Buf, page_valid_tokens: Buf,
+                        num_page_ids: int, kmean: Buf, stream=None) -> None:
+    _check(_lib.kv_block_mean_build(ctypes.byref(shape), _p(k_cache), _p(page_ids),
+                                    _p(page_valid_tokens), num_page_ids, _p(kmean),
+                                    _stream(stream)))
+
+
 def kv_append_token(shape: KVShape, k_new: Buf, v_new: Buf, block_table: Buf, seq_lens: Buf,
-                    k_cache: Buf, v_cache: Buf, kmeta: Buf = None, stream=None) -> None:
+                    k_cache: Buf, v_cache: Buf, kmeta: Buf = None, kmean: Buf = None,
+                    stream=None) -> None:
     _check(_lib.kv_append_token(ctypes.byref(shape), _p(k_new), _p(v_new), _p(block_table),
-                                _p(seq_lens), _p(k_cache), _p(v_cache), _p(kmeta),
+                                _p(seq_lens), _p(k_cache), _p(v_cache), _p(kmeta), _p(kmean),
                                 _stream(stream)))
 
 
@@ -153,6 +166,20 @@ def kv_block_score_topk(shape: KVShape, q: Buf, kmeta: Buf, block_table: Buf, se
                                     _p(seq_lens), topk_blocks, _p(scores_out), _p(sel_blocks),
                                     _p(sel_count), _p(workspace), workspace_bytes,
                                     _stream(stream)))
+
+
+def kv_max_forced_blocks(shape: KVShape, sink_tokens: int, local_tokens: int) -> int:
+    return int(_lib.kv_max_forced_blocks(ctypes.byref(shape), sink_tokens, local_tokens))
+
+
+def kv_block_select(shape: KVShape, index_kind: int, q: Buf, index: Buf, block_table: Buf,
+                    seq_lens: Buf, topk_blocks: int, sink_tokens: int, local_tokens: int,
+                    scores_out: Buf, sel_blocks: Buf, sel_count: Buf, workspace: Buf = None,
+                    workspace_bytes: int = 0, stream=None) -> None:
+    _check(_lib.kv_block_select(ctypes.byref(shape), index_kind, _p(q), _p(index),
+                                _p(block_table), _p(seq_lens), topk_blocks, sink_tokens,
+                                local_tokens, _p(scores_out), _p(sel_blocks), _p(sel_count),
+                                _p(workspace), workspace_bytes, _stream(stream)))
 
 
 def kv_auto_num_splits(shape: KVShape, blocks_per_unit: int) -> int:

@@ -72,6 +72,7 @@ class DeviceWorkload:
             self.v_cache = storage_tensor(data.v_raw, dt).to(dev)
         P, Hkv, bs, D = data.k_raw.shape
         self.kmeta = torch.zeros((P, Hkv, 2, D), dtype=TORCH_DTYPES[dt], device=dev)
+        self.kmean = None          # fp32 mean-key index, allocated by mean_build()
         ids, val = [], []
         for b in range(spec.num_seqs):
             for n in range(spec.blocks(b)):
@@ -130,20 +131,42 @@ class DeviceWorkload:
         kd.kv_block_meta_build(self.shape, self.k_cache, self.page_ids, self.page_valid,
                                int(self.page_ids.numel()), self.kmeta, stream)
 
-    def append(self, k_new=None, v_new=None, stream=None):
-        """Store one new token per sequence at position seq_lens - 1 and fold it into the meta."""
+    def mean_build(self, stream=None):
+        if self.kmean is None:
+            P, Hkv, _, D = self.kmeta.shape
+            self.kmean = torch.zeros((P, Hkv, D), dtype=torch.float32, device=self.device)
+        kd.kv_block_mean_build(self.shape, self.k_cache, self.page_ids, self.page_valid,
+                               int(self.page_ids.numel()), self.kmean, stream)
+
+    def append(self, k_new=None, v_new=None, stream=None, meta: bool = True):
+        """Store one new token per sequence at position seq_lens - 1 and refresh the
+        index rows of its page (min/max when ``meta``; the mean once mean_build ran)."""
         kd.kv_append_token(self.shape, self.last_k if k_new is None else k_new,
                            self.last_v if v_new is None else v_new, self.block_table,
-                           self.seq_lens, self.k_cache, self.v_cache, self.kmeta, stream)
+                           self.seq_lens, self.k_cache, self.v_cache,
+                           self.kmeta if meta else None, self.kmean, stream)
 
-    def score_topk(self, k: int, stream=None):
+    def _sel_buffers(self, k: int):
         if self.topk != k or self.sel is None:
             B, Hkv = self.spec.num_seqs, self.spec.num_kv_heads
             self.sel = torch.empty((B, Hkv, k), dtype=torch.int32, device=self.device)
             self.sel_count = torch.empty((B, Hkv), dtype=torch.int32, device=self.device)
             self.topk = k
+
+    def score_topk(self, k: int, stream=None):
+        self._sel_buffers(k)
         kd.kv_block_score_topk(self.shape, self.q, self.kmeta, self.block_table, self.seq_lens, k,
                                self.scores, self.sel, self.sel_count, None, 0, stream)
+
+    def select(self, k: int, index: str = "minmax", sink_tokens: int = 0, local_tokens: int = 0,
+               stream=None):
+        """kv_block_select over the min/max index ("minmax") or the mean index ("mean")."""
+        self._sel_buffers(k)
+        kind, idx = ((kd.KV_INDEX_MEAN, self.kmean) if index == "mean"
+                     else (kd.KV_INDEX_MINMAX, self.kmeta))
+        kd.kv_block_select(self.shape, kind, self.q, idx, self.block_table, self.seq_lens, k,
+                           sink_tokens, local_tokens, self.scores, self.sel, self.sel_count, None,
+                           0, stream)
 
     def attention(self, sparse: bool, num_splits: Optional[int] = None, stream=None):
         S = num_splits or self.auto_splits(sparse)

@@ -11,7 +11,13 @@ Tolerances:
 * selection: the GPU set equals the oracle set, except for blocks whose oracle
   score lies within 1e-6 * |S_K| of the K-th largest oracle score S_K; the GPU
   list must also be a valid Top-K of the GPU's own scores (ascending, unique,
-  lower index first on equal scores).
+  lower index first on equal scores);
+* mean-key index: bit-exact against the oracle's fp64 mean rounded to fp32
+  (the kernel takes the same fp64 sum in slot order and rounds once); mean
+  scores within 1e-6 of sum_c |q_c kmean_c|, as above.  A mean score can cancel
+  to near zero, so its selection band is also widened to 2e-6 times the row's
+  largest magnitude bound: two blocks can only trade places when their oracle
+  scores differ by less than the sum of their fp32 errors.
 """
 from __future__ import annotations
 
@@ -94,6 +100,22 @@ class OracleRun:
                                 self.spec.block_size)
         return oracle.group_scores(hs, self.spec.num_kv_heads)
 
+    def mean(self):
+        if getattr(self, "_mean", None) is None:
+            ids, val = page_lists(self.data)
+            self._mean = oracle.block_mean(self.k, ids, val)
+        return self._mean
+
+    def mean_scores(self):
+        hs = oracle.head_scores_mean(self.q, self.mean(), self.data.block_table,
+                                     self.data.seq_lens, self.spec.block_size)
+        return oracle.group_scores(hs, self.spec.num_kv_heads)
+
+    def mean_score_bound(self):
+        hs = oracle.head_scores_mean(np.abs(self.q), np.abs(self.mean()), self.data.block_table,
+                                     self.data.seq_lens, self.spec.block_size)
+        return oracle.group_scores(hs, self.spec.num_kv_heads)
+
     def score_bound(self):
         """Per (b, KV head, block): an upper bound of sum_c |term_c| over the group's heads."""
         hs = oracle.head_scores(np.abs(self.q), np.abs(self.meta()), self.data.block_table,
@@ -142,14 +164,46 @@ def check_selection_valid(sel: np.ndarray, cnt: np.ndarray, scores: np.ndarray,
             assert sorted(order[:keff]) == s.tolist(), "not the Top-K of the GPU's own scores"
 
 
+def forced_blocks(L: int, bs: int, sink: int, local: int) -> set:
+    """Blocks that hold one of the first ``sink`` or the last ``local`` tokens."""
+    nb = -(-L // bs)
+    return {n for n in range(nb) if n * bs < sink or (local > 0 and (n + 1) * bs > L - local)}
+
+
+def check_selection_valid_forced(sel, cnt, scores, seq_lens, k, sink, local, bs=16):
+    """Every forced block is in the list and the rest is the Top-(K_eff - #forced)
+    of the other blocks by the GPU's own scores, lower index first on ties."""
+    B, Hkv, _ = sel.shape
+    for b in range(B):
+        L = int(seq_lens[b])
+        nb = -(-L // bs)
+        keff = min(k, nb)
+        forced = forced_blocks(L, bs, sink, local)
+        for j in range(Hkv):
+            c = int(cnt[b, j])
+            assert c == keff, f"sel_count {c} != K_eff {keff}"
+            s = sel[b, j, :c]
+            assert np.all(sel[b, j, c:] == -1), "padding must be -1"
+            assert np.all(np.diff(s) > 0) and s.min() >= 0 and s.max() < nb, "ascending, in range"
+            sc = scores[b, j, :nb].astype(np.float64)
+            rest = sorted((n for n in range(nb) if n not in forced), key=lambda i: (-sc[i], i))
+            want = sorted(forced | set(rest[:keff - len(forced)]))
+            assert s.tolist() == want, f"b={b} j={j}: not forced + Top-K of the GPU's own scores"
+
+
 def check_selection_vs_oracle(sel: np.ndarray, cnt: np.ndarray, ref_sel: np.ndarray,
-                              ref_cnt: np.ndarray, ref_scores: np.ndarray, nblocks: np.ndarray):
-    """Same set as the oracle except inside the tie band around the K-th score.
+                              ref_cnt: np.ndarray, ref_scores: np.ndarray, nblocks: np.ndarray,
+                              bound: np.ndarray = None, forced=None):
+    """Same set as the oracle except inside the tie band around the K-th score of
+    the competing (not forced) blocks.  ``bound`` (per block magnitude bound of
+    the score) widens the band to 2 * SCORE_RTOL * the row's largest bound;
+    ``forced(b)`` gives the forced block set of sequence b.
     Returns the number of rows whose sets differ (inside the band)."""
     B, Hkv, _ = sel.shape
     differing = 0
     for b in range(B):
         nb = int(nblocks[b])
+        fb = forced(b) if forced else set()
         for j in range(Hkv):
             assert cnt[b, j] == ref_cnt[b, j]
             got = set(sel[b, j, :cnt[b, j]].tolist())
@@ -157,10 +211,17 @@ def check_selection_vs_oracle(sel: np.ndarray, cnt: np.ndarray, ref_sel: np.ndar
             if got == want:
                 continue
             differing += 1
+            assert fb <= got, "a forced block is missing"
             sc = ref_scores[b, j, :nb]
-            kth = np.sort(sc)[::-1][ref_cnt[b, j] - 1]
+            free = int(ref_cnt[b, j]) - len(fb)
+            assert free > 0, f"b={b} j={j}: only forced blocks fit, yet the sets differ"
+            comp = np.sort([sc[n] for n in range(nb) if n not in fb])[::-1]
+            kth = comp[free - 1]
+            band = TIE_BAND * abs(kth)
+            if bound is not None:
+                band = max(band, 2 * SCORE_RTOL * float(bound[b, j, :nb].max()))
             for n in got ^ want:
-                assert abs(sc[n] - kth) <= TIE_BAND * abs(kth), (
+                assert abs(sc[n] - kth) <= band, (
                     f"block {n} (b={b}, j={j}) differs outside the tie band: "
-                    f"score {sc[n]!r}, K-th {kth!r}")
+                    f"score {sc[n]!r}, K-th {kth!r}, band {band:.3e}")
     return differing

@@ -92,6 +92,12 @@ def test_shape_validation_in_every_call(bad, status):
                                                          stream=stream))
     expect(status, lambda stream: kd.kv_decode_combine(s, 2, A16, A16, A16, A16, None,
                                                        stream=stream))
+    expect(status, lambda stream: kd.kv_block_mean_build(s, A16, A16, A16, 4, A16, stream=stream))
+    expect(status, lambda stream: kd.kv_block_select(s, kd.KV_INDEX_MEAN, A16, A16, A16, A16, 8, 4,
+                                                     64, A16, A16, A16, stream=stream))
+    expect(status, lambda stream: kd.kv_append_token(s, A16, A16, A16, A16, A16, A16, A16, A16,
+                                                     stream=stream))
+    assert kd.kv_max_forced_blocks(s, 4, 64) == -1
     assert kd.kv_auto_num_splits(s, 100) == 1
     assert kd.kv_score_topk_workspace_size(s, 2) == 0
 
@@ -189,6 +195,57 @@ def test_append_argument_checks():
     expect(kd.KV_ERR_INVALID_ARG, lambda stream: f(s, A16, A16, A16, A16, A16, None, A16, stream=stream))
     expect(kd.KV_ERR_ALIGNMENT, lambda stream: f(s, A4, A16, A16, A16, A16, A16, A16, stream=stream))
     expect(kd.KV_ERR_ALIGNMENT, lambda stream: f(s, A16, A16, A16, A16, A16, A16, A4, stream=stream))
+    expect(kd.KV_ERR_ALIGNMENT, lambda stream: f(s, A16, A16, A16, A16, A16, A16, None, A4,
+                                                 stream=stream))
     expect(kd.KV_ERR_ALIGNMENT, lambda stream: f(s, A16, A16, ODD, A16, A16, A16, None, stream=stream))
     expect(kd.KV_ERR_UNSUPPORTED, lambda stream: f(shape(head_dim=80), A16, A16, A16, A16, A16, A16,
                                                    None, stream=stream))
+
+
+def test_mean_build_argument_checks():
+    s = shape()
+    m = kd.kv_block_mean_build
+    expect(kd.KV_ERR_INVALID_ARG, lambda stream: m(s, A16, A16, A16, -1, A16, stream=stream))
+    expect(kd.KV_ERR_INVALID_ARG, lambda stream: m(s, A16, A16, A16, 3, None, stream=stream))
+    expect(kd.KV_ERR_ALIGNMENT, lambda stream: m(s, A16, A16, A16, 3, A4, stream=stream))
+    expect(kd.KV_ERR_ALIGNMENT, lambda stream: m(s, A16, ODD, A16, 3, A16, stream=stream))
+    m(s, None, None, None, 0, None, stream=0)            # nothing to do: OK, no launch
+
+
+@pytest.mark.parametrize("sink,local,want", [
+    (0, 0, 0), (4, 0, 1), (16, 0, 1), (17, 0, 2), (0, 1, 1), (0, 16, 2), (0, 17, 2),
+    (0, 33, 3), (4, 64, 6), (0, 64, 5),
+])
+def test_max_forced_blocks(sink, local, want):
+    """ceil(sink / 16) for the first tokens; local consecutive tokens touch at most
+    ceil((local - 1) / 16) + 1 pages of 16 (checked by sliding the window)."""
+    s = shape()
+    assert kd.kv_max_forced_blocks(s, sink, local) == want
+    worst = 0
+    for L in range(1, 300):
+        toks = set(range(min(sink, L))) | set(range(max(L - local, 0), L))
+        worst = max(worst, len({t // 16 for t in toks}))
+    assert worst <= want
+    assert kd.kv_max_forced_blocks(s, -1, 0) == -1
+
+
+def test_select_argument_checks():
+    s = shape()
+    f = kd.kv_block_select
+
+    def call(kind=kd.KV_INDEX_MEAN, q=A16, index=A16, k=8, sink=4, local=64, scores=A16, **kw):
+        return lambda stream: f(s, kind, q, index, A16, A16, k, sink, local, scores, A16, A16,
+                                stream=stream, **kw)
+
+    expect(kd.KV_ERR_INVALID_ARG, call(kind=2))
+    expect(kd.KV_ERR_INVALID_ARG, call(k=0))
+    expect(kd.KV_ERR_INVALID_ARG, call(sink=-1))
+    expect(kd.KV_ERR_INVALID_ARG, call(local=-3))
+    expect(kd.KV_ERR_INVALID_ARG, call(k=5))                   # 4 + 64 can force 6 blocks
+    expect(kd.KV_ERR_INVALID_ARG, call(index=None))
+    expect(kd.KV_ERR_ALIGNMENT, call(index=A4))
+    expect(kd.KV_ERR_ALIGNMENT, call(q=A4))
+    expect(kd.KV_ERR_WORKSPACE, call(scores=None))
+    big = shape(max_blocks_per_seq=32769)
+    expect(kd.KV_ERR_UNSUPPORTED, lambda stream: f(big, 0, A16, A16, A16, A16, 8, 0, 0, A16, A16,
+                                                   A16, stream=stream))

@@ -1,10 +1,12 @@
 """Decode-step append: the incremental index equals a full rebuild (GPU).
 
 The final workload is generated, the slots of its last n tokens are replaced by
-NaN, the meta is built over the shorter prefix, and the n tokens are appended
-one at a time through kv_append_token.  Afterwards the pools hold the final
-bytes in every valid slot, the block meta equals the oracle's meta of the
-final lengths (bit-exact), and decode attention matches the oracle.
+NaN, the min/max and mean indexes are built over the shorter prefix, and the n
+tokens are appended one at a time through kv_append_token.  Afterwards the
+pools hold the final bytes in every valid slot, the block meta equals the
+oracle's meta of the final lengths and the mean rows equal the oracle's fp64
+means rounded to fp32 (both bit-exact), and decode attention matches the
+oracle.
 """
 import numpy as np
 import pytest
@@ -47,12 +49,15 @@ def test_append_matches_full_rebuild(gpu, dtype, D, G):
     ids, val = page_lists(start)
     kd.kv_block_meta_build(dw.shape, dw.k_cache, torch.from_numpy(ids).to(gpu),
                            torch.from_numpy(val).to(gpu), len(ids), dw.kmeta)
+    kmean = torch.zeros(dw.kmeta.shape[:2] + (D,), dtype=torch.float32, device=gpu)
+    kd.kv_block_mean_build(dw.shape, dw.k_cache, torch.from_numpy(ids).to(gpu),
+                           torch.from_numpy(val).to(gpu), len(ids), kmean)
     lens = torch.from_numpy(L0.astype(np.int32)).to(gpu)
     for i in range(n_app):
         lens += 1
         kd.kv_append_token(dw.shape, storage_tensor(new_k[i], dtype).to(gpu),
                            storage_tensor(new_v[i], dtype).to(gpu), dw.block_table, lens,
-                           dw.k_cache, dw.v_cache, dw.kmeta)
+                           dw.k_cache, dw.v_cache, dw.kmeta, kmean)
         if i in (0, 7, n_app - 1):      # the index of the current lengths, every time checked
             cur = wl.WorkloadData(spec=spec, q_raw=final.q_raw, k_raw=final.k_raw,
                                   v_raw=final.v_raw, block_table=final.block_table,
@@ -60,6 +65,9 @@ def test_append_matches_full_rebuild(gpu, dtype, D, G):
             cids, cval = page_lists(cur)
             ref = oracle.block_meta(final.k64(), cids, cval)
             np.testing.assert_array_equal(to_f64(dw.kmeta)[cids], ref[cids])
+            ref_mean = oracle.block_mean(final.k64(), cids, cval)
+            np.testing.assert_array_equal(kmean.cpu().numpy()[cids],
+                                          ref_mean[cids].astype(np.float32))
     torch.cuda.synchronize()
     assert np.array_equal(lens.cpu().numpy(), L_final)
 
@@ -102,7 +110,8 @@ def test_append_without_meta_only_writes_the_slot(gpu):
     before_v = dw.v_cache.clone()
     kn = torch.full((2, 2, 128), 3.0, dtype=torch.bfloat16, device=gpu)
     vn = torch.full((2, 2, 128), -2.0, dtype=torch.bfloat16, device=gpu)
-    kd.kv_append_token(dw.shape, kn, vn, dw.block_table, dw.seq_lens, dw.k_cache, dw.v_cache, None)
+    kd.kv_append_token(dw.shape, kn, vn, dw.block_table, dw.seq_lens, dw.k_cache, dw.v_cache, None,
+                       None)
     torch.cuda.synchronize()
     changed_k = (dw.k_cache != before_k).any(dim=-1)          # [P, Hkv, 16]
     changed_v = (dw.v_cache != before_v).any(dim=-1)

@@ -62,3 +62,44 @@ def test_named_workload_full_size(gpu, name):
     finally:
         torch.cuda.synchronize()
         dw.close()
+
+
+VARIANT_WORKLOADS = [n for n in wl.WORKLOAD_ORDER
+                     if wl.WORKLOADS[n].topk_blocks is not None and not wl.WORKLOADS[n].host_kv]
+
+
+@pytest.mark.parametrize("name", VARIANT_WORKLOADS)
+def test_named_workload_mean_index_forced(gpu, name):
+    """Mean-key index with the first 4 and last 64 tokens forced in, full size."""
+    import oracle
+    from parity import check_selection_valid_forced, forced_blocks
+    spec = wl.WORKLOADS[name]
+    print(f"\n[{name}] generating", flush=True)
+    data = wl.generate(spec)
+    o = OracleRun(data)
+    dw = _dw(data, gpu)
+    nb = data.num_blocks()
+    k = spec.topk_blocks
+    try:
+        dw.mean_build()
+        dw.select(k, "mean", 4, 64)
+        torch.cuda.synchronize()
+        pages = np.concatenate([data.block_table[b, :nb[b]] for b in range(spec.num_seqs)])
+        np.testing.assert_array_equal(dw.kmean.cpu().numpy()[pages],
+                                      o.mean()[pages].astype(np.float32))
+        ref_gs, bound = o.mean_scores(), o.mean_score_bound()
+        check_scores(to_f64(dw.scores), ref_gs, nb, bound)
+        sel, cnt = dw.sel.cpu().numpy(), dw.sel_count.cpu().numpy()
+        check_selection_valid_forced(sel, cnt, dw.scores.cpu().numpy(), data.seq_lens, k, 4, 64)
+        rsel, rcnt = oracle.select(ref_gs, data.seq_lens, 16, k, 4, 64)
+        ndiff = check_selection_vs_oracle(
+            sel, cnt, rsel, rcnt, ref_gs, nb, bound=bound,
+            forced=lambda b: forced_blocks(int(data.seq_lens[b]), 16, 4, 64))
+        print(f"[{name}] mean selection ok ({ndiff} rows differ inside the band)", flush=True)
+        S = dw.decode(sparse=True)
+        ref_sp, _ = o.attention(sel, cnt)
+        rel = assert_rows_close(to_f64(dw.out), ref_sp, ROW_TOL[spec.dtype], f"{name} mean sparse")
+        print(f"[{name}] mean sparse ok, S={S}, worst row rel-err {rel:.2e}", flush=True)
+    finally:
+        torch.cuda.synchronize()
+        dw.close()
