@@ -328,9 +328,12 @@ __global__ __launch_bounds__(WAVES * kWave) void block_score_kernel(
 // above T, or equal to T and among the first K_eff - #{key > T} equal keys in
 // index order; one exclusive scan of packed (#greater, #equal) counts gives
 // every selected block its output position, so the list comes out ascending.
-// A block holding one of the first `sink` or the last `local` tokens takes the
-// key 0xFFFFFFFF, above every score's key: forced blocks are always selected
-// (the caller keeps their count <= K) and the others compete for the rest.
+// A block holding one of the first `sink` or the last `local` tokens is forced:
+// it is kept out of the radix select (its key slot is 0, like a block past
+// N_b, and a bit of the thread's forced mask records it), the select looks for
+// the (K_eff - #forced)-th largest key among the other blocks, and in the
+// output scan a forced block counts like a key above the threshold.  The
+// caller keeps #forced <= K, so #forced <= K_eff.
 
 __device__ inline uint32_t score_key(float f) {
   if (f == 0.0f) f = 0.0f;
@@ -377,7 +380,7 @@ __global__ __launch_bounds__(1024) void topk_kernel(const float* __restrict__ sc
                                                     int32_t* __restrict__ sel_count) {
   constexpr int NW = 1024 / kWave;
   __shared__ __align__(16) uint32_t hist[NW][256];
-  __shared__ uint32_t buf_a[NW], buf_b[NW], buf_c[NW];
+  __shared__ uint32_t buf_a[NW], buf_b[NW], buf_c[NW], buf_d[NW];
   __shared__ uint32_t state[2];
   const int j = blockIdx.x, b = blockIdx.y;
   const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid >> 6;
@@ -411,29 +414,43 @@ __global__ __launch_bounds__(1024) void topk_kernel(const float* __restrict__ sc
 #pragma unroll
     for (int r = 0; r < EPT; ++r) sc[r] = (n0 + r < maxN) ? row[n0 + r] : 0.0f;
   }
+  static_assert(EPT <= 32, "forced mask holds 32 blocks");
+  uint32_t fmask = 0u;
 #pragma unroll
   for (int r = 0; r < EPT; ++r) {
     key[r] = 0u;
-    if (n0 + r < nb) {
-      const int n = n0 + r;
-      const bool forced = n * kBlockSize < sink || (n + 1) * kBlockSize > local_from;
-      key[r] = forced ? 0xFFFFFFFFu : score_key(sc[r]);  // valid keys are >= key(-inf) > 0
-      kmn = min(kmn, key[r]);
-      kmx = max(kmx, key[r]);
+    const int n = n0 + r;
+    if (n < nb) {
+      if (n * kBlockSize < sink || (n + 1) * kBlockSize > local_from) {
+        fmask |= 1u << r;
+      } else {
+        key[r] = score_key(sc[r]);  // valid keys are >= key(-inf) > 0
+        kmn = min(kmn, key[r]);
+        kmx = max(kmx, key[r]);
+      }
     }
   }
   kmn = wave_min_u32(kmn);
   kmx = wave_max_u32(kmx);
-  if (lane == 0) { buf_a[wave] = kmn; buf_b[wave] = kmx; }
-  __syncthreads();
+  uint32_t nf = (uint32_t)__popc(fmask);
 #pragma unroll
-  for (int w = 0; w < NW; ++w) { kmn = min(kmn, buf_a[w]); kmx = max(kmx, buf_b[w]); }
+  for (int off = 1; off < kWave; off <<= 1) nf += (uint32_t)__shfl_xor((int)nf, off, kWave);
+  if (lane == 0) { buf_a[wave] = kmn; buf_b[wave] = kmx; buf_d[wave] = nf; }
+  __syncthreads();
+  nf = 0;
+#pragma unroll
+  for (int w = 0; w < NW; ++w) {
+    kmn = min(kmn, buf_a[w]);
+    kmx = max(kmx, buf_b[w]);
+    nf += buf_d[w];
+  }
 
+  // places left for the blocks that compete; with none, T is above every key
+  uint32_t krem = (uint32_t)keff - nf;
   // bits [lo, 32) of T are known; resolve the rest 8 bits at a time
   const uint32_t diff = kmn ^ kmx;
-  int lo = diff ? 32 - __clz(diff) : 0;
-  uint32_t prefix = (lo >= 32) ? 0u : (kmx >> lo) << lo;
-  uint32_t krem = (uint32_t)keff;
+  int lo = (krem == 0u) ? 0 : (diff ? 32 - __clz(diff) : 0);
+  uint32_t prefix = (krem == 0u) ? 0xFFFFFFFFu : ((lo >= 32) ? 0u : (kmx >> lo) << lo);
   while (lo > 0) {
     const int width = min(8, lo);
     const int shift = lo - width;
@@ -473,12 +490,14 @@ __global__ __launch_bounds__(1024) void topk_kernel(const float* __restrict__ sc
     krem = state[1];
     lo = shift;
   }
-  const uint32_t T = prefix;   // the K_eff-th largest key; krem of its copies are taken
+  const uint32_t T = prefix;   // the (K_eff - #forced)-th largest competing key; krem of its copies are taken
 
+  // forced blocks rank with the keys above T (key slot 0 never equals T > 0)
   uint32_t n_gt = 0, n_eq = 0;
 #pragma unroll
   for (int r = 0; r < EPT; ++r) {
-    n_gt += key[r] > T;
+    const bool f = (fmask >> r) & 1u;
+    n_gt += f || key[r] > T;
     n_eq += key[r] == T;
   }
   // own buffer: with no radix pass, slower waves may still read buf_a / buf_b
@@ -487,7 +506,7 @@ __global__ __launch_bounds__(1024) void topk_kernel(const float* __restrict__ sc
 #pragma unroll
   for (int r = 0; r < EPT; ++r) {
     const int n = tid * EPT + r;
-    if (key[r] > T) {
+    if (((fmask >> r) & 1u) || key[r] > T) {
       out[gt_before + min(eq_before, krem)] = n;
       ++gt_before;
     } else if (key[r] == T) {
