@@ -17,7 +17,12 @@ Also in the same run: the zero-copy variant (K/V pools in mapped pinned host
 memory; its roofline is the measured host-to-device copy bandwidth), and the
 fp64 oracle timed on the host cores on the same workload (cpu_baseline).
 
+Beside the step, kernel-level timings of the selection variants: the mean-key
+index (build and select) and either index with the first 4 / last 64 tokens
+forced in (selection_variants).
+
 Usage: python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-cpu-baseline]
+       [--no-variants | --only-variants] [--no-zero-copy] [--no-other-workloads]
        python bench.py --copy-calibration    (a plain 1 GiB device copy, for counter scaling)
 """
 from __future__ import annotations
@@ -157,20 +162,6 @@ def run_gpu(args, spec, data):
         if ev is not None:
             ev[len(actions)].record()
 
-    for i in range(args.warmup):
-        step(copies[i % len(copies)])
-    torch.cuda.synchronize()
-
-    # per-stage timing: eager launches bracketed by events on the launch stream
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(len(stages) + 1)]
-           for _ in range(args.steps)]
-    torch.cuda.synchronize()
-    for i in range(args.steps):
-        step(copies[i % len(copies)], evs[i])
-    torch.cuda.synchronize()
-    per_stage_ms = {s: float(np.mean([e[i].elapsed_time(e[i + 1]) for e in evs]))
-                    for i, s in enumerate(stages)}
-
     def time_loop(run_one):
         t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         torch.cuda.synchronize()
@@ -181,50 +172,6 @@ def run_gpu(args, spec, data):
         t1.record()
         torch.cuda.synchronize()
         return t0.elapsed_time(t1), time.perf_counter() - wall0
-
-    # whole-step timing, eager launches without stage events
-    eager_ms, _ = time_loop(lambda i: step(copies[i % len(copies)]))
-
-    # the dominant kernel alone: back-to-back dense launches over the rotated
-    # copies, so per-launch event overhead does not enter its average
-    dense_loop_ms, _ = time_loop(
-        lambda i: copies[i % len(copies)].attention(sparse=False, num_splits=s_dense))
-
-    # whole-step timing, one HIP graph per workload copy
-    launch = "hip_graph"
-    try:
-        graphs = []
-        side = torch.cuda.Stream()
-        for c in copies:
-            side.wait_stream(torch.cuda.current_stream())
-            with torch.cuda.stream(side):
-                step(c)
-            torch.cuda.current_stream().wait_stream(side)
-            g = torch.cuda.CUDAGraph()
-            with torch.cuda.graph(g):
-                step(c)
-            graphs.append(g)
-        for i in range(args.warmup):
-            graphs[i % len(graphs)].replay()
-        total_ms, wall = time_loop(lambda i: graphs[i % len(graphs)].replay())
-        del graphs
-    except RuntimeError as e:          # capture unavailable: report eager launches
-        log(f"[bench] graph capture failed ({e}); timing eager launches")
-        launch = "eager"
-        total_ms, wall = time_loop(lambda i: step(copies[i % len(copies)]))
-    # the per-token decode steps on their own, each one HIP graph per copy:
-    # sparse = append + score/Top-K + sparse attention + merge,
-    # dense  = append + dense attention + merge
-    def decode_sparse(c):
-        c.append()
-        c.score_topk(k)
-        c.attention(sparse=True, num_splits=s_sparse)
-        c.combine(s_sparse)
-
-    def decode_dense(c):
-        c.append()
-        c.attention(sparse=False, num_splits=s_dense)
-        c.combine(s_dense)
 
     def graph_us(fn):
         """Average replay time of one HIP graph per copy holding fn(copy)."""
@@ -248,10 +195,89 @@ def run_gpu(args, spec, data):
             ms_, _ = time_loop(lambda i: fn(copies[i % len(copies)]))
         return ms_ * 1e3 / args.steps
 
-    decode_us = {"sparse": graph_us(decode_sparse), "dense": graph_us(decode_dense)}
+    res = {"s_sparse": s_sparse, "s_dense": s_dense}
+    if not args.only_variants:
+        for i in range(args.warmup):
+            step(copies[i % len(copies)])
+        torch.cuda.synchronize()
+
+        # per-stage timing: eager launches bracketed by events on the launch stream
+        evs = [[torch.cuda.Event(enable_timing=True) for _ in range(len(stages) + 1)]
+               for _ in range(args.steps)]
+        torch.cuda.synchronize()
+        for i in range(args.steps):
+            step(copies[i % len(copies)], evs[i])
+        torch.cuda.synchronize()
+        per_stage_ms = {s: float(np.mean([e[i].elapsed_time(e[i + 1]) for e in evs]))
+                        for i, s in enumerate(stages)}
+
+        # whole-step timing, eager launches without stage events
+        eager_ms, _ = time_loop(lambda i: step(copies[i % len(copies)]))
+
+        # the dominant kernel alone: back-to-back dense launches over the rotated
+        # copies, so per-launch event overhead does not enter its average
+        dense_loop_ms, _ = time_loop(
+            lambda i: copies[i % len(copies)].attention(sparse=False, num_splits=s_dense))
+
+        # whole-step timing, one HIP graph per workload copy
+        launch = "hip_graph"
+        try:
+            graphs = []
+            side = torch.cuda.Stream()
+            for c in copies:
+                side.wait_stream(torch.cuda.current_stream())
+                with torch.cuda.stream(side):
+                    step(c)
+                torch.cuda.current_stream().wait_stream(side)
+                g = torch.cuda.CUDAGraph()
+                with torch.cuda.graph(g):
+                    step(c)
+                graphs.append(g)
+            for i in range(args.warmup):
+                graphs[i % len(graphs)].replay()
+            total_ms, wall = time_loop(lambda i: graphs[i % len(graphs)].replay())
+            del graphs
+        except RuntimeError as e:          # capture unavailable: report eager launches
+            log(f"[bench] graph capture failed ({e}); timing eager launches")
+            launch = "eager"
+            total_ms, wall = time_loop(lambda i: step(copies[i % len(copies)]))
+        # the per-token decode steps on their own, each one HIP graph per copy:
+        # sparse = append + score/Top-K + sparse attention + merge,
+        # dense  = append + dense attention + merge
+        def decode_sparse(c):
+            c.append()
+            c.score_topk(k)
+            c.attention(sparse=True, num_splits=s_sparse)
+            c.combine(s_sparse)
+
+        def decode_dense(c):
+            c.append()
+            c.attention(sparse=False, num_splits=s_dense)
+            c.combine(s_dense)
+
+        decode_us = {"sparse": graph_us(decode_sparse), "dense": graph_us(decode_dense)}
+        res.update({
+            "total_ms": total_ms, "wall_s": wall, "stage_ms": per_stage_ms,
+            "decode_us": decode_us, "launch": launch,
+            "dense_attn_loop_us": dense_loop_ms * 1e3 / args.steps,
+            "eager_ms_per_step": eager_ms / args.steps,
+        })
 
     # selection variants, kernel level (not part of the step): the mean-key
     # index, and either index with the first 4 / last 64 tokens forced in
+    variants = None if args.no_variants else time_variants(args, copies, k, s_sparse,
+                                                            time_loop, graph_us)
+    for c in copies:
+        c.close()
+    del copies
+    torch.cuda.empty_cache()
+    res["variants"] = variants
+    return res
+
+
+def time_variants(args, copies, k, s_sparse, time_loop, graph_us):
+    import torch
+
     def kernel_us(fn):
         for i in range(args.warmup):
             fn(copies[i % len(copies)])
@@ -276,18 +302,7 @@ def run_gpu(args, spec, data):
         c.combine(s_sparse)
 
     variants["decode_sparse_mean_forced_us"] = graph_us(decode_sparse_mean)
-
-    for c in copies:
-        c.close()
-    del copies
-    torch.cuda.empty_cache()
-    return {
-        "total_ms": total_ms, "wall_s": wall, "stage_ms": per_stage_ms,
-        "decode_us": decode_us, "variants": variants,
-        "s_sparse": s_sparse, "s_dense": s_dense, "launch": launch,
-        "dense_attn_loop_us": dense_loop_ms * 1e3 / args.steps,
-        "eager_ms_per_step": eager_ms / args.steps,
-    }
+    return variants
 
 
 def run_other_workload(args, name):
@@ -490,6 +505,10 @@ def main():
     ap.add_argument("--copy-calibration", action="store_true")
     ap.add_argument("--only-zero-copy", action="store_true",
                     help="run only the host-KV variant (for profiling it)")
+    ap.add_argument("--no-variants", action="store_true",
+                    help="skip the selection-variant timings (mean-key index, forced tokens)")
+    ap.add_argument("--only-variants", action="store_true",
+                    help="run only the selection-variant timings (for profiling them)")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -513,6 +532,11 @@ def main():
     spec = wl.WORKLOADS[WORKLOAD]
     log(f"[bench] generating {spec.name}")
     data = wl.generate(spec)
+    if args.only_variants:
+        args.no_variants = False
+        g = run_gpu(args, spec, data)
+        print(json.dumps({"selection_variants": variants_record(spec, g["variants"])}), flush=True)
+        return
     log("[bench] timing GPU steps")
     g = run_gpu(args, spec, data)
     sb = stage_bytes(spec, spec.topk_blocks, g["s_sparse"], g["s_dense"])
@@ -591,7 +615,7 @@ def main():
             "avg_launch_us": dense_us,
             "timing": f"{args.steps} back-to-back launches between two HIP events",
         },
-        "selection_variants": variants_record(spec, g["variants"]),
+        "selection_variants": variants_record(spec, g["variants"]) if g["variants"] else None,
         "other_workloads": others,
         "zero_copy": zc,
         "cpu_baseline": cpu,

@@ -190,16 +190,23 @@ __global__ __launch_bounds__(kWave) void append_token_kernel(
     }
   }
   if (kmean) {
-    // slots before s come from the cache; this lane wrote none of them
+    // slots before s come from the cache (this lane wrote none of them), slot s
+    // is the new key; all rows of the page are loaded at once, rows past s unused
     const St* rows = static_cast<const St*>(k_cache) + tile * kBlockSize * D + (size_t)c * E;
+    uint4 w[kBlockSize];
+#pragma unroll
+    for (int t = 0; t < kBlockSize; ++t) w[t] = (t < s) ? load16(rows + (size_t)t * D) : kw;
     double acc[E];
 #pragma unroll
     for (int e = 0; e < E; ++e) acc[e] = 0.0;
-    for (int t = 0; t <= s; ++t) {
-      float f[E];
-      DT::widen(t < s ? load16(rows + (size_t)t * D) : kw, f);
 #pragma unroll
-      for (int e = 0; e < E; ++e) acc[e] += (double)f[e];
+    for (int t = 0; t < kBlockSize; ++t) {
+      if (t <= s) {
+        float f[E];
+        DT::widen(w[t], f);
+#pragma unroll
+        for (int e = 0; e < E; ++e) acc[e] += (double)f[e];
+      }
     }
     float mv[E];
 #pragma unroll
