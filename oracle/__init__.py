@@ -14,6 +14,9 @@ Functions (each computed as oracle.c states it):
 * ``block_mean``      mean key per (page, KV head)             (KVDrive §2.3, §4)
 * ``head_scores_mean``  q . mean key per (sequence, query head, block)
 * ``select``          Top-K with the first / last tokens' blocks forced in  (KVDrive §9.1)
+* ``fp8_encode`` / ``fp8_decode``  OCP FP8 E4M3 codes (round to nearest even, saturating)
+* ``fp8_quantize``    per-(page, KV head) scaled E4M3 pages      (KVDrive §11; DirectKV review)
+* ``fp8_dequantize``  decode(code) * scale
 * ``attention``       softmax decode attention, dense or over selected blocks
                       (Dual-Blade background; KVDrive §2.3 step 3)
 * ``attention_splits``  the same on each contiguous chunk of the block list
@@ -55,6 +58,14 @@ def _load():
     lib.oracle_block_mean.argtypes = [_D, _int, _int, _int, _I, _I, _int, _D]
     lib.oracle_head_scores_mean.argtypes = [_D, _D, _I, _I, _int, _int, _int, _int, _int, _int, _D]
     lib.oracle_select.argtypes = [_D, _I, _int, _int, _int, _int, _int, _int, _int, _I, _I]
+    _U8 = ctypes.POINTER(ctypes.c_uint8)
+    _F = ctypes.POINTER(ctypes.c_float)
+    lib.oracle_fp8_decode.argtypes = [ctypes.c_uint8]
+    lib.oracle_fp8_decode.restype = ctypes.c_double
+    lib.oracle_fp8_encode.argtypes = [ctypes.c_float]
+    lib.oracle_fp8_encode.restype = ctypes.c_uint8
+    lib.oracle_fp8_quantize.argtypes = [_D, _int, _int, _int, _I, _I, _int, _U8, _F, _int]
+    lib.oracle_fp8_quantize.restype = None
     lib.oracle_topk.argtypes = [_D, _I, _int, _int, _int, _int, _int, _I, _I]
     lib.oracle_attention.argtypes = [_D, _D, _D, _I, _I, _I, _I, _int, _int, _int, _int, _int,
                                      _int, _int, ctypes.c_double, _D, _D]
@@ -149,6 +160,41 @@ def select(group_scores_, seq_lens, block_size: int, k: int, sink: int = 0, loca
     _load().oracle_select(_pd(gs), _pi(sl), B, Hkv, maxN, block_size, k, sink, local, _pi(sel),
                           _pi(cnt))
     return sel, cnt
+
+
+def fp8_decode(codes) -> np.ndarray:
+    """Value of each FP8 E4M3 code (uint8 array), float64."""
+    lib = _load()
+    c = np.ascontiguousarray(codes, dtype=np.uint8)
+    table = np.array([lib.oracle_fp8_decode(i) for i in range(256)])
+    return table[c]
+
+
+def fp8_encode(values) -> np.ndarray:
+    """E4M3 code of each float32 value (round to nearest even, saturating)."""
+    lib = _load()
+    v = np.ascontiguousarray(values, dtype=np.float32)
+    return np.array([lib.oracle_fp8_encode(float(x)) for x in v.ravel()],
+                    dtype=np.uint8).reshape(v.shape)
+
+
+def fp8_quantize(pool, page_ids, valid_tokens):
+    """(codes uint8 [P, Hkv, bs, D], scales float32 [P, Hkv]) of the listed pages;
+    pages not listed keep code 0 and scale 0."""
+    x = _f64(pool)
+    P, Hkv, bs, D = x.shape
+    ids, val = _i32(page_ids), _i32(valid_tokens)
+    codes = np.zeros((P, Hkv, bs, D), dtype=np.uint8)
+    scales = np.zeros((P, Hkv), dtype=np.float32)
+    _load().oracle_fp8_quantize(_pd(x), Hkv, bs, D, _pi(ids), _pi(val), len(ids),
+                                codes.ctypes.data_as(ctypes.POINTER(ctypes.c_uint8)),
+                                scales.ctypes.data_as(ctypes.POINTER(ctypes.c_float)), 1)
+    return codes, scales
+
+
+def fp8_dequantize(codes, scales) -> np.ndarray:
+    """decode(code) * scale per (page, KV head), float64 [P, Hkv, bs, D]."""
+    return fp8_decode(codes) * np.asarray(scales, np.float64)[:, :, None, None]
 
 
 def group_scores(head_scores_, num_kv_heads: int) -> np.ndarray:

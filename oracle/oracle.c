@@ -44,7 +44,17 @@
  *    first tokens and the most recent tokens): every block holding one of the
  *    first `sink` or the last `local` tokens of a sequence is selected and
  *    counts against the budget K; the other K_eff - |forced| places go to the
- *    best of the remaining blocks.
+ *    best of the remaining blocks;
+ *  - quantised cold pages (KVDrive §11 future work: cold blocks stored with
+ *    aggressive quantisation, hot blocks in high precision; DirectKV review,
+ *    "Assumption stress test": FP8/INT4 KV): K and V pages as FP8 E4M3 codes
+ *    (the OCP 8-bit floating-point format: bias 7, 3 mantissa bits, no
+ *    infinities, largest finite value 448) with one fp32 scale per (page, KV
+ *    head) and tensor: s = amax / 448 over the valid slots (1 for an all-zero
+ *    tile), code = round-to-nearest-even(x / s) saturated to +-448, code 0 for
+ *    slots past the valid count; the value a code stands for is
+ *    decode(code) * s.  The scale and the quotient are taken in fp32, the
+ *    precision in which the quantiser decides the codes.
  */
 #include <math.h>
 #include <stdint.h>
@@ -275,6 +285,84 @@ void oracle_select(const double* group_scores, const int32_t* seq_lens, int B, i
       }
       for (i64 r = w; r < K; ++r) out[r] = -1;
       sel_count[(i64)b * Hkv + j] = (int32_t)w;
+    }
+  }
+}
+
+/*
+ * FP8 E4M3 (OCP 8-bit floating point, E4M3 variant).  A code is s eeee mmm:
+ * e = 0 encodes the subnormals m * 2^-9, e = 1..15 the normals
+ * (1 + m/8) * 2^(e - 7); s eeee mmm = s 1111 111 is NaN (never produced here),
+ * so the largest finite magnitude is 1.75 * 2^8 = 448.
+ */
+double oracle_fp8_decode(uint8_t code) {
+  const int e = (code >> 3) & 15, m = code & 7;
+  if (e == 15 && m == 7) return NAN;
+  const double mag = (e == 0) ? ldexp((double)m, -9) : ldexp(8.0 + m, e - 10);
+  return (code & 0x80) ? -mag : mag;
+}
+
+/*
+ * Encode an fp32 value: round to the nearest E4M3 value, ties to the even
+ * code (even mantissa), magnitudes that round past 448 saturate to 448.  The
+ * representable magnitudes of exponent ex are multiples of 2^(ex - 3) for
+ * 2^ex <= |y| < 2^(ex+1), ex >= -6; below 2^-6 they are multiples of 2^-9.
+ */
+uint8_t oracle_fp8_encode(float y) {
+  const uint8_t sign = signbit(y) ? 0x80 : 0x00;
+  const double a = fabs((double)y);
+  if (isnan(a)) return (uint8_t)(sign | 0x7F);
+  int e2;
+  frexp(a, &e2);                       /* a = f * 2^e2, f in [0.5, 1) */
+  int ex = (a == 0.0) ? -6 : e2 - 1;   /* floor(log2 a) */
+  if (ex < -6) ex = -6;
+  const double step = ldexp(1.0, ex - 3);
+  double r = nearbyint(a / step) * step; /* exact: a / step is a power-of-two scaling */
+  if (r > 448.0) r = 448.0;
+  if (r == 0.0) return sign;
+  frexp(r, &e2);
+  int er = e2 - 1;
+  if (er < -6) return (uint8_t)(sign | (uint8_t)(r / ldexp(1.0, -9)));   /* subnormal */
+  const int m = (int)((r / ldexp(1.0, er) - 1.0) * 8.0);
+  return (uint8_t)(sign | ((er + 7) << 3) | m);
+}
+
+/*
+ * Quantise the listed pages of one pool (K or V): for i < n_ids and KV head j,
+ * p = page_ids[i], v = valid_tokens[i]:
+ *   amax = max_{s < v, c} |X[p, j, s, c]|  (fp32 values of the stored dtype)
+ *   scale[p, j] = amax / 448 in fp32, or 1 when amax == 0
+ *   code[p, j, s, c] = encode(X / scale in fp32) for s < v, 0 for s >= v.
+ * codes: uint8 [P, Hkv, bs, D]; scales: float [P, Hkv] (strided by
+ * scale_stride floats, so K and V scales can interleave).
+ */
+void oracle_fp8_quantize(const double* pool, int Hkv, int bs, int D, const int32_t* page_ids,
+                         const int32_t* valid_tokens, int n_ids, uint8_t* codes, float* scales,
+                         int scale_stride) {
+#pragma omp parallel for schedule(static)
+  for (int i = 0; i < n_ids; ++i) {
+    const i64 p = page_ids[i];
+    const int nv = valid_tokens[i];
+    for (int j = 0; j < Hkv; ++j) {
+      float amax = 0.0f;
+      for (int s = 0; s < nv; ++s) {
+        const double* row = pool_row(pool, p, j, s, Hkv, bs, D);
+        for (int c = 0; c < D; ++c) {
+          const float x = fabsf((float)row[c]);
+          if (x > amax) amax = x;
+        }
+      }
+      const float sc = (amax > 0.0f) ? amax / 448.0f : 1.0f;
+      scales[(p * Hkv + j) * (i64)scale_stride] = sc;
+      for (int s = 0; s < bs; ++s) {
+        uint8_t* out = codes + ((p * Hkv + j) * bs + s) * (i64)D;
+        if (s >= nv) {
+          memset(out, 0, (size_t)D);
+          continue;
+        }
+        const double* row = pool_row(pool, p, j, s, Hkv, bs, D);
+        for (int c = 0; c < D; ++c) out[c] = oracle_fp8_encode((float)row[c] / sc);
+      }
     }
   }
 }

@@ -44,6 +44,14 @@ MUTANTS = [
     ("forced_not_counted_against_k", "const i64 free_slots = keff - n_forced;",
      "const i64 free_slots = keff;", 0),
     ("forced_blocks_compete_for_rank", "if (is_forced(m, L, bs, sink, local)) continue;", "", 0),
+    ("fp8_decode_bias_8", "ldexp(8.0 + m, e - 10)", "ldexp(8.0 + m, e - 11)", 0),
+    ("fp8_subnormal_step", "ldexp((double)m, -9)", "ldexp((double)m, -10)", 0),
+    ("fp8_round_half_away", "double r = nearbyint(a / step) * step;", "double r = round(a / step) * step;", 0),
+    ("fp8_no_saturation", "if (r > 448.0) r = 448.0;", "", 0),
+    ("fp8_scale_240", "amax / 448.0f", "amax / 240.0f", 0),
+    ("fp8_amax_over_every_slot", "for (int s = 0; s < nv; ++s) {\n        const double* row = pool_row(pool",
+     "for (int s = 0; s < bs; ++s) {\n        const double* row = pool_row(pool", 0),
+    ("fp8_tail_slots_encoded", "if (s >= nv) {\n          memset", "if (s >= bs) {\n          memset", 0),
     ("combine_lse_drops_max", "if (lse) lse[r] = M + log(wsum);", "if (lse) lse[r] = log(wsum);", 0),
 ]
 

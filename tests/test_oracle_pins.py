@@ -610,3 +610,112 @@ def test_select_without_forcing_is_topk():
         a = oracle.select(gs, lens, 16, k)
         b = oracle.topk(gs, lens, 16, k)
         assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
+
+
+# ---------------------------------------------------------------- FP8 E4M3 cold pages
+# OCP 8-bit floating point (E4M3); quantised cold pages per KVDrive §11 and the
+# DirectKV review's assumption stress test
+
+def _torch_e4m3(values_f32):
+    return torch.from_numpy(np.ascontiguousarray(values_f32, np.float32)).to(
+        torch.float8_e4m3fn).view(torch.uint8).numpy()
+
+
+def test_fp8_golden(variants):
+    g = variants["fp8_e4m3"]
+    for d in g["decode"]:
+        v = oracle.fp8_decode(np.array([d["code"]]))[0]
+        assert v == d["value"] and np.signbit(v) == np.signbit(d["value"]), d
+    codes = oracle.fp8_encode(np.array([e["value"] for e in g["encode"]], np.float32))
+    assert codes.tolist() == [e["code"] for e in g["encode"]]
+    q = g["quantize"]
+    x = np.array(q["x_slots"], np.float64).reshape(1, 1, q["block_size"], q["head_dim"])
+    c, s = oracle.fp8_quantize(x, [0], [q["valid_tokens"]])
+    assert s[0, 0] == q["scale"]
+    assert c[0, 0].tolist() == q["codes"]
+
+
+def test_fp8_decode_matches_torch_float8_e4m3fn():
+    ref = torch.arange(256, dtype=torch.uint8).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    got = oracle.fp8_decode(np.arange(256))
+    nan = np.isnan(ref)
+    assert np.array_equal(np.isnan(got), nan) and nan.sum() == 2      # 0x7F and 0xFF
+    assert np.array_equal(got[~nan], ref[~nan])
+    assert np.array_equal(np.signbit(got[~nan]), np.signbit(ref[~nan]))
+
+
+@pytest.mark.parametrize("seed", range(3))
+def test_fp8_encode_matches_torch_in_range(seed):
+    """torch rounds to nearest even; it gives NaN past 464 where the oracle
+    saturates, so the comparison stays below 464.  Every grid midpoint is
+    included (the ties)."""
+    rng = np.random.default_rng(300 + seed)
+    y = (rng.standard_normal(100000) * rng.choice([1e-5, 1e-3, 1e-1, 1, 30, 300], 100000))
+    grid = oracle.fp8_decode(np.arange(0, 127))                     # the non-negative finite values
+    mids = (grid[:-1] + grid[1:]) / 2
+    y = np.concatenate([y, grid, mids, -mids, np.nextafter(mids, 0), np.nextafter(mids, 1e9)])
+    y = y.astype(np.float32)
+    y = y[np.abs(y) < 464]
+    np.testing.assert_array_equal(oracle.fp8_encode(y), _torch_e4m3(y))
+
+
+def test_fp8_encode_saturates_and_round_trips():
+    assert oracle.fp8_encode(np.array([464, 480, 1e30, -500], np.float32)).tolist() == [
+        0x7E, 0x7E, 0x7E, 0xFE]
+    codes = np.array([c for c in range(256) if c not in (0x7F, 0xFF)], np.uint8)
+    vals = oracle.fp8_decode(codes).astype(np.float32)
+    back = oracle.fp8_encode(vals)
+    assert np.array_equal(back, codes)          # every finite code, -0 included
+
+
+@pytest.mark.parametrize("dtype", ["f32", "f16", "bf16"])
+def test_fp8_quantize_matches_torch_and_error_bound(dtype):
+    data = mk(B=2, Hq=4, Hkv=2, D=16, lens=(45, 16), dtype=dtype, seed=41, extra_pages=1)
+    k64 = data.k64()
+    ids, val = page_lists(data)
+    codes, scales = oracle.fp8_quantize(k64, ids, val)
+    x32 = k64.astype(np.float32)
+    for p, nv in zip(ids, val):
+        for j in range(2):
+            tile = x32[p, j, :nv]
+            amax = np.abs(tile).max()
+            s = scales[p, j]
+            # the largest magnitude lands on +-448 (code 0x7E / 0xFE)
+            big = np.abs(tile) == amax
+            assert np.all((codes[p, j, :nv][big] & 0x7F) == 0x7E)
+            # the codes are torch's conversion of x / s taken in fp32
+            np.testing.assert_array_equal(codes[p, j, :nv], _torch_e4m3(tile / s))
+            # round-to-nearest error: half a grid step
+            deq = oracle.fp8_decode(codes[p, j, :nv]) * float(s)
+            y = np.abs(tile.astype(np.float64)) / float(s)
+            half = np.where(y >= 2.0 ** -6, 2.0 ** (np.floor(np.log2(np.maximum(y, 2.0 ** -6))) - 4),
+                            2.0 ** -10) * float(s)
+            assert np.all(np.abs(deq - tile) <= half * (1 + 1e-6))
+            assert np.all(codes[p, j, nv:] == 0)
+    untouched = np.setdiff1d(np.arange(k64.shape[0]), ids)
+    assert untouched.size and np.all(codes[untouched] == 0) and np.all(scales[untouched] == 0)
+
+
+def test_fp8_quantize_zero_tile_has_unit_scale():
+    x = np.zeros((1, 2, 16, 8))
+    x[0, 1, 3, 2] = -1.5
+    codes, scales = oracle.fp8_quantize(x, [0], [16])
+    assert scales[0, 0] == 1.0 and np.all(codes[0, 0] == 0)
+    assert scales[0, 1] == np.float32(1.5) / np.float32(448)
+    assert codes[0, 1, 3, 2] == 0xFE
+
+
+def test_fp8_dequantized_attention_is_attention_over_decoded_values():
+    """Attention over fp8 pages is the plain attention over decode(code) * scale:
+    checked against torch's fused attention on the decoded tensors."""
+    data = mk(B=1, Hq=2, Hkv=1, D=16, lens=(40,), seed=42)
+    ids, val = page_lists(data)
+    kc, ks = oracle.fp8_quantize(data.k64(), ids, val)
+    vc, vs = oracle.fp8_quantize(data.v64(), ids, val)
+    kd, vd = oracle.fp8_dequantize(kc, ks), oracle.fp8_dequantize(vc, vs)
+    out, _ = oracle.attention(data.q64(), kd, vd, data.block_table, data.seq_lens, 0.25)
+    for h in range(2):
+        K = gather(kd, data, 0, 0, range(3))
+        V = gather(vd, data, 0, 0, range(3))
+        np.testing.assert_allclose(out[0, h], sdpa(data.q64()[0, h], K, V, 0.25), rtol=1e-12,
+                                   atol=1e-14)
