@@ -267,11 +267,48 @@ def run_gpu(args, spec, data):
     # index, and either index with the first 4 / last 64 tokens forced in
     variants = None if args.no_variants else time_variants(args, copies, k, s_sparse,
                                                             time_loop, graph_us)
+    # FP8 E4M3 cold pages in HBM: the same attention over 1-byte codes
+    fp8 = None if args.no_variants else time_fp8(args, copies, k, s_sparse, s_dense, time_loop,
+                                                 graph_us)
     for c in copies:
         c.close()
     del copies
     torch.cuda.empty_cache()
     res["variants"] = variants
+    res["fp8"] = fp8
+    return res
+
+
+def time_fp8(args, copies, k, s_sparse, s_dense, time_loop, graph_us):
+    import torch
+
+    def kernel_us(fn):
+        for i in range(args.warmup):
+            fn(copies[i % len(copies)])
+        ms_, _ = time_loop(lambda i: fn(copies[i % len(copies)]))
+        return ms_ * 1e3 / args.steps
+
+    for c in copies:
+        c.quantize_fp8(host=False)
+        c.score_topk(k)
+    torch.cuda.synchronize()
+    res = {
+        "quantize_us": kernel_us(lambda c: c.quantize_fp8(host=False)),
+        "dense_attn_us": kernel_us(lambda c: c.attention_fp8(sparse=False, num_splits=s_dense)),
+        "sparse_attn_us": kernel_us(lambda c: c.attention_fp8(sparse=True, num_splits=s_sparse)),
+    }
+
+    def decode_sparse_fp8(c):
+        c.score_topk(k)
+        c.attention_fp8(sparse=True, num_splits=s_sparse)
+        c.combine(s_sparse)
+
+    def decode_dense_fp8(c):
+        c.attention_fp8(sparse=False, num_splits=s_dense)
+        c.combine(s_dense)
+
+    res["decode_sparse_us"] = graph_us(decode_sparse_fp8)
+    res["decode_dense_us"] = graph_us(decode_dense_fp8)
     return res
 
 
@@ -391,6 +428,18 @@ def run_zero_copy(args):
     e[1].record()
     torch.cuda.synchronize()
     dense_ms = e[0].elapsed_time(e[1])
+    # the same sparse step over FP8 E4M3 code pages in host memory: half the bytes
+    fp8_ms = []
+    if not args.no_variants:
+        dw.quantize_fp8(host=True)
+        for _ in range(3):
+            dw.attention_fp8(sparse=True, num_splits=S)
+        for _ in range(reps):
+            e[0].record()
+            dw.attention_fp8(sparse=True, num_splits=S)
+            e[1].record()
+            torch.cuda.synchronize()
+            fp8_ms.append(e[0].elapsed_time(e[1]))
     dw.close()
 
     # measured host-to-device copy bandwidth: 256 MiB from pinned memory, best of 10
@@ -413,7 +462,16 @@ def run_zero_copy(args):
     dense_link_bytes = spec.used_pages * spec.num_kv_heads * 2 * spec.block_size * spec.head_dim * eb
     attn = float(np.median(attn_ms))
     host_gbps = link_bytes / (attn * 1e-3) / 1e9
+    fp8 = None
+    if fp8_ms:
+        f8 = float(np.median(fp8_ms))
+        f8_bytes = link_bytes // eb
+        fp8 = {"sparse_attn_us": f8 * 1e3, "host_link_bytes": f8_bytes,
+               "host_link_gbps": f8_bytes / (f8 * 1e-3) / 1e9,
+               "frac_of_h2d": f8_bytes / (f8 * 1e-3) / 1e9 / h2d_gbps,
+               "speedup_vs_bf16": attn / f8}
     return {
+        "fp8_pages": fp8,
         "workload": HOSTKV_WORKLOAD,
         "sparse_attn_us": attn * 1e3,
         "sparse_combine_us": float(np.median(comb_ms)) * 1e3,
@@ -480,6 +538,34 @@ def copy_calibration():
     print(json.dumps({"copy_bytes_read": n, "copy_bytes_written": n}), flush=True)
 
 
+def fp8_record(spec, f: dict, s_sparse: int, s_dense: int) -> dict:
+    """FP8 E4M3 cold pages in HBM: per (page, KV head) unit the attention reads
+    2 * 16 * D code bytes and 8 bytes of scales instead of 2 * 16 * D * eb."""
+    D, Hkv, B, Hq = spec.head_dim, spec.num_kv_heads, spec.num_seqs, spec.num_q_heads
+    k = spec.topk_blocks
+    unit = 2 * spec.block_size * D + 8
+    keff = sum(min(k, spec.blocks(b)) for b in range(B))
+    part = lambda S: B * Hq * S * (D + 2) * 4
+    q_bytes = B * Hq * D * spec.elem_bytes
+    dense_b = spec.used_pages * Hkv * (unit + 4) + q_bytes + part(s_dense)
+    sparse_b = keff * Hkv * (unit + 8) + q_bytes + part(s_sparse)
+    quant_b = spec.used_pages * Hkv * (2 * spec.block_size * D * (spec.elem_bytes + 1) + 8) \
+        + spec.used_pages * 8
+    dense_gbps = dense_b / (f["dense_attn_us"] * 1e-6) / 1e9
+    return {
+        "format": "OCP FP8 E4M3, one fp32 scale per (page, KV head) and tensor",
+        "quantize": {"us": f["quantize_us"], "bytes": quant_b,
+                     "gbps": quant_b / (f["quantize_us"] * 1e-6) / 1e9},
+        "dense_attn": {"us": f["dense_attn_us"], "bytes": dense_b, "gbps": dense_gbps,
+                       "frac_of_hbm_peak": dense_gbps / HBM_PEAK_GBPS},
+        "sparse_attn": {"us": f["sparse_attn_us"], "bytes": sparse_b,
+                        "gbps": sparse_b / (f["sparse_attn_us"] * 1e-6) / 1e9},
+        "decode_step_us": {"sparse": f["decode_sparse_us"], "dense": f["decode_dense_us"]},
+        "decode_steps_per_s": {"sparse": 1e6 / f["decode_sparse_us"],
+                               "dense": 1e6 / f["decode_dense_us"]},
+    }
+
+
 def variants_record(spec, v: dict) -> dict:
     vb = variant_bytes(spec, spec.topk_blocks)
     rec = {"forced_tokens": {"sink": 4, "local": 64}}
@@ -506,9 +592,9 @@ def main():
     ap.add_argument("--only-zero-copy", action="store_true",
                     help="run only the host-KV variant (for profiling it)")
     ap.add_argument("--no-variants", action="store_true",
-                    help="skip the selection-variant timings (mean-key index, forced tokens)")
+                    help="skip the variant timings (mean-key index, forced tokens, FP8 pages)")
     ap.add_argument("--only-variants", action="store_true",
-                    help="run only the selection-variant timings (for profiling them)")
+                    help="run only the variant timings (for profiling them)")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -535,7 +621,9 @@ def main():
     if args.only_variants:
         args.no_variants = False
         g = run_gpu(args, spec, data)
-        print(json.dumps({"selection_variants": variants_record(spec, g["variants"])}), flush=True)
+        print(json.dumps({"selection_variants": variants_record(spec, g["variants"]),
+                          "fp8_pages": fp8_record(spec, g["fp8"], g["s_sparse"], g["s_dense"])}),
+              flush=True)
         return
     log("[bench] timing GPU steps")
     g = run_gpu(args, spec, data)
@@ -616,6 +704,7 @@ def main():
             "timing": f"{args.steps} back-to-back launches between two HIP events",
         },
         "selection_variants": variants_record(spec, g["variants"]) if g["variants"] else None,
+        "fp8_pages": fp8_record(spec, g["fp8"], g["s_sparse"], g["s_dense"]) if g.get("fp8") else None,
         "other_workloads": others,
         "zero_copy": zc,
         "cpu_baseline": cpu,

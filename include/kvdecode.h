@@ -8,6 +8,8 @@
  *   kv_block_mean_build   mean key of every KV page (the mean-key block index)
  *   kv_block_select       block scores from either index, then Top-K with the
  *                         blocks of the first / last tokens forced in
+ *   kv_quantize_pages_fp8 K/V pages -> FP8 E4M3 cold pages with per-page scales
+ *   kv_paged_decode_attn_fp8  decode attention over FP8 E4M3 cold pages
  *   kv_paged_decode_attn  split-K softmax decode attention, dense or over selected blocks
  *   kv_decode_combine     log-sum-exp merge of the split partials
  *   kv_append_token       store the new token's K/V and fold it into its page's meta
@@ -41,6 +43,8 @@
  *     K, V     [P, Hkv, bs, D]       dtype   (page p, KV head j, slot s, channel c)
  *     kmeta    [P, Hkv, 2, D]        dtype   (index 0 = channel min, 1 = channel max)
  *     kmean    [P, Hkv, D]           fp32    (mean key of the page's valid slots)
+ *     K8, V8   [P, Hkv, bs, D]       uint8   FP8 E4M3 codes of cold pages
+ *     kv_scales [P, Hkv, 2]          fp32    (K scale, V scale) of each cold page
  *     block_table int32 [B, maxN]    logical block n of sequence b -> page
  *     seq_lens    int32 [B]          L_b >= 1 tokens, current token included,
  *                                    N_b = ceil(L_b / bs) <= maxN
@@ -50,7 +54,8 @@
  *     part_o   fp32 [B, Hq, S, D]    per-split normalised output
  *     part_m, part_l fp32 [B, Hq, S] per-split max logit and sum of exp(logit - max)
  *     out      fp32 [B, Hq, D];  lse fp32 [B, Hq]
- * - Alignment: q, K, V, kmeta and kmean 16 bytes; part_o and out 16 bytes; the rest 4.
+ * - Alignment: q, K, V, K8, V8, kmeta and kmean 16 bytes; part_o and out 16 bytes;
+ *   kv_scales 8; the rest 4.
  */
 #ifndef KVDECODE_H
 #define KVDECODE_H
@@ -238,6 +243,44 @@ kv_status kv_paged_decode_attn(const kv_shape* shape, const void* q, const void*
 kv_status kv_decode_combine(const kv_shape* shape, int32_t num_splits, const float* part_o,
                             const float* part_m, const float* part_l, float* out, float* lse_out,
                             void* stream);
+
+/*
+ * FP8 cold pages (KVDrive §11: cold blocks stored with aggressive quantisation
+ * while hot blocks keep high precision; DirectKV review, assumption stress
+ * test: FP8 KV).  The format is OCP FP8 E4M3 (bias 7, no infinities, largest
+ * finite value 448).  For i < num_page_ids, every KV head j and tensor
+ * X in {K, V}, with p = page_ids[i] and v = page_valid_tokens[i] in [1, bs]:
+ *   amax = max_{s < v, c} |X[p, j, s, c]|
+ *   kv_scales[p, j, t] = amax / 448 (fp32, correctly rounded; 1 if amax == 0),
+ *                        t = 0 for K, 1 for V
+ *   X8[p, j, s, c] = E4M3 code of X[p, j, s, c] / scale (fp32, correctly
+ *                    rounded), rounded to nearest with ties to the even code,
+ *                    saturated to +-448;  0 for s >= v.
+ * The codes are a deterministic function of the stored values.  K/V keep the
+ * layout of the source pools with one byte per channel.  Pages not listed are
+ * not touched; ids as in kv_block_meta_build.  The block index (kmeta, kmean)
+ * is built from the high-precision keys and is not affected.
+ */
+kv_status kv_quantize_pages_fp8(const kv_shape* shape, const void* k_cache, const void* v_cache,
+                                const int32_t* page_ids, const int32_t* page_valid_tokens,
+                                int32_t num_page_ids, uint8_t* k_fp8, uint8_t* v_fp8,
+                                float* kv_scales, void* stream);
+
+/*
+ * kv_paged_decode_attn over FP8 E4M3 cold pages: every K and V value is
+ * decode(code) * scale of its (page, KV head), and the call computes exactly
+ * what kv_paged_decode_attn computes over those values (fp32 accumulation;
+ * the decoded codes are exact in the 16-bit MFMA operands, the K scale
+ * multiplies the logits and the V scale the softmax weights).  q keeps
+ * shape->dtype.  kv_scales must be device memory; with KV_FLAG_HOST_KV the code
+ * pools may be device pointers of kv_host_alloc memory.
+ */
+kv_status kv_paged_decode_attn_fp8(const kv_shape* shape, const void* q, const uint8_t* k_fp8,
+                                   const uint8_t* v_fp8, const float* kv_scales,
+                                   const int32_t* block_table, const int32_t* seq_lens,
+                                   const int32_t* sel_blocks, const int32_t* sel_count,
+                                   int32_t sel_stride, float scale, int32_t num_splits,
+                                   float* part_o, float* part_m, float* part_l, void* stream);
 
 /*
  * Pinned, device-mapped host memory for a zero-copy K/V pool (DirectKV review,

@@ -80,6 +80,41 @@ size_t scores_bytes(const kv_shape* s) {
   return (size_t)s->num_seqs * s->num_kv_heads * s->max_blocks_per_seq * sizeof(float);
 }
 
+// Validation and launch shared by the 16-bit/fp32 pools and the E4M3 code
+// pools (kv_scales != nullptr).
+kv_status attn_common(const kv_shape* shape, const void* q, const void* k_cache,
+                      const void* v_cache, const float* kv_scales, const int32_t* block_table,
+                      const int32_t* seq_lens, const int32_t* sel_blocks,
+                      const int32_t* sel_count, int32_t sel_stride, float scale,
+                      int32_t num_splits, float* part_o, float* part_m, float* part_l,
+                      void* stream) {
+  kv_status st = check_shape(shape);
+  if (st != KV_OK) return st;
+  if (num_splits < 1 || num_splits > 65535 * 4)
+    return fail(KV_ERR_INVALID_ARG, "num_splits=%d must be in [1, 262140]", num_splits);
+  if (!q || !k_cache || !v_cache || !block_table || !seq_lens || !part_o || !part_m || !part_l)
+    return fail(KV_ERR_INVALID_ARG, "q, k_cache, v_cache, block_table, seq_lens and partials are required");
+  if ((sel_blocks == nullptr) != (sel_count == nullptr))
+    return fail(KV_ERR_INVALID_ARG, "sel_blocks and sel_count go together");
+  if (sel_blocks && sel_stride < 1)
+    return fail(KV_ERR_INVALID_ARG, "sel_stride=%d must be >= 1", sel_stride);
+  if (!(scale > 0.0f) || !(scale < INFINITY))
+    return fail(KV_ERR_INVALID_ARG, "scale must be finite and positive");
+  if (!aligned(q, 16) || !aligned(k_cache, 16) || !aligned(v_cache, 16) || !aligned(part_o, 16))
+    return fail(KV_ERR_ALIGNMENT, "q, k_cache, v_cache and part_o must be 16-byte aligned");
+  if (!aligned(block_table, 4) || !aligned(seq_lens, 4) || !aligned(part_m, 4) ||
+      !aligned(part_l, 4) || (sel_blocks && (!aligned(sel_blocks, 4) || !aligned(sel_count, 4))))
+    return fail(KV_ERR_ALIGNMENT, "integer and partial arrays must be 4-byte aligned");
+  const int G = shape->num_q_heads / shape->num_kv_heads;
+  return hip_status(
+      kvd::launch_paged_attn(shape->dtype, shape->head_dim, G, q, k_cache, v_cache, kv_scales,
+                             block_table, seq_lens, sel_blocks, sel_count, sel_stride,
+                             shape->num_seqs, shape->num_q_heads, shape->num_kv_heads,
+                             shape->max_blocks_per_seq, num_splits, scale, part_o, part_m, part_l,
+                             (hipStream_t)stream),
+      kv_scales ? "kv_paged_decode_attn_fp8 launch" : "kv_paged_decode_attn launch");
+}
+
 }  // namespace
 
 extern "C" {
@@ -254,30 +289,47 @@ kv_status kv_paged_decode_attn(const kv_shape* shape, const void* q, const void*
                                const int32_t* sel_count, int32_t sel_stride, float scale,
                                int32_t num_splits, float* part_o, float* part_m, float* part_l,
                                void* stream) {
+  return attn_common(shape, q, k_cache, v_cache, nullptr, block_table, seq_lens, sel_blocks,
+                     sel_count, sel_stride, scale, num_splits, part_o, part_m, part_l, stream);
+}
+
+kv_status kv_quantize_pages_fp8(const kv_shape* shape, const void* k_cache, const void* v_cache,
+                                const int32_t* page_ids, const int32_t* page_valid_tokens,
+                                int32_t num_page_ids, uint8_t* k_fp8, uint8_t* v_fp8,
+                                float* kv_scales, void* stream) {
   kv_status st = check_shape(shape);
   if (st != KV_OK) return st;
-  if (num_splits < 1 || num_splits > 65535 * 4)
-    return fail(KV_ERR_INVALID_ARG, "num_splits=%d must be in [1, 262140]", num_splits);
-  if (!q || !k_cache || !v_cache || !block_table || !seq_lens || !part_o || !part_m || !part_l)
-    return fail(KV_ERR_INVALID_ARG, "q, k_cache, v_cache, block_table, seq_lens and partials are required");
-  if ((sel_blocks == nullptr) != (sel_count == nullptr))
-    return fail(KV_ERR_INVALID_ARG, "sel_blocks and sel_count go together");
-  if (sel_blocks && sel_stride < 1)
-    return fail(KV_ERR_INVALID_ARG, "sel_stride=%d must be >= 1", sel_stride);
-  if (!(scale > 0.0f) || !(scale < INFINITY))
-    return fail(KV_ERR_INVALID_ARG, "scale must be finite and positive");
-  if (!aligned(q, 16) || !aligned(k_cache, 16) || !aligned(v_cache, 16) || !aligned(part_o, 16))
-    return fail(KV_ERR_ALIGNMENT, "q, k_cache, v_cache and part_o must be 16-byte aligned");
-  if (!aligned(block_table, 4) || !aligned(seq_lens, 4) || !aligned(part_m, 4) ||
-      !aligned(part_l, 4) || (sel_blocks && (!aligned(sel_blocks, 4) || !aligned(sel_count, 4))))
-    return fail(KV_ERR_ALIGNMENT, "integer and partial arrays must be 4-byte aligned");
-  const int G = shape->num_q_heads / shape->num_kv_heads;
-  return hip_status(
-      kvd::launch_paged_attn(shape->dtype, shape->head_dim, G, q, k_cache, v_cache, block_table,
-                             seq_lens, sel_blocks, sel_count, sel_stride, shape->num_seqs,
-                             shape->num_q_heads, shape->num_kv_heads, shape->max_blocks_per_seq,
-                             num_splits, scale, part_o, part_m, part_l, (hipStream_t)stream),
-      "kv_paged_decode_attn launch");
+  if (num_page_ids < 0) return fail(KV_ERR_INVALID_ARG, "num_page_ids=%d < 0", num_page_ids);
+  if (num_page_ids == 0) return ok();
+  if (!k_cache || !v_cache || !page_ids || !page_valid_tokens || !k_fp8 || !v_fp8 || !kv_scales)
+    return fail(KV_ERR_INVALID_ARG,
+                "k_cache, v_cache, page_ids, page_valid_tokens, k_fp8, v_fp8 and kv_scales are required");
+  if ((long)num_page_ids * shape->num_kv_heads > 0x7fffffffL)
+    return fail(KV_ERR_INVALID_ARG, "num_page_ids * num_kv_heads overflows int32");
+  if (!aligned(k_cache, 16) || !aligned(v_cache, 16) || !aligned(k_fp8, 16) || !aligned(v_fp8, 16))
+    return fail(KV_ERR_ALIGNMENT, "k_cache, v_cache, k_fp8 and v_fp8 must be 16-byte aligned");
+  if (!aligned(page_ids, 4) || !aligned(page_valid_tokens, 4) || !aligned(kv_scales, 8))
+    return fail(KV_ERR_ALIGNMENT,
+                "page_ids and page_valid_tokens must be 4-byte aligned, kv_scales 8-byte aligned");
+  return hip_status(kvd::launch_quantize_fp8(shape->dtype, shape->head_dim, k_cache, v_cache,
+                                             page_ids, page_valid_tokens, num_page_ids,
+                                             shape->num_kv_heads, k_fp8, v_fp8, kv_scales,
+                                             (hipStream_t)stream),
+                    "kv_quantize_pages_fp8 launch");
+}
+
+kv_status kv_paged_decode_attn_fp8(const kv_shape* shape, const void* q, const uint8_t* k_fp8,
+                                   const uint8_t* v_fp8, const float* kv_scales,
+                                   const int32_t* block_table, const int32_t* seq_lens,
+                                   const int32_t* sel_blocks, const int32_t* sel_count,
+                                   int32_t sel_stride, float scale, int32_t num_splits,
+                                   float* part_o, float* part_m, float* part_l, void* stream) {
+  kv_status st = check_shape(shape);
+  if (st != KV_OK) return st;
+  if (!kv_scales) return fail(KV_ERR_INVALID_ARG, "kv_scales is required");
+  if (!aligned(kv_scales, 8)) return fail(KV_ERR_ALIGNMENT, "kv_scales must be 8-byte aligned");
+  return attn_common(shape, q, k_fp8, v_fp8, kv_scales, block_table, seq_lens, sel_blocks,
+                     sel_count, sel_stride, scale, num_splits, part_o, part_m, part_l, stream);
 }
 
 kv_status kv_decode_combine(const kv_shape* shape, int32_t num_splits, const float* part_o,

@@ -2,7 +2,13 @@
 //
 //   paged_attn_kernel   split-K streaming-softmax decode attention      DirectKV review, core
 //                       method 2-3; Dual-Blade background; KVDrive §2.3
+//   paged_attn_mfma_kernel  the same on the matrix cores (16-bit q, G >= 2)
 //   combine_kernel      log-sum-exp merge of the split partials
+//
+// Both attention kernels also read FP8 E4M3 cold pages (KV8): one code byte
+// per channel plus one fp32 scale per (page, KV head) and tensor (KVDrive §11;
+// DirectKV review, assumption stress test).  Codes are decoded in registers;
+// the K scale multiplies the page's logits and the V scale its softmax weights.
 //
 // Each K/V byte is read exactly once; nothing is re-read from another
 // workgroup, so the blockIdx -> XCD placement carries no L2 reuse to exploit.
@@ -46,16 +52,50 @@ namespace kvd {
 // split are fetched once (one per lane) and broadcast with readlane, so the
 // K/V loads never wait on a table lookup.
 
-template <typename DT, int D, int G, int WAVES, bool SPARSE>
+// A lane's chunk of one K or V row: E channels as 16 bytes of the storage
+// dtype, or (KV8) as E code bytes.
+template <typename DT, bool KV8>
+struct KVChunk {
+  using raw = uint4;
+  static constexpr int EB = sizeof(typename DT::storage);   // bytes per channel
+  __device__ static inline raw load(const uint8_t* p) { return load16_stream(p); }
+  __device__ static inline void widen(const raw& w, float* f) { DT::widen(w, f); }
+};
+template <typename DT>
+struct KVChunk<DT, true> {
+  static constexpr int E = DT::E;
+  using raw = typename std::conditional<E == 8, uint2, uint32_t>::type;
+  static constexpr int EB = 1;
+  __device__ static inline raw load(const uint8_t* p) {
+    if constexpr (E == 8) return load8_stream(p);
+    else return load4_stream(p);
+  }
+  __device__ static inline void widen(const raw& w, float* f) {
+    if constexpr (E == 8) {
+      fp8x4_to_f32(w.x, f);
+      fp8x4_to_f32(w.y, f + 4);
+    } else {
+      fp8x4_to_f32(w, f);
+    }
+  }
+};
+
+__device__ inline float readlane_f(float v, int lane) {
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), lane));
+}
+
+template <typename DT, int D, int G, int WAVES, bool SPARSE, bool KV8>
 __global__ __launch_bounds__(WAVES * kWave) void paged_attn_kernel(
     const void* __restrict__ q, const void* __restrict__ k_cache, const void* __restrict__ v_cache,
-    const int32_t* __restrict__ block_table, const int32_t* __restrict__ seq_lens,
-    const int32_t* __restrict__ sel, const int32_t* __restrict__ sel_count, int sel_stride,
-    int Hq, int Hkv, int maxN, int S, float qscale, float* __restrict__ part_o,
-    float* __restrict__ part_m, float* __restrict__ part_l) {
+    const float* __restrict__ kv_scales, const int32_t* __restrict__ block_table,
+    const int32_t* __restrict__ seq_lens, const int32_t* __restrict__ sel,
+    const int32_t* __restrict__ sel_count, int sel_stride, int Hq, int Hkv, int maxN, int S,
+    float qscale, float* __restrict__ part_o, float* __restrict__ part_m,
+    float* __restrict__ part_l) {
   using G_ = RowGeom<DT, D>;
   using St = typename DT::storage;
-  constexpr int E = G_::E, LPR = G_::LPR, TPI = G_::TPI, NI = G_::NI;
+  using KC = KVChunk<DT, KV8>;
+  constexpr int E = G_::E, LPR = G_::LPR, TPI = G_::TPI, NI = G_::NI, EB = KC::EB;
   const int lane = threadIdx.x & (kWave - 1);
   const int s = blockIdx.x * WAVES + (threadIdx.x >> 6);
   if (s >= S) return;
@@ -86,54 +126,65 @@ __global__ __launch_bounds__(WAVES * kWave) void paged_attn_kernel(
     for (int e = 0; e < E; ++e) acc[g][e] = 0.0f;
   }
 
-  const size_t page_stride = (size_t)Hkv * kBlockSize * D;
-  const size_t lane_off = ((size_t)j * kBlockSize + rg) * D + (size_t)c * E;
-  const St* kb = static_cast<const St*>(k_cache) + lane_off;
-  const St* vb = static_cast<const St*>(v_cache) + lane_off;
+  // byte addressing: EB bytes per channel (1 for code pages)
+  const size_t page_stride = (size_t)Hkv * kBlockSize * D * EB;
+  const size_t lane_off = (((size_t)j * kBlockSize + rg) * D + (size_t)c * E) * EB;
+  const size_t row_step = (size_t)TPI * D * EB;
+  const uint8_t* kb = static_cast<const uint8_t*>(k_cache) + lane_off;
+  const uint8_t* vb = static_cast<const uint8_t*>(v_cache) + lane_off;
   const int32_t* sel_row = SPARSE ? sel + ((size_t)b * Hkv + j) * sel_stride : nullptr;
   const int32_t* bt_row = block_table + (size_t)b * maxN;
 
   for (int base = p0; base < p1; base += kWave) {
     const int cnt = min(kWave, p1 - base);
     int my_page = 0, my_valid = 0;
+    float my_sk = 1.0f, my_sv = 1.0f;
     if (lane < cnt) {
       const int n = SPARSE ? sel_row[base + lane] : base + lane;
       my_page = bt_row[n];
       my_valid = min(kBlockSize, L - n * kBlockSize);
+      if constexpr (KV8) {
+        const float2 sc = *reinterpret_cast<const float2*>(kv_scales + ((size_t)my_page * Hkv + j) * 2);
+        my_sk = sc.x;
+        my_sv = sc.y;
+      }
     }
-    uint4 kc[NI], vc[NI];
+    typename KC::raw kc[NI], vc[NI];
     {
       const size_t off = (size_t)readlane(my_page, 0) * page_stride;
 #pragma unroll
       for (int it = 0; it < NI; ++it) {
-        kc[it] = load16_stream(kb + off + (size_t)it * TPI * D);
-        vc[it] = load16_stream(vb + off + (size_t)it * TPI * D);
+        kc[it] = KC::load(kb + off + it * row_step);
+        vc[it] = KC::load(vb + off + it * row_step);
       }
     }
     for (int i = 0; i < cnt; ++i) {
-      uint4 kn[NI], vn[NI];
+      typename KC::raw kn[NI], vn[NI];
       if (i + 1 < cnt) {
         const size_t off = (size_t)readlane(my_page, i + 1) * page_stride;
 #pragma unroll
         for (int it = 0; it < NI; ++it) {
-          kn[it] = load16_stream(kb + off + (size_t)it * TPI * D);
-          vn[it] = load16_stream(vb + off + (size_t)it * TPI * D);
+          kn[it] = KC::load(kb + off + it * row_step);
+          vn[it] = KC::load(vb + off + it * row_step);
         }
       }
       const int valid = readlane(my_valid, i);
+      const float sk = KV8 ? readlane_f(my_sk, i) : 1.0f;
+      const float sv = KV8 ? readlane_f(my_sv, i) : 1.0f;
 
       // logits (log2 units) of the lane's NI tokens for every head
       float z[NI][G];
 #pragma unroll
       for (int it = 0; it < NI; ++it) {
         float kf[E];
-        DT::widen(kc[it], kf);
+        KC::widen(kc[it], kf);
 #pragma unroll
         for (int g = 0; g < G; ++g) {
           float a = 0.0f;
 #pragma unroll
           for (int e = 0; e < E; ++e) a = fmaf(qf[g][e], kf[e], a);
           z[it][g] = group_reduce<LPR, OpSum>(a);
+          if constexpr (KV8) z[it][g] *= sk;
         }
         if (it * TPI + rg >= valid) {
 #pragma unroll
@@ -165,7 +216,7 @@ __global__ __launch_bounds__(WAVES * kWave) void paged_attn_kernel(
 #pragma unroll
       for (int it = 0; it < NI; ++it) {
         float vf[E];
-        DT::widen(vc[it], vf);
+        KC::widen(vc[it], vf);
         if (it * TPI + rg >= valid) {  // slots past the sequence end may hold anything
 #pragma unroll
           for (int e = 0; e < E; ++e) vf[e] = 0.0f;
@@ -174,8 +225,9 @@ __global__ __launch_bounds__(WAVES * kWave) void paged_attn_kernel(
         for (int g = 0; g < G; ++g) {
           const float p = fast_exp2(z[it][g] - m[g]);
           lsum[g] += p;
+          const float pv = KV8 ? p * sv : p;
 #pragma unroll
-          for (int e = 0; e < E; ++e) acc[g][e] = fmaf(p, vf[e], acc[g][e]);
+          for (int e = 0; e < E; ++e) acc[g][e] = fmaf(pv, vf[e], acc[g][e]);
         }
       }
 #pragma unroll
@@ -285,6 +337,24 @@ struct MfmaOps<F16> {
   }
 };
 
+// Four E4M3 codes (one dword) as four 16-bit values (two dwords), exact.
+template <typename DT>
+__device__ inline uint2 fp8x4_to_16(uint32_t w);
+template <>
+__device__ inline uint2 fp8x4_to_16<BF16>(uint32_t w) {
+  const f32x2_v a = __builtin_amdgcn_cvt_pk_f32_fp8((int)w, false);
+  const f32x2_v b = __builtin_amdgcn_cvt_pk_f32_fp8((int)w, true);
+  // the bf16 of an exactly representable fp32 is its high half
+  return make_uint2(__builtin_amdgcn_perm(__float_as_uint(a.y), __float_as_uint(a.x), 0x07060302u),
+                    __builtin_amdgcn_perm(__float_as_uint(b.y), __float_as_uint(b.x), 0x07060302u));
+}
+template <>
+__device__ inline uint2 fp8x4_to_16<F16>(uint32_t w) {
+  const f32x2_v a = __builtin_amdgcn_cvt_pk_f32_fp8((int)w, false);
+  const f32x2_v b = __builtin_amdgcn_cvt_pk_f32_fp8((int)w, true);
+  return make_uint2(F16::pack2(a.x, a.y), F16::pack2(b.x, b.y));
+}
+
 // NDW dwords (2*NDW 16-bit channels) of one token row, as one vector load.
 template <int NDW>
 struct RowWords {
@@ -301,13 +371,24 @@ struct RowWords {
   }
 };
 
-template <typename DT, int D, int G, int WAVES, bool SPARSE>
+// With code pages (KV8) lane (col, grp) reads 16 K codes at a time: channels
+// 64*sp + 16*grp .. +16 of token col feed QK steps 2*sp (first 8) and 2*sp+1
+// (next 8).  The QK sum runs over all channels in any order, so q's B operand
+// simply uses the same channel assignment.  V codes come as D/16 bytes per
+// token and decode into the 16-bit words the repack expects.
+template <bool KV8>
+__device__ inline int qk_channel(int st, int grp) {
+  return KV8 ? 64 * (st >> 1) + 16 * grp + 8 * (st & 1) : 8 * (4 * st + grp);
+}
+
+template <typename DT, int D, int G, int WAVES, bool SPARSE, bool KV8>
 __global__ __launch_bounds__(WAVES * kWave) KVD_MFMA_OCCUPANCY void paged_attn_mfma_kernel(
     const void* __restrict__ q, const void* __restrict__ k_cache, const void* __restrict__ v_cache,
-    const int32_t* __restrict__ block_table, const int32_t* __restrict__ seq_lens,
-    const int32_t* __restrict__ sel, const int32_t* __restrict__ sel_count, int sel_stride,
-    int Hq, int Hkv, int maxN, int S, float qscale, float* __restrict__ part_o,
-    float* __restrict__ part_m, float* __restrict__ part_l) {
+    const float* __restrict__ kv_scales, const int32_t* __restrict__ block_table,
+    const int32_t* __restrict__ seq_lens, const int32_t* __restrict__ sel,
+    const int32_t* __restrict__ sel_count, int sel_stride, int Hq, int Hkv, int maxN, int S,
+    float qscale, float* __restrict__ part_o, float* __restrict__ part_m,
+    float* __restrict__ part_l) {
   static_assert(G >= 2 && G <= 8, "the group fills 2..8 of the 16 MFMA rows");
   using St = typename DT::storage;
   using Ops = MfmaOps<DT>;
@@ -331,7 +412,7 @@ __global__ __launch_bounds__(WAVES * kWave) KVD_MFMA_OCCUPANCY void paged_attn_m
   uint4 qB[KS];
 #pragma unroll
   for (int st = 0; st < KS; ++st)
-    qB[st] = col < G ? load16(static_cast<const St*>(q) + (row0 + col) * D + 8 * (4 * st + grp))
+    qB[st] = col < G ? load16(static_cast<const St*>(q) + (row0 + col) * D + qk_channel<KV8>(st, grp))
                      : make_uint4(0, 0, 0, 0);
 
   f32x4_v o[NT];
@@ -339,32 +420,62 @@ __global__ __launch_bounds__(WAVES * kWave) KVD_MFMA_OCCUPANCY void paged_attn_m
   for (int n = 0; n < NT; ++n) o[n] = f32x4_v{0.f, 0.f, 0.f, 0.f};
   float m = -INFINITY, lsum = 0.0f;
 
-  const size_t page_stride = (size_t)Hkv * kBlockSize * D;
-  const St* kb = static_cast<const St*>(k_cache) + (size_t)j * kBlockSize * D + (size_t)col * D +
-                 8 * grp;
-  const St* vb = static_cast<const St*>(v_cache) + (size_t)j * kBlockSize * D +
-                 (size_t)(4 * grp) * D + 2 * NDW * col;
+  // byte addressing: EB bytes per channel (1 for code pages)
+  constexpr int EB = KV8 ? 1 : (int)sizeof(St);
+  const size_t page_stride = (size_t)Hkv * kBlockSize * D * EB;
+  const uint8_t* kb = static_cast<const uint8_t*>(k_cache) +
+                      ((size_t)j * kBlockSize * D + (size_t)col * D + (KV8 ? 16 : 8) * grp) * EB;
+  const uint8_t* vb = static_cast<const uint8_t*>(v_cache) +
+                      ((size_t)j * kBlockSize * D + (size_t)(4 * grp) * D + 2 * NDW * col) * EB;
   const int32_t* sel_row = SPARSE ? sel + ((size_t)b * Hkv + j) * sel_stride : nullptr;
   const int32_t* bt_row = block_table + (size_t)b * maxN;
 
   for (int base = p0; base < p1; base += kWave) {
     const int cnt = min(kWave, p1 - base);
     int my_page = 0, my_valid = 0;
+    float my_sk = 1.0f, my_sv = 1.0f;
     if (lane < cnt) {
       const int n = SPARSE ? sel_row[base + lane] : base + lane;
       my_page = bt_row[n];
       my_valid = min(kBlockSize, L - n * kBlockSize);
+      if constexpr (KV8) {
+        const float2 sc = *reinterpret_cast<const float2*>(kv_scales + ((size_t)my_page * Hkv + j) * 2);
+        my_sk = sc.x;
+        my_sv = sc.y;
+      }
     }
-    struct PageRegs {
+    // raw registers of one page: 16-bit rows, or E4M3 codes (K: 16 per load,
+    // V: D/16 per token row, NDW/2 dwords)
+    struct PageRegs16 {
       uint4 k[KS];
       RowWords<NDW> v[4];
     };
+    struct PageRegs8 {
+      uint4 k[KS / 2];
+      uint32_t v[4][NDW / 2];
+    };
+    using PageRegs = typename std::conditional<KV8, PageRegs8, PageRegs16>::type;
     auto load_page = [&](PageRegs& r, int idx) {
       const size_t off = (size_t)readlane(my_page, idx) * page_stride;
+      if constexpr (KV8) {
 #pragma unroll
-      for (int st = 0; st < KS; ++st) r.k[st] = load16_stream(kb + off + 32 * st);
+        for (int sp = 0; sp < KS / 2; ++sp) r.k[sp] = load16_stream(kb + off + 64 * sp);
 #pragma unroll
-      for (int i = 0; i < 4; ++i) r.v[i].load(vb + off + (size_t)i * D);
+        for (int i = 0; i < 4; ++i) {
+          if constexpr (NDW / 2 == 2) {
+            const uint2 t = load8_stream(vb + off + (size_t)i * D);
+            r.v[i][0] = t.x;
+            r.v[i][1] = t.y;
+          } else {
+            r.v[i][0] = load4_stream(vb + off + (size_t)i * D);
+          }
+        }
+      } else {
+#pragma unroll
+        for (int st = 0; st < KS; ++st) r.k[st] = load16_stream(kb + off + 32 * st * EB);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) r.v[i].load(vb + off + (size_t)i * D * EB);
+      }
     };
     PageRegs cur, nxt;
     load_page(cur, 0);
@@ -379,13 +490,42 @@ __global__ __launch_bounds__(WAVES * kWave) KVD_MFMA_OCCUPANCY void paged_attn_m
       if (it + 1 < cnt) load_page(nxt, it + 1);
 #endif
       const int valid = readlane(my_valid, it);
+      const float sk = KV8 ? readlane_f(my_sk, it) : 1.0f;
+      const float sv = KV8 ? readlane_f(my_sv, it) : 1.0f;
+
+      // 16-bit operands of the page
+      uint4 kA[KS];
+      RowWords<NDW> vr[4];
+      if constexpr (KV8) {
+#pragma unroll
+        for (int sp = 0; sp < KS / 2; ++sp) {
+          const uint2 a0 = fp8x4_to_16<DT>(cur.k[sp].x), a1 = fp8x4_to_16<DT>(cur.k[sp].y);
+          const uint2 b0 = fp8x4_to_16<DT>(cur.k[sp].z), b1 = fp8x4_to_16<DT>(cur.k[sp].w);
+          kA[2 * sp] = make_uint4(a0.x, a0.y, a1.x, a1.y);
+          kA[2 * sp + 1] = make_uint4(b0.x, b0.y, b1.x, b1.y);
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+          for (int k = 0; k < NDW / 2; ++k) {
+            const uint2 t = fp8x4_to_16<DT>(cur.v[i][k]);
+            vr[i].w[2 * k] = t.x;
+            vr[i].w[2 * k + 1] = t.y;
+          }
+      } else {
+#pragma unroll
+        for (int st = 0; st < KS; ++st) kA[st] = cur.k[st];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) vr[i] = cur.v[i];
+      }
 
       f32x4_v sacc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int st = 0; st < KS; ++st) sacc = Ops::qk(cur.k[st], qB[st], sacc);
+      for (int st = 0; st < KS; ++st) sacc = Ops::qk(kA[st], qB[st], sacc);
+      const float zs = qscale * sk;
       float z[4];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) z[i] = (4 * grp + i < valid) ? sacc[i] * qscale : -INFINITY;
+      for (int i = 0; i < 4; ++i) z[i] = (4 * grp + i < valid) ? sacc[i] * zs : -INFINITY;
       float bm = fmaxf(fmaxf(z[0], z[1]), fmaxf(z[2], z[3]));
       bm = fmaxf(bm, xor16(bm));
       bm = fmaxf(bm, xor32(bm));
@@ -406,6 +546,10 @@ __global__ __launch_bounds__(WAVES * kWave) KVD_MFMA_OCCUPANCY void paged_attn_m
 #pragma unroll
       for (int i = 0; i < 4; ++i) p[i] = fast_exp2(z[i] - m);
       lsum += (p[0] + p[1]) + (p[2] + p[3]);
+      if constexpr (KV8) {    // the page's V scale rides on its weights
+#pragma unroll
+        for (int i = 0; i < 4; ++i) p[i] *= sv;
+      }
       uint2 phi, plo;
       phi.x = Ops::pack(p[0], p[1]);
       phi.y = Ops::pack(p[2], p[3]);
@@ -417,15 +561,15 @@ __global__ __launch_bounds__(WAVES * kWave) KVD_MFMA_OCCUPANCY void paged_attn_m
         for (int i = 0; i < 4; ++i)
           if (4 * grp + i >= valid)
 #pragma unroll
-            for (int k = 0; k < NDW; ++k) cur.v[i].w[k] = 0u;
+            for (int k = 0; k < NDW; ++k) vr[i].w[k] = 0u;
       }
       uint2 vB[NT];
 #pragma unroll
       for (int k = 0; k < NDW; ++k) {
-        vB[2 * k].x = __builtin_amdgcn_perm(cur.v[1].w[k], cur.v[0].w[k], 0x05040100u);
-        vB[2 * k].y = __builtin_amdgcn_perm(cur.v[3].w[k], cur.v[2].w[k], 0x05040100u);
-        vB[2 * k + 1].x = __builtin_amdgcn_perm(cur.v[1].w[k], cur.v[0].w[k], 0x07060302u);
-        vB[2 * k + 1].y = __builtin_amdgcn_perm(cur.v[3].w[k], cur.v[2].w[k], 0x07060302u);
+        vB[2 * k].x = __builtin_amdgcn_perm(vr[1].w[k], vr[0].w[k], 0x05040100u);
+        vB[2 * k].y = __builtin_amdgcn_perm(vr[3].w[k], vr[2].w[k], 0x05040100u);
+        vB[2 * k + 1].x = __builtin_amdgcn_perm(vr[1].w[k], vr[0].w[k], 0x07060302u);
+        vB[2 * k + 1].y = __builtin_amdgcn_perm(vr[3].w[k], vr[2].w[k], 0x07060302u);
       }
 #pragma unroll
       for (int n = 0; n < NT; ++n) o[n] = Ops::pv(phi, vB[n], o[n]);
@@ -536,11 +680,11 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
 
 
 hipError_t launch_paged_attn(int dtype, int D, int G, const void* q, const void* k_cache,
-                             const void* v_cache, const int32_t* block_table,
-                             const int32_t* seq_lens, const int32_t* sel,
-                             const int32_t* sel_count, int sel_stride, int B, int Hq, int Hkv,
-                             int maxN, int S, float scale, float* part_o, float* part_m,
-                             float* part_l, hipStream_t stream) {
+                             const void* v_cache, const float* kv_scales,
+                             const int32_t* block_table, const int32_t* seq_lens,
+                             const int32_t* sel, const int32_t* sel_count, int sel_stride, int B,
+                             int Hq, int Hkv, int maxN, int S, float scale, float* part_o,
+                             float* part_m, float* part_l, hipStream_t stream) {
   constexpr int WAVES = KVD_ATTN_WAVES;
   const dim3 grid((S + WAVES - 1) / WAVES, Hkv, B);
   const float qscale = scale * kLog2e;
@@ -549,22 +693,25 @@ hipError_t launch_paged_attn(int dtype, int D, int G, const void* q, const void*
       return with_group(G, [&](auto g) {
         using DT = decltype(dt);
         constexpr int DD = decltype(d)::value, GG = decltype(g)::value;
-        auto go = [&](auto sparse) {
-          constexpr bool SP = decltype(sparse)::value;
+        auto go = [&](auto sparse, auto kv8) {
+          constexpr bool SP = decltype(sparse)::value, K8 = decltype(kv8)::value;
           if constexpr (!std::is_same_v<DT, F32> && GG >= 2) {
-            hipLaunchKernelGGL((paged_attn_mfma_kernel<DT, DD, GG, WAVES, SP>), grid,
-                               dim3(WAVES * kWave), 0, stream, q, k_cache, v_cache, block_table,
-                               seq_lens, sel, sel_count, sel_stride, Hq, Hkv, maxN, S, qscale,
-                               part_o, part_m, part_l);
+            hipLaunchKernelGGL((paged_attn_mfma_kernel<DT, DD, GG, WAVES, SP, K8>), grid,
+                               dim3(WAVES * kWave), 0, stream, q, k_cache, v_cache, kv_scales,
+                               block_table, seq_lens, sel, sel_count, sel_stride, Hq, Hkv, maxN,
+                               S, qscale, part_o, part_m, part_l);
           } else {
-            hipLaunchKernelGGL((paged_attn_kernel<DT, DD, GG, WAVES, SP>), grid,
-                               dim3(WAVES * kWave), 0, stream, q, k_cache, v_cache, block_table,
-                               seq_lens, sel, sel_count, sel_stride, Hq, Hkv, maxN, S, qscale,
-                               part_o, part_m, part_l);
+            hipLaunchKernelGGL((paged_attn_kernel<DT, DD, GG, WAVES, SP, K8>), grid,
+                               dim3(WAVES * kWave), 0, stream, q, k_cache, v_cache, kv_scales,
+                               block_table, seq_lens, sel, sel_count, sel_stride, Hq, Hkv, maxN,
+                               S, qscale, part_o, part_m, part_l);
           }
         };
-        if (sel) go(std::true_type{});
-        else go(std::false_type{});
+        // kv_scales marks code pages
+        if (sel && kv_scales) go(std::true_type{}, std::true_type{});
+        else if (sel) go(std::true_type{}, std::false_type{});
+        else if (kv_scales) go(std::false_type{}, std::true_type{});
+        else go(std::false_type{}, std::false_type{});
         return hipGetLastError();
       });
     });

@@ -106,7 +106,49 @@ __device__ inline uint2 load8_stream(const void* p) {
   return *reinterpret_cast<const uint2*>(p);
 #endif
 }
+__device__ inline uint32_t load4_stream(const void* p) {
+#if KVD_NT_LOADS
+  return __builtin_nontemporal_load(reinterpret_cast<const unsigned int*>(p));
+#else
+  return *reinterpret_cast<const unsigned int*>(p);
+#endif
+}
 __device__ inline void store16(void* p, const uint4& v) { *reinterpret_cast<uint4*>(p) = v; }
+
+// ---------------------------------------------------------------- FP8 E4M3 pages
+//
+// Cold K/V pages hold OCP FP8 E4M3 codes (1 byte per channel) with one fp32
+// scale per (page, KV head) and tensor.  gfx950's v_cvt_pk_f32_fp8 decodes
+// E4M3 exactly (every one of the 256 codes was checked on the GPU against the
+// format's table); a decoded value has at most 4 significant bits and lies in
+// [2^-9, 448], so it is also exact in bf16 and fp16.
+
+typedef float f32x2_v __attribute__((ext_vector_type(2)));
+
+__device__ inline void fp8x4_to_f32(uint32_t w, float* f) {
+  const f32x2_v a = __builtin_amdgcn_cvt_pk_f32_fp8((int)w, false);
+  const f32x2_v b = __builtin_amdgcn_cvt_pk_f32_fp8((int)w, true);
+  f[0] = a.x;
+  f[1] = a.y;
+  f[2] = b.x;
+  f[3] = b.y;
+}
+
+// Round an fp32 value to the nearest E4M3 code (ties to the even code);
+// magnitudes of 464 and more saturate to 448.  Below 2^-6 the grid is the
+// multiples of 2^-9; above, fp32's mantissa is cut to 3 bits with the usual
+// round-half-even carry, and the exponent is rebiased from 127 to 7.
+__device__ inline uint32_t fp8_encode(float y) {
+  const uint32_t u = __float_as_uint(y);
+  const uint32_t sign = (u >> 24) & 0x80u;
+  const uint32_t a = u & 0x7fffffffu;
+  uint32_t code;
+  if (a > 0x7f800000u) code = 0x7fu;                          // NaN
+  else if (a >= 0x43e80000u) code = 0x7eu;                    // >= 464
+  else if (a < 0x3c800000u) code = (uint32_t)__builtin_rintf(__uint_as_float(a) * 512.0f);
+  else code = ((a + 0x7ffffu + ((a >> 20) & 1u)) >> 20) - (120u << 3);
+  return sign | code;
+}
 
 // ---------------------------------------------------------------- lane shuffles
 //

@@ -32,12 +32,19 @@ hipError_t launch_topk(const float* scores, const int32_t* seq_lens, int B, int 
                        int K, int sink, int local, int32_t* sel, int32_t* sel_count,
                        hipStream_t stream);
 
+// kv_scales == nullptr: K/V pools in `dtype`; otherwise E4M3 code pools with
+// fp32 (k, v) scales per (page, KV head)
 hipError_t launch_paged_attn(int dtype, int D, int G, const void* q, const void* k_cache,
-                             const void* v_cache, const int32_t* block_table,
-                             const int32_t* seq_lens, const int32_t* sel,
-                             const int32_t* sel_count, int sel_stride, int B, int Hq, int Hkv,
-                             int maxN, int S, float scale, float* part_o, float* part_m,
-                             float* part_l, hipStream_t stream);
+                             const void* v_cache, const float* kv_scales,
+                             const int32_t* block_table, const int32_t* seq_lens,
+                             const int32_t* sel, const int32_t* sel_count, int sel_stride, int B,
+                             int Hq, int Hkv, int maxN, int S, float scale, float* part_o,
+                             float* part_m, float* part_l, hipStream_t stream);
+
+hipError_t launch_quantize_fp8(int dtype, int D, const void* k_cache, const void* v_cache,
+                               const int32_t* page_ids, const int32_t* valid_tokens, int n_ids,
+                               int Hkv, uint8_t* k8, uint8_t* v8, float* scales,
+                               hipStream_t stream);
 
 hipError_t launch_combine(int D, const float* part_o, const float* part_m, const float* part_l,
                           int rows, int S, float* out, float* lse, hipStream_t stream);

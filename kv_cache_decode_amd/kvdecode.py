@@ -28,8 +28,9 @@ DTYPE_CODES = {"f32": KV_F32, "f16": KV_F16, "bf16": KV_BF16}
 EXPORTS = (
     "kv_block_meta_build", "kv_block_mean_build", "kv_append_token",
     "kv_score_topk_workspace_size", "kv_block_score_topk", "kv_max_forced_blocks",
-    "kv_block_select", "kv_auto_num_splits", "kv_paged_decode_attn", "kv_decode_combine", "kv_host_alloc",
-    "kv_host_free", "kv_status_string", "kv_last_error_message",
+    "kv_block_select", "kv_auto_num_splits", "kv_paged_decode_attn", "kv_decode_combine",
+    "kv_quantize_pages_fp8", "kv_paged_decode_attn_fp8", "kv_host_alloc", "kv_host_free",
+    "kv_status_string", "kv_last_error_message",
 )
 
 
@@ -86,6 +87,8 @@ def _load() -> ctypes.CDLL:
         "kv_auto_num_splits": (I32, [S, I32]),
         "kv_paged_decode_attn": (I32, [S, P, P, P, P, P, P, P, I32, F, I32, P, P, P, P]),
         "kv_decode_combine": (I32, [S, I32, P, P, P, P, P, P]),
+        "kv_quantize_pages_fp8": (I32, [S, P, P, P, P, I32, P, P, P, P]),
+        "kv_paged_decode_attn_fp8": (I32, [S, P, P, P, P, P, P, P, P, I32, F, I32, P, P, P, P]),
         "kv_host_alloc": (I32, [SZ, U32, ctypes.POINTER(P), ctypes.POINTER(P)]),
         "kv_host_free": (I32, [P]),
         "kv_status_string": (ctypes.c_char_p, [I32]),
@@ -200,6 +203,25 @@ def kv_decode_combine(shape: KVShape, num_splits: int, part_o: Buf, part_m: Buf,
                       out: Buf, lse_out: Buf = None, stream=None) -> None:
     _check(_lib.kv_decode_combine(ctypes.byref(shape), num_splits, _p(part_o), _p(part_m),
                                   _p(part_l), _p(out), _p(lse_out), _stream(stream)))
+
+
+def kv_quantize_pages_fp8(shape: KVShape, k_cache: Buf, v_cache: Buf, page_ids: Buf,
+                          page_valid_tokens: Buf, num_page_ids: int, k_fp8: Buf, v_fp8: Buf,
+                          kv_scales: Buf, stream=None) -> None:
+    _check(_lib.kv_quantize_pages_fp8(ctypes.byref(shape), _p(k_cache), _p(v_cache), _p(page_ids),
+                                      _p(page_valid_tokens), num_page_ids, _p(k_fp8), _p(v_fp8),
+                                      _p(kv_scales), _stream(stream)))
+
+
+def kv_paged_decode_attn_fp8(shape: KVShape, q: Buf, k_fp8: Buf, v_fp8: Buf, kv_scales: Buf,
+                             block_table: Buf, seq_lens: Buf, sel_blocks: Buf, sel_count: Buf,
+                             sel_stride: int, scale: float, num_splits: int, part_o: Buf,
+                             part_m: Buf, part_l: Buf, stream=None) -> None:
+    _check(_lib.kv_paged_decode_attn_fp8(ctypes.byref(shape), _p(q), _p(k_fp8), _p(v_fp8),
+                                         _p(kv_scales), _p(block_table), _p(seq_lens),
+                                         _p(sel_blocks), _p(sel_count), sel_stride, scale,
+                                         num_splits, _p(part_o), _p(part_m), _p(part_l),
+                                         _stream(stream)))
 
 
 def kv_host_alloc(nbytes: int, flags: int = KV_HOST_COHERENT):

@@ -73,6 +73,8 @@ class DeviceWorkload:
         P, Hkv, bs, D = data.k_raw.shape
         self.kmeta = torch.zeros((P, Hkv, 2, D), dtype=TORCH_DTYPES[dt], device=dev)
         self.kmean = None          # fp32 mean-key index, allocated by mean_build()
+        self.k8 = self.v8 = self.kv_scales = None   # E4M3 cold pages, from quantize_fp8()
+        self._host8 = []
         ids, val = [], []
         for b in range(spec.num_seqs):
             for n in range(spec.blocks(b)):
@@ -181,6 +183,43 @@ class DeviceWorkload:
                                     po, pm, pl, stream)
         return S
 
+    def quantize_fp8(self, host: Optional[bool] = None, stream=None):
+        """E4M3 code pools and (k, v) scales of every used page.  With ``host``
+        (default: the workload's host_kv) the code pools then move to mapped
+        pinned host memory for zero-copy reads."""
+        P, Hkv, bs, D = self.data.k_raw.shape
+        dev = self.device
+        k8 = torch.zeros((P, Hkv, bs, D), dtype=torch.uint8, device=dev)
+        v8 = torch.zeros_like(k8)
+        self.kv_scales = torch.zeros((P, Hkv, 2), dtype=torch.float32, device=dev)
+        kd.kv_quantize_pages_fp8(self.shape, self.k_cache, self.v_cache, self.page_ids,
+                                 self.page_valid, int(self.page_ids.numel()), k8, v8,
+                                 self.kv_scales, stream)
+        host = self.host_kv if host is None else host
+        if host:
+            torch.cuda.synchronize(dev)
+            hk, hv = HostBuffer(k8.cpu().numpy()), HostBuffer(v8.cpu().numpy())
+            self._host8 = [hk, hv]
+            self.k8, self.v8 = hk.dev, hv.dev
+            self.k8_dev, self.v8_dev = k8, v8
+        else:
+            self.k8, self.v8 = k8, v8
+            self.k8_dev, self.v8_dev = k8, v8
+
+    def attention_fp8(self, sparse: bool, num_splits: Optional[int] = None, stream=None):
+        S = num_splits or self.auto_splits(sparse)
+        po, pm, pl = self.partials(S)
+        sel, cnt, stride = (self.sel, self.sel_count, self.topk) if sparse else (None, None, 0)
+        kd.kv_paged_decode_attn_fp8(self.shape, self.q, self.k8, self.v8, self.kv_scales,
+                                    self.block_table, self.seq_lens, sel, cnt, stride, self.scale,
+                                    S, po, pm, pl, stream)
+        return S
+
+    def decode_fp8(self, sparse: bool, num_splits: Optional[int] = None, stream=None):
+        S = self.attention_fp8(sparse, num_splits, stream)
+        self.combine(S, stream)
+        return S
+
     def combine(self, num_splits: int, stream=None):
         po, pm, pl = self.partials(num_splits)
         kd.kv_decode_combine(self.shape, num_splits, po, pm, pl, self.out, self.lse, stream)
@@ -191,6 +230,7 @@ class DeviceWorkload:
         return S
 
     def close(self):
-        for h in self._host:
+        for h in self._host + self._host8:
             h.free()
         self._host = []
+        self._host8 = []

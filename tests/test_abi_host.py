@@ -23,7 +23,7 @@ ODD = 0x10002          # 2-byte aligned
 def declared_functions():
     text = open(HEADER).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(kv_[a-z_]+)\s*\(", text)))
+    return sorted(set(re.findall(r"\b(kv_[a-z0-9_]+)\s*\(", text)))
 
 
 def test_header_declares_exactly_the_binding_exports():
@@ -249,3 +249,30 @@ def test_select_argument_checks():
     big = shape(max_blocks_per_seq=32769)
     expect(kd.KV_ERR_UNSUPPORTED, lambda stream: f(big, 0, A16, A16, A16, A16, 8, 0, 0, A16, A16,
                                                    A16, stream=stream))
+
+
+def test_fp8_argument_checks():
+    s = shape()
+    qz = kd.kv_quantize_pages_fp8
+    expect(kd.KV_ERR_INVALID_ARG, lambda stream: qz(s, A16, A16, A16, A16, -1, A16, A16, A16, stream=stream))
+    expect(kd.KV_ERR_INVALID_ARG, lambda stream: qz(s, A16, None, A16, A16, 3, A16, A16, A16, stream=stream))
+    expect(kd.KV_ERR_INVALID_ARG, lambda stream: qz(s, A16, A16, A16, A16, 3, A16, A16, None, stream=stream))
+    expect(kd.KV_ERR_ALIGNMENT, lambda stream: qz(s, A16, A16, A16, A16, 3, A4, A16, A16, stream=stream))
+    expect(kd.KV_ERR_ALIGNMENT, lambda stream: qz(s, A16, A16, A16, A16, 3, A16, A16, A4 + 2, stream=stream))
+    qz(s, None, None, None, None, 0, None, None, None, stream=0)     # nothing to do: OK
+    at = kd.kv_paged_decode_attn_fp8
+
+    def call(scales=A16 + 8, k8=A16, **kw):
+        args = dict(q=A16, k_fp8=k8, v_fp8=A16, kv_scales=scales, block_table=A16, seq_lens=A16,
+                    sel_blocks=None, sel_count=None, sel_stride=0, scale=0.1, num_splits=2,
+                    part_o=A16, part_m=A16, part_l=A16)
+        args.update(kw)
+        return lambda stream: at(s, stream=stream, **args)
+
+    expect(kd.KV_ERR_INVALID_ARG, call(scales=None))
+    expect(kd.KV_ERR_ALIGNMENT, call(scales=A4))
+    expect(kd.KV_ERR_ALIGNMENT, call(k8=A4))
+    expect(kd.KV_ERR_INVALID_ARG, call(num_splits=0))
+    expect(kd.KV_ERR_UNSUPPORTED, lambda stream: at(shape(head_dim=96), A16, A16, A16, A16, A16, A16,
+                                                    None, None, 0, 0.1, 1, A16, A16, A16,
+                                                    stream=stream))
