@@ -23,10 +23,7 @@
 // choice), which caps its register allocation: 3 fits in 142 VGPRs without
 // spilling, where the unconstrained allocation gave 180 registers (2 waves).
 #ifndef KVD_ATTN_WAVES
-#define KVD_ATTN_WAVES 4
-#endif
-#ifndef KVD_ATTN_PREFETCH
-#define KVD_ATTN_PREFETCH 1   // pages of K/V loaded ahead by the MFMA kernel
+#define KVD_ATTN_WAVES 2
 #endif
 #ifndef KVD_MFMA_WAVES_PER_EU
 #define KVD_MFMA_WAVES_PER_EU 3
@@ -149,25 +146,20 @@ __global__ __launch_bounds__(WAVES * kWave) void paged_attn_kernel(
         my_sv = sc.y;
       }
     }
-    typename KC::raw kc[NI], vc[NI];
-    {
-      const size_t off = (size_t)readlane(my_page, 0) * page_stride;
+    struct PageRegs {
+      typename KC::raw k[NI], v[NI];
+    };
+    auto load_page = [&](PageRegs& r, int idx) {
+      const size_t off = (size_t)readlane(my_page, idx) * page_stride;
 #pragma unroll
       for (int it = 0; it < NI; ++it) {
-        kc[it] = KC::load(kb + off + it * row_step);
-        vc[it] = KC::load(vb + off + it * row_step);
+        r.k[it] = KC::load(kb + off + it * row_step);
+        r.v[it] = KC::load(vb + off + it * row_step);
       }
-    }
-    for (int i = 0; i < cnt; ++i) {
-      typename KC::raw kn[NI], vn[NI];
-      if (i + 1 < cnt) {
-        const size_t off = (size_t)readlane(my_page, i + 1) * page_stride;
-#pragma unroll
-        for (int it = 0; it < NI; ++it) {
-          kn[it] = KC::load(kb + off + it * row_step);
-          vn[it] = KC::load(vb + off + it * row_step);
-        }
-      }
+    };
+    auto process = [&](const PageRegs& cur, int i) {
+      const typename KC::raw* kc = cur.k;
+      const typename KC::raw* vc = cur.v;
       const int valid = readlane(my_valid, i);
       const float sk = KV8 ? readlane_f(my_sk, i) : 1.0f;
       const float sv = KV8 ? readlane_f(my_sv, i) : 1.0f;
@@ -230,9 +222,17 @@ __global__ __launch_bounds__(WAVES * kWave) void paged_attn_kernel(
           for (int e = 0; e < E; ++e) acc[g][e] = fmaf(pv, vf[e], acc[g][e]);
         }
       }
-#pragma unroll
-      for (int it = 0; it < NI; ++it) { kc[it] = kn[it]; vc[it] = vn[it]; }
+    };
+    // page i+1 loads while page i is computed; the last page of the group is
+    // peeled off so that every load in the loop is unconditional
+    PageRegs cur, nxt;
+    load_page(cur, 0);
+    for (int i = 0; i + 1 < cnt; ++i) {
+      load_page(nxt, i + 1);
+      process(cur, i);
+      cur = nxt;
     }
+    process(cur, cnt - 1);
   }
 
   // merge the row groups (each saw a disjoint set of tokens) and write the split
@@ -477,18 +477,8 @@ __global__ __launch_bounds__(WAVES * kWave) KVD_MFMA_OCCUPANCY void paged_attn_m
         for (int i = 0; i < 4; ++i) r.v[i].load(vb + off + (size_t)i * D * EB);
       }
     };
-    PageRegs cur, nxt;
-    load_page(cur, 0);
-#if KVD_ATTN_PREFETCH >= 2
-    if (cnt > 1) load_page(nxt, 1);
-#endif
-    for (int it = 0; it < cnt; ++it) {
-#if KVD_ATTN_PREFETCH >= 2
-      PageRegs nx2;
-      if (it + 2 < cnt) load_page(nx2, it + 2);
-#else
-      if (it + 1 < cnt) load_page(nxt, it + 1);
-#endif
+    // one page of compute; `cur` holds page `it` of the group
+    auto process = [&](const PageRegs& cur, int it) {
       const int valid = readlane(my_valid, it);
       const float sk = KV8 ? readlane_f(my_sk, it) : 1.0f;
       const float sv = KV8 ? readlane_f(my_sv, it) : 1.0f;
@@ -576,13 +566,19 @@ __global__ __launch_bounds__(WAVES * kWave) KVD_MFMA_OCCUPANCY void paged_attn_m
 #pragma unroll
       for (int n = 0; n < NT; ++n) o[n] = Ops::pv(plo, vB[n], o[n]);
 
-#if KVD_ATTN_PREFETCH >= 2
+    };
+    // page it+1 loads while page it is computed; the group's last page is
+    // peeled off so every load in the loop is unconditional.  (With a
+    // conditional prefetch the compiler waited for every outstanding load, the
+    // prefetch included, before using a page.)
+    PageRegs cur, nxt;
+    load_page(cur, 0);
+    for (int it = 0; it + 1 < cnt; ++it) {
+      load_page(nxt, it + 1);
+      process(cur, it);
       cur = nxt;
-      nxt = nx2;
-#else
-      cur = nxt;
-#endif
     }
+    process(cur, cnt - 1);
   }
 
   // totals per head (the four k-groups of a column saw disjoint tokens)
