@@ -17,6 +17,9 @@ Functions (each computed as oracle.c states it):
 * ``fp8_encode`` / ``fp8_decode``  OCP FP8 E4M3 codes (round to nearest even, saturating)
 * ``fp8_quantize``    per-(page, KV head) scaled E4M3 pages      (KVDrive §11; DirectKV review)
 * ``fp8_dequantize``  decode(code) * scale
+* ``block_lse``       ln sum exp(logits) of each attended block          (KVDrive §5.1)
+* ``slot_mass``       eviction mass of each cache slot after a step
+* ``cache_plan``      one step of the GPU block cache: hits, misses, victims
 * ``attention``       softmax decode attention, dense or over selected blocks
                       (Dual-Blade background; KVDrive §2.3 step 3)
 * ``attention_splits``  the same on each contiguous chunk of the block list
@@ -66,6 +69,14 @@ def _load():
     lib.oracle_fp8_encode.restype = ctypes.c_uint8
     lib.oracle_fp8_quantize.argtypes = [_D, _int, _int, _int, _I, _I, _int, _U8, _F, _int]
     lib.oracle_fp8_quantize.restype = None
+    lib.oracle_block_lse.argtypes = [_D, _D, _I, _I, _I, _I, _int, _int, _int, _int, _int, _int,
+                                     _int, ctypes.c_double, _D]
+    lib.oracle_block_lse.restype = None
+    lib.oracle_slot_mass.argtypes = [_D, _D, _I, _I, _int, _int, _int, _int, _int, _D]
+    lib.oracle_slot_mass.restype = None
+    lib.oracle_cache_plan.argtypes = [_I, _I, _int, _int, _int, _int, _int, _I, _I, _F, _I, _I,
+                                      _I, _I]
+    lib.oracle_cache_plan.restype = None
     lib.oracle_topk.argtypes = [_D, _I, _int, _int, _int, _int, _int, _I, _I]
     lib.oracle_attention.argtypes = [_D, _D, _D, _I, _I, _I, _I, _int, _int, _int, _int, _int,
                                      _int, _int, ctypes.c_double, _D, _D]
@@ -195,6 +206,55 @@ def fp8_quantize(pool, page_ids, valid_tokens):
 def fp8_dequantize(codes, scales) -> np.ndarray:
     """decode(code) * scale per (page, KV head), float64 [P, Hkv, bs, D]."""
     return fp8_decode(codes) * np.asarray(scales, np.float64)[:, :, None, None]
+
+
+def block_lse(q, k_pool, block_table, seq_lens, block_size: int, scale: float, sel=None,
+              sel_count=None) -> np.ndarray:
+    """ln of the summed exp-logits of every attended block [B, Hq, stride] (-inf past the list)."""
+    q, k = _f64(q), _f64(k_pool)
+    bt, sl = _i32(block_table), _i32(seq_lens)
+    B, Hq, D = q.shape
+    Hkv = k.shape[1]
+    maxN = bt.shape[1]
+    stride = maxN if sel is None else np.asarray(sel).shape[-1]
+    out = np.empty((B, Hq, stride))
+    s_, c_ = (None, None) if sel is None else (_i32(sel), _i32(sel_count))
+    _load().oracle_block_lse(_pd(q), _pd(k), _pi(bt), _pi(sl), _pi(s_), _pi(c_), stride, B, Hq,
+                             Hkv, D, block_size, maxN, scale, _pd(out))
+    return out
+
+
+def slot_mass(block_lse_, lse, sel_count, sel_slots, num_slots: int) -> np.ndarray:
+    """Eviction mass per cache slot [B, Hkv, C]: max over the group's heads of
+    exp(block_lse - lse) at the block's slot, 0 elsewhere."""
+    bl, ls = _f64(block_lse_), _f64(lse)
+    cnt, slots = _i32(sel_count), _i32(sel_slots)
+    B, Hq, stride = bl.shape
+    Hkv = slots.shape[1]
+    out = np.empty((B, Hkv, num_slots))
+    _load().oracle_slot_mass(_pd(bl), _pd(ls), _pi(cnt), _pi(slots), stride, B, Hq, Hkv,
+                             num_slots, _pd(out))
+    return out
+
+
+def cache_plan(sel, sel_count, slot_block, block_slot, slot_mass_):
+    """One cache step; returns (slot_block, block_slot, sel_slots, fetch_block,
+    fetch_slot, fetch_count) with the maps updated (inputs are not modified)."""
+    sl_ = _i32(sel)
+    cnt = _i32(sel_count)
+    sb = np.array(slot_block, dtype=np.int32, copy=True)
+    bs_ = np.array(block_slot, dtype=np.int32, copy=True)
+    mass = np.ascontiguousarray(slot_mass_, dtype=np.float32)
+    B, Hkv, stride = sl_.shape
+    C, maxN = sb.shape[-1], bs_.shape[-1]
+    sel_slots = np.empty((B, Hkv, stride), np.int32)
+    fb = np.empty((B, Hkv, stride), np.int32)
+    fs = np.empty((B, Hkv, stride), np.int32)
+    fc = np.empty((B, Hkv), np.int32)
+    _load().oracle_cache_plan(_pi(sl_), _pi(cnt), stride, B, Hkv, maxN, C, _pi(sb), _pi(bs_),
+                              mass.ctypes.data_as(ctypes.POINTER(ctypes.c_float)), _pi(sel_slots),
+                              _pi(fb), _pi(fs), _pi(fc))
+    return sb, bs_, sel_slots, fb, fs, fc
 
 
 def group_scores(head_scores_, num_kv_heads: int) -> np.ndarray:

@@ -54,7 +54,18 @@
  *    tile), code = round-to-nearest-even(x / s) saturated to +-448, code 0 for
  *    slots past the valid count; the value a code stands for is
  *    decode(code) * s.  The scale and the quotient are taken in fp32, the
- *    precision in which the quantiser decides the codes.
+ *    precision in which the quantiser decides the codes;
+ *  - GPU-resident block cache with lookahead eviction (KVDrive §5.1: a window
+ *    of critical KV entries stays on the GPU; each step the new critical
+ *    entries are fetched from host memory and the entries with the lowest
+ *    attention in the step are the ones dropped): per (sequence, KV head) a
+ *    cache of C >= K block slots.  A step's selected blocks that are resident
+ *    keep their slots; each missing block takes, in list order, the next of:
+ *    the free slots in slot order, then the slots whose block is not
+ *    selected, by increasing attention mass of the latest step (ties: lower
+ *    slot first).  The mass of a slot is the attention weight its block
+ *    received in the latest step, summed over the block's tokens, max over
+ *    the query heads of the group; 0 for a block the step did not attend.
  */
 #include <math.h>
 #include <stdint.h>
@@ -469,6 +480,151 @@ void oracle_attention(const double* q, const double* k_pool, const double* v_poo
     }
     free(z_buf);
   }
+}
+
+/*
+ * Block log-sum-exp of the attended list: for (b, h) and list position pos
+ * (block n of the list of (b, h / G)),
+ *   block_lse[b, h, pos] = ln sum_{t in block n, t < L_b} exp(scale * (q . k_t)),
+ * so that exp(block_lse - lse) is the attention weight the block receives in
+ * the step (KVDrive §5.1 ranks cached entries by it).  Positions past the list
+ * are -inf.  block_lse [B, Hq, sel_stride] (dense: sel == NULL, stride maxN).
+ */
+void oracle_block_lse(const double* q, const double* k_pool, const int32_t* block_table,
+                      const int32_t* seq_lens, const int32_t* sel, const int32_t* sel_count,
+                      int sel_stride, int B, int Hq, int Hkv, int D, int bs, int maxN,
+                      double scale, double* block_lse) {
+  const int G = Hq / Hkv;
+  const int stride = sel ? sel_stride : maxN;
+#pragma omp parallel for collapse(2) schedule(dynamic)
+  for (int b = 0; b < B; ++b) {
+    for (int h = 0; h < Hq; ++h) {
+      const int j = h / G;
+      const i64 L = seq_lens[b];
+      const i64 nb = ceil_div(L, bs);
+      const i64 n_list = list_len(sel_count, b, j, Hkv, nb);
+      const double* qh = q + ((i64)b * Hq + h) * D;
+      double* out = block_lse + ((i64)b * Hq + h) * stride;
+      for (i64 pos = 0; pos < stride; ++pos) {
+        if (pos >= n_list) { out[pos] = -INFINITY; continue; }
+        const i64 n = block_list(sel, sel_stride, b, j, Hkv, pos);
+        const i64 p = block_table[(i64)b * maxN + n];
+        double z[64];
+        int nt = 0;
+        double m = -INFINITY;
+        for (int s = 0; s < bs && n * bs + s < L; ++s) {
+          const double* k = pool_row(k_pool, p, j, s, Hkv, bs, D);
+          double dot = 0.0;
+          for (int c = 0; c < D; ++c) dot += qh[c] * k[c];
+          z[nt] = scale * dot;
+          if (z[nt] > m) m = z[nt];
+          ++nt;
+        }
+        double l = 0.0;
+        for (int t = 0; t < nt; ++t) l += exp(z[t] - m);
+        out[pos] = m + log(l);
+      }
+    }
+  }
+}
+
+/*
+ * Eviction mass of every cache slot after a step (KVDrive §5.1): slot_mass is
+ * set to 0 everywhere, then for each list position pos of (b, j) whose block
+ * sits in slot sel_slots[b, j, pos]:
+ *   slot_mass[b, j, slot] = max over the G query heads h of group j of
+ *                           exp(block_lse[b, h, pos] - lse[b, h]).
+ * block_lse [B, Hq, sel_stride]; lse [B, Hq]; slot_mass [B, Hkv, C].
+ */
+void oracle_slot_mass(const double* block_lse, const double* lse, const int32_t* sel_count,
+                      const int32_t* sel_slots, int sel_stride, int B, int Hq, int Hkv, int C,
+                      double* slot_mass) {
+  const int G = Hq / Hkv;
+  for (int b = 0; b < B; ++b) {
+    for (int j = 0; j < Hkv; ++j) {
+      double* out = slot_mass + ((i64)b * Hkv + j) * C;
+      for (int c = 0; c < C; ++c) out[c] = 0.0;
+      const i64 cnt = sel_count[(i64)b * Hkv + j];
+      for (i64 pos = 0; pos < cnt; ++pos) {
+        double best = 0.0;
+        for (int g = 0; g < G; ++g) {
+          const i64 h = (i64)j * G + g;
+          const double w = exp(block_lse[((i64)b * Hq + h) * sel_stride + pos] - lse[(i64)b * Hq + h]);
+          if (w > best) best = w;
+        }
+        out[sel_slots[((i64)b * Hkv + j) * sel_stride + pos]] = best;
+      }
+    }
+  }
+}
+
+/*
+ * One step of the block cache (KVDrive §5.1) for every (b, j).  In and out:
+ * slot_block [B, Hkv, C] (block held by each slot, -1 free) and block_slot
+ * [B, Hkv, maxN] (slot of each resident block, -1 otherwise).  In: the step's
+ * list sel / sel_count (distinct blocks), slot_mass [B, Hkv, C] of the latest
+ * step (compared as fp32, the precision the cache keeps it in).  Out:
+ * sel_slots [B, Hkv, sel_stride] (slot of every list position, -1 past the
+ * list), the fetch list fetch_block / fetch_slot [B, Hkv, sel_stride] of the
+ * blocks that were not resident (-1 padded) and fetch_count [B, Hkv].
+ * Requires C >= sel_count.
+ */
+void oracle_cache_plan(const int32_t* sel, const int32_t* sel_count, int sel_stride, int B,
+                       int Hkv, int maxN, int C, int32_t* slot_block, int32_t* block_slot,
+                       const float* slot_mass, int32_t* sel_slots, int32_t* fetch_block,
+                       int32_t* fetch_slot, int32_t* fetch_count) {
+  int* in_use = (int*)malloc(sizeof(int) * (size_t)C);
+  int* cand = (int*)malloc(sizeof(int) * (size_t)C);
+  for (int b = 0; b < B; ++b) {
+    for (int j = 0; j < Hkv; ++j) {
+      const i64 u = (i64)b * Hkv + j;
+      int32_t* sb = slot_block + u * C;
+      int32_t* bsl = block_slot + u * maxN;
+      const float* mass = slot_mass + u * C;
+      const int32_t* list = sel + u * sel_stride;
+      int32_t* out_slots = sel_slots + u * sel_stride;
+      int32_t* fb = fetch_block + u * sel_stride;
+      int32_t* fs = fetch_slot + u * sel_stride;
+      const int cnt = sel_count[u];
+      for (int c = 0; c < C; ++c) in_use[c] = 0;
+      for (int pos = 0; pos < sel_stride; ++pos) { out_slots[pos] = -1; fb[pos] = -1; fs[pos] = -1; }
+      /* hits keep their slots */
+      for (int pos = 0; pos < cnt; ++pos) {
+        const int s = bsl[list[pos]];
+        if (s >= 0) { out_slots[pos] = s; in_use[s] = 1; }
+      }
+      /* reuse order: free slots by index, then unselected resident blocks by
+       * (mass, slot) -- a selection sort keeps the rule plain */
+      int nc = 0;
+      for (int c = 0; c < C; ++c) if (sb[c] < 0) cand[nc++] = c;
+      const int n_free = nc;
+      for (int c = 0; c < C; ++c) if (sb[c] >= 0 && !in_use[c]) cand[nc++] = c;
+      for (int a = n_free; a < nc; ++a) {
+        int best = a;
+        for (int k = a + 1; k < nc; ++k) {
+          const int ck = cand[k], cb = cand[best];
+          if (mass[ck] < mass[cb] || (mass[ck] == mass[cb] && ck < cb)) best = k;
+        }
+        const int t = cand[a]; cand[a] = cand[best]; cand[best] = t;
+      }
+      /* misses take the candidates in list order */
+      int nf = 0;
+      for (int pos = 0; pos < cnt; ++pos) {
+        if (out_slots[pos] >= 0) continue;
+        const int s = cand[nf];
+        if (sb[s] >= 0) bsl[sb[s]] = -1;
+        sb[s] = list[pos];
+        bsl[list[pos]] = s;
+        out_slots[pos] = s;
+        fb[nf] = list[pos];
+        fs[nf] = s;
+        ++nf;
+      }
+      fetch_count[u] = nf;
+    }
+  }
+  free(in_use);
+  free(cand);
 }
 
 /*

@@ -52,6 +52,15 @@ MUTANTS = [
     ("fp8_amax_over_every_slot", "for (int s = 0; s < nv; ++s) {\n        const double* row = pool_row(pool",
      "for (int s = 0; s < bs; ++s) {\n        const double* row = pool_row(pool", 0),
     ("fp8_tail_slots_encoded", "if (s >= nv) {\n          memset", "if (s >= bs) {\n          memset", 0),
+    ("cache_evicts_highest_mass", "if (mass[ck] < mass[cb] || (mass[ck] == mass[cb] && ck < cb)) best = k;",
+     "if (mass[ck] > mass[cb] || (mass[ck] == mass[cb] && ck < cb)) best = k;", 0),
+    ("cache_ties_to_higher_slot", "(mass[ck] == mass[cb] && ck < cb)", "(mass[ck] == mass[cb] && ck > cb)", 0),
+    ("cache_free_slots_not_first", "for (int c = 0; c < C; ++c) if (sb[c] < 0) cand[nc++] = c;\n      const int n_free = nc;",
+     "const int n_free = 0;", 0),
+    ("cache_stale_reverse_map", "if (sb[s] >= 0) bsl[sb[s]] = -1;", "", 0),
+    ("cache_hits_refetched", "if (s >= 0) { out_slots[pos] = s; in_use[s] = 1; }", "", 0),
+    ("block_lse_reads_past_the_end", "for (int s = 0; s < bs && n * bs + s < L; ++s) {", "for (int s = 0; s < bs; ++s) {", 0),
+    ("slot_mass_sums_heads", "if (w > best) best = w;", "best += w;", 0),
     ("combine_lse_drops_max", "if (lse) lse[r] = M + log(wsum);", "if (lse) lse[r] = log(wsum);", 0),
 ]
 

@@ -719,3 +719,132 @@ def test_fp8_dequantized_attention_is_attention_over_decoded_values():
         V = gather(vd, data, 0, 0, range(3))
         np.testing.assert_allclose(out[0, h], sdpa(data.q64()[0, h], K, V, 0.25), rtol=1e-12,
                                    atol=1e-14)
+
+
+# ---------------------------------------------------------------- GPU block cache
+# KVDrive §5.1: a GPU window of critical blocks with lookahead eviction
+
+def test_cache_plan_golden(variants):
+    g = variants["cache_plan"]
+    C, N = g["num_slots"], g["num_blocks"]
+    sb = np.full((1, 1, C), -1, np.int32)
+    bsl = np.full((1, 1, N), -1, np.int32)
+    for st in g["steps"]:
+        k = len(st["sel"])
+        sel = np.array(st["sel"], np.int32).reshape(1, 1, k)
+        mass = np.array(st["mass_before"], np.float32).reshape(1, 1, C)
+        sb, bsl, slots, fb, fs, fc = oracle.cache_plan(sel, np.array([[k]], np.int32), sb, bsl, mass)
+        assert slots[0, 0].tolist() == st["sel_slots"], st["why"]
+        assert fc[0, 0] == len(st["fetch"])
+        assert [[int(a), int(b)] for a, b in zip(fb[0, 0, :fc[0, 0]], fs[0, 0, :fc[0, 0]])] == st["fetch"]
+        assert sb[0, 0].tolist() == st["slot_block"]
+        for c, blk in enumerate(st["slot_block"]):
+            if blk >= 0:
+                assert bsl[0, 0, blk] == c
+        assert (bsl[0, 0] >= 0).sum() == sum(1 for x in st["slot_block"] if x >= 0)
+
+
+def _check_plan_step(sel, cnt, sb0, bsl0, mass, out):
+    """Invariants of one cache step, checked independently of the plan's code."""
+    sb, bsl, slots, fb, fs, fc = out
+    B, Hkv, C = sb.shape
+    for b in range(B):
+        for j in range(Hkv):
+            k = int(cnt[b, j])
+            chosen = sel[b, j, :k].tolist()
+            before = {int(c): int(x) for c, x in enumerate(sb0[b, j])}
+            # every selected block is resident, at the slot reported for it
+            for pos, n in enumerate(chosen):
+                s = int(slots[b, j, pos])
+                assert sb[b, j, s] == n and bsl[b, j, n] == s
+            assert np.all(slots[b, j, k:] == -1)
+            # the two maps are inverse of each other
+            res = {int(x): c for c, x in enumerate(sb[b, j]) if x >= 0}
+            assert len(res) == int((sb[b, j] >= 0).sum())
+            assert {int(n): int(s) for n, s in enumerate(bsl[b, j]) if s >= 0} == res
+            # hits keep their slots; misses are exactly the fetches
+            hits = [n for n in chosen if bsl0[b, j, n] >= 0]
+            for n in hits:
+                assert bsl[b, j, n] == bsl0[b, j, n]
+            misses = [n for n in chosen if bsl0[b, j, n] < 0]
+            assert int(fc[b, j]) == len(misses)
+            assert fb[b, j, :len(misses)].tolist() == misses
+            used = fs[b, j, :len(misses)].tolist()
+            assert len(set(used)) == len(used)
+            free = [c for c in range(C) if before[c] < 0]
+            # free slots go first, in slot order
+            assert used[:min(len(free), len(used))] == free[:len(used)]
+            victims = used[len(free):]
+            survivors = [c for c in range(C) if before[c] >= 0 and before[c] not in chosen
+                         and c not in victims]
+            for v in victims:
+                assert before[v] >= 0 and before[v] not in chosen
+                for s in survivors:
+                    assert (mass[b, j, v], v) < (mass[b, j, s], s)
+            # every other slot keeps its block
+            for c in range(C):
+                if c not in used:
+                    assert sb[b, j, c] == before[c]
+
+
+@pytest.mark.parametrize("seed", range(4))
+def test_cache_plan_invariants_over_many_steps(seed):
+    rng = np.random.default_rng(400 + seed)
+    B, Hkv, N, C, K = 2, 3, 40, 12, 8
+    sb = np.full((B, Hkv, C), -1, np.int32)
+    bsl = np.full((B, Hkv, N), -1, np.int32)
+    for step in range(25):
+        cnt = rng.integers(1, K + 1, size=(B, Hkv)).astype(np.int32)
+        sel = np.full((B, Hkv, K), -1, np.int32)
+        for b in range(B):
+            for j in range(Hkv):
+                sel[b, j, :cnt[b, j]] = np.sort(rng.choice(N, cnt[b, j], replace=False))
+        # masses with many exact ties (multiples of 1/8, zeros for free slots)
+        mass = (rng.integers(0, 4, size=(B, Hkv, C)) / 8).astype(np.float32)
+        out = oracle.cache_plan(sel, cnt, sb, bsl, mass)
+        _check_plan_step(sel, cnt, sb, bsl, mass, out)
+        sb, bsl = out[0], out[1]
+
+
+def test_block_lse_sums_to_the_row_lse_and_matches_numpy():
+    data = mk(B=2, Hq=4, Hkv=2, D=16, lens=(61, 16), seed=51)
+    q64, k64 = data.q64(), data.k64()
+    scale = 0.25
+    bl = oracle.block_lse(q64, k64, data.block_table, data.seq_lens, 16, scale)
+    _, lse = oracle.attention(q64, k64, data.v64(), data.block_table, data.seq_lens, scale)
+    for b in range(2):
+        nb = data.spec.blocks(b)
+        for h in range(4):
+            np.testing.assert_allclose(scipy.special.logsumexp(bl[b, h, :nb]), lse[b, h], rtol=1e-13)
+            assert np.all(np.isneginf(bl[b, h, nb:]))
+            for n in range(nb):
+                z = gather(k64, data, b, h // 2, [n]) @ q64[b, h] * scale
+                np.testing.assert_allclose(bl[b, h, n], scipy.special.logsumexp(z), rtol=1e-13)
+
+
+def test_block_lse_over_a_selection():
+    data = mk(B=1, Hq=2, Hkv=1, D=8, lens=(100,), seed=52)
+    sel = np.array([[[1, 4, 6, -1]]], np.int32)
+    cnt = np.array([[3]], np.int32)
+    bl = oracle.block_lse(data.q64(), data.k64(), data.block_table, data.seq_lens, 16, 0.5, sel, cnt)
+    full = oracle.block_lse(data.q64(), data.k64(), data.block_table, data.seq_lens, 16, 0.5)
+    np.testing.assert_array_equal(bl[0, :, :3], full[0, :, [1, 4, 6]].T)
+    assert np.all(np.isneginf(bl[0, :, 3]))
+
+
+def test_slot_mass_is_the_attention_weight_of_each_block():
+    data = mk(B=1, Hq=4, Hkv=2, D=16, lens=(90,), seed=53)
+    q64, k64 = data.q64(), data.k64()
+    sel = np.array([[[0, 2, 5, -1], [1, 3, -1, -1]]], np.int32)
+    cnt = np.array([[3, 2]], np.int32)
+    slots = np.array([[[4, 0, 2, -1], [1, 5, -1, -1]]], np.int32)
+    bl = oracle.block_lse(q64, k64, data.block_table, data.seq_lens, 16, 0.25, sel, cnt)
+    _, lse = oracle.attention(q64, k64, data.v64(), data.block_table, data.seq_lens, 0.25, sel, cnt)
+    m = oracle.slot_mass(bl, lse, cnt, slots, 6)
+    for j in range(2):
+        w = np.exp(bl[0, 2 * j:2 * j + 2, :cnt[0, j]] - lse[0, 2 * j:2 * j + 2, None])
+        np.testing.assert_allclose(w.sum(axis=1), 1.0, rtol=1e-12)     # each head's weights
+        for pos in range(cnt[0, j]):
+            assert m[0, j, slots[0, j, pos]] == pytest.approx(w[:, pos].max(), rel=1e-14)
+        untouched = set(range(6)) - set(slots[0, j, :cnt[0, j]].tolist())
+        assert all(m[0, j, c] == 0 for c in untouched)
