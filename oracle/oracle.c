@@ -60,10 +60,11 @@
  *    entries are fetched from host memory and the entries with the lowest
  *    attention in the step are the ones dropped): per (sequence, KV head) a
  *    cache of C >= K block slots.  A step's selected blocks that are resident
- *    keep their slots; each missing block takes, in list order, the next of:
- *    the free slots in slot order, then the slots whose block is not
+ *    keep their slots; for m missing blocks the reused slots are the first m
+ *    of: the free slots in slot order, then the slots whose block is not
  *    selected, by increasing attention mass of the latest step (ties: lower
- *    slot first).  The mass of a slot is the attention weight its block
+ *    slot first); the missing blocks, in list order, take the reused slots in
+ *    increasing slot order.  The mass of a slot is the attention weight its block
  *    received in the latest step, summed over the block's tokens, max over
  *    the query heads of the group; 0 for a block the step did not attend.
  */
@@ -607,7 +608,14 @@ void oracle_cache_plan(const int32_t* sel, const int32_t* sel_count, int sel_str
         }
         const int t = cand[a]; cand[a] = cand[best]; cand[best] = t;
       }
-      /* misses take the candidates in list order */
+      /* the first m candidates are reused; misses take them in slot order */
+      int m = 0;
+      for (int pos = 0; pos < cnt; ++pos) if (out_slots[pos] < 0) ++m;
+      for (int a = 0; a < m; ++a) {
+        int lo = a;
+        for (int k = a + 1; k < m; ++k) if (cand[k] < cand[lo]) lo = k;
+        const int t = cand[a]; cand[a] = cand[lo]; cand[lo] = t;
+      }
       int nf = 0;
       for (int pos = 0; pos < cnt; ++pos) {
         if (out_slots[pos] >= 0) continue;

@@ -59,6 +59,7 @@ MUTANTS = [
      "const int n_free = 0;", 0),
     ("cache_stale_reverse_map", "if (sb[s] >= 0) bsl[sb[s]] = -1;", "", 0),
     ("cache_hits_refetched", "if (s >= 0) { out_slots[pos] = s; in_use[s] = 1; }", "", 0),
+    ("cache_misses_in_mass_order", "if (cand[k] < cand[lo]) lo = k;", "if (0) lo = k;", 0),
     ("block_lse_reads_past_the_end", "for (int s = 0; s < bs && n * bs + s < L; ++s) {", "for (int s = 0; s < bs; ++s) {", 0),
     ("slot_mass_sums_heads", "if (w > best) best = w;", "best += w;", 0),
     ("combine_lse_drops_max", "if (lse) lse[r] = M + log(wsum);", "if (lse) lse[r] = log(wsum);", 0),

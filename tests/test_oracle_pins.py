@@ -771,10 +771,14 @@ def _check_plan_step(sel, cnt, sb0, bsl0, mass, out):
             assert fb[b, j, :len(misses)].tolist() == misses
             used = fs[b, j, :len(misses)].tolist()
             assert len(set(used)) == len(used)
+            assert used == sorted(used), "misses take the reused slots in slot order"
             free = [c for c in range(C) if before[c] < 0]
-            # free slots go first, in slot order
-            assert used[:min(len(free), len(used))] == free[:len(used)]
-            victims = used[len(free):]
+            # free slots are reused first, in slot order
+            if len(used) <= len(free):
+                assert used == free[:len(used)]
+            else:
+                assert set(free) <= set(used)
+            victims = [c for c in used if before[c] >= 0]
             survivors = [c for c in range(C) if before[c] >= 0 and before[c] not in chosen
                          and c not in victims]
             for v in victims:
