@@ -10,6 +10,11 @@
  *                         blocks of the first / last tokens forced in
  *   kv_quantize_pages_fp8 K/V pages -> FP8 E4M3 cold pages with per-page scales
  *   kv_paged_decode_attn_fp8  decode attention over FP8 E4M3 cold pages
+ *   kv_cache_plan         GPU block cache: hits, misses and lookahead eviction
+ *   kv_cache_fetch        copy only the missing blocks into their cache slots
+ *   kv_cached_decode_attn decode attention over the cached blocks, with each
+ *                         block's log-sum-exp for the next eviction
+ *   kv_cache_slot_mass    eviction mass of every cache slot after a step
  *   kv_paged_decode_attn  split-K softmax decode attention, dense or over selected blocks
  *   kv_decode_combine     log-sum-exp merge of the split partials
  *   kv_append_token       store the new token's K/V and fold it into its page's meta
@@ -45,6 +50,14 @@
  *     kmean    [P, Hkv, D]           fp32    (mean key of the page's valid slots)
  *     K8, V8   [P, Hkv, bs, D]       uint8   FP8 E4M3 codes of cold pages
  *     kv_scales [P, Hkv, 2]          fp32    (K scale, V scale) of each cold page
+ *   GPU block cache with C = num_slots slots per (sequence, KV head):
+ *     cache_k, cache_v [B * C, Hkv, bs, D]  dtype  page b*C + s: slot s of sequence b
+ *     slot_block  int32 [B, Hkv, C]     block held by each slot, -1 free
+ *     block_slot  int32 [B, Hkv, maxN]  slot of each resident block, -1 otherwise
+ *     slot_mass   fp32  [B, Hkv, C]     eviction mass of each slot (latest step)
+ *     sel_slots   int32 [B, Hkv, sel_stride]  slot of each list position
+ *     fetch_block, fetch_slot int32 [B, Hkv, sel_stride]; fetch_count int32 [B, Hkv]
+ *     block_lse   fp32  [B, Hq, sel_stride]   per list position
  *     block_table int32 [B, maxN]    logical block n of sequence b -> page
  *     seq_lens    int32 [B]          L_b >= 1 tokens, current token included,
  *                                    N_b = ceil(L_b / bs) <= maxN
@@ -281,6 +294,77 @@ kv_status kv_paged_decode_attn_fp8(const kv_shape* shape, const void* q, const u
                                    const int32_t* sel_blocks, const int32_t* sel_count,
                                    int32_t sel_stride, float scale, int32_t num_splits,
                                    float* part_o, float* part_m, float* part_l, void* stream);
+
+/*
+ * GPU-resident block cache with lookahead eviction (KVDrive §5.1: a window of
+ * critical KV entries stays in GPU memory; each decode step fetches the new
+ * critical entries from host memory and drops the entries that received the
+ * least attention in the latest step, so host-to-GPU traffic is the set
+ * difference between consecutive selections).  Each (sequence, KV head) owns
+ * C = num_slots >= sel_stride slots of one 16-token K/V tile each.  A step is
+ *   kv_block_score_topk / kv_block_select -> kv_cache_plan -> kv_cache_fetch
+ *   -> kv_cached_decode_attn -> kv_decode_combine -> kv_cache_slot_mass.
+ * The caller initialises slot_block and block_slot to -1 and slot_mass to 0.
+ *
+ * kv_cache_plan: for every (b, j), with the step's list sel_blocks[b, j, 0..n)
+ * (distinct blocks, n = sel_count[b, j] <= sel_stride <= num_slots):
+ *   - a resident block (block_slot >= 0) keeps its slot;
+ *   - for the m missing blocks the reused slots are the first m of: the free
+ *     slots in slot order, then the slots whose block is not in the list, by
+ *     increasing slot_mass (ties: lower slot);
+ *   - the missing blocks, in list order, take the reused slots in increasing
+ *     slot order; an evicted block's block_slot becomes -1.
+ * Writes sel_slots (-1 past n), the fetch list fetch_block / fetch_slot (the m
+ * missing blocks and their slots, in list order, -1 padded to sel_stride) and
+ * fetch_count = m, and updates slot_block / block_slot in place.  One
+ * workgroup per (b, j); num_slots <= 8192.
+ */
+kv_status kv_cache_plan(const kv_shape* shape, int32_t num_slots, const int32_t* sel_blocks,
+                        const int32_t* sel_count, int32_t sel_stride, int32_t* slot_block,
+                        int32_t* block_slot, const float* slot_mass, int32_t* sel_slots,
+                        int32_t* fetch_block, int32_t* fetch_slot, int32_t* fetch_count,
+                        void* stream);
+
+/*
+ * Delta fetch: for k < fetch_count[b, j], copies the K and V tiles of block
+ * n = fetch_block[b, j, k] (pool page block_table[b, n], KV head j) into cache
+ * page b * num_slots + fetch_slot[b, j, k], KV head j.  With KV_FLAG_HOST_KV the
+ * pools are kv_host_alloc memory, read directly by the kernel (only the missing
+ * blocks cross the host link); the cache pools are device memory.
+ */
+kv_status kv_cache_fetch(const kv_shape* shape, int32_t num_slots, const void* k_cache,
+                         const void* v_cache, const int32_t* block_table,
+                         const int32_t* fetch_block, const int32_t* fetch_slot,
+                         const int32_t* fetch_count, int32_t fetch_stride, void* cache_k,
+                         void* cache_v, void* stream);
+
+/*
+ * kv_paged_decode_attn over the list sel_blocks with every block read from
+ * cache page b * num_slots + sel_slots[b, j, pos] (the block index n still sets
+ * the token positions and the valid count).  When block_lse is not NULL it
+ * also receives, per query head and list position,
+ *   block_lse[b, h, pos] = ln sum_{t in block} exp(scale * (q . k_t)),
+ * so exp(block_lse - lse) is the block's attention weight in the step.
+ */
+kv_status kv_cached_decode_attn(const kv_shape* shape, int32_t num_slots, const void* q,
+                                const void* cache_k, const void* cache_v,
+                                const int32_t* seq_lens, const int32_t* sel_blocks,
+                                const int32_t* sel_count, const int32_t* sel_slots,
+                                int32_t sel_stride, float scale, int32_t num_splits,
+                                float* part_o, float* part_m, float* part_l, float* block_lse,
+                                void* stream);
+
+/*
+ * Eviction mass after a step: slot_mass[b, j, :] = 0, then for every list
+ * position pos < sel_count[b, j]:
+ *   slot_mass[b, j, sel_slots[b, j, pos]] = max over the G query heads h of
+ *                                           group j of exp(block_lse[b, h, pos] - lse[b, h])
+ * (lse from kv_decode_combine of the same step).
+ */
+kv_status kv_cache_slot_mass(const kv_shape* shape, int32_t num_slots, const float* block_lse,
+                             const float* lse, const int32_t* sel_count,
+                             const int32_t* sel_slots, int32_t sel_stride, float* slot_mass,
+                             void* stream);
 
 /*
  * Pinned, device-mapped host memory for a zero-copy K/V pool (DirectKV review,

@@ -108,10 +108,10 @@ kv_status attn_common(const kv_shape* shape, const void* q, const void* k_cache,
   const int G = shape->num_q_heads / shape->num_kv_heads;
   return hip_status(
       kvd::launch_paged_attn(shape->dtype, shape->head_dim, G, q, k_cache, v_cache, kv_scales,
-                             block_table, seq_lens, sel_blocks, sel_count, sel_stride,
+                             block_table, seq_lens, sel_blocks, sel_count, sel_stride, nullptr, 0,
                              shape->num_seqs, shape->num_q_heads, shape->num_kv_heads,
                              shape->max_blocks_per_seq, num_splits, scale, part_o, part_m, part_l,
-                             (hipStream_t)stream),
+                             nullptr, (hipStream_t)stream),
       kv_scales ? "kv_paged_decode_attn_fp8 launch" : "kv_paged_decode_attn launch");
 }
 
@@ -349,6 +349,121 @@ kv_status kv_decode_combine(const kv_shape* shape, int32_t num_splits, const flo
   return hip_status(kvd::launch_combine(shape->head_dim, part_o, part_m, part_l, (int)rows,
                                         num_splits, out, lse_out, (hipStream_t)stream),
                     "kv_decode_combine launch");
+}
+
+static kv_status check_cache(const kv_shape* shape, int32_t num_slots, int32_t sel_stride) {
+  kv_status st = check_shape(shape);
+  if (st != KV_OK) return st;
+  if (num_slots < 1 || num_slots > kvd::kCacheMaxSlots)
+    return fail(KV_ERR_INVALID_ARG, "num_slots=%d must be in [1, %d]", num_slots,
+                kvd::kCacheMaxSlots);
+  if (sel_stride < 1 || sel_stride > num_slots)
+    return fail(KV_ERR_INVALID_ARG, "sel_stride=%d must be in [1, num_slots=%d]", sel_stride,
+                num_slots);
+  if ((long)shape->num_seqs * num_slots * shape->num_kv_heads > 0x7fffffffL)
+    return fail(KV_ERR_INVALID_ARG, "num_seqs * num_slots * num_kv_heads must fit in int32");
+  return KV_OK;
+}
+
+kv_status kv_cache_plan(const kv_shape* shape, int32_t num_slots, const int32_t* sel_blocks,
+                        const int32_t* sel_count, int32_t sel_stride, int32_t* slot_block,
+                        int32_t* block_slot, const float* slot_mass, int32_t* sel_slots,
+                        int32_t* fetch_block, int32_t* fetch_slot, int32_t* fetch_count,
+                        void* stream) {
+  kv_status st = check_cache(shape, num_slots, sel_stride);
+  if (st != KV_OK) return st;
+  if (!sel_blocks || !sel_count || !slot_block || !block_slot || !slot_mass || !sel_slots ||
+      !fetch_block || !fetch_slot || !fetch_count)
+    return fail(KV_ERR_INVALID_ARG, "every array of kv_cache_plan is required");
+  const void* ptrs[] = {sel_blocks, sel_count, slot_block, block_slot, slot_mass, sel_slots,
+                        fetch_block, fetch_slot, fetch_count};
+  for (const void* p : ptrs)
+    if (!aligned(p, 4)) return fail(KV_ERR_ALIGNMENT, "cache arrays must be 4-byte aligned");
+  return hip_status(kvd::launch_cache_plan(sel_blocks, sel_count, sel_stride, shape->num_seqs,
+                                           shape->num_kv_heads, shape->max_blocks_per_seq,
+                                           num_slots, slot_block, block_slot, slot_mass,
+                                           sel_slots, fetch_block, fetch_slot, fetch_count,
+                                           (hipStream_t)stream),
+                    "kv_cache_plan launch");
+}
+
+kv_status kv_cache_fetch(const kv_shape* shape, int32_t num_slots, const void* k_cache,
+                         const void* v_cache, const int32_t* block_table,
+                         const int32_t* fetch_block, const int32_t* fetch_slot,
+                         const int32_t* fetch_count, int32_t fetch_stride, void* cache_k,
+                         void* cache_v, void* stream) {
+  kv_status st = check_cache(shape, num_slots, fetch_stride);
+  if (st != KV_OK) return st;
+  if (!k_cache || !v_cache || !block_table || !fetch_block || !fetch_slot || !fetch_count ||
+      !cache_k || !cache_v)
+    return fail(KV_ERR_INVALID_ARG, "every array of kv_cache_fetch is required");
+  if (!aligned(k_cache, 16) || !aligned(v_cache, 16) || !aligned(cache_k, 16) ||
+      !aligned(cache_v, 16))
+    return fail(KV_ERR_ALIGNMENT, "the pools and the cache pools must be 16-byte aligned");
+  if (!aligned(block_table, 4) || !aligned(fetch_block, 4) || !aligned(fetch_slot, 4) ||
+      !aligned(fetch_count, 4))
+    return fail(KV_ERR_ALIGNMENT, "integer arrays must be 4-byte aligned");
+  return hip_status(kvd::launch_cache_fetch(shape->dtype, shape->head_dim, k_cache, v_cache,
+                                            block_table, fetch_block, fetch_slot, fetch_count,
+                                            fetch_stride, shape->num_seqs, shape->num_kv_heads,
+                                            shape->max_blocks_per_seq, num_slots, cache_k,
+                                            cache_v, (hipStream_t)stream),
+                    "kv_cache_fetch launch");
+}
+
+kv_status kv_cached_decode_attn(const kv_shape* shape, int32_t num_slots, const void* q,
+                                const void* cache_k, const void* cache_v,
+                                const int32_t* seq_lens, const int32_t* sel_blocks,
+                                const int32_t* sel_count, const int32_t* sel_slots,
+                                int32_t sel_stride, float scale, int32_t num_splits,
+                                float* part_o, float* part_m, float* part_l, float* block_lse,
+                                void* stream) {
+  kv_status st = check_cache(shape, num_slots, sel_stride);
+  if (st != KV_OK) return st;
+  if (!sel_blocks || !sel_count || !sel_slots)
+    return fail(KV_ERR_INVALID_ARG, "sel_blocks, sel_count and sel_slots are required");
+  if (!aligned(sel_slots, 4) || (block_lse && !aligned(block_lse, 4)))
+    return fail(KV_ERR_ALIGNMENT, "sel_slots and block_lse must be 4-byte aligned");
+  if (num_splits < 1 || num_splits > 65535 * 4)
+    return fail(KV_ERR_INVALID_ARG, "num_splits=%d must be in [1, 262140]", num_splits);
+  if (!q || !cache_k || !cache_v || !seq_lens || !part_o || !part_m || !part_l)
+    return fail(KV_ERR_INVALID_ARG, "q, cache_k, cache_v, seq_lens and partials are required");
+  if (!(scale > 0.0f) || !(scale < INFINITY))
+    return fail(KV_ERR_INVALID_ARG, "scale must be finite and positive");
+  if (!aligned(q, 16) || !aligned(cache_k, 16) || !aligned(cache_v, 16) || !aligned(part_o, 16))
+    return fail(KV_ERR_ALIGNMENT, "q, cache_k, cache_v and part_o must be 16-byte aligned");
+  if (!aligned(seq_lens, 4) || !aligned(part_m, 4) || !aligned(part_l, 4) ||
+      !aligned(sel_blocks, 4) || !aligned(sel_count, 4))
+    return fail(KV_ERR_ALIGNMENT, "integer and partial arrays must be 4-byte aligned");
+  // the cache pools hold num_seqs * num_slots pages and are device memory
+  kv_shape cs = *shape;
+  cs.flags = 0;
+  const int G = shape->num_q_heads / shape->num_kv_heads;
+  return hip_status(
+      kvd::launch_paged_attn(cs.dtype, cs.head_dim, G, q, cache_k, cache_v, nullptr,
+                             /*block_table=*/nullptr, seq_lens, sel_blocks, sel_count,
+                             sel_stride, sel_slots, num_slots, cs.num_seqs, cs.num_q_heads,
+                             cs.num_kv_heads, cs.max_blocks_per_seq, num_splits, scale, part_o,
+                             part_m, part_l, block_lse, (hipStream_t)stream),
+      "kv_cached_decode_attn launch");
+}
+
+kv_status kv_cache_slot_mass(const kv_shape* shape, int32_t num_slots, const float* block_lse,
+                             const float* lse, const int32_t* sel_count,
+                             const int32_t* sel_slots, int32_t sel_stride, float* slot_mass,
+                             void* stream) {
+  kv_status st = check_cache(shape, num_slots, sel_stride);
+  if (st != KV_OK) return st;
+  if (!block_lse || !lse || !sel_count || !sel_slots || !slot_mass)
+    return fail(KV_ERR_INVALID_ARG, "every array of kv_cache_slot_mass is required");
+  const void* ptrs[] = {block_lse, lse, sel_count, sel_slots, slot_mass};
+  for (const void* p : ptrs)
+    if (!aligned(p, 4)) return fail(KV_ERR_ALIGNMENT, "arrays must be 4-byte aligned");
+  return hip_status(kvd::launch_slot_mass(block_lse, lse, sel_count, sel_slots, sel_stride,
+                                          shape->num_seqs, shape->num_q_heads,
+                                          shape->num_kv_heads, num_slots, slot_mass,
+                                          (hipStream_t)stream),
+                    "kv_cache_slot_mass launch");
 }
 
 kv_status kv_host_alloc(size_t bytes, uint32_t flags, void** host_ptr, void** dev_ptr) {

@@ -86,9 +86,9 @@ __global__ __launch_bounds__(WAVES * kWave) void paged_attn_kernel(
     const void* __restrict__ q, const void* __restrict__ k_cache, const void* __restrict__ v_cache,
     const float* __restrict__ kv_scales, const int32_t* __restrict__ block_table,
     const int32_t* __restrict__ seq_lens, const int32_t* __restrict__ sel,
-    const int32_t* __restrict__ sel_count, int sel_stride, int Hq, int Hkv, int maxN, int S,
-    float qscale, float* __restrict__ part_o, float* __restrict__ part_m,
-    float* __restrict__ part_l) {
+    const int32_t* __restrict__ sel_count, int sel_stride, const int32_t* __restrict__ sel_slots,
+    int num_slots, int Hq, int Hkv, int maxN, int S, float qscale, float* __restrict__ part_o,
+    float* __restrict__ part_m, float* __restrict__ part_l, float* __restrict__ block_lse) {
   using G_ = RowGeom<DT, D>;
   using St = typename DT::storage;
   using KC = KVChunk<DT, KV8>;
@@ -130,7 +130,9 @@ __global__ __launch_bounds__(WAVES * kWave) void paged_attn_kernel(
   const uint8_t* kb = static_cast<const uint8_t*>(k_cache) + lane_off;
   const uint8_t* vb = static_cast<const uint8_t*>(v_cache) + lane_off;
   const int32_t* sel_row = SPARSE ? sel + ((size_t)b * Hkv + j) * sel_stride : nullptr;
-  const int32_t* bt_row = block_table + (size_t)b * maxN;
+  const int32_t* slots_row = (SPARSE && sel_slots) ? sel_slots + ((size_t)b * Hkv + j) * sel_stride
+                                                   : nullptr;
+  const int32_t* bt_row = block_table ? block_table + (size_t)b * maxN : nullptr;
 
   for (int base = p0; base < p1; base += kWave) {
     const int cnt = min(kWave, p1 - base);
@@ -138,7 +140,8 @@ __global__ __launch_bounds__(WAVES * kWave) void paged_attn_kernel(
     float my_sk = 1.0f, my_sv = 1.0f;
     if (lane < cnt) {
       const int n = SPARSE ? sel_row[base + lane] : base + lane;
-      my_page = bt_row[n];
+      // cached list: the block sits in slot sel_slots[.] of cache page b*C + slot
+      my_page = slots_row ? b * num_slots + slots_row[base + lane] : bt_row[n];
       my_valid = min(kBlockSize, L - n * kBlockSize);
       if constexpr (KV8) {
         const float2 sc = *reinterpret_cast<const float2*>(kv_scales + ((size_t)my_page * Hkv + j) * 2);
@@ -185,7 +188,7 @@ __global__ __launch_bounds__(WAVES * kWave) void paged_attn_kernel(
       }
       // running max per head; rescale only when it grows (wave-uniform test)
       bool grow = false;
-      float bm[G];
+      float bm[G], psum[G];
 #pragma unroll
       for (int g = 0; g < G; ++g) {
         float v = z[0][g];
@@ -206,6 +209,8 @@ __global__ __launch_bounds__(WAVES * kWave) void paged_attn_kernel(
         }
       }
 #pragma unroll
+      for (int g = 0; g < G; ++g) psum[g] = 0.0f;
+#pragma unroll
       for (int it = 0; it < NI; ++it) {
         float vf[E];
         KC::widen(vc[it], vf);
@@ -217,9 +222,20 @@ __global__ __launch_bounds__(WAVES * kWave) void paged_attn_kernel(
         for (int g = 0; g < G; ++g) {
           const float p = fast_exp2(z[it][g] - m[g]);
           lsum[g] += p;
+          psum[g] += p;
           const float pv = KV8 ? p * sv : p;
 #pragma unroll
           for (int e = 0; e < E; ++e) acc[g][e] = fmaf(pv, vf[e], acc[g][e]);
+        }
+      }
+      if (block_lse) {   // ln of the page's summed exp-logits per head (its attention weight
+                         // is exp(block_lse - lse))
+#pragma unroll
+        for (int g = 0; g < G; ++g) {
+          // every lane of a token row holds that token's p: sum over the row groups
+          const float t = cross_group_reduce<LPR, OpSum>(psum[g]);
+          if (lane == 0)
+            block_lse[(row0 + g) * sel_stride + base + i] = (m[g] + __log2f(t)) * kLn2;
         }
       }
     };
@@ -386,9 +402,9 @@ __global__ __launch_bounds__(WAVES * kWave) KVD_MFMA_OCCUPANCY void paged_attn_m
     const void* __restrict__ q, const void* __restrict__ k_cache, const void* __restrict__ v_cache,
     const float* __restrict__ kv_scales, const int32_t* __restrict__ block_table,
     const int32_t* __restrict__ seq_lens, const int32_t* __restrict__ sel,
-    const int32_t* __restrict__ sel_count, int sel_stride, int Hq, int Hkv, int maxN, int S,
-    float qscale, float* __restrict__ part_o, float* __restrict__ part_m,
-    float* __restrict__ part_l) {
+    const int32_t* __restrict__ sel_count, int sel_stride, const int32_t* __restrict__ sel_slots,
+    int num_slots, int Hq, int Hkv, int maxN, int S, float qscale, float* __restrict__ part_o,
+    float* __restrict__ part_m, float* __restrict__ part_l, float* __restrict__ block_lse) {
   static_assert(G >= 2 && G <= 8, "the group fills 2..8 of the 16 MFMA rows");
   using St = typename DT::storage;
   using Ops = MfmaOps<DT>;
@@ -428,7 +444,9 @@ __global__ __launch_bounds__(WAVES * kWave) KVD_MFMA_OCCUPANCY void paged_attn_m
   const uint8_t* vb = static_cast<const uint8_t*>(v_cache) +
                       ((size_t)j * kBlockSize * D + (size_t)(4 * grp) * D + 2 * NDW * col) * EB;
   const int32_t* sel_row = SPARSE ? sel + ((size_t)b * Hkv + j) * sel_stride : nullptr;
-  const int32_t* bt_row = block_table + (size_t)b * maxN;
+  const int32_t* slots_row = (SPARSE && sel_slots) ? sel_slots + ((size_t)b * Hkv + j) * sel_stride
+                                                   : nullptr;
+  const int32_t* bt_row = block_table ? block_table + (size_t)b * maxN : nullptr;
 
   for (int base = p0; base < p1; base += kWave) {
     const int cnt = min(kWave, p1 - base);
@@ -436,7 +454,8 @@ __global__ __launch_bounds__(WAVES * kWave) KVD_MFMA_OCCUPANCY void paged_attn_m
     float my_sk = 1.0f, my_sv = 1.0f;
     if (lane < cnt) {
       const int n = SPARSE ? sel_row[base + lane] : base + lane;
-      my_page = bt_row[n];
+      // cached list: the block sits in slot sel_slots[.] of cache page b*C + slot
+      my_page = slots_row ? b * num_slots + slots_row[base + lane] : bt_row[n];
       my_valid = min(kBlockSize, L - n * kBlockSize);
       if constexpr (KV8) {
         const float2 sc = *reinterpret_cast<const float2*>(kv_scales + ((size_t)my_page * Hkv + j) * 2);
@@ -536,6 +555,13 @@ __global__ __launch_bounds__(WAVES * kWave) KVD_MFMA_OCCUPANCY void paged_attn_m
 #pragma unroll
       for (int i = 0; i < 4; ++i) p[i] = fast_exp2(z[i] - m);
       lsum += (p[0] + p[1]) + (p[2] + p[3]);
+      if (block_lse) {   // ln of the page's summed exp-logits per head
+        float ps = (p[0] + p[1]) + (p[2] + p[3]);
+        ps += xor16(ps);
+        ps += xor32(ps);
+        if (grp == 0 && col < G)
+          block_lse[(row0 + col) * sel_stride + base + it] = (m + __log2f(ps)) * kLn2;
+      }
       if constexpr (KV8) {    // the page's V scale rides on its weights
 #pragma unroll
         for (int i = 0; i < 4; ++i) p[i] *= sv;
@@ -678,9 +704,10 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
 hipError_t launch_paged_attn(int dtype, int D, int G, const void* q, const void* k_cache,
                              const void* v_cache, const float* kv_scales,
                              const int32_t* block_table, const int32_t* seq_lens,
-                             const int32_t* sel, const int32_t* sel_count, int sel_stride, int B,
-                             int Hq, int Hkv, int maxN, int S, float scale, float* part_o,
-                             float* part_m, float* part_l, hipStream_t stream) {
+                             const int32_t* sel, const int32_t* sel_count, int sel_stride,
+                             const int32_t* sel_slots, int num_slots, int B, int Hq, int Hkv,
+                             int maxN, int S, float scale, float* part_o, float* part_m,
+                             float* part_l, float* block_lse, hipStream_t stream) {
   constexpr int WAVES = KVD_ATTN_WAVES;
   const dim3 grid((S + WAVES - 1) / WAVES, Hkv, B);
   const float qscale = scale * kLog2e;
@@ -694,13 +721,15 @@ hipError_t launch_paged_attn(int dtype, int D, int G, const void* q, const void*
           if constexpr (!std::is_same_v<DT, F32> && GG >= 2) {
             hipLaunchKernelGGL((paged_attn_mfma_kernel<DT, DD, GG, WAVES, SP, K8>), grid,
                                dim3(WAVES * kWave), 0, stream, q, k_cache, v_cache, kv_scales,
-                               block_table, seq_lens, sel, sel_count, sel_stride, Hq, Hkv, maxN,
-                               S, qscale, part_o, part_m, part_l);
+                               block_table, seq_lens, sel, sel_count, sel_stride, sel_slots,
+                               num_slots, Hq, Hkv, maxN, S, qscale, part_o, part_m, part_l,
+                               block_lse);
           } else {
             hipLaunchKernelGGL((paged_attn_kernel<DT, DD, GG, WAVES, SP, K8>), grid,
                                dim3(WAVES * kWave), 0, stream, q, k_cache, v_cache, kv_scales,
-                               block_table, seq_lens, sel, sel_count, sel_stride, Hq, Hkv, maxN,
-                               S, qscale, part_o, part_m, part_l);
+                               block_table, seq_lens, sel, sel_count, sel_stride, sel_slots,
+                               num_slots, Hq, Hkv, maxN, S, qscale, part_o, part_m, part_l,
+                               block_lse);
           }
         };
         // kv_scales marks code pages

@@ -34,12 +34,33 @@ hipError_t launch_topk(const float* scores, const int32_t* seq_lens, int B, int 
 
 // kv_scales == nullptr: K/V pools in `dtype`; otherwise E4M3 code pools with
 // fp32 (k, v) scales per (page, KV head)
+// sel_slots (with sel): the list's blocks live in cache page b*num_slots + slot;
+// block_lse (with sel, nullable): ln of each list block's summed exp-logits per query head
 hipError_t launch_paged_attn(int dtype, int D, int G, const void* q, const void* k_cache,
                              const void* v_cache, const float* kv_scales,
                              const int32_t* block_table, const int32_t* seq_lens,
-                             const int32_t* sel, const int32_t* sel_count, int sel_stride, int B,
-                             int Hq, int Hkv, int maxN, int S, float scale, float* part_o,
-                             float* part_m, float* part_l, hipStream_t stream);
+                             const int32_t* sel, const int32_t* sel_count, int sel_stride,
+                             const int32_t* sel_slots, int num_slots, int B, int Hq, int Hkv,
+                             int maxN, int S, float scale, float* part_o, float* part_m,
+                             float* part_l, float* block_lse, hipStream_t stream);
+
+hipError_t launch_cache_plan(const int32_t* sel, const int32_t* sel_count, int sel_stride, int B,
+                             int Hkv, int maxN, int C, int32_t* slot_block, int32_t* block_slot,
+                             const float* slot_mass, int32_t* sel_slots, int32_t* fetch_block,
+                             int32_t* fetch_slot, int32_t* fetch_count, hipStream_t stream);
+
+hipError_t launch_cache_fetch(int dtype, int D, const void* k_pool, const void* v_pool,
+                              const int32_t* block_table, const int32_t* fetch_block,
+                              const int32_t* fetch_slot, const int32_t* fetch_count,
+                              int fetch_stride, int B, int Hkv, int maxN, int C, void* cache_k,
+                              void* cache_v, hipStream_t stream);
+
+hipError_t launch_slot_mass(const float* block_lse, const float* lse, const int32_t* sel_count,
+                            const int32_t* sel_slots, int sel_stride, int B, int Hq, int Hkv,
+                            int C, float* slot_mass, hipStream_t stream);
+
+// Largest cache (slots per sequence and KV head) the plan kernel holds.
+constexpr int kCacheMaxSlots = 8192;
 
 hipError_t launch_quantize_fp8(int dtype, int D, const void* k_cache, const void* v_cache,
                                const int32_t* page_ids, const int32_t* valid_tokens, int n_ids,

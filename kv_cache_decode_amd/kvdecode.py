@@ -29,7 +29,8 @@ EXPORTS = (
     "kv_block_meta_build", "kv_block_mean_build", "kv_append_token",
     "kv_score_topk_workspace_size", "kv_block_score_topk", "kv_max_forced_blocks",
     "kv_block_select", "kv_auto_num_splits", "kv_paged_decode_attn", "kv_decode_combine",
-    "kv_quantize_pages_fp8", "kv_paged_decode_attn_fp8", "kv_host_alloc", "kv_host_free",
+    "kv_quantize_pages_fp8", "kv_paged_decode_attn_fp8", "kv_cache_plan", "kv_cache_fetch",
+    "kv_cached_decode_attn", "kv_cache_slot_mass", "kv_host_alloc", "kv_host_free",
     "kv_status_string", "kv_last_error_message",
 )
 
@@ -89,6 +90,10 @@ def _load() -> ctypes.CDLL:
         "kv_decode_combine": (I32, [S, I32, P, P, P, P, P, P]),
         "kv_quantize_pages_fp8": (I32, [S, P, P, P, P, I32, P, P, P, P]),
         "kv_paged_decode_attn_fp8": (I32, [S, P, P, P, P, P, P, P, P, I32, F, I32, P, P, P, P]),
+        "kv_cache_plan": (I32, [S, I32, P, P, I32, P, P, P, P, P, P, P, P]),
+        "kv_cache_fetch": (I32, [S, I32, P, P, P, P, P, P, I32, P, P, P]),
+        "kv_cached_decode_attn": (I32, [S, I32, P, P, P, P, P, P, P, I32, F, I32, P, P, P, P, P]),
+        "kv_cache_slot_mass": (I32, [S, I32, P, P, P, P, I32, P, P]),
         "kv_host_alloc": (I32, [SZ, U32, ctypes.POINTER(P), ctypes.POINTER(P)]),
         "kv_host_free": (I32, [P]),
         "kv_status_string": (ctypes.c_char_p, [I32]),
@@ -222,6 +227,41 @@ def kv_paged_decode_attn_fp8(shape: KVShape, q: Buf, k_fp8: Buf, v_fp8: Buf, kv_
                                          _p(sel_blocks), _p(sel_count), sel_stride, scale,
                                          num_splits, _p(part_o), _p(part_m), _p(part_l),
                                          _stream(stream)))
+
+
+def kv_cache_plan(shape: KVShape, num_slots: int, sel_blocks: Buf, sel_count: Buf,
+                  sel_stride: int, slot_block: Buf, block_slot: Buf, slot_mass: Buf,
+                  sel_slots: Buf, fetch_block: Buf, fetch_slot: Buf, fetch_count: Buf,
+                  stream=None) -> None:
+    _check(_lib.kv_cache_plan(ctypes.byref(shape), num_slots, _p(sel_blocks), _p(sel_count),
+                              sel_stride, _p(slot_block), _p(block_slot), _p(slot_mass),
+                              _p(sel_slots), _p(fetch_block), _p(fetch_slot), _p(fetch_count),
+                              _stream(stream)))
+
+
+def kv_cache_fetch(shape: KVShape, num_slots: int, k_cache: Buf, v_cache: Buf,
+                   block_table: Buf, fetch_block: Buf, fetch_slot: Buf, fetch_count: Buf,
+                   fetch_stride: int, cache_k: Buf, cache_v: Buf, stream=None) -> None:
+    _check(_lib.kv_cache_fetch(ctypes.byref(shape), num_slots, _p(k_cache), _p(v_cache),
+                               _p(block_table), _p(fetch_block), _p(fetch_slot), _p(fetch_count),
+                               fetch_stride, _p(cache_k), _p(cache_v), _stream(stream)))
+
+
+def kv_cached_decode_attn(shape: KVShape, num_slots: int, q: Buf, cache_k: Buf, cache_v: Buf,
+                          seq_lens: Buf, sel_blocks: Buf, sel_count: Buf, sel_slots: Buf,
+                          sel_stride: int, scale: float, num_splits: int, part_o: Buf,
+                          part_m: Buf, part_l: Buf, block_lse: Buf = None, stream=None) -> None:
+    _check(_lib.kv_cached_decode_attn(ctypes.byref(shape), num_slots, _p(q), _p(cache_k),
+                                      _p(cache_v), _p(seq_lens), _p(sel_blocks), _p(sel_count),
+                                      _p(sel_slots), sel_stride, scale, num_splits, _p(part_o),
+                                      _p(part_m), _p(part_l), _p(block_lse), _stream(stream)))
+
+
+def kv_cache_slot_mass(shape: KVShape, num_slots: int, block_lse: Buf, lse: Buf, sel_count: Buf,
+                       sel_slots: Buf, sel_stride: int, slot_mass: Buf, stream=None) -> None:
+    _check(_lib.kv_cache_slot_mass(ctypes.byref(shape), num_slots, _p(block_lse), _p(lse),
+                                   _p(sel_count), _p(sel_slots), sel_stride, _p(slot_mass),
+                                   _stream(stream)))
 
 
 def kv_host_alloc(nbytes: int, flags: int = KV_HOST_COHERENT):

@@ -220,6 +220,59 @@ class DeviceWorkload:
         self.combine(S, stream)
         return S
 
+    # ------------------------------------------------------------ GPU block cache
+    def cache_init(self, num_slots: int, k: int):
+        """Cache pools [B * C, Hkv, bs, D] and an empty directory for lists of k blocks."""
+        spec, dev = self.spec, self.device
+        B, Hq, Hkv, D, bs = spec.num_seqs, spec.num_q_heads, spec.num_kv_heads, spec.head_dim, \
+            spec.block_size
+        C = num_slots
+        self.num_slots = C
+        self.cache_k = torch.zeros((B * C, Hkv, bs, D), dtype=TORCH_DTYPES[spec.dtype], device=dev)
+        self.cache_v = torch.zeros_like(self.cache_k)
+        self.slot_block = torch.full((B, Hkv, C), -1, dtype=torch.int32, device=dev)
+        self.block_slot = torch.full((B, Hkv, spec.max_blocks), -1, dtype=torch.int32, device=dev)
+        self.slot_mass = torch.zeros((B, Hkv, C), dtype=torch.float32, device=dev)
+        self.sel_slots = torch.empty((B, Hkv, k), dtype=torch.int32, device=dev)
+        self.fetch_block = torch.empty((B, Hkv, k), dtype=torch.int32, device=dev)
+        self.fetch_slot = torch.empty((B, Hkv, k), dtype=torch.int32, device=dev)
+        self.fetch_count = torch.empty((B, Hkv), dtype=torch.int32, device=dev)
+        self.block_lse = torch.empty((B, Hq, k), dtype=torch.float32, device=dev)
+
+    def cache_plan(self, stream=None):
+        kd.kv_cache_plan(self.shape, self.num_slots, self.sel, self.sel_count, self.topk,
+                         self.slot_block, self.block_slot, self.slot_mass, self.sel_slots,
+                         self.fetch_block, self.fetch_slot, self.fetch_count, stream)
+
+    def cache_fetch(self, stream=None):
+        kd.kv_cache_fetch(self.shape, self.num_slots, self.k_cache, self.v_cache,
+                          self.block_table, self.fetch_block, self.fetch_slot, self.fetch_count,
+                          self.topk, self.cache_k, self.cache_v, stream)
+
+    def cached_attention(self, num_splits: Optional[int] = None, with_lse: bool = True,
+                         stream=None):
+        S = num_splits or self.auto_splits(True)
+        po, pm, pl = self.partials(S)
+        kd.kv_cached_decode_attn(self.shape, self.num_slots, self.q, self.cache_k, self.cache_v,
+                                 self.seq_lens, self.sel, self.sel_count, self.sel_slots,
+                                 self.topk, self.scale, S, po, pm, pl,
+                                 self.block_lse if with_lse else None, stream)
+        return S
+
+    def cache_slot_mass(self, stream=None):
+        kd.kv_cache_slot_mass(self.shape, self.num_slots, self.block_lse, self.lse,
+                              self.sel_count, self.sel_slots, self.topk, self.slot_mass, stream)
+
+    def cache_step(self, k: int, num_splits: Optional[int] = None, stream=None):
+        """select -> plan -> delta fetch -> attention over the cache -> merge -> masses."""
+        self.score_topk(k, stream)
+        self.cache_plan(stream)
+        self.cache_fetch(stream)
+        S = self.cached_attention(num_splits, True, stream)
+        self.combine(S, stream)
+        self.cache_slot_mass(stream)
+        return S
+
     def combine(self, num_splits: int, stream=None):
         po, pm, pl = self.partials(num_splits)
         kd.kv_decode_combine(self.shape, num_splits, po, pm, pl, self.out, self.lse, stream)

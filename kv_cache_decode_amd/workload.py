@@ -277,3 +277,24 @@ def random_selection(data: WorkloadData, k: int, seed: int) -> tuple:
 def kv_bytes(spec: Workload, blocks: int) -> int:
     """Bytes of K plus V for ``blocks`` (block, KV head) tiles."""
     return 2 * blocks * spec.block_size * spec.head_dim * spec.elem_bytes
+
+
+def query_trajectory(data: WorkloadData, steps: int, rho: float, seed: int) -> list:
+    """Seeded queries of `steps` consecutive decode steps, in the storage dtype.
+
+    Step 0 is the workload's own query.  Each later query follows an AR(1) walk
+    per element, q_t = rho * q_{t-1} + sqrt(1 - rho^2) * xi_t with xi_t standard
+    normal (float64, then float32, then the storage dtype by round-to-nearest-
+    even), so consecutive steps attend to similar blocks (the temporal locality
+    of the selections that a GPU block cache relies on) while the marginal
+    distribution stays N(0, 1).
+    """
+    rng = np.random.default_rng(seed)
+    spec = data.spec
+    q = data.q64()
+    out = [data.q_raw]
+    for _ in range(1, steps):
+        q = rho * q + np.sqrt(1.0 - rho * rho) * rng.standard_normal(q.shape)
+        out.append(to_storage(q.astype(np.float32), spec.dtype))
+        q = storage_to_f64(out[-1], spec.dtype)
+    return out

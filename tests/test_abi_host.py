@@ -276,3 +276,31 @@ def test_fp8_argument_checks():
     expect(kd.KV_ERR_UNSUPPORTED, lambda stream: at(shape(head_dim=96), A16, A16, A16, A16, A16, A16,
                                                     None, None, 0, 0.1, 1, A16, A16, A16,
                                                     stream=stream))
+
+
+def test_cache_argument_checks():
+    s = shape()
+    pl = kd.kv_cache_plan
+    args = lambda C=16, stride=8: (s, C, A16, A16, stride, A16, A16, A16, A16, A16, A16, A16)
+    expect(kd.KV_ERR_INVALID_ARG, lambda stream: pl(*args(C=0), stream=stream))
+    expect(kd.KV_ERR_INVALID_ARG, lambda stream: pl(*args(C=8193, stride=8), stream=stream))
+    expect(kd.KV_ERR_INVALID_ARG, lambda stream: pl(*args(C=16, stride=17), stream=stream))
+    expect(kd.KV_ERR_INVALID_ARG, lambda stream: pl(s, 16, None, A16, 8, A16, A16, A16, A16, A16,
+                                                    A16, A16, stream=stream))
+    expect(kd.KV_ERR_ALIGNMENT, lambda stream: pl(s, 16, ODD, A16, 8, A16, A16, A16, A16, A16,
+                                                  A16, A16, stream=stream))
+    f = kd.kv_cache_fetch
+    expect(kd.KV_ERR_ALIGNMENT, lambda stream: f(s, 16, A16, A16, A16, A16, A16, A16, 8, A4, A16,
+                                                 stream=stream))
+    expect(kd.KV_ERR_INVALID_ARG, lambda stream: f(s, 16, A16, None, A16, A16, A16, A16, 8, A16,
+                                                   A16, stream=stream))
+    at = kd.kv_cached_decode_attn
+    expect(kd.KV_ERR_INVALID_ARG, lambda stream: at(s, 16, A16, A16, A16, A16, A16, A16, None, 8,
+                                                    0.1, 2, A16, A16, A16, None, stream=stream))
+    expect(kd.KV_ERR_INVALID_ARG, lambda stream: at(s, 16, A16, A16, A16, A16, A16, A16, A16, 8,
+                                                    0.0, 2, A16, A16, A16, None, stream=stream))
+    expect(kd.KV_ERR_ALIGNMENT, lambda stream: at(s, 16, A16, A4, A16, A16, A16, A16, A16, 8,
+                                                  0.1, 2, A16, A16, A16, None, stream=stream))
+    m = kd.kv_cache_slot_mass
+    expect(kd.KV_ERR_INVALID_ARG, lambda stream: m(s, 16, A16, None, A16, A16, 8, A16, stream=stream))
+    expect(kd.KV_ERR_ALIGNMENT, lambda stream: m(s, 16, A16, A16, A16, A16, 8, ODD, stream=stream))
