@@ -428,6 +428,9 @@ def run_zero_copy(args):
     e[1].record()
     torch.cuda.synchronize()
     dense_ms = e[0].elapsed_time(e[1])
+    # decode trajectories through the GPU block cache (delta fetch of the missing
+    # blocks only) against the plain zero-copy step, on the same queries
+    cache = None if args.no_variants else time_cache_trajectory(args, dw, data, k, S)
     # the same sparse step over FP8 E4M3 code pages in host memory: half the bytes
     fp8_ms = []
     if not args.no_variants:
@@ -471,6 +474,7 @@ def run_zero_copy(args):
                "frac_of_h2d": f8_bytes / (f8 * 1e-3) / 1e9 / h2d_gbps,
                "speedup_vs_bf16": attn / f8}
     return {
+        "block_cache": cache,
         "fp8_pages": fp8,
         "workload": HOSTKV_WORKLOAD,
         "sparse_attn_us": attn * 1e3,
@@ -483,6 +487,69 @@ def run_zero_copy(args):
         "frac_of_h2d": host_gbps / h2d_gbps,
         "splits": S,
     }
+
+
+CACHE_STEPS = 32
+CACHE_RHO = 0.95
+
+
+def time_cache_trajectory(args, dw, data, k, S):
+    """Per-step time of a CACHE_STEPS-step decode trajectory (queries: the seeded
+    AR(1) walk of workload.query_trajectory, rho = CACHE_RHO), plain zero-copy
+    against the GPU block cache at several capacities.  The trajectory runs once
+    untimed to fill the cache (and to count the fetched blocks), then once timed."""
+    import torch
+    from kv_cache_decode_amd import workload as wl
+    from kv_cache_decode_amd.step import storage_tensor
+
+    spec = data.spec
+    q0 = dw.q
+    qs = [storage_tensor(q, spec.dtype).to(dw.device)
+          for q in wl.query_trajectory(data, CACHE_STEPS, CACHE_RHO, seed=21)]
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+
+    def run(step_fn, record=None):
+        torch.cuda.synchronize()
+        e0.record()
+        for t, q in enumerate(qs):
+            dw.q = q
+            step_fn()
+            if record is not None:
+                record.append(dw.fetch_count.clone())
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) * 1e3 / len(qs)
+
+    def plain():
+        dw.score_topk(k)
+        dw.attention(sparse=True, num_splits=S)
+        dw.combine(S)
+
+    run(plain)
+    res = {"steps": CACHE_STEPS, "rho": CACHE_RHO, "topk_blocks": k,
+           "plain_zero_copy_step_us": run(plain)}
+    tile = spec.block_size * spec.head_dim * spec.elem_bytes * 2        # K + V of one block
+    for C in (256, 512, 1024):
+        dw.cache_init(C, k)
+        counts = []
+        run(lambda: dw.cache_step(k, S), counts)                        # cold start, counted
+        cold = int(sum(int(c.sum()) for c in counts))
+        counts = []
+        run(lambda: dw.cache_step(k, S), counts)                        # warm, counted
+        warm = [int(c.sum()) for c in counts]
+        us = run(lambda: dw.cache_step(k, S))                           # warm, timed
+        selected = k * spec.num_seqs * spec.num_kv_heads
+        res[f"slots_{C}"] = {
+            "step_us": us,
+            "fetched_blocks_per_step": float(np.mean(warm)),
+            "hit_rate": 1.0 - float(np.mean(warm)) / selected,
+            "host_link_bytes_per_step": float(np.mean(warm)) * tile,
+            "cold_fetched_blocks_first_pass": cold,
+        }
+        del dw.cache_k, dw.cache_v
+    dw.q = q0
+    torch.cuda.empty_cache()
+    return res
 
 
 # ---------------------------------------------------------------- CPU baseline (oracle)

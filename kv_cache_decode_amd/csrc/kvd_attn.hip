@@ -222,14 +222,14 @@ __global__ __launch_bounds__(WAVES * kWave) void paged_attn_kernel(
         for (int g = 0; g < G; ++g) {
           const float p = fast_exp2(z[it][g] - m[g]);
           lsum[g] += p;
-          psum[g] += p;
+          if constexpr (SPARSE) psum[g] += p;
           const float pv = KV8 ? p * sv : p;
 #pragma unroll
           for (int e = 0; e < E; ++e) acc[g][e] = fmaf(pv, vf[e], acc[g][e]);
         }
       }
-      if (block_lse) {   // ln of the page's summed exp-logits per head (its attention weight
-                         // is exp(block_lse - lse))
+      if (SPARSE && block_lse) {   // ln of the page's summed exp-logits per head (its
+                                   // attention weight is exp(block_lse - lse)); lists only
 #pragma unroll
         for (int g = 0; g < G; ++g) {
           // every lane of a token row holds that token's p: sum over the row groups
@@ -555,7 +555,7 @@ __global__ __launch_bounds__(WAVES * kWave) KVD_MFMA_OCCUPANCY void paged_attn_m
 #pragma unroll
       for (int i = 0; i < 4; ++i) p[i] = fast_exp2(z[i] - m);
       lsum += (p[0] + p[1]) + (p[2] + p[3]);
-      if (block_lse) {   // ln of the page's summed exp-logits per head
+      if (SPARSE && block_lse) {   // ln of the page's summed exp-logits per head; lists only
         float ps = (p[0] + p[1]) + (p[2] + p[3]);
         ps += xor16(ps);
         ps += xor32(ps);
