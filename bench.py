@@ -41,6 +41,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBPS = 8000.0
+GRAPH_STEPS = 8          # decode steps captured per HIP graph (cycling over the copies)
 WORKLOAD = "llama3.1_8b_gqa_b1_128k_bf16"
 HOSTKV_WORKLOAD = "llama3.1_8b_gqa_b1_128k_bf16_hostkv"
 # measured beside the headline step at kernel level (not part of `value`)
@@ -174,26 +175,36 @@ def run_gpu(args, spec, data):
         return t0.elapsed_time(t1), time.perf_counter() - wall0
 
     def graph_us(fn):
-        """Average replay time of one HIP graph per copy holding fn(copy)."""
+        """Average time per step of fn, replayed from one HIP graph that holds
+        GRAPH_STEPS steps cycling over the workload copies (one host launch per
+        GRAPH_STEPS steps, so a short step is not timed at the host's graph
+        launch rate)."""
         try:
-            gs = []
             side = torch.cuda.Stream()
-            for c in copies:
-                side.wait_stream(torch.cuda.current_stream())
-                with torch.cuda.stream(side):
+            side.wait_stream(torch.cuda.current_stream())
+            with torch.cuda.stream(side):
+                for c in copies:
                     fn(c)
-                torch.cuda.current_stream().wait_stream(side)
-                g_ = torch.cuda.CUDAGraph()
-                with torch.cuda.graph(g_):
-                    fn(c)
-                gs.append(g_)
-            for i in range(args.warmup):
-                gs[i % len(gs)].replay()
-            ms_, _ = time_loop(lambda i: gs[i % len(gs)].replay())
-            del gs
+            torch.cuda.current_stream().wait_stream(side)
+            g_ = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g_):
+                for i in range(GRAPH_STEPS):
+                    fn(copies[i % len(copies)])
+            reps = max(1, args.steps // GRAPH_STEPS)
+            for _ in range(max(1, args.warmup // GRAPH_STEPS)):
+                g_.replay()
+            t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            torch.cuda.synchronize()
+            t0.record()
+            for _ in range(reps):
+                g_.replay()
+            t1.record()
+            torch.cuda.synchronize()
+            del g_
+            return t0.elapsed_time(t1) * 1e3 / (reps * GRAPH_STEPS)
         except RuntimeError:
             ms_, _ = time_loop(lambda i: fn(copies[i % len(copies)]))
-        return ms_ * 1e3 / args.steps
+            return ms_ * 1e3 / args.steps
 
     res = {"s_sparse": s_sparse, "s_dense": s_dense}
     if not args.only_variants:
@@ -281,6 +292,10 @@ def run_gpu(args, spec, data):
 
 def time_fp8(args, copies, k, s_sparse, s_dense, time_loop, graph_us):
     import torch
+    from kv_cache_decode_amd import kvdecode as kd
+    # the code-page path has its own split heuristic
+    s_sparse = kd.kv_auto_num_splits_fp8(copies[0].shape, k)
+    s_dense = kd.kv_auto_num_splits_fp8(copies[0].shape, copies[0].spec.max_blocks)
 
     def kernel_us(fn):
         for i in range(args.warmup):
@@ -309,6 +324,7 @@ def time_fp8(args, copies, k, s_sparse, s_dense, time_loop, graph_us):
 
     res["decode_sparse_us"] = graph_us(decode_sparse_fp8)
     res["decode_dense_us"] = graph_us(decode_dense_fp8)
+    res["s_sparse"], res["s_dense"] = s_sparse, s_dense
     return res
 
 
@@ -605,11 +621,12 @@ def copy_calibration():
     print(json.dumps({"copy_bytes_read": n, "copy_bytes_written": n}), flush=True)
 
 
-def fp8_record(spec, f: dict, s_sparse: int, s_dense: int) -> dict:
+def fp8_record(spec, f: dict) -> dict:
     """FP8 E4M3 cold pages in HBM: per (page, KV head) unit the attention reads
     2 * 16 * D code bytes and 8 bytes of scales instead of 2 * 16 * D * eb."""
     D, Hkv, B, Hq = spec.head_dim, spec.num_kv_heads, spec.num_seqs, spec.num_q_heads
     k = spec.topk_blocks
+    s_sparse, s_dense = f["s_sparse"], f["s_dense"]
     unit = 2 * spec.block_size * D + 8
     keff = sum(min(k, spec.blocks(b)) for b in range(B))
     part = lambda S: B * Hq * S * (D + 2) * 4
@@ -620,6 +637,7 @@ def fp8_record(spec, f: dict, s_sparse: int, s_dense: int) -> dict:
         + spec.used_pages * 8
     dense_gbps = dense_b / (f["dense_attn_us"] * 1e-6) / 1e9
     return {
+        "splits": {"sparse": s_sparse, "dense": s_dense},
         "format": "OCP FP8 E4M3, one fp32 scale per (page, KV head) and tensor",
         "quantize": {"us": f["quantize_us"], "bytes": quant_b,
                      "gbps": quant_b / (f["quantize_us"] * 1e-6) / 1e9},
@@ -689,7 +707,7 @@ def main():
         args.no_variants = False
         g = run_gpu(args, spec, data)
         print(json.dumps({"selection_variants": variants_record(spec, g["variants"]),
-                          "fp8_pages": fp8_record(spec, g["fp8"], g["s_sparse"], g["s_dense"])}),
+                          "fp8_pages": fp8_record(spec, g["fp8"])}),
               flush=True)
         return
     log("[bench] timing GPU steps")
@@ -771,7 +789,7 @@ def main():
             "timing": f"{args.steps} back-to-back launches between two HIP events",
         },
         "selection_variants": variants_record(spec, g["variants"]) if g["variants"] else None,
-        "fp8_pages": fp8_record(spec, g["fp8"], g["s_sparse"], g["s_dense"]) if g.get("fp8") else None,
+        "fp8_pages": fp8_record(spec, g["fp8"]) if g.get("fp8") else None,
         "other_workloads": others,
         "zero_copy": zc,
         "cpu_baseline": cpu,

@@ -217,12 +217,16 @@ kv_status kv_block_select(const kv_shape* shape, int32_t index_kind, const void*
                           void* workspace, size_t workspace_bytes, void* stream);
 
 /*
- * Number of splits the library would pick for `blocks_per_unit` blocks per
- * (sequence, KV head) (maxN for dense calls, the selection length for sparse
- * ones): about 8 waves per compute unit, at least 2 blocks per split (8 with
- * KV_FLAG_HOST_KV).  Always >= 1.
+ * Number of splits the library would pick for kv_paged_decode_attn (and the
+ * cached attention) with `blocks_per_unit` blocks per (sequence, KV head)
+ * (maxN for dense calls, the list length for sparse ones): about 6 waves per
+ * compute unit on the matrix-core path (16-bit, G >= 2), 4 on the vector path,
+ * at least 2 blocks per split (8 with KV_FLAG_HOST_KV).  Always >= 1.
  */
 int32_t kv_auto_num_splits(const kv_shape* shape, int32_t blocks_per_unit);
+
+/* The same for kv_paged_decode_attn_fp8: about 8 waves per compute unit. */
+int32_t kv_auto_num_splits_fp8(const kv_shape* shape, int32_t blocks_per_unit);
 
 /*
  * Split-K decode attention (Dual-Blade background: a decode step attends over

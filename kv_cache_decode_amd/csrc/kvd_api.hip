@@ -11,10 +11,19 @@
 #include "../../include/kvdecode.h"
 #include "kvd_launch.hpp"
 
-// Split heuristic knobs (build macros): target waves per compute unit and the
-// fewest pages a split should own.
+// Split heuristic knobs (build macros): target waves per compute unit of each
+// attention path (measured on the 128k and 32k GQA and the OPT MHA workloads:
+// the bf16 MFMA kernel is fastest at 6, the FP8 code path at 8, the VALU
+// kernel at 4; odd targets leave the 2-wave workgroups unevenly spread over the
+// compute units), and the fewest pages a split should own.
 #ifndef KVD_SPLIT_WAVES_PER_CU
-#define KVD_SPLIT_WAVES_PER_CU 8
+#define KVD_SPLIT_WAVES_PER_CU 6
+#endif
+#ifndef KVD_SPLIT_WAVES_PER_CU_FP8
+#define KVD_SPLIT_WAVES_PER_CU_FP8 8
+#endif
+#ifndef KVD_SPLIT_WAVES_PER_CU_VALU
+#define KVD_SPLIT_WAVES_PER_CU_VALU 4
 #endif
 #ifndef KVD_SPLIT_MIN_BLOCKS
 #define KVD_SPLIT_MIN_BLOCKS 2
@@ -270,17 +279,36 @@ kv_status kv_block_score_topk(const kv_shape* shape, const void* q, const void* 
                          0, scores_out, sel_blocks, sel_count, workspace, workspace_bytes, stream);
 }
 
-int32_t kv_auto_num_splits(const kv_shape* shape, int32_t blocks_per_unit) {
+}  // extern "C"
+
+namespace {
+int32_t auto_splits(const kv_shape* shape, int32_t blocks_per_unit, long waves_per_cu) {
   if (check_shape(shape) != KV_OK || blocks_per_unit < 1) return 1;
   const long units = (long)shape->num_seqs * shape->num_kv_heads;
-  // about KVD_SPLIT_WAVES_PER_CU waves per compute unit, each over at least
-  // KVD_SPLIT_MIN_BLOCKS pages
-  const long target_waves = (long)kvd::device_cu_count() * KVD_SPLIT_WAVES_PER_CU;
+  const long target_waves = (long)kvd::device_cu_count() * waves_per_cu;
   long s = (target_waves + units - 1) / units;
   // pages read over the host link favour fewer, longer splits
   const long min_blocks = (shape->flags & KV_FLAG_HOST_KV) ? 8 : KVD_SPLIT_MIN_BLOCKS;
   s = std::min<long>(s, (blocks_per_unit + min_blocks - 1) / min_blocks);
   return (int32_t)std::max<long>(1, std::min<long>(s, 65535L * 4));
+}
+
+bool mfma_path(const kv_shape* s) {
+  return s->dtype != KV_F32 && s->num_q_heads / std::max(1, s->num_kv_heads) >= 2;
+}
+}  // namespace
+
+extern "C" {
+
+int32_t kv_auto_num_splits(const kv_shape* shape, int32_t blocks_per_unit) {
+  if (!shape) return 1;
+  return auto_splits(shape, blocks_per_unit,
+                     mfma_path(shape) ? KVD_SPLIT_WAVES_PER_CU : KVD_SPLIT_WAVES_PER_CU_VALU);
+}
+
+int32_t kv_auto_num_splits_fp8(const kv_shape* shape, int32_t blocks_per_unit) {
+  if (!shape) return 1;
+  return auto_splits(shape, blocks_per_unit, KVD_SPLIT_WAVES_PER_CU_FP8);
 }
 
 kv_status kv_paged_decode_attn(const kv_shape* shape, const void* q, const void* k_cache,

@@ -28,7 +28,7 @@ DTYPE_CODES = {"f32": KV_F32, "f16": KV_F16, "bf16": KV_BF16}
 EXPORTS = (
     "kv_block_meta_build", "kv_block_mean_build", "kv_append_token",
     "kv_score_topk_workspace_size", "kv_block_score_topk", "kv_max_forced_blocks",
-    "kv_block_select", "kv_auto_num_splits", "kv_paged_decode_attn", "kv_decode_combine",
+    "kv_block_select", "kv_auto_num_splits", "kv_auto_num_splits_fp8", "kv_paged_decode_attn", "kv_decode_combine",
     "kv_quantize_pages_fp8", "kv_paged_decode_attn_fp8", "kv_cache_plan", "kv_cache_fetch",
     "kv_cached_decode_attn", "kv_cache_slot_mass", "kv_host_alloc", "kv_host_free",
     "kv_status_string", "kv_last_error_message",
@@ -86,6 +86,7 @@ def _load() -> ctypes.CDLL:
         "kv_score_topk_workspace_size": (SZ, [S, I32]),
         "kv_block_score_topk": (I32, [S, P, P, P, P, I32, P, P, P, P, SZ, P]),
         "kv_auto_num_splits": (I32, [S, I32]),
+        "kv_auto_num_splits_fp8": (I32, [S, I32]),
         "kv_paged_decode_attn": (I32, [S, P, P, P, P, P, P, P, I32, F, I32, P, P, P, P]),
         "kv_decode_combine": (I32, [S, I32, P, P, P, P, P, P]),
         "kv_quantize_pages_fp8": (I32, [S, P, P, P, P, I32, P, P, P, P]),
@@ -174,6 +175,10 @@ def kv_block_score_topk(shape: KVShape, q: Buf, kmeta: Buf, block_table: Buf, se
                                     _p(seq_lens), topk_blocks, _p(scores_out), _p(sel_blocks),
                                     _p(sel_count), _p(workspace), workspace_bytes,
                                     _stream(stream)))
+
+
+def kv_auto_num_splits_fp8(shape: KVShape, blocks_per_unit: int) -> int:
+    return int(_lib.kv_auto_num_splits_fp8(ctypes.byref(shape), blocks_per_unit))
 
 
 def kv_max_forced_blocks(shape: KVShape, sink_tokens: int, local_tokens: int) -> int:

@@ -207,7 +207,8 @@ class DeviceWorkload:
             self.k8_dev, self.v8_dev = k8, v8
 
     def attention_fp8(self, sparse: bool, num_splits: Optional[int] = None, stream=None):
-        S = num_splits or self.auto_splits(sparse)
+        S = num_splits or kd.kv_auto_num_splits_fp8(self.shape,
+                                                    self.topk if sparse else self.spec.max_blocks)
         po, pm, pl = self.partials(S)
         sel, cnt, stride = (self.sel, self.sel_count, self.topk) if sparse else (None, None, 0)
         kd.kv_paged_decode_attn_fp8(self.shape, self.q, self.k8, self.v8, self.kv_scales,
