@@ -22,6 +22,9 @@
 #ifndef KVD_META_WGS_PER_CU
 #define KVD_META_WGS_PER_CU 16
 #endif
+#ifndef KVD_META_WAVES
+#define KVD_META_WAVES 4
+#endif
 #ifndef KVD_SCORE_STEPS
 #define KVD_SCORE_STEPS 8
 #endif
@@ -379,27 +382,33 @@ __device__ inline uint32_t block_exclusive_scan(uint32_t v, uint32_t* buf) {
   return before + inc - v;
 }
 
-template <int EPT>
-__global__ __launch_bounds__(1024) void topk_kernel(const float* __restrict__ scores,
-                                                    const int32_t* __restrict__ seq_lens,
-                                                    int Hkv, int maxN, int K, int sink,
-                                                    int local, int32_t* __restrict__ sel,
-                                                    int32_t* __restrict__ sel_count) {
-  constexpr int NW = 1024 / kWave;
-  __shared__ __align__(16) uint32_t hist[NW][256];
-  __shared__ uint32_t buf_a[NW], buf_b[NW], buf_c[NW], buf_d[NW];
-  __shared__ uint32_t state[2];
-  const int j = blockIdx.x, b = blockIdx.y;
+// Top-K of one row by the NT threads of a workgroup (all of them call it);
+// EPT keys per thread, NT * EPT >= maxN.
+template <int NT>
+struct TopkSmem {
+  alignas(16) uint32_t hist[NT / kWave][256];
+  uint32_t buf_a[NT / kWave], buf_b[NT / kWave], buf_c[NT / kWave], buf_d[NT / kWave];
+  uint32_t state[2];
+};
+
+template <int NT, int EPT>
+__device__ inline void topk_row(const float* __restrict__ row, int maxN, int L, int K, int sink,
+                                int local, int32_t* __restrict__ out,
+                                int32_t* __restrict__ count_out, TopkSmem<NT>& sm) {
+  constexpr int NW = NT / kWave;
+  auto& hist = sm.hist;
+  auto& buf_a = sm.buf_a;
+  auto& buf_b = sm.buf_b;
+  auto& buf_c = sm.buf_c;
+  auto& buf_d = sm.buf_d;
+  auto& state = sm.state;
   const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid >> 6;
-  const int L = seq_lens[b];
   const int nb = (L + kBlockSize - 1) / kBlockSize;
   const int keff = min(K, nb);
   const int local_from = local > 0 ? L - local : 0x7fffffff;  // first forced local token
-  int32_t* out = sel + ((size_t)b * Hkv + j) * K;
-  if (tid == 0) sel_count[(size_t)b * Hkv + j] = max(keff, 0);
-  for (int i = max(keff, 0) + tid; i < K; i += 1024) out[i] = -1;
+  if (tid == 0) *count_out = max(keff, 0);
+  for (int i = max(keff, 0) + tid; i < K; i += NT) out[i] = -1;
   if (keff <= 0) return;  // workgroup-uniform
-  const float* row = scores + ((size_t)b * Hkv + j) * maxN;
 
   uint32_t key[EPT];
   uint32_t kmn = 0xFFFFFFFFu, kmx = 0u;
@@ -523,6 +532,19 @@ __global__ __launch_bounds__(1024) void topk_kernel(const float* __restrict__ sc
   }
 }
 
+template <int EPT>
+__global__ __launch_bounds__(1024) void topk_kernel(const float* __restrict__ scores,
+                                                    const int32_t* __restrict__ seq_lens,
+                                                    int Hkv, int maxN, int K, int sink,
+                                                    int local, int32_t* __restrict__ sel,
+                                                    int32_t* __restrict__ sel_count) {
+  __shared__ TopkSmem<1024> sm;
+  const int j = blockIdx.x, b = blockIdx.y;
+  const size_t u = (size_t)b * Hkv + j;
+  topk_row<1024, EPT>(scores + u * maxN, maxN, seq_lens[b], K, sink, local, sel + u * K,
+                      sel_count + u, sm);
+}
+
 // ============================================================== launchers
 
 
@@ -534,7 +556,7 @@ hipError_t launch_block_meta(int dtype, int D, const void* k_cache, const int32_
     return with_dim(D, [&](auto d) {
       using DT = decltype(dt);
       constexpr int DD = decltype(d)::value;
-      constexpr int WAVES = 4;
+      constexpr int WAVES = KVD_META_WAVES;
       constexpr int UPS = kWave / RowGeom<DT, DD>::LPR;
       const long steps = ((long)n_ids * Hkv + UPS - 1) / UPS;
       const long want = (steps + WAVES - 1) / WAVES;
@@ -554,7 +576,7 @@ hipError_t launch_block_mean(int dtype, int D, const void* k_cache, const int32_
     return with_dim(D, [&](auto d) {
       using DT = decltype(dt);
       constexpr int DD = decltype(d)::value;
-      constexpr int WAVES = 4;
+      constexpr int WAVES = KVD_META_WAVES;
       constexpr int UPS = kWave / RowGeom<DT, DD>::LPR;
       const long steps = ((long)n_ids * Hkv + UPS - 1) / UPS;
       const long want = (steps + WAVES - 1) / WAVES;

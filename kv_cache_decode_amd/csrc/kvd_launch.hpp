@@ -88,4 +88,5 @@ inline int device_cu_count() { return cu_count(); }
 // Largest maxN the Top-K kernel keeps in registers (1024 threads x 32 keys).
 constexpr int kTopkMaxBlocks = 32768;
 
+
 }  // namespace kvd
