@@ -17,6 +17,10 @@ Also in the same run: the zero-copy variant (K/V pools in mapped pinned host
 memory; its roofline is the measured host-to-device copy bandwidth), and the
 fp64 oracle timed on the host cores on the same workload (cpu_baseline).
 
+The dominant kernel is also reported against two read ceilings measured in the
+same run by kernels that compute nothing: a plain stream read of 1 GiB, and
+the dense attention's own gather of K/V tiles (roofline.read_ceilings).
+
 Beside the step, kernel-level timings of the selection variants: the mean-key
 index (build and select) and either index with the first 4 / last 64 tokens
 forced in (selection_variants).
@@ -42,6 +46,9 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBPS = 8000.0
 GRAPH_STEPS = 8          # decode steps captured per HIP graph (cycling over the copies)
+GRAPH_MIN_REPLAYS = 25   # decode-step figures: median over >= 25 x 8 = 200 timed steps
+GRAPH_WARM_REPLAYS = 3   # ... after >= 24 untimed ones
+STREAM_PROBE_BYTES = 1 << 30
 WORKLOAD = "llama3.1_8b_gqa_b1_128k_bf16"
 HOSTKV_WORKLOAD = "llama3.1_8b_gqa_b1_128k_bf16_hostkv"
 # measured beside the headline step at kernel level (not part of `value`)
@@ -175,10 +182,11 @@ def run_gpu(args, spec, data):
         return t0.elapsed_time(t1), time.perf_counter() - wall0
 
     def graph_us(fn):
-        """Average time per step of fn, replayed from one HIP graph that holds
+        """Time per step of fn, replayed from one HIP graph that holds
         GRAPH_STEPS steps cycling over the workload copies (one host launch per
         GRAPH_STEPS steps, so a short step is not timed at the host's graph
-        launch rate)."""
+        launch rate): the median over at least GRAPH_MIN_REPLAYS replays, each
+        bracketed by its own events."""
         try:
             side = torch.cuda.Stream()
             side.wait_stream(torch.cuda.current_stream())
@@ -190,18 +198,19 @@ def run_gpu(args, spec, data):
             with torch.cuda.graph(g_):
                 for i in range(GRAPH_STEPS):
                     fn(copies[i % len(copies)])
-            reps = max(1, args.steps // GRAPH_STEPS)
-            for _ in range(max(1, args.warmup // GRAPH_STEPS)):
+            reps = max(GRAPH_MIN_REPLAYS, args.steps // GRAPH_STEPS)
+            for _ in range(max(GRAPH_WARM_REPLAYS, args.warmup // GRAPH_STEPS)):
                 g_.replay()
-            t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                  for _ in range(reps)]
             torch.cuda.synchronize()
-            t0.record()
-            for _ in range(reps):
+            for a, b in ev:
+                a.record()
                 g_.replay()
-            t1.record()
+                b.record()
             torch.cuda.synchronize()
             del g_
-            return t0.elapsed_time(t1) * 1e3 / (reps * GRAPH_STEPS)
+            return float(np.median([a.elapsed_time(b) for a, b in ev])) * 1e3 / GRAPH_STEPS
         except RuntimeError:
             ms_, _ = time_loop(lambda i: fn(copies[i % len(copies)]))
             return ms_ * 1e3 / args.steps
@@ -229,6 +238,8 @@ def run_gpu(args, spec, data):
         # copies, so per-launch event overhead does not enter its average
         dense_loop_ms, _ = time_loop(
             lambda i: copies[i % len(copies)].attention(sparse=False, num_splits=s_dense))
+
+        ceilings = time_read_ceilings(copies, s_dense, time_loop, args.steps)
 
         # whole-step timing, one HIP graph per workload copy
         launch = "hip_graph"
@@ -271,6 +282,7 @@ def run_gpu(args, spec, data):
             "total_ms": total_ms, "wall_s": wall, "stage_ms": per_stage_ms,
             "decode_us": decode_us, "launch": launch,
             "dense_attn_loop_us": dense_loop_ms * 1e3 / args.steps,
+            "ceilings": ceilings,
             "eager_ms_per_step": eager_ms / args.steps,
         })
 
@@ -288,6 +300,44 @@ def run_gpu(args, spec, data):
     res["variants"] = variants
     res["fp8"] = fp8
     return res
+
+
+def time_read_ceilings(copies, s_dense, time_loop, steps):
+    """What the memory system delivers to kernels that compute nothing, on this
+    GPU in this run: a plain front-to-back stream read (two 1 GiB buffers
+    alternated, together beyond the last-level cache), and the dense decode
+    attention's own gather of K/V tiles (same pages, order, splits, lane layout
+    and prefetch depth, rotated over the same workload copies)."""
+    import torch
+    from kv_cache_decode_amd import kvdecode as kd
+
+    dev = copies[0].device
+    n = STREAM_PROBE_BYTES
+    bufs = [torch.empty(n, dtype=torch.uint8, device=dev) for _ in range(2)]
+    for b_ in bufs:
+        b_.fill_(5)
+    sink = torch.empty(kd.PROBE_SINK_WORDS, dtype=torch.int32, device=dev)
+    for i in range(4):
+        kd.kv_probe_stream_read(bufs[i % 2], n, sink)
+    stream_ms, _ = time_loop(lambda i: kd.kv_probe_stream_read(bufs[i % 2], n, sink))
+    stream_us = stream_ms * 1e3 / steps
+    del bufs
+    spec = copies[0].spec
+    B, Hkv = spec.num_seqs, spec.num_kv_heads
+    gsink = torch.empty(B * Hkv * s_dense, dtype=torch.int32, device=dev)
+
+    def gather(c):
+        kd.kv_probe_gather_read(c.shape, c.k_cache, c.v_cache, c.block_table, c.seq_lens,
+                                s_dense, gsink)
+    for c in copies:
+        gather(c)
+    gather_ms, _ = time_loop(lambda i: gather(copies[i % len(copies)]))
+    gather_us = gather_ms * 1e3 / steps
+    kv_bytes = spec.used_pages * Hkv * 2 * spec.block_size * spec.head_dim * spec.elem_bytes
+    torch.cuda.empty_cache()
+    return {"stream_read": {"bytes": n, "us": stream_us, "gbps": n / (stream_us * 1e-6) / 1e9},
+            "dense_gather_read": {"bytes": kv_bytes, "us": gather_us, "splits": s_dense,
+                                  "gbps": kv_bytes / (gather_us * 1e-6) / 1e9}}
 
 
 def time_fp8(args, copies, k, s_sparse, s_dense, time_loop, graph_us):
@@ -385,16 +435,17 @@ def run_other_workload(args, name):
 
     s_dense = kd.kv_auto_num_splits(copies[0].shape, spec.max_blocks)
     dense_us = loop(lambda c: c.attention(sparse=False, num_splits=s_dense))
-    sb = stage_bytes(spec, spec.topk_blocks or 1, 1, s_dense)
-    res = {"dense_attn_us": dense_us, "dense_attn_gbps": sb["dense_attn"] / (dense_us * 1e-6) / 1e9,
-           "dense_frac_of_hbm_peak": sb["dense_attn"] / (dense_us * 1e-6) / 1e9 / HBM_PEAK_GBPS,
+    k = spec.topk_blocks
+    s_sp = kd.kv_auto_num_splits(copies[0].shape, k) if k else 1
+    sb = stage_bytes(spec, k or 1, s_sp, s_dense)
+    gbps = lambda name, us: sb[name] / (us * 1e-6) / 1e9
+    res = {"dense_attn_us": dense_us, "dense_attn_gbps": gbps("dense_attn", dense_us),
+           "dense_frac_of_hbm_peak": gbps("dense_attn", dense_us) / HBM_PEAK_GBPS,
            "splits_dense": s_dense, "dtype": spec.dtype, "group": spec.group}
-    if spec.topk_blocks:
-        k = spec.topk_blocks
+    if k:
         for c in copies:
             c.meta_build()
             c.score_topk(k)
-        s_sp = kd.kv_auto_num_splits(copies[0].shape, k)
         res["meta_build_us"] = loop(lambda c: c.meta_build())
         res["score_topk_us"] = loop(lambda c: c.score_topk(k))
         res["sparse_attn_us"] = loop(lambda c: c.attention(sparse=True, num_splits=s_sp))
@@ -402,6 +453,9 @@ def run_other_workload(args, name):
                                                                            num_splits=s_sp)))
         res["sparse_decode_steps_per_s"] = 1e6 / res["sparse_decode_us"]
         res["splits_sparse"] = s_sp
+        res["stage_gbps"] = {name: gbps(name, res[f"{name}_us"])
+                             for name in ("meta_build", "score_topk", "sparse_attn")}
+        res["stage_gbps"]["dense_attn"] = res["dense_attn_gbps"]
     for c in copies:
         c.close()
     del copies
@@ -461,7 +515,8 @@ def run_zero_copy(args):
             fp8_ms.append(e[0].elapsed_time(e[1]))
     dw.close()
 
-    # measured host-to-device copy bandwidth: 256 MiB from pinned memory, best of 10
+    # measured host-to-device copy bandwidth: 256 MiB from pinned memory, best of 10,
+    # and a stream-read kernel over 256 MiB of mapped pinned memory, best of 10
     n = 256 << 20
     src = torch.empty(n, dtype=torch.uint8, pin_memory=True)
     src.fill_(1)
@@ -474,6 +529,24 @@ def run_zero_copy(args):
         torch.cuda.synchronize()
         best = min(best, e[0].elapsed_time(e[1]))
     h2d_gbps = n / (best * 1e-3) / 1e9
+    del src, dst
+    # the same bytes read by a kernel straight from mapped pinned memory
+    from kv_cache_decode_amd import kvdecode as kd
+    hp, dp = kd.kv_host_alloc(n)
+    try:
+        sink = torch.empty(kd.PROBE_SINK_WORDS, dtype=torch.int32, device=dev)
+        kd.kv_probe_stream_read(dp, n, sink)
+        rd = []
+        for _ in range(10):
+            e[0].record()
+            kd.kv_probe_stream_read(dp, n, sink)
+            e[1].record()
+            torch.cuda.synchronize()
+            rd.append(e[0].elapsed_time(e[1]))
+    finally:
+        torch.cuda.synchronize()
+        kd.kv_host_free(hp)
+    host_read_gbps = n / (min(rd) * 1e-3) / 1e9
 
     eb = spec.elem_bytes
     keff = sum(min(k, spec.blocks(b)) for b in range(spec.num_seqs))
@@ -501,6 +574,8 @@ def run_zero_copy(args):
         "dense_host_link_gbps": dense_link_bytes / (dense_ms * 1e-3) / 1e9,
         "h2d_memcpy_gbps": h2d_gbps,
         "frac_of_h2d": host_gbps / h2d_gbps,
+        "kernel_host_read_gbps": host_read_gbps,
+        "frac_of_kernel_host_read": host_gbps / host_read_gbps,
         "splits": S,
     }
 
@@ -570,7 +645,22 @@ def time_cache_trajectory(args, dw, data, k, S):
 
 # ---------------------------------------------------------------- CPU baseline (oracle)
 
-def run_cpu_baseline(spec, data, step_bytes: int, reps: int):
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def run_cpu_baseline(spec, data, step_bytes: int, min_reps: int, budget_s: float):
+    """The fp64 oracle on the host cores: whole steps of the timed workload
+    (meta build, Quest scores, Top-K, sparse and dense attention), at least
+    min_reps of them and more until about budget_s seconds have been spent;
+    each stage timed on its own within the step, medians reported."""
     import oracle
 
     q, kp, vp = data.q64(), data.k64(), data.v64()
@@ -583,26 +673,41 @@ def run_cpu_baseline(spec, data, step_bytes: int, reps: int):
             val.append(min(bs, spec.seq_lens[b] - n * bs))
     ids, val = np.array(ids, np.int32), np.array(val, np.int32)
     scale = 1.0 / np.sqrt(spec.head_dim)
-    times = []
-    for _ in range(reps):
+    stages = {"meta_build": [], "score_topk": [], "sparse_attn": [], "dense_attn": []}
+    steps = []
+    start = time.perf_counter()
+    while len(steps) < min_reps or (time.perf_counter() - start < budget_s and len(steps) < 200):
         t0 = time.perf_counter()
         km = oracle.block_meta(kp, ids, val)
+        t1 = time.perf_counter()
         hs = oracle.head_scores(q, km, bt, sl, bs)
         gs = oracle.group_scores(hs, spec.num_kv_heads)
         sel, cnt = oracle.topk(gs, sl, bs, k)
+        t2 = time.perf_counter()
         oracle.attention(q, kp, vp, bt, sl, scale, sel, cnt)
+        t3 = time.perf_counter()
         oracle.attention(q, kp, vp, bt, sl, scale)
-        times.append(time.perf_counter() - t0)
-    t = float(np.median(times))
+        t4 = time.perf_counter()
+        for name, dt in zip(stages, (t1 - t0, t2 - t1, t3 - t2, t4 - t3)):
+            stages[name].append(dt)
+        steps.append(t4 - t0)
+    t = float(np.median(steps))
+    sb = stage_bytes(spec, k, 1, 1)
+    stage_s = {name: float(np.median(v)) for name, v in stages.items()}
     return {
         "value": step_bytes / t / 1e9,
         "unit": "GB/s",
         "cores": oracle.num_threads(),
         "kind": "oracle",
-        "sample": f"{reps} full steps of {spec.name} (meta build, scores, Top-K, sparse and "
-                  f"dense attention) in fp64; median step {t:.2f} s",
+        "sample": f"{len(steps)} full steps of {spec.name} (meta build, scores, Top-K, sparse "
+                  f"and dense attention; the append is not part of the oracle step) in fp64, "
+                  f"{sum(steps):.1f} s in all; median step {t:.3f} s",
         "step_s": t,
         "steps_per_s": 1.0 / t,
+        "stage_s": stage_s,
+        "stage_gbps": {name: sb[name] / v / 1e9 for name, v in stage_s.items()},
+        "host": {"cpu_model": cpu_model(), "logical_cpus": os.cpu_count(),
+                 "affinity": len(os.sched_getaffinity(0))},
     }
 
 
@@ -669,7 +774,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--copies", type=int, default=4)
     ap.add_argument("--zc-reps", type=int, default=5)
-    ap.add_argument("--cpu-reps", type=int, default=3)
+    ap.add_argument("--cpu-reps", type=int, default=5, help="fewest oracle steps timed")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0,
+                    help="oracle steps are added until about this much host time is spent")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-zero-copy", action="store_true")
     ap.add_argument("--no-other-workloads", action="store_true")
@@ -735,7 +842,7 @@ def main():
     cpu = None
     if not args.no_cpu_baseline:
         log("[bench] CPU baseline (oracle)")
-        cpu = run_cpu_baseline(spec, data, step_bytes, args.cpu_reps)
+        cpu = run_cpu_baseline(spec, data, step_bytes, args.cpu_reps, args.cpu_seconds)
 
     rec = {
         "metric": "KV GB/s streamed by decode attention (% of HBM peak) + decode steps/sec",
@@ -767,6 +874,8 @@ def main():
                                "dense": 1e6 / g["decode_us"]["dense"],
                                "full_step": 1e3 / ms},
         "decode_step_us": g["decode_us"],
+        "decode_step_timing": f"median per step over >= {GRAPH_MIN_REPLAYS} replays of a "
+                              f"{GRAPH_STEPS}-step HIP graph, each between its own events",
         "decode_step_gbps": {
             "sparse": (sb["append"] + sb["score_topk"] + sb["sparse_attn"] + sb["sparse_combine"])
                       / (g["decode_us"]["sparse"] * 1e-6) / 1e9,
@@ -787,6 +896,10 @@ def main():
             "algorithmic_bytes_per_launch": sb["dense_attn"],
             "avg_launch_us": dense_us,
             "timing": f"{args.steps} back-to-back launches between two HIP events",
+            # measured in the same run by kernels that read and compute nothing
+            "read_ceilings": g["ceilings"],
+            "frac_of_stream_read": dense_gbps / g["ceilings"]["stream_read"]["gbps"],
+            "frac_of_gather_read": g["ceilings"]["dense_gather_read"]["us"] / dense_us,
         },
         "selection_variants": variants_record(spec, g["variants"]) if g["variants"] else None,
         "fp8_pages": fp8_record(spec, g["fp8"]) if g.get("fp8") else None,

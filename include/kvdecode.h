@@ -371,6 +371,23 @@ kv_status kv_cache_slot_mass(const kv_shape* shape, int32_t num_slots, const flo
                              void* stream);
 
 /*
+ * Read-ceiling probes, for measurement: they read bytes as the path does and
+ * compute nothing, so the path's kernels can be reported against what the
+ * memory system delivers for the same access pattern on the same GPU.
+ * kv_probe_stream_read reads `bytes` (a positive multiple of 16) of `buf`
+ * front to back with 16-byte non-temporal loads; buf may be device memory or
+ * a kv_host_alloc device pointer (the kernel-side host-read rate).  sink:
+ * 4096 uint32 words.  kv_probe_gather_read performs exactly the loads of
+ * dense kv_paged_decode_attn with `num_splits` splits on 16-bit pools (the
+ * matrix-core kernel's lane layout, one page ahead); sink: B * Hkv * num_splits
+ * words.
+ */
+kv_status kv_probe_stream_read(const void* buf, size_t bytes, uint32_t* sink, void* stream);
+kv_status kv_probe_gather_read(const kv_shape* shape, const void* k_cache, const void* v_cache,
+                               const int32_t* block_table, const int32_t* seq_lens,
+                               int32_t num_splits, uint32_t* sink, void* stream);
+
+/*
  * Pinned, device-mapped host memory for a zero-copy K/V pool (DirectKV review,
  * core method 4: KV kept in pinned host memory behind a device-visible pointer).
  * *host_ptr is the CPU address, *dev_ptr the address to pass to the kernels.

@@ -494,6 +494,36 @@ kv_status kv_cache_slot_mass(const kv_shape* shape, int32_t num_slots, const flo
                     "kv_cache_slot_mass launch");
 }
 
+kv_status kv_probe_stream_read(const void* buf, size_t bytes, uint32_t* sink, void* stream) {
+  if (!buf || !sink) return fail(KV_ERR_INVALID_ARG, "buf and sink are required");
+  if (bytes == 0 || bytes % 16) return fail(KV_ERR_INVALID_ARG, "bytes must be a positive multiple of 16");
+  if (!aligned(buf, 16) || !aligned(sink, 4))
+    return fail(KV_ERR_ALIGNMENT, "buf must be 16-byte aligned, sink 4-byte aligned");
+  return hip_status(kvd::launch_stream_read(buf, bytes, sink, kvd::kProbeSinkWords,
+                                            (hipStream_t)stream),
+                    "kv_probe_stream_read launch");
+}
+
+kv_status kv_probe_gather_read(const kv_shape* shape, const void* k_cache, const void* v_cache,
+                               const int32_t* block_table, const int32_t* seq_lens,
+                               int32_t num_splits, uint32_t* sink, void* stream) {
+  kv_status st = check_shape(shape);
+  if (st != KV_OK) return st;
+  if (shape->dtype == KV_F32) return fail(KV_ERR_UNSUPPORTED, "the gather probe models 16-bit pools");
+  if (num_splits < 1 || num_splits > 65535 * 2)
+    return fail(KV_ERR_INVALID_ARG, "num_splits=%d out of range", num_splits);
+  if (!k_cache || !v_cache || !block_table || !seq_lens || !sink)
+    return fail(KV_ERR_INVALID_ARG, "every array of kv_probe_gather_read is required");
+  if (!aligned(k_cache, 16) || !aligned(v_cache, 16) || !aligned(block_table, 4) ||
+      !aligned(seq_lens, 4) || !aligned(sink, 4))
+    return fail(KV_ERR_ALIGNMENT, "pools 16-byte aligned, integer arrays 4-byte aligned");
+  return hip_status(kvd::launch_gather_read(shape->dtype, shape->head_dim, k_cache, v_cache,
+                                            block_table, seq_lens, shape->num_seqs,
+                                            shape->num_kv_heads, shape->max_blocks_per_seq,
+                                            num_splits, sink, (hipStream_t)stream),
+                    "kv_probe_gather_read launch");
+}
+
 kv_status kv_host_alloc(size_t bytes, uint32_t flags, void** host_ptr, void** dev_ptr) {
   if (!host_ptr || !dev_ptr) return fail(KV_ERR_INVALID_ARG, "host_ptr and dev_ptr are required");
   *host_ptr = nullptr;

@@ -59,6 +59,16 @@ hipError_t launch_slot_mass(const float* block_lse, const float* lse, const int3
                             const int32_t* sel_slots, int sel_stride, int B, int Hq, int Hkv,
                             int C, float* slot_mass, hipStream_t stream);
 
+hipError_t launch_stream_read(const void* buf, size_t bytes, uint32_t* sink, int sink_words,
+                              hipStream_t stream);
+
+hipError_t launch_gather_read(int dtype, int D, const void* k_cache, const void* v_cache,
+                              const int32_t* block_table, const int32_t* seq_lens, int B, int Hkv,
+                              int maxN, int S, uint32_t* sink, hipStream_t stream);
+
+// Words of the stream-read probe's sink (one per workgroup).
+constexpr int kProbeSinkWords = 4096;
+
 // Largest cache (slots per sequence and KV head) the plan kernel holds.
 constexpr int kCacheMaxSlots = 8192;
 

@@ -30,7 +30,8 @@ EXPORTS = (
     "kv_score_topk_workspace_size", "kv_block_score_topk", "kv_max_forced_blocks",
     "kv_block_select", "kv_auto_num_splits", "kv_auto_num_splits_fp8", "kv_paged_decode_attn", "kv_decode_combine",
     "kv_quantize_pages_fp8", "kv_paged_decode_attn_fp8", "kv_cache_plan", "kv_cache_fetch",
-    "kv_cached_decode_attn", "kv_cache_slot_mass", "kv_host_alloc", "kv_host_free",
+    "kv_cached_decode_attn", "kv_cache_slot_mass", "kv_probe_stream_read",
+    "kv_probe_gather_read", "kv_host_alloc", "kv_host_free",
     "kv_status_string", "kv_last_error_message",
 )
 
@@ -95,6 +96,8 @@ def _load() -> ctypes.CDLL:
         "kv_cache_fetch": (I32, [S, I32, P, P, P, P, P, P, I32, P, P, P]),
         "kv_cached_decode_attn": (I32, [S, I32, P, P, P, P, P, P, P, I32, F, I32, P, P, P, P, P]),
         "kv_cache_slot_mass": (I32, [S, I32, P, P, P, P, I32, P, P]),
+        "kv_probe_stream_read": (I32, [P, SZ, P, P]),
+        "kv_probe_gather_read": (I32, [S, P, P, P, P, I32, P, P]),
         "kv_host_alloc": (I32, [SZ, U32, ctypes.POINTER(P), ctypes.POINTER(P)]),
         "kv_host_free": (I32, [P]),
         "kv_status_string": (ctypes.c_char_p, [I32]),
@@ -267,6 +270,20 @@ def kv_cache_slot_mass(shape: KVShape, num_slots: int, block_lse: Buf, lse: Buf,
     _check(_lib.kv_cache_slot_mass(ctypes.byref(shape), num_slots, _p(block_lse), _p(lse),
                                    _p(sel_count), _p(sel_slots), sel_stride, _p(slot_mass),
                                    _stream(stream)))
+
+
+PROBE_SINK_WORDS = 4096
+
+
+def kv_probe_stream_read(buf: Buf, nbytes: int, sink: Buf, stream=None) -> None:
+    _check(_lib.kv_probe_stream_read(_p(buf), nbytes, _p(sink), _stream(stream)))
+
+
+def kv_probe_gather_read(shape: KVShape, k_cache: Buf, v_cache: Buf, block_table: Buf,
+                         seq_lens: Buf, num_splits: int, sink: Buf, stream=None) -> None:
+    _check(_lib.kv_probe_gather_read(ctypes.byref(shape), _p(k_cache), _p(v_cache),
+                                     _p(block_table), _p(seq_lens), num_splits, _p(sink),
+                                     _stream(stream)))
 
 
 def kv_host_alloc(nbytes: int, flags: int = KV_HOST_COHERENT):

@@ -304,3 +304,20 @@ def test_cache_argument_checks():
     m = kd.kv_cache_slot_mass
     expect(kd.KV_ERR_INVALID_ARG, lambda stream: m(s, 16, A16, None, A16, A16, 8, A16, stream=stream))
     expect(kd.KV_ERR_ALIGNMENT, lambda stream: m(s, 16, A16, A16, A16, A16, 8, ODD, stream=stream))
+
+
+def test_probe_argument_checks():
+    sr = kd.kv_probe_stream_read
+    expect(kd.KV_ERR_INVALID_ARG, lambda stream: sr(A16, 0, A16, stream=stream))
+    expect(kd.KV_ERR_INVALID_ARG, lambda stream: sr(A16, 24, A16, stream=stream))
+    expect(kd.KV_ERR_INVALID_ARG, lambda stream: sr(None, 32, A16, stream=stream))
+    expect(kd.KV_ERR_ALIGNMENT, lambda stream: sr(A4, 32, A16, stream=stream))
+    g = kd.kv_probe_gather_read
+    expect(kd.KV_ERR_INVALID_ARG, lambda stream: g(shape(), A16, A16, A16, A16, 0, A16,
+                                                   stream=stream))
+    expect(kd.KV_ERR_INVALID_ARG, lambda stream: g(shape(), A16, None, A16, A16, 2, A16,
+                                                   stream=stream))
+    expect(kd.KV_ERR_ALIGNMENT, lambda stream: g(shape(), A4, A16, A16, A16, 2, A16,
+                                                 stream=stream))
+    expect(kd.KV_ERR_UNSUPPORTED, lambda stream: g(shape(dtype="f32"), A16, A16, A16, A16, 2,
+                                                   A16, stream=stream))
