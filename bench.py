@@ -5,7 +5,8 @@ Workload: Llama-3.1-8B-shaped GQA decode of one layer at 128k context (batch 1,
 table, 5% planted blocks, Top-K 256 blocks), synthetic seeded data.
 
 One step = one pass over every stage of the path on that input:
-  block meta build over all 8192 pages -> append of the newest token -> Quest scores + Top-K 256 ->
+  block meta build over all 8192 pages -> append of the newest token + Quest scores + Top-K 256
+  (one call) ->
   sparse split-K attention -> merge -> dense split-K attention -> merge.
 The metric is KV GB/s (algorithmic bytes of the step / step time, and the same
 per stage) and decode steps/s; the dominant kernel (dense attention) is also
@@ -150,12 +151,12 @@ def run_gpu(args, spec, data):
     from kv_cache_decode_amd import kvdecode as kd
     s_sparse = kd.kv_auto_num_splits(copies[0].shape, k)
     s_dense = kd.kv_auto_num_splits(copies[0].shape, spec.max_blocks)
-    stages = ["meta_build", "append", "score_topk", "sparse_attn", "sparse_combine",
-              "dense_attn", "dense_combine"]
+    stages = ["meta_build", "append_select", "sparse_attn", "sparse_combine", "dense_attn",
+              "dense_combine"]
     actions = [
         lambda c: c.meta_build(),
-        lambda c: c.append(),            # the newest token again: state is unchanged
-        lambda c: c.score_topk(k),
+        # append of the newest token again (state is unchanged) + score + Top-K
+        lambda c: c.decode_select(k),
         lambda c: c.attention(sparse=True, num_splits=s_sparse),
         lambda c: c.combine(s_sparse),
         lambda c: c.attention(sparse=False, num_splits=s_dense),
@@ -264,9 +265,15 @@ def run_gpu(args, spec, data):
             launch = "eager"
             total_ms, wall = time_loop(lambda i: step(copies[i % len(copies)]))
         # the per-token decode steps on their own, each one HIP graph per copy:
-        # sparse = append + score/Top-K + sparse attention + merge,
-        # dense  = append + dense attention + merge
+        # sparse = append + score/Top-K (one call) + sparse attention + merge,
+        # dense  = append + dense attention + merge; and the sparse step with
+        # the append, score and Top-K as three separate calls, for comparison
         def decode_sparse(c):
+            c.decode_select(k)
+            c.attention(sparse=True, num_splits=s_sparse)
+            c.combine(s_sparse)
+
+        def decode_sparse_unfused(c):
             c.append()
             c.score_topk(k)
             c.attention(sparse=True, num_splits=s_sparse)
@@ -277,7 +284,8 @@ def run_gpu(args, spec, data):
             c.attention(sparse=False, num_splits=s_dense)
             c.combine(s_dense)
 
-        decode_us = {"sparse": graph_us(decode_sparse), "dense": graph_us(decode_dense)}
+        decode_us = {"sparse": graph_us(decode_sparse), "dense": graph_us(decode_dense),
+                     "sparse_unfused": graph_us(decode_sparse_unfused)}
         res.update({
             "total_ms": total_ms, "wall_s": wall, "stage_ms": per_stage_ms,
             "decode_us": decode_us, "launch": launch,
@@ -399,8 +407,7 @@ def time_variants(args, copies, k, s_sparse, time_loop, graph_us):
     }
 
     def decode_sparse_mean(c):
-        c.append()
-        c.select(k, "mean", 4, 64)
+        c.decode_select(k, "mean", 4, 64)
         c.attention(sparse=True, num_splits=s_sparse)
         c.combine(s_sparse)
 
@@ -449,8 +456,8 @@ def run_other_workload(args, name):
         res["meta_build_us"] = loop(lambda c: c.meta_build())
         res["score_topk_us"] = loop(lambda c: c.score_topk(k))
         res["sparse_attn_us"] = loop(lambda c: c.attention(sparse=True, num_splits=s_sp))
-        res["sparse_decode_us"] = loop(lambda c: (c.score_topk(k), c.decode(sparse=True,
-                                                                           num_splits=s_sp)))
+        res["sparse_decode_us"] = loop(lambda c: (c.decode_select(k),
+                                                  c.decode(sparse=True, num_splits=s_sp)))
         res["sparse_decode_steps_per_s"] = 1e6 / res["sparse_decode_us"]
         res["splits_sparse"] = s_sp
         res["stage_gbps"] = {name: gbps(name, res[f"{name}_us"])
@@ -819,7 +826,10 @@ def main():
         return
     log("[bench] timing GPU steps")
     g = run_gpu(args, spec, data)
-    sb = stage_bytes(spec, spec.topk_blocks, g["s_sparse"], g["s_dense"])
+    sb_all = stage_bytes(spec, spec.topk_blocks, g["s_sparse"], g["s_dense"])
+    sb = {s_: sb_all[s_] for s_ in ("meta_build", "sparse_attn", "sparse_combine", "dense_attn",
+                                    "dense_combine")}
+    sb["append_select"] = sb_all["append"] + sb_all["score_topk"]
     step_bytes = int(sum(sb.values()))
     ms = g["total_ms"] / args.steps
     st = g["stage_ms"]
@@ -863,8 +873,8 @@ def main():
             "head_dim": spec.head_dim, "block_size": spec.block_size,
             "kv_storage": spec.dtype, "topk_blocks": spec.topk_blocks,
             "splits_sparse": g["s_sparse"], "splits_dense": g["s_dense"],
-            "step": "meta_build(all pages) + append + score_topk + sparse attn + combine + "
-                    "dense attn + combine",
+            "step": "meta_build(all pages) + append_select (append + score + Top-K) + sparse "
+                    "attn + combine + dense attn + combine",
             "launch": g["launch"],
         },
         "eager_ms_per_step": g["eager_ms_per_step"],
@@ -872,14 +882,15 @@ def main():
         # one decode step of this layer, timed on its own as a HIP graph replay
         "decode_steps_per_s": {"sparse": 1e6 / g["decode_us"]["sparse"],
                                "dense": 1e6 / g["decode_us"]["dense"],
+                               "sparse_unfused": 1e6 / g["decode_us"]["sparse_unfused"],
                                "full_step": 1e3 / ms},
         "decode_step_us": g["decode_us"],
         "decode_step_timing": f"median per step over >= {GRAPH_MIN_REPLAYS} replays of a "
                               f"{GRAPH_STEPS}-step HIP graph, each between its own events",
         "decode_step_gbps": {
-            "sparse": (sb["append"] + sb["score_topk"] + sb["sparse_attn"] + sb["sparse_combine"])
+            "sparse": (sb["append_select"] + sb["sparse_attn"] + sb["sparse_combine"])
                       / (g["decode_us"]["sparse"] * 1e-6) / 1e9,
-            "dense": (sb["append"] + sb["dense_attn"] + sb["dense_combine"])
+            "dense": (sb_all["append"] + sb["dense_attn"] + sb["dense_combine"])
                      / (g["decode_us"]["dense"] * 1e-6) / 1e9},
         "step_bytes": step_bytes,
         "stage_bytes": sb,

@@ -18,6 +18,7 @@
  *   kv_paged_decode_attn  split-K softmax decode attention, dense or over selected blocks
  *   kv_decode_combine     log-sum-exp merge of the split partials
  *   kv_append_token       store the new token's K/V and fold it into its page's meta
+ *   kv_decode_select      kv_append_token followed by kv_block_select, in two launches
  *
  * The method is the select -> fetch -> compute decode step of the KVDrive paper
  * (§2.3, §4): a GPU-resident index picks the critical KV blocks, only those are
@@ -164,6 +165,29 @@ kv_status kv_block_mean_build(const kv_shape* shape, const void* k_cache, const 
 kv_status kv_append_token(const kv_shape* shape, const void* k_new, const void* v_new,
                           const int32_t* block_table, const int32_t* seq_lens, void* k_cache,
                           void* v_cache, void* kmeta, float* kmean, void* stream);
+
+/*
+ * The decode step's append and selection in one call (Dual-Blade background
+ * and DirectKV review, core method 4: the new K/V is stored at decode; KVDrive
+ * §2.3: the index then picks the blocks).  Results are bit for bit those of
+ * kv_append_token(shape, k_new, v_new, block_table, seq_lens, k_cache, v_cache,
+ * kmeta, kmean) followed by kv_block_select(shape, index_kind, q, index, ...,
+ * topk_blocks, sink_tokens, local_tokens, scores_out, sel_blocks, sel_count,
+ * workspace, workspace_bytes), with index = kmeta for KV_INDEX_MINMAX and kmean
+ * for KV_INDEX_MEAN (that one is required; the other may be NULL and is then
+ * not maintained).  Arguments, layouts, ownership and errors are those of the
+ * two calls.  It takes two launches instead of three: one extra workgroup per
+ * (sequence, KV head) of the scoring launch appends the token and scores its
+ * block from the updated index rows, while the other workgroups score the rest
+ * of the blocks; the Top-K follows.
+ */
+kv_status kv_decode_select(const kv_shape* shape, int32_t index_kind, const void* q,
+                           const void* k_new, const void* v_new, const int32_t* block_table,
+                           const int32_t* seq_lens, void* k_cache, void* v_cache, void* kmeta,
+                           float* kmean, int32_t topk_blocks, int32_t sink_tokens,
+                           int32_t local_tokens, float* scores_out, int32_t* sel_blocks,
+                           int32_t* sel_count, void* workspace, size_t workspace_bytes,
+                           void* stream);
 
 /* Workspace bytes kv_block_score_topk needs when scores_out is NULL (0 otherwise). */
 size_t kv_score_topk_workspace_size(const kv_shape* shape, int32_t topk_blocks);

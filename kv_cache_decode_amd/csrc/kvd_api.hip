@@ -184,6 +184,70 @@ kv_status kv_block_mean_build(const kv_shape* shape, const void* k_cache, const 
                     "kv_block_mean_build launch");
 }
 
+kv_status kv_decode_select(const kv_shape* shape, int32_t index_kind, const void* q,
+                           const void* k_new, const void* v_new, const int32_t* block_table,
+                           const int32_t* seq_lens, void* k_cache, void* v_cache, void* kmeta,
+                           float* kmean, int32_t topk_blocks, int32_t sink_tokens,
+                           int32_t local_tokens, float* scores_out, int32_t* sel_blocks,
+                           int32_t* sel_count, void* workspace, size_t workspace_bytes,
+                           void* stream) {
+  kv_status st = check_shape(shape);
+  if (st != KV_OK) return st;
+  if (index_kind != KV_INDEX_MINMAX && index_kind != KV_INDEX_MEAN)
+    return fail(KV_ERR_INVALID_ARG, "index_kind=%d unknown", index_kind);
+  const void* index = index_kind == KV_INDEX_MINMAX ? kmeta : static_cast<const void*>(kmean);
+  if (!index)
+    return fail(KV_ERR_INVALID_ARG, "the index selected by index_kind (%s) is required",
+                index_kind == KV_INDEX_MINMAX ? "kmeta" : "kmean");
+  if (topk_blocks < 1) return fail(KV_ERR_INVALID_ARG, "topk_blocks=%d must be >= 1", topk_blocks);
+  if (sink_tokens < 0 || local_tokens < 0)
+    return fail(KV_ERR_INVALID_ARG, "sink_tokens=%d and local_tokens=%d must be >= 0", sink_tokens,
+                local_tokens);
+  const int32_t forced = kv_max_forced_blocks(shape, sink_tokens, local_tokens);
+  if (forced > topk_blocks)
+    return fail(KV_ERR_INVALID_ARG,
+                "sink_tokens=%d and local_tokens=%d can force %d blocks, more than topk_blocks=%d",
+                sink_tokens, local_tokens, forced, topk_blocks);
+  if (shape->max_blocks_per_seq > kvd::kTopkMaxBlocks)
+    return fail(KV_ERR_UNSUPPORTED, "max_blocks_per_seq=%d above the Top-K limit %d",
+                shape->max_blocks_per_seq, kvd::kTopkMaxBlocks);
+  if (!q || !k_new || !v_new || !block_table || !seq_lens || !k_cache || !v_cache || !sel_blocks ||
+      !sel_count)
+    return fail(KV_ERR_INVALID_ARG,
+                "q, k_new, v_new, block_table, seq_lens, k_cache, v_cache, sel_blocks and "
+                "sel_count are required");
+  if (!aligned(q, 16) || !aligned(k_new, 16) || !aligned(v_new, 16) || !aligned(k_cache, 16) ||
+      !aligned(v_cache, 16) || (kmeta && !aligned(kmeta, 16)) || (kmean && !aligned(kmean, 16)))
+    return fail(KV_ERR_ALIGNMENT,
+                "q, k_new, v_new, k_cache, v_cache, kmeta and kmean must be 16-byte aligned");
+  if (!aligned(block_table, 4) || !aligned(seq_lens, 4) || !aligned(sel_blocks, 4) ||
+      !aligned(sel_count, 4) || (scores_out && !aligned(scores_out, 4)))
+    return fail(KV_ERR_ALIGNMENT, "integer and score arrays must be 4-byte aligned");
+  float* scores = scores_out;
+  if (!scores) {
+    const size_t need = kv_score_topk_workspace_size(shape, topk_blocks);
+    if (!workspace || workspace_bytes < need)
+      return fail(KV_ERR_WORKSPACE, "workspace of %zu bytes needed (got %zu)", need,
+                  workspace ? workspace_bytes : (size_t)0);
+    if (!aligned(workspace, 4)) return fail(KV_ERR_ALIGNMENT, "workspace must be 4-byte aligned");
+    scores = static_cast<float*>(workspace);
+  }
+  const int G = shape->num_q_heads / shape->num_kv_heads;
+  hipStream_t s = (hipStream_t)stream;
+  // the scorer's extra workgroups append the token and score its block from the
+  // updated index rows; the other blocks' index rows are not touched by it
+  hipError_t e = kvd::launch_block_score(shape->dtype, shape->head_dim, G, index_kind, q, index,
+                                         block_table, seq_lens, shape->num_seqs,
+                                         shape->num_q_heads, shape->num_kv_heads,
+                                         shape->max_blocks_per_seq, scores, s, k_new, v_new,
+                                         k_cache, v_cache, kmeta, kmean);
+  if (e != hipSuccess) return hip_status(e, "append + block score launch");
+  return hip_status(kvd::launch_topk(scores, seq_lens, shape->num_seqs, shape->num_kv_heads,
+                                     shape->max_blocks_per_seq, topk_blocks, sink_tokens,
+                                     local_tokens, sel_blocks, sel_count, s),
+                    "top-k launch");
+}
+
 kv_status kv_append_token(const kv_shape* shape, const void* k_new, const void* v_new,
                           const int32_t* block_table, const int32_t* seq_lens, void* k_cache,
                           void* v_cache, void* kmeta, float* kmean, void* stream) {

@@ -210,6 +210,53 @@ __device__ inline float cross_group_reduce(float v) {
   return v;
 }
 
+// ---------------------------------------------------------------- integer wave ops
+//
+// Without LDS round trips: DPP row_shr:n (each 16-lane row shifted up by n
+// lanes; lanes with no source read 0), row_bcast:15 / row_bcast:31 (lane 15 /
+// lane 31 fed to the rows enabled by the row mask), and readlane.  Every lane
+// of the wave must be active.
+
+enum : int {
+  kDppRowShr1 = 0x111,
+  kDppRowShr2 = 0x112,
+  kDppRowShr4 = 0x114,
+  kDppRowShr8 = 0x118,
+  kDppRowBcast15 = 0x142,
+  kDppRowBcast31 = 0x143,
+};
+
+template <int CTRL, int ROW_MASK = 0xF>
+__device__ inline uint32_t dpp_u32(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, ROW_MASK, 0xF, false);
+}
+
+// inclusive prefix sum over the wave's 64 lanes
+__device__ inline uint32_t wave_scan_add_u32(uint32_t v) {
+  v += dpp_u32<kDppRowShr1>(v);
+  v += dpp_u32<kDppRowShr2>(v);
+  v += dpp_u32<kDppRowShr4>(v);
+  v += dpp_u32<kDppRowShr8>(v);
+  v += dpp_u32<kDppRowBcast15, 0xA>(v);   // row 0's total into row 1, row 2's into row 3
+  v += dpp_u32<kDppRowBcast31, 0xC>(v);   // rows 0-1's total into rows 2 and 3
+  return v;
+}
+
+// all-reduce over the wave: inside each 16-lane row with DPP, then the four
+// row results read as scalars (the result is wave-uniform)
+template <typename Op>
+__device__ inline uint32_t wave_reduce_u32(uint32_t v, Op op) {
+  v = op(v, dpp_u32<kDppXor1>(v));
+  v = op(v, dpp_u32<kDppXor2>(v));
+  v = op(v, dpp_u32<kDppHalfMirror>(v));
+  v = op(v, dpp_u32<kDppMirror>(v));
+  const uint32_t r0 = (uint32_t)__builtin_amdgcn_readlane((int)v, 0);
+  const uint32_t r1 = (uint32_t)__builtin_amdgcn_readlane((int)v, 16);
+  const uint32_t r2 = (uint32_t)__builtin_amdgcn_readlane((int)v, 32);
+  const uint32_t r3 = (uint32_t)__builtin_amdgcn_readlane((int)v, 48);
+  return op(op(r0, r1), op(r2, r3));
+}
+
 __device__ inline float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
 __device__ inline int lane_id() { return __lane_id(); }

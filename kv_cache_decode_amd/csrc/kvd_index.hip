@@ -28,6 +28,9 @@
 #ifndef KVD_SCORE_STEPS
 #define KVD_SCORE_STEPS 8
 #endif
+#ifndef KVD_SCORE_WAVES
+#define KVD_SCORE_WAVES 4
+#endif
 
 namespace kvd {
 
@@ -150,24 +153,23 @@ __global__ __launch_bounds__(WAVES * kWave) void block_mean_kernel(
 
 // ============================================================== decode-step append
 //
-// One wave per (sequence, KV head); lane c < LPR owns channel chunk c.  The
-// new key and value rows are stored into their slot, and the key is folded
-// into the page's min/max rows (a fresh page, slot 0, starts them over).  The
-// page's mean row is recomputed from slots 0..s with the mean build's exact
+// One wave per (sequence, KV head); lane c < LPR owns channel chunk c
+// (append_lane, shared with the fused append + select kernel).  The new key
+// and value rows are stored into their slot, and the key is folded into the
+// page's min/max rows (a fresh page, slot 0, starts them over).  The page's
+// mean row is recomputed from slots 0..s with the mean build's exact
 // arithmetic (fp64 sum in slot order, one rounding), so it equals a rebuild.
+// The lane returns its chunk of the updated rows.
 
-template <typename DT, int D>
-__global__ __launch_bounds__(kWave) void append_token_kernel(
-    const void* __restrict__ k_new, const void* __restrict__ v_new,
-    const int32_t* __restrict__ block_table, const int32_t* __restrict__ seq_lens, int Hkv,
-    int maxN, void* __restrict__ k_cache, void* __restrict__ v_cache, void* __restrict__ kmeta,
-    float* __restrict__ kmean) {
-  using G_ = RowGeom<DT, D>;
+template <typename DT, int D, int E = RowGeom<DT, D>::E>
+__device__ inline void append_lane(const void* __restrict__ k_new, const void* __restrict__ v_new,
+                                   const int32_t* __restrict__ block_table,
+                                   const int32_t* __restrict__ seq_lens, int Hkv, int maxN, int j,
+                                   int b, int c, void* __restrict__ k_cache,
+                                   void* __restrict__ v_cache, void* __restrict__ kmeta,
+                                   float* __restrict__ kmean, float (&mn)[E], float (&mx)[E],
+                                   float (&mv)[E]) {
   using St = typename DT::storage;
-  constexpr int E = G_::E, LPR = G_::LPR;
-  const int c = threadIdx.x;
-  if (c >= LPR) return;
-  const int j = blockIdx.x, b = blockIdx.y;
   const int t = seq_lens[b] - 1;
   const int s = t % kBlockSize;
   const size_t tile = (size_t)block_table[(size_t)b * maxN + t / kBlockSize] * Hkv + j;
@@ -181,8 +183,11 @@ __global__ __launch_bounds__(kWave) void append_token_kernel(
     if (s == 0) {
       store16(m, kw);
       store16(m + D, kw);
+      DT::widen(kw, mn);
+#pragma unroll
+      for (int e = 0; e < E; ++e) mx[e] = mn[e];
     } else {
-      float f[E], mn[E], mx[E];
+      float f[E];
       DT::widen(kw, f);
       DT::widen(load16(m), mn);
       DT::widen(load16(m + D), mx);
@@ -194,28 +199,49 @@ __global__ __launch_bounds__(kWave) void append_token_kernel(
   }
   if (kmean) {
     // slots before s come from the cache (this lane wrote none of them), slot s
-    // is the new key; all rows of the page are loaded at once, rows past s unused
+    // is the new key; rows are loaded half a page at a time (rows past s unused)
+    // and summed in slot order
     const St* rows = static_cast<const St*>(k_cache) + tile * kBlockSize * D + (size_t)c * E;
-    uint4 w[kBlockSize];
-#pragma unroll
-    for (int t = 0; t < kBlockSize; ++t) w[t] = (t < s) ? load16(rows + (size_t)t * D) : kw;
     double acc[E];
 #pragma unroll
     for (int e = 0; e < E; ++e) acc[e] = 0.0;
+    constexpr int kHalf = kBlockSize / 2;
 #pragma unroll
-    for (int t = 0; t < kBlockSize; ++t) {
-      if (t <= s) {
-        float f[E];
-        DT::widen(w[t], f);
+    for (int h = 0; h < 2; ++h) {
+      uint4 w[kHalf];
 #pragma unroll
-        for (int e = 0; e < E; ++e) acc[e] += (double)f[e];
+      for (int r = 0; r < kHalf; ++r) {
+        const int t = h * kHalf + r;
+        w[r] = (t < s) ? load16(rows + (size_t)t * D) : kw;
+      }
+#pragma unroll
+      for (int r = 0; r < kHalf; ++r) {
+        if (h * kHalf + r <= s) {
+          float f[E];
+          DT::widen(w[r], f);
+#pragma unroll
+          for (int e = 0; e < E; ++e) acc[e] += (double)f[e];
+        }
       }
     }
-    float mv[E];
 #pragma unroll
     for (int e = 0; e < E; ++e) mv[e] = (float)(acc[e] / (double)(s + 1));
     store_f32_chunk<E>(kmean + tile * D + (size_t)c * E, mv);
   }
+}
+
+template <typename DT, int D>
+__global__ __launch_bounds__(kWave) void append_token_kernel(
+    const void* __restrict__ k_new, const void* __restrict__ v_new,
+    const int32_t* __restrict__ block_table, const int32_t* __restrict__ seq_lens, int Hkv,
+    int maxN, void* __restrict__ k_cache, void* __restrict__ v_cache, void* __restrict__ kmeta,
+    float* __restrict__ kmean) {
+  constexpr int E = RowGeom<DT, D>::E, LPR = RowGeom<DT, D>::LPR;
+  const int c = threadIdx.x;
+  if (c >= LPR) return;
+  float mn[E], mx[E], mv[E];
+  append_lane<DT, D>(k_new, v_new, block_table, seq_lens, Hkv, maxN, blockIdx.x, blockIdx.y, c,
+                     k_cache, v_cache, kmeta, kmean, mn, mx, mv);
 }
 
 // ============================================================== block score
@@ -231,17 +257,99 @@ __global__ __launch_bounds__(kWave) void append_token_kernel(
 
 constexpr int kIndexMinMax = 0, kIndexMean = 1;
 
-template <typename DT, int D, int G, int WAVES, int STEPS, int IDX>
+// Where the scorer's append workgroups store the new token (kernel argument).
+struct AppendArgs {
+  const void* k_new;
+  const void* v_new;
+  void* k_cache;
+  void* v_cache;
+  void* kmeta;
+  float* kmean;
+};
+
+// One lane's query chunk as the score uses it: q+ and q- for min/max, q and 0
+// for the mean index.
+template <int E, int IDX>
+__device__ inline void split_query(const float (&f)[E], float (&qp)[E], float (&qn)[E]) {
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    if constexpr (IDX == kIndexMinMax) {
+      qp[e] = fmaxf(f[e], 0.0f);
+      qn[e] = fminf(f[e], 0.0f);
+    } else {
+      qp[e] = f[e];
+      qn[e] = 0.0f;
+    }
+  }
+}
+
+// One head's block score from the LPR lanes of an aligned lane group, lane c
+// holding channels [c*E, c*E+E): ka / kb are the kmin / kmax chunks (ka the
+// mean chunk for the mean index).  Every lane of the wave must take part; each
+// lane of the group ends with the group's sum.
+template <int E, int LPR, int IDX>
+__device__ inline float head_score_lane(const float (&qp)[E], const float (&qn)[E],
+                                        const float (&ka)[E], const float (&kb)[E]) {
+  float acc = 0.0f;
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    if constexpr (IDX == kIndexMinMax) {
+      acc = fmaf(qp[e], kb[e], acc);
+      acc = fmaf(qn[e], ka[e], acc);
+    } else {
+      acc = fmaf(qp[e], ka[e], acc);
+    }
+  }
+  return group_reduce<LPR, OpSum>(acc);
+}
+
+template <typename DT, int D, int G, int WAVES, int STEPS, int IDX, bool APPEND>
 __global__ __launch_bounds__(WAVES * kWave) void block_score_kernel(
     const void* __restrict__ q, const void* __restrict__ kmeta,
     const int32_t* __restrict__ block_table, const int32_t* __restrict__ seq_lens, int Hq,
-    int Hkv, int maxN, float* __restrict__ scores) {
+    int Hkv, int maxN, float* __restrict__ scores, AppendArgs ap) {
   using G_ = RowGeom<DT, D>;
   using St = typename DT::storage;
   constexpr int E = G_::E, LPR = G_::LPR, TPI = G_::TPI;
   const int lane = threadIdx.x & (kWave - 1);
   const int rg = lane / LPR, c = lane % LPR;
   const int j = blockIdx.y, b = blockIdx.z;
+  // with APPEND, the last workgroup of every (b, j) row appends the new token
+  // and scores its block from the updated rows; the others skip that block
+  int nskip = -1;
+  if constexpr (APPEND) {
+    nskip = (seq_lens[b] - 1) / kBlockSize;
+    if (blockIdx.x == gridDim.x - 1) {
+      if (threadIdx.x >= kWave) return;                  // wave 0 only
+      const bool mine = lane < LPR;
+      float qp[G][E], qn[G][E];
+#pragma unroll
+      for (int g = 0; g < G; ++g) {
+        float f[E];
+        DT::widen(mine ? load16(static_cast<const St*>(q) + ((size_t)b * Hq + j * G + g) * D +
+                                lane * E)
+                       : make_uint4(0, 0, 0, 0),
+                  f);
+        split_query<E, IDX>(f, qp[g], qn[g]);
+      }
+      float mn[E], mx[E], mv[E];
+#pragma unroll
+      for (int e = 0; e < E; ++e) mn[e] = mx[e] = mv[e] = 0.0f;
+      if (mine)
+        append_lane<DT, D>(ap.k_new, ap.v_new, block_table, seq_lens, Hkv, maxN, j, b, lane,
+                           ap.k_cache, ap.v_cache, ap.kmeta, ap.kmean, mn, mx, mv);
+      float best = -INFINITY;
+#pragma unroll
+      for (int g = 0; g < G; ++g) {
+        if constexpr (IDX == kIndexMinMax)
+          best = fmaxf(best, head_score_lane<E, LPR, IDX>(qp[g], qn[g], mn, mx));
+        else
+          best = fmaxf(best, head_score_lane<E, LPR, IDX>(qp[g], qn[g], mv, mv));
+      }
+      if (lane == 0) scores[((size_t)b * Hkv + j) * maxN + nskip] = best;
+      return;
+    }
+  }
   const int n0 = (blockIdx.x * WAVES + (threadIdx.x >> 6)) * (STEPS * TPI);
   if (n0 >= maxN) return;
   const int nb = (seq_lens[b] + kBlockSize - 1) / kBlockSize;
@@ -276,16 +384,7 @@ __global__ __launch_bounds__(WAVES * kWave) void block_score_kernel(
   for (int g = 0; g < G; ++g) {
     float f[E];
     DT::widen(load16(static_cast<const St*>(q) + ((size_t)b * Hq + j * G + g) * D + c * E), f);
-#pragma unroll
-    for (int e = 0; e < E; ++e) {
-      if constexpr (IDX == kIndexMinMax) {
-        qp[g][e] = fmaxf(f[e], 0.0f);
-        qn[g][e] = fminf(f[e], 0.0f);
-      } else {
-        qp[g][e] = f[e];
-        qn[g][e] = 0.0f;
-      }
-    }
+    split_query<E, IDX>(f, qp[g], qn[g]);
   }
 
   float* out = scores + ((size_t)b * Hkv + j) * maxN;
@@ -307,21 +406,8 @@ __global__ __launch_bounds__(WAVES * kWave) void block_score_kernel(
     }
     float best = -INFINITY;
 #pragma unroll
-    for (int g = 0; g < G; ++g) {
-      float acc = 0.0f;
-#pragma unroll
-      for (int e = 0; e < E; ++e) {
-        if constexpr (IDX == kIndexMinMax) {
-          acc = fmaf(qp[g][e], kb[e], acc);
-          acc = fmaf(qn[g][e], ka[e], acc);
-        } else {
-          acc = fmaf(qp[g][e], ka[e], acc);
-        }
-      }
-      acc = group_reduce<LPR, OpSum>(acc);
-      best = fmaxf(best, acc);
-    }
-    if (c == 0 && n < maxN) out[n] = (n < nb) ? best : -INFINITY;
+    for (int g = 0; g < G; ++g) best = fmaxf(best, head_score_lane<E, LPR, IDX>(qp[g], qn[g], ka, kb));
+    if (c == 0 && n < maxN && n != nskip) out[n] = (n < nb) ? best : -INFINITY;
   }
 }
 
@@ -332,9 +418,12 @@ __global__ __launch_bounds__(WAVES * kWave) void block_score_kernel(
 // give equal keys); thread t keeps the keys of blocks [t*EPT, t*EPT+EPT) in
 // registers.  The K_eff-th largest key T is found by a radix select: the bits
 // above the highest bit where the smallest and largest valid keys differ are
-// fixed at once, then 8-bit digits below them are resolved from the top, each
-// pass building one private LDS histogram per wave (no atomic traffic between
-// waves) that wave 0 merges and scans.  A block is selected if its key is
+// fixed at once; the next 12 bits (4 * 1024 digits) are resolved by one pass
+// over a shared LDS histogram and a block scan.  If at most kTopkCandMax keys
+// share the bits known so far, they are gathered in LDS and each is ranked
+// against the others, which gives T directly; otherwise 8-bit digits are
+// resolved from the top, each pass building one private LDS histogram per
+// wave that wave 0 merges and scans.  A block is selected if its key is
 // above T, or equal to T and among the first K_eff - #{key > T} equal keys in
 // index order; one exclusive scan of packed (#greater, #equal) counts gives
 // every selected block its output position, so the list comes out ascending.
@@ -351,25 +440,16 @@ __device__ inline uint32_t score_key(float f) {
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
-__device__ inline uint32_t wave_min_u32(uint32_t v) {
-#pragma unroll
-  for (int off = 1; off < kWave; off <<= 1) v = min(v, (uint32_t)__shfl_xor((int)v, off, kWave));
-  return v;
-}
-__device__ inline uint32_t wave_max_u32(uint32_t v) {
-#pragma unroll
-  for (int off = 1; off < kWave; off <<= 1) v = max(v, (uint32_t)__shfl_xor((int)v, off, kWave));
-  return v;
-}
-__device__ inline uint32_t wave_inclusive_scan(uint32_t v) {
-  const int lane = threadIdx.x & (kWave - 1);
-#pragma unroll
-  for (int off = 1; off < kWave; off <<= 1) {
-    const uint32_t o = __shfl_up(v, off, kWave);
-    if (lane >= off) v += o;
-  }
-  return v;
-}
+struct MinU32 {
+  __device__ uint32_t operator()(uint32_t a, uint32_t b) const { return min(a, b); }
+};
+struct MaxU32 {
+  __device__ uint32_t operator()(uint32_t a, uint32_t b) const { return max(a, b); }
+};
+struct AddU32 {
+  __device__ uint32_t operator()(uint32_t a, uint32_t b) const { return a + b; }
+};
+__device__ inline uint32_t wave_inclusive_scan(uint32_t v) { return wave_scan_add_u32(v); }
 
 template <int NWAVES>
 __device__ inline uint32_t block_exclusive_scan(uint32_t v, uint32_t* buf) {
@@ -384,11 +464,19 @@ __device__ inline uint32_t block_exclusive_scan(uint32_t v, uint32_t* buf) {
 
 // Top-K of one row by the NT threads of a workgroup (all of them call it);
 // EPT keys per thread, NT * EPT >= maxN.
+// Most keys the rank count after the wide pass resolves (else 8-bit passes go on).
+constexpr int kTopkCandMax = 512;
+
 template <int NT>
 struct TopkSmem {
+  // per-wave 256-bin histograms of the 8-bit passes; the wide first pass uses
+  // the same words as one shared histogram of NT * 4 bins
   alignas(16) uint32_t hist[NT / kWave][256];
   uint32_t buf_a[NT / kWave], buf_b[NT / kWave], buf_c[NT / kWave], buf_d[NT / kWave];
-  uint32_t state[2];
+  uint32_t state[3];
+  uint32_t cand_n;
+  uint32_t cand_key[kTopkCandMax];
+  int32_t cand_idx[kTopkCandMax];
 };
 
 template <int NT, int EPT>
@@ -446,12 +534,14 @@ __device__ inline void topk_row(const float* __restrict__ row, int maxN, int L, 
       }
     }
   }
-  kmn = wave_min_u32(kmn);
-  kmx = wave_max_u32(kmx);
-  uint32_t nf = (uint32_t)__popc(fmask);
-#pragma unroll
-  for (int off = 1; off < kWave; off <<= 1) nf += (uint32_t)__shfl_xor((int)nf, off, kWave);
+  kmn = wave_reduce_u32(kmn, MinU32());
+  kmx = wave_reduce_u32(kmx, MaxU32());
+  uint32_t nf = wave_reduce_u32((uint32_t)__popc(fmask), AddU32());
   if (lane == 0) { buf_a[wave] = kmn; buf_b[wave] = kmx; buf_d[wave] = nf; }
+  if (tid == 0) sm.cand_n = 0u;
+  // the wide pass's shared histogram is cleared under the same barrier
+#pragma unroll
+  for (int i = 0; i < 4; ++i) (&hist[0][0])[tid + i * NT] = 0u;
   __syncthreads();
   nf = 0;
 #pragma unroll
@@ -463,10 +553,86 @@ __device__ inline void topk_row(const float* __restrict__ row, int maxN, int L, 
 
   // places left for the blocks that compete; with none, T is above every key
   uint32_t krem = (uint32_t)keff - nf;
-  // bits [lo, 32) of T are known; resolve the rest 8 bits at a time
+  // bits [lo, 32) of T are known; resolve the rest
   const uint32_t diff = kmn ^ kmx;
   int lo = (krem == 0u) ? 0 : (diff ? 32 - __clz(diff) : 0);
   uint32_t prefix = (krem == 0u) ? 0xFFFFFFFFu : ((lo >= 32) ? 0u : (kmx >> lo) << lo);
+  if (lo > 0) {
+    // one wide digit first: a shared histogram of NB = NT * 4 bins (thread t
+    // owns digits NB-1-4t .. NB-4-4t, top down) and one block scan over them
+    constexpr int NB = NT * 4;
+    constexpr int WB = 31 - __builtin_clz(NB);
+    const int width = min(WB, lo);
+    const int shift = lo - width;
+    const uint32_t dmask = (1u << width) - 1u;
+    uint32_t* hs = &hist[0][0];
+    static_assert(sizeof(sm.hist) == NB * sizeof(uint32_t), "shared histogram size");
+#pragma unroll
+    for (int r = 0; r < EPT; ++r) {
+      const bool match = key[r] != 0u && (lo >= 32 || (key[r] >> lo) == (prefix >> lo));
+      if (match) atomicAdd(&hs[(key[r] >> shift) & dmask], 1u);
+    }
+    __syncthreads();
+    const uint4 v4 = *reinterpret_cast<const uint4*>(&hs[NB - 4 - 4 * tid]);
+    const uint32_t cs[4] = {v4.w, v4.z, v4.y, v4.x};   // digits NB-1-4t down to NB-4-4t
+    uint32_t above = block_exclusive_scan<NW>(v4.x + v4.y + v4.z + v4.w, buf_a);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      if (above < krem && above + cs[q] >= krem) {
+        state[0] = (uint32_t)(NB - 1 - 4 * tid - q);
+        state[1] = krem - above;
+        state[2] = cs[q];
+      }
+      above += cs[q];
+    }
+    __syncthreads();
+    prefix |= state[0] << shift;
+    krem = state[1];
+    lo = shift;
+    const uint32_t nc = state[2];
+    if (lo > 0 && nc <= (uint32_t)kTopkCandMax) {
+      // few keys share the known bits: gather them and rank each against the
+      // others by (key descending, index ascending); the key ranked krem-1 is T
+#pragma unroll
+      for (int r = 0; r < EPT; ++r) {
+        if (key[r] != 0u && (key[r] >> lo) == (prefix >> lo)) {
+          const uint32_t pos = atomicAdd(&sm.cand_n, 1u);
+          sm.cand_key[pos] = key[r];
+          sm.cand_idx[pos] = n0 + r;
+        }
+      }
+      __syncthreads();
+      // wave w ranks candidates 64w .. 64w+63 (then 64(w+NW) ...), one per
+      // lane, against the others read 64 at a time into registers and
+      // broadcast with readlane
+      for (int cw = wave; cw * kWave < (int)nc; cw += NW) {
+        const int i = cw * kWave + lane;
+        const bool own = i < (int)nc;
+        const uint32_t ki = own ? sm.cand_key[i] : 0u;
+        const int ii = own ? sm.cand_idx[i] : 0;
+        uint32_t gt = 0, rank = 0;
+        for (int base = 0; base < (int)nc; base += kWave) {
+          const int cnt = min(kWave, (int)nc - base);
+          const int kc_l = (int)sm.cand_key[base + lane];   // base + 63 < kTopkCandMax
+          const int ic_l = sm.cand_idx[base + lane];
+          for (int c2 = 0; c2 < cnt; ++c2) {
+            const uint32_t kc = (uint32_t)__builtin_amdgcn_readlane(kc_l, c2);
+            const int ic = __builtin_amdgcn_readlane(ic_l, c2);
+            gt += kc > ki;
+            rank += kc > ki || (kc == ki && ic < ii);
+          }
+        }
+        if (own && rank == krem - 1u) {
+          state[0] = ki;
+          state[1] = krem - gt;
+        }
+      }
+      __syncthreads();
+      prefix = state[0];
+      krem = state[1];
+      lo = 0;
+    }
+  }
   while (lo > 0) {
     const int width = min(8, lo);
     const int shift = lo - width;
@@ -532,16 +698,16 @@ __device__ inline void topk_row(const float* __restrict__ row, int maxN, int L, 
   }
 }
 
-template <int EPT>
-__global__ __launch_bounds__(1024) void topk_kernel(const float* __restrict__ scores,
+template <int NT, int EPT>
+__global__ __launch_bounds__(NT) void topk_kernel(const float* __restrict__ scores,
                                                     const int32_t* __restrict__ seq_lens,
                                                     int Hkv, int maxN, int K, int sink,
                                                     int local, int32_t* __restrict__ sel,
                                                     int32_t* __restrict__ sel_count) {
-  __shared__ TopkSmem<1024> sm;
+  __shared__ TopkSmem<NT> sm;
   const int j = blockIdx.x, b = blockIdx.y;
   const size_t u = (size_t)b * Hkv + j;
-  topk_row<1024, EPT>(scores + u * maxN, maxN, seq_lens[b], K, sink, local, sel + u * K,
+  topk_row<NT, EPT>(scores + u * maxN, maxN, seq_lens[b], K, sink, local, sel + u * K,
                       sel_count + u, sm);
 }
 
@@ -605,24 +771,33 @@ hipError_t launch_append_token(int dtype, int D, const void* k_new, const void* 
 hipError_t launch_block_score(int dtype, int D, int G, int index_kind, const void* q,
                               const void* index, const int32_t* block_table,
                               const int32_t* seq_lens, int B, int Hq, int Hkv, int maxN,
-                              float* scores, hipStream_t stream) {
+                              float* scores, hipStream_t stream, const void* k_new,
+                              const void* v_new, void* k_cache, void* v_cache, void* kmeta,
+                              float* kmean) {
+  const AppendArgs ap{k_new, v_new, k_cache, v_cache, kmeta, kmean};
+  const bool append = k_new != nullptr;
   return with_dtype(dtype, [&](auto dt) {
     return with_dim(D, [&](auto d) {
       return with_group(G, [&](auto g) {
         using DT = decltype(dt);
         constexpr int DD = decltype(d)::value;
         constexpr int GG = decltype(g)::value;
-        constexpr int WAVES = 4, STEPS = KVD_SCORE_STEPS;
+        constexpr int WAVES = KVD_SCORE_WAVES, STEPS = KVD_SCORE_STEPS;
         constexpr int per_wg = WAVES * STEPS * RowGeom<DT, DD>::TPI;
-        const dim3 grid((maxN + per_wg - 1) / per_wg, Hkv, B);
-        if (index_kind == kIndexMean)
-          hipLaunchKernelGGL((block_score_kernel<DT, DD, GG, WAVES, STEPS, kIndexMean>), grid,
-                             dim3(WAVES * kWave), 0, stream, q, index, block_table, seq_lens, Hq,
-                             Hkv, maxN, scores);
-        else
-          hipLaunchKernelGGL((block_score_kernel<DT, DD, GG, WAVES, STEPS, kIndexMinMax>), grid,
-                             dim3(WAVES * kWave), 0, stream, q, index, block_table, seq_lens, Hq,
-                             Hkv, maxN, scores);
+        // one more workgroup per row does the append
+        const dim3 grid((maxN + per_wg - 1) / per_wg + (append ? 1 : 0), Hkv, B);
+#define KVD_SCORE(IDX, APP)                                                                     \
+  hipLaunchKernelGGL((block_score_kernel<DT, DD, GG, WAVES, STEPS, IDX, APP>), grid,           \
+                     dim3(WAVES * kWave), 0, stream, q, index, block_table, seq_lens, Hq, Hkv, \
+                     maxN, scores, ap)
+        if (index_kind == kIndexMean) {
+          if (append) KVD_SCORE(kIndexMean, true);
+          else KVD_SCORE(kIndexMean, false);
+        } else {
+          if (append) KVD_SCORE(kIndexMinMax, true);
+          else KVD_SCORE(kIndexMinMax, false);
+        }
+#undef KVD_SCORE
         return hipGetLastError();
       });
     });
@@ -635,7 +810,7 @@ hipError_t launch_topk(const float* scores, const int32_t* seq_lens, int B, int 
   const dim3 grid(Hkv, B);
   const int ept = (maxN + 1023) / 1024;
 #define KVD_TOPK(N)                                                                          \
-  hipLaunchKernelGGL((topk_kernel<N>), grid, dim3(1024), 0, stream, scores, seq_lens, Hkv, \
+  hipLaunchKernelGGL((topk_kernel<1024, N>), grid, dim3(1024), 0, stream, scores, seq_lens, Hkv, \
                      maxN, K, sink, local, sel, sel_count)
   if (ept <= 1) KVD_TOPK(1);
   else if (ept <= 2) KVD_TOPK(2);

@@ -26,7 +26,10 @@ hipError_t launch_append_token(int dtype, int D, const void* k_new, const void* 
 hipError_t launch_block_score(int dtype, int D, int G, int index_kind, const void* q,
                               const void* index, const int32_t* block_table,
                               const int32_t* seq_lens, int B, int Hq, int Hkv, int maxN,
-                              float* scores, hipStream_t stream);
+                              float* scores, hipStream_t stream, const void* k_new = nullptr,
+                              const void* v_new = nullptr, void* k_cache = nullptr,
+                              void* v_cache = nullptr, void* kmeta = nullptr,
+                              float* kmean = nullptr);
 
 hipError_t launch_topk(const float* scores, const int32_t* seq_lens, int B, int Hkv, int maxN,
                        int K, int sink, int local, int32_t* sel, int32_t* sel_count,

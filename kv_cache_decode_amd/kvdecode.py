@@ -26,7 +26,7 @@ DTYPE_CODES = {"f32": KV_F32, "f16": KV_F16, "bf16": KV_BF16}
 
 # every symbol the header declares
 EXPORTS = (
-    "kv_block_meta_build", "kv_block_mean_build", "kv_append_token",
+    "kv_block_meta_build", "kv_block_mean_build", "kv_append_token", "kv_decode_select",
     "kv_score_topk_workspace_size", "kv_block_score_topk", "kv_max_forced_blocks",
     "kv_block_select", "kv_auto_num_splits", "kv_auto_num_splits_fp8", "kv_paged_decode_attn", "kv_decode_combine",
     "kv_quantize_pages_fp8", "kv_paged_decode_attn_fp8", "kv_cache_plan", "kv_cache_fetch",
@@ -83,6 +83,8 @@ def _load() -> ctypes.CDLL:
         "kv_block_mean_build": (I32, [S, P, P, P, I32, P, P]),
         "kv_append_token": (I32, [S, P, P, P, P, P, P, P, P, P]),
         "kv_max_forced_blocks": (I32, [S, I32, I32]),
+        "kv_decode_select": (I32, [S, I32, P, P, P, P, P, P, P, P, P, I32, I32, I32, P, P, P, P,
+                                   SZ, P]),
         "kv_block_select": (I32, [S, I32, P, P, P, P, I32, I32, I32, P, P, P, P, SZ, P]),
         "kv_score_topk_workspace_size": (SZ, [S, I32]),
         "kv_block_score_topk": (I32, [S, P, P, P, P, I32, P, P, P, P, SZ, P]),
@@ -165,6 +167,18 @@ def kv_append_token(shape: KVShape, k_new: Buf, v_new: Buf, block_table: Buf, se
     _check(_lib.kv_append_token(ctypes.byref(shape), _p(k_new), _p(v_new), _p(block_table),
                                 _p(seq_lens), _p(k_cache), _p(v_cache), _p(kmeta), _p(kmean),
                                 _stream(stream)))
+
+
+def kv_decode_select(shape: KVShape, index_kind: int, q: Buf, k_new: Buf, v_new: Buf,
+                     block_table: Buf, seq_lens: Buf, k_cache: Buf, v_cache: Buf, kmeta: Buf,
+                     kmean: Buf, topk_blocks: int, sink_tokens: int, local_tokens: int,
+                     scores_out: Buf, sel_blocks: Buf, sel_count: Buf, workspace: Buf = None,
+                     workspace_bytes: int = 0, stream=None) -> None:
+    _check(_lib.kv_decode_select(ctypes.byref(shape), index_kind, _p(q), _p(k_new), _p(v_new),
+                                 _p(block_table), _p(seq_lens), _p(k_cache), _p(v_cache),
+                                 _p(kmeta), _p(kmean), topk_blocks, sink_tokens, local_tokens,
+                                 _p(scores_out), _p(sel_blocks), _p(sel_count), _p(workspace),
+                                 workspace_bytes, _stream(stream)))
 
 
 def kv_score_topk_workspace_size(shape: KVShape, topk_blocks: int) -> int:

@@ -170,6 +170,18 @@ class DeviceWorkload:
                            sink_tokens, local_tokens, self.scores, self.sel, self.sel_count, None,
                            0, stream)
 
+    def decode_select(self, k: int, index: str = "minmax", sink_tokens: int = 0,
+                      local_tokens: int = 0, k_new=None, v_new=None, meta: bool = True,
+                      stream=None):
+        """kv_decode_select: append (as append()) and select (as select()) in one call."""
+        self._sel_buffers(k)
+        kind = kd.KV_INDEX_MEAN if index == "mean" else kd.KV_INDEX_MINMAX
+        kd.kv_decode_select(self.shape, kind, self.q, self.last_k if k_new is None else k_new,
+                            self.last_v if v_new is None else v_new, self.block_table,
+                            self.seq_lens, self.k_cache, self.v_cache,
+                            self.kmeta if meta else None, self.kmean, k, sink_tokens,
+                            local_tokens, self.scores, self.sel, self.sel_count, None, 0, stream)
+
     def attention(self, sparse: bool, num_splits: Optional[int] = None, stream=None):
         S = num_splits or self.auto_splits(sparse)
         po, pm, pl = self.partials(S)

@@ -321,3 +321,26 @@ def test_probe_argument_checks():
                                                  stream=stream))
     expect(kd.KV_ERR_UNSUPPORTED, lambda stream: g(shape(dtype="f32"), A16, A16, A16, A16, 2,
                                                    A16, stream=stream))
+
+
+def test_decode_select_argument_checks():
+    s = shape()
+    f = kd.kv_decode_select
+
+    def call(**kw):
+        args = dict(index_kind=kd.KV_INDEX_MINMAX, q=A16, k_new=A16, v_new=A16, block_table=A16,
+                    seq_lens=A16, k_cache=A16, v_cache=A16, kmeta=A16, kmean=None, topk_blocks=2,
+                    sink_tokens=0, local_tokens=0, scores_out=A16, sel_blocks=A16, sel_count=A16)
+        args.update(kw)
+        return lambda stream: f(s, stream=stream, **args)
+
+    expect(kd.KV_ERR_INVALID_ARG, call(kmeta=None))                       # the chosen index
+    expect(kd.KV_ERR_INVALID_ARG, call(index_kind=kd.KV_INDEX_MEAN))       # kmean missing
+    expect(kd.KV_ERR_INVALID_ARG, call(index_kind=5))
+    expect(kd.KV_ERR_INVALID_ARG, call(topk_blocks=0))
+    expect(kd.KV_ERR_INVALID_ARG, call(sink_tokens=64, local_tokens=64))  # forces > topk
+    expect(kd.KV_ERR_INVALID_ARG, call(k_new=None))
+    expect(kd.KV_ERR_ALIGNMENT, call(v_new=A4))
+    expect(kd.KV_ERR_ALIGNMENT, call(index_kind=kd.KV_INDEX_MEAN, kmean=A4))
+    expect(kd.KV_ERR_ALIGNMENT, call(sel_count=ODD))
+    expect(kd.KV_ERR_WORKSPACE, call(scores_out=None))
