@@ -94,3 +94,20 @@ def test_largest_table_32768_blocks(gpu):
     rows = [rng.standard_normal((1, 32768)).astype(np.float32)]
     for k in (1, 1024, 32768):
         run_case(gpu, rows, k, Hkv=1, G=2)
+
+
+@pytest.mark.parametrize("n_eq", [511, 512, 513, 1700])
+def test_boundary_digit_holding_many_equal_keys(gpu, n_eq):
+    """n_eq equal top scores: after the wide first pass the boundary digit holds
+    n_eq keys, which the rank count resolves (up to 512) or the 8-bit passes do
+    (above); with a few larger keys in front of them and a spread of smaller ones."""
+    rng = np.random.default_rng(n_eq)
+    n = 4000
+    r = np.empty(n, np.float32)
+    r[:] = rng.uniform(-4.0, 0.5, n).astype(np.float32)
+    pos = rng.permutation(n)
+    r[pos[:n_eq]] = 1.0
+    r[pos[n_eq:n_eq + 3]] = [2.0, 3.0, 5.0]
+    rows = [np.stack([r, r[::-1].copy()])]
+    for k in (1, 4, 256, n_eq + 2, n_eq + 4):
+        run_case(gpu, rows, k)
