@@ -473,6 +473,7 @@ struct TopkSmem {
   // the same words as one shared histogram of NT * 4 bins
   alignas(16) uint32_t hist[NT / kWave][256];
   uint32_t buf_a[NT / kWave], buf_b[NT / kWave], buf_c[NT / kWave], buf_d[NT / kWave];
+  uint32_t buf_e[NT / kWave], buf_f[NT / kWave], buf_g[NT / kWave];
   uint32_t state[3];
   uint32_t cand_n;
   uint32_t cand_key[kTopkCandMax];
@@ -489,6 +490,9 @@ __device__ inline void topk_row(const float* __restrict__ row, int maxN, int L, 
   auto& buf_b = sm.buf_b;
   auto& buf_c = sm.buf_c;
   auto& buf_d = sm.buf_d;
+  auto& buf_e = sm.buf_e;
+  auto& buf_f = sm.buf_f;
+  auto& buf_g = sm.buf_g;
   auto& state = sm.state;
   const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid >> 6;
   const int nb = (L + kBlockSize - 1) / kBlockSize;
@@ -500,6 +504,8 @@ __device__ inline void topk_row(const float* __restrict__ row, int maxN, int L, 
 
   uint32_t key[EPT];
   uint32_t kmn = 0xFFFFFFFFu, kmx = 0u;
+  // the same over the keys of scores >= +0 (top bit set) and below it
+  uint32_t kmn_pos = 0xFFFFFFFFu, kmx_neg = 0u, npos = 0u;
   float sc[EPT];
   const int n0 = tid * EPT;
   if constexpr (EPT % 4 == 0) {
@@ -531,28 +537,54 @@ __device__ inline void topk_row(const float* __restrict__ row, int maxN, int L, 
         key[r] = score_key(sc[r]);  // valid keys are >= key(-inf) > 0
         kmn = min(kmn, key[r]);
         kmx = max(kmx, key[r]);
+        if (key[r] >> 31) {
+          kmn_pos = min(kmn_pos, key[r]);
+          ++npos;
+        } else {
+          kmx_neg = max(kmx_neg, key[r]);
+        }
       }
     }
   }
   kmn = wave_reduce_u32(kmn, MinU32());
   kmx = wave_reduce_u32(kmx, MaxU32());
   uint32_t nf = wave_reduce_u32((uint32_t)__popc(fmask), AddU32());
-  if (lane == 0) { buf_a[wave] = kmn; buf_b[wave] = kmx; buf_d[wave] = nf; }
+  kmn_pos = wave_reduce_u32(kmn_pos, MinU32());
+  kmx_neg = wave_reduce_u32(kmx_neg, MaxU32());
+  npos = wave_reduce_u32(npos, AddU32());
+  if (lane == 0) {
+    buf_a[wave] = kmn; buf_b[wave] = kmx; buf_d[wave] = nf;
+    buf_e[wave] = kmn_pos; buf_f[wave] = kmx_neg; buf_g[wave] = npos;
+  }
   if (tid == 0) sm.cand_n = 0u;
   // the wide pass's shared histogram is cleared under the same barrier
 #pragma unroll
   for (int i = 0; i < 4; ++i) (&hist[0][0])[tid + i * NT] = 0u;
   __syncthreads();
   nf = 0;
+  npos = 0;
 #pragma unroll
   for (int w = 0; w < NW; ++w) {
     kmn = min(kmn, buf_a[w]);
     kmx = max(kmx, buf_b[w]);
     nf += buf_d[w];
+    kmn_pos = min(kmn_pos, buf_e[w]);
+    kmx_neg = max(kmx_neg, buf_f[w]);
+    npos += buf_g[w];
   }
 
   // places left for the blocks that compete; with none, T is above every key
   uint32_t krem = (uint32_t)keff - nf;
+  // scores of both signs: the counts say on which side of zero T lies, so the
+  // select starts inside that half (the top bit is then known)
+  if (krem != 0u && ((kmn ^ kmx) >> 31)) {
+    if (npos >= krem) {
+      kmn = kmn_pos;
+    } else {
+      krem -= npos;             // every key of a score >= +0 ranks above T
+      kmx = kmx_neg;
+    }
+  }
   // bits [lo, 32) of T are known; resolve the rest
   const uint32_t diff = kmn ^ kmx;
   int lo = (krem == 0u) ? 0 : (diff ? 32 - __clz(diff) : 0);
