@@ -314,12 +314,13 @@ __global__ __launch_bounds__(WAVES * kWave) void block_score_kernel(
   const int lane = threadIdx.x & (kWave - 1);
   const int rg = lane / LPR, c = lane % LPR;
   const int j = blockIdx.y, b = blockIdx.z;
-  // with APPEND, the last workgroup of every (b, j) row appends the new token
-  // and scores its block from the updated rows; the others skip that block
+  // with APPEND, the first workgroup of every (b, j) row (dispatched first, so
+  // its dependent loads overlap the scoring) appends the new token and scores
+  // its block from the updated rows; the others skip that block
   int nskip = -1;
   if constexpr (APPEND) {
     nskip = (seq_lens[b] - 1) / kBlockSize;
-    if (blockIdx.x == gridDim.x - 1) {
+    if (blockIdx.x == 0) {
       if (threadIdx.x >= kWave) return;                  // wave 0 only
       const bool mine = lane < LPR;
       float qp[G][E], qn[G][E];
@@ -350,7 +351,8 @@ __global__ __launch_bounds__(WAVES * kWave) void block_score_kernel(
       return;
     }
   }
-  const int n0 = (blockIdx.x * WAVES + (threadIdx.x >> 6)) * (STEPS * TPI);
+  const int wg = APPEND ? (int)blockIdx.x - 1 : (int)blockIdx.x;
+  const int n0 = (wg * WAVES + (threadIdx.x >> 6)) * (STEPS * TPI);
   if (n0 >= maxN) return;
   const int nb = (seq_lens[b] + kBlockSize - 1) / kBlockSize;
 
