@@ -69,6 +69,12 @@ def _load():
     lib.oracle_fp8_encode.restype = ctypes.c_uint8
     lib.oracle_fp8_quantize.argtypes = [_D, _int, _int, _int, _I, _I, _int, _U8, _F, _int]
     lib.oracle_fp8_quantize.restype = None
+    lib.oracle_int4_code.argtypes = [ctypes.c_float]
+    lib.oracle_int4_code.restype = ctypes.c_int
+    lib.oracle_int4_quantize.argtypes = [_D, _int, _int, _int, _I, _I, _int, _U8, _F, _int]
+    lib.oracle_int4_quantize.restype = None
+    lib.oracle_int4_unpack.argtypes = [_U8, _int]
+    lib.oracle_int4_unpack.restype = ctypes.c_int
     lib.oracle_block_lse.argtypes = [_D, _D, _I, _I, _I, _I, _int, _int, _int, _int, _int, _int,
                                      _int, ctypes.c_double, _D]
     lib.oracle_block_lse.restype = None
@@ -206,6 +212,45 @@ def fp8_quantize(pool, page_ids, valid_tokens):
 def fp8_dequantize(codes, scales) -> np.ndarray:
     """decode(code) * scale per (page, KV head), float64 [P, Hkv, bs, D]."""
     return fp8_decode(codes) * np.asarray(scales, np.float64)[:, :, None, None]
+
+
+def int4_code(y: float) -> int:
+    """The INT4 code of an fp32 quotient x / scale: round half to even, clamp to [-7, 7]."""
+    return int(_load().oracle_int4_code(float(np.float32(y))))
+
+
+def int4_quantize(pool, page_ids, valid_tokens):
+    """(codes uint8 [P, Hkv, bs, D/2], scales float32 [P, Hkv]) of the listed pages;
+    pages not listed keep code 0 and scale 0."""
+    x = _f64(pool)
+    P, Hkv, bs, D = x.shape
+    ids, val = _i32(page_ids), _i32(valid_tokens)
+    codes = np.zeros((P, Hkv, bs, D // 2), dtype=np.uint8)
+    scales = np.zeros((P, Hkv), dtype=np.float32)
+    _load().oracle_int4_quantize(_pd(x), Hkv, bs, D, _pi(ids), _pi(val), len(ids),
+                                 codes.ctypes.data_as(ctypes.POINTER(ctypes.c_uint8)),
+                                 scales.ctypes.data_as(ctypes.POINTER(ctypes.c_float)), 1)
+    return codes, scales
+
+
+def int4_unpack(codes) -> np.ndarray:
+    """Signed codes int8 [..., D] of packed rows [..., D/2]: byte b holds channel 2b
+    in its low nibble and 2b+1 in its high nibble, each 4-bit two's complement."""
+    c = np.asarray(codes, dtype=np.uint8)
+    nib = np.stack([c & 15, c >> 4], axis=-1).astype(np.int8)      # [..., D/2, 2]
+    nib = np.where(nib >= 8, nib - 16, nib).astype(np.int8)
+    return nib.reshape(c.shape[:-1] + (2 * c.shape[-1],))
+
+
+def int4_unpack_c(packed_row, c: int) -> int:
+    """The oracle's C unpack of channel c of one packed row."""
+    r = np.ascontiguousarray(packed_row, dtype=np.uint8)
+    return int(_load().oracle_int4_unpack(r.ctypes.data_as(ctypes.POINTER(ctypes.c_uint8)), c))
+
+
+def int4_dequantize(codes, scales) -> np.ndarray:
+    """n * scale per (page, KV head), float64 [P, Hkv, bs, D]."""
+    return int4_unpack(codes).astype(np.float64) * np.asarray(scales, np.float64)[:, :, None, None]
 
 
 def block_lse(q, k_pool, block_table, seq_lens, block_size: int, scale: float, sel=None,

@@ -55,6 +55,13 @@
  *    slots past the valid count; the value a code stands for is
  *    decode(code) * s.  The scale and the quotient are taken in fp32, the
  *    precision in which the quantiser decides the codes;
+ *  - INT4 cold pages (the same passages name INT4; they fix no format, so the
+ *    reading is the plain symmetric one): per (page, KV head) and tensor
+ *    s = amax / 7 over the valid slots (1 for an all-zero tile), code n =
+ *    round-half-even(x / s) clamped to [-7, 7], code 0 past the valid count;
+ *    the value a code stands for is n * s.  Scale and quotient in fp32, as for
+ *    FP8.  A code is stored as a 4-bit two's complement nibble, two per byte,
+ *    the even channel in the low nibble;
  *  - GPU-resident block cache with lookahead eviction (KVDrive §5.1: a window
  *    of critical KV entries stays on the GPU; each step the new critical
  *    entries are fetched from host memory and the entries with the lowest
@@ -377,6 +384,61 @@ void oracle_fp8_quantize(const double* pool, int Hkv, int bs, int D, const int32
       }
     }
   }
+}
+
+/*
+ * INT4 (symmetric, one scale per tile).  Quantise the listed pages of one pool
+ * (K or V): for i < n_ids and KV head j, p = page_ids[i], v = valid_tokens[i]:
+ *   amax = max_{s < v, c} |X[p, j, s, c]|  (fp32 values of the stored dtype)
+ *   scale[p, j] = amax / 7 in fp32, or 1 when amax == 0
+ *   n = round-half-even(X / scale in fp32), clamped to [-7, 7], for s < v;
+ *   n = 0 for s >= v.
+ * codes: uint8 [P, Hkv, bs, D/2], byte c/2 of a row holding channel c (even c)
+ * in bits 0..3 and channel c+1 in bits 4..7, each as two's complement.
+ */
+int oracle_int4_code(float y) {
+  double r = nearbyint((double)y);     /* y is an fp32 value: exact in double */
+  if (r > 7.0) r = 7.0;
+  if (r < -7.0) r = -7.0;
+  return (int)r;
+}
+
+void oracle_int4_quantize(const double* pool, int Hkv, int bs, int D, const int32_t* page_ids,
+                          const int32_t* valid_tokens, int n_ids, uint8_t* codes, float* scales,
+                          int scale_stride) {
+#pragma omp parallel for schedule(static)
+  for (int i = 0; i < n_ids; ++i) {
+    const i64 p = page_ids[i];
+    const int nv = valid_tokens[i];
+    for (int j = 0; j < Hkv; ++j) {
+      float amax = 0.0f;
+      for (int s = 0; s < nv; ++s) {
+        const double* row = pool_row(pool, p, j, s, Hkv, bs, D);
+        for (int c = 0; c < D; ++c) {
+          const float x = fabsf((float)row[c]);
+          if (x > amax) amax = x;
+        }
+      }
+      const float sc = (amax > 0.0f) ? amax / 7.0f : 1.0f;
+      scales[(p * Hkv + j) * (i64)scale_stride] = sc;
+      for (int s = 0; s < bs; ++s) {
+        uint8_t* out = codes + ((p * Hkv + j) * bs + s) * (i64)(D / 2);
+        memset(out, 0, (size_t)(D / 2));
+        if (s >= nv) continue;
+        const double* row = pool_row(pool, p, j, s, Hkv, bs, D);
+        for (int c = 0; c < D; ++c) {
+          const int n = oracle_int4_code((float)row[c] / sc);
+          out[c / 2] |= (uint8_t)((n & 15) << (4 * (c & 1)));
+        }
+      }
+    }
+  }
+}
+
+/* The code of channel c in a packed row: the nibble, sign-extended. */
+int oracle_int4_unpack(const uint8_t* row, int c) {
+  const int nib = (row[c / 2] >> (4 * (c & 1))) & 15;
+  return nib >= 8 ? nib - 16 : nib;
 }
 
 /*

@@ -52,6 +52,13 @@ MUTANTS = [
     ("fp8_amax_over_every_slot", "for (int s = 0; s < nv; ++s) {\n        const double* row = pool_row(pool",
      "for (int s = 0; s < bs; ++s) {\n        const double* row = pool_row(pool", 0),
     ("fp8_tail_slots_encoded", "if (s >= nv) {\n          memset", "if (s >= bs) {\n          memset", 0),
+    ("int4_scale_8", "amax / 7.0f", "amax / 8.0f", 0),
+    ("int4_round_half_away", "double r = nearbyint((double)y);", "double r = round((double)y);", 0),
+    ("int4_nibbles_swapped", "out[c / 2] |= (uint8_t)((n & 15) << (4 * (c & 1)));",
+     "out[c / 2] |= (uint8_t)((n & 15) << (4 * (1 - (c & 1))));", 0),
+    ("int4_amax_over_every_slot", "for (int s = 0; s < nv; ++s) {\n        const double* row = pool_row(pool",
+     "for (int s = 0; s < bs; ++s) {\n        const double* row = pool_row(pool", 1),
+    ("int4_tail_slots_encoded", "if (s >= nv) continue;", "if (s >= bs) continue;", 0),
     ("cache_evicts_highest_mass", "if (mass[ck] < mass[cb] || (mass[ck] == mass[cb] && ck < cb)) best = k;",
      "if (mass[ck] > mass[cb] || (mass[ck] == mass[cb] && ck < cb)) best = k;", 0),
     ("cache_ties_to_higher_slot", "(mass[ck] == mass[cb] && ck < cb)", "(mass[ck] == mass[cb] && ck > cb)", 0),

@@ -721,6 +721,83 @@ def test_fp8_dequantized_attention_is_attention_over_decoded_values():
                                    atol=1e-14)
 
 
+# ---------------------------------------------------------------- INT4 cold pages
+# KVDrive §11 and the DirectKV review name INT4 for cold KV; symmetric reading
+
+def test_int4_golden(variants):
+    g = variants["int4"]
+    for u in g["unpack"]:
+        assert oracle.int4_unpack(np.array([u["byte"]], np.uint8)).tolist() == u["codes"], u
+    for q in g["quantize"]:
+        x = np.array(q["x_slots"], np.float64).reshape(1, 1, q["block_size"], q["head_dim"])
+        c, s = oracle.int4_quantize(x, [0], [q["valid_tokens"]])
+        assert s[0, 0] == q["scale"], q["derivation"]
+        assert c[0, 0].tolist() == q["codes"], q["derivation"]
+
+
+def test_int4_unpack_c_and_numpy_agree_on_every_byte():
+    for b in range(256):
+        row = np.array([b], np.uint8)
+        assert oracle.int4_unpack(row).tolist() == [oracle.int4_unpack_c(row, 0),
+                                                    oracle.int4_unpack_c(row, 1)]
+
+
+def test_int4_code_rounding_and_clamp():
+    cases = {2.5: 2, 3.5: 4, -2.5: -2, -0.5: 0, 0.49999997: 0, 6.5: 6, 7.49: 7, 100.0: 7,
+             -7.5: -7, -1e30: -7, 1.5: 2}
+    for y, n in cases.items():
+        assert oracle.int4_code(y) == n, (y, n)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "f16", "bf16"])
+def test_int4_quantize_matches_numpy_and_error_bound(dtype):
+    data = mk(B=2, Hq=4, Hkv=2, D=16, lens=(45, 16), dtype=dtype, seed=43, extra_pages=1)
+    k64 = data.k64()
+    ids, val = page_lists(data)
+    codes, scales = oracle.int4_quantize(k64, ids, val)
+    n_all = oracle.int4_unpack(codes)
+    x32 = k64.astype(np.float32)
+    for p, nv in zip(ids, val):
+        for j in range(2):
+            tile = x32[p, j, :nv]
+            amax = np.abs(tile).max()
+            s = scales[p, j]
+            assert s == np.float32(amax) / np.float32(7)
+            n = n_all[p, j, :nv]
+            # numpy's fp32 quotient, rounded half to even, clamped
+            np.testing.assert_array_equal(n, np.clip(np.rint(tile / s), -7, 7).astype(np.int8))
+            big = np.abs(tile) == amax
+            assert np.all(np.abs(n[big]) == 7)
+            deq = n.astype(np.float64) * float(s)
+            assert np.all(np.abs(deq - tile) <= 0.5 * float(s) * (1 + 1e-6))
+            assert np.all(codes[p, j, nv:] == 0)
+    untouched = np.setdiff1d(np.arange(k64.shape[0]), ids)
+    assert untouched.size and np.all(codes[untouched] == 0) and np.all(scales[untouched] == 0)
+
+
+def test_int4_quantize_zero_tile_has_unit_scale():
+    x = np.zeros((1, 2, 16, 8))
+    x[0, 1, 3, 2] = -1.5
+    codes, scales = oracle.int4_quantize(x, [0], [16])
+    assert scales[0, 0] == 1.0 and np.all(codes[0, 0] == 0)
+    assert scales[0, 1] == np.float32(1.5) / np.float32(7)
+    assert oracle.int4_unpack(codes)[0, 1, 3, 2] == -7
+
+
+def test_int4_dequantized_attention_is_attention_over_decoded_values():
+    data = mk(B=1, Hq=2, Hkv=1, D=16, lens=(40,), seed=44)
+    ids, val = page_lists(data)
+    kc, ks = oracle.int4_quantize(data.k64(), ids, val)
+    vc, vs = oracle.int4_quantize(data.v64(), ids, val)
+    kd, vd = oracle.int4_dequantize(kc, ks), oracle.int4_dequantize(vc, vs)
+    out, _ = oracle.attention(data.q64(), kd, vd, data.block_table, data.seq_lens, 0.25)
+    for h in range(2):
+        K = gather(kd, data, 0, 0, range(3))
+        V = gather(vd, data, 0, 0, range(3))
+        np.testing.assert_allclose(out[0, h], sdpa(data.q64()[0, h], K, V, 0.25), rtol=1e-12,
+                                   atol=1e-14)
+
+
 # ---------------------------------------------------------------- GPU block cache
 # KVDrive §5.1: a GPU window of critical blocks with lookahead eviction
 
