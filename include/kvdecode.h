@@ -10,6 +10,8 @@
  *                         blocks of the first / last tokens forced in
  *   kv_quantize_pages_fp8 K/V pages -> FP8 E4M3 cold pages with per-page scales
  *   kv_paged_decode_attn_fp8  decode attention over FP8 E4M3 cold pages
+ *   kv_quantize_pages_int4 K/V pages -> INT4 cold pages with per-page scales
+ *   kv_paged_decode_attn_int4 decode attention over INT4 cold pages
  *   kv_cache_plan         GPU block cache: hits, misses and lookahead eviction
  *   kv_cache_fetch        copy only the missing blocks into their cache slots
  *   kv_cached_decode_attn decode attention over the cached blocks, with each
@@ -50,6 +52,7 @@
  *     kmeta    [P, Hkv, 2, D]        dtype   (index 0 = channel min, 1 = channel max)
  *     kmean    [P, Hkv, D]           fp32    (mean key of the page's valid slots)
  *     K8, V8   [P, Hkv, bs, D]       uint8   FP8 E4M3 codes of cold pages
+ *     K4, V4   [P, Hkv, bs, D/2]     uint8   INT4 codes of cold pages, two per byte
  *     kv_scales [P, Hkv, 2]          fp32    (K scale, V scale) of each cold page
  *   GPU block cache with C = num_slots slots per (sequence, KV head):
  *     cache_k, cache_v [B * C, Hkv, bs, D]  dtype  page b*C + s: slot s of sequence b
@@ -322,6 +325,45 @@ kv_status kv_paged_decode_attn_fp8(const kv_shape* shape, const void* q, const u
                                    const int32_t* sel_blocks, const int32_t* sel_count,
                                    int32_t sel_stride, float scale, int32_t num_splits,
                                    float* part_o, float* part_m, float* part_l, void* stream);
+
+/*
+ * INT4 cold pages (KVDrive §11 names INT4 for the cold blocks of its
+ * mixed-precision tiering; DirectKV review, assumption stress test: FP8/INT4
+ * KV).  The pages fix no format; this one is symmetric with one scale per tile.
+ * For i < num_page_ids, every KV head j and tensor X in {K, V}, with
+ * p = page_ids[i] and v = page_valid_tokens[i] in [1, bs]:
+ *   amax = max_{s < v, c} |X[p, j, s, c]|
+ *   kv_scales[p, j, t] = amax / 7 (fp32, correctly rounded; 1 if amax == 0),
+ *                        t = 0 for K, 1 for V
+ *   n[p, j, s, c] = X[p, j, s, c] / scale (fp32, correctly rounded), rounded to
+ *                   nearest with ties to even, clamped to [-7, 7];  0 for s >= v
+ *   X4[p, j, s, c / 2] holds n of channel c in bits 4 * (c mod 2) .. +3, as
+ *                   4-bit two's complement (the even channel in the low nibble).
+ * The value a code stands for is n * scale.  fp16 and bf16 pools only
+ * (KV_ERR_UNSUPPORTED for fp32).  Pages not listed are not touched; the block
+ * index is not affected.
+ */
+kv_status kv_quantize_pages_int4(const kv_shape* shape, const void* k_cache, const void* v_cache,
+                                 const int32_t* page_ids, const int32_t* page_valid_tokens,
+                                 int32_t num_page_ids, uint8_t* k_int4, uint8_t* v_int4,
+                                 float* kv_scales, void* stream);
+
+/*
+ * kv_paged_decode_attn over INT4 cold pages: every K and V value is n * scale
+ * of its (page, KV head), and the call computes exactly what
+ * kv_paged_decode_attn computes over those values (fp32 accumulation; the
+ * codes are exact in the 16-bit operands, the K scale multiplies the logits
+ * and the V scale the softmax weights).  q keeps shape->dtype (fp16 or bf16).
+ * kv_scales must be device memory; with KV_FLAG_HOST_KV the code pools may be
+ * device pointers of kv_host_alloc memory.  kv_auto_num_splits_fp8 serves
+ * these pages too.
+ */
+kv_status kv_paged_decode_attn_int4(const kv_shape* shape, const void* q, const uint8_t* k_int4,
+                                    const uint8_t* v_int4, const float* kv_scales,
+                                    const int32_t* block_table, const int32_t* seq_lens,
+                                    const int32_t* sel_blocks, const int32_t* sel_count,
+                                    int32_t sel_stride, float scale, int32_t num_splits,
+                                    float* part_o, float* part_m, float* part_l, void* stream);
 
 /*
  * GPU-resident block cache with lookahead eviction (KVDrive §5.1: a window of

@@ -89,9 +89,9 @@ size_t scores_bytes(const kv_shape* s) {
   return (size_t)s->num_seqs * s->num_kv_heads * s->max_blocks_per_seq * sizeof(float);
 }
 
-// Validation and launch shared by the 16-bit/fp32 pools and the E4M3 code
-// pools (kv_scales != nullptr).
-kv_status attn_common(const kv_shape* shape, const void* q, const void* k_cache,
+// Validation and launch shared by the 16-bit/fp32 pools (kvq 0) and the code
+// pools (kvq 8: E4M3, kvq 4: INT4; kv_scales != nullptr).
+kv_status attn_common(const kv_shape* shape, int kvq, const void* q, const void* k_cache,
                       const void* v_cache, const float* kv_scales, const int32_t* block_table,
                       const int32_t* seq_lens, const int32_t* sel_blocks,
                       const int32_t* sel_count, int32_t sel_stride, float scale,
@@ -116,12 +116,13 @@ kv_status attn_common(const kv_shape* shape, const void* q, const void* k_cache,
     return fail(KV_ERR_ALIGNMENT, "integer and partial arrays must be 4-byte aligned");
   const int G = shape->num_q_heads / shape->num_kv_heads;
   return hip_status(
-      kvd::launch_paged_attn(shape->dtype, shape->head_dim, G, q, k_cache, v_cache, kv_scales,
-                             block_table, seq_lens, sel_blocks, sel_count, sel_stride, nullptr, 0,
-                             shape->num_seqs, shape->num_q_heads, shape->num_kv_heads,
+      kvd::launch_paged_attn(shape->dtype, shape->head_dim, G, kvq, q, k_cache, v_cache,
+                             kv_scales, block_table, seq_lens, sel_blocks, sel_count, sel_stride,
+                             nullptr, 0, shape->num_seqs, shape->num_q_heads, shape->num_kv_heads,
                              shape->max_blocks_per_seq, num_splits, scale, part_o, part_m, part_l,
                              nullptr, (hipStream_t)stream),
-      kv_scales ? "kv_paged_decode_attn_fp8 launch" : "kv_paged_decode_attn launch");
+      kvq == 8 ? "kv_paged_decode_attn_fp8 launch"
+               : (kvq == 4 ? "kv_paged_decode_attn_int4 launch" : "kv_paged_decode_attn launch"));
 }
 
 }  // namespace
@@ -381,33 +382,60 @@ kv_status kv_paged_decode_attn(const kv_shape* shape, const void* q, const void*
                                const int32_t* sel_count, int32_t sel_stride, float scale,
                                int32_t num_splits, float* part_o, float* part_m, float* part_l,
                                void* stream) {
-  return attn_common(shape, q, k_cache, v_cache, nullptr, block_table, seq_lens, sel_blocks,
+  return attn_common(shape, 0, q, k_cache, v_cache, nullptr, block_table, seq_lens, sel_blocks,
                      sel_count, sel_stride, scale, num_splits, part_o, part_m, part_l, stream);
 }
+
+}  // extern "C"
+
+namespace {
+kv_status quantize_common(const kv_shape* shape, int fmt, const void* k_cache, const void* v_cache,
+                          const int32_t* page_ids, const int32_t* page_valid_tokens,
+                          int32_t num_page_ids, uint8_t* k_codes, uint8_t* v_codes,
+                          float* kv_scales, void* stream, const char* name) {
+  kv_status st = check_shape(shape);
+  if (st != KV_OK) return st;
+  if (fmt == 4 && shape->dtype == KV_F32)
+    return fail(KV_ERR_UNSUPPORTED, "%s: INT4 pages are made from fp16 or bf16 pools", name);
+  if (num_page_ids < 0) return fail(KV_ERR_INVALID_ARG, "num_page_ids=%d < 0", num_page_ids);
+  if (num_page_ids == 0) return ok();
+  if (!k_cache || !v_cache || !page_ids || !page_valid_tokens || !k_codes || !v_codes || !kv_scales)
+    return fail(KV_ERR_INVALID_ARG,
+                "%s: k_cache, v_cache, page_ids, page_valid_tokens, the code pools and kv_scales "
+                "are required", name);
+  if ((long)num_page_ids * shape->num_kv_heads > 0x7fffffffL)
+    return fail(KV_ERR_INVALID_ARG, "num_page_ids * num_kv_heads overflows int32");
+  if (!aligned(k_cache, 16) || !aligned(v_cache, 16) || !aligned(k_codes, 16) ||
+      !aligned(v_codes, 16))
+    return fail(KV_ERR_ALIGNMENT, "k_cache, v_cache and the code pools must be 16-byte aligned");
+  if (!aligned(page_ids, 4) || !aligned(page_valid_tokens, 4) || !aligned(kv_scales, 8))
+    return fail(KV_ERR_ALIGNMENT,
+                "page_ids and page_valid_tokens must be 4-byte aligned, kv_scales 8-byte aligned");
+  std::string what = std::string(name) + " launch";
+  return hip_status(kvd::launch_quantize(fmt, shape->dtype, shape->head_dim, k_cache, v_cache,
+                                         page_ids, page_valid_tokens, num_page_ids,
+                                         shape->num_kv_heads, k_codes, v_codes, kv_scales,
+                                         (hipStream_t)stream),
+                    what.c_str());
+}
+}  // namespace
+
+extern "C" {
 
 kv_status kv_quantize_pages_fp8(const kv_shape* shape, const void* k_cache, const void* v_cache,
                                 const int32_t* page_ids, const int32_t* page_valid_tokens,
                                 int32_t num_page_ids, uint8_t* k_fp8, uint8_t* v_fp8,
                                 float* kv_scales, void* stream) {
-  kv_status st = check_shape(shape);
-  if (st != KV_OK) return st;
-  if (num_page_ids < 0) return fail(KV_ERR_INVALID_ARG, "num_page_ids=%d < 0", num_page_ids);
-  if (num_page_ids == 0) return ok();
-  if (!k_cache || !v_cache || !page_ids || !page_valid_tokens || !k_fp8 || !v_fp8 || !kv_scales)
-    return fail(KV_ERR_INVALID_ARG,
-                "k_cache, v_cache, page_ids, page_valid_tokens, k_fp8, v_fp8 and kv_scales are required");
-  if ((long)num_page_ids * shape->num_kv_heads > 0x7fffffffL)
-    return fail(KV_ERR_INVALID_ARG, "num_page_ids * num_kv_heads overflows int32");
-  if (!aligned(k_cache, 16) || !aligned(v_cache, 16) || !aligned(k_fp8, 16) || !aligned(v_fp8, 16))
-    return fail(KV_ERR_ALIGNMENT, "k_cache, v_cache, k_fp8 and v_fp8 must be 16-byte aligned");
-  if (!aligned(page_ids, 4) || !aligned(page_valid_tokens, 4) || !aligned(kv_scales, 8))
-    return fail(KV_ERR_ALIGNMENT,
-                "page_ids and page_valid_tokens must be 4-byte aligned, kv_scales 8-byte aligned");
-  return hip_status(kvd::launch_quantize_fp8(shape->dtype, shape->head_dim, k_cache, v_cache,
-                                             page_ids, page_valid_tokens, num_page_ids,
-                                             shape->num_kv_heads, k_fp8, v_fp8, kv_scales,
-                                             (hipStream_t)stream),
-                    "kv_quantize_pages_fp8 launch");
+  return quantize_common(shape, 8, k_cache, v_cache, page_ids, page_valid_tokens, num_page_ids,
+                         k_fp8, v_fp8, kv_scales, stream, "kv_quantize_pages_fp8");
+}
+
+kv_status kv_quantize_pages_int4(const kv_shape* shape, const void* k_cache, const void* v_cache,
+                                 const int32_t* page_ids, const int32_t* page_valid_tokens,
+                                 int32_t num_page_ids, uint8_t* k_int4, uint8_t* v_int4,
+                                 float* kv_scales, void* stream) {
+  return quantize_common(shape, 4, k_cache, v_cache, page_ids, page_valid_tokens, num_page_ids,
+                         k_int4, v_int4, kv_scales, stream, "kv_quantize_pages_int4");
 }
 
 kv_status kv_paged_decode_attn_fp8(const kv_shape* shape, const void* q, const uint8_t* k_fp8,
@@ -420,7 +448,23 @@ kv_status kv_paged_decode_attn_fp8(const kv_shape* shape, const void* q, const u
   if (st != KV_OK) return st;
   if (!kv_scales) return fail(KV_ERR_INVALID_ARG, "kv_scales is required");
   if (!aligned(kv_scales, 8)) return fail(KV_ERR_ALIGNMENT, "kv_scales must be 8-byte aligned");
-  return attn_common(shape, q, k_fp8, v_fp8, kv_scales, block_table, seq_lens, sel_blocks,
+  return attn_common(shape, 8, q, k_fp8, v_fp8, kv_scales, block_table, seq_lens, sel_blocks,
+                     sel_count, sel_stride, scale, num_splits, part_o, part_m, part_l, stream);
+}
+
+kv_status kv_paged_decode_attn_int4(const kv_shape* shape, const void* q, const uint8_t* k_int4,
+                                    const uint8_t* v_int4, const float* kv_scales,
+                                    const int32_t* block_table, const int32_t* seq_lens,
+                                    const int32_t* sel_blocks, const int32_t* sel_count,
+                                    int32_t sel_stride, float scale, int32_t num_splits,
+                                    float* part_o, float* part_m, float* part_l, void* stream) {
+  kv_status st = check_shape(shape);
+  if (st != KV_OK) return st;
+  if (shape->dtype == KV_F32)
+    return fail(KV_ERR_UNSUPPORTED, "INT4 pages are read with fp16 or bf16 queries");
+  if (!kv_scales) return fail(KV_ERR_INVALID_ARG, "kv_scales is required");
+  if (!aligned(kv_scales, 8)) return fail(KV_ERR_ALIGNMENT, "kv_scales must be 8-byte aligned");
+  return attn_common(shape, 4, q, k_int4, v_int4, kv_scales, block_table, seq_lens, sel_blocks,
                      sel_count, sel_stride, scale, num_splits, part_o, part_m, part_l, stream);
 }
 
@@ -532,7 +576,7 @@ kv_status kv_cached_decode_attn(const kv_shape* shape, int32_t num_slots, const 
   cs.flags = 0;
   const int G = shape->num_q_heads / shape->num_kv_heads;
   return hip_status(
-      kvd::launch_paged_attn(cs.dtype, cs.head_dim, G, q, cache_k, cache_v, nullptr,
+      kvd::launch_paged_attn(cs.dtype, cs.head_dim, G, 0, q, cache_k, cache_v, nullptr,
                              /*block_table=*/nullptr, seq_lens, sel_blocks, sel_count,
                              sel_stride, sel_slots, num_slots, cs.num_seqs, cs.num_q_heads,
                              cs.num_kv_heads, cs.max_blocks_per_seq, num_splits, scale, part_o,

@@ -5,10 +5,11 @@
 //   paged_attn_mfma_kernel  the same on the matrix cores (16-bit q, G >= 2)
 //   combine_kernel      log-sum-exp merge of the split partials
 //
-// Both attention kernels also read FP8 E4M3 cold pages (KV8): one code byte
-// per channel plus one fp32 scale per (page, KV head) and tensor (KVDrive §11;
-// DirectKV review, assumption stress test).  Codes are decoded in registers;
-// the K scale multiplies the page's logits and the V scale its softmax weights.
+// Both attention kernels also read quantised cold pages (KVQ = 8: FP8 E4M3,
+// one code byte per channel; KVQ = 4: INT4, two codes per byte) with one fp32
+// scale per (page, KV head) and tensor (KVDrive §11; DirectKV review,
+// assumption stress test).  Codes are decoded in registers; the K scale
+// multiplies the page's logits and the V scale its softmax weights.
 //
 // Each K/V byte is read exactly once; nothing is re-read from another
 // workgroup, so the blockIdx -> XCD placement carries no L2 reuse to exploit.
@@ -49,20 +50,32 @@ namespace kvd {
 // split are fetched once (one per lane) and broadcast with readlane, so the
 // K/V loads never wait on a table lookup.
 
+// Bytes of x channels of a pool row: the storage dtype, or code bytes (KVQ 8:
+// one per channel; KVQ 4: one per two channels -- x is always even there).
+template <typename DT, int KVQ>
+__host__ __device__ constexpr size_t kv_bytes(size_t x) {
+  return KVQ == 0 ? x * sizeof(typename DT::storage) : (KVQ == 8 ? x : x / 2);
+}
+
 // A lane's chunk of one K or V row: E channels as 16 bytes of the storage
-// dtype, or (KV8) as E code bytes.
-template <typename DT, bool KV8>
+// dtype, or E codes (KVQ 8: E bytes; KVQ 4: E/2 bytes, 16-bit dtypes only).
+template <typename DT, int KVQ>
 struct KVChunk {
   using raw = uint4;
-  static constexpr int EB = sizeof(typename DT::storage);   // bytes per channel
   __device__ static inline raw load(const uint8_t* p) { return load16_stream(p); }
   __device__ static inline void widen(const raw& w, float* f) { DT::widen(w, f); }
 };
 template <typename DT>
-struct KVChunk<DT, true> {
+struct KVChunk<DT, 4> {
+  static_assert(DT::E == 8, "INT4 pages hold 16-bit channels");
+  using raw = uint32_t;
+  __device__ static inline raw load(const uint8_t* p) { return load4_stream(p); }
+  __device__ static inline void widen(const raw& w, float* f) { int4x8_to_f32(w, f); }
+};
+template <typename DT>
+struct KVChunk<DT, 8> {
   static constexpr int E = DT::E;
   using raw = typename std::conditional<E == 8, uint2, uint32_t>::type;
-  static constexpr int EB = 1;
   __device__ static inline raw load(const uint8_t* p) {
     if constexpr (E == 8) return load8_stream(p);
     else return load4_stream(p);
@@ -81,7 +94,7 @@ __device__ inline float readlane_f(float v, int lane) {
   return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), lane));
 }
 
-template <typename DT, int D, int G, int WAVES, bool SPARSE, bool KV8>
+template <typename DT, int D, int G, int WAVES, bool SPARSE, int KVQ>
 __global__ __launch_bounds__(WAVES * kWave) void paged_attn_kernel(
     const void* __restrict__ q, const void* __restrict__ k_cache, const void* __restrict__ v_cache,
     const float* __restrict__ kv_scales, const int32_t* __restrict__ block_table,
@@ -91,8 +104,8 @@ __global__ __launch_bounds__(WAVES * kWave) void paged_attn_kernel(
     float* __restrict__ part_m, float* __restrict__ part_l, float* __restrict__ block_lse) {
   using G_ = RowGeom<DT, D>;
   using St = typename DT::storage;
-  using KC = KVChunk<DT, KV8>;
-  constexpr int E = G_::E, LPR = G_::LPR, TPI = G_::TPI, NI = G_::NI, EB = KC::EB;
+  using KC = KVChunk<DT, KVQ>;
+  constexpr int E = G_::E, LPR = G_::LPR, TPI = G_::TPI, NI = G_::NI;
   const int lane = threadIdx.x & (kWave - 1);
   const int s = blockIdx.x * WAVES + (threadIdx.x >> 6);
   if (s >= S) return;
@@ -123,10 +136,10 @@ __global__ __launch_bounds__(WAVES * kWave) void paged_attn_kernel(
     for (int e = 0; e < E; ++e) acc[g][e] = 0.0f;
   }
 
-  // byte addressing: EB bytes per channel (1 for code pages)
-  const size_t page_stride = (size_t)Hkv * kBlockSize * D * EB;
-  const size_t lane_off = (((size_t)j * kBlockSize + rg) * D + (size_t)c * E) * EB;
-  const size_t row_step = (size_t)TPI * D * EB;
+  // byte addressing (code pages: fewer bytes per channel)
+  const size_t page_stride = kv_bytes<DT, KVQ>((size_t)Hkv * kBlockSize * D);
+  const size_t lane_off = kv_bytes<DT, KVQ>(((size_t)j * kBlockSize + rg) * D + (size_t)c * E);
+  const size_t row_step = kv_bytes<DT, KVQ>((size_t)TPI * D);
   const uint8_t* kb = static_cast<const uint8_t*>(k_cache) + lane_off;
   const uint8_t* vb = static_cast<const uint8_t*>(v_cache) + lane_off;
   const int32_t* sel_row = SPARSE ? sel + ((size_t)b * Hkv + j) * sel_stride : nullptr;
@@ -143,7 +156,7 @@ __global__ __launch_bounds__(WAVES * kWave) void paged_attn_kernel(
       // cached list: the block sits in slot sel_slots[.] of cache page b*C + slot
       my_page = slots_row ? b * num_slots + slots_row[base + lane] : bt_row[n];
       my_valid = min(kBlockSize, L - n * kBlockSize);
-      if constexpr (KV8) {
+      if constexpr (KVQ != 0) {
         const float2 sc = *reinterpret_cast<const float2*>(kv_scales + ((size_t)my_page * Hkv + j) * 2);
         my_sk = sc.x;
         my_sv = sc.y;
@@ -164,8 +177,8 @@ __global__ __launch_bounds__(WAVES * kWave) void paged_attn_kernel(
       const typename KC::raw* kc = cur.k;
       const typename KC::raw* vc = cur.v;
       const int valid = readlane(my_valid, i);
-      const float sk = KV8 ? readlane_f(my_sk, i) : 1.0f;
-      const float sv = KV8 ? readlane_f(my_sv, i) : 1.0f;
+      const float sk = KVQ ? readlane_f(my_sk, i) : 1.0f;
+      const float sv = KVQ ? readlane_f(my_sv, i) : 1.0f;
 
       // logits (log2 units) of the lane's NI tokens for every head
       float z[NI][G];
@@ -179,7 +192,7 @@ __global__ __launch_bounds__(WAVES * kWave) void paged_attn_kernel(
 #pragma unroll
           for (int e = 0; e < E; ++e) a = fmaf(qf[g][e], kf[e], a);
           z[it][g] = group_reduce<LPR, OpSum>(a);
-          if constexpr (KV8) z[it][g] *= sk;
+          if constexpr (KVQ != 0) z[it][g] *= sk;
         }
         if (it * TPI + rg >= valid) {
 #pragma unroll
@@ -223,7 +236,7 @@ __global__ __launch_bounds__(WAVES * kWave) void paged_attn_kernel(
           const float p = fast_exp2(z[it][g] - m[g]);
           lsum[g] += p;
           if constexpr (SPARSE) psum[g] += p;
-          const float pv = KV8 ? p * sv : p;
+          const float pv = KVQ ? p * sv : p;
 #pragma unroll
           for (int e = 0; e < E; ++e) acc[g][e] = fmaf(pv, vf[e], acc[g][e]);
         }
@@ -387,17 +400,45 @@ struct RowWords {
   }
 };
 
-// With code pages (KV8) lane (col, grp) reads 16 K codes at a time: channels
-// 64*sp + 16*grp .. +16 of token col feed QK steps 2*sp (first 8) and 2*sp+1
-// (next 8).  The QK sum runs over all channels in any order, so q's B operand
-// simply uses the same channel assignment.  V codes come as D/16 bytes per
-// token and decode into the 16-bit words the repack expects.
-template <bool KV8>
-__device__ inline int qk_channel(int st, int grp) {
-  return KV8 ? 64 * (st >> 1) + 16 * grp + 8 * (st & 1) : 8 * (4 * st + grp);
+// Eight INT4 codes (one dword) as eight 16-bit values (four dwords), and four
+// (the low 16 bits) as two dwords; exact.
+template <typename DT>
+__device__ inline uint32_t pack16_exact(float a, float b);
+template <>
+__device__ inline uint32_t pack16_exact<BF16>(float a, float b) {
+  return __builtin_amdgcn_perm(__float_as_uint(b), __float_as_uint(a), 0x07060302u);
+}
+template <>
+__device__ inline uint32_t pack16_exact<F16>(float a, float b) {
+  return F16::pack2(a, b);
+}
+template <typename DT>
+__device__ inline uint4 int4x8_to_16(uint32_t w) {
+  float f[8];
+  int4x8_to_f32(w, f);
+  return make_uint4(pack16_exact<DT>(f[0], f[1]), pack16_exact<DT>(f[2], f[3]),
+                    pack16_exact<DT>(f[4], f[5]), pack16_exact<DT>(f[6], f[7]));
+}
+template <typename DT>
+__device__ inline uint2 int4x4_to_16(uint32_t w) {
+  return make_uint2(pack16_exact<DT>((float)int4_code(w, 0), (float)int4_code(w, 1)),
+                    pack16_exact<DT>((float)int4_code(w, 2), (float)int4_code(w, 3)));
 }
 
-template <typename DT, int D, int G, int WAVES, bool SPARSE, bool KV8>
+// With FP8 code pages (KVQ 8) lane (col, grp) reads 16 K codes at a time:
+// channels 64*sp + 16*grp .. +16 of token col feed QK steps 2*sp (first 8) and
+// 2*sp+1 (next 8).  With INT4 pages (KVQ 4) it reads its quarter of the row at
+// once: channels D/4*grp .. +D/4, eight per QK step.  The QK sum runs over all
+// channels in any order, so q's B operand simply uses the same channel
+// assignment.  V codes come as D/16 codes per token and decode into the 16-bit
+// words the repack expects.
+template <int KVQ, int D>
+__device__ inline int qk_channel(int st, int grp) {
+  return KVQ == 8 ? 64 * (st >> 1) + 16 * grp + 8 * (st & 1)
+                  : (KVQ == 4 ? D / 4 * grp + 8 * st : 8 * (4 * st + grp));
+}
+
+template <typename DT, int D, int G, int WAVES, bool SPARSE, int KVQ>
 __global__ __launch_bounds__(WAVES * kWave) KVD_MFMA_OCCUPANCY void paged_attn_mfma_kernel(
     const void* __restrict__ q, const void* __restrict__ k_cache, const void* __restrict__ v_cache,
     const float* __restrict__ kv_scales, const int32_t* __restrict__ block_table,
@@ -428,7 +469,7 @@ __global__ __launch_bounds__(WAVES * kWave) KVD_MFMA_OCCUPANCY void paged_attn_m
   uint4 qB[KS];
 #pragma unroll
   for (int st = 0; st < KS; ++st)
-    qB[st] = col < G ? load16(static_cast<const St*>(q) + (row0 + col) * D + qk_channel<KV8>(st, grp))
+    qB[st] = col < G ? load16(static_cast<const St*>(q) + (row0 + col) * D + qk_channel<KVQ, D>(st, grp))
                      : make_uint4(0, 0, 0, 0);
 
   f32x4_v o[NT];
@@ -436,13 +477,14 @@ __global__ __launch_bounds__(WAVES * kWave) KVD_MFMA_OCCUPANCY void paged_attn_m
   for (int n = 0; n < NT; ++n) o[n] = f32x4_v{0.f, 0.f, 0.f, 0.f};
   float m = -INFINITY, lsum = 0.0f;
 
-  // byte addressing: EB bytes per channel (1 for code pages)
-  constexpr int EB = KV8 ? 1 : (int)sizeof(St);
-  const size_t page_stride = (size_t)Hkv * kBlockSize * D * EB;
+  // byte addressing (code pages: fewer bytes per channel)
+  constexpr int KCH = KVQ == 8 ? 16 : (KVQ == 4 ? D / 4 : 8);   // K channels a lane starts at, per grp
+  const size_t page_stride = kv_bytes<DT, KVQ>((size_t)Hkv * kBlockSize * D);
   const uint8_t* kb = static_cast<const uint8_t*>(k_cache) +
-                      ((size_t)j * kBlockSize * D + (size_t)col * D + (KV8 ? 16 : 8) * grp) * EB;
+                      kv_bytes<DT, KVQ>((size_t)j * kBlockSize * D + (size_t)col * D + KCH * grp);
   const uint8_t* vb = static_cast<const uint8_t*>(v_cache) +
-                      ((size_t)j * kBlockSize * D + (size_t)(4 * grp) * D + 2 * NDW * col) * EB;
+                      kv_bytes<DT, KVQ>((size_t)j * kBlockSize * D + (size_t)(4 * grp) * D +
+                                        2 * NDW * col);
   const int32_t* sel_row = SPARSE ? sel + ((size_t)b * Hkv + j) * sel_stride : nullptr;
   const int32_t* slots_row = (SPARSE && sel_slots) ? sel_slots + ((size_t)b * Hkv + j) * sel_stride
                                                    : nullptr;
@@ -457,14 +499,15 @@ __global__ __launch_bounds__(WAVES * kWave) KVD_MFMA_OCCUPANCY void paged_attn_m
       // cached list: the block sits in slot sel_slots[.] of cache page b*C + slot
       my_page = slots_row ? b * num_slots + slots_row[base + lane] : bt_row[n];
       my_valid = min(kBlockSize, L - n * kBlockSize);
-      if constexpr (KV8) {
+      if constexpr (KVQ != 0) {
         const float2 sc = *reinterpret_cast<const float2*>(kv_scales + ((size_t)my_page * Hkv + j) * 2);
         my_sk = sc.x;
         my_sv = sc.y;
       }
     }
-    // raw registers of one page: 16-bit rows, or E4M3 codes (K: 16 per load,
-    // V: D/16 per token row, NDW/2 dwords)
+    // raw registers of one page: 16-bit rows, E4M3 codes (K: 16 per load,
+    // V: D/16 per token row, NDW/2 dwords), or INT4 codes (K: D/4 per lane in
+    // one load, one dword per QK step; V: D/16 per token row in 4 or 2 bytes)
     struct PageRegs16 {
       uint4 k[KS];
       RowWords<NDW> v[4];
@@ -473,10 +516,28 @@ __global__ __launch_bounds__(WAVES * kWave) KVD_MFMA_OCCUPANCY void paged_attn_m
       uint4 k[KS / 2];
       uint32_t v[4][NDW / 2];
     };
-    using PageRegs = typename std::conditional<KV8, PageRegs8, PageRegs16>::type;
+    struct PageRegs4 {
+      uint32_t k[KS];
+      uint32_t v[4];
+    };
+    using PageRegs = typename std::conditional<
+        KVQ == 8, PageRegs8, typename std::conditional<KVQ == 4, PageRegs4, PageRegs16>::type>::type;
     auto load_page = [&](PageRegs& r, int idx) {
       const size_t off = (size_t)readlane(my_page, idx) * page_stride;
-      if constexpr (KV8) {
+      if constexpr (KVQ == 4) {
+        if constexpr (KS == 4) {
+          const uint4 t = load16_stream(kb + off);
+          r.k[0] = t.x; r.k[1] = t.y; r.k[2] = t.z; r.k[3] = t.w;
+        } else {
+          const uint2 t = load8_stream(kb + off);
+          r.k[0] = t.x; r.k[1] = t.y;
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          if constexpr (NDW == 4) r.v[i] = load4_stream(vb + off + (size_t)i * (D / 2));
+          else r.v[i] = load2_stream(vb + off + (size_t)i * (D / 2));
+        }
+      } else if constexpr (KVQ == 8) {
 #pragma unroll
         for (int sp = 0; sp < KS / 2; ++sp) r.k[sp] = load16_stream(kb + off + 64 * sp);
 #pragma unroll
@@ -491,21 +552,34 @@ __global__ __launch_bounds__(WAVES * kWave) KVD_MFMA_OCCUPANCY void paged_attn_m
         }
       } else {
 #pragma unroll
-        for (int st = 0; st < KS; ++st) r.k[st] = load16_stream(kb + off + 32 * st * EB);
+        for (int st = 0; st < KS; ++st) r.k[st] = load16_stream(kb + off + kv_bytes<DT, 0>(32 * st));
 #pragma unroll
-        for (int i = 0; i < 4; ++i) r.v[i].load(vb + off + (size_t)i * D * EB);
+        for (int i = 0; i < 4; ++i) r.v[i].load(vb + off + kv_bytes<DT, 0>((size_t)i * D));
       }
     };
     // one page of compute; `cur` holds page `it` of the group
     auto process = [&](const PageRegs& cur, int it) {
       const int valid = readlane(my_valid, it);
-      const float sk = KV8 ? readlane_f(my_sk, it) : 1.0f;
-      const float sv = KV8 ? readlane_f(my_sv, it) : 1.0f;
+      const float sk = KVQ ? readlane_f(my_sk, it) : 1.0f;
+      const float sv = KVQ ? readlane_f(my_sv, it) : 1.0f;
 
       // 16-bit operands of the page
       uint4 kA[KS];
       RowWords<NDW> vr[4];
-      if constexpr (KV8) {
+      if constexpr (KVQ == 4) {
+#pragma unroll
+        for (int st = 0; st < KS; ++st) kA[st] = int4x8_to_16<DT>(cur.k[st]);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          if constexpr (NDW == 4) {
+            const uint4 t = int4x8_to_16<DT>(cur.v[i]);
+            vr[i].w[0] = t.x; vr[i].w[1] = t.y; vr[i].w[2] = t.z; vr[i].w[3] = t.w;
+          } else {
+            const uint2 t = int4x4_to_16<DT>(cur.v[i]);
+            vr[i].w[0] = t.x; vr[i].w[1] = t.y;
+          }
+        }
+      } else if constexpr (KVQ == 8) {
 #pragma unroll
         for (int sp = 0; sp < KS / 2; ++sp) {
           const uint2 a0 = fp8x4_to_16<DT>(cur.k[sp].x), a1 = fp8x4_to_16<DT>(cur.k[sp].y);
@@ -562,7 +636,7 @@ __global__ __launch_bounds__(WAVES * kWave) KVD_MFMA_OCCUPANCY void paged_attn_m
         if (grp == 0 && col < G)
           block_lse[(row0 + col) * sel_stride + base + it] = (m + __log2f(ps)) * kLn2;
       }
-      if constexpr (KV8) {    // the page's V scale rides on its weights
+      if constexpr (KVQ != 0) {    // the page's V scale rides on its weights
 #pragma unroll
         for (int i = 0; i < 4; ++i) p[i] *= sv;
       }
@@ -701,8 +775,8 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
 // ============================================================== launchers
 
 
-hipError_t launch_paged_attn(int dtype, int D, int G, const void* q, const void* k_cache,
-                             const void* v_cache, const float* kv_scales,
+hipError_t launch_paged_attn(int dtype, int D, int G, int kvq, const void* q,
+                             const void* k_cache, const void* v_cache, const float* kv_scales,
                              const int32_t* block_table, const int32_t* seq_lens,
                              const int32_t* sel, const int32_t* sel_count, int sel_stride,
                              const int32_t* sel_slots, int num_slots, int B, int Hq, int Hkv,
@@ -716,27 +790,38 @@ hipError_t launch_paged_attn(int dtype, int D, int G, const void* q, const void*
       return with_group(G, [&](auto g) {
         using DT = decltype(dt);
         constexpr int DD = decltype(d)::value, GG = decltype(g)::value;
-        auto go = [&](auto sparse, auto kv8) {
-          constexpr bool SP = decltype(sparse)::value, K8 = decltype(kv8)::value;
-          if constexpr (!std::is_same_v<DT, F32> && GG >= 2) {
-            hipLaunchKernelGGL((paged_attn_mfma_kernel<DT, DD, GG, WAVES, SP, K8>), grid,
+        auto go = [&](auto sparse, auto fmt) {
+          constexpr bool SP = decltype(sparse)::value;
+          constexpr int KQ = decltype(fmt)::value;
+          if constexpr (KQ == 4 && std::is_same_v<DT, F32>) {
+            return;                           // INT4 pages: 16-bit dtypes only
+          } else if constexpr (!std::is_same_v<DT, F32> && GG >= 2) {
+            hipLaunchKernelGGL((paged_attn_mfma_kernel<DT, DD, GG, WAVES, SP, KQ>), grid,
                                dim3(WAVES * kWave), 0, stream, q, k_cache, v_cache, kv_scales,
                                block_table, seq_lens, sel, sel_count, sel_stride, sel_slots,
                                num_slots, Hq, Hkv, maxN, S, qscale, part_o, part_m, part_l,
                                block_lse);
           } else {
-            hipLaunchKernelGGL((paged_attn_kernel<DT, DD, GG, WAVES, SP, K8>), grid,
+            hipLaunchKernelGGL((paged_attn_kernel<DT, DD, GG, WAVES, SP, KQ>), grid,
                                dim3(WAVES * kWave), 0, stream, q, k_cache, v_cache, kv_scales,
                                block_table, seq_lens, sel, sel_count, sel_stride, sel_slots,
                                num_slots, Hq, Hkv, maxN, S, qscale, part_o, part_m, part_l,
                                block_lse);
           }
         };
-        // kv_scales marks code pages
-        if (sel && kv_scales) go(std::true_type{}, std::true_type{});
-        else if (sel) go(std::true_type{}, std::false_type{});
-        else if (kv_scales) go(std::false_type{}, std::true_type{});
-        else go(std::false_type{}, std::false_type{});
+        using C0 = std::integral_constant<int, 0>;
+        using C8 = std::integral_constant<int, 8>;
+        using C4 = std::integral_constant<int, 4>;
+        if (kvq == 4 && std::is_same_v<DT, F32>) return hipErrorInvalidValue;
+        if (sel) {
+          if (kvq == 8) go(std::true_type{}, C8{});
+          else if (kvq == 4) go(std::true_type{}, C4{});
+          else go(std::true_type{}, C0{});
+        } else {
+          if (kvq == 8) go(std::false_type{}, C8{});
+          else if (kvq == 4) go(std::false_type{}, C4{});
+          else go(std::false_type{}, C0{});
+        }
         return hipGetLastError();
       });
     });

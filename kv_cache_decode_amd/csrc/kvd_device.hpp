@@ -113,6 +113,13 @@ __device__ inline uint32_t load4_stream(const void* p) {
   return *reinterpret_cast<const unsigned int*>(p);
 #endif
 }
+__device__ inline uint32_t load2_stream(const void* p) {
+#if KVD_NT_LOADS
+  return __builtin_nontemporal_load(reinterpret_cast<const unsigned short*>(p));
+#else
+  return *reinterpret_cast<const unsigned short*>(p);
+#endif
+}
 __device__ inline void store16(void* p, const uint4& v) { *reinterpret_cast<uint4*>(p) = v; }
 
 // ---------------------------------------------------------------- FP8 E4M3 pages
@@ -148,6 +155,28 @@ __device__ inline uint32_t fp8_encode(float y) {
   else if (a < 0x3c800000u) code = (uint32_t)__builtin_rintf(__uint_as_float(a) * 512.0f);
   else code = ((a + 0x7ffffu + ((a >> 20) & 1u)) >> 20) - (120u << 3);
   return sign | code;
+}
+
+// ---------------------------------------------------------------- INT4 pages
+//
+// Cold K/V pages may hold symmetric INT4 codes n in [-7, 7] (two per byte,
+// 4-bit two's complement, the even channel in the low nibble) with one fp32
+// scale per (page, KV head) and tensor.  Small integers are exact in fp32,
+// bf16 and fp16.
+
+// Code e (0..7) of a dword of eight nibbles, sign-extended.
+__device__ inline int int4_code(uint32_t w, int e) { return (int)(w << (28 - 4 * e)) >> 28; }
+
+__device__ inline void int4x8_to_f32(uint32_t w, float* f) {
+#pragma unroll
+  for (int e = 0; e < 8; ++e) f[e] = (float)int4_code(w, e);
+}
+
+// Round an fp32 quotient x / scale to an INT4 code: nearest, ties to even,
+// clamped to [-7, 7]; returned as its nibble.
+__device__ inline uint32_t int4_encode(float y) {
+  const float r = fminf(fmaxf(__builtin_rintf(y), -7.0f), 7.0f);
+  return (uint32_t)(int)r & 15u;
 }
 
 // ---------------------------------------------------------------- lane shuffles

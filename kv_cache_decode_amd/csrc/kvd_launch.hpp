@@ -39,8 +39,10 @@ hipError_t launch_topk(const float* scores, const int32_t* seq_lens, int B, int 
 // fp32 (k, v) scales per (page, KV head)
 // sel_slots (with sel): the list's blocks live in cache page b*num_slots + slot;
 // block_lse (with sel, nullable): ln of each list block's summed exp-logits per query head
-hipError_t launch_paged_attn(int dtype, int D, int G, const void* q, const void* k_cache,
-                             const void* v_cache, const float* kv_scales,
+// kvq: 0 = pools of the storage dtype, 8 = FP8 E4M3 code pools, 4 = INT4 code
+// pools (16-bit dtypes); code pools need kv_scales
+hipError_t launch_paged_attn(int dtype, int D, int G, int kvq, const void* q,
+                             const void* k_cache, const void* v_cache, const float* kv_scales,
                              const int32_t* block_table, const int32_t* seq_lens,
                              const int32_t* sel, const int32_t* sel_count, int sel_stride,
                              const int32_t* sel_slots, int num_slots, int B, int Hq, int Hkv,
@@ -75,10 +77,10 @@ constexpr int kProbeSinkWords = 4096;
 // Largest cache (slots per sequence and KV head) the plan kernel holds.
 constexpr int kCacheMaxSlots = 8192;
 
-hipError_t launch_quantize_fp8(int dtype, int D, const void* k_cache, const void* v_cache,
-                               const int32_t* page_ids, const int32_t* valid_tokens, int n_ids,
-                               int Hkv, uint8_t* k8, uint8_t* v8, float* scales,
-                               hipStream_t stream);
+// fmt 8: FP8 E4M3 pages; fmt 4: INT4 pages (16-bit sources only)
+hipError_t launch_quantize(int fmt, int dtype, int D, const void* k_cache, const void* v_cache,
+                           const int32_t* page_ids, const int32_t* valid_tokens, int n_ids,
+                           int Hkv, uint8_t* k8, uint8_t* v8, float* scales, hipStream_t stream);
 
 hipError_t launch_combine(int D, const float* part_o, const float* part_m, const float* part_l,
                           int rows, int S, float* out, float* lse, hipStream_t stream);

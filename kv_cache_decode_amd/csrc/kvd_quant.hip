@@ -1,9 +1,12 @@
-// gfx950 kernel that turns K/V pages into FP8 E4M3 cold pages.
+// gfx950 kernel that turns K/V pages into quantised cold pages.
 //
-//   quantize_fp8_kernel  per (page, KV head): amax of the valid slots, scale
-//                        amax / 448, codes round-to-nearest-even(x / scale)
-//                        KVDrive §11 (cold blocks quantised, hot blocks kept in
-//                        high precision); DirectKV review, assumption stress test
+//   quantize_kernel<FP8>   per (page, KV head): amax of the valid slots, scale
+//                          amax / 448, E4M3 codes round-to-nearest-even(x / scale)
+//   quantize_kernel<INT4>  scale amax / 7, codes round-half-even(x / scale)
+//                          clamped to [-7, 7], two per byte
+//                          KVDrive §11 (cold blocks quantised, hot blocks kept in
+//                          high precision); DirectKV review, assumption stress test
+//                          (FP8/INT4 KV)
 //
 // The E4M3 format is the OCP 8-bit floating-point one (bias 7, no infinities,
 // largest finite value 448).  Scale and quotient are correctly rounded fp32
@@ -39,14 +42,19 @@ __device__ inline void store_codes(uint8_t* dst, const CodeChunk<E>& cc) {
 // 64 / LPR consecutive units.  The lane keeps the unit's 16 rows of its chunk
 // in registers, the LPR lanes of the unit reduce the amax, and every lane then
 // encodes and stores its own chunk.  K and V are done one after the other.
-template <typename DT, int D, int WAVES>
-__global__ __launch_bounds__(WAVES * kWave) void quantize_fp8_kernel(
+constexpr int kFmtFp8 = 8, kFmtInt4 = 4;
+
+template <typename DT, int D, int WAVES, int FMT>
+__global__ __launch_bounds__(WAVES * kWave) void quantize_kernel(
     const void* __restrict__ k_cache, const void* __restrict__ v_cache,
     const int32_t* __restrict__ page_ids, const int32_t* __restrict__ valid_tokens, int n_ids,
     int Hkv, uint8_t* __restrict__ k8, uint8_t* __restrict__ v8, float* __restrict__ scales) {
   using G_ = RowGeom<DT, D>;
   using St = typename DT::storage;
   constexpr int E = G_::E, LPR = G_::LPR;
+  static_assert(FMT == kFmtFp8 || E == 8, "INT4 pages hold 16-bit sources (8 channels per lane)");
+  // code bytes per row and per lane chunk
+  constexpr int RB = FMT == kFmtFp8 ? D : D / 2, CB = FMT == kFmtFp8 ? E : E / 2;
   constexpr int UPS = kWave / LPR;
   const int lane = threadIdx.x & (kWave - 1);
   const int us = lane / LPR, c = lane % LPR;
@@ -65,7 +73,7 @@ __global__ __launch_bounds__(WAVES * kWave) void quantize_fp8_kernel(
     for (int t = 0; t < 2; ++t) {
       const St* src = static_cast<const St*>(t ? v_cache : k_cache) + tile * kBlockSize * D +
                       (size_t)c * E;
-      uint8_t* dst = (t ? v8 : k8) + tile * kBlockSize * D + (size_t)c * E;
+      uint8_t* dst = (t ? v8 : k8) + tile * kBlockSize * RB + (size_t)c * CB;
       uint4 w[kBlockSize];
 #pragma unroll
       for (int r = 0; r < kBlockSize; ++r) w[r] = load16_stream(src + (size_t)r * D);
@@ -80,29 +88,40 @@ __global__ __launch_bounds__(WAVES * kWave) void quantize_fp8_kernel(
         }
       }
       amax = group_reduce<LPR, OpMax>(amax);
-      const float sc = amax > 0.0f ? __fdiv_rn(amax, 448.0f) : 1.0f;
+      const float sc = amax > 0.0f ? __fdiv_rn(amax, FMT == kFmtFp8 ? 448.0f : 7.0f) : 1.0f;
 #pragma unroll
       for (int r = 0; r < kBlockSize; ++r) {
-        CodeChunk<E> cc;
+        if constexpr (FMT == kFmtFp8) {
+          CodeChunk<E> cc;
 #pragma unroll
-        for (int k = 0; k < E / 4; ++k) cc.w[k] = 0u;
-        if (r < nv) {
-          float f[E];
-          DT::widen(w[r], f);
+          for (int k = 0; k < E / 4; ++k) cc.w[k] = 0u;
+          if (r < nv) {
+            float f[E];
+            DT::widen(w[r], f);
 #pragma unroll
-          for (int e = 0; e < E; ++e) cc.w[e / 4] |= fp8_encode(__fdiv_rn(f[e], sc)) << (8 * (e % 4));
+            for (int e = 0; e < E; ++e)
+              cc.w[e / 4] |= fp8_encode(__fdiv_rn(f[e], sc)) << (8 * (e % 4));
+          }
+          store_codes<E>(dst + (size_t)r * RB, cc);
+        } else {
+          uint32_t cw = 0u;                  // eight nibbles, channel e in bits 4e..4e+3
+          if (r < nv) {
+            float f[E];
+            DT::widen(w[r], f);
+#pragma unroll
+            for (int e = 0; e < E; ++e) cw |= int4_encode(__fdiv_rn(f[e], sc)) << (4 * e);
+          }
+          *reinterpret_cast<uint32_t*>(dst + (size_t)r * RB) = cw;
         }
-        store_codes<E>(dst + (size_t)r * D, cc);
       }
       if (c == 0) scales[tile * 2 + t] = sc;
     }
   }
 }
 
-hipError_t launch_quantize_fp8(int dtype, int D, const void* k_cache, const void* v_cache,
-                               const int32_t* page_ids, const int32_t* valid_tokens, int n_ids,
-                               int Hkv, uint8_t* k8, uint8_t* v8, float* scales,
-                               hipStream_t stream) {
+hipError_t launch_quantize(int fmt, int dtype, int D, const void* k_cache, const void* v_cache,
+                           const int32_t* page_ids, const int32_t* valid_tokens, int n_ids,
+                           int Hkv, uint8_t* k8, uint8_t* v8, float* scales, hipStream_t stream) {
   if (n_ids <= 0) return hipSuccess;
   return with_dtype(dtype, [&](auto dt) {
     return with_dim(D, [&](auto d) {
@@ -113,9 +132,17 @@ hipError_t launch_quantize_fp8(int dtype, int D, const void* k_cache, const void
       const long steps = ((long)n_ids * Hkv + UPS - 1) / UPS;
       const long want = (steps + WAVES - 1) / WAVES;
       const int grid = (int)std::min<long>(want, (long)cu_count() * KVD_QUANT_WGS_PER_CU);
-      hipLaunchKernelGGL((quantize_fp8_kernel<DT, DD, WAVES>), dim3(grid), dim3(WAVES * kWave),
-                         0, stream, k_cache, v_cache, page_ids, valid_tokens, n_ids, Hkv, k8, v8,
-                         scales);
+      if (fmt == kFmtFp8) {
+        hipLaunchKernelGGL((quantize_kernel<DT, DD, WAVES, kFmtFp8>), dim3(grid),
+                           dim3(WAVES * kWave), 0, stream, k_cache, v_cache, page_ids,
+                           valid_tokens, n_ids, Hkv, k8, v8, scales);
+      } else if constexpr (DT::E == 8) {
+        hipLaunchKernelGGL((quantize_kernel<DT, DD, WAVES, kFmtInt4>), dim3(grid),
+                           dim3(WAVES * kWave), 0, stream, k_cache, v_cache, page_ids,
+                           valid_tokens, n_ids, Hkv, k8, v8, scales);
+      } else {
+        return hipErrorInvalidValue;          // INT4 pages from 16-bit sources only
+      }
       return hipGetLastError();
     });
   });

@@ -29,7 +29,8 @@ EXPORTS = (
     "kv_block_meta_build", "kv_block_mean_build", "kv_append_token", "kv_decode_select",
     "kv_score_topk_workspace_size", "kv_block_score_topk", "kv_max_forced_blocks",
     "kv_block_select", "kv_auto_num_splits", "kv_auto_num_splits_fp8", "kv_paged_decode_attn", "kv_decode_combine",
-    "kv_quantize_pages_fp8", "kv_paged_decode_attn_fp8", "kv_cache_plan", "kv_cache_fetch",
+    "kv_quantize_pages_fp8", "kv_paged_decode_attn_fp8", "kv_quantize_pages_int4",
+    "kv_paged_decode_attn_int4", "kv_cache_plan", "kv_cache_fetch",
     "kv_cached_decode_attn", "kv_cache_slot_mass", "kv_probe_stream_read",
     "kv_probe_gather_read", "kv_host_alloc", "kv_host_free",
     "kv_status_string", "kv_last_error_message",
@@ -94,6 +95,8 @@ def _load() -> ctypes.CDLL:
         "kv_decode_combine": (I32, [S, I32, P, P, P, P, P, P]),
         "kv_quantize_pages_fp8": (I32, [S, P, P, P, P, I32, P, P, P, P]),
         "kv_paged_decode_attn_fp8": (I32, [S, P, P, P, P, P, P, P, P, I32, F, I32, P, P, P, P]),
+        "kv_quantize_pages_int4": (I32, [S, P, P, P, P, I32, P, P, P, P]),
+        "kv_paged_decode_attn_int4": (I32, [S, P, P, P, P, P, P, P, P, I32, F, I32, P, P, P, P]),
         "kv_cache_plan": (I32, [S, I32, P, P, I32, P, P, P, P, P, P, P, P]),
         "kv_cache_fetch": (I32, [S, I32, P, P, P, P, P, P, I32, P, P, P]),
         "kv_cached_decode_attn": (I32, [S, I32, P, P, P, P, P, P, P, I32, F, I32, P, P, P, P, P]),
@@ -249,6 +252,25 @@ def kv_paged_decode_attn_fp8(shape: KVShape, q: Buf, k_fp8: Buf, v_fp8: Buf, kv_
                                          _p(sel_blocks), _p(sel_count), sel_stride, scale,
                                          num_splits, _p(part_o), _p(part_m), _p(part_l),
                                          _stream(stream)))
+
+
+def kv_quantize_pages_int4(shape: KVShape, k_cache: Buf, v_cache: Buf, page_ids: Buf,
+                           page_valid_tokens: Buf, num_page_ids: int, k_int4: Buf, v_int4: Buf,
+                           kv_scales: Buf, stream=None) -> None:
+    _check(_lib.kv_quantize_pages_int4(ctypes.byref(shape), _p(k_cache), _p(v_cache),
+                                       _p(page_ids), _p(page_valid_tokens), num_page_ids,
+                                       _p(k_int4), _p(v_int4), _p(kv_scales), _stream(stream)))
+
+
+def kv_paged_decode_attn_int4(shape: KVShape, q: Buf, k_int4: Buf, v_int4: Buf, kv_scales: Buf,
+                              block_table: Buf, seq_lens: Buf, sel_blocks: Buf, sel_count: Buf,
+                              sel_stride: int, scale: float, num_splits: int, part_o: Buf,
+                              part_m: Buf, part_l: Buf, stream=None) -> None:
+    _check(_lib.kv_paged_decode_attn_int4(ctypes.byref(shape), _p(q), _p(k_int4), _p(v_int4),
+                                          _p(kv_scales), _p(block_table), _p(seq_lens),
+                                          _p(sel_blocks), _p(sel_count), sel_stride, scale,
+                                          num_splits, _p(part_o), _p(part_m), _p(part_l),
+                                          _stream(stream)))
 
 
 def kv_cache_plan(shape: KVShape, num_slots: int, sel_blocks: Buf, sel_count: Buf,

@@ -75,6 +75,8 @@ class DeviceWorkload:
         self.kmean = None          # fp32 mean-key index, allocated by mean_build()
         self.k8 = self.v8 = self.kv_scales = None   # E4M3 cold pages, from quantize_fp8()
         self._host8 = []
+        self._host4 = []
+        self.k4 = self.v4 = self.kv_scales4 = None  # INT4 cold pages, from quantize_int4()
         ids, val = [], []
         for b in range(spec.num_seqs):
             for n in range(spec.blocks(b)):
@@ -233,6 +235,42 @@ class DeviceWorkload:
         self.combine(S, stream)
         return S
 
+    def quantize_int4(self, host: Optional[bool] = None, stream=None):
+        """INT4 code pools ([P, Hkv, bs, D/2], two codes per byte) and (k, v)
+        scales of every used page; ``host`` as in quantize_fp8."""
+        P, Hkv, bs, D = self.data.k_raw.shape
+        dev = self.device
+        k4 = torch.zeros((P, Hkv, bs, D // 2), dtype=torch.uint8, device=dev)
+        v4 = torch.zeros_like(k4)
+        self.kv_scales4 = torch.zeros((P, Hkv, 2), dtype=torch.float32, device=dev)
+        kd.kv_quantize_pages_int4(self.shape, self.k_cache, self.v_cache, self.page_ids,
+                                  self.page_valid, int(self.page_ids.numel()), k4, v4,
+                                  self.kv_scales4, stream)
+        host = self.host_kv if host is None else host
+        if host:
+            torch.cuda.synchronize(dev)
+            hk, hv = HostBuffer(k4.cpu().numpy()), HostBuffer(v4.cpu().numpy())
+            self._host4 = [hk, hv]
+            self.k4, self.v4 = hk.dev, hv.dev
+        else:
+            self.k4, self.v4 = k4, v4
+        self.k4_dev, self.v4_dev = k4, v4
+
+    def attention_int4(self, sparse: bool, num_splits: Optional[int] = None, stream=None):
+        S = num_splits or kd.kv_auto_num_splits_fp8(self.shape,
+                                                    self.topk if sparse else self.spec.max_blocks)
+        po, pm, pl = self.partials(S)
+        sel, cnt, stride = (self.sel, self.sel_count, self.topk) if sparse else (None, None, 0)
+        kd.kv_paged_decode_attn_int4(self.shape, self.q, self.k4, self.v4, self.kv_scales4,
+                                     self.block_table, self.seq_lens, sel, cnt, stride,
+                                     self.scale, S, po, pm, pl, stream)
+        return S
+
+    def decode_int4(self, sparse: bool, num_splits: Optional[int] = None, stream=None):
+        S = self.attention_int4(sparse, num_splits, stream)
+        self.combine(S, stream)
+        return S
+
     # ------------------------------------------------------------ GPU block cache
     def cache_init(self, num_slots: int, k: int):
         """Cache pools [B * C, Hkv, bs, D] and an empty directory for lists of k blocks."""
@@ -296,7 +334,8 @@ class DeviceWorkload:
         return S
 
     def close(self):
-        for h in self._host + self._host8:
+        for h in self._host + self._host8 + self._host4:
             h.free()
         self._host = []
         self._host8 = []
+        self._host4 = []

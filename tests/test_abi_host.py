@@ -344,3 +344,26 @@ def test_decode_select_argument_checks():
     expect(kd.KV_ERR_ALIGNMENT, call(index_kind=kd.KV_INDEX_MEAN, kmean=A4))
     expect(kd.KV_ERR_ALIGNMENT, call(sel_count=ODD))
     expect(kd.KV_ERR_WORKSPACE, call(scores_out=None))
+
+
+def test_int4_argument_checks():
+    s = shape()
+    qz = kd.kv_quantize_pages_int4
+    expect(kd.KV_ERR_UNSUPPORTED, lambda stream: qz(shape(dtype="f32"), A16, A16, A16, A16, 2,
+                                                    A16, A16, A16, stream=stream))
+    expect(kd.KV_ERR_INVALID_ARG, lambda stream: qz(s, A16, A16, A16, A16, -1, A16, A16, A16,
+                                                    stream=stream))
+    expect(kd.KV_ERR_INVALID_ARG, lambda stream: qz(s, A16, A16, A16, A16, 2, None, A16, A16,
+                                                    stream=stream))
+    expect(kd.KV_ERR_ALIGNMENT, lambda stream: qz(s, A16, A16, A16, A16, 2, A4, A16, A16,
+                                                  stream=stream))
+    at = kd.kv_paged_decode_attn_int4
+    expect(kd.KV_ERR_UNSUPPORTED, lambda stream: at(shape(dtype="f32"), A16, A16, A16, A16, A16,
+                                                    A16, None, None, 0, 0.1, 1, A16, A16, A16,
+                                                    stream=stream))
+    expect(kd.KV_ERR_INVALID_ARG, lambda stream: at(s, A16, A16, A16, None, A16, A16, None, None,
+                                                    0, 0.1, 1, A16, A16, A16, stream=stream))
+    expect(kd.KV_ERR_ALIGNMENT, lambda stream: at(s, A16, A16, A16, A4, A16, A16, None, None, 0,
+                                                  0.1, 1, A16, A16, A16, stream=stream))
+    expect(kd.KV_ERR_INVALID_ARG, lambda stream: at(s, A16, A16, A16, A16, A16, A16, None, None,
+                                                    0, 0.1, 0, A16, A16, A16, stream=stream))
