@@ -298,15 +298,17 @@ def run_gpu(args, spec, data):
     # index, and either index with the first 4 / last 64 tokens forced in
     variants = None if args.no_variants else time_variants(args, copies, k, s_sparse,
                                                             time_loop, graph_us)
-    # FP8 E4M3 cold pages in HBM: the same attention over 1-byte codes
-    fp8 = None if args.no_variants else time_fp8(args, copies, k, s_sparse, s_dense, time_loop,
-                                                 graph_us)
+    # cold pages in HBM: the same attention over FP8 E4M3 (1 byte) and INT4
+    # (half a byte per channel) codes
+    fp8 = None if args.no_variants else time_codes(args, copies, k, time_loop, graph_us, "fp8")
+    int4 = None if args.no_variants else time_codes(args, copies, k, time_loop, graph_us, "int4")
     for c in copies:
         c.close()
     del copies
     torch.cuda.empty_cache()
     res["variants"] = variants
     res["fp8"] = fp8
+    res["int4"] = int4
     return res
 
 
@@ -348,12 +350,18 @@ def time_read_ceilings(copies, s_dense, time_loop, steps):
                                   "gbps": kv_bytes / (gather_us * 1e-6) / 1e9}}
 
 
-def time_fp8(args, copies, k, s_sparse, s_dense, time_loop, graph_us):
+def time_codes(args, copies, k, time_loop, graph_us, fmt: str):
+    """Code pages in HBM (fmt "fp8" or "int4"): quantiser, dense and sparse
+    attention kernels (back-to-back launches), and the decode graphs."""
     import torch
     from kv_cache_decode_amd import kvdecode as kd
-    # the code-page path has its own split heuristic
+    # the code-page paths share their own split heuristic
     s_sparse = kd.kv_auto_num_splits_fp8(copies[0].shape, k)
     s_dense = kd.kv_auto_num_splits_fp8(copies[0].shape, copies[0].spec.max_blocks)
+    quantize = (lambda c: c.quantize_fp8(host=False)) if fmt == "fp8" else \
+        (lambda c: c.quantize_int4(host=False))
+    attn = (lambda c, sp, S: c.attention_fp8(sparse=sp, num_splits=S)) if fmt == "fp8" else \
+        (lambda c, sp, S: c.attention_int4(sparse=sp, num_splits=S))
 
     def kernel_us(fn):
         for i in range(args.warmup):
@@ -362,26 +370,26 @@ def time_fp8(args, copies, k, s_sparse, s_dense, time_loop, graph_us):
         return ms_ * 1e3 / args.steps
 
     for c in copies:
-        c.quantize_fp8(host=False)
+        quantize(c)
         c.score_topk(k)
     torch.cuda.synchronize()
     res = {
-        "quantize_us": kernel_us(lambda c: c.quantize_fp8(host=False)),
-        "dense_attn_us": kernel_us(lambda c: c.attention_fp8(sparse=False, num_splits=s_dense)),
-        "sparse_attn_us": kernel_us(lambda c: c.attention_fp8(sparse=True, num_splits=s_sparse)),
+        "quantize_us": kernel_us(quantize),
+        "dense_attn_us": kernel_us(lambda c: attn(c, False, s_dense)),
+        "sparse_attn_us": kernel_us(lambda c: attn(c, True, s_sparse)),
     }
 
-    def decode_sparse_fp8(c):
+    def decode_sparse(c):
         c.score_topk(k)
-        c.attention_fp8(sparse=True, num_splits=s_sparse)
+        attn(c, True, s_sparse)
         c.combine(s_sparse)
 
-    def decode_dense_fp8(c):
-        c.attention_fp8(sparse=False, num_splits=s_dense)
+    def decode_dense(c):
+        attn(c, False, s_dense)
         c.combine(s_dense)
 
-    res["decode_sparse_us"] = graph_us(decode_sparse_fp8)
-    res["decode_dense_us"] = graph_us(decode_dense_fp8)
+    res["decode_sparse_us"] = graph_us(decode_sparse)
+    res["decode_dense_us"] = graph_us(decode_dense)
     res["s_sparse"], res["s_dense"] = s_sparse, s_dense
     return res
 
@@ -520,6 +528,18 @@ def run_zero_copy(args):
             e[1].record()
             torch.cuda.synchronize()
             fp8_ms.append(e[0].elapsed_time(e[1]))
+    # and over INT4 code pages in host memory: a quarter of the bytes
+    int4_ms = []
+    if not args.no_variants:
+        dw.quantize_int4(host=True)
+        for _ in range(3):
+            dw.attention_int4(sparse=True, num_splits=S)
+        for _ in range(reps):
+            e[0].record()
+            dw.attention_int4(sparse=True, num_splits=S)
+            e[1].record()
+            torch.cuda.synchronize()
+            int4_ms.append(e[0].elapsed_time(e[1]))
     dw.close()
 
     # measured host-to-device copy bandwidth: 256 MiB from pinned memory, best of 10,
@@ -569,9 +589,18 @@ def run_zero_copy(args):
                "host_link_gbps": f8_bytes / (f8 * 1e-3) / 1e9,
                "frac_of_h2d": f8_bytes / (f8 * 1e-3) / 1e9 / h2d_gbps,
                "speedup_vs_bf16": attn / f8}
+    int4 = None
+    if int4_ms:
+        f4 = float(np.median(int4_ms))
+        f4_bytes = link_bytes // (2 * eb)
+        int4 = {"sparse_attn_us": f4 * 1e3, "host_link_bytes": f4_bytes,
+                "host_link_gbps": f4_bytes / (f4 * 1e-3) / 1e9,
+                "frac_of_h2d": f4_bytes / (f4 * 1e-3) / 1e9 / h2d_gbps,
+                "speedup_vs_bf16": attn / f4}
     return {
         "block_cache": cache,
         "fp8_pages": fp8,
+        "int4_pages": int4,
         "workload": HOSTKV_WORKLOAD,
         "sparse_attn_us": attn * 1e3,
         "sparse_combine_us": float(np.median(comb_ms)) * 1e3,
@@ -733,24 +762,29 @@ def copy_calibration():
     print(json.dumps({"copy_bytes_read": n, "copy_bytes_written": n}), flush=True)
 
 
-def fp8_record(spec, f: dict) -> dict:
-    """FP8 E4M3 cold pages in HBM: per (page, KV head) unit the attention reads
-    2 * 16 * D code bytes and 8 bytes of scales instead of 2 * 16 * D * eb."""
+def codes_record(spec, f: dict, fmt: str) -> dict:
+    """Code pages in HBM: per (page, KV head) unit the attention reads 2 * 16 * D
+    code bytes (FP8; half that for INT4) and 8 bytes of scales instead of
+    2 * 16 * D * eb."""
     D, Hkv, B, Hq = spec.head_dim, spec.num_kv_heads, spec.num_seqs, spec.num_q_heads
     k = spec.topk_blocks
     s_sparse, s_dense = f["s_sparse"], f["s_dense"]
-    unit = 2 * spec.block_size * D + 8
+    code_bytes = 2 * spec.block_size * D // (1 if fmt == "fp8" else 2)
+    unit = code_bytes + 8
     keff = sum(min(k, spec.blocks(b)) for b in range(B))
     part = lambda S: B * Hq * S * (D + 2) * 4
     q_bytes = B * Hq * D * spec.elem_bytes
     dense_b = spec.used_pages * Hkv * (unit + 4) + q_bytes + part(s_dense)
     sparse_b = keff * Hkv * (unit + 8) + q_bytes + part(s_sparse)
-    quant_b = spec.used_pages * Hkv * (2 * spec.block_size * D * (spec.elem_bytes + 1) + 8) \
+    quant_b = spec.used_pages * Hkv * (2 * spec.block_size * D * spec.elem_bytes + code_bytes + 8) \
         + spec.used_pages * 8
     dense_gbps = dense_b / (f["dense_attn_us"] * 1e-6) / 1e9
+    fmt_text = ("OCP FP8 E4M3, one fp32 scale per (page, KV head) and tensor" if fmt == "fp8" else
+                "symmetric INT4 (scale amax/7, codes in [-7, 7], two per byte), one fp32 scale "
+                "per (page, KV head) and tensor")
     return {
         "splits": {"sparse": s_sparse, "dense": s_dense},
-        "format": "OCP FP8 E4M3, one fp32 scale per (page, KV head) and tensor",
+        "format": fmt_text,
         "quantize": {"us": f["quantize_us"], "bytes": quant_b,
                      "gbps": quant_b / (f["quantize_us"] * 1e-6) / 1e9},
         "dense_attn": {"us": f["dense_attn_us"], "bytes": dense_b, "gbps": dense_gbps,
@@ -821,7 +855,8 @@ def main():
         args.no_variants = False
         g = run_gpu(args, spec, data)
         print(json.dumps({"selection_variants": variants_record(spec, g["variants"]),
-                          "fp8_pages": fp8_record(spec, g["fp8"])}),
+                          "fp8_pages": codes_record(spec, g["fp8"], "fp8"),
+                          "int4_pages": codes_record(spec, g["int4"], "int4")}),
               flush=True)
         return
     log("[bench] timing GPU steps")
@@ -913,7 +948,8 @@ def main():
             "frac_of_gather_read": g["ceilings"]["dense_gather_read"]["us"] / dense_us,
         },
         "selection_variants": variants_record(spec, g["variants"]) if g["variants"] else None,
-        "fp8_pages": fp8_record(spec, g["fp8"]) if g.get("fp8") else None,
+        "fp8_pages": codes_record(spec, g["fp8"], "fp8") if g.get("fp8") else None,
+        "int4_pages": codes_record(spec, g["int4"], "int4") if g.get("int4") else None,
         "other_workloads": others,
         "zero_copy": zc,
         "cpu_baseline": cpu,
