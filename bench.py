@@ -454,8 +454,11 @@ def run_other_workload(args, name):
     s_sp = kd.kv_auto_num_splits(copies[0].shape, k) if k else 1
     sb = stage_bytes(spec, k or 1, s_sp, s_dense)
     gbps = lambda name, us: sb[name] / (us * 1e-6) / 1e9
+    dense_comb_us = loop(lambda c: c.combine(s_dense))
     res = {"dense_attn_us": dense_us, "dense_attn_gbps": gbps("dense_attn", dense_us),
            "dense_frac_of_hbm_peak": gbps("dense_attn", dense_us) / HBM_PEAK_GBPS,
+           "dense_combine_us": dense_comb_us,
+           "dense_combine_gbps": gbps("dense_combine", dense_comb_us),
            "splits_dense": s_dense, "dtype": spec.dtype, "group": spec.group}
     if k:
         for c in copies:
@@ -464,13 +467,17 @@ def run_other_workload(args, name):
         res["meta_build_us"] = loop(lambda c: c.meta_build())
         res["score_topk_us"] = loop(lambda c: c.score_topk(k))
         res["sparse_attn_us"] = loop(lambda c: c.attention(sparse=True, num_splits=s_sp))
+        res["sparse_combine_us"] = loop(lambda c: c.combine(s_sp))
         res["sparse_decode_us"] = loop(lambda c: (c.decode_select(k),
                                                   c.decode(sparse=True, num_splits=s_sp)))
         res["sparse_decode_steps_per_s"] = 1e6 / res["sparse_decode_us"]
         res["splits_sparse"] = s_sp
         res["stage_gbps"] = {name: gbps(name, res[f"{name}_us"])
-                             for name in ("meta_build", "score_topk", "sparse_attn")}
-        res["stage_gbps"]["dense_attn"] = res["dense_attn_gbps"]
+                             for name in ("meta_build", "score_topk", "sparse_attn",
+                                          "sparse_combine")}
+    res.setdefault("stage_gbps", {})
+    res["stage_gbps"]["dense_attn"] = res["dense_attn_gbps"]
+    res["stage_gbps"]["dense_combine"] = res["dense_combine_gbps"]
     for c in copies:
         c.close()
     del copies
@@ -822,6 +829,8 @@ def main():
     ap.add_argument("--no-zero-copy", action="store_true")
     ap.add_argument("--no-other-workloads", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true")
+    ap.add_argument("--only-other-workloads", action="store_true",
+                    help="run only the other named workloads (for profiling them)")
     ap.add_argument("--only-zero-copy", action="store_true",
                     help="run only the host-KV variant (for profiling it)")
     ap.add_argument("--no-variants", action="store_true",
@@ -845,6 +854,10 @@ def main():
         sys.exit(1)
     from kv_cache_decode_amd import workload as wl
 
+    if args.only_other_workloads:
+        print(json.dumps({"other_workloads": {n: run_other_workload(args, n)
+                                              for n in OTHER_WORKLOADS}}), flush=True)
+        return
     if args.only_zero_copy:
         print(json.dumps({"zero_copy": run_zero_copy(args)}), flush=True)
         return
