@@ -21,6 +21,7 @@
  *   kv_decode_combine     log-sum-exp merge of the split partials
  *   kv_append_token       store the new token's K/V and fold it into its page's meta
  *   kv_decode_select      kv_append_token followed by kv_block_select, in two launches
+ *   kv_check_tables       device-side check of the block table, lengths and selection
  *
  * The method is the select -> fetch -> compute decode step of the KVDrive paper
  * (§2.3, §4): a GPU-resident index picks the critical KV blocks, only those are
@@ -45,6 +46,8 @@
  *   gives the reason (thread-local).
  * - Device-side integer data (page ids, block tables, sequence lengths,
  *   selections) is trusted: it must satisfy the ranges stated below.
+ *   kv_check_tables verifies them on the device when a caller cannot vouch
+ *   for them.
  * - Head mapping: query head h reads KV head h / G, G = num_q_heads / num_kv_heads.
  * - Layouts (row-major, innermost last):
  *     q        [B, Hq, D]            dtype
@@ -435,6 +438,30 @@ kv_status kv_cache_slot_mass(const kv_shape* shape, int32_t num_slots, const flo
                              const float* lse, const int32_t* sel_count,
                              const int32_t* sel_slots, int32_t sel_stride, float* slot_mass,
                              void* stream);
+
+/*
+ * Check of the device-side tables the other calls trust (block_table,
+ * seq_lens and, when sel_blocks is not NULL, a selection with row stride
+ * sel_stride).  For every sequence b it writes result[b] (uint32, device
+ * memory, B words) as the OR of:
+ *   KV_CHECK_BAD_SEQ_LEN    L_b < 1 or L_b > maxN * bs (nothing else of b is checked)
+ *   KV_CHECK_BAD_PAGE_ID    block_table[b, n] outside [0, P) for some n < N_b
+ *   KV_CHECK_BAD_SEL_COUNT  sel_count[b, j] outside [0, min(sel_stride, N_b)] for some j
+ *   KV_CHECK_BAD_SEL_BLOCK  a listed block outside [0, N_b), or a list not
+ *                           strictly ascending
+ * and 0 when the tables of b are fit for every call.  It reads only the
+ * tables, at indexes bounded by the shape, so it is safe on any contents.
+ * The selection of kv_cache_plan's callers and of kv_paged_decode_attn obeys
+ * these same rules.
+ */
+#define KV_CHECK_BAD_SEQ_LEN 0x1u
+#define KV_CHECK_BAD_PAGE_ID 0x2u
+#define KV_CHECK_BAD_SEL_COUNT 0x4u
+#define KV_CHECK_BAD_SEL_BLOCK 0x8u
+kv_status kv_check_tables(const kv_shape* shape, const int32_t* block_table,
+                          const int32_t* seq_lens, const int32_t* sel_blocks,
+                          const int32_t* sel_count, int32_t sel_stride, uint32_t* result,
+                          void* stream);
 
 /*
  * Read-ceiling probes, for measurement: they read bytes as the path does and

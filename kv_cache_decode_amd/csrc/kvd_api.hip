@@ -602,6 +602,28 @@ kv_status kv_cache_slot_mass(const kv_shape* shape, int32_t num_slots, const flo
                     "kv_cache_slot_mass launch");
 }
 
+kv_status kv_check_tables(const kv_shape* shape, const int32_t* block_table,
+                          const int32_t* seq_lens, const int32_t* sel_blocks,
+                          const int32_t* sel_count, int32_t sel_stride, uint32_t* result,
+                          void* stream) {
+  kv_status st = check_shape(shape);
+  if (st != KV_OK) return st;
+  if (!block_table || !seq_lens || !result)
+    return fail(KV_ERR_INVALID_ARG, "block_table, seq_lens and result are required");
+  if ((sel_blocks == nullptr) != (sel_count == nullptr))
+    return fail(KV_ERR_INVALID_ARG, "sel_blocks and sel_count go together");
+  if (sel_blocks && sel_stride < 1)
+    return fail(KV_ERR_INVALID_ARG, "sel_stride=%d must be >= 1", sel_stride);
+  if (!aligned(block_table, 4) || !aligned(seq_lens, 4) || !aligned(result, 4) ||
+      (sel_blocks && (!aligned(sel_blocks, 4) || !aligned(sel_count, 4))))
+    return fail(KV_ERR_ALIGNMENT, "the tables and result must be 4-byte aligned");
+  return hip_status(kvd::launch_check_tables(block_table, seq_lens, sel_blocks, sel_count,
+                                             sel_blocks ? sel_stride : 0, shape->num_seqs,
+                                             shape->num_kv_heads, shape->max_blocks_per_seq,
+                                             shape->num_pages, result, (hipStream_t)stream),
+                    "kv_check_tables launch");
+}
+
 kv_status kv_probe_stream_read(const void* buf, size_t bytes, uint32_t* sink, void* stream) {
   if (!buf || !sink) return fail(KV_ERR_INVALID_ARG, "buf and sink are required");
   if (bytes == 0 || bytes % 16) return fail(KV_ERR_INVALID_ARG, "bytes must be a positive multiple of 16");

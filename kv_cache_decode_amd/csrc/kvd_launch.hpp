@@ -64,6 +64,15 @@ hipError_t launch_slot_mass(const float* block_lse, const float* lse, const int3
                             const int32_t* sel_slots, int sel_stride, int B, int Hq, int Hkv,
                             int C, float* slot_mass, hipStream_t stream);
 
+// Result bits of the table check (one word per sequence).
+constexpr uint32_t kCheckBadSeqLen = 0x1u, kCheckBadPageId = 0x2u, kCheckBadSelCount = 0x4u,
+                   kCheckBadSelBlock = 0x8u;
+
+hipError_t launch_check_tables(const int32_t* block_table, const int32_t* seq_lens,
+                               const int32_t* sel, const int32_t* sel_count, int sel_stride,
+                               int B, int Hkv, int maxN, int num_pages, uint32_t* result,
+                               hipStream_t stream);
+
 hipError_t launch_stream_read(const void* buf, size_t bytes, uint32_t* sink, int sink_words,
                               hipStream_t stream);
 

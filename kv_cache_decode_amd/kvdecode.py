@@ -31,7 +31,7 @@ EXPORTS = (
     "kv_block_select", "kv_auto_num_splits", "kv_auto_num_splits_fp8", "kv_paged_decode_attn", "kv_decode_combine",
     "kv_quantize_pages_fp8", "kv_paged_decode_attn_fp8", "kv_quantize_pages_int4",
     "kv_paged_decode_attn_int4", "kv_cache_plan", "kv_cache_fetch",
-    "kv_cached_decode_attn", "kv_cache_slot_mass", "kv_probe_stream_read",
+    "kv_cached_decode_attn", "kv_cache_slot_mass", "kv_check_tables", "kv_probe_stream_read",
     "kv_probe_gather_read", "kv_host_alloc", "kv_host_free",
     "kv_status_string", "kv_last_error_message",
 )
@@ -101,6 +101,7 @@ def _load() -> ctypes.CDLL:
         "kv_cache_fetch": (I32, [S, I32, P, P, P, P, P, P, I32, P, P, P]),
         "kv_cached_decode_attn": (I32, [S, I32, P, P, P, P, P, P, P, I32, F, I32, P, P, P, P, P]),
         "kv_cache_slot_mass": (I32, [S, I32, P, P, P, P, I32, P, P]),
+        "kv_check_tables": (I32, [S, P, P, P, P, I32, P, P]),
         "kv_probe_stream_read": (I32, [P, SZ, P, P]),
         "kv_probe_gather_read": (I32, [S, P, P, P, P, I32, P, P]),
         "kv_host_alloc": (I32, [SZ, U32, ctypes.POINTER(P), ctypes.POINTER(P)]),
@@ -306,6 +307,19 @@ def kv_cache_slot_mass(shape: KVShape, num_slots: int, block_lse: Buf, lse: Buf,
     _check(_lib.kv_cache_slot_mass(ctypes.byref(shape), num_slots, _p(block_lse), _p(lse),
                                    _p(sel_count), _p(sel_slots), sel_stride, _p(slot_mass),
                                    _stream(stream)))
+
+
+KV_CHECK_BAD_SEQ_LEN = 0x1
+KV_CHECK_BAD_PAGE_ID = 0x2
+KV_CHECK_BAD_SEL_COUNT = 0x4
+KV_CHECK_BAD_SEL_BLOCK = 0x8
+
+
+def kv_check_tables(shape: KVShape, block_table: Buf, seq_lens: Buf, sel_blocks: Buf,
+                    sel_count: Buf, sel_stride: int, result: Buf, stream=None) -> None:
+    _check(_lib.kv_check_tables(ctypes.byref(shape), _p(block_table), _p(seq_lens),
+                                _p(sel_blocks), _p(sel_count), sel_stride, _p(result),
+                                _stream(stream)))
 
 
 PROBE_SINK_WORDS = 4096

@@ -367,3 +367,12 @@ def test_int4_argument_checks():
                                                   0.1, 1, A16, A16, A16, stream=stream))
     expect(kd.KV_ERR_INVALID_ARG, lambda stream: at(s, A16, A16, A16, A16, A16, A16, None, None,
                                                     0, 0.1, 0, A16, A16, A16, stream=stream))
+
+
+def test_check_tables_argument_checks():
+    s = shape()
+    f = kd.kv_check_tables
+    expect(kd.KV_ERR_INVALID_ARG, lambda stream: f(s, None, A16, None, None, 0, A16, stream=stream))
+    expect(kd.KV_ERR_INVALID_ARG, lambda stream: f(s, A16, A16, A16, None, 4, A16, stream=stream))
+    expect(kd.KV_ERR_INVALID_ARG, lambda stream: f(s, A16, A16, A16, A16, 0, A16, stream=stream))
+    expect(kd.KV_ERR_ALIGNMENT, lambda stream: f(s, A16, ODD, None, None, 0, A16, stream=stream))
