@@ -26,7 +26,7 @@
 #define KVD_META_WAVES 4
 #endif
 #ifndef KVD_SCORE_STEPS
-#define KVD_SCORE_STEPS 8
+#define KVD_SCORE_STEPS 2
 #endif
 #ifndef KVD_SCORE_WAVES
 #define KVD_SCORE_WAVES 4
