@@ -12,6 +12,7 @@
  *   kv_paged_decode_attn_fp8  decode attention over FP8 E4M3 cold pages
  *   kv_quantize_pages_int4 K/V pages -> INT4 cold pages with per-page scales
  *   kv_paged_decode_attn_int4 decode attention over INT4 cold pages
+ *   kv_paged_decode_attn_tiered decode attention over hot 16-bit and cold code pages
  *   kv_cache_plan         GPU block cache: hits, misses and lookahead eviction
  *   kv_cache_fetch        copy only the missing blocks into their cache slots
  *   kv_cached_decode_attn decode attention over the cached blocks, with each
@@ -258,6 +259,9 @@ int32_t kv_auto_num_splits(const kv_shape* shape, int32_t blocks_per_unit);
 /* The same for kv_paged_decode_attn_fp8: about 8 waves per compute unit. */
 int32_t kv_auto_num_splits_fp8(const kv_shape* shape, int32_t blocks_per_unit);
 
+/* The same for kv_paged_decode_attn_tiered: about 12 waves per compute unit. */
+int32_t kv_auto_num_splits_tiered(const kv_shape* shape, int32_t blocks_per_unit);
+
 /*
  * Split-K decode attention (Dual-Blade background: a decode step attends over
  * all previous KV; KVDrive §2.3 step 3: sparse attention over the selected
@@ -367,6 +371,32 @@ kv_status kv_paged_decode_attn_int4(const kv_shape* shape, const void* q, const 
                                     const int32_t* sel_blocks, const int32_t* sel_count,
                                     int32_t sel_stride, float scale, int32_t num_splits,
                                     float* part_o, float* part_m, float* part_l, void* stream);
+
+/* Cold-page formats of kv_paged_decode_attn_tiered. */
+#define KV_COLD_FP8 8  /* the pages of kv_quantize_pages_fp8 */
+#define KV_COLD_INT4 4 /* the pages of kv_quantize_pages_int4 */
+
+/*
+ * Decode attention over tiered pools (KVDrive §11: hot blocks keep high
+ * precision in HBM while cold blocks are stored with aggressive quantisation,
+ * chosen per block from what the cache manager knows of hot and cold).  Page
+ * p is read from k_cache / v_cache (shape->dtype) when page_tier[p] == 0, and
+ * from the code pools k_cold / v_cold in cold_format, with kv_scales[p], when
+ * page_tier[p] != 0 (uint8 [P], device memory).  The result is exactly what
+ * kv_paged_decode_attn computes over the pools whose cold pages hold their
+ * decoded values (code * scale); the other arguments, layouts and errors are
+ * those of kv_paged_decode_attn.  The cold pools have the layouts of
+ * kv_quantize_pages_fp8 / _int4 and may be device pointers of kv_host_alloc
+ * memory.  fp16 or bf16 with G >= 2 (KV_ERR_UNSUPPORTED otherwise).
+ */
+kv_status kv_paged_decode_attn_tiered(const kv_shape* shape, const void* q, const void* k_cache,
+                                      const void* v_cache, const uint8_t* k_cold,
+                                      const uint8_t* v_cold, const float* kv_scales,
+                                      int32_t cold_format, const uint8_t* page_tier,
+                                      const int32_t* block_table, const int32_t* seq_lens,
+                                      const int32_t* sel_blocks, const int32_t* sel_count,
+                                      int32_t sel_stride, float scale, int32_t num_splits,
+                                      float* part_o, float* part_m, float* part_l, void* stream);
 
 /*
  * GPU-resident block cache with lookahead eviction (KVDrive §5.1: a window of

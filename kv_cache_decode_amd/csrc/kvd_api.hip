@@ -22,6 +22,9 @@
 #ifndef KVD_SPLIT_WAVES_PER_CU_FP8
 #define KVD_SPLIT_WAVES_PER_CU_FP8 8
 #endif
+#ifndef KVD_SPLIT_WAVES_PER_CU_TIERED
+#define KVD_SPLIT_WAVES_PER_CU_TIERED 12   // tiered pools: cold pages want more waves
+#endif
 #ifndef KVD_SPLIT_WAVES_PER_CU_VALU
 #define KVD_SPLIT_WAVES_PER_CU_VALU 4
 #endif
@@ -376,6 +379,11 @@ int32_t kv_auto_num_splits_fp8(const kv_shape* shape, int32_t blocks_per_unit) {
   return auto_splits(shape, blocks_per_unit, KVD_SPLIT_WAVES_PER_CU_FP8);
 }
 
+int32_t kv_auto_num_splits_tiered(const kv_shape* shape, int32_t blocks_per_unit) {
+  if (!shape) return 1;
+  return auto_splits(shape, blocks_per_unit, KVD_SPLIT_WAVES_PER_CU_TIERED);
+}
+
 kv_status kv_paged_decode_attn(const kv_shape* shape, const void* q, const void* k_cache,
                                const void* v_cache, const int32_t* block_table,
                                const int32_t* seq_lens, const int32_t* sel_blocks,
@@ -466,6 +474,54 @@ kv_status kv_paged_decode_attn_int4(const kv_shape* shape, const void* q, const 
   if (!aligned(kv_scales, 8)) return fail(KV_ERR_ALIGNMENT, "kv_scales must be 8-byte aligned");
   return attn_common(shape, 4, q, k_int4, v_int4, kv_scales, block_table, seq_lens, sel_blocks,
                      sel_count, sel_stride, scale, num_splits, part_o, part_m, part_l, stream);
+}
+
+kv_status kv_paged_decode_attn_tiered(const kv_shape* shape, const void* q, const void* k_cache,
+                                      const void* v_cache, const uint8_t* k_cold,
+                                      const uint8_t* v_cold, const float* kv_scales,
+                                      int32_t cold_format, const uint8_t* page_tier,
+                                      const int32_t* block_table, const int32_t* seq_lens,
+                                      const int32_t* sel_blocks, const int32_t* sel_count,
+                                      int32_t sel_stride, float scale, int32_t num_splits,
+                                      float* part_o, float* part_m, float* part_l,
+                                      void* stream) {
+  kv_status st = check_shape(shape);
+  if (st != KV_OK) return st;
+  if (!mfma_path(shape))
+    return fail(KV_ERR_UNSUPPORTED,
+                "tiered pools need fp16 or bf16 and a GQA group of 2 or more query heads");
+  if (cold_format != KV_COLD_FP8 && cold_format != KV_COLD_INT4)
+    return fail(KV_ERR_INVALID_ARG, "cold_format=%d must be KV_COLD_FP8 or KV_COLD_INT4",
+                cold_format);
+  if (!k_cold || !v_cold || !kv_scales || !page_tier)
+    return fail(KV_ERR_INVALID_ARG, "k_cold, v_cold, kv_scales and page_tier are required");
+  if (!aligned(k_cold, 16) || !aligned(v_cold, 16) || !aligned(kv_scales, 8))
+    return fail(KV_ERR_ALIGNMENT, "the cold pools must be 16-byte aligned, kv_scales 8-byte");
+  // the 16-bit checks and the launch
+  if (num_splits < 1 || num_splits > 65535 * 4)
+    return fail(KV_ERR_INVALID_ARG, "num_splits=%d must be in [1, 262140]", num_splits);
+  if (!q || !k_cache || !v_cache || !block_table || !seq_lens || !part_o || !part_m || !part_l)
+    return fail(KV_ERR_INVALID_ARG, "q, k_cache, v_cache, block_table, seq_lens and partials are required");
+  if ((sel_blocks == nullptr) != (sel_count == nullptr))
+    return fail(KV_ERR_INVALID_ARG, "sel_blocks and sel_count go together");
+  if (sel_blocks && sel_stride < 1)
+    return fail(KV_ERR_INVALID_ARG, "sel_stride=%d must be >= 1", sel_stride);
+  if (!(scale > 0.0f) || !(scale < INFINITY))
+    return fail(KV_ERR_INVALID_ARG, "scale must be finite and positive");
+  if (!aligned(q, 16) || !aligned(k_cache, 16) || !aligned(v_cache, 16) || !aligned(part_o, 16))
+    return fail(KV_ERR_ALIGNMENT, "q, k_cache, v_cache and part_o must be 16-byte aligned");
+  if (!aligned(block_table, 4) || !aligned(seq_lens, 4) || !aligned(part_m, 4) ||
+      !aligned(part_l, 4) || (sel_blocks && (!aligned(sel_blocks, 4) || !aligned(sel_count, 4))))
+    return fail(KV_ERR_ALIGNMENT, "integer and partial arrays must be 4-byte aligned");
+  const int G = shape->num_q_heads / shape->num_kv_heads;
+  return hip_status(
+      kvd::launch_paged_attn(shape->dtype, shape->head_dim, G, 0, q, k_cache, v_cache, kv_scales,
+                             block_table, seq_lens, sel_blocks, sel_count, sel_stride, nullptr, 0,
+                             shape->num_seqs, shape->num_q_heads, shape->num_kv_heads,
+                             shape->max_blocks_per_seq, num_splits, scale, part_o, part_m, part_l,
+                             nullptr, (hipStream_t)stream, cold_format, k_cold, v_cold,
+                             page_tier),
+      "kv_paged_decode_attn_tiered launch");
 }
 
 kv_status kv_decode_combine(const kv_shape* shape, int32_t num_splits, const float* part_o,

@@ -31,8 +31,15 @@
 #endif
 #if KVD_MFMA_WAVES_PER_EU > 0
 #define KVD_MFMA_OCCUPANCY __attribute__((amdgpu_waves_per_eu(KVD_MFMA_WAVES_PER_EU)))
+// tiered instances carry both page paths
+#ifndef KVD_MFMA_TIER_WAVES_PER_EU
+#define KVD_MFMA_TIER_WAVES_PER_EU 2
+#endif
+#define KVD_MFMA_OCCUPANCY_T(cold) \
+  __attribute__((amdgpu_waves_per_eu((cold) ? KVD_MFMA_TIER_WAVES_PER_EU : KVD_MFMA_WAVES_PER_EU)))
 #else
 #define KVD_MFMA_OCCUPANCY
+#define KVD_MFMA_OCCUPANCY_T(cold)
 #endif
 
 namespace kvd {
@@ -438,15 +445,25 @@ __device__ inline int qk_channel(int st, int grp) {
                   : (KVQ == 4 ? D / 4 * grp + 8 * st : 8 * (4 * st + grp));
 }
 
-template <typename DT, int D, int G, int WAVES, bool SPARSE, int KVQ>
-__global__ __launch_bounds__(WAVES * kWave) KVD_MFMA_OCCUPANCY void paged_attn_mfma_kernel(
+// Tiered pools (COLD = 8 or 4, with KVQ = 0): page p is read from the 16-bit
+// pools when page_tier[p] == 0 (hot) and from the code pools k_cold / v_cold
+// in format COLD when page_tier[p] != 0 (cold, scales in kv_scales).  The tier
+// is uniform per page, so each page takes one branch for the whole wave.  A
+// cold page's codes sit in the first registers of the 16-bit page buffer, and
+// its K codes are read in the 16-bit layout (the 8 channels of each QK step,
+// as 4 or 8 code bytes), so both tiers share q's B operand.
+template <typename DT, int D, int G, int WAVES, bool SPARSE, int KVQ, int COLD = 0>
+__global__ __launch_bounds__(WAVES * kWave) KVD_MFMA_OCCUPANCY_T(COLD) void paged_attn_mfma_kernel(
     const void* __restrict__ q, const void* __restrict__ k_cache, const void* __restrict__ v_cache,
     const float* __restrict__ kv_scales, const int32_t* __restrict__ block_table,
     const int32_t* __restrict__ seq_lens, const int32_t* __restrict__ sel,
     const int32_t* __restrict__ sel_count, int sel_stride, const int32_t* __restrict__ sel_slots,
     int num_slots, int Hq, int Hkv, int maxN, int S, float qscale, float* __restrict__ part_o,
-    float* __restrict__ part_m, float* __restrict__ part_l, float* __restrict__ block_lse) {
+    float* __restrict__ part_m, float* __restrict__ part_l, float* __restrict__ block_lse,
+    const void* __restrict__ k_cold, const void* __restrict__ v_cold,
+    const uint8_t* __restrict__ page_tier) {
   static_assert(G >= 2 && G <= 8, "the group fills 2..8 of the 16 MFMA rows");
+  static_assert(COLD == 0 || KVQ == 0, "tiered pools pair 16-bit hot pages with code pages");
   using St = typename DT::storage;
   using Ops = MfmaOps<DT>;
   constexpr int KS = D / 32;   // QK steps of 32 channels
@@ -472,6 +489,7 @@ __global__ __launch_bounds__(WAVES * kWave) KVD_MFMA_OCCUPANCY void paged_attn_m
     qB[st] = col < G ? load16(static_cast<const St*>(q) + (row0 + col) * D + qk_channel<KVQ, D>(st, grp))
                      : make_uint4(0, 0, 0, 0);
 
+
   f32x4_v o[NT];
 #pragma unroll
   for (int n = 0; n < NT; ++n) o[n] = f32x4_v{0.f, 0.f, 0.f, 0.f};
@@ -485,6 +503,18 @@ __global__ __launch_bounds__(WAVES * kWave) KVD_MFMA_OCCUPANCY void paged_attn_m
   const uint8_t* vb = static_cast<const uint8_t*>(v_cache) +
                       kv_bytes<DT, KVQ>((size_t)j * kBlockSize * D + (size_t)(4 * grp) * D +
                                         2 * NDW * col);
+  // the cold pools of tiered calls (K in the 16-bit lane layout: channel 8*grp
+  // of step 0, steps 32 channels apart)
+  constexpr int KCHC = 8;
+  const size_t page_stride_c = kv_bytes<DT, COLD>((size_t)Hkv * kBlockSize * D);
+  const uint8_t* kbc = COLD ? static_cast<const uint8_t*>(k_cold) +
+                                  kv_bytes<DT, COLD>((size_t)j * kBlockSize * D + (size_t)col * D +
+                                                     KCHC * grp)
+                            : nullptr;
+  const uint8_t* vbc = COLD ? static_cast<const uint8_t*>(v_cold) +
+                                  kv_bytes<DT, COLD>((size_t)j * kBlockSize * D +
+                                                     (size_t)(4 * grp) * D + 2 * NDW * col)
+                            : nullptr;
   const int32_t* sel_row = SPARSE ? sel + ((size_t)b * Hkv + j) * sel_stride : nullptr;
   const int32_t* slots_row = (SPARSE && sel_slots) ? sel_slots + ((size_t)b * Hkv + j) * sel_stride
                                                    : nullptr;
@@ -492,18 +522,19 @@ __global__ __launch_bounds__(WAVES * kWave) KVD_MFMA_OCCUPANCY void paged_attn_m
 
   for (int base = p0; base < p1; base += kWave) {
     const int cnt = min(kWave, p1 - base);
-    int my_page = 0, my_valid = 0;
+    int my_page = 0, my_valid = 0, my_tier = 0;
     float my_sk = 1.0f, my_sv = 1.0f;
     if (lane < cnt) {
       const int n = SPARSE ? sel_row[base + lane] : base + lane;
       // cached list: the block sits in slot sel_slots[.] of cache page b*C + slot
       my_page = slots_row ? b * num_slots + slots_row[base + lane] : bt_row[n];
       my_valid = min(kBlockSize, L - n * kBlockSize);
-      if constexpr (KVQ != 0) {
+      if constexpr (KVQ != 0 || COLD != 0) {
         const float2 sc = *reinterpret_cast<const float2*>(kv_scales + ((size_t)my_page * Hkv + j) * 2);
         my_sk = sc.x;
         my_sv = sc.y;
       }
+      if constexpr (COLD != 0) my_tier = page_tier[my_page];
     }
     // raw registers of one page: 16-bit rows, E4M3 codes (K: 16 per load,
     // V: D/16 per token row, NDW/2 dwords), or INT4 codes (K: D/4 per lane in
@@ -523,6 +554,38 @@ __global__ __launch_bounds__(WAVES * kWave) KVD_MFMA_OCCUPANCY void paged_attn_m
     using PageRegs = typename std::conditional<
         KVQ == 8, PageRegs8, typename std::conditional<KVQ == 4, PageRegs4, PageRegs16>::type>::type;
     auto load_page = [&](PageRegs& r, int idx) {
+      if constexpr (COLD != 0) {
+        if (readlane(my_tier, idx)) {          // a cold page: codes into the first registers
+          const size_t offc = (size_t)readlane(my_page, idx) * page_stride_c;
+          if constexpr (COLD == 4) {
+#pragma unroll
+            for (int st = 0; st < KS; ++st) r.k[st].x = load4_stream(kbc + offc + 16 * st);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              if constexpr (NDW == 4) r.v[i].w[0] = load4_stream(vbc + offc + (size_t)i * (D / 2));
+              else r.v[i].w[0] = load2_stream(vbc + offc + (size_t)i * (D / 2));
+            }
+          } else {
+#pragma unroll
+            for (int st = 0; st < KS; ++st) {
+              const uint2 t = load8_stream(kbc + offc + 32 * st);
+              r.k[st].x = t.x;
+              r.k[st].y = t.y;
+            }
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              if constexpr (NDW / 2 == 2) {
+                const uint2 t = load8_stream(vbc + offc + (size_t)i * D);
+                r.v[i].w[0] = t.x;
+                r.v[i].w[1] = t.y;
+              } else {
+                r.v[i].w[0] = load4_stream(vbc + offc + (size_t)i * D);
+              }
+            }
+          }
+          return;
+        }
+      }
       const size_t off = (size_t)readlane(my_page, idx) * page_stride;
       if constexpr (KVQ == 4) {
         if constexpr (KS == 4) {
@@ -560,8 +623,9 @@ __global__ __launch_bounds__(WAVES * kWave) KVD_MFMA_OCCUPANCY void paged_attn_m
     // one page of compute; `cur` holds page `it` of the group
     auto process = [&](const PageRegs& cur, int it) {
       const int valid = readlane(my_valid, it);
-      const float sk = KVQ ? readlane_f(my_sk, it) : 1.0f;
-      const float sv = KVQ ? readlane_f(my_sv, it) : 1.0f;
+      const bool cold = COLD != 0 && readlane(my_tier, it) != 0;   // wave-uniform
+      const float sk = (KVQ || cold) ? readlane_f(my_sk, it) : 1.0f;
+      const float sv = (KVQ || cold) ? readlane_f(my_sv, it) : 1.0f;
 
       // 16-bit operands of the page
       uint4 kA[KS];
@@ -595,6 +659,35 @@ __global__ __launch_bounds__(WAVES * kWave) KVD_MFMA_OCCUPANCY void paged_attn_m
             vr[i].w[2 * k] = t.x;
             vr[i].w[2 * k + 1] = t.y;
           }
+      } else if (cold) {                      // tiered call, a cold page's codes
+        if constexpr (COLD == 4) {
+#pragma unroll
+          for (int st = 0; st < KS; ++st) kA[st] = int4x8_to_16<DT>(cur.k[st].x);
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            if constexpr (NDW == 4) {
+              const uint4 t = int4x8_to_16<DT>(cur.v[i].w[0]);
+              vr[i].w[0] = t.x; vr[i].w[1] = t.y; vr[i].w[2] = t.z; vr[i].w[3] = t.w;
+            } else {
+              const uint2 t = int4x4_to_16<DT>(cur.v[i].w[0]);
+              vr[i].w[0] = t.x; vr[i].w[1] = t.y;
+            }
+          }
+        } else if constexpr (COLD == 8) {
+#pragma unroll
+          for (int st = 0; st < KS; ++st) {
+            const uint2 a0 = fp8x4_to_16<DT>(cur.k[st].x), a1 = fp8x4_to_16<DT>(cur.k[st].y);
+            kA[st] = make_uint4(a0.x, a0.y, a1.x, a1.y);
+          }
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int k = 0; k < NDW / 2; ++k) {
+              const uint2 t = fp8x4_to_16<DT>(cur.v[i].w[k]);
+              vr[i].w[2 * k] = t.x;
+              vr[i].w[2 * k + 1] = t.y;
+            }
+        }
       } else {
 #pragma unroll
         for (int st = 0; st < KS; ++st) kA[st] = cur.k[st];
@@ -636,7 +729,7 @@ __global__ __launch_bounds__(WAVES * kWave) KVD_MFMA_OCCUPANCY void paged_attn_m
         if (grp == 0 && col < G)
           block_lse[(row0 + col) * sel_stride + base + it] = (m + __log2f(ps)) * kLn2;
       }
-      if constexpr (KVQ != 0) {    // the page's V scale rides on its weights
+      if (KVQ != 0 || cold) {    // the page's V scale rides on its weights
 #pragma unroll
         for (int i = 0; i < 4; ++i) p[i] *= sv;
       }
@@ -781,7 +874,8 @@ hipError_t launch_paged_attn(int dtype, int D, int G, int kvq, const void* q,
                              const int32_t* sel, const int32_t* sel_count, int sel_stride,
                              const int32_t* sel_slots, int num_slots, int B, int Hq, int Hkv,
                              int maxN, int S, float scale, float* part_o, float* part_m,
-                             float* part_l, float* block_lse, hipStream_t stream) {
+                             float* part_l, float* block_lse, hipStream_t stream, int cold,
+                             const void* k_cold, const void* v_cold, const uint8_t* page_tier) {
   constexpr int WAVES = KVD_ATTN_WAVES;
   const dim3 grid((S + WAVES - 1) / WAVES, Hkv, B);
   const float qscale = scale * kLog2e;
@@ -790,18 +884,18 @@ hipError_t launch_paged_attn(int dtype, int D, int G, int kvq, const void* q,
       return with_group(G, [&](auto g) {
         using DT = decltype(dt);
         constexpr int DD = decltype(d)::value, GG = decltype(g)::value;
-        auto go = [&](auto sparse, auto fmt) {
+        auto go = [&](auto sparse, auto fmt, auto coldc) {
           constexpr bool SP = decltype(sparse)::value;
-          constexpr int KQ = decltype(fmt)::value;
+          constexpr int KQ = decltype(fmt)::value, CQ = decltype(coldc)::value;
           if constexpr (KQ == 4 && std::is_same_v<DT, F32>) {
             return;                           // INT4 pages: 16-bit dtypes only
           } else if constexpr (!std::is_same_v<DT, F32> && GG >= 2) {
-            hipLaunchKernelGGL((paged_attn_mfma_kernel<DT, DD, GG, WAVES, SP, KQ>), grid,
+            hipLaunchKernelGGL((paged_attn_mfma_kernel<DT, DD, GG, WAVES, SP, KQ, CQ>), grid,
                                dim3(WAVES * kWave), 0, stream, q, k_cache, v_cache, kv_scales,
                                block_table, seq_lens, sel, sel_count, sel_stride, sel_slots,
                                num_slots, Hq, Hkv, maxN, S, qscale, part_o, part_m, part_l,
-                               block_lse);
-          } else {
+                               block_lse, k_cold, v_cold, page_tier);
+          } else if constexpr (CQ == 0) {
             hipLaunchKernelGGL((paged_attn_kernel<DT, DD, GG, WAVES, SP, KQ>), grid,
                                dim3(WAVES * kWave), 0, stream, q, k_cache, v_cache, kv_scales,
                                block_table, seq_lens, sel, sel_count, sel_stride, sel_slots,
@@ -813,14 +907,24 @@ hipError_t launch_paged_attn(int dtype, int D, int G, int kvq, const void* q,
         using C8 = std::integral_constant<int, 8>;
         using C4 = std::integral_constant<int, 4>;
         if (kvq == 4 && std::is_same_v<DT, F32>) return hipErrorInvalidValue;
-        if (sel) {
-          if (kvq == 8) go(std::true_type{}, C8{});
-          else if (kvq == 4) go(std::true_type{}, C4{});
-          else go(std::true_type{}, C0{});
+        if (cold != 0) {
+          // tiered pools: 16-bit hot pages on the matrix-core path only
+          if (kvq != 0 || std::is_same_v<DT, F32> || GG < 2) return hipErrorInvalidValue;
+          if (sel) {
+            if (cold == 8) go(std::true_type{}, C0{}, C8{});
+            else go(std::true_type{}, C0{}, C4{});
+          } else {
+            if (cold == 8) go(std::false_type{}, C0{}, C8{});
+            else go(std::false_type{}, C0{}, C4{});
+          }
+        } else if (sel) {
+          if (kvq == 8) go(std::true_type{}, C8{}, C0{});
+          else if (kvq == 4) go(std::true_type{}, C4{}, C0{});
+          else go(std::true_type{}, C0{}, C0{});
         } else {
-          if (kvq == 8) go(std::false_type{}, C8{});
-          else if (kvq == 4) go(std::false_type{}, C4{});
-          else go(std::false_type{}, C0{});
+          if (kvq == 8) go(std::false_type{}, C8{}, C0{});
+          else if (kvq == 4) go(std::false_type{}, C4{}, C0{});
+          else go(std::false_type{}, C0{}, C0{});
         }
         return hipGetLastError();
       });

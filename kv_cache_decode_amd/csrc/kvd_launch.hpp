@@ -40,14 +40,18 @@ hipError_t launch_topk(const float* scores, const int32_t* seq_lens, int B, int 
 // sel_slots (with sel): the list's blocks live in cache page b*num_slots + slot;
 // block_lse (with sel, nullable): ln of each list block's summed exp-logits per query head
 // kvq: 0 = pools of the storage dtype, 8 = FP8 E4M3 code pools, 4 = INT4 code
-// pools (16-bit dtypes); code pools need kv_scales
+// pools (16-bit dtypes); code pools need kv_scales.  cold = 8 / 4 (with kvq 0):
+// tiered pools, page p read from k_cold / v_cold in that format when
+// page_tier[p] != 0 (16-bit dtypes, G >= 2)
 hipError_t launch_paged_attn(int dtype, int D, int G, int kvq, const void* q,
                              const void* k_cache, const void* v_cache, const float* kv_scales,
                              const int32_t* block_table, const int32_t* seq_lens,
                              const int32_t* sel, const int32_t* sel_count, int sel_stride,
                              const int32_t* sel_slots, int num_slots, int B, int Hq, int Hkv,
                              int maxN, int S, float scale, float* part_o, float* part_m,
-                             float* part_l, float* block_lse, hipStream_t stream);
+                             float* part_l, float* block_lse, hipStream_t stream, int cold = 0,
+                             const void* k_cold = nullptr, const void* v_cold = nullptr,
+                             const uint8_t* page_tier = nullptr);
 
 hipError_t launch_cache_plan(const int32_t* sel, const int32_t* sel_count, int sel_stride, int B,
                              int Hkv, int maxN, int C, int32_t* slot_block, int32_t* block_slot,

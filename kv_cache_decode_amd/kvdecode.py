@@ -28,9 +28,11 @@ DTYPE_CODES = {"f32": KV_F32, "f16": KV_F16, "bf16": KV_BF16}
 EXPORTS = (
     "kv_block_meta_build", "kv_block_mean_build", "kv_append_token", "kv_decode_select",
     "kv_score_topk_workspace_size", "kv_block_score_topk", "kv_max_forced_blocks",
-    "kv_block_select", "kv_auto_num_splits", "kv_auto_num_splits_fp8", "kv_paged_decode_attn", "kv_decode_combine",
+    "kv_block_select", "kv_auto_num_splits", "kv_auto_num_splits_fp8",
+    "kv_auto_num_splits_tiered", "kv_paged_decode_attn", "kv_decode_combine",
     "kv_quantize_pages_fp8", "kv_paged_decode_attn_fp8", "kv_quantize_pages_int4",
-    "kv_paged_decode_attn_int4", "kv_cache_plan", "kv_cache_fetch",
+    "kv_paged_decode_attn_int4", "kv_paged_decode_attn_tiered", "kv_cache_plan",
+    "kv_cache_fetch",
     "kv_cached_decode_attn", "kv_cache_slot_mass", "kv_check_tables", "kv_probe_stream_read",
     "kv_probe_gather_read", "kv_host_alloc", "kv_host_free",
     "kv_status_string", "kv_last_error_message",
@@ -91,12 +93,15 @@ def _load() -> ctypes.CDLL:
         "kv_block_score_topk": (I32, [S, P, P, P, P, I32, P, P, P, P, SZ, P]),
         "kv_auto_num_splits": (I32, [S, I32]),
         "kv_auto_num_splits_fp8": (I32, [S, I32]),
+        "kv_auto_num_splits_tiered": (I32, [S, I32]),
         "kv_paged_decode_attn": (I32, [S, P, P, P, P, P, P, P, I32, F, I32, P, P, P, P]),
         "kv_decode_combine": (I32, [S, I32, P, P, P, P, P, P]),
         "kv_quantize_pages_fp8": (I32, [S, P, P, P, P, I32, P, P, P, P]),
         "kv_paged_decode_attn_fp8": (I32, [S, P, P, P, P, P, P, P, P, I32, F, I32, P, P, P, P]),
         "kv_quantize_pages_int4": (I32, [S, P, P, P, P, I32, P, P, P, P]),
         "kv_paged_decode_attn_int4": (I32, [S, P, P, P, P, P, P, P, P, I32, F, I32, P, P, P, P]),
+        "kv_paged_decode_attn_tiered": (I32, [S, P, P, P, P, P, P, I32, P, P, P, P, P, I32, F, I32,
+                                              P, P, P, P]),
         "kv_cache_plan": (I32, [S, I32, P, P, I32, P, P, P, P, P, P, P, P]),
         "kv_cache_fetch": (I32, [S, I32, P, P, P, P, P, P, I32, P, P, P]),
         "kv_cached_decode_attn": (I32, [S, I32, P, P, P, P, P, P, P, I32, F, I32, P, P, P, P, P]),
@@ -202,6 +207,10 @@ def kv_auto_num_splits_fp8(shape: KVShape, blocks_per_unit: int) -> int:
     return int(_lib.kv_auto_num_splits_fp8(ctypes.byref(shape), blocks_per_unit))
 
 
+def kv_auto_num_splits_tiered(shape: KVShape, blocks_per_unit: int) -> int:
+    return int(_lib.kv_auto_num_splits_tiered(ctypes.byref(shape), blocks_per_unit))
+
+
 def kv_max_forced_blocks(shape: KVShape, sink_tokens: int, local_tokens: int) -> int:
     return int(_lib.kv_max_forced_blocks(ctypes.byref(shape), sink_tokens, local_tokens))
 
@@ -272,6 +281,23 @@ def kv_paged_decode_attn_int4(shape: KVShape, q: Buf, k_int4: Buf, v_int4: Buf, 
                                           _p(sel_blocks), _p(sel_count), sel_stride, scale,
                                           num_splits, _p(part_o), _p(part_m), _p(part_l),
                                           _stream(stream)))
+
+
+KV_COLD_FP8 = 8
+KV_COLD_INT4 = 4
+
+
+def kv_paged_decode_attn_tiered(shape: KVShape, q: Buf, k_cache: Buf, v_cache: Buf, k_cold: Buf,
+                                v_cold: Buf, kv_scales: Buf, cold_format: int, page_tier: Buf,
+                                block_table: Buf, seq_lens: Buf, sel_blocks: Buf, sel_count: Buf,
+                                sel_stride: int, scale: float, num_splits: int, part_o: Buf,
+                                part_m: Buf, part_l: Buf, stream=None) -> None:
+    _check(_lib.kv_paged_decode_attn_tiered(ctypes.byref(shape), _p(q), _p(k_cache), _p(v_cache),
+                                            _p(k_cold), _p(v_cold), _p(kv_scales), cold_format,
+                                            _p(page_tier), _p(block_table), _p(seq_lens),
+                                            _p(sel_blocks), _p(sel_count), sel_stride, scale,
+                                            num_splits, _p(part_o), _p(part_m), _p(part_l),
+                                            _stream(stream)))
 
 
 def kv_cache_plan(shape: KVShape, num_slots: int, sel_blocks: Buf, sel_count: Buf,

@@ -271,6 +271,29 @@ class DeviceWorkload:
         self.combine(S, stream)
         return S
 
+    def attention_tiered(self, sparse: bool, cold: str, page_tier, num_splits: Optional[int] = None,
+                         stream=None):
+        """kv_paged_decode_attn_tiered: hot pages from the 16-bit pools, pages with
+        page_tier != 0 from the FP8 (cold="fp8") or INT4 (cold="int4") code pools."""
+        S = num_splits or kd.kv_auto_num_splits_tiered(
+            self.shape, self.topk if sparse else self.spec.max_blocks)
+        po, pm, pl = self.partials(S)
+        sel, cnt, stride = (self.sel, self.sel_count, self.topk) if sparse else (None, None, 0)
+        if cold == "fp8":
+            kc, vc, sc, fmt = self.k8, self.v8, self.kv_scales, kd.KV_COLD_FP8
+        else:
+            kc, vc, sc, fmt = self.k4, self.v4, self.kv_scales4, kd.KV_COLD_INT4
+        kd.kv_paged_decode_attn_tiered(self.shape, self.q, self.k_cache, self.v_cache, kc, vc, sc,
+                                       fmt, page_tier, self.block_table, self.seq_lens, sel, cnt,
+                                       stride, self.scale, S, po, pm, pl, stream)
+        return S
+
+    def decode_tiered(self, sparse: bool, cold: str, page_tier, num_splits: Optional[int] = None,
+                      stream=None):
+        S = self.attention_tiered(sparse, cold, page_tier, num_splits, stream)
+        self.combine(S, stream)
+        return S
+
     # ------------------------------------------------------------ GPU block cache
     def cache_init(self, num_slots: int, k: int):
         """Cache pools [B * C, Hkv, bs, D] and an empty directory for lists of k blocks."""

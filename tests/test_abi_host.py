@@ -376,3 +376,25 @@ def test_check_tables_argument_checks():
     expect(kd.KV_ERR_INVALID_ARG, lambda stream: f(s, A16, A16, A16, None, 4, A16, stream=stream))
     expect(kd.KV_ERR_INVALID_ARG, lambda stream: f(s, A16, A16, A16, A16, 0, A16, stream=stream))
     expect(kd.KV_ERR_ALIGNMENT, lambda stream: f(s, A16, ODD, None, None, 0, A16, stream=stream))
+
+
+def test_tiered_argument_checks():
+    s = shape()
+    f = kd.kv_paged_decode_attn_tiered
+
+    def call(**kw):
+        args = dict(q=A16, k_cache=A16, v_cache=A16, k_cold=A16, v_cold=A16, kv_scales=A16,
+                    cold_format=kd.KV_COLD_INT4, page_tier=A16, block_table=A16, seq_lens=A16,
+                    sel_blocks=None, sel_count=None, sel_stride=0, scale=0.1, num_splits=2,
+                    part_o=A16, part_m=A16, part_l=A16)
+        args.update(kw)
+        return lambda stream: f(s, stream=stream, **args)
+
+    expect(kd.KV_ERR_INVALID_ARG, call(cold_format=5))
+    expect(kd.KV_ERR_INVALID_ARG, call(page_tier=None))
+    expect(kd.KV_ERR_INVALID_ARG, call(k_cold=None))
+    expect(kd.KV_ERR_ALIGNMENT, call(v_cold=A4))
+    expect(kd.KV_ERR_INVALID_ARG, call(num_splits=0))
+    expect(kd.KV_ERR_UNSUPPORTED, lambda stream: f(shape(dtype="f32"), A16, A16, A16, A16, A16,
+                                                   A16, kd.KV_COLD_INT4, A16, A16, A16, None,
+                                                   None, 0, 0.1, 2, A16, A16, A16, stream=stream))
