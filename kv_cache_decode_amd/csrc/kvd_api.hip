@@ -99,7 +99,8 @@ kv_status attn_common(const kv_shape* shape, int kvq, const void* q, const void*
                       const int32_t* seq_lens, const int32_t* sel_blocks,
                       const int32_t* sel_count, int32_t sel_stride, float scale,
                       int32_t num_splits, float* part_o, float* part_m, float* part_l,
-                      void* stream) {
+                      void* stream, int cold = 0, const void* k_cold = nullptr,
+                      const void* v_cold = nullptr, const uint8_t* page_tier = nullptr) {
   kv_status st = check_shape(shape);
   if (st != KV_OK) return st;
   if (num_splits < 1 || num_splits > 65535 * 4)
@@ -123,9 +124,11 @@ kv_status attn_common(const kv_shape* shape, int kvq, const void* q, const void*
                              kv_scales, block_table, seq_lens, sel_blocks, sel_count, sel_stride,
                              nullptr, 0, shape->num_seqs, shape->num_q_heads, shape->num_kv_heads,
                              shape->max_blocks_per_seq, num_splits, scale, part_o, part_m, part_l,
-                             nullptr, (hipStream_t)stream),
-      kvq == 8 ? "kv_paged_decode_attn_fp8 launch"
-               : (kvq == 4 ? "kv_paged_decode_attn_int4 launch" : "kv_paged_decode_attn launch"));
+                             nullptr, (hipStream_t)stream, cold, k_cold, v_cold, page_tier),
+      cold ? "kv_paged_decode_attn_tiered launch"
+           : (kvq == 8 ? "kv_paged_decode_attn_fp8 launch"
+                       : (kvq == 4 ? "kv_paged_decode_attn_int4 launch"
+                                   : "kv_paged_decode_attn launch")));
 }
 
 }  // namespace
@@ -497,31 +500,9 @@ kv_status kv_paged_decode_attn_tiered(const kv_shape* shape, const void* q, cons
     return fail(KV_ERR_INVALID_ARG, "k_cold, v_cold, kv_scales and page_tier are required");
   if (!aligned(k_cold, 16) || !aligned(v_cold, 16) || !aligned(kv_scales, 8))
     return fail(KV_ERR_ALIGNMENT, "the cold pools must be 16-byte aligned, kv_scales 8-byte");
-  // the 16-bit checks and the launch
-  if (num_splits < 1 || num_splits > 65535 * 4)
-    return fail(KV_ERR_INVALID_ARG, "num_splits=%d must be in [1, 262140]", num_splits);
-  if (!q || !k_cache || !v_cache || !block_table || !seq_lens || !part_o || !part_m || !part_l)
-    return fail(KV_ERR_INVALID_ARG, "q, k_cache, v_cache, block_table, seq_lens and partials are required");
-  if ((sel_blocks == nullptr) != (sel_count == nullptr))
-    return fail(KV_ERR_INVALID_ARG, "sel_blocks and sel_count go together");
-  if (sel_blocks && sel_stride < 1)
-    return fail(KV_ERR_INVALID_ARG, "sel_stride=%d must be >= 1", sel_stride);
-  if (!(scale > 0.0f) || !(scale < INFINITY))
-    return fail(KV_ERR_INVALID_ARG, "scale must be finite and positive");
-  if (!aligned(q, 16) || !aligned(k_cache, 16) || !aligned(v_cache, 16) || !aligned(part_o, 16))
-    return fail(KV_ERR_ALIGNMENT, "q, k_cache, v_cache and part_o must be 16-byte aligned");
-  if (!aligned(block_table, 4) || !aligned(seq_lens, 4) || !aligned(part_m, 4) ||
-      !aligned(part_l, 4) || (sel_blocks && (!aligned(sel_blocks, 4) || !aligned(sel_count, 4))))
-    return fail(KV_ERR_ALIGNMENT, "integer and partial arrays must be 4-byte aligned");
-  const int G = shape->num_q_heads / shape->num_kv_heads;
-  return hip_status(
-      kvd::launch_paged_attn(shape->dtype, shape->head_dim, G, 0, q, k_cache, v_cache, kv_scales,
-                             block_table, seq_lens, sel_blocks, sel_count, sel_stride, nullptr, 0,
-                             shape->num_seqs, shape->num_q_heads, shape->num_kv_heads,
-                             shape->max_blocks_per_seq, num_splits, scale, part_o, part_m, part_l,
-                             nullptr, (hipStream_t)stream, cold_format, k_cold, v_cold,
-                             page_tier),
-      "kv_paged_decode_attn_tiered launch");
+  return attn_common(shape, 0, q, k_cache, v_cache, kv_scales, block_table, seq_lens, sel_blocks,
+                     sel_count, sel_stride, scale, num_splits, part_o, part_m, part_l, stream,
+                     cold_format, k_cold, v_cold, page_tier);
 }
 
 kv_status kv_decode_combine(const kv_shape* shape, int32_t num_splits, const float* part_o,
