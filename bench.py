@@ -94,6 +94,23 @@ def stage_bytes(spec, topk: int, s_sparse: int, s_dense: int) -> dict:
     }
 
 
+def tiered_bytes(spec, block_table, tier, fmt: str, splits: int):
+    """Algorithmic bytes of one dense attention over tiered pools: per (page, KV
+    head) unit a hot page gives 2 * 16 * D 16-bit values, a cold one its codes
+    (D bytes per row in FP8, D / 2 in INT4) and two fp32 scales; every unit adds
+    its 4-byte table entry and its tier byte; q in, the split partials out.
+    Returns (bytes, fraction of the listed pages that are cold)."""
+    used = np.concatenate([block_table[b, :spec.blocks(b)] for b in range(spec.num_seqs)])
+    n_cold = int((tier[used] != 0).sum())
+    n_hot = len(used) - n_cold
+    D, Hkv, B, Hq = spec.head_dim, spec.num_kv_heads, spec.num_seqs, spec.num_q_heads
+    tile = spec.block_size * D
+    code_tile = tile if fmt == "fp8" else tile // 2
+    units = Hkv * (n_hot * 2 * tile * spec.elem_bytes + n_cold * (2 * code_tile + 8)) \
+        + len(used) * Hkv * (4 + 1)
+    return units + B * Hq * D * spec.elem_bytes + B * Hq * splits * (D + 2) * 4, n_cold / len(used)
+
+
 def variant_bytes(spec, topk: int) -> dict:
     """Algorithmic bytes of the selection variants: the mean-key index holds one
     fp32 row of D per (page, KV head)."""
@@ -402,14 +419,8 @@ def time_codes(args, copies, k, time_loop, graph_us, fmt: str):
     tier = torch.from_numpy(tier_np).to(copies[0].device)
     s_tier = kd.kv_auto_num_splits_tiered(copies[0].shape, spec.max_blocks)
     res["tiered_dense_us"] = kernel_us(lambda c: c.attention_tiered(False, fmt, tier, s_tier))
-    used = np.concatenate([data.block_table[b, :spec.blocks(b)] for b in range(spec.num_seqs)])
-    n_cold = int(tier_np[used].sum())
-    n_hot = len(used) - n_cold
-    tile = spec.block_size * spec.head_dim
-    code_tile = tile if fmt == "fp8" else tile // 2
-    res["tiered_dense_bytes"] = spec.num_kv_heads * (n_hot * 2 * tile * spec.elem_bytes
-                                                     + n_cold * (2 * code_tile + 8))
-    res["tiered_cold_fraction"] = n_cold / len(used)
+    res["tiered_dense_bytes"], res["tiered_cold_fraction"] = tiered_bytes(spec, data.block_table,
+                                                                          tier_np, fmt, s_tier)
     res["tiered_splits"] = s_tier
     return res
 
