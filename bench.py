@@ -568,6 +568,7 @@ def run_zero_copy(args):
             fp8_ms.append(e[0].elapsed_time(e[1]))
     # and over INT4 code pages in host memory: a quarter of the bytes
     int4_ms = []
+    cache4 = None
     if not args.no_variants:
         dw.quantize_int4(host=True)
         for _ in range(3):
@@ -578,6 +579,8 @@ def run_zero_copy(args):
             e[1].record()
             torch.cuda.synchronize()
             int4_ms.append(e[0].elapsed_time(e[1]))
+        # the block cache over the INT4 host pages: codes and scales in the cache
+        cache4 = time_cache_trajectory(args, dw, data, k, S, codes="int4")
     # KVDrive's tiering: the most recent quarter of each sequence hot in HBM (16-bit
     # pages), the rest cold INT4 pages in host memory; each selected block is read
     # from its own tier, so only the cold ones cross the link
@@ -674,6 +677,7 @@ def run_zero_copy(args):
                 "speedup_vs_bf16": attn / f4}
     return {
         "block_cache": cache,
+        "block_cache_int4": cache4,
         "fp8_pages": fp8,
         "int4_pages": int4,
         "tiered_int4": tiered,
@@ -696,11 +700,13 @@ CACHE_STEPS = 32
 CACHE_RHO = 0.95
 
 
-def time_cache_trajectory(args, dw, data, k, S):
+def time_cache_trajectory(args, dw, data, k, S, codes=None):
     """Per-step time of a CACHE_STEPS-step decode trajectory (queries: the seeded
     AR(1) walk of workload.query_trajectory, rho = CACHE_RHO), plain zero-copy
     against the GPU block cache at several capacities.  The trajectory runs once
-    untimed to fill the cache (and to count the fetched blocks), then once timed."""
+    untimed to fill the cache (and to count the fetched blocks), then once timed.
+    With ``codes`` ("fp8" / "int4", after the matching quantize_* call) both the
+    plain step and the cache read the code pages in host memory."""
     import torch
     from kv_cache_decode_amd import workload as wl
     from kv_cache_decode_amd.step import storage_tensor
@@ -723,17 +729,21 @@ def time_cache_trajectory(args, dw, data, k, S):
         torch.cuda.synchronize()
         return e0.elapsed_time(e1) * 1e3 / len(qs)
 
+    attend = {None: dw.attention, "fp8": dw.attention_fp8, "int4": dw.attention_int4}[codes]
+
     def plain():
         dw.score_topk(k)
-        dw.attention(sparse=True, num_splits=S)
+        attend(sparse=True, num_splits=S)
         dw.combine(S)
 
     run(plain)
     res = {"steps": CACHE_STEPS, "rho": CACHE_RHO, "topk_blocks": k,
-           "plain_zero_copy_step_us": run(plain)}
-    tile = spec.block_size * spec.head_dim * spec.elem_bytes * 2        # K + V of one block
+           "pages": codes or spec.dtype, "plain_zero_copy_step_us": run(plain)}
+    rows = spec.block_size * spec.head_dim                              # elements of one tile
+    tile = {None: 2 * rows * spec.elem_bytes, "fp8": 2 * rows + 8,       # K + V (+ scales)
+            "int4": rows + 8}[codes]
     for C in (256, 512, 1024):
-        dw.cache_init(C, k)
+        dw.cache_init(C, k, codes=codes)
         counts = []
         run(lambda: dw.cache_step(k, S), counts)                        # cold start, counted
         cold = int(sum(int(c.sum()) for c in counts))
@@ -749,7 +759,7 @@ def time_cache_trajectory(args, dw, data, k, S):
             "host_link_bytes_per_step": float(np.mean(warm)) * tile,
             "cold_fetched_blocks_first_pass": cold,
         }
-        del dw.cache_k, dw.cache_v
+        del dw.cache_k, dw.cache_v, dw.cache_scales
     dw.q = q0
     torch.cuda.empty_cache()
     return res

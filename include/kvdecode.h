@@ -17,6 +17,8 @@
  *   kv_cache_fetch        copy only the missing blocks into their cache slots
  *   kv_cached_decode_attn decode attention over the cached blocks, with each
  *                         block's log-sum-exp for the next eviction
+ *   kv_cache_fetch_codes, kv_cached_decode_attn_codes  the same over FP8 / INT4
+ *                         code pools: the cache holds codes and scales
  *   kv_cache_slot_mass    eviction mass of every cache slot after a step
  *   kv_paged_decode_attn  split-K softmax decode attention, dense or over selected blocks
  *   kv_decode_combine     log-sum-exp merge of the split partials
@@ -456,6 +458,42 @@ kv_status kv_cached_decode_attn(const kv_shape* shape, int32_t num_slots, const 
                                 int32_t sel_stride, float scale, int32_t num_splits,
                                 float* part_o, float* part_m, float* part_l, float* block_lse,
                                 void* stream);
+
+/*
+ * The block cache over code pools (KVDrive §5.1's GPU window combined with
+ * §11's quantised cold blocks: the host pool holds FP8 or INT4 pages, so the
+ * delta fetch moves a quarter or an eighth of the 16-bit bytes).  The cache
+ * pools keep the pool's format: cache_k / cache_v [B * C, Hkv, 16, D] bytes of
+ * E4M3 codes (code_format KV_COLD_FP8) or [B * C, Hkv, 16, D / 2] INT4 bytes
+ * (KV_COLD_INT4), and cache_scales fp32 [B * C, Hkv, 2] beside them.
+ *
+ * kv_cache_fetch_codes: kv_cache_fetch over the code pools k_codes / v_codes
+ * (the layouts of kv_quantize_pages_fp8 / _int4, device memory or kv_host_alloc
+ * memory with KV_FLAG_HOST_KV); each fetched tile's scale pair
+ * kv_scales[page, j, 0..1] (device or kv_host_alloc memory) is copied to
+ * cache_scales[b * C + slot, j, 0..1].
+ *
+ * kv_cached_decode_attn_codes: kv_cached_decode_attn over the code cache; the
+ * result is what kv_paged_decode_attn_fp8 / _int4 compute with the same list,
+ * splits and codes (each block read from its cache page and scales).  INT4
+ * needs fp16 or bf16 (KV_ERR_UNSUPPORTED for fp32); an unknown code_format is
+ * KV_ERR_INVALID_ARG.
+ */
+kv_status kv_cache_fetch_codes(const kv_shape* shape, int32_t num_slots, int32_t code_format,
+                               const uint8_t* k_codes, const uint8_t* v_codes,
+                               const float* kv_scales, const int32_t* block_table,
+                               const int32_t* fetch_block, const int32_t* fetch_slot,
+                               const int32_t* fetch_count, int32_t fetch_stride,
+                               uint8_t* cache_k, uint8_t* cache_v, float* cache_scales,
+                               void* stream);
+kv_status kv_cached_decode_attn_codes(const kv_shape* shape, int32_t num_slots,
+                                      int32_t code_format, const void* q, const uint8_t* cache_k,
+                                      const uint8_t* cache_v, const float* cache_scales,
+                                      const int32_t* seq_lens, const int32_t* sel_blocks,
+                                      const int32_t* sel_count, const int32_t* sel_slots,
+                                      int32_t sel_stride, float scale, int32_t num_splits,
+                                      float* part_o, float* part_m, float* part_l,
+                                      float* block_lse, void* stream);
 
 /*
  * Eviction mass after a step: slot_mass[b, j, :] = 0, then for every list

@@ -560,39 +560,44 @@ kv_status kv_cache_plan(const kv_shape* shape, int32_t num_slots, const int32_t*
                     "kv_cache_plan launch");
 }
 
-kv_status kv_cache_fetch(const kv_shape* shape, int32_t num_slots, const void* k_cache,
-                         const void* v_cache, const int32_t* block_table,
-                         const int32_t* fetch_block, const int32_t* fetch_slot,
-                         const int32_t* fetch_count, int32_t fetch_stride, void* cache_k,
-                         void* cache_v, void* stream) {
-  kv_status st = check_cache(shape, num_slots, fetch_stride);
-  if (st != KV_OK) return st;
-  if (!k_cache || !v_cache || !block_table || !fetch_block || !fetch_slot || !fetch_count ||
+}  // extern "C"
+
+namespace {
+
+// Delta fetch of tiles of tile_bytes (16-bit / fp32 pools, or code pools with
+// their scales: kv_scales != nullptr).
+kv_status fetch_common(const kv_shape* shape, int32_t num_slots, int tile_bytes,
+                       const void* k_pool, const void* v_pool, const float* kv_scales,
+                       const int32_t* block_table, const int32_t* fetch_block,
+                       const int32_t* fetch_slot, const int32_t* fetch_count,
+                       int32_t fetch_stride, void* cache_k, void* cache_v, float* cache_scales,
+                       void* stream, const char* name) {
+  if (!k_pool || !v_pool || !block_table || !fetch_block || !fetch_slot || !fetch_count ||
       !cache_k || !cache_v)
-    return fail(KV_ERR_INVALID_ARG, "every array of kv_cache_fetch is required");
-  if (!aligned(k_cache, 16) || !aligned(v_cache, 16) || !aligned(cache_k, 16) ||
+    return fail(KV_ERR_INVALID_ARG, "every array of %s is required", name);
+  if (!aligned(k_pool, 16) || !aligned(v_pool, 16) || !aligned(cache_k, 16) ||
       !aligned(cache_v, 16))
     return fail(KV_ERR_ALIGNMENT, "the pools and the cache pools must be 16-byte aligned");
   if (!aligned(block_table, 4) || !aligned(fetch_block, 4) || !aligned(fetch_slot, 4) ||
       !aligned(fetch_count, 4))
     return fail(KV_ERR_ALIGNMENT, "integer arrays must be 4-byte aligned");
-  return hip_status(kvd::launch_cache_fetch(shape->dtype, shape->head_dim, k_cache, v_cache,
-                                            block_table, fetch_block, fetch_slot, fetch_count,
-                                            fetch_stride, shape->num_seqs, shape->num_kv_heads,
+  return hip_status(kvd::launch_cache_fetch(tile_bytes, k_pool, v_pool, kv_scales, block_table,
+                                            fetch_block, fetch_slot, fetch_count, fetch_stride,
+                                            shape->num_seqs, shape->num_kv_heads,
                                             shape->max_blocks_per_seq, num_slots, cache_k,
-                                            cache_v, (hipStream_t)stream),
-                    "kv_cache_fetch launch");
+                                            cache_v, cache_scales, (hipStream_t)stream),
+                    name);
 }
 
-kv_status kv_cached_decode_attn(const kv_shape* shape, int32_t num_slots, const void* q,
-                                const void* cache_k, const void* cache_v,
-                                const int32_t* seq_lens, const int32_t* sel_blocks,
-                                const int32_t* sel_count, const int32_t* sel_slots,
-                                int32_t sel_stride, float scale, int32_t num_splits,
-                                float* part_o, float* part_m, float* part_l, float* block_lse,
-                                void* stream) {
-  kv_status st = check_cache(shape, num_slots, sel_stride);
-  if (st != KV_OK) return st;
+// Attention over the cached blocks: kvq 0 (16-bit / fp32 cache pools) or a
+// code format with the cache's scales.
+kv_status cached_attn_common(const kv_shape* shape, int32_t num_slots, int kvq, const void* q,
+                             const void* cache_k, const void* cache_v, const float* cache_scales,
+                             const int32_t* seq_lens, const int32_t* sel_blocks,
+                             const int32_t* sel_count, const int32_t* sel_slots,
+                             int32_t sel_stride, float scale, int32_t num_splits, float* part_o,
+                             float* part_m, float* part_l, float* block_lse, void* stream,
+                             const char* name) {
   if (!sel_blocks || !sel_count || !sel_slots)
     return fail(KV_ERR_INVALID_ARG, "sel_blocks, sel_count and sel_slots are required");
   if (!aligned(sel_slots, 4) || (block_lse && !aligned(block_lse, 4)))
@@ -609,16 +614,101 @@ kv_status kv_cached_decode_attn(const kv_shape* shape, int32_t num_slots, const 
       !aligned(sel_blocks, 4) || !aligned(sel_count, 4))
     return fail(KV_ERR_ALIGNMENT, "integer and partial arrays must be 4-byte aligned");
   // the cache pools hold num_seqs * num_slots pages and are device memory
-  kv_shape cs = *shape;
-  cs.flags = 0;
   const int G = shape->num_q_heads / shape->num_kv_heads;
   return hip_status(
-      kvd::launch_paged_attn(cs.dtype, cs.head_dim, G, 0, q, cache_k, cache_v, nullptr,
-                             /*block_table=*/nullptr, seq_lens, sel_blocks, sel_count,
-                             sel_stride, sel_slots, num_slots, cs.num_seqs, cs.num_q_heads,
-                             cs.num_kv_heads, cs.max_blocks_per_seq, num_splits, scale, part_o,
-                             part_m, part_l, block_lse, (hipStream_t)stream),
-      "kv_cached_decode_attn launch");
+      kvd::launch_paged_attn(shape->dtype, shape->head_dim, G, kvq, q, cache_k, cache_v,
+                             cache_scales, /*block_table=*/nullptr, seq_lens, sel_blocks,
+                             sel_count, sel_stride, sel_slots, num_slots, shape->num_seqs,
+                             shape->num_q_heads, shape->num_kv_heads, shape->max_blocks_per_seq,
+                             num_splits, scale, part_o, part_m, part_l, block_lse,
+                             (hipStream_t)stream),
+      name);
+}
+
+// Bytes of one (page, KV head) tile of a code pool; 0 for an unknown format.
+int code_tile_bytes(const kv_shape* shape, int32_t code_format) {
+  const int tile = shape->block_size * shape->head_dim;
+  return code_format == KV_COLD_FP8 ? tile : (code_format == KV_COLD_INT4 ? tile / 2 : 0);
+}
+
+kv_status check_code_format(const kv_shape* shape, int32_t code_format) {
+  if (code_format != KV_COLD_FP8 && code_format != KV_COLD_INT4)
+    return fail(KV_ERR_INVALID_ARG, "code_format=%d must be KV_COLD_FP8 or KV_COLD_INT4",
+                code_format);
+  if (code_format == KV_COLD_INT4 && shape->dtype == KV_F32)
+    return fail(KV_ERR_UNSUPPORTED, "INT4 pages are read with fp16 or bf16 queries");
+  return KV_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+kv_status kv_cache_fetch(const kv_shape* shape, int32_t num_slots, const void* k_cache,
+                         const void* v_cache, const int32_t* block_table,
+                         const int32_t* fetch_block, const int32_t* fetch_slot,
+                         const int32_t* fetch_count, int32_t fetch_stride, void* cache_k,
+                         void* cache_v, void* stream) {
+  kv_status st = check_cache(shape, num_slots, fetch_stride);
+  if (st != KV_OK) return st;
+  const int tile = shape->block_size * shape->head_dim * (shape->dtype == KV_F32 ? 4 : 2);
+  return fetch_common(shape, num_slots, tile, k_cache, v_cache, nullptr, block_table,
+                      fetch_block, fetch_slot, fetch_count, fetch_stride, cache_k, cache_v,
+                      nullptr, stream, "kv_cache_fetch launch");
+}
+
+kv_status kv_cache_fetch_codes(const kv_shape* shape, int32_t num_slots, int32_t code_format,
+                               const uint8_t* k_codes, const uint8_t* v_codes,
+                               const float* kv_scales, const int32_t* block_table,
+                               const int32_t* fetch_block, const int32_t* fetch_slot,
+                               const int32_t* fetch_count, int32_t fetch_stride,
+                               uint8_t* cache_k, uint8_t* cache_v, float* cache_scales,
+                               void* stream) {
+  kv_status st = check_cache(shape, num_slots, fetch_stride);
+  if (st != KV_OK) return st;
+  if ((st = check_code_format(shape, code_format)) != KV_OK) return st;
+  if (!kv_scales || !cache_scales)
+    return fail(KV_ERR_INVALID_ARG, "kv_scales and cache_scales are required");
+  if (!aligned(kv_scales, 8) || !aligned(cache_scales, 8))
+    return fail(KV_ERR_ALIGNMENT, "kv_scales and cache_scales must be 8-byte aligned");
+  return fetch_common(shape, num_slots, code_tile_bytes(shape, code_format), k_codes, v_codes,
+                      kv_scales, block_table, fetch_block, fetch_slot, fetch_count, fetch_stride,
+                      cache_k, cache_v, cache_scales, stream, "kv_cache_fetch_codes launch");
+}
+
+kv_status kv_cached_decode_attn(const kv_shape* shape, int32_t num_slots, const void* q,
+                                const void* cache_k, const void* cache_v,
+                                const int32_t* seq_lens, const int32_t* sel_blocks,
+                                const int32_t* sel_count, const int32_t* sel_slots,
+                                int32_t sel_stride, float scale, int32_t num_splits,
+                                float* part_o, float* part_m, float* part_l, float* block_lse,
+                                void* stream) {
+  kv_status st = check_cache(shape, num_slots, sel_stride);
+  if (st != KV_OK) return st;
+  return cached_attn_common(shape, num_slots, 0, q, cache_k, cache_v, nullptr, seq_lens,
+                            sel_blocks, sel_count, sel_slots, sel_stride, scale, num_splits,
+                            part_o, part_m, part_l, block_lse, stream,
+                            "kv_cached_decode_attn launch");
+}
+
+kv_status kv_cached_decode_attn_codes(const kv_shape* shape, int32_t num_slots,
+                                      int32_t code_format, const void* q, const uint8_t* cache_k,
+                                      const uint8_t* cache_v, const float* cache_scales,
+                                      const int32_t* seq_lens, const int32_t* sel_blocks,
+                                      const int32_t* sel_count, const int32_t* sel_slots,
+                                      int32_t sel_stride, float scale, int32_t num_splits,
+                                      float* part_o, float* part_m, float* part_l,
+                                      float* block_lse, void* stream) {
+  kv_status st = check_cache(shape, num_slots, sel_stride);
+  if (st != KV_OK) return st;
+  if ((st = check_code_format(shape, code_format)) != KV_OK) return st;
+  if (!cache_scales) return fail(KV_ERR_INVALID_ARG, "cache_scales is required");
+  if (!aligned(cache_scales, 8))
+    return fail(KV_ERR_ALIGNMENT, "cache_scales must be 8-byte aligned");
+  return cached_attn_common(shape, num_slots, code_format, q, cache_k, cache_v, cache_scales,
+                            seq_lens, sel_blocks, sel_count, sel_slots, sel_stride, scale,
+                            num_splits, part_o, part_m, part_l, block_lse, stream,
+                            "kv_cached_decode_attn_codes launch");
 }
 
 kv_status kv_cache_slot_mass(const kv_shape* shape, int32_t num_slots, const float* block_lse,

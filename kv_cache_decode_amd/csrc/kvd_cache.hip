@@ -227,36 +227,49 @@ __global__ __launch_bounds__(kPlanThreads) void cache_plan_kernel(
 // page b*C + fetch_slot[b, j, k].  Source bytes are read once (non-temporal;
 // they may be mapped host memory), the cache tile is read by the attention
 // right after and is stored normally.
-template <typename DT, int D>
+// One wave per missing (block, KV head) tile.  TILE is the tile's size in the
+// pools' format: 16 * D elements of a 16-bit or fp32 pool, or the codes of a
+// code pool (16 * D bytes of E4M3, 16 * D / 2 of INT4); a code pool's tile also
+// brings its (k, v) scale pair along.
+template <int TILE>
 __global__ __launch_bounds__(kWave) void cache_fetch_kernel(
     const void* __restrict__ k_pool, const void* __restrict__ v_pool,
-    const int32_t* __restrict__ block_table, const int32_t* __restrict__ fetch_block,
-    const int32_t* __restrict__ fetch_slot, const int32_t* __restrict__ fetch_count,
-    int fetch_stride, int Hkv, int maxN, int C, void* __restrict__ cache_k,
-    void* __restrict__ cache_v) {
-  using St = typename DT::storage;
-  constexpr int TILE = kBlockSize * D * (int)sizeof(St);   // bytes of one (page, head) tile
-  constexpr int ITER = TILE / (16 * kWave);
-  static_assert(TILE % (16 * kWave) == 0, "tile is a multiple of one wave load");
+    const float* __restrict__ kv_scales, const int32_t* __restrict__ block_table,
+    const int32_t* __restrict__ fetch_block, const int32_t* __restrict__ fetch_slot,
+    const int32_t* __restrict__ fetch_count, int fetch_stride, int Hkv, int maxN, int C,
+    void* __restrict__ cache_k, void* __restrict__ cache_v, float* __restrict__ cache_scales) {
+  constexpr int ITER = (TILE + 16 * kWave - 1) / (16 * kWave);
+  constexpr bool FULL = TILE % (16 * kWave) == 0;   // else the last load is partial
+  static_assert(TILE % 16 == 0, "tiles are whole 16-byte chunks");
   const int k = blockIdx.x, j = blockIdx.y, b = blockIdx.z;
   const size_t u = (size_t)b * Hkv + j;
   if (k >= fetch_count[u]) return;
   const int n = fetch_block[u * fetch_stride + k];
   const int s = fetch_slot[u * fetch_stride + k];
-  const size_t src = ((size_t)block_table[(size_t)b * maxN + n] * Hkv + j) * TILE;
-  const size_t dst = (((size_t)b * C + s) * Hkv + j) * TILE;
+  const size_t src_unit = (size_t)block_table[(size_t)b * maxN + n] * Hkv + j;
+  const size_t dst_unit = ((size_t)b * C + s) * Hkv + j;
+  const size_t src = src_unit * TILE, dst = dst_unit * TILE;
   const int lane = threadIdx.x;
   uint4 kw[ITER], vw[ITER];
 #pragma unroll
   for (int i = 0; i < ITER; ++i) {
-    kw[i] = load16_stream(static_cast<const uint8_t*>(k_pool) + src + (size_t)(i * kWave + lane) * 16);
-    vw[i] = load16_stream(static_cast<const uint8_t*>(v_pool) + src + (size_t)(i * kWave + lane) * 16);
+    const size_t off = (size_t)(i * kWave + lane) * 16;
+    if (FULL || off < TILE) {
+      kw[i] = load16_stream(static_cast<const uint8_t*>(k_pool) + src + off);
+      vw[i] = load16_stream(static_cast<const uint8_t*>(v_pool) + src + off);
+    }
   }
+  float2 sc = make_float2(0.0f, 0.0f);
+  if (kv_scales && lane == 0) sc = *reinterpret_cast<const float2*>(kv_scales + src_unit * 2);
 #pragma unroll
   for (int i = 0; i < ITER; ++i) {
-    store16(static_cast<uint8_t*>(cache_k) + dst + (size_t)(i * kWave + lane) * 16, kw[i]);
-    store16(static_cast<uint8_t*>(cache_v) + dst + (size_t)(i * kWave + lane) * 16, vw[i]);
+    const size_t off = (size_t)(i * kWave + lane) * 16;
+    if (FULL || off < TILE) {
+      store16(static_cast<uint8_t*>(cache_k) + dst + off, kw[i]);
+      store16(static_cast<uint8_t*>(cache_v) + dst + off, vw[i]);
+    }
   }
+  if (kv_scales && lane == 0) *reinterpret_cast<float2*>(cache_scales + dst_unit * 2) = sc;
 }
 
 // One 256-thread workgroup per (sequence, KV head): every slot's mass to 0,
@@ -310,20 +323,27 @@ hipError_t launch_cache_plan(const int32_t* sel, const int32_t* sel_count, int s
   return hipErrorInvalidValue;
 }
 
-hipError_t launch_cache_fetch(int dtype, int D, const void* k_pool, const void* v_pool,
-                              const int32_t* block_table, const int32_t* fetch_block,
-                              const int32_t* fetch_slot, const int32_t* fetch_count,
-                              int fetch_stride, int B, int Hkv, int maxN, int C, void* cache_k,
-                              void* cache_v, hipStream_t stream) {
-  return with_dtype(dtype, [&](auto dt) {
-    return with_dim(D, [&](auto d) {
-      hipLaunchKernelGGL((cache_fetch_kernel<decltype(dt), decltype(d)::value>),
-                         dim3(fetch_stride, Hkv, B), dim3(kWave), 0, stream, k_pool, v_pool,
-                         block_table, fetch_block, fetch_slot, fetch_count, fetch_stride, Hkv,
-                         maxN, C, cache_k, cache_v);
-      return hipGetLastError();
-    });
-  });
+hipError_t launch_cache_fetch(int tile_bytes, const void* k_pool, const void* v_pool,
+                              const float* kv_scales, const int32_t* block_table,
+                              const int32_t* fetch_block, const int32_t* fetch_slot,
+                              const int32_t* fetch_count, int fetch_stride, int B, int Hkv,
+                              int maxN, int C, void* cache_k, void* cache_v, float* cache_scales,
+                              hipStream_t stream) {
+  const dim3 grid(fetch_stride, Hkv, B);
+  auto go = [&](auto tile) {
+    hipLaunchKernelGGL((cache_fetch_kernel<decltype(tile)::value>), grid, dim3(kWave), 0, stream,
+                       k_pool, v_pool, kv_scales, block_table, fetch_block, fetch_slot,
+                       fetch_count, fetch_stride, Hkv, maxN, C, cache_k, cache_v, cache_scales);
+    return hipGetLastError();
+  };
+  switch (tile_bytes) {
+    case 512: return go(std::integral_constant<int, 512>{});
+    case 1024: return go(std::integral_constant<int, 1024>{});
+    case 2048: return go(std::integral_constant<int, 2048>{});
+    case 4096: return go(std::integral_constant<int, 4096>{});
+    case 8192: return go(std::integral_constant<int, 8192>{});
+  }
+  return hipErrorInvalidValue;
 }
 
 hipError_t launch_slot_mass(const float* block_lse, const float* lse, const int32_t* sel_count,

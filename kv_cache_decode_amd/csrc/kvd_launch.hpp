@@ -58,11 +58,14 @@ hipError_t launch_cache_plan(const int32_t* sel, const int32_t* sel_count, int s
                              const float* slot_mass, int32_t* sel_slots, int32_t* fetch_block,
                              int32_t* fetch_slot, int32_t* fetch_count, hipStream_t stream);
 
-hipError_t launch_cache_fetch(int dtype, int D, const void* k_pool, const void* v_pool,
-                              const int32_t* block_table, const int32_t* fetch_block,
-                              const int32_t* fetch_slot, const int32_t* fetch_count,
-                              int fetch_stride, int B, int Hkv, int maxN, int C, void* cache_k,
-                              void* cache_v, hipStream_t stream);
+// tile_bytes: one (page, KV head) tile of the pools (512 .. 8192); with
+// kv_scales (code pools) each fetched tile's scale pair goes to cache_scales.
+hipError_t launch_cache_fetch(int tile_bytes, const void* k_pool, const void* v_pool,
+                              const float* kv_scales, const int32_t* block_table,
+                              const int32_t* fetch_block, const int32_t* fetch_slot,
+                              const int32_t* fetch_count, int fetch_stride, int B, int Hkv,
+                              int maxN, int C, void* cache_k, void* cache_v, float* cache_scales,
+                              hipStream_t stream);
 
 hipError_t launch_slot_mass(const float* block_lse, const float* lse, const int32_t* sel_count,
                             const int32_t* sel_slots, int sel_stride, int B, int Hq, int Hkv,

@@ -295,14 +295,25 @@ class DeviceWorkload:
         return S
 
     # ------------------------------------------------------------ GPU block cache
-    def cache_init(self, num_slots: int, k: int):
-        """Cache pools [B * C, Hkv, bs, D] and an empty directory for lists of k blocks."""
+    def cache_init(self, num_slots: int, k: int, codes: Optional[str] = None):
+        """Cache pools [B * C, Hkv, bs, D] and an empty directory for lists of k
+        blocks.  With ``codes`` ("fp8" or "int4", after quantize_fp8 /
+        quantize_int4) the cache holds code pages and their scales, fetched from
+        the code pools."""
         spec, dev = self.spec, self.device
         B, Hq, Hkv, D, bs = spec.num_seqs, spec.num_q_heads, spec.num_kv_heads, spec.head_dim, \
             spec.block_size
         C = num_slots
         self.num_slots = C
-        self.cache_k = torch.zeros((B * C, Hkv, bs, D), dtype=TORCH_DTYPES[spec.dtype], device=dev)
+        self.cache_codes = codes
+        if codes is None:
+            self.cache_k = torch.zeros((B * C, Hkv, bs, D), dtype=TORCH_DTYPES[spec.dtype],
+                                       device=dev)
+            self.cache_scales = None
+        else:
+            width = D if codes == "fp8" else D // 2
+            self.cache_k = torch.zeros((B * C, Hkv, bs, width), dtype=torch.uint8, device=dev)
+            self.cache_scales = torch.zeros((B * C, Hkv, 2), dtype=torch.float32, device=dev)
         self.cache_v = torch.zeros_like(self.cache_k)
         self.slot_block = torch.full((B, Hkv, C), -1, dtype=torch.int32, device=dev)
         self.block_slot = torch.full((B, Hkv, spec.max_blocks), -1, dtype=torch.int32, device=dev)
@@ -318,19 +329,39 @@ class DeviceWorkload:
                          self.slot_block, self.block_slot, self.slot_mass, self.sel_slots,
                          self.fetch_block, self.fetch_slot, self.fetch_count, stream)
 
+    def _code_pools(self):
+        if self.cache_codes == "fp8":
+            return kd.KV_COLD_FP8, self.k8, self.v8, self.kv_scales
+        return kd.KV_COLD_INT4, self.k4, self.v4, self.kv_scales4
+
     def cache_fetch(self, stream=None):
-        kd.kv_cache_fetch(self.shape, self.num_slots, self.k_cache, self.v_cache,
-                          self.block_table, self.fetch_block, self.fetch_slot, self.fetch_count,
-                          self.topk, self.cache_k, self.cache_v, stream)
+        if self.cache_codes is None:
+            kd.kv_cache_fetch(self.shape, self.num_slots, self.k_cache, self.v_cache,
+                              self.block_table, self.fetch_block, self.fetch_slot,
+                              self.fetch_count, self.topk, self.cache_k, self.cache_v, stream)
+            return
+        fmt, kc, vc, sc = self._code_pools()
+        kd.kv_cache_fetch_codes(self.shape, self.num_slots, fmt, kc, vc, sc, self.block_table,
+                                self.fetch_block, self.fetch_slot, self.fetch_count, self.topk,
+                                self.cache_k, self.cache_v, self.cache_scales, stream)
 
     def cached_attention(self, num_splits: Optional[int] = None, with_lse: bool = True,
                          stream=None):
-        S = num_splits or self.auto_splits(True)
+        lse = self.block_lse if with_lse else None
+        if self.cache_codes is None:
+            S = num_splits or self.auto_splits(True)
+            po, pm, pl = self.partials(S)
+            kd.kv_cached_decode_attn(self.shape, self.num_slots, self.q, self.cache_k,
+                                     self.cache_v, self.seq_lens, self.sel, self.sel_count,
+                                     self.sel_slots, self.topk, self.scale, S, po, pm, pl, lse,
+                                     stream)
+            return S
+        S = num_splits or kd.kv_auto_num_splits_fp8(self.shape, self.topk)
         po, pm, pl = self.partials(S)
-        kd.kv_cached_decode_attn(self.shape, self.num_slots, self.q, self.cache_k, self.cache_v,
-                                 self.seq_lens, self.sel, self.sel_count, self.sel_slots,
-                                 self.topk, self.scale, S, po, pm, pl,
-                                 self.block_lse if with_lse else None, stream)
+        kd.kv_cached_decode_attn_codes(self.shape, self.num_slots, self._code_pools()[0], self.q,
+                                       self.cache_k, self.cache_v, self.cache_scales,
+                                       self.seq_lens, self.sel, self.sel_count, self.sel_slots,
+                                       self.topk, self.scale, S, po, pm, pl, lse, stream)
         return S
 
     def cache_slot_mass(self, stream=None):

@@ -398,3 +398,45 @@ def test_tiered_argument_checks():
     expect(kd.KV_ERR_UNSUPPORTED, lambda stream: f(shape(dtype="f32"), A16, A16, A16, A16, A16,
                                                    A16, kd.KV_COLD_INT4, A16, A16, A16, None,
                                                    None, 0, 0.1, 2, A16, A16, A16, stream=stream))
+
+
+def test_code_cache_argument_checks():
+    s = shape()
+    f = kd.kv_cache_fetch_codes
+
+    def fetch(sh=s, **kw):
+        args = dict(num_slots=16, code_format=kd.KV_COLD_INT4, k_codes=A16, v_codes=A16,
+                    kv_scales=A16, block_table=A16, fetch_block=A16, fetch_slot=A16,
+                    fetch_count=A16, fetch_stride=8, cache_k=A16, cache_v=A16, cache_scales=A16)
+        args.update(kw)
+        return lambda stream: f(sh, stream=stream, **args)
+
+    expect(kd.KV_ERR_INVALID_ARG, fetch(code_format=0))
+    expect(kd.KV_ERR_INVALID_ARG, fetch(code_format=16))
+    expect(kd.KV_ERR_UNSUPPORTED, fetch(sh=shape(dtype="f32")))
+    expect(kd.KV_ERR_INVALID_ARG, fetch(kv_scales=None))
+    expect(kd.KV_ERR_INVALID_ARG, fetch(cache_scales=None))
+    expect(kd.KV_ERR_INVALID_ARG, fetch(v_codes=None))
+    expect(kd.KV_ERR_ALIGNMENT, fetch(cache_scales=A4))
+    expect(kd.KV_ERR_ALIGNMENT, fetch(k_codes=A4))
+    expect(kd.KV_ERR_INVALID_ARG, fetch(fetch_stride=17))
+    expect(kd.KV_ERR_INVALID_ARG, fetch(num_slots=0))
+    at = kd.kv_cached_decode_attn_codes
+
+    def attend(sh=s, **kw):
+        args = dict(num_slots=16, code_format=kd.KV_COLD_FP8, q=A16, cache_k=A16, cache_v=A16,
+                    cache_scales=A16, seq_lens=A16, sel_blocks=A16, sel_count=A16,
+                    sel_slots=A16, sel_stride=8, scale=0.1, num_splits=2, part_o=A16,
+                    part_m=A16, part_l=A16, block_lse=None)
+        args.update(kw)
+        return lambda stream: at(sh, stream=stream, **args)
+
+    expect(kd.KV_ERR_INVALID_ARG, attend(code_format=2))
+    expect(kd.KV_ERR_UNSUPPORTED, attend(sh=shape(dtype="f32"), code_format=kd.KV_COLD_INT4))
+    expect(kd.KV_ERR_INVALID_ARG, attend(cache_scales=None))
+    expect(kd.KV_ERR_ALIGNMENT, attend(cache_scales=A4))
+    expect(kd.KV_ERR_INVALID_ARG, attend(sel_slots=None))
+    expect(kd.KV_ERR_INVALID_ARG, attend(num_splits=0))
+    expect(kd.KV_ERR_INVALID_ARG, attend(scale=-1.0))
+    expect(kd.KV_ERR_ALIGNMENT, attend(cache_v=A4))
+    expect(kd.KV_ERR_INVALID_ARG, attend(sel_stride=17))
