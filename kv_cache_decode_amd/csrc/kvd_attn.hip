@@ -327,6 +327,7 @@ __global__ __launch_bounds__(WAVES * kWave) void paged_attn_kernel(
 typedef __bf16 bf16x8_v __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x8_v __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x4_v __attribute__((ext_vector_type(4)));
+typedef _Float16 f16x2_v __attribute__((ext_vector_type(2)));
 typedef short s16x4_v __attribute__((ext_vector_type(4)));
 typedef float f32x4_v __attribute__((ext_vector_type(4)));
 
@@ -407,8 +408,35 @@ struct RowWords {
   }
 };
 
-// Eight INT4 codes (one dword) as eight 16-bit values (four dwords), and four
-// (the low 16 bits) as two dwords; exact.
+// INT4 codes as 16-bit MFMA operand words.  With u = n + 8 (the code's
+// nibble with its sign bit flipped, 0..15) in the low four bits, the 16-bit
+// pattern kExp | u is the number 2^p + u exactly (bf16: 128 + u, f16: 1024 +
+// u).  f16 words then take one packed f16 subtraction of 1032, which leaves
+// the code n exactly.  gfx950 has no packed bf16 arithmetic, so bf16 words
+// keep the value n + kOffset (136): the kernel starts each logit sum at
+// -136 * sum(q) and takes 136 * (the page's summed softmax weights) off the
+// P.V sums (see the kernel).  Either way the operands are integers, exact in
+// the 16-bit format, and the products are exact in fp32.
+template <typename DT>
+struct Int4Words;
+template <>
+struct Int4Words<BF16> {
+  static constexpr uint32_t kExp = 0x43004300u;
+  static constexpr float kOffset = 136.0f;
+  __device__ static inline uint32_t fix(uint32_t w) { return w; }
+};
+template <>
+struct Int4Words<F16> {
+  static constexpr uint32_t kExp = 0x64006400u;
+  static constexpr float kOffset = 0.0f;
+  __device__ static inline uint32_t fix(uint32_t w) {
+    const f16x2_v v = __builtin_bit_cast(f16x2_v, w) - f16x2_v{(_Float16)1032.0f, (_Float16)1032.0f};
+    return __builtin_bit_cast(uint32_t, v);
+  }
+};
+// Eight (or, from the low 16 bits, four) INT4 codes as 16-bit words of
+// channel pairs through fp32, exact: the tiered kernel's cold pages, where the
+// registers of the offset bookkeeping below are not to spare.
 template <typename DT>
 __device__ inline uint32_t pack16_exact(float a, float b);
 template <>
@@ -419,17 +447,55 @@ template <>
 __device__ inline uint32_t pack16_exact<F16>(float a, float b) {
   return F16::pack2(a, b);
 }
-template <typename DT>
-__device__ inline uint4 int4x8_to_16(uint32_t w) {
-  float f[8];
-  int4x8_to_f32(w, f);
-  return make_uint4(pack16_exact<DT>(f[0], f[1]), pack16_exact<DT>(f[2], f[3]),
-                    pack16_exact<DT>(f[4], f[5]), pack16_exact<DT>(f[6], f[7]));
+template <typename DT, int NDW>
+__device__ inline void int4_exact_words(uint32_t w, uint32_t (&r)[NDW]) {
+#pragma unroll
+  for (int k = 0; k < NDW; ++k)
+    r[k] = pack16_exact<DT>((float)int4_code(w, 2 * k), (float)int4_code(w, 2 * k + 1));
 }
+
+// perm selector: byte d of src1 into byte 0, byte d of src0 into byte 2, zeros
+// elsewhere
+__device__ constexpr uint32_t pair_sel(int d) {
+  return (0x0Cu << 24) | ((4u + (uint32_t)d) << 16) | (0x0Cu << 8) | (uint32_t)d;
+}
+// One dword of eight K codes (channel c in nibble c) as four words holding
+// the channel pairs (0, 4), (1, 5), (2, 6), (3, 7): nibbles c and c + 4 sit
+// 16 bits apart, so each word is one shift and one and-or.  q's B operand
+// takes the same channel order (int4_q_order).
 template <typename DT>
-__device__ inline uint2 int4x4_to_16(uint32_t w) {
-  return make_uint2(pack16_exact<DT>((float)int4_code(w, 0), (float)int4_code(w, 1)),
-                    pack16_exact<DT>((float)int4_code(w, 2), (float)int4_code(w, 3)));
+__device__ inline uint4 int4_k_words(uint32_t w) {
+  const uint32_t x = w ^ 0x88888888u;
+  using W = Int4Words<DT>;
+  return make_uint4(W::fix((x & 0x000F000Fu) | W::kExp), W::fix(((x >> 4) & 0x000F000Fu) | W::kExp),
+                    W::fix(((x >> 8) & 0x000F000Fu) | W::kExp),
+                    W::fix(((x >> 12) & 0x000F000Fu) | W::kExp));
+}
+// Eight consecutive 16-bit q values (channel pairs (0, 1) .. (6, 7)) in the
+// order of int4_k_words.
+__device__ inline uint4 int4_q_order(const uint4& q) {
+  return make_uint4(__builtin_amdgcn_perm(q.z, q.x, 0x05040100u),
+                    __builtin_amdgcn_perm(q.z, q.x, 0x07060302u),
+                    __builtin_amdgcn_perm(q.w, q.y, 0x05040100u),
+                    __builtin_amdgcn_perm(q.w, q.y, 0x07060302u));
+}
+// The V codes of the lane's four tokens (v[i]: 2*NDW channels of token 4*grp+i,
+// channel c in nibble c) straight into the B operands of P.V: vB[2k] holds
+// channel 2k and vB[2k+1] channel 2k+1 of tokens (0, 1) in .x and (2, 3) in .y.
+template <typename DT, int NDW>
+__device__ inline void int4_v_operands(const uint32_t (&v)[4], uint2 (&vB)[2 * NDW]) {
+  using W = Int4Words<DT>;
+  const uint32_t x0 = v[0] ^ 0x88888888u, x1 = v[1] ^ 0x88888888u;
+  const uint32_t x2 = v[2] ^ 0x88888888u, x3 = v[3] ^ 0x88888888u;
+#pragma unroll
+  for (int k = 0; k < NDW; ++k) {
+    const uint32_t t01 = __builtin_amdgcn_perm(x1, x0, pair_sel(k));
+    const uint32_t t23 = __builtin_amdgcn_perm(x3, x2, pair_sel(k));
+    vB[2 * k].x = W::fix((t01 & 0x000F000Fu) | W::kExp);
+    vB[2 * k].y = W::fix((t23 & 0x000F000Fu) | W::kExp);
+    vB[2 * k + 1].x = W::fix(((t01 >> 4) & 0x000F000Fu) | W::kExp);
+    vB[2 * k + 1].y = W::fix(((t23 >> 4) & 0x000F000Fu) | W::kExp);
+  }
 }
 
 // With FP8 code pages (KVQ 8) lane (col, grp) reads 16 K codes at a time:
@@ -488,12 +554,43 @@ __global__ __launch_bounds__(WAVES * kWave) KVD_MFMA_OCCUPANCY_T(COLD) void page
   for (int st = 0; st < KS; ++st)
     qB[st] = col < G ? load16(static_cast<const St*>(q) + (row0 + col) * D + qk_channel<KVQ, D>(st, grp))
                      : make_uint4(0, 0, 0, 0);
+  // bf16 INT4 pages give operands of code + 136 (Int4Words): a page's logit
+  // sums start at -136 * sum_c q_c of their head (the lane's column), and
+  // vcorr accumulates P times a row of ones (each head's summed weights)
+  // beside o, so o - 136 * vcorr is the sum over the codes.  vcorr is folded
+  // into o every eight pages, which keeps o's magnitude (and so its rounding)
+  // near that of the true sum.  (The tiered kernel decodes its cold pages
+  // exactly through fp32 instead: it has no registers to spare.)
+  if constexpr (KVQ == 4) {
+#pragma unroll
+    for (int st = 0; st < KS; ++st) qB[st] = int4_q_order(qB[st]);
+  }
+  constexpr bool kInt4Off = std::is_same<DT, BF16>::value && KVQ == 4;
+  float qcorr = 0.0f;
+  if constexpr (kInt4Off) {
+    float t = 0.0f;
+#pragma unroll
+    for (int st = 0; st < KS; ++st)
+      t += ((Ops::lo(qB[st].x) + Ops::hi(qB[st].x)) + (Ops::lo(qB[st].y) + Ops::hi(qB[st].y))) +
+           ((Ops::lo(qB[st].z) + Ops::hi(qB[st].z)) + (Ops::lo(qB[st].w) + Ops::hi(qB[st].w)));
+    t += xor16(t);
+    t += xor32(t);
+    qcorr = -Int4Words<DT>::kOffset * t;
+  }
+  f32x4_v vcorr = {0.f, 0.f, 0.f, 0.f};
 
 
   f32x4_v o[NT];
 #pragma unroll
   for (int n = 0; n < NT; ++n) o[n] = f32x4_v{0.f, 0.f, 0.f, 0.f};
   float m = -INFINITY, lsum = 0.0f;
+  auto fold_vcorr = [&]() {
+#pragma unroll
+    for (int n = 0; n < NT; ++n)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) o[n][i] = fmaf(-Int4Words<DT>::kOffset, vcorr[i], o[n][i]);
+    vcorr = f32x4_v{0.f, 0.f, 0.f, 0.f};
+  };
 
   // byte addressing (code pages: fewer bytes per channel)
   constexpr int KCH = KVQ == 8 ? 16 : (KVQ == 4 ? D / 4 : 8);   // K channels a lane starts at, per grp
@@ -627,22 +724,16 @@ __global__ __launch_bounds__(WAVES * kWave) KVD_MFMA_OCCUPANCY_T(COLD) void page
       const float sk = (KVQ || cold) ? readlane_f(my_sk, it) : 1.0f;
       const float sv = (KVQ || cold) ? readlane_f(my_sv, it) : 1.0f;
 
-      // 16-bit operands of the page
+      // 16-bit operands of the page: K words kA, and V rows vr that become the
+      // P.V operands below (INT4 V codes are decoded straight into them there,
+      // after the softmax, when fewer registers are live)
       uint4 kA[KS];
       RowWords<NDW> vr[4];
+      bool v_int4 = false;
       if constexpr (KVQ == 4) {
 #pragma unroll
-        for (int st = 0; st < KS; ++st) kA[st] = int4x8_to_16<DT>(cur.k[st]);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          if constexpr (NDW == 4) {
-            const uint4 t = int4x8_to_16<DT>(cur.v[i]);
-            vr[i].w[0] = t.x; vr[i].w[1] = t.y; vr[i].w[2] = t.z; vr[i].w[3] = t.w;
-          } else {
-            const uint2 t = int4x4_to_16<DT>(cur.v[i]);
-            vr[i].w[0] = t.x; vr[i].w[1] = t.y;
-          }
-        }
+        for (int st = 0; st < KS; ++st) kA[st] = int4_k_words<DT>(cur.k[st]);
+        v_int4 = true;
       } else if constexpr (KVQ == 8) {
 #pragma unroll
         for (int sp = 0; sp < KS / 2; ++sp) {
@@ -662,17 +753,13 @@ __global__ __launch_bounds__(WAVES * kWave) KVD_MFMA_OCCUPANCY_T(COLD) void page
       } else if (cold) {                      // tiered call, a cold page's codes
         if constexpr (COLD == 4) {
 #pragma unroll
-          for (int st = 0; st < KS; ++st) kA[st] = int4x8_to_16<DT>(cur.k[st].x);
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            if constexpr (NDW == 4) {
-              const uint4 t = int4x8_to_16<DT>(cur.v[i].w[0]);
-              vr[i].w[0] = t.x; vr[i].w[1] = t.y; vr[i].w[2] = t.z; vr[i].w[3] = t.w;
-            } else {
-              const uint2 t = int4x4_to_16<DT>(cur.v[i].w[0]);
-              vr[i].w[0] = t.x; vr[i].w[1] = t.y;
-            }
+          for (int st = 0; st < KS; ++st) {
+            uint32_t t[4];
+            int4_exact_words<DT, 4>(cur.k[st].x, t);
+            kA[st] = make_uint4(t[0], t[1], t[2], t[3]);
           }
+#pragma unroll
+          for (int i = 0; i < 4; ++i) int4_exact_words<DT, NDW>(cur.v[i].w[0], vr[i].w);
         } else if constexpr (COLD == 8) {
 #pragma unroll
           for (int st = 0; st < KS; ++st) {
@@ -696,6 +783,9 @@ __global__ __launch_bounds__(WAVES * kWave) KVD_MFMA_OCCUPANCY_T(COLD) void page
       }
 
       f32x4_v sacc = {0.f, 0.f, 0.f, 0.f};
+      if constexpr (kInt4Off) {
+        sacc = f32x4_v{qcorr, qcorr, qcorr, qcorr};
+      }
 #pragma unroll
       for (int st = 0; st < KS; ++st) sacc = Ops::qk(kA[st], qB[st], sacc);
       const float zs = qscale * sk;
@@ -717,6 +807,10 @@ __global__ __launch_bounds__(WAVES * kWave) KVD_MFMA_OCCUPANCY_T(COLD) void page
         for (int n = 0; n < NT; ++n)
 #pragma unroll
           for (int i = 0; i < 4; ++i) o[n][i] *= ar[i];
+        if constexpr (kInt4Off) {
+#pragma unroll
+          for (int i = 0; i < 4; ++i) vcorr[i] *= ar[i];
+        }
       }
       float p[4];
 #pragma unroll
@@ -739,25 +833,37 @@ __global__ __launch_bounds__(WAVES * kWave) KVD_MFMA_OCCUPANCY_T(COLD) void page
       plo.x = Ops::pack(p[0] - Ops::lo(phi.x), p[1] - Ops::hi(phi.x));
       plo.y = Ops::pack(p[2] - Ops::lo(phi.y), p[3] - Ops::hi(phi.y));
 
-      if (valid < kBlockSize) {  // slots past the sequence end may hold anything
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-          if (4 * grp + i >= valid)
-#pragma unroll
-            for (int k = 0; k < NDW; ++k) vr[i].w[k] = 0u;
-      }
       uint2 vB[NT];
+      if (v_int4) {
+        if constexpr (KVQ == 4) int4_v_operands<DT, NDW>(cur.v, vB);
+      } else {
+        if (valid < kBlockSize) {  // slots past the sequence end may hold anything
 #pragma unroll
-      for (int k = 0; k < NDW; ++k) {
-        vB[2 * k].x = __builtin_amdgcn_perm(vr[1].w[k], vr[0].w[k], 0x05040100u);
-        vB[2 * k].y = __builtin_amdgcn_perm(vr[3].w[k], vr[2].w[k], 0x05040100u);
-        vB[2 * k + 1].x = __builtin_amdgcn_perm(vr[1].w[k], vr[0].w[k], 0x07060302u);
-        vB[2 * k + 1].y = __builtin_amdgcn_perm(vr[3].w[k], vr[2].w[k], 0x07060302u);
+          for (int i = 0; i < 4; ++i)
+            if (4 * grp + i >= valid)
+#pragma unroll
+              for (int k = 0; k < NDW; ++k) vr[i].w[k] = 0u;
+        }
+#pragma unroll
+        for (int k = 0; k < NDW; ++k) {
+          vB[2 * k].x = __builtin_amdgcn_perm(vr[1].w[k], vr[0].w[k], 0x05040100u);
+          vB[2 * k].y = __builtin_amdgcn_perm(vr[3].w[k], vr[2].w[k], 0x05040100u);
+          vB[2 * k + 1].x = __builtin_amdgcn_perm(vr[1].w[k], vr[0].w[k], 0x07060302u);
+          vB[2 * k + 1].y = __builtin_amdgcn_perm(vr[3].w[k], vr[2].w[k], 0x07060302u);
+        }
       }
+      // (INT4 operands of slots past the sequence end are finite and meet
+      // weights of exactly 0)
 #pragma unroll
       for (int n = 0; n < NT; ++n) o[n] = Ops::pv(phi, vB[n], o[n]);
 #pragma unroll
       for (int n = 0; n < NT; ++n) o[n] = Ops::pv(plo, vB[n], o[n]);
+      if constexpr (kInt4Off) {
+        const uint2 ones = make_uint2(0x3F803F80u, 0x3F803F80u);   // bf16 1.0 pairs
+        vcorr = Ops::pv(phi, ones, vcorr);
+        vcorr = Ops::pv(plo, ones, vcorr);
+        if ((it & 7) == 7) fold_vcorr();
+      }
 
     };
     // page it+1 loads while page it is computed; the group's last page is
@@ -774,6 +880,7 @@ __global__ __launch_bounds__(WAVES * kWave) KVD_MFMA_OCCUPANCY_T(COLD) void page
     process(cur, cnt - 1);
   }
 
+  if constexpr (kInt4Off) fold_vcorr();
   // totals per head (the four k-groups of a column saw disjoint tokens)
   lsum += xor16(lsum);
   lsum += xor32(lsum);

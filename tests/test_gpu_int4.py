@@ -123,6 +123,34 @@ def test_int4_tail_codes_are_ignored(gpu):
     dw.close()
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+@pytest.mark.parametrize("q_scale", [0.0, 1.0, 6.0])
+def test_int4_one_split_long_context(gpu, dtype, q_scale):
+    """32768 tokens in one split: the longest accumulation the kernel runs.
+    q = 0 gives every token the same weight, so the output is the mean of V,
+    a small number from a long cancelling sum (the case the bf16 offset
+    bookkeeping is most exposed to); larger q spreads the logits."""
+    data = mk(1, 8, 2, 128, (32768,), dtype, seed=5800 + int(q_scale), planted_frac=0.05)
+    data.q_raw = wl.to_storage((data.q64() * q_scale).astype(np.float32), dtype)
+    ref = oracle_int4(data)
+    dw = device(data, gpu)
+    try:
+        dw.quantize_int4()
+        check_codes(dw, data, ref)
+        o = DequantRun(data, ref)
+        ref_out, ref_lse = o.attention()
+        worst = 0.0
+        for S in (1, 3):
+            dw.decode_int4(sparse=False, num_splits=S)
+            rel = assert_rows_close(to_f64(dw.out), ref_out, ROW_TOL[dtype], f"int4 S={S}")
+            np.testing.assert_allclose(to_f64(dw.lse), ref_lse, rtol=0, atol=1e-4)
+            worst = max(worst, rel)
+        print(f"\n[int4 one split {dtype} q*{q_scale}] worst row rel-err {worst:.2e}")
+    finally:
+        torch.cuda.synchronize()
+        dw.close()
+
+
 def test_int4_rejects_fp32(gpu):
     from kv_cache_decode_amd import kvdecode as kd
     data = mk(1, 2, 1, 64, (32,), "f32", seed=5650)
