@@ -915,6 +915,11 @@ __global__ __launch_bounds__(WAVES * kWave) KVD_MFMA_OCCUPANCY_T(COLD) void page
 
 constexpr int kCombineChunk = 32;
 
+// R > 0: S <= R * SLOTS, and each thread issues the loads of all its split
+// slots (m, l and its four o channels) before the first reduction, so the
+// partials arrive in one memory round trip; R = 0 loops for larger S, with
+// the m loads first and the o loads after the maximum.
+template <int R>
 __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ part_o,
                                                       const float* __restrict__ part_m,
                                                       const float* __restrict__ part_l, int S,
@@ -931,27 +936,57 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
   const float* pm = part_m + row * S;
   const float* pl = part_l + row * S;
 
-  float M = -INFINITY;
-  for (int s = tid; s < S; s += 256) M = fmaxf(M, pm[s]);
-  M = group_reduce<kWave, OpMax>(M);
-  if ((tid & (kWave - 1)) == 0) red[tid >> 6] = M;
-  __syncthreads();
-  M = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
-
   const int slot = tid / TPS, q4 = tid % TPS;
   const float* po = part_o + (row * S) * D + d0 + q4 * 4;
   float4 a = make_float4(0.f, 0.f, 0.f, 0.f);
   float W = 0.0f;
+  float M = -INFINITY;
+  if constexpr (R > 0) {
+    float ms[R], ls[R];
+    float4 os[R];
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      const int s = slot + r * SLOTS;
+      ms[r] = -INFINITY;
+      ls[r] = 0.0f;
+      os[r] = make_float4(0.f, 0.f, 0.f, 0.f);
+      if (s < S) {
+        ms[r] = pm[s];
+        ls[r] = pl[s];
+        os[r] = *reinterpret_cast<const float4*>(po + (size_t)s * D);
+      }
+      M = fmaxf(M, ms[r]);
+    }
+    M = group_reduce<kWave, OpMax>(M);
+    if ((tid & (kWave - 1)) == 0) red[tid >> 6] = M;
+    __syncthreads();
+    M = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      const float w = (ms[r] == -INFINITY) ? 0.0f : ls[r] * expf(ms[r] - M);
+      W += w;
+      a.x = fmaf(w, os[r].x, a.x);
+      a.y = fmaf(w, os[r].y, a.y);
+      a.z = fmaf(w, os[r].z, a.z);
+      a.w = fmaf(w, os[r].w, a.w);
+    }
+  } else {
+    for (int s = tid; s < S; s += 256) M = fmaxf(M, pm[s]);
+    M = group_reduce<kWave, OpMax>(M);
+    if ((tid & (kWave - 1)) == 0) red[tid >> 6] = M;
+    __syncthreads();
+    M = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
 #pragma unroll 4
-  for (int s = slot; s < S; s += SLOTS) {
-    const float ms = pm[s];
-    const float w = (ms == -INFINITY) ? 0.0f : pl[s] * expf(ms - M);
-    const float4 o = *reinterpret_cast<const float4*>(po + (size_t)s * D);
-    W += w;
-    a.x = fmaf(w, o.x, a.x);
-    a.y = fmaf(w, o.y, a.y);
-    a.z = fmaf(w, o.z, a.z);
-    a.w = fmaf(w, o.w, a.w);
+    for (int s = slot; s < S; s += SLOTS) {
+      const float ms = pm[s];
+      const float w = (ms == -INFINITY) ? 0.0f : pl[s] * expf(ms - M);
+      const float4 o = *reinterpret_cast<const float4*>(po + (size_t)s * D);
+      W += w;
+      a.x = fmaf(w, o.x, a.x);
+      a.y = fmaf(w, o.y, a.y);
+      a.z = fmaf(w, o.z, a.z);
+      a.w = fmaf(w, o.w, a.w);
+    }
   }
   acc_s[slot][q4] = a;
   if (q4 == 0) w_s[slot] = W;
@@ -1042,8 +1077,17 @@ hipError_t launch_paged_attn(int dtype, int D, int G, int kvq, const void* q,
 hipError_t launch_combine(int D, const float* part_o, const float* part_m, const float* part_l,
                           int rows, int S, float* out, float* lse, hipStream_t stream) {
   if (D % kCombineChunk) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(combine_kernel, dim3(rows, D / kCombineChunk), dim3(256), 0, stream, part_o,
-                     part_m, part_l, S, D, out, lse);
+  constexpr int SLOTS = 256 / (kCombineChunk / 4);
+  const dim3 grid(rows, D / kCombineChunk);
+  auto go = [&](auto r) {
+    hipLaunchKernelGGL((combine_kernel<decltype(r)::value>), grid, dim3(256), 0, stream, part_o,
+                       part_m, part_l, S, D, out, lse);
+  };
+  if (S <= SLOTS) go(std::integral_constant<int, 1>{});
+  else if (S <= 2 * SLOTS) go(std::integral_constant<int, 2>{});
+  else if (S <= 4 * SLOTS) go(std::integral_constant<int, 4>{});
+  else if (S <= 8 * SLOTS) go(std::integral_constant<int, 8>{});
+  else go(std::integral_constant<int, 0>{});
   return hipGetLastError();
 }
 
