@@ -188,12 +188,12 @@ def run_gpu(args, spec, data):
         if ev is not None:
             ev[len(actions)].record()
 
-    def time_loop(run_one):
+    def time_loop(run_one, calls=None):
         t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         torch.cuda.synchronize()
         wall0 = time.perf_counter()
         t0.record()
-        for i in range(args.steps):
+        for i in range(args.steps if calls is None else calls):
             run_one(i)
         t1.record()
         torch.cuda.synchronize()
@@ -259,24 +259,42 @@ def run_gpu(args, spec, data):
 
         ceilings = time_read_ceilings(copies, s_dense, time_loop, args.steps)
 
-        # whole-step timing, one HIP graph per workload copy
+        # whole-step timing: HIP graphs of GRAPH_STEPS consecutive steps cycling
+        # over the workload copies (so each graph launch's fixed cost of a few us
+        # is spread over several steps, as a decode loop that captures its
+        # layers would), replayed args.steps // GRAPH_STEPS times, plus one graph
+        # of the remaining steps: exactly args.steps steps between the events
         launch = "hip_graph"
         try:
-            graphs = []
             side = torch.cuda.Stream()
-            for c in copies:
-                side.wait_stream(torch.cuda.current_stream())
-                with torch.cuda.stream(side):
+            side.wait_stream(torch.cuda.current_stream())
+            with torch.cuda.stream(side):
+                for c in copies:
                     step(c)
-                torch.cuda.current_stream().wait_stream(side)
+            torch.cuda.current_stream().wait_stream(side)
+
+            def capture(n):
                 g = torch.cuda.CUDAGraph()
                 with torch.cuda.graph(g):
-                    step(c)
-                graphs.append(g)
-            for i in range(args.warmup):
-                graphs[i % len(graphs)].replay()
-            total_ms, wall = time_loop(lambda i: graphs[i % len(graphs)].replay())
-            del graphs
+                    for i in range(n):
+                        step(copies[i % len(copies)])
+                return g
+
+            per = GRAPH_STEPS
+            full_g = capture(per)
+            tail = args.steps % per
+            tail_g = capture(tail) if tail else None
+            for _ in range(max(1, args.warmup // per)):
+                full_g.replay()
+
+            def replay(i):
+                if i < args.steps // per:
+                    full_g.replay()
+                elif tail_g is not None:
+                    tail_g.replay()
+
+            total_ms, wall = time_loop(replay, args.steps // per + (1 if tail else 0))
+            del full_g, tail_g
         except RuntimeError as e:          # capture unavailable: report eager launches
             log(f"[bench] graph capture failed ({e}); timing eager launches")
             launch = "eager"
@@ -1009,6 +1027,8 @@ def main():
             "step": "meta_build(all pages) + append_select (append + score + Top-K) + sparse "
                     "attn + combine + dense attn + combine",
             "launch": g["launch"],
+            "step_timing": f"all timed steps between two events, as replays of HIP graphs of "
+                           f"{GRAPH_STEPS} steps cycling over the workload copies",
         },
         "eager_ms_per_step": g["eager_ms_per_step"],
         "frac_of_hbm_peak": step_bytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBPS,
