@@ -769,9 +769,15 @@ def time_cache_trajectory(args, dw, data, k, S, codes=None):
         run(lambda: dw.cache_step(k, S), counts)                        # warm, counted
         warm = [int(c.sum()) for c in counts]
         us = run(lambda: dw.cache_step(k, S))                           # warm, timed
+        # the same warm trajectory with the fetch fused into the attention
+        dw.cache_init(C, k, codes=codes)
+        run(lambda: dw.cache_step(k, S, fused=True))
+        run(lambda: dw.cache_step(k, S, fused=True))
+        us_fused = run(lambda: dw.cache_step(k, S, fused=True))
         selected = k * spec.num_seqs * spec.num_kv_heads
         res[f"slots_{C}"] = {
             "step_us": us,
+            "step_us_fused_fetch": us_fused,
             "fetched_blocks_per_step": float(np.mean(warm)),
             "hit_rate": 1.0 - float(np.mean(warm)) / selected,
             "host_link_bytes_per_step": float(np.mean(warm)) * tile,

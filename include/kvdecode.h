@@ -19,6 +19,8 @@
  *                         block's log-sum-exp for the next eviction
  *   kv_cache_fetch_codes, kv_cached_decode_attn_codes  the same over FP8 / INT4
  *                         code pools: the cache holds codes and scales
+ *   kv_cached_decode_attn_fetch(_codes)  the delta fetch and the cached attention
+ *                         in one launch
  *   kv_cache_slot_mass    eviction mass of every cache slot after a step
  *   kv_paged_decode_attn  split-K softmax decode attention, dense or over selected blocks
  *   kv_decode_combine     log-sum-exp merge of the split partials
@@ -494,6 +496,42 @@ kv_status kv_cached_decode_attn_codes(const kv_shape* shape, int32_t num_slots,
                                       int32_t sel_stride, float scale, int32_t num_splits,
                                       float* part_o, float* part_m, float* part_l,
                                       float* block_lse, void* stream);
+
+/*
+ * The delta fetch fused into the cached attention (KVDrive §6 overlaps the
+ * fetch of the missing entries with computation; here both are one launch, so
+ * the waves whose blocks are cached compute while the others read theirs over
+ * the host link, and a fetched tile is read once instead of written to the
+ * cache and read back).  kv_cached_decode_attn_fetch computes exactly what
+ * kv_cache_fetch(shape, num_slots, k_pool, v_pool, block_table, *, fetch_slot,
+ * fetch_count, sel_stride, cache_k, cache_v) followed by kv_cached_decode_attn
+ * computes, outputs and cache contents alike: a list position whose slot is
+ * among fetch_slot[b, j, 0 .. fetch_count[b, j]) (rows of sel_stride, as
+ * kv_cache_plan writes them; every such slot is in this step's list) reads
+ * block n's tiles from pool page block_table[b, n] and stores them into its
+ * cache page; the others read the cache.  The pools may be device pointers of
+ * kv_host_alloc memory (KV_FLAG_HOST_KV); the cache pools must not overlap
+ * them.  kv_cached_decode_attn_fetch_codes does the same over FP8 / INT4 code
+ * pools (the layouts of kv_cache_fetch_codes) and also copies each fetched
+ * block's scale pair from kv_scales to cache_scales.
+ */
+kv_status kv_cached_decode_attn_fetch(const kv_shape* shape, int32_t num_slots, const void* q,
+                                      const void* k_pool, const void* v_pool,
+                                      const int32_t* block_table, const int32_t* fetch_slot,
+                                      const int32_t* fetch_count, void* cache_k, void* cache_v,
+                                      const int32_t* seq_lens, const int32_t* sel_blocks,
+                                      const int32_t* sel_count, const int32_t* sel_slots,
+                                      int32_t sel_stride, float scale, int32_t num_splits,
+                                      float* part_o, float* part_m, float* part_l,
+                                      float* block_lse, void* stream);
+kv_status kv_cached_decode_attn_fetch_codes(
+    const kv_shape* shape, int32_t num_slots, int32_t code_format, const void* q,
+    const uint8_t* k_codes, const uint8_t* v_codes, const float* kv_scales,
+    const int32_t* block_table, const int32_t* fetch_slot, const int32_t* fetch_count,
+    uint8_t* cache_k, uint8_t* cache_v, float* cache_scales, const int32_t* seq_lens,
+    const int32_t* sel_blocks, const int32_t* sel_count, const int32_t* sel_slots,
+    int32_t sel_stride, float scale, int32_t num_splits, float* part_o, float* part_m,
+    float* part_l, float* block_lse, void* stream);
 
 /*
  * Eviction mass after a step: slot_mass[b, j, :] = 0, then for every list

@@ -600,7 +600,8 @@ kv_status cached_attn_common(const kv_shape* shape, int32_t num_slots, int kvq, 
                              const int32_t* sel_count, const int32_t* sel_slots,
                              int32_t sel_stride, float scale, int32_t num_splits, float* part_o,
                              float* part_m, float* part_l, float* block_lse, void* stream,
-                             const char* name) {
+                             const char* name, const int32_t* block_table = nullptr,
+                             const kvd::FetchArgs* fetch = nullptr) {
   if (!sel_blocks || !sel_count || !sel_slots)
     return fail(KV_ERR_INVALID_ARG, "sel_blocks, sel_count and sel_slots are required");
   if (!aligned(sel_slots, 4) || (block_lse && !aligned(block_lse, 4)))
@@ -620,11 +621,11 @@ kv_status cached_attn_common(const kv_shape* shape, int32_t num_slots, int kvq, 
   const int G = shape->num_q_heads / shape->num_kv_heads;
   return hip_status(
       kvd::launch_paged_attn(shape->dtype, shape->head_dim, G, kvq, q, cache_k, cache_v,
-                             cache_scales, /*block_table=*/nullptr, seq_lens, sel_blocks,
-                             sel_count, sel_stride, sel_slots, num_slots, shape->num_seqs,
+                             cache_scales, block_table, seq_lens, sel_blocks, sel_count,
+                             sel_stride, sel_slots, num_slots, shape->num_seqs,
                              shape->num_q_heads, shape->num_kv_heads, shape->max_blocks_per_seq,
                              num_splits, scale, part_o, part_m, part_l, block_lse,
-                             (hipStream_t)stream),
+                             (hipStream_t)stream, 0, nullptr, nullptr, nullptr, fetch),
       name);
 }
 
@@ -712,6 +713,67 @@ kv_status kv_cached_decode_attn_codes(const kv_shape* shape, int32_t num_slots,
                             seq_lens, sel_blocks, sel_count, sel_slots, sel_stride, scale,
                             num_splits, part_o, part_m, part_l, block_lse, stream,
                             "kv_cached_decode_attn_codes launch");
+}
+
+}  // extern "C"
+
+namespace {
+// Arguments of the fused fetch shared by both entry points.
+kv_status check_fetch(const void* k_pool, const void* v_pool, const int32_t* block_table,
+                      const int32_t* fetch_slot, const int32_t* fetch_count) {
+  if (!k_pool || !v_pool || !block_table || !fetch_slot || !fetch_count)
+    return fail(KV_ERR_INVALID_ARG, "the pools, block_table, fetch_slot and fetch_count are required");
+  if (!aligned(k_pool, 16) || !aligned(v_pool, 16))
+    return fail(KV_ERR_ALIGNMENT, "the pools must be 16-byte aligned");
+  if (!aligned(block_table, 4) || !aligned(fetch_slot, 4) || !aligned(fetch_count, 4))
+    return fail(KV_ERR_ALIGNMENT, "integer arrays must be 4-byte aligned");
+  return KV_OK;
+}
+}  // namespace
+
+extern "C" {
+
+kv_status kv_cached_decode_attn_fetch(const kv_shape* shape, int32_t num_slots, const void* q,
+                                      const void* k_pool, const void* v_pool,
+                                      const int32_t* block_table, const int32_t* fetch_slot,
+                                      const int32_t* fetch_count, void* cache_k, void* cache_v,
+                                      const int32_t* seq_lens, const int32_t* sel_blocks,
+                                      const int32_t* sel_count, const int32_t* sel_slots,
+                                      int32_t sel_stride, float scale, int32_t num_splits,
+                                      float* part_o, float* part_m, float* part_l,
+                                      float* block_lse, void* stream) {
+  kv_status st = check_cache(shape, num_slots, sel_stride);
+  if (st != KV_OK) return st;
+  if ((st = check_fetch(k_pool, v_pool, block_table, fetch_slot, fetch_count)) != KV_OK) return st;
+  const kvd::FetchArgs fa{k_pool, v_pool, nullptr, nullptr, fetch_slot, fetch_count};
+  return cached_attn_common(shape, num_slots, 0, q, cache_k, cache_v, nullptr, seq_lens,
+                            sel_blocks, sel_count, sel_slots, sel_stride, scale, num_splits,
+                            part_o, part_m, part_l, block_lse, stream,
+                            "kv_cached_decode_attn_fetch launch", block_table, &fa);
+}
+
+kv_status kv_cached_decode_attn_fetch_codes(
+    const kv_shape* shape, int32_t num_slots, int32_t code_format, const void* q,
+    const uint8_t* k_codes, const uint8_t* v_codes, const float* kv_scales,
+    const int32_t* block_table, const int32_t* fetch_slot, const int32_t* fetch_count,
+    uint8_t* cache_k, uint8_t* cache_v, float* cache_scales, const int32_t* seq_lens,
+    const int32_t* sel_blocks, const int32_t* sel_count, const int32_t* sel_slots,
+    int32_t sel_stride, float scale, int32_t num_splits, float* part_o, float* part_m,
+    float* part_l, float* block_lse, void* stream) {
+  kv_status st = check_cache(shape, num_slots, sel_stride);
+  if (st != KV_OK) return st;
+  if ((st = check_code_format(shape, code_format)) != KV_OK) return st;
+  if ((st = check_fetch(k_codes, v_codes, block_table, fetch_slot, fetch_count)) != KV_OK)
+    return st;
+  if (!kv_scales || !cache_scales)
+    return fail(KV_ERR_INVALID_ARG, "kv_scales and cache_scales are required");
+  if (!aligned(kv_scales, 8) || !aligned(cache_scales, 8))
+    return fail(KV_ERR_ALIGNMENT, "kv_scales and cache_scales must be 8-byte aligned");
+  const kvd::FetchArgs fa{k_codes, v_codes, kv_scales, cache_scales, fetch_slot, fetch_count};
+  return cached_attn_common(shape, num_slots, code_format, q, cache_k, cache_v, cache_scales,
+                            seq_lens, sel_blocks, sel_count, sel_slots, sel_stride, scale,
+                            num_splits, part_o, part_m, part_l, block_lse, stream,
+                            "kv_cached_decode_attn_fetch_codes launch", block_table, &fa);
 }
 
 kv_status kv_cache_slot_mass(const kv_shape* shape, int32_t num_slots, const float* block_lse,

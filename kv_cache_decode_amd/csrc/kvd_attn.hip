@@ -70,6 +70,7 @@ template <typename DT, int KVQ>
 struct KVChunk {
   using raw = uint4;
   __device__ static inline raw load(const uint8_t* p) { return load16_stream(p); }
+  __device__ static inline void store(uint8_t* p, const raw& w) { store16(p, w); }
   __device__ static inline void widen(const raw& w, float* f) { DT::widen(w, f); }
 };
 template <typename DT>
@@ -77,6 +78,7 @@ struct KVChunk<DT, 4> {
   static_assert(DT::E == 8, "INT4 pages hold 16-bit channels");
   using raw = uint32_t;
   __device__ static inline raw load(const uint8_t* p) { return load4_stream(p); }
+  __device__ static inline void store(uint8_t* p, const raw& w) { store4(p, w); }
   __device__ static inline void widen(const raw& w, float* f) { int4x8_to_f32(w, f); }
 };
 template <typename DT>
@@ -86,6 +88,10 @@ struct KVChunk<DT, 8> {
   __device__ static inline raw load(const uint8_t* p) {
     if constexpr (E == 8) return load8_stream(p);
     else return load4_stream(p);
+  }
+  __device__ static inline void store(uint8_t* p, const raw& w) {
+    if constexpr (E == 8) store8(p, w);
+    else store4(p, w);
   }
   __device__ static inline void widen(const raw& w, float* f) {
     if constexpr (E == 8) {
@@ -101,22 +107,46 @@ __device__ inline float readlane_f(float v, int lane) {
   return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), lane));
 }
 
-template <typename DT, int D, int G, int WAVES, bool SPARSE, int KVQ>
+// The cache slots of (b, j) that this step fetches, as a bitmap in LDS built
+// by the whole workgroup (all waves of a workgroup serve the same (b, j)).
+// Slots lie below num_slots <= kCacheMaxSlots.
+template <int NT>
+__device__ inline const uint32_t* fetched_slot_bits(const FetchArgs& fa, int b, int j, int Hkv,
+                                                   int stride, int num_slots) {
+  __shared__ uint32_t bits[kCacheMaxSlots / 32];
+  const size_t u = (size_t)b * Hkv + j;
+  const int words = (num_slots + 31) >> 5;
+  for (int w = threadIdx.x; w < words; w += NT) bits[w] = 0u;
+  __syncthreads();
+  const int fc = fa.fetch_count[u];
+  for (int k = threadIdx.x; k < fc; k += NT) {
+    const int sl = fa.fetch_slot[u * stride + k];
+    atomicOr(&bits[sl >> 5], 1u << (sl & 31));
+  }
+  __syncthreads();
+  return bits;
+}
+
+template <typename DT, int D, int G, int WAVES, bool SPARSE, int KVQ, bool FETCH = false>
 __global__ __launch_bounds__(WAVES * kWave) void paged_attn_kernel(
     const void* __restrict__ q, const void* __restrict__ k_cache, const void* __restrict__ v_cache,
     const float* __restrict__ kv_scales, const int32_t* __restrict__ block_table,
     const int32_t* __restrict__ seq_lens, const int32_t* __restrict__ sel,
     const int32_t* __restrict__ sel_count, int sel_stride, const int32_t* __restrict__ sel_slots,
     int num_slots, int Hq, int Hkv, int maxN, int S, float qscale, float* __restrict__ part_o,
-    float* __restrict__ part_m, float* __restrict__ part_l, float* __restrict__ block_lse) {
+    float* __restrict__ part_m, float* __restrict__ part_l, float* __restrict__ block_lse,
+    FetchArgs fa) {
+  static_assert(!FETCH || SPARSE, "the fused fetch serves cached lists");
   using G_ = RowGeom<DT, D>;
   using St = typename DT::storage;
   using KC = KVChunk<DT, KVQ>;
   constexpr int E = G_::E, LPR = G_::LPR, TPI = G_::TPI, NI = G_::NI;
   const int lane = threadIdx.x & (kWave - 1);
   const int s = blockIdx.x * WAVES + (threadIdx.x >> 6);
-  if (s >= S) return;
   const int j = blockIdx.y, b = blockIdx.z;
+  [[maybe_unused]] const uint32_t* fetched = nullptr;
+  if constexpr (FETCH) fetched = fetched_slot_bits<WAVES * kWave>(fa, b, j, Hkv, sel_stride, num_slots);
+  if (s >= S) return;
   const int rg = lane / LPR, c = lane % LPR;
 
   const int L = seq_lens[b];
@@ -149,6 +179,10 @@ __global__ __launch_bounds__(WAVES * kWave) void paged_attn_kernel(
   const size_t row_step = kv_bytes<DT, KVQ>((size_t)TPI * D);
   const uint8_t* kb = static_cast<const uint8_t*>(k_cache) + lane_off;
   const uint8_t* vb = static_cast<const uint8_t*>(v_cache) + lane_off;
+  const uint8_t* kbp = FETCH ? static_cast<const uint8_t*>(fa.k_pool) + lane_off : nullptr;
+  const uint8_t* vbp = FETCH ? static_cast<const uint8_t*>(fa.v_pool) + lane_off : nullptr;
+  uint8_t* kbw = FETCH ? static_cast<uint8_t*>(const_cast<void*>(k_cache)) + lane_off : nullptr;
+  uint8_t* vbw = FETCH ? static_cast<uint8_t*>(const_cast<void*>(v_cache)) + lane_off : nullptr;
   const int32_t* sel_row = SPARSE ? sel + ((size_t)b * Hkv + j) * sel_stride : nullptr;
   const int32_t* slots_row = (SPARSE && sel_slots) ? sel_slots + ((size_t)b * Hkv + j) * sel_stride
                                                    : nullptr;
@@ -156,31 +190,63 @@ __global__ __launch_bounds__(WAVES * kWave) void paged_attn_kernel(
 
   for (int base = p0; base < p1; base += kWave) {
     const int cnt = min(kWave, p1 - base);
-    int my_page = 0, my_valid = 0;
+    int my_page = 0, my_valid = 0, my_pool = -1;
     float my_sk = 1.0f, my_sv = 1.0f;
     if (lane < cnt) {
       const int n = SPARSE ? sel_row[base + lane] : base + lane;
       // cached list: the block sits in slot sel_slots[.] of cache page b*C + slot
-      my_page = slots_row ? b * num_slots + slots_row[base + lane] : bt_row[n];
+      const int slot = slots_row ? slots_row[base + lane] : 0;
+      my_page = slots_row ? b * num_slots + slot : bt_row[n];
+      if constexpr (FETCH) {   // fetched this step: read from the pool page
+        if ((fetched[slot >> 5] >> (slot & 31)) & 1u) my_pool = bt_row[n];
+      }
       my_valid = min(kBlockSize, L - n * kBlockSize);
       if constexpr (KVQ != 0) {
-        const float2 sc = *reinterpret_cast<const float2*>(kv_scales + ((size_t)my_page * Hkv + j) * 2);
+        const float* sp = kv_scales + ((size_t)my_page * Hkv + j) * 2;
+        if constexpr (FETCH) {
+          if (my_pool >= 0) sp = fa.pool_scales + ((size_t)my_pool * Hkv + j) * 2;
+        }
+        const float2 sc = *reinterpret_cast<const float2*>(sp);
         my_sk = sc.x;
         my_sv = sc.y;
+        if constexpr (FETCH) {
+          if (my_pool >= 0)
+            *reinterpret_cast<float2*>(fa.cache_scales + ((size_t)my_page * Hkv + j) * 2) = sc;
+        }
       }
     }
     struct PageRegs {
       typename KC::raw k[NI], v[NI];
     };
     auto load_page = [&](PageRegs& r, int idx) {
-      const size_t off = (size_t)readlane(my_page, idx) * page_stride;
+      const uint8_t* kb_ = kb;
+      const uint8_t* vb_ = vb;
+      size_t off = (size_t)readlane(my_page, idx) * page_stride;
+      if constexpr (FETCH) {
+        const int pp = readlane(my_pool, idx);   // wave-uniform
+        if (pp >= 0) {
+          kb_ = kbp;
+          vb_ = vbp;
+          off = (size_t)pp * page_stride;
+        }
+      }
 #pragma unroll
       for (int it = 0; it < NI; ++it) {
-        r.k[it] = KC::load(kb + off + it * row_step);
-        r.v[it] = KC::load(vb + off + it * row_step);
+        r.k[it] = KC::load(kb_ + off + it * row_step);
+        r.v[it] = KC::load(vb_ + off + it * row_step);
       }
     };
     auto process = [&](const PageRegs& cur, int i) {
+      if constexpr (FETCH) {   // a page read from the pool goes to its cache page
+        if (readlane(my_pool, i) >= 0) {
+          const size_t off = (size_t)readlane(my_page, i) * page_stride;
+#pragma unroll
+          for (int it = 0; it < NI; ++it) {
+            KC::store(kbw + off + it * row_step, cur.k[it]);
+            KC::store(vbw + off + it * row_step, cur.v[it]);
+          }
+        }
+      }
       const typename KC::raw* kc = cur.k;
       const typename KC::raw* vc = cur.v;
       const int valid = readlane(my_valid, i);
@@ -406,6 +472,10 @@ struct RowWords {
       w[0] = v.x; w[1] = v.y;
     }
   }
+  __device__ inline void store(void* p) const {
+    if constexpr (NDW == 4) store16(p, make_uint4(w[0], w[1], w[2], w[3]));
+    else store8(p, make_uint2(w[0], w[1]));
+  }
 };
 
 // INT4 codes as 16-bit MFMA operand words.  With u = n + 8 (the code's
@@ -518,7 +588,7 @@ __device__ inline int qk_channel(int st, int grp) {
 // cold page's codes sit in the first registers of the 16-bit page buffer, and
 // its K codes are read in the 16-bit layout (the 8 channels of each QK step,
 // as 4 or 8 code bytes), so both tiers share q's B operand.
-template <typename DT, int D, int G, int WAVES, bool SPARSE, int KVQ, int COLD = 0>
+template <typename DT, int D, int G, int WAVES, bool SPARSE, int KVQ, int COLD = 0, bool FETCH = false>
 __global__ __launch_bounds__(WAVES * kWave) KVD_MFMA_OCCUPANCY_T(COLD) void paged_attn_mfma_kernel(
     const void* __restrict__ q, const void* __restrict__ k_cache, const void* __restrict__ v_cache,
     const float* __restrict__ kv_scales, const int32_t* __restrict__ block_table,
@@ -527,9 +597,10 @@ __global__ __launch_bounds__(WAVES * kWave) KVD_MFMA_OCCUPANCY_T(COLD) void page
     int num_slots, int Hq, int Hkv, int maxN, int S, float qscale, float* __restrict__ part_o,
     float* __restrict__ part_m, float* __restrict__ part_l, float* __restrict__ block_lse,
     const void* __restrict__ k_cold, const void* __restrict__ v_cold,
-    const uint8_t* __restrict__ page_tier) {
+    const uint8_t* __restrict__ page_tier, FetchArgs fa) {
   static_assert(G >= 2 && G <= 8, "the group fills 2..8 of the 16 MFMA rows");
   static_assert(COLD == 0 || KVQ == 0, "tiered pools pair 16-bit hot pages with code pages");
+  static_assert(!FETCH || (SPARSE && COLD == 0), "the fused fetch serves cached lists");
   using St = typename DT::storage;
   using Ops = MfmaOps<DT>;
   constexpr int KS = D / 32;   // QK steps of 32 channels
@@ -537,8 +608,10 @@ __global__ __launch_bounds__(WAVES * kWave) KVD_MFMA_OCCUPANCY_T(COLD) void page
   constexpr int NDW = D / 32;  // dwords of V per lane and token (D/16 channels)
   const int lane = threadIdx.x & (kWave - 1);
   const int s = blockIdx.x * WAVES + (threadIdx.x >> 6);
-  if (s >= S) return;
   const int j = blockIdx.y, b = blockIdx.z;
+  [[maybe_unused]] const uint32_t* fetched = nullptr;
+  if constexpr (FETCH) fetched = fetched_slot_bits<WAVES * kWave>(fa, b, j, Hkv, sel_stride, num_slots);
+  if (s >= S) return;
   const int col = lane & 15, grp = lane >> 4;
 
   const int L = seq_lens[b];
@@ -595,11 +668,17 @@ __global__ __launch_bounds__(WAVES * kWave) KVD_MFMA_OCCUPANCY_T(COLD) void page
   // byte addressing (code pages: fewer bytes per channel)
   constexpr int KCH = KVQ == 8 ? 16 : (KVQ == 4 ? D / 4 : 8);   // K channels a lane starts at, per grp
   const size_t page_stride = kv_bytes<DT, KVQ>((size_t)Hkv * kBlockSize * D);
-  const uint8_t* kb = static_cast<const uint8_t*>(k_cache) +
-                      kv_bytes<DT, KVQ>((size_t)j * kBlockSize * D + (size_t)col * D + KCH * grp);
-  const uint8_t* vb = static_cast<const uint8_t*>(v_cache) +
-                      kv_bytes<DT, KVQ>((size_t)j * kBlockSize * D + (size_t)(4 * grp) * D +
-                                        2 * NDW * col);
+  const size_t k_lane = kv_bytes<DT, KVQ>((size_t)j * kBlockSize * D + (size_t)col * D + KCH * grp);
+  const size_t v_lane = kv_bytes<DT, KVQ>((size_t)j * kBlockSize * D + (size_t)(4 * grp) * D +
+                                          2 * NDW * col);
+  const uint8_t* kb = static_cast<const uint8_t*>(k_cache) + k_lane;
+  const uint8_t* vb = static_cast<const uint8_t*>(v_cache) + v_lane;
+  // fused fetch: the pools a fetched block is read from, and the cache pages
+  // it is stored to (the same lane offsets: pools and cache share the layout)
+  const uint8_t* kbp = FETCH ? static_cast<const uint8_t*>(fa.k_pool) + k_lane : nullptr;
+  const uint8_t* vbp = FETCH ? static_cast<const uint8_t*>(fa.v_pool) + v_lane : nullptr;
+  uint8_t* kbw = FETCH ? static_cast<uint8_t*>(const_cast<void*>(k_cache)) + k_lane : nullptr;
+  uint8_t* vbw = FETCH ? static_cast<uint8_t*>(const_cast<void*>(v_cache)) + v_lane : nullptr;
   // the cold pools of tiered calls (K in the 16-bit lane layout: channel 8*grp
   // of step 0, steps 32 channels apart)
   constexpr int KCHC = 8;
@@ -619,17 +698,29 @@ __global__ __launch_bounds__(WAVES * kWave) KVD_MFMA_OCCUPANCY_T(COLD) void page
 
   for (int base = p0; base < p1; base += kWave) {
     const int cnt = min(kWave, p1 - base);
-    int my_page = 0, my_valid = 0, my_tier = 0;
+    int my_page = 0, my_valid = 0, my_tier = 0, my_pool = -1;
     float my_sk = 1.0f, my_sv = 1.0f;
     if (lane < cnt) {
       const int n = SPARSE ? sel_row[base + lane] : base + lane;
       // cached list: the block sits in slot sel_slots[.] of cache page b*C + slot
-      my_page = slots_row ? b * num_slots + slots_row[base + lane] : bt_row[n];
+      const int slot = slots_row ? slots_row[base + lane] : 0;
+      my_page = slots_row ? b * num_slots + slot : bt_row[n];
+      if constexpr (FETCH) {   // fetched this step: read from the pool page
+        if ((fetched[slot >> 5] >> (slot & 31)) & 1u) my_pool = bt_row[n];
+      }
       my_valid = min(kBlockSize, L - n * kBlockSize);
       if constexpr (KVQ != 0 || COLD != 0) {
-        const float2 sc = *reinterpret_cast<const float2*>(kv_scales + ((size_t)my_page * Hkv + j) * 2);
+        const float* sp = kv_scales + ((size_t)my_page * Hkv + j) * 2;
+        if constexpr (FETCH) {
+          if (my_pool >= 0) sp = fa.pool_scales + ((size_t)my_pool * Hkv + j) * 2;
+        }
+        const float2 sc = *reinterpret_cast<const float2*>(sp);
         my_sk = sc.x;
         my_sv = sc.y;
+        if constexpr (FETCH) {
+          if (my_pool >= 0)
+            *reinterpret_cast<float2*>(fa.cache_scales + ((size_t)my_page * Hkv + j) * 2) = sc;
+        }
       }
       if constexpr (COLD != 0) my_tier = page_tier[my_page];
     }
@@ -683,42 +774,81 @@ __global__ __launch_bounds__(WAVES * kWave) KVD_MFMA_OCCUPANCY_T(COLD) void page
           return;
         }
       }
-      const size_t off = (size_t)readlane(my_page, idx) * page_stride;
+      const uint8_t* kb_ = kb;
+      const uint8_t* vb_ = vb;
+      size_t off = (size_t)readlane(my_page, idx) * page_stride;
+      if constexpr (FETCH) {
+        const int pp = readlane(my_pool, idx);   // wave-uniform
+        if (pp >= 0) {
+          kb_ = kbp;
+          vb_ = vbp;
+          off = (size_t)pp * page_stride;
+        }
+      }
       if constexpr (KVQ == 4) {
         if constexpr (KS == 4) {
-          const uint4 t = load16_stream(kb + off);
+          const uint4 t = load16_stream(kb_ + off);
           r.k[0] = t.x; r.k[1] = t.y; r.k[2] = t.z; r.k[3] = t.w;
         } else {
-          const uint2 t = load8_stream(kb + off);
+          const uint2 t = load8_stream(kb_ + off);
           r.k[0] = t.x; r.k[1] = t.y;
         }
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          if constexpr (NDW == 4) r.v[i] = load4_stream(vb + off + (size_t)i * (D / 2));
-          else r.v[i] = load2_stream(vb + off + (size_t)i * (D / 2));
+          if constexpr (NDW == 4) r.v[i] = load4_stream(vb_ + off + (size_t)i * (D / 2));
+          else r.v[i] = load2_stream(vb_ + off + (size_t)i * (D / 2));
         }
       } else if constexpr (KVQ == 8) {
 #pragma unroll
-        for (int sp = 0; sp < KS / 2; ++sp) r.k[sp] = load16_stream(kb + off + 64 * sp);
+        for (int sp = 0; sp < KS / 2; ++sp) r.k[sp] = load16_stream(kb_ + off + 64 * sp);
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           if constexpr (NDW / 2 == 2) {
-            const uint2 t = load8_stream(vb + off + (size_t)i * D);
+            const uint2 t = load8_stream(vb_ + off + (size_t)i * D);
             r.v[i][0] = t.x;
             r.v[i][1] = t.y;
           } else {
-            r.v[i][0] = load4_stream(vb + off + (size_t)i * D);
+            r.v[i][0] = load4_stream(vb_ + off + (size_t)i * D);
           }
         }
       } else {
 #pragma unroll
-        for (int st = 0; st < KS; ++st) r.k[st] = load16_stream(kb + off + kv_bytes<DT, 0>(32 * st));
+        for (int st = 0; st < KS; ++st) r.k[st] = load16_stream(kb_ + off + kv_bytes<DT, 0>(32 * st));
 #pragma unroll
-        for (int i = 0; i < 4; ++i) r.v[i].load(vb + off + kv_bytes<DT, 0>((size_t)i * D));
+        for (int i = 0; i < 4; ++i) r.v[i].load(vb_ + off + kv_bytes<DT, 0>((size_t)i * D));
+      }
+    };
+    // fused fetch: a page read from the pool goes to its cache page, from the
+    // same registers and lane offsets it was loaded with
+    auto store_page = [&](const PageRegs& r, size_t off) {
+      if constexpr (KVQ == 4) {
+        if constexpr (KS == 4) store16(kbw + off, make_uint4(r.k[0], r.k[1], r.k[2], r.k[3]));
+        else store8(kbw + off, make_uint2(r.k[0], r.k[1]));
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          if constexpr (NDW == 4) store4(vbw + off + (size_t)i * (D / 2), r.v[i]);
+          else store2(vbw + off + (size_t)i * (D / 2), r.v[i]);
+        }
+      } else if constexpr (KVQ == 8) {
+#pragma unroll
+        for (int sp = 0; sp < KS / 2; ++sp) store16(kbw + off + 64 * sp, r.k[sp]);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          if constexpr (NDW / 2 == 2) store8(vbw + off + (size_t)i * D, make_uint2(r.v[i][0], r.v[i][1]));
+          else store4(vbw + off + (size_t)i * D, r.v[i][0]);
+        }
+      } else {
+#pragma unroll
+        for (int st = 0; st < KS; ++st) store16(kbw + off + kv_bytes<DT, 0>(32 * st), r.k[st]);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) r.v[i].store(vbw + off + kv_bytes<DT, 0>((size_t)i * D));
       }
     };
     // one page of compute; `cur` holds page `it` of the group
     auto process = [&](const PageRegs& cur, int it) {
+      if constexpr (FETCH) {
+        if (readlane(my_pool, it) >= 0) store_page(cur, (size_t)readlane(my_page, it) * page_stride);
+      }
       const int valid = readlane(my_valid, it);
       const bool cold = COLD != 0 && readlane(my_tier, it) != 0;   // wave-uniform
       const float sk = (KVQ || cold) ? readlane_f(my_sk, it) : 1.0f;
@@ -1017,8 +1147,10 @@ hipError_t launch_paged_attn(int dtype, int D, int G, int kvq, const void* q,
                              const int32_t* sel_slots, int num_slots, int B, int Hq, int Hkv,
                              int maxN, int S, float scale, float* part_o, float* part_m,
                              float* part_l, float* block_lse, hipStream_t stream, int cold,
-                             const void* k_cold, const void* v_cold, const uint8_t* page_tier) {
+                             const void* k_cold, const void* v_cold, const uint8_t* page_tier,
+                             const FetchArgs* fetch) {
   constexpr int WAVES = KVD_ATTN_WAVES;
+  const FetchArgs fa = fetch ? *fetch : FetchArgs{};
   const dim3 grid((S + WAVES - 1) / WAVES, Hkv, B);
   const float qscale = scale * kLog2e;
   return with_dtype(dtype, [&](auto dt) {
@@ -1026,47 +1158,55 @@ hipError_t launch_paged_attn(int dtype, int D, int G, int kvq, const void* q,
       return with_group(G, [&](auto g) {
         using DT = decltype(dt);
         constexpr int DD = decltype(d)::value, GG = decltype(g)::value;
-        auto go = [&](auto sparse, auto fmt, auto coldc) {
-          constexpr bool SP = decltype(sparse)::value;
+        auto go = [&](auto sparse, auto fmt, auto coldc, auto fetchc) {
+          constexpr bool SP = decltype(sparse)::value, FE = decltype(fetchc)::value;
           constexpr int KQ = decltype(fmt)::value, CQ = decltype(coldc)::value;
           if constexpr (KQ == 4 && std::is_same_v<DT, F32>) {
             return;                           // INT4 pages: 16-bit dtypes only
           } else if constexpr (!std::is_same_v<DT, F32> && GG >= 2) {
-            hipLaunchKernelGGL((paged_attn_mfma_kernel<DT, DD, GG, WAVES, SP, KQ, CQ>), grid,
+            hipLaunchKernelGGL((paged_attn_mfma_kernel<DT, DD, GG, WAVES, SP, KQ, CQ, FE>), grid,
                                dim3(WAVES * kWave), 0, stream, q, k_cache, v_cache, kv_scales,
                                block_table, seq_lens, sel, sel_count, sel_stride, sel_slots,
                                num_slots, Hq, Hkv, maxN, S, qscale, part_o, part_m, part_l,
-                               block_lse, k_cold, v_cold, page_tier);
+                               block_lse, k_cold, v_cold, page_tier, fa);
           } else if constexpr (CQ == 0) {
-            hipLaunchKernelGGL((paged_attn_kernel<DT, DD, GG, WAVES, SP, KQ>), grid,
+            hipLaunchKernelGGL((paged_attn_kernel<DT, DD, GG, WAVES, SP, KQ, FE>), grid,
                                dim3(WAVES * kWave), 0, stream, q, k_cache, v_cache, kv_scales,
                                block_table, seq_lens, sel, sel_count, sel_stride, sel_slots,
                                num_slots, Hq, Hkv, maxN, S, qscale, part_o, part_m, part_l,
-                               block_lse);
+                               block_lse, fa);
           }
         };
         using C0 = std::integral_constant<int, 0>;
         using C8 = std::integral_constant<int, 8>;
         using C4 = std::integral_constant<int, 4>;
+        using T = std::true_type;
+        using F = std::false_type;
         if (kvq == 4 && std::is_same_v<DT, F32>) return hipErrorInvalidValue;
-        if (cold != 0) {
+        if (fetch) {
+          // fused delta fetch: cached lists only
+          if (!sel || !sel_slots || !block_table || cold != 0) return hipErrorInvalidValue;
+          if (kvq == 8) go(T{}, C8{}, C0{}, T{});
+          else if (kvq == 4) go(T{}, C4{}, C0{}, T{});
+          else go(T{}, C0{}, C0{}, T{});
+        } else if (cold != 0) {
           // tiered pools: 16-bit hot pages on the matrix-core path only
           if (kvq != 0 || std::is_same_v<DT, F32> || GG < 2) return hipErrorInvalidValue;
           if (sel) {
-            if (cold == 8) go(std::true_type{}, C0{}, C8{});
-            else go(std::true_type{}, C0{}, C4{});
+            if (cold == 8) go(T{}, C0{}, C8{}, F{});
+            else go(T{}, C0{}, C4{}, F{});
           } else {
-            if (cold == 8) go(std::false_type{}, C0{}, C8{});
-            else go(std::false_type{}, C0{}, C4{});
+            if (cold == 8) go(F{}, C0{}, C8{}, F{});
+            else go(F{}, C0{}, C4{}, F{});
           }
         } else if (sel) {
-          if (kvq == 8) go(std::true_type{}, C8{}, C0{});
-          else if (kvq == 4) go(std::true_type{}, C4{}, C0{});
-          else go(std::true_type{}, C0{}, C0{});
+          if (kvq == 8) go(T{}, C8{}, C0{}, F{});
+          else if (kvq == 4) go(T{}, C4{}, C0{}, F{});
+          else go(T{}, C0{}, C0{}, F{});
         } else {
-          if (kvq == 8) go(std::false_type{}, C8{}, C0{});
-          else if (kvq == 4) go(std::false_type{}, C4{}, C0{});
-          else go(std::false_type{}, C0{}, C0{});
+          if (kvq == 8) go(F{}, C8{}, C0{}, F{});
+          else if (kvq == 4) go(F{}, C4{}, C0{}, F{});
+          else go(F{}, C0{}, C0{}, F{});
         }
         return hipGetLastError();
       });

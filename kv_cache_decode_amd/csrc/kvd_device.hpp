@@ -121,6 +121,9 @@ __device__ inline uint32_t load2_stream(const void* p) {
 #endif
 }
 __device__ inline void store16(void* p, const uint4& v) { *reinterpret_cast<uint4*>(p) = v; }
+__device__ inline void store8(void* p, const uint2& v) { *reinterpret_cast<uint2*>(p) = v; }
+__device__ inline void store4(void* p, uint32_t v) { *reinterpret_cast<uint32_t*>(p) = v; }
+__device__ inline void store2(void* p, uint32_t v) { *reinterpret_cast<uint16_t*>(p) = (uint16_t)v; }
 
 // ---------------------------------------------------------------- FP8 E4M3 pages
 //

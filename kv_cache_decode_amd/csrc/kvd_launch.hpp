@@ -43,6 +43,20 @@ hipError_t launch_topk(const float* scores, const int32_t* seq_lens, int B, int 
 // pools (16-bit dtypes); code pools need kv_scales.  cold = 8 / 4 (with kvq 0):
 // tiered pools, page p read from k_cold / v_cold in that format when
 // page_tier[p] != 0 (16-bit dtypes, G >= 2)
+// The step's delta fetch inside a cached attention launch: the list positions
+// whose cache slot is among fetch_slot[b, j, 0 .. fetch_count[b, j]) (rows of
+// sel_stride) read their block from the pools (page block_table[b, n]) instead
+// of the cache, and store it into that slot; with code pools the pools' scale
+// pair of the block goes to cache_scales too.
+struct FetchArgs {
+  const void* k_pool;
+  const void* v_pool;
+  const float* pool_scales;
+  float* cache_scales;
+  const int32_t* fetch_slot;
+  const int32_t* fetch_count;
+};
+
 hipError_t launch_paged_attn(int dtype, int D, int G, int kvq, const void* q,
                              const void* k_cache, const void* v_cache, const float* kv_scales,
                              const int32_t* block_table, const int32_t* seq_lens,
@@ -51,7 +65,7 @@ hipError_t launch_paged_attn(int dtype, int D, int G, int kvq, const void* q,
                              int maxN, int S, float scale, float* part_o, float* part_m,
                              float* part_l, float* block_lse, hipStream_t stream, int cold = 0,
                              const void* k_cold = nullptr, const void* v_cold = nullptr,
-                             const uint8_t* page_tier = nullptr);
+                             const uint8_t* page_tier = nullptr, const FetchArgs* fetch = nullptr);
 
 hipError_t launch_cache_plan(const int32_t* sel, const int32_t* sel_count, int sel_stride, int B,
                              int Hkv, int maxN, int C, int32_t* slot_block, int32_t* block_slot,

@@ -33,6 +33,7 @@ EXPORTS = (
     "kv_quantize_pages_fp8", "kv_paged_decode_attn_fp8", "kv_quantize_pages_int4",
     "kv_paged_decode_attn_int4", "kv_paged_decode_attn_tiered", "kv_cache_plan",
     "kv_cache_fetch", "kv_cache_fetch_codes", "kv_cached_decode_attn_codes",
+    "kv_cached_decode_attn_fetch", "kv_cached_decode_attn_fetch_codes",
     "kv_cached_decode_attn", "kv_cache_slot_mass", "kv_check_tables", "kv_probe_stream_read",
     "kv_probe_gather_read", "kv_host_alloc", "kv_host_free",
     "kv_status_string", "kv_last_error_message",
@@ -108,6 +109,10 @@ def _load() -> ctypes.CDLL:
         "kv_cache_fetch_codes": (I32, [S, I32, I32, P, P, P, P, P, P, P, I32, P, P, P, P]),
         "kv_cached_decode_attn_codes": (I32, [S, I32, I32, P, P, P, P, P, P, P, P, I32, F, I32,
                                               P, P, P, P, P]),
+        "kv_cached_decode_attn_fetch": (I32, [S, I32, P, P, P, P, P, P, P, P, P, P, P, P, I32, F,
+                                              I32, P, P, P, P, P]),
+        "kv_cached_decode_attn_fetch_codes": (I32, [S, I32, I32, P, P, P, P, P, P, P, P, P, P, P,
+                                                    P, P, P, I32, F, I32, P, P, P, P, P]),
         "kv_cache_slot_mass": (I32, [S, I32, P, P, P, P, I32, P, P]),
         "kv_check_tables": (I32, [S, P, P, P, P, I32, P, P]),
         "kv_probe_stream_read": (I32, [P, SZ, P, P]),
@@ -353,6 +358,35 @@ def kv_cached_decode_attn_codes(shape: KVShape, num_slots: int, code_format: int
                                             _p(sel_slots), sel_stride, scale, num_splits,
                                             _p(part_o), _p(part_m), _p(part_l), _p(block_lse),
                                             _stream(stream)))
+
+
+def kv_cached_decode_attn_fetch(shape: KVShape, num_slots: int, q: Buf, k_pool: Buf, v_pool: Buf,
+                                block_table: Buf, fetch_slot: Buf, fetch_count: Buf,
+                                cache_k: Buf, cache_v: Buf, seq_lens: Buf, sel_blocks: Buf,
+                                sel_count: Buf, sel_slots: Buf, sel_stride: int, scale: float,
+                                num_splits: int, part_o: Buf, part_m: Buf, part_l: Buf,
+                                block_lse: Buf = None, stream=None) -> None:
+    _check(_lib.kv_cached_decode_attn_fetch(
+        ctypes.byref(shape), num_slots, _p(q), _p(k_pool), _p(v_pool), _p(block_table),
+        _p(fetch_slot), _p(fetch_count), _p(cache_k), _p(cache_v), _p(seq_lens), _p(sel_blocks),
+        _p(sel_count), _p(sel_slots), sel_stride, scale, num_splits, _p(part_o), _p(part_m),
+        _p(part_l), _p(block_lse), _stream(stream)))
+
+
+def kv_cached_decode_attn_fetch_codes(shape: KVShape, num_slots: int, code_format: int, q: Buf,
+                                      k_codes: Buf, v_codes: Buf, kv_scales: Buf,
+                                      block_table: Buf, fetch_slot: Buf, fetch_count: Buf,
+                                      cache_k: Buf, cache_v: Buf, cache_scales: Buf,
+                                      seq_lens: Buf, sel_blocks: Buf, sel_count: Buf,
+                                      sel_slots: Buf, sel_stride: int, scale: float,
+                                      num_splits: int, part_o: Buf, part_m: Buf, part_l: Buf,
+                                      block_lse: Buf = None, stream=None) -> None:
+    _check(_lib.kv_cached_decode_attn_fetch_codes(
+        ctypes.byref(shape), num_slots, code_format, _p(q), _p(k_codes), _p(v_codes),
+        _p(kv_scales), _p(block_table), _p(fetch_slot), _p(fetch_count), _p(cache_k),
+        _p(cache_v), _p(cache_scales), _p(seq_lens), _p(sel_blocks), _p(sel_count),
+        _p(sel_slots), sel_stride, scale, num_splits, _p(part_o), _p(part_m), _p(part_l),
+        _p(block_lse), _stream(stream)))
 
 
 def kv_cache_slot_mass(shape: KVShape, num_slots: int, block_lse: Buf, lse: Buf, sel_count: Buf,

@@ -364,16 +364,48 @@ class DeviceWorkload:
                                        self.topk, self.scale, S, po, pm, pl, lse, stream)
         return S
 
+    def cached_attention_fetch(self, num_splits: Optional[int] = None, with_lse: bool = True,
+                               stream=None):
+        """The step's delta fetch and the attention over the cache in one launch
+        (kv_cached_decode_attn_fetch / _codes): what cache_fetch() followed by
+        cached_attention() computes."""
+        lse = self.block_lse if with_lse else None
+        if self.cache_codes is None:
+            S = num_splits or self.auto_splits(True)
+            po, pm, pl = self.partials(S)
+            kd.kv_cached_decode_attn_fetch(self.shape, self.num_slots, self.q, self.k_cache,
+                                           self.v_cache, self.block_table, self.fetch_slot,
+                                           self.fetch_count, self.cache_k, self.cache_v,
+                                           self.seq_lens, self.sel, self.sel_count,
+                                           self.sel_slots, self.topk, self.scale, S, po, pm, pl,
+                                           lse, stream)
+            return S
+        fmt, kc, vc, sc = self._code_pools()
+        S = num_splits or kd.kv_auto_num_splits_fp8(self.shape, self.topk)
+        po, pm, pl = self.partials(S)
+        kd.kv_cached_decode_attn_fetch_codes(self.shape, self.num_slots, fmt, self.q, kc, vc, sc,
+                                             self.block_table, self.fetch_slot, self.fetch_count,
+                                             self.cache_k, self.cache_v, self.cache_scales,
+                                             self.seq_lens, self.sel, self.sel_count,
+                                             self.sel_slots, self.topk, self.scale, S, po, pm, pl,
+                                             lse, stream)
+        return S
+
     def cache_slot_mass(self, stream=None):
         kd.kv_cache_slot_mass(self.shape, self.num_slots, self.block_lse, self.lse,
                               self.sel_count, self.sel_slots, self.topk, self.slot_mass, stream)
 
-    def cache_step(self, k: int, num_splits: Optional[int] = None, stream=None):
-        """select -> plan -> delta fetch -> attention over the cache -> merge -> masses."""
+    def cache_step(self, k: int, num_splits: Optional[int] = None, stream=None,
+                   fused: bool = False):
+        """select -> plan -> delta fetch -> attention over the cache -> merge ->
+        masses; with ``fused`` the fetch and the attention are one launch."""
         self.score_topk(k, stream)
         self.cache_plan(stream)
-        self.cache_fetch(stream)
-        S = self.cached_attention(num_splits, True, stream)
+        if fused:
+            S = self.cached_attention_fetch(num_splits, True, stream)
+        else:
+            self.cache_fetch(stream)
+            S = self.cached_attention(num_splits, True, stream)
         self.combine(S, stream)
         self.cache_slot_mass(stream)
         return S

@@ -440,3 +440,43 @@ def test_code_cache_argument_checks():
     expect(kd.KV_ERR_INVALID_ARG, attend(scale=-1.0))
     expect(kd.KV_ERR_ALIGNMENT, attend(cache_v=A4))
     expect(kd.KV_ERR_INVALID_ARG, attend(sel_stride=17))
+
+
+def test_fused_fetch_argument_checks():
+    s = shape()
+    f = kd.kv_cached_decode_attn_fetch
+
+    def plain(sh=s, **kw):
+        args = dict(num_slots=16, q=A16, k_pool=A16, v_pool=A16, block_table=A16,
+                    fetch_slot=A16, fetch_count=A16, cache_k=A16, cache_v=A16, seq_lens=A16,
+                    sel_blocks=A16, sel_count=A16, sel_slots=A16, sel_stride=8, scale=0.1,
+                    num_splits=2, part_o=A16, part_m=A16, part_l=A16, block_lse=None)
+        args.update(kw)
+        return lambda stream: f(sh, stream=stream, **args)
+
+    expect(kd.KV_ERR_INVALID_ARG, plain(k_pool=None))
+    expect(kd.KV_ERR_INVALID_ARG, plain(block_table=None))
+    expect(kd.KV_ERR_INVALID_ARG, plain(fetch_count=None))
+    expect(kd.KV_ERR_ALIGNMENT, plain(v_pool=A4))
+    expect(kd.KV_ERR_ALIGNMENT, plain(fetch_slot=ODD))
+    expect(kd.KV_ERR_INVALID_ARG, plain(sel_slots=None))
+    expect(kd.KV_ERR_INVALID_ARG, plain(num_slots=0))
+    expect(kd.KV_ERR_INVALID_ARG, plain(sel_stride=17))
+    expect(kd.KV_ERR_INVALID_ARG, plain(num_splits=0))
+    g = kd.kv_cached_decode_attn_fetch_codes
+
+    def codes(sh=s, **kw):
+        args = dict(num_slots=16, code_format=kd.KV_COLD_INT4, q=A16, k_codes=A16, v_codes=A16,
+                    kv_scales=A16, block_table=A16, fetch_slot=A16, fetch_count=A16,
+                    cache_k=A16, cache_v=A16, cache_scales=A16, seq_lens=A16, sel_blocks=A16,
+                    sel_count=A16, sel_slots=A16, sel_stride=8, scale=0.1, num_splits=2,
+                    part_o=A16, part_m=A16, part_l=A16, block_lse=None)
+        args.update(kw)
+        return lambda stream: g(sh, stream=stream, **args)
+
+    expect(kd.KV_ERR_INVALID_ARG, codes(code_format=3))
+    expect(kd.KV_ERR_UNSUPPORTED, codes(sh=shape(dtype="f32")))
+    expect(kd.KV_ERR_INVALID_ARG, codes(kv_scales=None))
+    expect(kd.KV_ERR_INVALID_ARG, codes(cache_scales=None))
+    expect(kd.KV_ERR_ALIGNMENT, codes(cache_scales=A4))
+    expect(kd.KV_ERR_INVALID_ARG, codes(v_codes=None))
