@@ -7,14 +7,17 @@
 //                       missing blocks reuse the first m of [free slots by
 //                       index, then unselected slots by increasing mass (ties:
 //                       lower slot)], taken in increasing slot order
-//   cache_fetch_kernel  copies only the missing K/V tiles from the (host) pool
-//                       into their cache slots: the delta fetch
+//   cache_fetch_kernel  copies only the missing K/V tiles (16-bit, fp32 or code
+//                       pages) from the (host) pool into their cache slots: the
+//                       delta fetch (the attention kernels can also do it
+//                       themselves, in the same launch)
 //   slot_mass_kernel    eviction mass of every slot from the step's attention:
 //                       max over the group's heads of exp(block_lse - lse), 0
 //                       for slots the step did not attend
 //
-// The cache pools are [B * C, Hkv, bs, D]: page b*C + s holds slot s of every
-// KV head of sequence b (each head's slot s caches its own block).
+// The cache pools are [B * C, Hkv, bs, D] (code pools: D or D/2 bytes per
+// row, with fp32 (k, v) scales [B * C, Hkv, 2]): page b*C + s holds slot s of
+// every KV head of sequence b (each head's slot s caches its own block).
 #include <math.h>
 
 #include "kvd_device.hpp"
@@ -26,21 +29,10 @@ namespace kvd {
 constexpr int kPlanThreads = 1024;
 constexpr int kPlanWaves = kPlanThreads / kWave;
 
-__device__ inline uint32_t block_sum_u32(uint32_t v, uint32_t* buf) {
-  const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x >> 6;
-#pragma unroll
-  for (int off = 1; off < kWave; off <<= 1) v += (uint32_t)__shfl_xor((int)v, off, kWave);
-  __syncthreads();                        // buf may still be read by a previous call
-  if (lane == 0) buf[wave] = v;
-  __syncthreads();
-  uint32_t t = 0;
-#pragma unroll
-  for (int w = 0; w < kPlanWaves; ++w) t += buf[w];
-  return t;
-}
-
 // Exclusive prefix over threads (in thread order) of v; buf holds kPlanWaves.
-__device__ inline uint32_t block_exclusive_u32(uint32_t v, uint32_t* buf) {
+// With total, also the sum over the block (same two barriers).
+__device__ inline uint32_t block_exclusive_u32(uint32_t v, uint32_t* buf,
+                                               uint32_t* total = nullptr) {
   const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x >> 6;
   uint32_t inc = v;
 #pragma unroll
@@ -51,8 +43,13 @@ __device__ inline uint32_t block_exclusive_u32(uint32_t v, uint32_t* buf) {
   __syncthreads();
   if (lane == kWave - 1) buf[wave] = inc;
   __syncthreads();
-  uint32_t before = 0;
-  for (int w = 0; w < wave; ++w) before += buf[w];
+  uint32_t before = 0, all = 0;
+#pragma unroll
+  for (int w = 0; w < kPlanWaves; ++w) {
+    if (w < wave) before += buf[w];
+    all += buf[w];
+  }
+  if (total) *total = all;
   return before + inc - v;
 }
 
@@ -81,6 +78,16 @@ __global__ __launch_bounds__(kPlanThreads) void cache_plan_kernel(
   int32_t* fb = fetch_block + u * sel_stride;
   int32_t* fs = fetch_slot + u * sel_stride;
 
+  // slot states first: they do not depend on the list (a slot's entry is
+  // rewritten below only by the one thread that reuses it, after these reads)
+  int32_t sbv[EPT];
+  float mv[EPT];
+#pragma unroll
+  for (int r = 0; r < EPT; ++r) {
+    const int c = tid * EPT + r;
+    sbv[r] = c < C ? sb[c] : 0;
+    mv[r] = c < C ? mass[c] : 0.0f;
+  }
   for (int c = tid; c < C; c += kPlanThreads) in_use[c] = 0;
   __syncthreads();
   // hits keep their slots; count the misses of this thread's positions
@@ -96,8 +103,8 @@ __global__ __launch_bounds__(kPlanThreads) void cache_plan_kernel(
       else ++my_miss;
     }
   }
-  const uint32_t miss_before = block_exclusive_u32(my_miss, buf);   // also orders in_use
-  const uint32_t m = block_sum_u32(my_miss, buf);
+  uint32_t m;
+  const uint32_t miss_before = block_exclusive_u32(my_miss, buf, &m);   // also orders in_use
 
   // slot states
   uint32_t key[EPT];
@@ -107,15 +114,15 @@ __global__ __launch_bounds__(kPlanThreads) void cache_plan_kernel(
     const int c = tid * EPT + r;
     key[r] = 0u;
     if (c < C) {
-      if (sb[c] < 0) free_mask |= 1u << r;
+      if (sbv[r] < 0) free_mask |= 1u << r;
       else if (!in_use[c]) {
         elig_mask |= 1u << r;
-        key[r] = __float_as_uint(fmaxf(mass[c], 0.0f));   // monotone for masses >= 0
+        key[r] = __float_as_uint(fmaxf(mv[r], 0.0f));   // monotone for masses >= 0
       }
     }
   }
-  const uint32_t n_free = block_sum_u32((uint32_t)__popc(free_mask), buf);
-  const uint32_t free_before = block_exclusive_u32((uint32_t)__popc(free_mask), buf);
+  uint32_t n_free;
+  const uint32_t free_before = block_exclusive_u32((uint32_t)__popc(free_mask), buf, &n_free);
 
   // reused: the first min(m, n_free) free slots, then the m - n_free smallest
   // (mass, slot) among the eligible slots (radix select from the top byte)
@@ -226,10 +233,9 @@ __global__ __launch_bounds__(kPlanThreads) void cache_plan_kernel(
 // block fetch_block[b, j, k] from the pool page block_table[b, n] into cache
 // page b*C + fetch_slot[b, j, k].  Source bytes are read once (non-temporal;
 // they may be mapped host memory), the cache tile is read by the attention
-// right after and is stored normally.
-// One wave per missing (block, KV head) tile.  TILE is the tile's size in the
-// pools' format: 16 * D elements of a 16-bit or fp32 pool, or the codes of a
-// code pool (16 * D bytes of E4M3, 16 * D / 2 of INT4); a code pool's tile also
+// right after and is stored normally.  TILE is the tile's size in the pools'
+// format: 16 * D elements of a 16-bit or fp32 pool, or the codes of a code
+// pool (16 * D bytes of E4M3, 16 * D / 2 of INT4); a code pool's tile also
 // brings its (k, v) scale pair along.
 template <int TILE>
 __global__ __launch_bounds__(kWave) void cache_fetch_kernel(
