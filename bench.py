@@ -1023,6 +1023,8 @@ def main():
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "f32",
+        "arithmetic": "K/V and q in their bf16 storage type as matrix-core operands (products "
+                      "exact in fp32); fp32 sums, softmax, Quest scores and merge",
         "data": "synthetic",
         "config": {
             "workload": spec.name, "batch": spec.num_seqs, "context": spec.seq_lens[0],
