@@ -437,6 +437,13 @@ def time_codes(args, copies, k, time_loop, graph_us, fmt: str):
     tier = torch.from_numpy(tier_np).to(copies[0].device)
     s_tier = kd.kv_auto_num_splits_tiered(copies[0].shape, spec.max_blocks)
     res["tiered_dense_us"] = kernel_us(lambda c: c.attention_tiered(False, fmt, tier, s_tier))
+    # the same as two launches over the block lists split by tier
+    nb = spec.max_blocks
+    s_hot = kd.kv_auto_num_splits(copies[0].shape, nb // 4)
+    s_cold = kd.kv_auto_num_splits_fp8(copies[0].shape, nb - nb // 4)
+    res["tiered_split_dense_us"] = kernel_us(
+        lambda c: c.attention_tiered_split(False, fmt, tier, s_hot, s_cold))
+    res["tiered_split_splits"] = [s_hot, s_cold]
     res["tiered_dense_bytes"], res["tiered_cold_fraction"] = tiered_bytes(spec, data.block_table,
                                                                           tier_np, fmt, s_tier)
     res["tiered_splits"] = s_tier
@@ -537,6 +544,7 @@ def run_other_workload(args, name):
 def run_zero_copy(args):
     """Sparse decode with K/V read directly from mapped pinned host memory."""
     import torch
+    from kv_cache_decode_amd import kvdecode as kd
     from kv_cache_decode_amd import workload as wl
     from kv_cache_decode_amd.step import DeviceWorkload
 
@@ -602,7 +610,7 @@ def run_zero_copy(args):
     # KVDrive's tiering: the most recent quarter of each sequence hot in HBM (16-bit
     # pages), the rest cold INT4 pages in host memory; each selected block is read
     # from its own tier, so only the cold ones cross the link
-    tier_ms, tier_link = [], 0
+    tier_ms, tier_split_ms, tier_link = [], [], 0
     if not args.no_variants:
         from kv_cache_decode_amd.step import storage_tensor
         tier_np = np.ones(spec.num_pages, np.uint8)
@@ -621,6 +629,18 @@ def run_zero_copy(args):
             e[1].record()
             torch.cuda.synchronize()
             tier_ms.append(e[0].elapsed_time(e[1]))
+        # the same as a hot launch (HBM) and a cold launch (host link) over the
+        # lists split by tier
+        s_hot = kd.kv_auto_num_splits(dw.shape, k // 4)
+        s_cold = kd.kv_auto_num_splits(dw.shape, k - k // 4)
+        for _ in range(3):
+            dw.attention_tiered_split(True, "int4", tier, s_hot, s_cold)
+        for _ in range(reps):
+            e[0].record()
+            dw.attention_tiered_split(True, "int4", tier, s_hot, s_cold)
+            e[1].record()
+            torch.cuda.synchronize()
+            tier_split_ms.append(e[0].elapsed_time(e[1]))
         sel_np, cnt_np = dw.sel.cpu().numpy(), dw.sel_count.cpu().numpy()
         cold_blocks = sum(int(tier_np[data.block_table[b, n]])
                           for b in range(spec.num_seqs) for j in range(spec.num_kv_heads)
@@ -646,7 +666,6 @@ def run_zero_copy(args):
     h2d_gbps = n / (best * 1e-3) / 1e9
     del src, dst
     # the same bytes read by a kernel straight from mapped pinned memory
-    from kv_cache_decode_amd import kvdecode as kd
     hp, dp = kd.kv_host_alloc(n)
     try:
         sink = torch.empty(kd.PROBE_SINK_WORDS, dtype=torch.int32, device=dev)
@@ -684,7 +703,8 @@ def run_zero_copy(args):
                   "pages in HBM", "cold": "INT4 pages in mapped host memory",
                   "host_link_bytes": tier_link,
                   "host_link_gbps": tier_link / (tm * 1e-3) / 1e9,
-                  "speedup_vs_bf16": attn / tm}
+                  "speedup_vs_bf16": attn / tm,
+                  "split_launches_us": float(np.median(tier_split_ms)) * 1e3}
     int4 = None
     if int4_ms:
         f4 = float(np.median(int4_ms))
@@ -909,7 +929,11 @@ def codes_record(spec, f: dict, fmt: str) -> dict:
             "cold_fraction": f["tiered_cold_fraction"], "us": f["tiered_dense_us"],
             "splits": f["tiered_splits"],
             "bytes": f["tiered_dense_bytes"],
-            "gbps": f["tiered_dense_bytes"] / (f["tiered_dense_us"] * 1e-6) / 1e9},
+            "gbps": f["tiered_dense_bytes"] / (f["tiered_dense_us"] * 1e-6) / 1e9,
+            "split_launches_us": f["tiered_split_dense_us"],
+            "split_launches_splits": f["tiered_split_splits"],
+            "split_launches_gbps": f["tiered_dense_bytes"] / (f["tiered_split_dense_us"] * 1e-6)
+            / 1e9},
     }
 
 

@@ -13,6 +13,8 @@
  *   kv_quantize_pages_int4 K/V pages -> INT4 cold pages with per-page scales
  *   kv_paged_decode_attn_int4 decode attention over INT4 cold pages
  *   kv_paged_decode_attn_tiered decode attention over hot 16-bit and cold code pages
+ *   kv_paged_decode_attn_tiered_split the same as a hot launch and a cold launch
+ *                         over the block lists split by tier
  *   kv_cache_plan         GPU block cache: hits, misses and lookahead eviction
  *   kv_cache_fetch        copy only the missing blocks into their cache slots
  *   kv_cached_decode_attn decode attention over the cached blocks, with each
@@ -401,6 +403,33 @@ kv_status kv_paged_decode_attn_tiered(const kv_shape* shape, const void* q, cons
                                       const int32_t* sel_blocks, const int32_t* sel_count,
                                       int32_t sel_stride, float scale, int32_t num_splits,
                                       float* part_o, float* part_m, float* part_l, void* stream);
+
+/*
+ * Tiered pools as two launches: the list (sel_blocks, or every block of the
+ * sequence when sel_blocks is NULL) of each (b, KV head) is split by page_tier
+ * into a hot list and a cold list (order kept) in the workspace, then the
+ * hot blocks are attended by the 16-bit kernel in num_splits_hot splits and
+ * the cold ones by the code-page kernel in num_splits_cold splits, each
+ * launch with the register budget of its own page format.  The partials hold
+ * S = num_splits_hot + num_splits_cold splits per row ([B, Hq, S, D] and
+ * [B, Hq, S]): columns [0, num_splits_hot) cover the hot list, the others the
+ * cold list, each list chunked as kv_paged_decode_attn chunks a list, and
+ * kv_decode_combine with S merges them.  The merged result is what
+ * kv_paged_decode_attn_tiered computes (up to the order of the fp32 sums).
+ * The pools, formats and errors are those of kv_paged_decode_attn_tiered,
+ * except that any dtype and group size the two kernels serve is accepted
+ * (INT4 needs fp16 or bf16).  The workspace holds the lists:
+ * kv_tiered_split_workspace_size(shape, sel_stride) bytes (sel_stride 0 for
+ * dense lists), 4-byte aligned, else KV_ERR_WORKSPACE.
+ */
+size_t kv_tiered_split_workspace_size(const kv_shape* shape, int32_t sel_stride);
+kv_status kv_paged_decode_attn_tiered_split(
+    const kv_shape* shape, const void* q, const void* k_cache, const void* v_cache,
+    const uint8_t* k_cold, const uint8_t* v_cold, const float* kv_scales, int32_t cold_format,
+    const uint8_t* page_tier, const int32_t* block_table, const int32_t* seq_lens,
+    const int32_t* sel_blocks, const int32_t* sel_count, int32_t sel_stride, float scale,
+    int32_t num_splits_hot, int32_t num_splits_cold, float* part_o, float* part_m,
+    float* part_l, void* workspace, size_t workspace_bytes, void* stream);
 
 /*
  * GPU-resident block cache with lookahead eviction (KVDrive §5.1: a window of

@@ -95,6 +95,21 @@ size_t scores_bytes(const kv_shape* s) {
   return (size_t)s->num_seqs * s->num_kv_heads * s->max_blocks_per_seq * sizeof(float);
 }
 
+// Bytes of one (page, KV head) tile of a code pool; 0 for an unknown format.
+int code_tile_bytes(const kv_shape* shape, int32_t code_format) {
+  const int tile = shape->block_size * shape->head_dim;
+  return code_format == KV_COLD_FP8 ? tile : (code_format == KV_COLD_INT4 ? tile / 2 : 0);
+}
+
+kv_status check_code_format(const kv_shape* shape, int32_t code_format) {
+  if (code_format != KV_COLD_FP8 && code_format != KV_COLD_INT4)
+    return fail(KV_ERR_INVALID_ARG, "code_format=%d must be KV_COLD_FP8 or KV_COLD_INT4",
+                code_format);
+  if (code_format == KV_COLD_INT4 && shape->dtype == KV_F32)
+    return fail(KV_ERR_UNSUPPORTED, "INT4 pages are read with fp16 or bf16 queries");
+  return KV_OK;
+}
+
 // Validation and launch shared by the 16-bit/fp32 pools (kvq 0) and the code
 // pools (kvq 8: E4M3, kvq 4: INT4; kv_scales != nullptr).
 kv_status attn_common(const kv_shape* shape, int kvq, const void* q, const void* k_cache,
@@ -508,6 +523,79 @@ kv_status kv_paged_decode_attn_tiered(const kv_shape* shape, const void* q, cons
                      cold_format, k_cold, v_cold, page_tier);
 }
 
+size_t kv_tiered_split_workspace_size(const kv_shape* shape, int32_t sel_stride) {
+  if (!shape || check_shape(shape) != KV_OK || sel_stride < 0) return 0;
+  const size_t stride = sel_stride > 0 ? (size_t)sel_stride : (size_t)shape->max_blocks_per_seq;
+  const size_t rows = (size_t)shape->num_seqs * shape->num_kv_heads;
+  return 2 * rows * (stride + 1) * sizeof(int32_t);
+}
+
+kv_status kv_paged_decode_attn_tiered_split(
+    const kv_shape* shape, const void* q, const void* k_cache, const void* v_cache,
+    const uint8_t* k_cold, const uint8_t* v_cold, const float* kv_scales, int32_t cold_format,
+    const uint8_t* page_tier, const int32_t* block_table, const int32_t* seq_lens,
+    const int32_t* sel_blocks, const int32_t* sel_count, int32_t sel_stride, float scale,
+    int32_t num_splits_hot, int32_t num_splits_cold, float* part_o, float* part_m,
+    float* part_l, void* workspace, size_t workspace_bytes, void* stream) {
+  kv_status st = check_shape(shape);
+  if (st != KV_OK) return st;
+  if ((st = check_code_format(shape, cold_format)) != KV_OK) return st;
+  if (num_splits_hot < 1 || num_splits_cold < 1 ||
+      (long)num_splits_hot + num_splits_cold > 65535L * 4)
+    return fail(KV_ERR_INVALID_ARG, "num_splits_hot=%d and num_splits_cold=%d must be >= 1 "
+                "with a sum of at most 262140", num_splits_hot, num_splits_cold);
+  if (!k_cold || !v_cold || !kv_scales || !page_tier)
+    return fail(KV_ERR_INVALID_ARG, "k_cold, v_cold, kv_scales and page_tier are required");
+  if (!aligned(k_cold, 16) || !aligned(v_cold, 16) || !aligned(kv_scales, 8))
+    return fail(KV_ERR_ALIGNMENT, "the cold pools must be 16-byte aligned, kv_scales 8-byte");
+  if ((sel_blocks == nullptr) != (sel_count == nullptr))
+    return fail(KV_ERR_INVALID_ARG, "sel_blocks and sel_count go together");
+  if (sel_blocks && sel_stride < 1)
+    return fail(KV_ERR_INVALID_ARG, "sel_stride=%d must be >= 1", sel_stride);
+  const size_t need = kv_tiered_split_workspace_size(shape, sel_blocks ? sel_stride : 0);
+  if (!workspace || workspace_bytes < need)
+    return fail(KV_ERR_WORKSPACE, "the workspace needs %zu bytes", need);
+  if (!aligned(workspace, 4)) return fail(KV_ERR_ALIGNMENT, "the workspace must be 4-byte aligned");
+  if (!q || !k_cache || !v_cache || !block_table || !seq_lens || !part_o || !part_m || !part_l)
+    return fail(KV_ERR_INVALID_ARG, "q, k_cache, v_cache, block_table, seq_lens and partials are required");
+  if (!(scale > 0.0f) || !(scale < INFINITY))
+    return fail(KV_ERR_INVALID_ARG, "scale must be finite and positive");
+  if (!aligned(q, 16) || !aligned(k_cache, 16) || !aligned(v_cache, 16) || !aligned(part_o, 16))
+    return fail(KV_ERR_ALIGNMENT, "q, k_cache, v_cache and part_o must be 16-byte aligned");
+  if (!aligned(block_table, 4) || !aligned(seq_lens, 4) || !aligned(part_m, 4) ||
+      !aligned(part_l, 4) || (sel_blocks && (!aligned(sel_blocks, 4) || !aligned(sel_count, 4))))
+    return fail(KV_ERR_ALIGNMENT, "integer and partial arrays must be 4-byte aligned");
+  const int stride = sel_blocks ? sel_stride : shape->max_blocks_per_seq;
+  const size_t rows = (size_t)shape->num_seqs * shape->num_kv_heads;
+  int32_t* ws = static_cast<int32_t*>(workspace);
+  int32_t* hot = ws;
+  int32_t* cold = hot + rows * stride;
+  int32_t* hot_n = cold + rows * stride;
+  int32_t* cold_n = hot_n + rows;
+  hipStream_t s = (hipStream_t)stream;
+  const int G = shape->num_q_heads / shape->num_kv_heads;
+  const int S = num_splits_hot + num_splits_cold;
+  hipError_t e = kvd::launch_tier_lists(sel_blocks, sel_count, sel_stride, block_table, seq_lens,
+                                        page_tier, shape->num_seqs, shape->num_kv_heads,
+                                        shape->max_blocks_per_seq, stride, hot, hot_n, cold,
+                                        cold_n, s);
+  if (e == hipSuccess)     // hot pages: columns [0, num_splits_hot) of the partials
+    e = kvd::launch_paged_attn(shape->dtype, shape->head_dim, G, 0, q, k_cache, v_cache, nullptr,
+                               block_table, seq_lens, hot, hot_n, stride, nullptr, 0,
+                               shape->num_seqs, shape->num_q_heads, shape->num_kv_heads,
+                               shape->max_blocks_per_seq, num_splits_hot, scale, part_o, part_m,
+                               part_l, nullptr, s, 0, nullptr, nullptr, nullptr, nullptr, S);
+  if (e == hipSuccess)     // cold pages: the columns after them
+    e = kvd::launch_paged_attn(shape->dtype, shape->head_dim, G, cold_format, q, k_cold, v_cold,
+                               kv_scales, block_table, seq_lens, cold, cold_n, stride, nullptr, 0,
+                               shape->num_seqs, shape->num_q_heads, shape->num_kv_heads,
+                               shape->max_blocks_per_seq, num_splits_cold, scale,
+                               part_o + (size_t)num_splits_hot * shape->head_dim,
+                               part_m + num_splits_hot, part_l + num_splits_hot, nullptr, s, 0,
+                               nullptr, nullptr, nullptr, nullptr, S);
+  return hip_status(e, "kv_paged_decode_attn_tiered_split launch");
+}
+
 kv_status kv_decode_combine(const kv_shape* shape, int32_t num_splits, const float* part_o,
                             const float* part_m, const float* part_l, float* out, float* lse_out,
                             void* stream) {
@@ -627,21 +715,6 @@ kv_status cached_attn_common(const kv_shape* shape, int32_t num_slots, int kvq, 
                              num_splits, scale, part_o, part_m, part_l, block_lse,
                              (hipStream_t)stream, 0, nullptr, nullptr, nullptr, fetch),
       name);
-}
-
-// Bytes of one (page, KV head) tile of a code pool; 0 for an unknown format.
-int code_tile_bytes(const kv_shape* shape, int32_t code_format) {
-  const int tile = shape->block_size * shape->head_dim;
-  return code_format == KV_COLD_FP8 ? tile : (code_format == KV_COLD_INT4 ? tile / 2 : 0);
-}
-
-kv_status check_code_format(const kv_shape* shape, int32_t code_format) {
-  if (code_format != KV_COLD_FP8 && code_format != KV_COLD_INT4)
-    return fail(KV_ERR_INVALID_ARG, "code_format=%d must be KV_COLD_FP8 or KV_COLD_INT4",
-                code_format);
-  if (code_format == KV_COLD_INT4 && shape->dtype == KV_F32)
-    return fail(KV_ERR_UNSUPPORTED, "INT4 pages are read with fp16 or bf16 queries");
-  return KV_OK;
 }
 
 }  // namespace

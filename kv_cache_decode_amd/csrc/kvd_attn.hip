@@ -133,7 +133,8 @@ __global__ __launch_bounds__(WAVES * kWave) void paged_attn_kernel(
     const float* __restrict__ kv_scales, const int32_t* __restrict__ block_table,
     const int32_t* __restrict__ seq_lens, const int32_t* __restrict__ sel,
     const int32_t* __restrict__ sel_count, int sel_stride, const int32_t* __restrict__ sel_slots,
-    int num_slots, int Hq, int Hkv, int maxN, int S, float qscale, float* __restrict__ part_o,
+    int num_slots, int Hq, int Hkv, int maxN, int S, int PS, float qscale,
+    float* __restrict__ part_o,
     float* __restrict__ part_m, float* __restrict__ part_l, float* __restrict__ block_lse,
     FetchArgs fa) {
   static_assert(!FETCH || SPARSE, "the fused fetch serves cached lists");
@@ -348,7 +349,7 @@ __global__ __launch_bounds__(WAVES * kWave) void paged_attn_kernel(
 #pragma unroll
     for (int g = 0; g < G; ++g) {
       const float inv = lsum[g] > 0.0f ? 1.0f / lsum[g] : 0.0f;
-      float* dst = part_o + ((row0 + g) * S + s) * D + c * E;
+      float* dst = part_o + ((row0 + g) * PS + s) * D + c * E;
 #pragma unroll
       for (int e4 = 0; e4 < E; e4 += 4)
         *reinterpret_cast<float4*>(dst + e4) =
@@ -359,8 +360,8 @@ __global__ __launch_bounds__(WAVES * kWave) void paged_attn_kernel(
   if (lane == 0) {
 #pragma unroll
     for (int g = 0; g < G; ++g) {
-      part_m[(row0 + g) * S + s] = m[g] * kLn2;
-      part_l[(row0 + g) * S + s] = lsum[g];
+      part_m[(row0 + g) * PS + s] = m[g] * kLn2;
+      part_l[(row0 + g) * PS + s] = lsum[g];
     }
   }
 }
@@ -594,7 +595,8 @@ __global__ __launch_bounds__(WAVES * kWave) KVD_MFMA_OCCUPANCY_T(COLD) void page
     const float* __restrict__ kv_scales, const int32_t* __restrict__ block_table,
     const int32_t* __restrict__ seq_lens, const int32_t* __restrict__ sel,
     const int32_t* __restrict__ sel_count, int sel_stride, const int32_t* __restrict__ sel_slots,
-    int num_slots, int Hq, int Hkv, int maxN, int S, float qscale, float* __restrict__ part_o,
+    int num_slots, int Hq, int Hkv, int maxN, int S, int PS, float qscale,
+    float* __restrict__ part_o,
     float* __restrict__ part_m, float* __restrict__ part_l, float* __restrict__ block_lse,
     const void* __restrict__ k_cold, const void* __restrict__ v_cold,
     const uint8_t* __restrict__ page_tier, FetchArgs fa) {
@@ -1020,7 +1022,7 @@ __global__ __launch_bounds__(WAVES * kWave) KVD_MFMA_OCCUPANCY_T(COLD) void page
     const float lt = __shfl(lsum, g & 15, kWave);
     if (g < G) {
       const float inv = lt > 0.0f ? 1.0f / lt : 0.0f;
-      float* dst = part_o + ((row0 + g) * S + s) * D + 2 * NDW * col;
+      float* dst = part_o + ((row0 + g) * PS + s) * D + 2 * NDW * col;
 #pragma unroll
       for (int n4 = 0; n4 < NT; n4 += 4)
         *reinterpret_cast<float4*>(dst + n4) =
@@ -1029,8 +1031,8 @@ __global__ __launch_bounds__(WAVES * kWave) KVD_MFMA_OCCUPANCY_T(COLD) void page
     }
   }
   if (grp == 0 && col < G) {
-    part_m[(row0 + col) * S + s] = m * kLn2;
-    part_l[(row0 + col) * S + s] = lsum;
+    part_m[(row0 + col) * PS + s] = m * kLn2;
+    part_l[(row0 + col) * PS + s] = lsum;
   }
 }
 
@@ -1137,6 +1139,77 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
   }
 }
 
+// ============================================================== tier lists
+//
+// One 1024-thread workgroup per (sequence, KV head).  Each thread takes EPT
+// consecutive list positions of a tile, looks up their pages' tiers, and one
+// block-wide exclusive scan of its (hot, cold) counts places every entry in
+// its list, order kept.  Tiles of 1024 * EPT positions follow one another.
+constexpr int kTierThreads = 1024;
+constexpr int kTierEPT = 8;
+
+__global__ __launch_bounds__(kTierThreads) void tier_lists_kernel(
+    const int32_t* __restrict__ sel, const int32_t* __restrict__ sel_count, int sel_stride,
+    const int32_t* __restrict__ block_table, const int32_t* __restrict__ seq_lens,
+    const uint8_t* __restrict__ page_tier, int Hkv, int maxN, int out_stride,
+    int32_t* __restrict__ hot, int32_t* __restrict__ hot_count, int32_t* __restrict__ cold,
+    int32_t* __restrict__ cold_count) {
+  __shared__ uint32_t wsum[kTierThreads / kWave];
+  const int j = blockIdx.x, b = blockIdx.y;
+  const size_t u = (size_t)b * Hkv + j;
+  const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid >> 6;
+  const int nb = (seq_lens[b] + kBlockSize - 1) / kBlockSize;
+  const int n = sel ? sel_count[u] : nb;
+  const int32_t* list = sel ? sel + u * sel_stride : nullptr;
+  const int32_t* bt = block_table + (size_t)b * maxN;
+  int32_t* hot_row = hot + u * out_stride;
+  int32_t* cold_row = cold + u * out_stride;
+  uint32_t hot_base = 0, cold_base = 0;
+  for (int t0 = 0; t0 < n; t0 += kTierThreads * kTierEPT) {
+    int blk[kTierEPT];
+    uint32_t is_cold = 0;
+#pragma unroll
+    for (int r = 0; r < kTierEPT; ++r) {
+      const int pos = t0 + tid * kTierEPT + r;
+      blk[r] = -1;
+      if (pos < n) {
+        blk[r] = list ? list[pos] : pos;
+        if (page_tier[bt[blk[r]]] != 0) is_cold |= 1u << r;
+      }
+    }
+    int valid = min(kTierEPT, max(0, n - (t0 + tid * kTierEPT)));
+    const uint32_t nc = (uint32_t)__popc(is_cold);
+    const uint32_t nh = (uint32_t)valid - nc;
+    // packed (hot << 16 | cold) counts: a tile holds at most 8192 of each
+    const uint32_t packed = (nh << 16) | nc;
+    const uint32_t incl = wave_scan_add_u32(packed);
+    if (lane == kWave - 1) wsum[wave] = incl;
+    __syncthreads();
+    uint32_t before = 0, total = 0;
+#pragma unroll
+    for (int w = 0; w < kTierThreads / kWave; ++w) {
+      if (w < wave) before += wsum[w];
+      total += wsum[w];
+    }
+    __syncthreads();                               // wsum is rewritten by the next tile
+    const uint32_t ex = before + incl - packed;
+    uint32_t h = hot_base + (ex >> 16), c = cold_base + (ex & 0xFFFFu);
+#pragma unroll
+    for (int r = 0; r < kTierEPT; ++r) {
+      if (r < valid) {
+        if ((is_cold >> r) & 1u) cold_row[c++] = blk[r];
+        else hot_row[h++] = blk[r];
+      }
+    }
+    hot_base += total >> 16;
+    cold_base += total & 0xFFFFu;
+  }
+  if (tid == 0) {
+    hot_count[u] = (int)hot_base;
+    cold_count[u] = (int)cold_base;
+  }
+}
+
 // ============================================================== launchers
 
 
@@ -1148,8 +1221,9 @@ hipError_t launch_paged_attn(int dtype, int D, int G, int kvq, const void* q,
                              int maxN, int S, float scale, float* part_o, float* part_m,
                              float* part_l, float* block_lse, hipStream_t stream, int cold,
                              const void* k_cold, const void* v_cold, const uint8_t* page_tier,
-                             const FetchArgs* fetch) {
+                             const FetchArgs* fetch, int part_stride) {
   constexpr int WAVES = KVD_ATTN_WAVES;
+  const int PS = part_stride > 0 ? part_stride : S;
   const FetchArgs fa = fetch ? *fetch : FetchArgs{};
   const dim3 grid((S + WAVES - 1) / WAVES, Hkv, B);
   const float qscale = scale * kLog2e;
@@ -1167,13 +1241,13 @@ hipError_t launch_paged_attn(int dtype, int D, int G, int kvq, const void* q,
             hipLaunchKernelGGL((paged_attn_mfma_kernel<DT, DD, GG, WAVES, SP, KQ, CQ, FE>), grid,
                                dim3(WAVES * kWave), 0, stream, q, k_cache, v_cache, kv_scales,
                                block_table, seq_lens, sel, sel_count, sel_stride, sel_slots,
-                               num_slots, Hq, Hkv, maxN, S, qscale, part_o, part_m, part_l,
+                               num_slots, Hq, Hkv, maxN, S, PS, qscale, part_o, part_m, part_l,
                                block_lse, k_cold, v_cold, page_tier, fa);
           } else if constexpr (CQ == 0) {
             hipLaunchKernelGGL((paged_attn_kernel<DT, DD, GG, WAVES, SP, KQ, FE>), grid,
                                dim3(WAVES * kWave), 0, stream, q, k_cache, v_cache, kv_scales,
                                block_table, seq_lens, sel, sel_count, sel_stride, sel_slots,
-                               num_slots, Hq, Hkv, maxN, S, qscale, part_o, part_m, part_l,
+                               num_slots, Hq, Hkv, maxN, S, PS, qscale, part_o, part_m, part_l,
                                block_lse, fa);
           }
         };
@@ -1212,6 +1286,17 @@ hipError_t launch_paged_attn(int dtype, int D, int G, int kvq, const void* q,
       });
     });
   });
+}
+
+hipError_t launch_tier_lists(const int32_t* sel, const int32_t* sel_count, int sel_stride,
+                             const int32_t* block_table, const int32_t* seq_lens,
+                             const uint8_t* page_tier, int B, int Hkv, int maxN, int out_stride,
+                             int32_t* hot, int32_t* hot_count, int32_t* cold, int32_t* cold_count,
+                             hipStream_t stream) {
+  hipLaunchKernelGGL(tier_lists_kernel, dim3(Hkv, B), dim3(kTierThreads), 0, stream, sel,
+                     sel_count, sel_stride, block_table, seq_lens, page_tier, Hkv, maxN,
+                     out_stride, hot, hot_count, cold, cold_count);
+  return hipGetLastError();
 }
 
 hipError_t launch_combine(int D, const float* part_o, const float* part_m, const float* part_l,

@@ -57,6 +57,9 @@ struct FetchArgs {
   const int32_t* fetch_count;
 };
 
+// part_stride: splits per row of the partial arrays (0: S).  With part_o,
+// part_m and part_l offset by s0 columns, a launch fills columns
+// [s0, s0 + S) of a wider partial set that one merge reads whole.
 hipError_t launch_paged_attn(int dtype, int D, int G, int kvq, const void* q,
                              const void* k_cache, const void* v_cache, const float* kv_scales,
                              const int32_t* block_table, const int32_t* seq_lens,
@@ -65,7 +68,17 @@ hipError_t launch_paged_attn(int dtype, int D, int G, int kvq, const void* q,
                              int maxN, int S, float scale, float* part_o, float* part_m,
                              float* part_l, float* block_lse, hipStream_t stream, int cold = 0,
                              const void* k_cold = nullptr, const void* v_cold = nullptr,
-                             const uint8_t* page_tier = nullptr, const FetchArgs* fetch = nullptr);
+                             const uint8_t* page_tier = nullptr, const FetchArgs* fetch = nullptr,
+                             int part_stride = 0);
+
+// Per (sequence, KV head): the list (sel, or every block of the sequence when
+// sel is null) split by page tier into the hot (tier 0) and cold lists, both
+// in list order, rows of out_stride entries.
+hipError_t launch_tier_lists(const int32_t* sel, const int32_t* sel_count, int sel_stride,
+                             const int32_t* block_table, const int32_t* seq_lens,
+                             const uint8_t* page_tier, int B, int Hkv, int maxN, int out_stride,
+                             int32_t* hot, int32_t* hot_count, int32_t* cold, int32_t* cold_count,
+                             hipStream_t stream);
 
 hipError_t launch_cache_plan(const int32_t* sel, const int32_t* sel_count, int sel_stride, int B,
                              int Hkv, int maxN, int C, int32_t* slot_block, int32_t* block_slot,

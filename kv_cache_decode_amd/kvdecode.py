@@ -31,7 +31,8 @@ EXPORTS = (
     "kv_block_select", "kv_auto_num_splits", "kv_auto_num_splits_fp8",
     "kv_auto_num_splits_tiered", "kv_paged_decode_attn", "kv_decode_combine",
     "kv_quantize_pages_fp8", "kv_paged_decode_attn_fp8", "kv_quantize_pages_int4",
-    "kv_paged_decode_attn_int4", "kv_paged_decode_attn_tiered", "kv_cache_plan",
+    "kv_paged_decode_attn_int4", "kv_paged_decode_attn_tiered",
+    "kv_tiered_split_workspace_size", "kv_paged_decode_attn_tiered_split", "kv_cache_plan",
     "kv_cache_fetch", "kv_cache_fetch_codes", "kv_cached_decode_attn_codes",
     "kv_cached_decode_attn_fetch", "kv_cached_decode_attn_fetch_codes",
     "kv_cached_decode_attn", "kv_cache_slot_mass", "kv_check_tables", "kv_probe_stream_read",
@@ -103,6 +104,9 @@ def _load() -> ctypes.CDLL:
         "kv_paged_decode_attn_int4": (I32, [S, P, P, P, P, P, P, P, P, I32, F, I32, P, P, P, P]),
         "kv_paged_decode_attn_tiered": (I32, [S, P, P, P, P, P, P, I32, P, P, P, P, P, I32, F, I32,
                                               P, P, P, P]),
+        "kv_tiered_split_workspace_size": (SZ, [S, I32]),
+        "kv_paged_decode_attn_tiered_split": (I32, [S, P, P, P, P, P, P, I32, P, P, P, P, P, I32,
+                                                    F, I32, I32, P, P, P, P, SZ, P]),
         "kv_cache_plan": (I32, [S, I32, P, P, I32, P, P, P, P, P, P, P, P]),
         "kv_cache_fetch": (I32, [S, I32, P, P, P, P, P, P, I32, P, P, P]),
         "kv_cached_decode_attn": (I32, [S, I32, P, P, P, P, P, P, P, I32, F, I32, P, P, P, P, P]),
@@ -306,6 +310,24 @@ def kv_paged_decode_attn_tiered(shape: KVShape, q: Buf, k_cache: Buf, v_cache: B
                                             _p(sel_blocks), _p(sel_count), sel_stride, scale,
                                             num_splits, _p(part_o), _p(part_m), _p(part_l),
                                             _stream(stream)))
+
+
+def kv_tiered_split_workspace_size(shape: KVShape, sel_stride: int) -> int:
+    return int(_lib.kv_tiered_split_workspace_size(ctypes.byref(shape), sel_stride))
+
+
+def kv_paged_decode_attn_tiered_split(shape: KVShape, q: Buf, k_cache: Buf, v_cache: Buf,
+                                      k_cold: Buf, v_cold: Buf, kv_scales: Buf, cold_format: int,
+                                      page_tier: Buf, block_table: Buf, seq_lens: Buf,
+                                      sel_blocks: Buf, sel_count: Buf, sel_stride: int,
+                                      scale: float, num_splits_hot: int, num_splits_cold: int,
+                                      part_o: Buf, part_m: Buf, part_l: Buf, workspace: Buf,
+                                      workspace_bytes: int, stream=None) -> None:
+    _check(_lib.kv_paged_decode_attn_tiered_split(
+        ctypes.byref(shape), _p(q), _p(k_cache), _p(v_cache), _p(k_cold), _p(v_cold),
+        _p(kv_scales), cold_format, _p(page_tier), _p(block_table), _p(seq_lens),
+        _p(sel_blocks), _p(sel_count), sel_stride, scale, num_splits_hot, num_splits_cold,
+        _p(part_o), _p(part_m), _p(part_l), _p(workspace), workspace_bytes, _stream(stream)))
 
 
 def kv_cache_plan(shape: KVShape, num_slots: int, sel_blocks: Buf, sel_count: Buf,

@@ -288,6 +288,28 @@ class DeviceWorkload:
                                        stride, self.scale, S, po, pm, pl, stream)
         return S
 
+    def attention_tiered_split(self, sparse: bool, cold: str, page_tier,
+                               num_splits_hot: int, num_splits_cold: int, stream=None):
+        """kv_paged_decode_attn_tiered_split: the hot and the cold blocks of each
+        list as two launches; returns the merged split count."""
+        S = num_splits_hot + num_splits_cold
+        po, pm, pl = self.partials(S)
+        sel, cnt, stride = (self.sel, self.sel_count, self.topk) if sparse else (None, None, 0)
+        if cold == "fp8":
+            kc, vc, sc, fmt = self.k8, self.v8, self.kv_scales, kd.KV_COLD_FP8
+        else:
+            kc, vc, sc, fmt = self.k4, self.v4, self.kv_scales4, kd.KV_COLD_INT4
+        need = kd.kv_tiered_split_workspace_size(self.shape, stride)
+        ws = getattr(self, "_tier_ws", None)
+        if ws is None or ws.numel() < need:
+            ws = self._tier_ws = torch.empty(need, dtype=torch.uint8, device=self.device)
+        kd.kv_paged_decode_attn_tiered_split(self.shape, self.q, self.k_cache, self.v_cache, kc,
+                                             vc, sc, fmt, page_tier, self.block_table,
+                                             self.seq_lens, sel, cnt, stride, self.scale,
+                                             num_splits_hot, num_splits_cold, po, pm, pl, ws,
+                                             need, stream)
+        return S
+
     def decode_tiered(self, sparse: bool, cold: str, page_tier, num_splits: Optional[int] = None,
                       stream=None):
         S = self.attention_tiered(sparse, cold, page_tier, num_splits, stream)

@@ -480,3 +480,33 @@ def test_fused_fetch_argument_checks():
     expect(kd.KV_ERR_INVALID_ARG, codes(cache_scales=None))
     expect(kd.KV_ERR_ALIGNMENT, codes(cache_scales=A4))
     expect(kd.KV_ERR_INVALID_ARG, codes(v_codes=None))
+
+
+def test_tiered_split_argument_checks():
+    s = shape()
+    f = kd.kv_paged_decode_attn_tiered_split
+    need = kd.kv_tiered_split_workspace_size(s, 0)
+    assert need == 2 * 2 * 2 * (4 + 1) * 4          # two lists of (maxN + 1) ints per (b, j)
+    assert kd.kv_tiered_split_workspace_size(s, 3) == 2 * 2 * 2 * (3 + 1) * 4
+    assert kd.kv_tiered_split_workspace_size(s, -1) == 0
+
+    def call(sh=s, **kw):
+        args = dict(q=A16, k_cache=A16, v_cache=A16, k_cold=A16, v_cold=A16, kv_scales=A16,
+                    cold_format=kd.KV_COLD_FP8, page_tier=A16, block_table=A16, seq_lens=A16,
+                    sel_blocks=None, sel_count=None, sel_stride=0, scale=0.1,
+                    num_splits_hot=2, num_splits_cold=3, part_o=A16, part_m=A16, part_l=A16,
+                    workspace=A16, workspace_bytes=need)
+        args.update(kw)
+        return lambda stream: f(sh, stream=stream, **args)
+
+    expect(kd.KV_ERR_INVALID_ARG, call(cold_format=7))
+    expect(kd.KV_ERR_UNSUPPORTED, call(sh=shape(dtype="f32"), cold_format=kd.KV_COLD_INT4))
+    expect(kd.KV_ERR_INVALID_ARG, call(num_splits_hot=0))
+    expect(kd.KV_ERR_INVALID_ARG, call(num_splits_cold=0))
+    expect(kd.KV_ERR_INVALID_ARG, call(page_tier=None))
+    expect(kd.KV_ERR_WORKSPACE, call(workspace_bytes=need - 1))
+    expect(kd.KV_ERR_WORKSPACE, call(workspace=None))
+    expect(kd.KV_ERR_ALIGNMENT, call(workspace=ODD))
+    expect(kd.KV_ERR_ALIGNMENT, call(k_cold=A4))
+    expect(kd.KV_ERR_INVALID_ARG, call(sel_blocks=A16))
+    expect(kd.KV_ERR_INVALID_ARG, call(scale=0.0))

@@ -51,7 +51,7 @@ def test_code_page_bytes():
     f = {"s_sparse": 3, "s_dense": 5, "quantize_us": 1.0, "dense_attn_us": 1.0,
          "sparse_attn_us": 1.0, "decode_sparse_us": 1.0, "decode_dense_us": 1.0,
          "tiered_dense_us": 1.0, "tiered_dense_bytes": 1, "tiered_cold_fraction": 0.5,
-         "tiered_splits": 5}
+         "tiered_splits": 5, "tiered_split_dense_us": 1.0, "tiered_split_splits": [1, 4]}
     pages, Hkv, D, bs = 10, 2, 64, 16
     q = 2 * 8 * D * 2
     parts = lambda S: 2 * 8 * S * (D + 2) * 4

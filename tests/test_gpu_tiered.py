@@ -122,3 +122,73 @@ def test_tiered_rejects_unsupported_shapes(gpu):
                                            *dw.partials(1))
         assert e.value.status == kd.KV_ERR_UNSUPPORTED
         dw.close()
+
+
+SPLIT_GRID = [("bf16", 128, 4, "int4", 6401), ("f16", 64, 2, "fp8", 6402),
+              ("bf16", 64, 8, "fp8", 6403), ("f16", 128, 1, "int4", 6404),
+              ("f32", 128, 2, "fp8", 6405), ("f32", 64, 1, "fp8", 6406)]
+
+
+@pytest.mark.parametrize("dtype,D,G,cold,seed", SPLIT_GRID,
+                         ids=[f"{d}-D{D}-G{G}-{c}" for d, D, G, c, _ in SPLIT_GRID])
+def test_tiered_split_launches(gpu, dtype, D, G, cold, seed):
+    """kv_paged_decode_attn_tiered_split: hot and cold lists as two launches,
+    merged over hot + cold splits, against the oracle over the decoded pools;
+    both kernels (G = 1 and fp32 run the VALU kernel), dense and selected
+    lists, split counts from 1 to more than a list holds, all-hot and
+    all-cold tiers (one launch then has only empty splits)."""
+    from kv_cache_decode_amd.step import DeviceWorkload
+    Hkv = 2
+    data = mk(5, Hkv * G, Hkv, D, (543, 1, 15, 16, 17), dtype, seed, extra_pages=3,
+              planted_frac=0.1)
+    dw = DeviceWorkload(data, device=gpu)
+    try:
+        dw.quantize_fp8(host=False) if cold == "fp8" else dw.quantize_int4(host=False)
+        rng = np.random.default_rng(seed)
+        P = data.spec.num_pages
+        tol = ROW_TOL[dtype]
+        sel, cnt = wl.random_selection(data, 6, seed=seed)
+        for tier in ((rng.random(P) < 0.5).astype(np.uint8), np.zeros(P, np.uint8),
+                     np.ones(P, np.uint8)):
+            tier_dev = torch.from_numpy(tier).to(gpu)
+            o = TieredRun(data, cold, tier)
+            ref_dense, ref_lse = o.attention()
+            for sh, sc in ((1, 1), (2, 5), (7, 3)):
+                S = dw.attention_tiered_split(False, cold, tier_dev, sh, sc)
+                dw.combine(S)
+                assert_rows_close(to_f64(dw.out), ref_dense, tol, f"split dense {sh}+{sc}")
+                np.testing.assert_allclose(to_f64(dw.lse), ref_lse, rtol=tol, atol=tol)
+            dw.set_selection(sel, cnt)
+            ref_sparse, _ = o.attention(sel, cnt)
+            for sh, sc in ((1, 1), (3, 2)):
+                S = dw.attention_tiered_split(True, cold, tier_dev, sh, sc)
+                dw.combine(S)
+                assert_rows_close(to_f64(dw.out), ref_sparse, tol, f"split sparse {sh}+{sc}")
+    finally:
+        torch.cuda.synchronize()
+        dw.close()
+
+
+def test_tiered_split_full_size_128k(gpu):
+    """The 128k GQA shape, a quarter hot, INT4 cold pages: split launches against
+    the oracle (dense, automatic split counts)."""
+    from kv_cache_decode_amd.step import DeviceWorkload
+    spec = wl.WORKLOADS["llama3.1_8b_gqa_b1_128k_bf16"]
+    print("\n[tiered split 128k] generating", flush=True)
+    data = wl.generate(spec)
+    dw = DeviceWorkload(data, device=gpu)
+    try:
+        dw.quantize_int4(host=False)
+        tier = np.ones(spec.num_pages, np.uint8)
+        nb = spec.blocks(0)
+        tier[data.block_table[0, nb - nb // 4:nb]] = 0
+        sh = kd.kv_auto_num_splits(dw.shape, nb // 4)
+        sc = kd.kv_auto_num_splits_fp8(dw.shape, nb - nb // 4)
+        S = dw.attention_tiered_split(False, "int4", torch.from_numpy(tier).to(gpu), sh, sc)
+        dw.combine(S)
+        rel = assert_rows_close(to_f64(dw.out), TieredRun(data, "int4", tier).attention()[0],
+                                ROW_TOL["bf16"], "tiered split 128k")
+        print(f"[tiered split 128k] {sh} + {sc} splits, worst row rel-err {rel:.2e}", flush=True)
+    finally:
+        torch.cuda.synchronize()
+        dw.close()
