@@ -525,9 +525,12 @@ kv_status kv_paged_decode_attn_tiered(const kv_shape* shape, const void* q, cons
 
 size_t kv_tiered_split_workspace_size(const kv_shape* shape, int32_t sel_stride) {
   if (!shape || check_shape(shape) != KV_OK || sel_stride < 0) return 0;
-  const size_t stride = sel_stride > 0 ? (size_t)sel_stride : (size_t)shape->max_blocks_per_seq;
+  const int stride = sel_stride > 0 ? sel_stride : shape->max_blocks_per_seq;
   const size_t rows = (size_t)shape->num_seqs * shape->num_kv_heads;
-  return 2 * rows * (stride + 1) * sizeof(int32_t);
+  const size_t chunks = (size_t)kvd::tier_chunks(stride);
+  // hot and cold lists and counts, then the tier flags and per-chunk counts
+  return rows * ((2 * (size_t)stride + 2 + chunks) * sizeof(int32_t) +
+                 chunks * kvd::kTierChunkPositions);
 }
 
 kv_status kv_paged_decode_attn_tiered_split(
@@ -572,13 +575,15 @@ kv_status kv_paged_decode_attn_tiered_split(
   int32_t* cold = hot + rows * stride;
   int32_t* hot_n = cold + rows * stride;
   int32_t* cold_n = hot_n + rows;
+  int32_t* chunk_cold = cold_n + rows;
+  uint8_t* flags = reinterpret_cast<uint8_t*>(chunk_cold + rows * kvd::tier_chunks(stride));
   hipStream_t s = (hipStream_t)stream;
   const int G = shape->num_q_heads / shape->num_kv_heads;
   const int S = num_splits_hot + num_splits_cold;
   hipError_t e = kvd::launch_tier_lists(sel_blocks, sel_count, sel_stride, block_table, seq_lens,
                                         page_tier, shape->num_seqs, shape->num_kv_heads,
                                         shape->max_blocks_per_seq, stride, hot, hot_n, cold,
-                                        cold_n, s);
+                                        cold_n, flags, chunk_cold, s);
   if (e == hipSuccess)     // hot pages: columns [0, num_splits_hot) of the partials
     e = kvd::launch_paged_attn(shape->dtype, shape->head_dim, G, 0, q, k_cache, v_cache, nullptr,
                                block_table, seq_lens, hot, hot_n, stride, nullptr, 0,

@@ -1141,72 +1141,117 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
 
 // ============================================================== tier lists
 //
-// One 1024-thread workgroup per (sequence, KV head).  Each thread takes EPT
-// consecutive list positions of a tile, looks up their pages' tiers, and one
-// block-wide exclusive scan of its (hot, cold) counts places every entry in
-// its list, order kept.  Tiles of 1024 * EPT positions follow one another.
-constexpr int kTierThreads = 1024;
-constexpr int kTierEPT = 8;
+// Two passes over chunks of kTierChunk list positions, so that a long list is
+// spread over many compute units (its page-tier lookups are scattered byte
+// loads).  tier_flags_kernel: per chunk, each position's tier as a byte, and
+// the chunk's cold count.  tier_write_kernel: per chunk, the hot / cold
+// entries before it from the counts of the chunks before, then one block
+// scan places the chunk's entries in the hot and the cold list, order kept;
+// the chunk holding the list's last entry writes the two counts.
+constexpr int kTierThreads = 256;
+constexpr int kTierEPT = 4;
+constexpr int kTierChunk = kTierThreads * kTierEPT;
+static_assert(kTierChunk == kTierChunkPositions, "the launcher sizes chunks by this");
 
-__global__ __launch_bounds__(kTierThreads) void tier_lists_kernel(
+__global__ __launch_bounds__(kTierThreads) void tier_flags_kernel(
     const int32_t* __restrict__ sel, const int32_t* __restrict__ sel_count, int sel_stride,
     const int32_t* __restrict__ block_table, const int32_t* __restrict__ seq_lens,
-    const uint8_t* __restrict__ page_tier, int Hkv, int maxN, int out_stride,
+    const uint8_t* __restrict__ page_tier, int Hkv, int maxN, int out_stride, int n_chunks,
+    uint8_t* __restrict__ flags, int32_t* __restrict__ chunk_cold) {
+  __shared__ uint32_t wsum[kTierThreads / kWave];
+  const int c = blockIdx.x, j = blockIdx.y, b = blockIdx.z;
+  const size_t u = (size_t)b * Hkv + j;
+  const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid >> 6;
+  const int n = sel ? sel_count[u] : (seq_lens[b] + kBlockSize - 1) / kBlockSize;
+  const int c0 = c * kTierChunk;
+  if (c0 >= n) return;                             // workgroup-uniform
+  const int32_t* list = sel ? sel + u * sel_stride : nullptr;
+  const int32_t* bt = block_table + (size_t)b * maxN;
+  uint32_t nc = 0;
+  uint32_t f = 0;
+#pragma unroll
+  for (int r = 0; r < kTierEPT; ++r) {
+    const int pos = c0 + tid * kTierEPT + r;
+    if (pos < n) {
+      const int blk = list ? list[pos] : pos;
+      const uint32_t t = page_tier[bt[blk]] != 0 ? 1u : 0u;
+      f |= t << (8 * r);
+      nc += t;
+    }
+  }
+  // the thread's 4 flags as one word (positions past n stay 0 and are never read)
+  *reinterpret_cast<uint32_t*>(flags + u * (size_t)n_chunks * kTierChunk + c0 + tid * kTierEPT) = f;
+  nc = wave_reduce_u32(nc, AddU32());
+  if (lane == 0) wsum[wave] = nc;
+  __syncthreads();
+  if (tid == 0) {
+    uint32_t t = 0;
+#pragma unroll
+    for (int w = 0; w < kTierThreads / kWave; ++w) t += wsum[w];
+    chunk_cold[u * n_chunks + c] = (int32_t)t;
+  }
+}
+
+__global__ __launch_bounds__(kTierThreads) void tier_write_kernel(
+    const int32_t* __restrict__ sel, const int32_t* __restrict__ sel_count, int sel_stride,
+    const int32_t* __restrict__ seq_lens, int Hkv, int out_stride, int n_chunks,
+    const uint8_t* __restrict__ flags, const int32_t* __restrict__ chunk_cold,
     int32_t* __restrict__ hot, int32_t* __restrict__ hot_count, int32_t* __restrict__ cold,
     int32_t* __restrict__ cold_count) {
   __shared__ uint32_t wsum[kTierThreads / kWave];
-  const int j = blockIdx.x, b = blockIdx.y;
+  const int c = blockIdx.x, j = blockIdx.y, b = blockIdx.z;
   const size_t u = (size_t)b * Hkv + j;
   const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid >> 6;
-  const int nb = (seq_lens[b] + kBlockSize - 1) / kBlockSize;
-  const int n = sel ? sel_count[u] : nb;
+  const int n = sel ? sel_count[u] : (seq_lens[b] + kBlockSize - 1) / kBlockSize;
+  const int c0 = c * kTierChunk;
+  const int last = n > 0 ? (n - 1) / kTierChunk : 0;
+  if (c > last) return;                            // workgroup-uniform
+  // cold entries before this chunk (every chunk before it is full)
+  uint32_t cold_before = 0;
+  for (int k = lane; k < c; k += kWave) cold_before += (uint32_t)chunk_cold[u * n_chunks + k];
+  cold_before = wave_reduce_u32(cold_before, AddU32());
+  const uint32_t hot_before = (uint32_t)c0 - cold_before;
   const int32_t* list = sel ? sel + u * sel_stride : nullptr;
-  const int32_t* bt = block_table + (size_t)b * maxN;
+  uint32_t f = 0;
+  int valid = 0;
+  int blk[kTierEPT];
+  if (c0 < n) {
+    f = *reinterpret_cast<const uint32_t*>(flags + u * (size_t)n_chunks * kTierChunk + c0 +
+                                           tid * kTierEPT);
+    valid = min(kTierEPT, max(0, n - (c0 + tid * kTierEPT)));
+  }
+#pragma unroll
+  for (int r = 0; r < kTierEPT; ++r) {
+    const int pos = c0 + tid * kTierEPT + r;
+    blk[r] = r < valid ? (list ? list[pos] : pos) : -1;
+  }
+  uint32_t nc = 0;
+#pragma unroll
+  for (int r = 0; r < kTierEPT; ++r) nc += r < valid ? ((f >> (8 * r)) & 1u) : 0u;
+  const uint32_t packed = (((uint32_t)valid - nc) << 16) | nc;   // (hot, cold) in 16 bits each
+  const uint32_t incl = wave_scan_add_u32(packed);
+  if (lane == kWave - 1) wsum[wave] = incl;
+  __syncthreads();
+  uint32_t before = 0, total = 0;
+#pragma unroll
+  for (int w = 0; w < kTierThreads / kWave; ++w) {
+    if (w < wave) before += wsum[w];
+    total += wsum[w];
+  }
+  const uint32_t ex = before + incl - packed;
+  uint32_t h = hot_before + (ex >> 16), cl = cold_before + (ex & 0xFFFFu);
   int32_t* hot_row = hot + u * out_stride;
   int32_t* cold_row = cold + u * out_stride;
-  uint32_t hot_base = 0, cold_base = 0;
-  for (int t0 = 0; t0 < n; t0 += kTierThreads * kTierEPT) {
-    int blk[kTierEPT];
-    uint32_t is_cold = 0;
 #pragma unroll
-    for (int r = 0; r < kTierEPT; ++r) {
-      const int pos = t0 + tid * kTierEPT + r;
-      blk[r] = -1;
-      if (pos < n) {
-        blk[r] = list ? list[pos] : pos;
-        if (page_tier[bt[blk[r]]] != 0) is_cold |= 1u << r;
-      }
+  for (int r = 0; r < kTierEPT; ++r) {
+    if (r < valid) {
+      if ((f >> (8 * r)) & 1u) cold_row[cl++] = blk[r];
+      else hot_row[h++] = blk[r];
     }
-    int valid = min(kTierEPT, max(0, n - (t0 + tid * kTierEPT)));
-    const uint32_t nc = (uint32_t)__popc(is_cold);
-    const uint32_t nh = (uint32_t)valid - nc;
-    // packed (hot << 16 | cold) counts: a tile holds at most 8192 of each
-    const uint32_t packed = (nh << 16) | nc;
-    const uint32_t incl = wave_scan_add_u32(packed);
-    if (lane == kWave - 1) wsum[wave] = incl;
-    __syncthreads();
-    uint32_t before = 0, total = 0;
-#pragma unroll
-    for (int w = 0; w < kTierThreads / kWave; ++w) {
-      if (w < wave) before += wsum[w];
-      total += wsum[w];
-    }
-    __syncthreads();                               // wsum is rewritten by the next tile
-    const uint32_t ex = before + incl - packed;
-    uint32_t h = hot_base + (ex >> 16), c = cold_base + (ex & 0xFFFFu);
-#pragma unroll
-    for (int r = 0; r < kTierEPT; ++r) {
-      if (r < valid) {
-        if ((is_cold >> r) & 1u) cold_row[c++] = blk[r];
-        else hot_row[h++] = blk[r];
-      }
-    }
-    hot_base += total >> 16;
-    cold_base += total & 0xFFFFu;
   }
-  if (tid == 0) {
-    hot_count[u] = (int)hot_base;
-    cold_count[u] = (int)cold_base;
+  if (c == last && tid == 0) {
+    hot_count[u] = (int)(hot_before + (total >> 16));
+    cold_count[u] = (int)(cold_before + (total & 0xFFFFu));
   }
 }
 
@@ -1292,10 +1337,17 @@ hipError_t launch_tier_lists(const int32_t* sel, const int32_t* sel_count, int s
                              const int32_t* block_table, const int32_t* seq_lens,
                              const uint8_t* page_tier, int B, int Hkv, int maxN, int out_stride,
                              int32_t* hot, int32_t* hot_count, int32_t* cold, int32_t* cold_count,
-                             hipStream_t stream) {
-  hipLaunchKernelGGL(tier_lists_kernel, dim3(Hkv, B), dim3(kTierThreads), 0, stream, sel,
-                     sel_count, sel_stride, block_table, seq_lens, page_tier, Hkv, maxN,
-                     out_stride, hot, hot_count, cold, cold_count);
+                             uint8_t* flags, int32_t* chunk_cold, hipStream_t stream) {
+  const int n_chunks = tier_chunks(out_stride);
+  const dim3 grid(n_chunks, Hkv, B);
+  hipLaunchKernelGGL(tier_flags_kernel, grid, dim3(kTierThreads), 0, stream, sel, sel_count,
+                     sel_stride, block_table, seq_lens, page_tier, Hkv, maxN, out_stride,
+                     n_chunks, flags, chunk_cold);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(tier_write_kernel, grid, dim3(kTierThreads), 0, stream, sel, sel_count,
+                     sel_stride, seq_lens, Hkv, out_stride, n_chunks, flags, chunk_cold, hot,
+                     hot_count, cold, cold_count);
   return hipGetLastError();
 }
 

@@ -274,6 +274,16 @@ __device__ inline uint32_t wave_scan_add_u32(uint32_t v) {
   return v;
 }
 
+struct MinU32 {
+  __device__ uint32_t operator()(uint32_t a, uint32_t b) const { return min(a, b); }
+};
+struct MaxU32 {
+  __device__ uint32_t operator()(uint32_t a, uint32_t b) const { return max(a, b); }
+};
+struct AddU32 {
+  __device__ uint32_t operator()(uint32_t a, uint32_t b) const { return a + b; }
+};
+
 // all-reduce over the wave: inside each 16-lane row with DPP, then the four
 // row results read as scalars (the result is wave-uniform)
 template <typename Op>

@@ -442,15 +442,6 @@ __device__ inline uint32_t score_key(float f) {
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
-struct MinU32 {
-  __device__ uint32_t operator()(uint32_t a, uint32_t b) const { return min(a, b); }
-};
-struct MaxU32 {
-  __device__ uint32_t operator()(uint32_t a, uint32_t b) const { return max(a, b); }
-};
-struct AddU32 {
-  __device__ uint32_t operator()(uint32_t a, uint32_t b) const { return a + b; }
-};
 __device__ inline uint32_t wave_inclusive_scan(uint32_t v) { return wave_scan_add_u32(v); }
 
 template <int NWAVES>

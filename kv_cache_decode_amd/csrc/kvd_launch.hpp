@@ -73,12 +73,18 @@ hipError_t launch_paged_attn(int dtype, int D, int G, int kvq, const void* q,
 
 // Per (sequence, KV head): the list (sel, or every block of the sequence when
 // sel is null) split by page tier into the hot (tier 0) and cold lists, both
-// in list order, rows of out_stride entries.
+// in list order, rows of out_stride entries.  Scratch: flags (B * Hkv rows of
+// out_stride bytes, rounded up to whole chunks) and chunk_cold (B * Hkv rows
+// of tier_chunks(out_stride) ints).
+constexpr int kTierChunkPositions = 1024;
+inline int tier_chunks(int out_stride) {
+  return (out_stride + kTierChunkPositions - 1) / kTierChunkPositions;
+}
 hipError_t launch_tier_lists(const int32_t* sel, const int32_t* sel_count, int sel_stride,
                              const int32_t* block_table, const int32_t* seq_lens,
                              const uint8_t* page_tier, int B, int Hkv, int maxN, int out_stride,
                              int32_t* hot, int32_t* hot_count, int32_t* cold, int32_t* cold_count,
-                             hipStream_t stream);
+                             uint8_t* flags, int32_t* chunk_cold, hipStream_t stream);
 
 hipError_t launch_cache_plan(const int32_t* sel, const int32_t* sel_count, int sel_stride, int B,
                              int Hkv, int maxN, int C, int32_t* slot_block, int32_t* block_slot,

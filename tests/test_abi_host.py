@@ -486,8 +486,9 @@ def test_tiered_split_argument_checks():
     s = shape()
     f = kd.kv_paged_decode_attn_tiered_split
     need = kd.kv_tiered_split_workspace_size(s, 0)
-    assert need == 2 * 2 * 2 * (4 + 1) * 4          # two lists of (maxN + 1) ints per (b, j)
-    assert kd.kv_tiered_split_workspace_size(s, 3) == 2 * 2 * 2 * (3 + 1) * 4
+    # per (b, j): two lists of maxN ints, two counts, one chunk count, 1024 flag bytes
+    assert need == 2 * 2 * ((2 * 4 + 2 + 1) * 4 + 1024)
+    assert kd.kv_tiered_split_workspace_size(s, 3) == 2 * 2 * ((2 * 3 + 2 + 1) * 4 + 1024)
     assert kd.kv_tiered_split_workspace_size(s, -1) == 0
 
     def call(sh=s, **kw):
