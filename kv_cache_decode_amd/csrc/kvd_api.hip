@@ -112,17 +112,12 @@ kv_status check_code_format(const kv_shape* shape, int32_t code_format) {
 
 // Validation and launch shared by the 16-bit/fp32 pools (kvq 0) and the code
 // pools (kvq 8: E4M3, kvq 4: INT4; kv_scales != nullptr).
-kv_status attn_common(const kv_shape* shape, int kvq, const void* q, const void* k_cache,
-                      const void* v_cache, const float* kv_scales, const int32_t* block_table,
-                      const int32_t* seq_lens, const int32_t* sel_blocks,
-                      const int32_t* sel_count, int32_t sel_stride, float scale,
-                      int32_t num_splits, float* part_o, float* part_m, float* part_l,
-                      void* stream, int cold = 0, const void* k_cold = nullptr,
-                      const void* v_cold = nullptr, const uint8_t* page_tier = nullptr) {
-  kv_status st = check_shape(shape);
-  if (st != KV_OK) return st;
-  if (num_splits < 1 || num_splits > 65535 * 4)
-    return fail(KV_ERR_INVALID_ARG, "num_splits=%d must be in [1, 262140]", num_splits);
+// Pointer, list and scale checks shared by the attention entry points.
+kv_status check_attn_args(const void* q, const void* k_cache, const void* v_cache,
+                          const int32_t* block_table, const int32_t* seq_lens,
+                          const int32_t* sel_blocks, const int32_t* sel_count, int32_t sel_stride,
+                          float scale, const float* part_o, const float* part_m,
+                          const float* part_l) {
   if (!q || !k_cache || !v_cache || !block_table || !seq_lens || !part_o || !part_m || !part_l)
     return fail(KV_ERR_INVALID_ARG, "q, k_cache, v_cache, block_table, seq_lens and partials are required");
   if ((sel_blocks == nullptr) != (sel_count == nullptr))
@@ -136,6 +131,23 @@ kv_status attn_common(const kv_shape* shape, int kvq, const void* q, const void*
   if (!aligned(block_table, 4) || !aligned(seq_lens, 4) || !aligned(part_m, 4) ||
       !aligned(part_l, 4) || (sel_blocks && (!aligned(sel_blocks, 4) || !aligned(sel_count, 4))))
     return fail(KV_ERR_ALIGNMENT, "integer and partial arrays must be 4-byte aligned");
+  return KV_OK;
+}
+
+kv_status attn_common(const kv_shape* shape, int kvq, const void* q, const void* k_cache,
+                      const void* v_cache, const float* kv_scales, const int32_t* block_table,
+                      const int32_t* seq_lens, const int32_t* sel_blocks,
+                      const int32_t* sel_count, int32_t sel_stride, float scale,
+                      int32_t num_splits, float* part_o, float* part_m, float* part_l,
+                      void* stream, int cold = 0, const void* k_cold = nullptr,
+                      const void* v_cold = nullptr, const uint8_t* page_tier = nullptr) {
+  kv_status st = check_shape(shape);
+  if (st != KV_OK) return st;
+  if (num_splits < 1 || num_splits > 65535 * 4)
+    return fail(KV_ERR_INVALID_ARG, "num_splits=%d must be in [1, 262140]", num_splits);
+  if ((st = check_attn_args(q, k_cache, v_cache, block_table, seq_lens, sel_blocks, sel_count,
+                            sel_stride, scale, part_o, part_m, part_l)) != KV_OK)
+    return st;
   const int G = shape->num_q_heads / shape->num_kv_heads;
   return hip_status(
       kvd::launch_paged_attn(shape->dtype, shape->head_dim, G, kvq, q, k_cache, v_cache,
@@ -551,23 +563,13 @@ kv_status kv_paged_decode_attn_tiered_split(
     return fail(KV_ERR_INVALID_ARG, "k_cold, v_cold, kv_scales and page_tier are required");
   if (!aligned(k_cold, 16) || !aligned(v_cold, 16) || !aligned(kv_scales, 8))
     return fail(KV_ERR_ALIGNMENT, "the cold pools must be 16-byte aligned, kv_scales 8-byte");
-  if ((sel_blocks == nullptr) != (sel_count == nullptr))
-    return fail(KV_ERR_INVALID_ARG, "sel_blocks and sel_count go together");
-  if (sel_blocks && sel_stride < 1)
-    return fail(KV_ERR_INVALID_ARG, "sel_stride=%d must be >= 1", sel_stride);
+  if ((st = check_attn_args(q, k_cache, v_cache, block_table, seq_lens, sel_blocks, sel_count,
+                            sel_stride, scale, part_o, part_m, part_l)) != KV_OK)
+    return st;
   const size_t need = kv_tiered_split_workspace_size(shape, sel_blocks ? sel_stride : 0);
   if (!workspace || workspace_bytes < need)
     return fail(KV_ERR_WORKSPACE, "the workspace needs %zu bytes", need);
   if (!aligned(workspace, 4)) return fail(KV_ERR_ALIGNMENT, "the workspace must be 4-byte aligned");
-  if (!q || !k_cache || !v_cache || !block_table || !seq_lens || !part_o || !part_m || !part_l)
-    return fail(KV_ERR_INVALID_ARG, "q, k_cache, v_cache, block_table, seq_lens and partials are required");
-  if (!(scale > 0.0f) || !(scale < INFINITY))
-    return fail(KV_ERR_INVALID_ARG, "scale must be finite and positive");
-  if (!aligned(q, 16) || !aligned(k_cache, 16) || !aligned(v_cache, 16) || !aligned(part_o, 16))
-    return fail(KV_ERR_ALIGNMENT, "q, k_cache, v_cache and part_o must be 16-byte aligned");
-  if (!aligned(block_table, 4) || !aligned(seq_lens, 4) || !aligned(part_m, 4) ||
-      !aligned(part_l, 4) || (sel_blocks && (!aligned(sel_blocks, 4) || !aligned(sel_count, 4))))
-    return fail(KV_ERR_ALIGNMENT, "integer and partial arrays must be 4-byte aligned");
   const int stride = sel_blocks ? sel_stride : shape->max_blocks_per_seq;
   const size_t rows = (size_t)shape->num_seqs * shape->num_kv_heads;
   int32_t* ws = static_cast<int32_t*>(workspace);
