@@ -127,6 +127,30 @@ __device__ inline const uint32_t* fetched_slot_bits(const FetchArgs& fa, int b, 
   return bits;
 }
 
+// The first 64 entries of split s's share of a selected list (and their cache
+// slots), loaded before the list's count arrives, on the guess that the list
+// fills its row of sel_stride entries (a Top-K selection of a long sequence
+// does).  The split's chunk is ceil(count / S); the preloaded entries stand in
+// for its first loads only when the guessed chunk ceil(sel_stride / S) equals
+// it, so the split covers the same positions either way.  Loads stay inside
+// the row.
+struct ListHead {
+  int n = 0, slot = 0, chunk = -1;
+};
+
+__device__ inline ListHead list_head(const int32_t* __restrict__ sel,
+                                     const int32_t* __restrict__ sel_slots, size_t row,
+                                     int sel_stride, int S, int s, int lane) {
+  ListHead h;
+  h.chunk = (sel_stride + S - 1) / S;
+  const int pos = s * h.chunk + lane;
+  if (lane < h.chunk && pos < sel_stride) {
+    h.n = sel[row * sel_stride + pos];
+    if (sel_slots) h.slot = sel_slots[row * sel_stride + pos];
+  }
+  return h;
+}
+
 template <typename DT, int D, int G, int WAVES, bool SPARSE, int KVQ, bool FETCH = false>
 __global__ __launch_bounds__(WAVES * kWave) void paged_attn_kernel(
     const void* __restrict__ q, const void* __restrict__ k_cache, const void* __restrict__ v_cache,
@@ -152,8 +176,11 @@ __global__ __launch_bounds__(WAVES * kWave) void paged_attn_kernel(
 
   const int L = seq_lens[b];
   const int nb = (L + kBlockSize - 1) / kBlockSize;
+  const ListHead pre = SPARSE ? list_head(sel, sel_slots, (size_t)b * Hkv + j, sel_stride, S, s, lane)
+                             : ListHead{};
   const int n_list = SPARSE ? sel_count[(size_t)b * Hkv + j] : nb;
   const int chunk = (n_list + S - 1) / S;
+  const bool pre_ok = SPARSE && pre.chunk == chunk;
   const int p0 = min(s * chunk, n_list);
   const int p1 = min(p0 + chunk, n_list);
   const size_t row0 = (size_t)b * Hq + (size_t)j * G;
@@ -194,9 +221,10 @@ __global__ __launch_bounds__(WAVES * kWave) void paged_attn_kernel(
     int my_page = 0, my_valid = 0, my_pool = -1;
     float my_sk = 1.0f, my_sv = 1.0f;
     if (lane < cnt) {
-      const int n = SPARSE ? sel_row[base + lane] : base + lane;
+      const bool use_pre = pre_ok && base == p0;
+      const int n = SPARSE ? (use_pre ? pre.n : sel_row[base + lane]) : base + lane;
       // cached list: the block sits in slot sel_slots[.] of cache page b*C + slot
-      const int slot = slots_row ? slots_row[base + lane] : 0;
+      const int slot = slots_row ? (use_pre ? pre.slot : slots_row[base + lane]) : 0;
       my_page = slots_row ? b * num_slots + slot : bt_row[n];
       if constexpr (FETCH) {   // fetched this step: read from the pool page
         if ((fetched[slot >> 5] >> (slot & 31)) & 1u) my_pool = bt_row[n];
@@ -618,8 +646,11 @@ __global__ __launch_bounds__(WAVES * kWave) KVD_MFMA_OCCUPANCY_T(COLD) void page
 
   const int L = seq_lens[b];
   const int nb = (L + kBlockSize - 1) / kBlockSize;
+  const ListHead pre = SPARSE ? list_head(sel, sel_slots, (size_t)b * Hkv + j, sel_stride, S, s, lane)
+                             : ListHead{};
   const int n_list = SPARSE ? sel_count[(size_t)b * Hkv + j] : nb;
   const int chunk = (n_list + S - 1) / S;
+  const bool pre_ok = SPARSE && pre.chunk == chunk;
   const int p0 = min(s * chunk, n_list);
   const int p1 = min(p0 + chunk, n_list);
   const size_t row0 = (size_t)b * Hq + (size_t)j * G;
@@ -703,9 +734,10 @@ __global__ __launch_bounds__(WAVES * kWave) KVD_MFMA_OCCUPANCY_T(COLD) void page
     int my_page = 0, my_valid = 0, my_tier = 0, my_pool = -1;
     float my_sk = 1.0f, my_sv = 1.0f;
     if (lane < cnt) {
-      const int n = SPARSE ? sel_row[base + lane] : base + lane;
+      const bool use_pre = pre_ok && base == p0;
+      const int n = SPARSE ? (use_pre ? pre.n : sel_row[base + lane]) : base + lane;
       // cached list: the block sits in slot sel_slots[.] of cache page b*C + slot
-      const int slot = slots_row ? slots_row[base + lane] : 0;
+      const int slot = slots_row ? (use_pre ? pre.slot : slots_row[base + lane]) : 0;
       my_page = slots_row ? b * num_slots + slot : bt_row[n];
       if constexpr (FETCH) {   // fetched this step: read from the pool page
         if ((fetched[slot >> 5] >> (slot & 31)) & 1u) my_pool = bt_row[n];
