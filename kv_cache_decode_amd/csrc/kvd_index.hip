@@ -354,9 +354,17 @@ __global__ __launch_bounds__(WAVES * kWave) void block_score_kernel(
   const int wg = APPEND ? (int)blockIdx.x - 1 : (int)blockIdx.x;
   const int n0 = (wg * WAVES + (threadIdx.x >> 6)) * (STEPS * TPI);
   if (n0 >= maxN) return;
+  // the wave's block-table entries are read beside the sequence length (every
+  // entry of the row is readable), so the index loads wait for one round trip
+  const int32_t* bt_row = block_table + (size_t)b * maxN;
+  int32_t pg[STEPS];
+#pragma unroll
+  for (int st = 0; st < STEPS; ++st) {
+    const int n = n0 + st * TPI + rg;
+    pg[st] = n < maxN ? bt_row[n] : 0;
+  }
   const int nb = (seq_lens[b] + kBlockSize - 1) / kBlockSize;
 
-  const int32_t* bt_row = block_table + (size_t)b * maxN;
   // 16-byte index loads per block and lane: the min and max chunks, or the
   // E floats of the mean chunk
   constexpr int NL = (IDX == kIndexMinMax) ? 2 : E / 4;
@@ -365,7 +373,7 @@ __global__ __launch_bounds__(WAVES * kWave) void block_score_kernel(
   for (int st = 0; st < STEPS; ++st) {
     const int n = n0 + st * TPI + rg;
     if (n < nb) {
-      const size_t p = (size_t)bt_row[n];
+      const size_t p = (size_t)pg[st];
       if constexpr (IDX == kIndexMinMax) {
         const St* src = static_cast<const St*>(kmeta) + (p * Hkv + j) * 2 * D + c * E;
         w[st][0] = load16(src);
@@ -488,17 +496,8 @@ __device__ inline void topk_row(const float* __restrict__ row, int maxN, int L, 
   auto& buf_g = sm.buf_g;
   auto& state = sm.state;
   const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid >> 6;
-  const int nb = (L + kBlockSize - 1) / kBlockSize;
-  const int keff = min(K, nb);
-  const int local_from = local > 0 ? L - local : 0x7fffffff;  // first forced local token
-  if (tid == 0) *count_out = max(keff, 0);
-  for (int i = max(keff, 0) + tid; i < K; i += NT) out[i] = -1;
-  if (keff <= 0) return;  // workgroup-uniform
-
-  uint32_t key[EPT];
-  uint32_t kmn = 0xFFFFFFFFu, kmx = 0u;
-  // the same over the keys of scores >= +0 (top bit set) and below it
-  uint32_t kmn_pos = 0xFFFFFFFFu, kmx_neg = 0u, npos = 0u;
+  // the scores are read first: the row is readable up to maxN whatever the
+  // length, so the loads need not wait for it
   float sc[EPT];
   const int n0 = tid * EPT;
   if constexpr (EPT % 4 == 0) {
@@ -517,6 +516,17 @@ __device__ inline void topk_row(const float* __restrict__ row, int maxN, int L, 
 #pragma unroll
     for (int r = 0; r < EPT; ++r) sc[r] = (n0 + r < maxN) ? row[n0 + r] : 0.0f;
   }
+  const int nb = (L + kBlockSize - 1) / kBlockSize;
+  const int keff = min(K, nb);
+  const int local_from = local > 0 ? L - local : 0x7fffffff;  // first forced local token
+  if (tid == 0) *count_out = max(keff, 0);
+  for (int i = max(keff, 0) + tid; i < K; i += NT) out[i] = -1;
+  if (keff <= 0) return;  // workgroup-uniform
+
+  uint32_t key[EPT];
+  uint32_t kmn = 0xFFFFFFFFu, kmx = 0u;
+  // the same over the keys of scores >= +0 (top bit set) and below it
+  uint32_t kmn_pos = 0xFFFFFFFFu, kmx_neg = 0u, npos = 0u;
   static_assert(EPT <= 32, "forced mask holds 32 blocks");
   uint32_t fmask = 0u;
 #pragma unroll
