@@ -155,6 +155,38 @@ def measured_traffic():
 
 # ---------------------------------------------------------------- GPU part
 
+def graph_step_us(fn, copies, args):
+    """Time per step of fn, replayed from one HIP graph that holds GRAPH_STEPS
+    steps cycling over the workload copies (one host launch per GRAPH_STEPS
+    steps, so a short step is not timed at the host's graph launch rate): the
+    median over at least GRAPH_MIN_REPLAYS replays, each bracketed by its own
+    events.  Raises RuntimeError where a call cannot be captured."""
+    import torch
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        for c in copies:
+            fn(c)
+    torch.cuda.current_stream().wait_stream(side)
+    g_ = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g_):
+        for i in range(GRAPH_STEPS):
+            fn(copies[i % len(copies)])
+    reps = max(GRAPH_MIN_REPLAYS, args.steps // GRAPH_STEPS)
+    for _ in range(max(GRAPH_WARM_REPLAYS, args.warmup // GRAPH_STEPS)):
+        g_.replay()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(reps)]
+    torch.cuda.synchronize()
+    for a, b in ev:
+        a.record()
+        g_.replay()
+        b.record()
+    torch.cuda.synchronize()
+    del g_
+    return float(np.median([a.elapsed_time(b) for a, b in ev])) * 1e3 / GRAPH_STEPS
+
+
 def run_gpu(args, spec, data):
     import torch
     from kv_cache_decode_amd.step import DeviceWorkload
@@ -200,35 +232,8 @@ def run_gpu(args, spec, data):
         return t0.elapsed_time(t1), time.perf_counter() - wall0
 
     def graph_us(fn):
-        """Time per step of fn, replayed from one HIP graph that holds
-        GRAPH_STEPS steps cycling over the workload copies (one host launch per
-        GRAPH_STEPS steps, so a short step is not timed at the host's graph
-        launch rate): the median over at least GRAPH_MIN_REPLAYS replays, each
-        bracketed by its own events."""
         try:
-            side = torch.cuda.Stream()
-            side.wait_stream(torch.cuda.current_stream())
-            with torch.cuda.stream(side):
-                for c in copies:
-                    fn(c)
-            torch.cuda.current_stream().wait_stream(side)
-            g_ = torch.cuda.CUDAGraph()
-            with torch.cuda.graph(g_):
-                for i in range(GRAPH_STEPS):
-                    fn(copies[i % len(copies)])
-            reps = max(GRAPH_MIN_REPLAYS, args.steps // GRAPH_STEPS)
-            for _ in range(max(GRAPH_WARM_REPLAYS, args.warmup // GRAPH_STEPS)):
-                g_.replay()
-            ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-                  for _ in range(reps)]
-            torch.cuda.synchronize()
-            for a, b in ev:
-                a.record()
-                g_.replay()
-                b.record()
-            torch.cuda.synchronize()
-            del g_
-            return float(np.median([a.elapsed_time(b) for a, b in ev])) * 1e3 / GRAPH_STEPS
+            return graph_step_us(fn, copies, args)
         except RuntimeError:
             ms_, _ = time_loop(lambda i: fn(copies[i % len(copies)]))
             return ms_ * 1e3 / args.steps
@@ -480,8 +485,9 @@ def time_variants(args, copies, k, s_sparse, time_loop, graph_us):
 
 
 def run_other_workload(args, name):
-    """Kernel-level figures of another named workload (back-to-back launches
-    over rotated copies): dense attention GB/s, and the sparse decode path."""
+    """Kernel-level figures of another named workload (steps replayed from HIP
+    graphs over rotated copies): dense attention GB/s, and the sparse decode
+    path."""
     import torch
     from kv_cache_decode_amd import kvdecode as kd
     from kv_cache_decode_amd import workload as wl
@@ -493,16 +499,19 @@ def run_other_workload(args, name):
     reps = max(20, args.steps // 2)
 
     def loop(fn):
-        for i in range(4):
-            fn(copies[i % len(copies)])
-        torch.cuda.synchronize()
-        t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        t0.record()
-        for i in range(reps):
-            fn(copies[i % len(copies)])
-        t1.record()
-        torch.cuda.synchronize()
-        return t0.elapsed_time(t1) * 1e3 / reps
+        try:
+            return graph_step_us(fn, copies, args)
+        except RuntimeError:       # eager back-to-back launches
+            for i in range(4):
+                fn(copies[i % len(copies)])
+            torch.cuda.synchronize()
+            t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            t0.record()
+            for i in range(reps):
+                fn(copies[i % len(copies)])
+            t1.record()
+            torch.cuda.synchronize()
+            return t0.elapsed_time(t1) * 1e3 / reps
 
     s_dense = kd.kv_auto_num_splits(copies[0].shape, spec.max_blocks)
     dense_us = loop(lambda c: c.attention(sparse=False, num_splits=s_dense))

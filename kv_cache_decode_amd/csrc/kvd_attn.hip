@@ -1171,6 +1171,59 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
   }
 }
 
+// Few splits (S <= kCombineFew): one thread per (row, float4 of channels)
+// walks all S splits, issuing every load before the first reduction; a row's
+// D/4 threads read the same m and l.  The sums run in split order, each term
+// rounded on its own as in the workgroup kernel's slots.  This keeps the
+// grid at rows * D / 1024 workgroups instead of rows * D / 32, which matters
+// when a single split is the whole list (one fully occupied launch of
+// short-context rows).
+constexpr int kCombineFew = 8;
+
+__global__ __launch_bounds__(256) void combine_few_kernel(const float* __restrict__ part_o,
+                                                          const float* __restrict__ part_m,
+                                                          const float* __restrict__ part_l,
+                                                          int rows, int S, int D,
+                                                          float* __restrict__ out,
+                                                          float* __restrict__ lse) {
+  const int q4n = D / 4;
+  const size_t gid = (size_t)blockIdx.x * 256 + threadIdx.x;
+  if (gid >= (size_t)rows * q4n) return;
+  const size_t row = gid / q4n;
+  const int c = (int)(gid % q4n) * 4;
+  float ms[kCombineFew], ls[kCombineFew];
+  float4 os[kCombineFew];
+  float M = -INFINITY;
+#pragma unroll
+  for (int s = 0; s < kCombineFew; ++s) {
+    ms[s] = -INFINITY;
+    ls[s] = 0.0f;
+    os[s] = make_float4(0.f, 0.f, 0.f, 0.f);
+    if (s < S) {
+      ms[s] = part_m[row * S + s];
+      ls[s] = part_l[row * S + s];
+      os[s] = *reinterpret_cast<const float4*>(part_o + (row * S + s) * D + c);
+    }
+    M = fmaxf(M, ms[s]);
+  }
+  float4 t = make_float4(0.f, 0.f, 0.f, 0.f);
+  float wt = 0.0f;
+#pragma unroll
+  for (int s = 0; s < kCombineFew; ++s) {
+    if (s < S) {
+      const float w = (ms[s] == -INFINITY) ? 0.0f : ls[s] * expf(ms[s] - M);
+      t.x += fmaf(w, os[s].x, 0.0f);
+      t.y += fmaf(w, os[s].y, 0.0f);
+      t.z += fmaf(w, os[s].z, 0.0f);
+      t.w += fmaf(w, os[s].w, 0.0f);
+      wt += w;
+    }
+  }
+  const float inv = 1.0f / wt;
+  *reinterpret_cast<float4*>(out + row * D + c) = make_float4(t.x * inv, t.y * inv, t.z * inv, t.w * inv);
+  if (lse && c == 0) lse[row] = M + logf(wt);
+}
+
 // ============================================================== tier lists
 //
 // Two passes over chunks of kTierChunk list positions, so that a long list is
@@ -1386,6 +1439,12 @@ hipError_t launch_tier_lists(const int32_t* sel, const int32_t* sel_count, int s
 hipError_t launch_combine(int D, const float* part_o, const float* part_m, const float* part_l,
                           int rows, int S, float* out, float* lse, hipStream_t stream) {
   if (D % kCombineChunk) return hipErrorInvalidValue;
+  if (S <= kCombineFew) {
+    const size_t threads = (size_t)rows * (D / 4);
+    hipLaunchKernelGGL(combine_few_kernel, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0,
+                       stream, part_o, part_m, part_l, rows, S, D, out, lse);
+    return hipGetLastError();
+  }
   constexpr int SLOTS = 256 / (kCombineChunk / 4);
   const dim3 grid(rows, D / kCombineChunk);
   auto go = [&](auto r) {
