@@ -280,8 +280,11 @@ int32_t kv_auto_num_splits_tiered(const kv_shape* shape, int32_t blocks_per_unit
  *   z_t = scale * (q . k_t),  m = max z_t,  l = sum exp(z_t - m),
  *   part_o = sum exp(z_t - m) v_t / l,  part_m = m,  part_l = l
  * (fp32 accumulation).  An empty split writes m = -inf, l = 0, o = 0.
- * num_splits >= 1 (see kv_auto_num_splits).  With KV_FLAG_HOST_KV the K/V
- * pointers may be device pointers of kv_host_alloc memory.
+ * num_splits >= 1 (see kv_auto_num_splits).  With num_splits = 1 (and a
+ * non-empty list) part_o, read as [B, Hq, D], already is the attention output
+ * and part_m + ln(part_l) its log-sum-exp, so the merge launch may be skipped.
+ * With KV_FLAG_HOST_KV the K/V pointers may be device pointers of
+ * kv_host_alloc memory.
  */
 kv_status kv_paged_decode_attn(const kv_shape* shape, const void* q, const void* k_cache,
                                const void* v_cache, const int32_t* block_table,

@@ -114,6 +114,28 @@ def test_split_partials_match_oracle_including_empty_splits(gpu, dtype, sparse):
     assert_rows_close(to_f64(dw.out), ref, tol, "combined")
 
 
+@pytest.mark.parametrize("dtype,G", [("f32", 1), ("f16", 1), ("bf16", 4), ("f16", 8)])
+@pytest.mark.parametrize("sparse", [False, True])
+def test_single_split_partials_are_the_output(gpu, dtype, G, sparse):
+    """With one split, part_o is the attention output and m + ln(l) its LSE,
+    so a caller may skip the merge (the header's promise)."""
+    data = mk(3, 2 * G, 2, 128, (200, 17, 1), dtype, seed=91 + G)
+    o = OracleRun(data)
+    dw = run_device(data, device=gpu)
+    sel = cnt = None
+    if sparse:
+        sel, cnt = wl.random_selection(data, 5, seed=3)
+        dw.set_selection(sel, cnt)
+    dw.attention(sparse=sparse, num_splits=1)
+    torch.cuda.synchronize()
+    po, pm, pl = (to_f64(t) for t in dw.partials(1))
+    B, Hq, D = 3, 2 * G, 128
+    ref, ref_lse = o.attention(sel, cnt)
+    tol = ROW_TOL[dtype]
+    assert_rows_close(po.reshape(B, Hq, D), ref, tol, "single-split part_o")
+    np.testing.assert_allclose((pm + np.log(pl)).reshape(B, Hq), ref_lse, rtol=tol, atol=tol)
+
+
 def test_topk_ties_go_to_the_lower_block(gpu):
     """q = 0 makes every score exactly 0: the selection must be blocks 0..K-1."""
     data = mk(2, 4, 2, 128, (300, 77), "bf16", seed=5)
