@@ -26,3 +26,16 @@ def gpu():
         pytest.skip("no GPU in this container")
     import torch
     return torch.device("cuda:0")
+
+
+def pytest_terminal_summary(terminalreporter):
+    """Print the worst errors of the passing parity checks (row relative error,
+    largest absolute error, largest error over its row's max |ref|)."""
+    parity = sys.modules.get("parity")
+    worst = getattr(parity, "WORST", None)
+    if not worst:
+        return
+    terminalreporter.section("worst parity errors against the oracle")
+    for what in sorted(worst):
+        terminalreporter.write_line(
+            f"{what:<60s} " + "  ".join(f"{k} {v:.3e}" for k, v in sorted(worst[what].items())))

@@ -1,8 +1,13 @@
 """Comparison helpers for the GPU-vs-oracle parity tests.
 
 Tolerances:
-* attention outputs, per (sequence, head) row: ||o - ref||_2 / ||ref||_2 <= 1e-5
-  for fp32 inputs and 2e-3 for fp16/bf16 inputs (fp32 accumulation);
+* attention outputs, per (sequence, head) row: ||o - ref||_2 / ||ref||_2 <= tol
+  with tol = 1e-5 for fp32 inputs and 2e-3 for fp16/bf16 inputs (fp32
+  accumulation), and element by element |o_c - ref_c| <= tol * max_c |ref_c|
+  over the same row (one wrong channel cannot hide inside the row norm);
+* log-sum-exp values (the merged lse, a split's m, m + ln l): |got - ref| <= tol
+  in absolute terms, since an lse error e is a relative error e^e - 1 ~ e of
+  the softmax normaliser; a split's l (a normaliser itself): rel-err <= tol;
 * block meta: bit-exact (compared by value, so -0 == +0);
 * scores: |gpu - ref| <= 1e-6 * sum_c |max(q_c kmin_c, q_c kmax_c)| (an fp32 sum
   of D terms is accurate relative to the sum of the terms' magnitudes, not to
@@ -36,17 +41,56 @@ def to_f64(t: torch.Tensor) -> np.ndarray:
     return t.detach().to("cpu").to(torch.float64).numpy()
 
 
+# Worst errors seen by the checks below in this process, printed at the end of a
+# pytest session (conftest.py): check name -> {measure: worst value}.
+WORST: dict = {}
+
+
+def _note(what: str, tol: float, **measures: float):
+    key = f"{what.split(' S=')[0].split(' step')[0]} [tol {tol:.0e}]"
+    cur = WORST.setdefault(key, {})
+    for k, v in measures.items():
+        cur[k] = max(cur.get(k, 0.0), float(v))
+
+
 def assert_rows_close(got: np.ndarray, ref: np.ndarray, tol: float, what: str = "out"):
+    """Row-norm and element-wise bounds (see the module docstring); returns the
+    worst row relative error."""
     got = got.reshape(-1, got.shape[-1])
     ref = ref.reshape(-1, ref.shape[-1])
     assert np.all(np.isfinite(got)), f"{what}: non-finite values"
+    diff = np.abs(got - ref)
     err = np.linalg.norm(got - ref, axis=1)
     nrm = np.linalg.norm(ref, axis=1)
     rel = err / np.maximum(nrm, 1e-300)
     worst = int(np.argmax(rel))
+    rowmax = np.abs(ref).max(axis=1)
+    erel = diff.max(axis=1) / np.maximum(rowmax, 1e-300)
+    ew = int(np.argmax(erel))
+    _note(what, tol, row_rel=rel.max(), max_abs=diff.max(), elem_rel=erel.max())
     assert rel.max() <= tol, (f"{what}: row rel-err {rel.max():.3e} > {tol:.1e} at row {worst} "
-                              f"(max abs err {np.abs(got - ref).max():.3e})")
+                              f"(max abs err {diff.max():.3e})")
+    assert erel.max() <= tol, (f"{what}: element err {diff[ew].max():.3e} > {tol:.1e} * "
+                               f"max|ref| ({rowmax[ew]:.3e}) at row {ew}, channel "
+                               f"{int(np.argmax(diff[ew]))}")
     return float(rel.max())
+
+
+def assert_lse_close(got: np.ndarray, ref: np.ndarray, tol: float, what: str = "lse"):
+    """|got - ref| <= tol: an lse error is a relative error of the normaliser."""
+    got, ref = np.asarray(got, np.float64), np.asarray(ref, np.float64)
+    assert np.all(np.isfinite(got)), f"{what}: non-finite values"
+    d = np.abs(got - ref)
+    _note(what, tol, max_abs=d.max())
+    assert d.max() <= tol, f"{what}: |err| {d.max():.3e} > {tol:.1e} at {np.unravel_index(np.argmax(d), d.shape)}"
+
+
+def assert_rel_close(got: np.ndarray, ref: np.ndarray, tol: float, what: str):
+    """|got - ref| <= tol * |ref| element by element (for positive normalisers)."""
+    got, ref = np.asarray(got, np.float64), np.asarray(ref, np.float64)
+    r = np.abs(got - ref) / np.maximum(np.abs(ref), 1e-300)
+    _note(what, tol, rel=r.max())
+    assert r.max() <= tol, f"{what}: rel-err {r.max():.3e} > {tol:.1e}"
 
 
 def page_lists(data: wl.WorkloadData):

@@ -9,7 +9,7 @@ import pytest
 import torch
 
 from kv_cache_decode_amd import workload as wl
-from parity import (ROW_TOL, OracleRun, assert_rows_close, check_scores,
+from parity import (ROW_TOL, OracleRun, assert_lse_close, assert_rows_close, check_scores,
                     check_selection_valid, check_selection_vs_oracle, to_f64)
 
 pytestmark = pytest.mark.gpu
@@ -34,7 +34,7 @@ def test_named_workload_full_size(gpu, name):
         S = dw.decode(sparse=False)
         ref, ref_lse = o.attention()
         rel = assert_rows_close(to_f64(dw.out), ref, tol, f"{name} dense S={S}")
-        np.testing.assert_allclose(to_f64(dw.lse), ref_lse, rtol=tol, atol=tol)
+        assert_lse_close(to_f64(dw.lse), ref_lse, tol)
         print(f"[{name}] dense ok, S={S}, worst row rel-err {rel:.2e}", flush=True)
         if spec.topk_blocks is None:
             return

@@ -11,7 +11,8 @@ import torch
 
 import oracle
 from kv_cache_decode_amd import workload as wl
-from parity import ROW_TOL, OracleRun, assert_rows_close, page_lists, to_f64
+from parity import (ROW_TOL, OracleRun, assert_lse_close, assert_rows_close, page_lists,
+                    to_f64)
 
 pytestmark = pytest.mark.gpu
 
@@ -94,7 +95,7 @@ def test_fp8_quantize_and_attention_grid(gpu, dtype, D, G, seed):
     for S in (1, 3, 7):
         dw.decode_fp8(sparse=False, num_splits=S)
         assert_rows_close(to_f64(dw.out), ref_dense, tol, f"fp8 dense S={S}")
-        np.testing.assert_allclose(to_f64(dw.lse), ref_lse, rtol=tol, atol=tol)
+        assert_lse_close(to_f64(dw.lse), ref_lse, tol)
     sel, cnt = wl.random_selection(data, 6, seed=seed)
     dw.set_selection(sel, cnt)
     ref_sparse, _ = o.attention(sel, cnt)

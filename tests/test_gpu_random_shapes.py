@@ -16,7 +16,7 @@ import torch
 
 import oracle
 from kv_cache_decode_amd import workload as wl
-from parity import (ROW_TOL, OracleRun, assert_rows_close, check_scores,
+from parity import (ROW_TOL, OracleRun, assert_lse_close, assert_rows_close, check_scores,
                     check_selection_valid_forced, check_selection_vs_oracle, forced_blocks,
                     to_f64)
 
@@ -93,7 +93,7 @@ def test_random_shape(gpu, case):
         ref_dense, ref_lse = o.attention()
         dw.decode(sparse=False, num_splits=S)
         assert_rows_close(to_f64(dw.out), ref_dense, tol, f"dense S={S}")
-        np.testing.assert_allclose(to_f64(dw.lse), ref_lse, rtol=tol, atol=tol)
+        assert_lse_close(to_f64(dw.lse), ref_lse, tol)
         ref_sparse, _ = o.attention(sel, cnt)
         dw.decode(sparse=True, num_splits=S)
         assert_rows_close(to_f64(dw.out), ref_sparse, tol, f"sparse S={S}")

@@ -8,7 +8,8 @@ import torch
 import oracle
 from kv_cache_decode_amd import kvdecode as kd
 from kv_cache_decode_amd import workload as wl
-from parity import ROW_TOL, OracleRun, assert_rows_close, page_lists, to_f64
+from parity import (ROW_TOL, OracleRun, assert_lse_close, assert_rows_close, page_lists,
+                    to_f64)
 
 pytestmark = pytest.mark.gpu
 
@@ -64,7 +65,7 @@ def test_tiered_attention_grid(gpu, dtype, D, G, cold, seed):
     for S in (1, 3, 7):
         dw.decode_tiered(False, cold, tier_dev, num_splits=S)
         assert_rows_close(to_f64(dw.out), ref_dense, tol, f"tiered dense S={S}")
-        np.testing.assert_allclose(to_f64(dw.lse), ref_lse, rtol=tol, atol=tol)
+        assert_lse_close(to_f64(dw.lse), ref_lse, tol)
     sel, cnt = wl.random_selection(data, 6, seed=seed)
     dw.set_selection(sel, cnt)
     ref_sparse, _ = o.attention(sel, cnt)
@@ -157,7 +158,7 @@ def test_tiered_split_launches(gpu, dtype, D, G, cold, seed):
                 S = dw.attention_tiered_split(False, cold, tier_dev, sh, sc)
                 dw.combine(S)
                 assert_rows_close(to_f64(dw.out), ref_dense, tol, f"split dense {sh}+{sc}")
-                np.testing.assert_allclose(to_f64(dw.lse), ref_lse, rtol=tol, atol=tol)
+                assert_lse_close(to_f64(dw.lse), ref_lse, tol)
             dw.set_selection(sel, cnt)
             ref_sparse, _ = o.attention(sel, cnt)
             for sh, sc in ((1, 1), (3, 2)):
