@@ -240,24 +240,37 @@ void oracle_group_scores(const double* head_scores, int B, int Hq, int Hkv, int 
  */
 void oracle_topk(const double* group_scores, const int32_t* seq_lens, int B, int Hkv, int maxN,
                  int bs, int K, int32_t* sel, int32_t* sel_count) {
-#pragma omp parallel for collapse(2) schedule(dynamic)
+  /* rank[b, j, n]: the number of blocks that come before block n; every
+     block's count is independent, so the counts are spread over the threads
+     by block (a 1M-token row alone has 65536 of them) */
+  const i64 rows = (i64)B * Hkv;
+  i64* ranks = (i64*)malloc((size_t)(rows * maxN > 0 ? rows * maxN : 1) * sizeof(i64));
+#pragma omp parallel for schedule(dynamic, 64)
+  for (i64 t = 0; t < rows * maxN; ++t) {
+    const i64 u = t / maxN, n = t % maxN;
+    const i64 nb = ceil_div(seq_lens[u / Hkv], bs);
+    const double* s = group_scores + u * maxN;
+    i64 rank = 0;
+    if (n < nb)
+      for (i64 m = 0; m < nb; ++m)
+        if (s[m] > s[n] || (s[m] == s[n] && m < n)) ++rank;
+    ranks[t] = rank;
+  }
   for (int b = 0; b < B; ++b) {
     for (int j = 0; j < Hkv; ++j) {
       const i64 nb = ceil_div(seq_lens[b], bs);
       const i64 keff = (K < nb) ? K : nb;
-      const double* s = group_scores + ((i64)b * Hkv + j) * maxN;
       int32_t* out = sel + ((i64)b * Hkv + j) * K;
       i64 w = 0;
       for (i64 n = 0; n < nb; ++n) {
-        i64 rank = 0;
-        for (i64 m = 0; m < nb; ++m)
-          if (s[m] > s[n] || (s[m] == s[n] && m < n)) ++rank;
+        const i64 rank = ranks[((i64)b * Hkv + j) * maxN + n];
         if (rank < keff) out[w++] = (int32_t)n;
       }
       for (i64 r = w; r < K; ++r) out[r] = -1;
       sel_count[(i64)b * Hkv + j] = (int32_t)w;
     }
   }
+  free(ranks);
 }
 
 /*
@@ -276,13 +289,30 @@ static int is_forced(i64 n, i64 L, int bs, int sink, int local) {
 
 void oracle_select(const double* group_scores, const int32_t* seq_lens, int B, int Hkv, int maxN,
                    int bs, int K, int sink, int local, int32_t* sel, int32_t* sel_count) {
-#pragma omp parallel for collapse(2) schedule(dynamic)
+  /* rank[b, j, n] of every block that is not forced, among the blocks that
+     are not forced; counted in parallel by block as in oracle_topk */
+  const i64 rows = (i64)B * Hkv;
+  i64* ranks = (i64*)malloc((size_t)(rows * maxN > 0 ? rows * maxN : 1) * sizeof(i64));
+#pragma omp parallel for schedule(dynamic, 64)
+  for (i64 t = 0; t < rows * maxN; ++t) {
+    const i64 u = t / maxN, n = t % maxN;
+    const i64 L = seq_lens[u / Hkv];
+    const i64 nb = ceil_div(L, bs);
+    const double* s = group_scores + u * maxN;
+    i64 rank = 0;
+    if (n < nb && !is_forced(n, L, bs, sink, local)) {
+      for (i64 m = 0; m < nb; ++m) {
+        if (is_forced(m, L, bs, sink, local)) continue;
+        if (s[m] > s[n] || (s[m] == s[n] && m < n)) ++rank;
+      }
+    }
+    ranks[t] = rank;
+  }
   for (int b = 0; b < B; ++b) {
     for (int j = 0; j < Hkv; ++j) {
       const i64 L = seq_lens[b];
       const i64 nb = ceil_div(L, bs);
       const i64 keff = (K < nb) ? K : nb;
-      const double* s = group_scores + ((i64)b * Hkv + j) * maxN;
       int32_t* out = sel + ((i64)b * Hkv + j) * K;
       i64 n_forced = 0;
       for (i64 n = 0; n < nb; ++n) n_forced += is_forced(n, L, bs, sink, local);
@@ -293,11 +323,7 @@ void oracle_select(const double* group_scores, const int32_t* seq_lens, int B, i
         if (is_forced(n, L, bs, sink, local)) {
           take = 1;
         } else {
-          i64 rank = 0;
-          for (i64 m = 0; m < nb; ++m) {
-            if (is_forced(m, L, bs, sink, local)) continue;
-            if (s[m] > s[n] || (s[m] == s[n] && m < n)) ++rank;
-          }
+          const i64 rank = ranks[((i64)b * Hkv + j) * maxN + n];
           take = rank < free_slots;
         }
         if (take) out[w++] = (int32_t)n;
@@ -306,6 +332,7 @@ void oracle_select(const double* group_scores, const int32_t* seq_lens, int B, i
       sel_count[(i64)b * Hkv + j] = (int32_t)w;
     }
   }
+  free(ranks);
 }
 
 /*
