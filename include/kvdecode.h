@@ -217,7 +217,9 @@ size_t kv_score_topk_workspace_size(const kv_shape* shape, int32_t topk_blocks);
  * after, and K_eff to sel_count[b, j].  sel_blocks has row stride topk_blocks.
  * scores_out (nullable) receives S ([B, Hkv, maxN], -inf for n >= N_b); when it
  * is NULL the scores go to `workspace`, which must hold
- * kv_score_topk_workspace_size() bytes.  topk_blocks >= 1; maxN <= 32768.
+ * kv_score_topk_workspace_size() bytes.  topk_blocks >= 1; maxN <= 65536 (a
+ * 1M-token context of 16-token blocks; rows past 32768 blocks take a slower
+ * instance that keeps part of its keys in scratch memory).
  */
 kv_status kv_block_score_topk(const kv_shape* shape, const void* q, const void* kmeta,
                               const int32_t* block_table, const int32_t* seq_lens,

@@ -444,37 +444,55 @@ __global__ __launch_bounds__(WAVES * kWave) void block_score_kernel(
 // output scan a forced block counts like a key above the threshold.  The
 // caller keeps #forced <= K, so #forced <= K_eff.
 
+// monotone key of a score: larger score -> larger key; f + 0 turns -0 into +0
+// so equal scores give equal keys; negative scores flip every bit, the
+// others only the sign bit
 __device__ inline uint32_t score_key(float f) {
-  if (f == 0.0f) f = 0.0f;
-  const uint32_t u = __float_as_uint(f);
-  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+  const uint32_t u = __float_as_uint(f + 0.0f);
+  return u ^ ((uint32_t)((int32_t)u >> 31) | 0x80000000u);
 }
 
 __device__ inline uint32_t wave_inclusive_scan(uint32_t v) { return wave_scan_add_u32(v); }
 
+// buf: NWAVES words, 16-byte aligned
 template <int NWAVES>
 __device__ inline uint32_t block_exclusive_scan(uint32_t v, uint32_t* buf) {
+  static_assert(NWAVES % 4 == 0, "wave totals are read 4 at a time");
   const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x >> 6;
   const uint32_t inc = wave_inclusive_scan(v);
   if (lane == kWave - 1) buf[wave] = inc;
   __syncthreads();
   uint32_t before = 0;
-  for (int w = 0; w < wave; ++w) before += buf[w];
+#pragma unroll
+  for (int w = 0; w < NWAVES; w += 4) {
+    const uint4 t = *reinterpret_cast<const uint4*>(buf + w);
+    before += (w < wave ? t.x : 0u) + (w + 1 < wave ? t.y : 0u) + (w + 2 < wave ? t.z : 0u) +
+              (w + 3 < wave ? t.w : 0u);
+  }
   return before + inc - v;
 }
 
 // Top-K of one row by the NT threads of a workgroup (all of them call it);
-// EPT keys per thread, NT * EPT >= maxN.
+// EPT keys per thread, NT * EPT >= maxN.  The per-key work is written without
+// branches (selects, unconditional LDS adds, one candidate reservation per
+// wave): with 16 waves sharing a compute unit's 4 SIMDs, per-key exec-mask
+// branches cost more time than the row's loads.
 // Most keys the rank count after the wide pass resolves (else 8-bit passes go on).
 constexpr int kTopkCandMax = 512;
 
 template <int NT>
 struct TopkSmem {
+  static constexpr int NW = NT / kWave;
+  static_assert(NW % 4 == 0, "wave partials are read 4 at a time");
   // per-wave 256-bin histograms of the 8-bit passes; the wide first pass uses
   // the same words as one shared histogram of NT * 4 bins
-  alignas(16) uint32_t hist[NT / kWave][256];
-  uint32_t buf_a[NT / kWave], buf_b[NT / kWave], buf_c[NT / kWave], buf_d[NT / kWave];
-  uint32_t buf_e[NT / kWave], buf_f[NT / kWave], buf_g[NT / kWave];
+  alignas(16) uint32_t hist[NW][256];
+  // per-wave partials of the first pass: min and max key, #forced, min of the
+  // keys of scores >= +0, max of the others, #keys of scores >= +0
+  alignas(16) uint32_t part[6][NW];
+  alignas(16) uint32_t scan_a[NW];
+  alignas(16) uint32_t scan_c[NW];
+  alignas(16) uint32_t scan_d[NW];
   uint32_t state[3];
   uint32_t cand_n;
   uint32_t cand_key[kTopkCandMax];
@@ -486,35 +504,29 @@ __device__ inline void topk_row(const float* __restrict__ row, int maxN, int L, 
                                 int local, int32_t* __restrict__ out,
                                 int32_t* __restrict__ count_out, TopkSmem<NT>& sm) {
   constexpr int NW = NT / kWave;
+  constexpr int FW = (EPT + 31) / 32;   // words of the forced mask
   auto& hist = sm.hist;
-  auto& buf_a = sm.buf_a;
-  auto& buf_b = sm.buf_b;
-  auto& buf_c = sm.buf_c;
-  auto& buf_d = sm.buf_d;
-  auto& buf_e = sm.buf_e;
-  auto& buf_f = sm.buf_f;
-  auto& buf_g = sm.buf_g;
   auto& state = sm.state;
   const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid >> 6;
-  // the scores are read first: the row is readable up to maxN whatever the
-  // length, so the loads need not wait for it
-  float sc[EPT];
   const int n0 = tid * EPT;
+  // the scores are read first: the row is readable up to maxN whatever the
+  // length, so the loads need not wait for it (key[] holds the score bits)
+  uint32_t key[EPT];
   if constexpr (EPT % 4 == 0) {
     // 16-byte loads of the thread's contiguous scores when the row allows it
     if ((reinterpret_cast<uintptr_t>(row) & 15u) == 0 && n0 + EPT <= maxN) {
 #pragma unroll
       for (int r = 0; r < EPT; r += 4) {
-        const float4 v = *reinterpret_cast<const float4*>(row + n0 + r);
-        sc[r] = v.x; sc[r + 1] = v.y; sc[r + 2] = v.z; sc[r + 3] = v.w;
+        const uint4 v = load16(row + n0 + r);
+        key[r] = v.x; key[r + 1] = v.y; key[r + 2] = v.z; key[r + 3] = v.w;
       }
     } else {
 #pragma unroll
-      for (int r = 0; r < EPT; ++r) sc[r] = (n0 + r < maxN) ? row[n0 + r] : 0.0f;
+      for (int r = 0; r < EPT; ++r) key[r] = (n0 + r < maxN) ? __float_as_uint(row[n0 + r]) : 0u;
     }
   } else {
 #pragma unroll
-    for (int r = 0; r < EPT; ++r) sc[r] = (n0 + r < maxN) ? row[n0 + r] : 0.0f;
+    for (int r = 0; r < EPT; ++r) key[r] = (n0 + r < maxN) ? __float_as_uint(row[n0 + r]) : 0u;
   }
   const int nb = (L + kBlockSize - 1) / kBlockSize;
   const int keff = min(K, nb);
@@ -523,64 +535,90 @@ __device__ inline void topk_row(const float* __restrict__ row, int maxN, int L, 
   for (int i = max(keff, 0) + tid; i < K; i += NT) out[i] = -1;
   if (keff <= 0) return;  // workgroup-uniform
 
-  uint32_t key[EPT];
-  uint32_t kmn = 0xFFFFFFFFu, kmx = 0u;
-  // the same over the keys of scores >= +0 (top bit set) and below it
-  uint32_t kmn_pos = 0xFFFFFFFFu, kmx_neg = 0u, npos = 0u;
-  static_assert(EPT <= 32, "forced mask holds 32 blocks");
-  uint32_t fmask = 0u;
+  // keys: valid competing blocks get monotone keys (> 0); blocks past N_b and
+  // forced blocks get 0, and a forced block sets its bit of fm
+  const bool forcing = sink > 0 || local > 0;   // workgroup-uniform
+  uint32_t fm[FW];
 #pragma unroll
-  for (int r = 0; r < EPT; ++r) {
-    key[r] = 0u;
-    const int n = n0 + r;
-    if (n < nb) {
-      if (n * kBlockSize < sink || (n + 1) * kBlockSize > local_from) {
-        fmask |= 1u << r;
-      } else {
-        key[r] = score_key(sc[r]);  // valid keys are >= key(-inf) > 0
-        kmn = min(kmn, key[r]);
-        kmx = max(kmx, key[r]);
-        if (key[r] >> 31) {
-          kmn_pos = min(kmn_pos, key[r]);
-          ++npos;
-        } else {
-          kmx_neg = max(kmx_neg, key[r]);
-        }
+  for (int w = 0; w < FW; ++w) fm[w] = 0u;
+  uint32_t kmn = 0xFFFFFFFFu, kmx = 0u, nf = 0u;
+  auto convert = [&](auto with_forcing) {
+#pragma unroll
+    for (int r = 0; r < EPT; ++r) {
+      const int n = n0 + r;
+      bool live = n < nb;
+      if constexpr (decltype(with_forcing)::value) {
+        const bool forced = live & ((n * kBlockSize < sink) | ((n + 1) * kBlockSize > local_from));
+        fm[r / 32] |= (uint32_t)forced << (r % 32);
+        nf += (uint32_t)forced;
+        live &= !forced;
       }
+      const uint32_t k = live ? score_key(__uint_as_float(key[r])) : 0u;
+      key[r] = k;
+      kmn = min(kmn, live ? k : 0xFFFFFFFFu);
+      kmx = max(kmx, k);
     }
-  }
+  };
+  if (forcing) convert(std::true_type{});
+  else convert(std::false_type{});
   kmn = wave_reduce_u32(kmn, MinU32());
   kmx = wave_reduce_u32(kmx, MaxU32());
-  uint32_t nf = wave_reduce_u32((uint32_t)__popc(fmask), AddU32());
-  kmn_pos = wave_reduce_u32(kmn_pos, MinU32());
-  kmx_neg = wave_reduce_u32(kmx_neg, MaxU32());
-  npos = wave_reduce_u32(npos, AddU32());
+  if (forcing) nf = wave_reduce_u32(nf, AddU32());
   if (lane == 0) {
-    buf_a[wave] = kmn; buf_b[wave] = kmx; buf_d[wave] = nf;
-    buf_e[wave] = kmn_pos; buf_f[wave] = kmx_neg; buf_g[wave] = npos;
+    sm.part[0][wave] = kmn;
+    sm.part[1][wave] = kmx;
+    sm.part[2][wave] = nf;
   }
   if (tid == 0) sm.cand_n = 0u;
   // the wide pass's shared histogram is cleared under the same barrier
 #pragma unroll
   for (int i = 0; i < 4; ++i) (&hist[0][0])[tid + i * NT] = 0u;
   __syncthreads();
-  nf = 0;
-  npos = 0;
+  nf = 0u;
 #pragma unroll
-  for (int w = 0; w < NW; ++w) {
-    kmn = min(kmn, buf_a[w]);
-    kmx = max(kmx, buf_b[w]);
-    nf += buf_d[w];
-    kmn_pos = min(kmn_pos, buf_e[w]);
-    kmx_neg = max(kmx_neg, buf_f[w]);
-    npos += buf_g[w];
+  for (int w = 0; w < NW; w += 4) {
+    const uint4 a = *reinterpret_cast<const uint4*>(&sm.part[0][w]);
+    const uint4 x = *reinterpret_cast<const uint4*>(&sm.part[1][w]);
+    const uint4 f = *reinterpret_cast<const uint4*>(&sm.part[2][w]);
+    kmn = min(min(kmn, min(a.x, a.y)), min(a.z, a.w));
+    kmx = max(max(kmx, max(x.x, x.y)), max(x.z, x.w));
+    nf += (f.x + f.y) + (f.z + f.w);
   }
 
   // places left for the blocks that compete; with none, T is above every key
   uint32_t krem = (uint32_t)keff - nf;
-  // scores of both signs: the counts say on which side of zero T lies, so the
-  // select starts inside that half (the top bit is then known)
-  if (krem != 0u && ((kmn ^ kmx) >> 31)) {
+  // keys of both signs (workgroup-uniform): the count of keys of scores >= +0
+  // says on which side of zero T lies, so the select starts inside that half
+  // (its top bit is then known); this pass runs only for such rows
+  const bool split = krem != 0u && ((kmn ^ kmx) >> 31);
+  if (split) {
+    uint32_t kmn_pos = 0xFFFFFFFFu, kmx_neg = 0u, npos = 0u;
+#pragma unroll
+    for (int r = 0; r < EPT; ++r) {
+      const bool pos = (key[r] >> 31) != 0u;
+      kmn_pos = min(kmn_pos, pos ? key[r] : 0xFFFFFFFFu);
+      kmx_neg = max(kmx_neg, pos ? 0u : key[r]);
+      npos += (uint32_t)pos;
+    }
+    kmn_pos = wave_reduce_u32(kmn_pos, MinU32());
+    kmx_neg = wave_reduce_u32(kmx_neg, MaxU32());
+    npos = wave_reduce_u32(npos, AddU32());
+    if (lane == 0) {
+      sm.part[3][wave] = kmn_pos;
+      sm.part[4][wave] = kmx_neg;
+      sm.part[5][wave] = npos;
+    }
+    __syncthreads();
+    npos = 0u;
+#pragma unroll
+    for (int w = 0; w < NW; w += 4) {
+      const uint4 mp = *reinterpret_cast<const uint4*>(&sm.part[3][w]);
+      const uint4 xn = *reinterpret_cast<const uint4*>(&sm.part[4][w]);
+      const uint4 np = *reinterpret_cast<const uint4*>(&sm.part[5][w]);
+      kmn_pos = min(min(kmn_pos, min(mp.x, mp.y)), min(mp.z, mp.w));
+      kmx_neg = max(max(kmx_neg, max(xn.x, xn.y)), max(xn.z, xn.w));
+      npos += (np.x + np.y) + (np.z + np.w);
+    }
     if (npos >= krem) {
       kmn = kmn_pos;
     } else {
@@ -592,6 +630,10 @@ __device__ inline void topk_row(const float* __restrict__ row, int maxN, int L, 
   const uint32_t diff = kmn ^ kmx;
   int lo = (krem == 0u) ? 0 : (diff ? 32 - __clz(diff) : 0);
   uint32_t prefix = (krem == 0u) ? 0xFFFFFFFFu : ((lo >= 32) ? 0u : (kmx >> lo) << lo);
+  // does key k share the known bits [lo, 32) of T? (key 0 never does)
+  auto known = [&](uint32_t k) {
+    return (k != 0u) & ((lo >= 32) | ((k >> (lo & 31)) == (prefix >> (lo & 31))));
+  };
   if (lo > 0) {
     // one wide digit first: a shared histogram of NB = NT * 4 bins (thread t
     // owns digits NB-1-4t .. NB-4-4t, top down) and one block scan over them
@@ -602,15 +644,19 @@ __device__ inline void topk_row(const float* __restrict__ row, int maxN, int L, 
     const uint32_t dmask = (1u << width) - 1u;
     uint32_t* hs = &hist[0][0];
     static_assert(sizeof(sm.hist) == NB * sizeof(uint32_t), "shared histogram size");
+    // without the sign split every valid key lies in [kmn, kmx] and so
+    // shares the known bits
+    if (split) {
 #pragma unroll
-    for (int r = 0; r < EPT; ++r) {
-      const bool match = key[r] != 0u && (lo >= 32 || (key[r] >> lo) == (prefix >> lo));
-      if (match) atomicAdd(&hs[(key[r] >> shift) & dmask], 1u);
+      for (int r = 0; r < EPT; ++r) atomicAdd(&hs[(key[r] >> shift) & dmask], (uint32_t)known(key[r]));
+    } else {
+#pragma unroll
+      for (int r = 0; r < EPT; ++r) atomicAdd(&hs[(key[r] >> shift) & dmask], (uint32_t)(key[r] != 0u));
     }
     __syncthreads();
     const uint4 v4 = *reinterpret_cast<const uint4*>(&hs[NB - 4 - 4 * tid]);
     const uint32_t cs[4] = {v4.w, v4.z, v4.y, v4.x};   // digits NB-1-4t down to NB-4-4t
-    uint32_t above = block_exclusive_scan<NW>(v4.x + v4.y + v4.z + v4.w, buf_a);
+    uint32_t above = block_exclusive_scan<NW>(v4.x + v4.y + v4.z + v4.w, sm.scan_a);
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
       if (above < krem && above + cs[q] >= krem) {
@@ -626,14 +672,22 @@ __device__ inline void topk_row(const float* __restrict__ row, int maxN, int L, 
     lo = shift;
     const uint32_t nc = state[2];
     if (lo > 0 && nc <= (uint32_t)kTopkCandMax) {
-      // few keys share the known bits: gather them and rank each against the
-      // others by (key descending, index ascending); the key ranked krem-1 is T
+      // few keys share the known bits: gather them (one reservation per wave)
+      // and rank each against the others by (key descending, index
+      // ascending); the key ranked krem-1 is T
+      uint32_t mine = 0u;
+#pragma unroll
+      for (int r = 0; r < EPT; ++r) mine += (uint32_t)known(key[r]);
+      const uint32_t incl = wave_scan_add_u32(mine);
+      uint32_t wbase = 0u;
+      if (lane == kWave - 1 && incl != 0u) wbase = atomicAdd(&sm.cand_n, incl);
+      uint32_t pos = (uint32_t)__builtin_amdgcn_readlane((int)wbase, kWave - 1) + incl - mine;
 #pragma unroll
       for (int r = 0; r < EPT; ++r) {
-        if (key[r] != 0u && (key[r] >> lo) == (prefix >> lo)) {
-          const uint32_t pos = atomicAdd(&sm.cand_n, 1u);
+        if (known(key[r])) {
           sm.cand_key[pos] = key[r];
           sm.cand_idx[pos] = n0 + r;
+          ++pos;
         }
       }
       __syncthreads();
@@ -676,10 +730,7 @@ __device__ inline void topk_row(const float* __restrict__ row, int maxN, int L, 
 #pragma unroll
     for (int i = lane; i < 256; i += kWave) h[i] = 0u;
 #pragma unroll
-    for (int r = 0; r < EPT; ++r) {
-      const bool match = key[r] != 0u && (lo >= 32 || (key[r] >> lo) == (prefix >> lo));
-      if (match) atomicAdd(&h[(key[r] >> shift) & dmask], 1u);
-    }
+    for (int r = 0; r < EPT; ++r) atomicAdd(&h[(key[r] >> shift) & dmask], (uint32_t)known(key[r]));
     __syncthreads();
     if (wave == 0) {
       // lane L owns digits 255-4L .. 252-4L (descending)
@@ -713,23 +764,27 @@ __device__ inline void topk_row(const float* __restrict__ row, int maxN, int L, 
   uint32_t n_gt = 0, n_eq = 0;
 #pragma unroll
   for (int r = 0; r < EPT; ++r) {
-    const bool f = (fmask >> r) & 1u;
-    n_gt += f || key[r] > T;
-    n_eq += key[r] == T;
+    n_gt += ((fm[r / 32] >> (r % 32)) & 1u) | (uint32_t)(key[r] > T);
+    n_eq += (uint32_t)(key[r] == T);
   }
-  // own buffer: with no radix pass, slower waves may still read buf_a / buf_b
-  const uint32_t ex = block_exclusive_scan<NW>((n_gt << 16) | n_eq, buf_c);
-  uint32_t gt_before = ex >> 16, eq_before = ex & 0xFFFFu;
+  // the scans use their own buffers: with no radix pass, slower waves may
+  // still read the partials, and a wide pass's readers the first scan buffer
+  uint32_t gt_before, eq_before;
+  if constexpr ((long)NT * EPT < 65536) {
+    const uint32_t ex = block_exclusive_scan<NW>((n_gt << 16) | n_eq, sm.scan_c);
+    gt_before = ex >> 16;
+    eq_before = ex & 0xFFFFu;
+  } else {   // a count can reach 65536: one scan per count
+    gt_before = block_exclusive_scan<NW>(n_gt, sm.scan_c);
+    eq_before = block_exclusive_scan<NW>(n_eq, sm.scan_d);
+  }
 #pragma unroll
   for (int r = 0; r < EPT; ++r) {
-    const int n = tid * EPT + r;
-    if (((fmask >> r) & 1u) || key[r] > T) {
-      out[gt_before + min(eq_before, krem)] = n;
-      ++gt_before;
-    } else if (key[r] == T) {
-      if (eq_before < krem) out[gt_before + eq_before] = n;
-      ++eq_before;
-    }
+    const bool gt = (((fm[r / 32] >> (r % 32)) & 1u) != 0u) | (key[r] > T);
+    const bool eq = key[r] == T;
+    if (gt | (eq & (eq_before < krem))) out[gt_before + min(eq_before, krem)] = n0 + r;
+    gt_before += (uint32_t)gt;
+    eq_before += (uint32_t)eq;
   }
 }
 
@@ -853,6 +908,7 @@ hipError_t launch_topk(const float* scores, const int32_t* seq_lens, int B, int 
   else if (ept <= 8) KVD_TOPK(8);
   else if (ept <= 16) KVD_TOPK(16);
   else if (ept <= 32) KVD_TOPK(32);
+  else if (ept <= 64) KVD_TOPK(64);
   else return hipErrorInvalidValue;
 #undef KVD_TOPK
   return hipGetLastError();

@@ -150,7 +150,7 @@ inline int cu_count() {
 inline int device_cu_count() { return cu_count(); }
 
 // Largest maxN the Top-K kernel keeps in registers (1024 threads x 32 keys).
-constexpr int kTopkMaxBlocks = 32768;
+constexpr int kTopkMaxBlocks = 65536;
 
 
 }  // namespace kvd

@@ -137,7 +137,7 @@ def test_score_topk_argument_checks():
                                                  stream=stream))
     expect(kd.KV_ERR_WORKSPACE, lambda stream: f(s, A16, A16, A16, A16, 2, None, A16, A16, A16,
                                                  need - 4, stream=stream))
-    big = shape(max_blocks_per_seq=32769)
+    big = shape(max_blocks_per_seq=65537)
     expect(kd.KV_ERR_UNSUPPORTED, lambda stream: f(big, A16, A16, A16, A16, 2, A16, A16, A16,
                                                    stream=stream))
 
@@ -246,7 +246,7 @@ def test_select_argument_checks():
     expect(kd.KV_ERR_ALIGNMENT, call(index=A4))
     expect(kd.KV_ERR_ALIGNMENT, call(q=A4))
     expect(kd.KV_ERR_WORKSPACE, call(scores=None))
-    big = shape(max_blocks_per_seq=32769)
+    big = shape(max_blocks_per_seq=65537)
     expect(kd.KV_ERR_UNSUPPORTED, lambda stream: f(big, 0, A16, A16, A16, A16, 8, 0, 0, A16, A16,
                                                    A16, stream=stream))
 

@@ -111,3 +111,42 @@ def test_boundary_digit_holding_many_equal_keys(gpu, n_eq):
     rows = [np.stack([r, r[::-1].copy()])]
     for k in (1, 4, 256, n_eq + 2, n_eq + 4):
         run_case(gpu, rows, k)
+
+
+def test_table_65536_blocks_ties_and_forced_tokens(gpu):
+    """A 1M-token context (65536 blocks of 16, one KV head; KVDrive evaluates
+    1M-token windows): exact integer scores with heavy ties and random scores,
+    plain Top-K and Top-K with 4 sink + 64 local tokens forced, against the
+    oracle's rank count."""
+    from kv_cache_decode_amd.step import DeviceWorkload
+    rng = np.random.default_rng(65536)
+    ties = rng.integers(-3, 4, size=(1, 65536)).astype(np.float32)
+    spread = rng.standard_normal((1, 65536)).astype(np.float32)
+    for rows, ks in (([ties], (2048, 65536)), ([spread], (256,))):
+        data = scored_workload(rows, Hkv=1, G=2, ragged=[7])
+        dw = DeviceWorkload(data, device=gpu)
+        dw.meta_build()
+        nb = data.num_blocks()
+        gs = None
+        for k in ks:
+            for sink, local in ((0, 0), (4, 64)):
+                dw.select(k, "minmax", sink, local)
+                torch.cuda.synchronize()
+                sel, cnt = dw.sel.cpu().numpy(), dw.sel_count.cpu().numpy()
+                scores = dw.scores.cpu().numpy()
+                exp = wl.bf16_bits_to_f32(wl.to_storage(rows[0], "bf16"))
+                np.testing.assert_array_equal(scores[0, :, :nb[0]], exp[:, :nb[0]] + 0.0)
+                if gs is None:
+                    gs = scores.astype(np.float64)
+                rsel, rcnt = oracle.select(gs, data.seq_lens, 16, k, sink, local)
+                np.testing.assert_array_equal(cnt, rcnt)
+                np.testing.assert_array_equal(sel[:, :, :k], rsel)
+        t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        t0.record()
+        for _ in range(10):
+            dw.select(256, "minmax")
+        t1.record()
+        torch.cuda.synchronize()
+        print(f"\n65536-block score + Top-K 256: {t0.elapsed_time(t1) * 100:.1f} us per call",
+              flush=True)
+        dw.close()
