@@ -256,6 +256,27 @@ kv_status kv_block_select(const kv_shape* shape, int32_t index_kind, const void*
                           void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * kv_block_select for callers that cannot allocate device memory (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid allocation):
+ * the same selection, written to the same sel_blocks / sel_count, without a
+ * scores buffer or workspace.  The scores are kept in device memory of the
+ * library itself, a 4 MiB array that each GPU it runs on holds until the
+ * process ends; its address on the current device is looked up (never
+ * allocated) on the first call on that device.  The call itself allocates
+ * nothing.  Limit: num_seqs * num_kv_heads * max_blocks_per_seq <= 1048576
+ * scores (for example 8 KV heads of 131072 blocks), else KV_ERR_WORKSPACE
+ * before any launch.  Every call on one GPU shares that array: calls that
+ * overlap on one GPU (other streams, other threads) race and may select from
+ * each other's scores; calls ordered on one stream do not.  Arguments, checks
+ * and errors are otherwise those of kv_block_select.
+ */
+kv_status kv_block_select_no_alloc(const kv_shape* shape, int32_t index_kind, const void* q,
+                                   const void* index, const int32_t* block_table,
+                                   const int32_t* seq_lens, int32_t topk_blocks,
+                                   int32_t sink_tokens, int32_t local_tokens, int32_t* sel_blocks,
+                                   int32_t* sel_count, void* stream);
+
+/*
  * Number of splits the library would pick for kv_paged_decode_attn (and the
  * cached attention) with `blocks_per_unit` blocks per (sequence, KV head)
  * (maxN for dense calls, the list length for sparse ones): about 6 waves per

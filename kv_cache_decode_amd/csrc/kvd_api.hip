@@ -6,6 +6,7 @@
 #include <algorithm>
 #include <cstdarg>
 #include <cstdio>
+#include <mutex>
 #include <string>
 
 #include "../../include/kvdecode.h"
@@ -321,11 +322,15 @@ int32_t kv_max_forced_blocks(const kv_shape* shape, int32_t sink_tokens, int32_t
   return (int32_t)std::min<long>(n, 0x7fffffffL);
 }
 
-kv_status kv_block_select(const kv_shape* shape, int32_t index_kind, const void* q,
-                          const void* index, const int32_t* block_table, const int32_t* seq_lens,
-                          int32_t topk_blocks, int32_t sink_tokens, int32_t local_tokens,
-                          float* scores_out, int32_t* sel_blocks, int32_t* sel_count,
-                          void* workspace, size_t workspace_bytes, void* stream) {
+}  // extern "C"
+
+namespace {
+// Argument checks of the selection calls; scores_out may be NULL (the caller
+// then supplies the score buffer).
+kv_status check_select(const kv_shape* shape, int32_t index_kind, const void* q, const void* index,
+                       const int32_t* block_table, const int32_t* seq_lens, int32_t topk_blocks,
+                       int32_t sink_tokens, int32_t local_tokens, const float* scores_out,
+                       const int32_t* sel_blocks, const int32_t* sel_count) {
   kv_status st = check_shape(shape);
   if (st != KV_OK) return st;
   if (index_kind != KV_INDEX_MINMAX && index_kind != KV_INDEX_MEAN)
@@ -349,15 +354,14 @@ kv_status kv_block_select(const kv_shape* shape, int32_t index_kind, const void*
   if (!aligned(block_table, 4) || !aligned(seq_lens, 4) || !aligned(sel_blocks, 4) ||
       !aligned(sel_count, 4) || (scores_out && !aligned(scores_out, 4)))
     return fail(KV_ERR_ALIGNMENT, "integer and score arrays must be 4-byte aligned");
-  float* scores = scores_out;
-  if (!scores) {
-    const size_t need = kv_score_topk_workspace_size(shape, topk_blocks);
-    if (!workspace || workspace_bytes < need)
-      return fail(KV_ERR_WORKSPACE, "workspace of %zu bytes needed (got %zu)", need,
-                  workspace ? workspace_bytes : (size_t)0);
-    if (!aligned(workspace, 4)) return fail(KV_ERR_ALIGNMENT, "workspace must be 4-byte aligned");
-    scores = static_cast<float*>(workspace);
-  }
+  return KV_OK;
+}
+
+// Score + Top-K launches into a checked score buffer.
+kv_status launch_select(const kv_shape* shape, int32_t index_kind, const void* q,
+                        const void* index, const int32_t* block_table, const int32_t* seq_lens,
+                        int32_t topk_blocks, int32_t sink_tokens, int32_t local_tokens,
+                        float* scores, int32_t* sel_blocks, int32_t* sel_count, void* stream) {
   const int G = shape->num_q_heads / shape->num_kv_heads;
   hipStream_t s = (hipStream_t)stream;
   hipError_t e = kvd::launch_block_score(shape->dtype, shape->head_dim, G, index_kind, q, index,
@@ -369,6 +373,81 @@ kv_status kv_block_select(const kv_shape* shape, int32_t index_kind, const void*
                                      shape->max_blocks_per_seq, topk_blocks, sink_tokens,
                                      local_tokens, sel_blocks, sel_count, s),
                     "top-k launch");
+}
+
+// The score buffer of kv_block_select_no_alloc: device memory of the library
+// itself (a copy per GPU, held until the process ends), so the call allocates
+// nothing.  Host code reaches it only through the address hipGetSymbolAddress
+// gives on each device (the name is a host-side stand-in there).
+constexpr size_t kNoAllocScores = (size_t)1 << 20;   // floats: B * Hkv * maxN at most (4 MiB)
+static __device__ __align__(256) float scratch[kNoAllocScores];
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+float* g_scratch[kMaxDevices] = {};
+
+// The current device's address of `scratch`, looked up on the first call on
+// that device (with it current) and kept.
+kv_status scratch_scores(float** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_status(e, "hipGetDevice");
+  if (dev < 0 || dev >= kMaxDevices)
+    return fail(KV_ERR_UNSUPPORTED, "device %d above the %d devices the scratch table holds", dev,
+                kMaxDevices);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return hip_status(e, "hipGetSymbolAddress(scratch)");
+    g_scratch[dev] = static_cast<float*>(p);
+  }
+  *out = g_scratch[dev];
+  return KV_OK;
+}
+}  // namespace
+
+extern "C" {
+
+kv_status kv_block_select(const kv_shape* shape, int32_t index_kind, const void* q,
+                          const void* index, const int32_t* block_table, const int32_t* seq_lens,
+                          int32_t topk_blocks, int32_t sink_tokens, int32_t local_tokens,
+                          float* scores_out, int32_t* sel_blocks, int32_t* sel_count,
+                          void* workspace, size_t workspace_bytes, void* stream) {
+  kv_status st = check_select(shape, index_kind, q, index, block_table, seq_lens, topk_blocks,
+                              sink_tokens, local_tokens, scores_out, sel_blocks, sel_count);
+  if (st != KV_OK) return st;
+  float* scores = scores_out;
+  if (!scores) {
+    const size_t need = kv_score_topk_workspace_size(shape, topk_blocks);
+    if (!workspace || workspace_bytes < need)
+      return fail(KV_ERR_WORKSPACE, "workspace of %zu bytes needed (got %zu)", need,
+                  workspace ? workspace_bytes : (size_t)0);
+    if (!aligned(workspace, 4)) return fail(KV_ERR_ALIGNMENT, "workspace must be 4-byte aligned");
+    scores = static_cast<float*>(workspace);
+  }
+  return launch_select(shape, index_kind, q, index, block_table, seq_lens, topk_blocks,
+                       sink_tokens, local_tokens, scores, sel_blocks, sel_count, stream);
+}
+
+kv_status kv_block_select_no_alloc(const kv_shape* shape, int32_t index_kind, const void* q,
+                                   const void* index, const int32_t* block_table,
+                                   const int32_t* seq_lens, int32_t topk_blocks,
+                                   int32_t sink_tokens, int32_t local_tokens, int32_t* sel_blocks,
+                                   int32_t* sel_count, void* stream) {
+  kv_status st = check_select(shape, index_kind, q, index, block_table, seq_lens, topk_blocks,
+                              sink_tokens, local_tokens, nullptr, sel_blocks, sel_count);
+  if (st != KV_OK) return st;
+  const size_t n = (size_t)shape->num_seqs * shape->num_kv_heads * shape->max_blocks_per_seq;
+  if (n > kNoAllocScores)
+    return fail(KV_ERR_WORKSPACE,
+                "num_seqs * num_kv_heads * max_blocks_per_seq = %zu scores, above the %zu the "
+                "library's scratch holds", n, kNoAllocScores);
+  float* scores = nullptr;
+  st = scratch_scores(&scores);
+  if (st != KV_OK) return st;
+  // the score launch writes every one of the n scores, so nothing is cleared
+  return launch_select(shape, index_kind, q, index, block_table, seq_lens, topk_blocks,
+                       sink_tokens, local_tokens, scores, sel_blocks, sel_count, stream);
 }
 
 kv_status kv_block_score_topk(const kv_shape* shape, const void* q, const void* kmeta,

@@ -28,7 +28,8 @@ DTYPE_CODES = {"f32": KV_F32, "f16": KV_F16, "bf16": KV_BF16}
 EXPORTS = (
     "kv_block_meta_build", "kv_block_mean_build", "kv_append_token", "kv_decode_select",
     "kv_score_topk_workspace_size", "kv_block_score_topk", "kv_max_forced_blocks",
-    "kv_block_select", "kv_auto_num_splits", "kv_auto_num_splits_fp8",
+    "kv_block_select", "kv_block_select_no_alloc", "kv_auto_num_splits",
+    "kv_auto_num_splits_fp8",
     "kv_auto_num_splits_tiered", "kv_paged_decode_attn", "kv_decode_combine",
     "kv_quantize_pages_fp8", "kv_paged_decode_attn_fp8", "kv_quantize_pages_int4",
     "kv_paged_decode_attn_int4", "kv_paged_decode_attn_tiered",
@@ -91,6 +92,7 @@ def _load() -> ctypes.CDLL:
         "kv_decode_select": (I32, [S, I32, P, P, P, P, P, P, P, P, P, I32, I32, I32, P, P, P, P,
                                    SZ, P]),
         "kv_block_select": (I32, [S, I32, P, P, P, P, I32, I32, I32, P, P, P, P, SZ, P]),
+        "kv_block_select_no_alloc": (I32, [S, I32, P, P, P, P, I32, I32, I32, P, P, P]),
         "kv_score_topk_workspace_size": (SZ, [S, I32]),
         "kv_block_score_topk": (I32, [S, P, P, P, P, I32, P, P, P, P, SZ, P]),
         "kv_auto_num_splits": (I32, [S, I32]),
@@ -235,6 +237,16 @@ def kv_block_select(shape: KVShape, index_kind: int, q: Buf, index: Buf, block_t
                                 _p(block_table), _p(seq_lens), topk_blocks, sink_tokens,
                                 local_tokens, _p(scores_out), _p(sel_blocks), _p(sel_count),
                                 _p(workspace), workspace_bytes, _stream(stream)))
+
+
+def kv_block_select_no_alloc(shape: KVShape, index_kind: int, q: Buf, index: Buf,
+                             block_table: Buf, seq_lens: Buf, topk_blocks: int, sink_tokens: int,
+                             local_tokens: int, sel_blocks: Buf, sel_count: Buf,
+                             stream=None) -> None:
+    _check(_lib.kv_block_select_no_alloc(ctypes.byref(shape), index_kind, _p(q), _p(index),
+                                         _p(block_table), _p(seq_lens), topk_blocks, sink_tokens,
+                                         local_tokens, _p(sel_blocks), _p(sel_count),
+                                         _stream(stream)))
 
 
 def kv_auto_num_splits(shape: KVShape, blocks_per_unit: int) -> int:

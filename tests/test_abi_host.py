@@ -251,6 +251,28 @@ def test_select_argument_checks():
                                                    A16, stream=stream))
 
 
+def test_select_no_alloc_argument_checks():
+    """The no-allocation selection validates like kv_block_select, and refuses
+    shapes whose scores exceed the library's scratch before any launch."""
+    s = shape()
+    f = kd.kv_block_select_no_alloc
+
+    def call(shp=s, kind=kd.KV_INDEX_MINMAX, q=A16, index=A16, k=8, sink=0, local=0, sel=A16):
+        return lambda stream: f(shp, kind, q, index, A16, A16, k, sink, local, sel, A16,
+                                stream=stream)
+
+    expect(kd.KV_ERR_INVALID_ARG, call(kind=2))
+    expect(kd.KV_ERR_INVALID_ARG, call(k=0))
+    expect(kd.KV_ERR_INVALID_ARG, call(sink=4, local=64, k=5))
+    expect(kd.KV_ERR_INVALID_ARG, call(index=None))
+    expect(kd.KV_ERR_INVALID_ARG, call(sel=None))
+    expect(kd.KV_ERR_ALIGNMENT, call(q=A4))
+    expect(kd.KV_ERR_UNSUPPORTED, call(shp=shape(max_blocks_per_seq=65537)))
+    # 64 sequences x 8 KV heads x 4096 blocks = 2 Mi scores > the 1 Mi the scratch holds
+    big = shape(num_seqs=64, num_q_heads=32, num_kv_heads=8, max_blocks_per_seq=4096)
+    expect(kd.KV_ERR_WORKSPACE, call(shp=big))
+
+
 def test_fp8_argument_checks():
     s = shape()
     qz = kd.kv_quantize_pages_fp8
