@@ -650,8 +650,10 @@ kv_status kv_probe_gather_read(const kv_shape* shape, const void* k_cache, const
 kv_status kv_host_alloc(size_t bytes, uint32_t flags, void** host_ptr, void** dev_ptr);
 kv_status kv_host_free(void* host_ptr);
 
-/* Static description of a status code. */
-const char* kv_status_string(kv_status status);
+/* Static description of a status code: the name of a kv_status value, or
+ * "unknown kv_status" for any other int (the code is taken as an int so that
+ * any value a caller holds may be passed). */
+const char* kv_status_string(int32_t status);
 
 /* Message of the last failing call on this thread ("" if none). */
 const char* kv_last_error_message(void);

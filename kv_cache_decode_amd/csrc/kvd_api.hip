@@ -166,8 +166,8 @@ kv_status attn_common(const kv_shape* shape, int kvq, const void* q, const void*
 
 extern "C" {
 
-const char* kv_status_string(kv_status st) {
-  switch (st) {
+const char* kv_status_string(int32_t status) {
+  switch (status) {
     case KV_OK: return "KV_OK";
     case KV_ERR_INVALID_ARG: return "KV_ERR_INVALID_ARG";
     case KV_ERR_UNSUPPORTED: return "KV_ERR_UNSUPPORTED";
