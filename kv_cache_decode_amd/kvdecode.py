@@ -153,12 +153,58 @@ def _check(status: int) -> None:
 Buf = Union[None, int, "torch.Tensor"]  # noqa: F821
 
 
-def _p(x: Buf) -> Optional[int]:
-    if x is None:
-        return None
-    if isinstance(x, int):
+def _p(x: Buf, need: int = 0, what: str = "buffer", i32: bool = False) -> Optional[int]:
+    """The address the C ABI receives for x: None, an int (a device address the
+    caller vouches for, such as the one kv_host_alloc returns), or a torch
+    tensor, which must be a contiguous tensor in GPU memory of at least `need`
+    bytes (int32 where the ABI takes integers).  The library can check only
+    null pointers and alignment, and a bad address reaches a kernel."""
+    if x is None or isinstance(x, int):
         return x
+    if not x.is_contiguous():
+        raise ValueError(f"{what}: the tensor must be contiguous")
+    if not x.is_cuda:
+        raise ValueError(f"{what}: a tensor in GPU memory is required (got one on {x.device}); "
+                         "host memory goes in as the device address kv_host_alloc returns")
+    if i32 and x.dtype != _torch().int32:
+        raise ValueError(f"{what}: int32 required (got {x.dtype})")
+    have = x.numel() * x.element_size()
+    if have < need:
+        raise ValueError(f"{what}: {have} bytes, the shape needs {need}")
     return x.data_ptr()
+
+
+def _torch():
+    import torch
+    return torch
+
+
+class _Lay:
+    """Byte counts of the arrays a kv_shape describes."""
+
+    def __init__(self, s: KVShape):
+        self.eb = 4 if s.dtype == KV_F32 else 2
+        self.B, self.Hq, self.Hkv, self.D = s.num_seqs, s.num_q_heads, s.num_kv_heads, s.head_dim
+        self.P, self.maxN, self.bs = s.num_pages, s.max_blocks_per_seq, s.block_size
+        self.q = self.B * self.Hq * self.D * self.eb
+        self.pool = self.P * self.Hkv * self.bs * self.D * self.eb
+        self.kmeta = self.P * self.Hkv * 2 * self.D * self.eb
+        self.kmean = self.P * self.Hkv * self.D * 4
+        self.table = self.B * self.maxN * 4
+        self.lens = self.B * 4
+        self.scores = self.B * self.Hkv * self.maxN * 4
+        self.rows = self.B * self.Hkv * 4
+        self.token = self.B * self.Hkv * self.D * self.eb
+
+    def sel(self, k: int) -> int:
+        return self.B * self.Hkv * max(k, 0) * 4
+
+    def index(self, kind: int) -> int:
+        return self.kmean if kind == KV_INDEX_MEAN else self.kmeta
+
+    def parts(self, splits: int):
+        n = self.B * self.Hq * max(splits, 0)
+        return n * self.D * 4, n * 4
 
 
 def _stream(stream) -> Optional[int]:
@@ -172,23 +218,32 @@ def _stream(stream) -> Optional[int]:
 
 def kv_block_meta_build(shape: KVShape, k_cache: Buf, page_ids: Buf, page_valid_tokens: Buf,
                         num_page_ids: int, kmeta: Buf, stream=None) -> None:
-    _check(_lib.kv_block_meta_build(ctypes.byref(shape), _p(k_cache), _p(page_ids),
-                                    _p(page_valid_tokens), num_page_ids, _p(kmeta),
-                                    _stream(stream)))
+    L, n = _Lay(shape), max(num_page_ids, 0) * 4
+    _check(_lib.kv_block_meta_build(ctypes.byref(shape), _p(k_cache, L.pool, "k_cache"),
+                                    _p(page_ids, n, "page_ids", True),
+                                    _p(page_valid_tokens, n, "page_valid_tokens", True),
+                                    num_page_ids, _p(kmeta, L.kmeta, "kmeta"), _stream(stream)))
 
 
 def kv_block_mean_build(shape: KVShape, k_cache: Buf, page_ids: Buf, page_valid_tokens: Buf,
                         num_page_ids: int, kmean: Buf, stream=None) -> None:
-    _check(_lib.kv_block_mean_build(ctypes.byref(shape), _p(k_cache), _p(page_ids),
-                                    _p(page_valid_tokens), num_page_ids, _p(kmean),
-                                    _stream(stream)))
+    L, n = _Lay(shape), max(num_page_ids, 0) * 4
+    _check(_lib.kv_block_mean_build(ctypes.byref(shape), _p(k_cache, L.pool, "k_cache"),
+                                    _p(page_ids, n, "page_ids", True),
+                                    _p(page_valid_tokens, n, "page_valid_tokens", True),
+                                    num_page_ids, _p(kmean, L.kmean, "kmean"), _stream(stream)))
 
 
 def kv_append_token(shape: KVShape, k_new: Buf, v_new: Buf, block_table: Buf, seq_lens: Buf,
                     k_cache: Buf, v_cache: Buf, kmeta: Buf = None, kmean: Buf = None,
                     stream=None) -> None:
-    _check(_lib.kv_append_token(ctypes.byref(shape), _p(k_new), _p(v_new), _p(block_table),
-                                _p(seq_lens), _p(k_cache), _p(v_cache), _p(kmeta), _p(kmean),
+    L = _Lay(shape)
+    _check(_lib.kv_append_token(ctypes.byref(shape), _p(k_new, L.token, "k_new"),
+                                _p(v_new, L.token, "v_new"),
+                                _p(block_table, L.table, "block_table", True),
+                                _p(seq_lens, L.lens, "seq_lens", True),
+                                _p(k_cache, L.pool, "k_cache"), _p(v_cache, L.pool, "v_cache"),
+                                _p(kmeta, L.kmeta, "kmeta"), _p(kmean, L.kmean, "kmean"),
                                 _stream(stream)))
 
 
@@ -197,11 +252,19 @@ def kv_decode_select(shape: KVShape, index_kind: int, q: Buf, k_new: Buf, v_new:
                      kmean: Buf, topk_blocks: int, sink_tokens: int, local_tokens: int,
                      scores_out: Buf, sel_blocks: Buf, sel_count: Buf, workspace: Buf = None,
                      workspace_bytes: int = 0, stream=None) -> None:
-    _check(_lib.kv_decode_select(ctypes.byref(shape), index_kind, _p(q), _p(k_new), _p(v_new),
-                                 _p(block_table), _p(seq_lens), _p(k_cache), _p(v_cache),
-                                 _p(kmeta), _p(kmean), topk_blocks, sink_tokens, local_tokens,
-                                 _p(scores_out), _p(sel_blocks), _p(sel_count), _p(workspace),
-                                 workspace_bytes, _stream(stream)))
+    L = _Lay(shape)
+    _check(_lib.kv_decode_select(ctypes.byref(shape), index_kind, _p(q, L.q, "q"),
+                                 _p(k_new, L.token, "k_new"), _p(v_new, L.token, "v_new"),
+                                 _p(block_table, L.table, "block_table", True),
+                                 _p(seq_lens, L.lens, "seq_lens", True),
+                                 _p(k_cache, L.pool, "k_cache"), _p(v_cache, L.pool, "v_cache"),
+                                 _p(kmeta, L.kmeta, "kmeta"), _p(kmean, L.kmean, "kmean"),
+                                 topk_blocks, sink_tokens, local_tokens,
+                                 _p(scores_out, L.scores, "scores_out"),
+                                 _p(sel_blocks, L.sel(topk_blocks), "sel_blocks", True),
+                                 _p(sel_count, L.rows, "sel_count", True),
+                                 _p(workspace, workspace_bytes, "workspace"), workspace_bytes,
+                                 _stream(stream)))
 
 
 def kv_score_topk_workspace_size(shape: KVShape, topk_blocks: int) -> int:
@@ -211,9 +274,15 @@ def kv_score_topk_workspace_size(shape: KVShape, topk_blocks: int) -> int:
 def kv_block_score_topk(shape: KVShape, q: Buf, kmeta: Buf, block_table: Buf, seq_lens: Buf,
                         topk_blocks: int, scores_out: Buf, sel_blocks: Buf, sel_count: Buf,
                         workspace: Buf = None, workspace_bytes: int = 0, stream=None) -> None:
-    _check(_lib.kv_block_score_topk(ctypes.byref(shape), _p(q), _p(kmeta), _p(block_table),
-                                    _p(seq_lens), topk_blocks, _p(scores_out), _p(sel_blocks),
-                                    _p(sel_count), _p(workspace), workspace_bytes,
+    L = _Lay(shape)
+    _check(_lib.kv_block_score_topk(ctypes.byref(shape), _p(q, L.q, "q"),
+                                    _p(kmeta, L.kmeta, "kmeta"),
+                                    _p(block_table, L.table, "block_table", True),
+                                    _p(seq_lens, L.lens, "seq_lens", True), topk_blocks,
+                                    _p(scores_out, L.scores, "scores_out"),
+                                    _p(sel_blocks, L.sel(topk_blocks), "sel_blocks", True),
+                                    _p(sel_count, L.rows, "sel_count", True),
+                                    _p(workspace, workspace_bytes, "workspace"), workspace_bytes,
                                     _stream(stream)))
 
 
@@ -233,19 +302,30 @@ def kv_block_select(shape: KVShape, index_kind: int, q: Buf, index: Buf, block_t
                     seq_lens: Buf, topk_blocks: int, sink_tokens: int, local_tokens: int,
                     scores_out: Buf, sel_blocks: Buf, sel_count: Buf, workspace: Buf = None,
                     workspace_bytes: int = 0, stream=None) -> None:
-    _check(_lib.kv_block_select(ctypes.byref(shape), index_kind, _p(q), _p(index),
-                                _p(block_table), _p(seq_lens), topk_blocks, sink_tokens,
-                                local_tokens, _p(scores_out), _p(sel_blocks), _p(sel_count),
-                                _p(workspace), workspace_bytes, _stream(stream)))
+    L = _Lay(shape)
+    _check(_lib.kv_block_select(ctypes.byref(shape), index_kind, _p(q, L.q, "q"),
+                                _p(index, L.index(index_kind), "index"),
+                                _p(block_table, L.table, "block_table", True),
+                                _p(seq_lens, L.lens, "seq_lens", True), topk_blocks, sink_tokens,
+                                local_tokens, _p(scores_out, L.scores, "scores_out"),
+                                _p(sel_blocks, L.sel(topk_blocks), "sel_blocks", True),
+                                _p(sel_count, L.rows, "sel_count", True),
+                                _p(workspace, workspace_bytes, "workspace"), workspace_bytes,
+                                _stream(stream)))
 
 
 def kv_block_select_no_alloc(shape: KVShape, index_kind: int, q: Buf, index: Buf,
                              block_table: Buf, seq_lens: Buf, topk_blocks: int, sink_tokens: int,
                              local_tokens: int, sel_blocks: Buf, sel_count: Buf,
                              stream=None) -> None:
-    _check(_lib.kv_block_select_no_alloc(ctypes.byref(shape), index_kind, _p(q), _p(index),
-                                         _p(block_table), _p(seq_lens), topk_blocks, sink_tokens,
-                                         local_tokens, _p(sel_blocks), _p(sel_count),
+    L = _Lay(shape)
+    _check(_lib.kv_block_select_no_alloc(ctypes.byref(shape), index_kind, _p(q, L.q, "q"),
+                                         _p(index, L.index(index_kind), "index"),
+                                         _p(block_table, L.table, "block_table", True),
+                                         _p(seq_lens, L.lens, "seq_lens", True), topk_blocks,
+                                         sink_tokens, local_tokens,
+                                         _p(sel_blocks, L.sel(topk_blocks), "sel_blocks", True),
+                                         _p(sel_count, L.rows, "sel_count", True),
                                          _stream(stream)))
 
 
@@ -257,16 +337,26 @@ def kv_paged_decode_attn(shape: KVShape, q: Buf, k_cache: Buf, v_cache: Buf, blo
                          seq_lens: Buf, sel_blocks: Buf, sel_count: Buf, sel_stride: int,
                          scale: float, num_splits: int, part_o: Buf, part_m: Buf, part_l: Buf,
                          stream=None) -> None:
-    _check(_lib.kv_paged_decode_attn(ctypes.byref(shape), _p(q), _p(k_cache), _p(v_cache),
-                                     _p(block_table), _p(seq_lens), _p(sel_blocks),
-                                     _p(sel_count), sel_stride, scale, num_splits, _p(part_o),
-                                     _p(part_m), _p(part_l), _stream(stream)))
+    L = _Lay(shape)
+    po, pm = L.parts(num_splits)
+    _check(_lib.kv_paged_decode_attn(ctypes.byref(shape), _p(q, L.q, "q"),
+                                     _p(k_cache, L.pool, "k_cache"), _p(v_cache, L.pool, "v_cache"),
+                                     _p(block_table, L.table, "block_table", True),
+                                     _p(seq_lens, L.lens, "seq_lens", True),
+                                     _p(sel_blocks, L.sel(sel_stride), "sel_blocks", True),
+                                     _p(sel_count, L.rows, "sel_count", True), sel_stride, scale,
+                                     num_splits, _p(part_o, po, "part_o"), _p(part_m, pm, "part_m"),
+                                     _p(part_l, pm, "part_l"), _stream(stream)))
 
 
 def kv_decode_combine(shape: KVShape, num_splits: int, part_o: Buf, part_m: Buf, part_l: Buf,
                       out: Buf, lse_out: Buf = None, stream=None) -> None:
-    _check(_lib.kv_decode_combine(ctypes.byref(shape), num_splits, _p(part_o), _p(part_m),
-                                  _p(part_l), _p(out), _p(lse_out), _stream(stream)))
+    L = _Lay(shape)
+    po, pm = L.parts(num_splits)
+    _check(_lib.kv_decode_combine(ctypes.byref(shape), num_splits, _p(part_o, po, "part_o"),
+                                  _p(part_m, pm, "part_m"), _p(part_l, pm, "part_l"),
+                                  _p(out, L.B * L.Hq * L.D * 4, "out"),
+                                  _p(lse_out, L.B * L.Hq * 4, "lse_out"), _stream(stream)))
 
 
 def kv_quantize_pages_fp8(shape: KVShape, k_cache: Buf, v_cache: Buf, page_ids: Buf,

@@ -533,3 +533,15 @@ def test_tiered_split_argument_checks():
     expect(kd.KV_ERR_ALIGNMENT, call(k_cold=A4))
     expect(kd.KV_ERR_INVALID_ARG, call(sel_blocks=A16))
     expect(kd.KV_ERR_INVALID_ARG, call(scale=0.0))
+
+
+def test_binding_refuses_host_and_strided_tensors():
+    """The binding hands the C ABI only contiguous tensors in GPU memory (or an
+    int address the caller vouches for); everything else fails in Python."""
+    import torch
+    s = shape()
+    q = torch.zeros(2, 8, 128, dtype=torch.bfloat16)
+    with pytest.raises(ValueError, match="GPU memory"):
+        kd.kv_block_score_topk(s, q, A16, A16, A16, 4, A16, A16, A16)
+    with pytest.raises(ValueError, match="contiguous"):
+        kd.kv_block_score_topk(s, q.transpose(0, 1), A16, A16, A16, 4, A16, A16, A16)

@@ -273,3 +273,31 @@ def test_slots_past_the_sequence_end_never_leak(gpu, dtype, G):
         dw.decode(sparse=True, num_splits=S)
         sel, cnt = dw.sel.cpu().numpy(), dw.sel_count.cpu().numpy()
         assert_rows_close(to_f64(dw.out), o.attention(sel, cnt)[0], tol, "sparse")
+
+
+def test_binding_refuses_wrong_dtype_and_short_buffers(gpu):
+    """A too-small or wrongly typed tensor is refused by the binding before any
+    launch (the library can check only null pointers and alignment)."""
+    from kv_cache_decode_amd import kvdecode as kd
+    data = mk(2, 8, 2, 128, (300, 40), "bf16", seed=12)
+    dw = run_device(data, device=gpu)
+    dw.meta_build()
+    k = 4
+    sel = torch.zeros(2, 2, k, dtype=torch.int32, device=gpu)
+    cnt = torch.zeros(2, 2, dtype=torch.int32, device=gpu)
+    args = lambda **kw: dict(dict(q=dw.q, kmeta=dw.kmeta, block_table=dw.block_table,
+                                  seq_lens=dw.seq_lens, topk_blocks=k, scores_out=dw.scores,
+                                  sel_blocks=sel, sel_count=cnt), **kw)
+    kd.kv_block_score_topk(dw.shape, **args())                       # the good call
+    with pytest.raises(ValueError, match="sel_blocks"):
+        kd.kv_block_score_topk(dw.shape, **args(sel_blocks=sel[:, :, :2].contiguous()))
+    with pytest.raises(ValueError, match="int32"):
+        kd.kv_block_score_topk(dw.shape, **args(sel_count=cnt.to(torch.int64)))
+    with pytest.raises(ValueError, match="kmeta"):
+        kd.kv_block_score_topk(dw.shape, **args(kmeta=dw.kmeta[:1]))
+    with pytest.raises(ValueError, match="part_o"):
+        kd.kv_paged_decode_attn(dw.shape, dw.q, dw.k_cache, dw.v_cache, dw.block_table,
+                                dw.seq_lens, None, None, 0, 0.1, 4,
+                                torch.zeros(8, dtype=torch.float32, device=gpu),
+                                torch.zeros(64, device=gpu), torch.zeros(64, device=gpu))
+    dw.close()
