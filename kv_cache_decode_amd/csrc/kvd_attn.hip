@@ -419,12 +419,9 @@ __global__ __launch_bounds__(WAVES * kWave) void paged_attn_kernel(
 // 16-bit product as a hi + lo pair (p = hi + lo exactly up to 2^-17 relative),
 // so the weights keep close to fp32 precision.
 
-typedef __bf16 bf16x8_v __attribute__((ext_vector_type(8)));
-typedef _Float16 f16x8_v __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x4_v __attribute__((ext_vector_type(4)));
 typedef _Float16 f16x2_v __attribute__((ext_vector_type(2)));
 typedef short s16x4_v __attribute__((ext_vector_type(4)));
-typedef float f32x4_v __attribute__((ext_vector_type(4)));
 
 template <typename DT>
 struct MfmaOps;
@@ -432,8 +429,7 @@ struct MfmaOps;
 template <>
 struct MfmaOps<BF16> {
   __device__ static inline f32x4_v qk(const uint4& a, const uint4& b, f32x4_v c) {
-    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_v, a),
-                                                   __builtin_bit_cast(bf16x8_v, b), c, 0, 0, 0);
+    return mfma_16x16x32<BF16>(a, b, c);
   }
   __device__ static inline f32x4_v pv(const uint2& a, const uint2& b, f32x4_v c) {
     return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(s16x4_v, a),
@@ -450,8 +446,7 @@ struct MfmaOps<BF16> {
 template <>
 struct MfmaOps<F16> {
   __device__ static inline f32x4_v qk(const uint4& a, const uint4& b, f32x4_v c) {
-    return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8_v, a),
-                                                  __builtin_bit_cast(f16x8_v, b), c, 0, 0, 0);
+    return mfma_16x16x32<F16>(a, b, c);
   }
   __device__ static inline f32x4_v pv(const uint2& a, const uint2& b, f32x4_v c) {
     return __builtin_amdgcn_mfma_f32_16x16x16f16(__builtin_bit_cast(f16x4_v, a),

@@ -182,6 +182,29 @@ __device__ inline uint32_t int4_encode(float y) {
   return (uint32_t)(int)r & 15u;
 }
 
+// ---------------------------------------------------------------- matrix cores
+//
+// v_mfma_f32_16x16x32_{bf16,f16}: D (16 x 16, fp32) = A (16 x 32) B (32 x 16) + C.
+// Lane l holds A[l % 16][8 (l / 16) .. + 8], B[8 (l / 16) .. + 8][l % 16] (eight
+// 16-bit values, 16 bytes) and D[4 (l / 16) + i][l % 16] for i = 0..3.
+
+typedef __bf16 bf16x8_v __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x8_v __attribute__((ext_vector_type(8)));
+typedef float f32x4_v __attribute__((ext_vector_type(4)));
+
+template <typename DT>
+__device__ inline f32x4_v mfma_16x16x32(const uint4& a, const uint4& b, f32x4_v c);
+template <>
+__device__ inline f32x4_v mfma_16x16x32<BF16>(const uint4& a, const uint4& b, f32x4_v c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_v, a),
+                                                 __builtin_bit_cast(bf16x8_v, b), c, 0, 0, 0);
+}
+template <>
+__device__ inline f32x4_v mfma_16x16x32<F16>(const uint4& a, const uint4& b, f32x4_v c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8_v, a),
+                                                __builtin_bit_cast(f16x8_v, b), c, 0, 0, 0);
+}
+
 // ---------------------------------------------------------------- lane shuffles
 //
 // DPP controls (gfx9 encoding): quad_perm, row_mirror (lane i <-> 15-i in a

@@ -31,6 +31,10 @@
 #ifndef KVD_SCORE_WAVES
 #define KVD_SCORE_WAVES 4
 #endif
+// waves per workgroup of the matrix-core scorer (16 blocks per wave)
+#ifndef KVD_SCORE_MFMA_WAVES
+#define KVD_SCORE_MFMA_WAVES 4
+#endif
 
 namespace kvd {
 
@@ -418,6 +422,125 @@ __global__ __launch_bounds__(WAVES * kWave) void block_score_kernel(
 #pragma unroll
     for (int g = 0; g < G; ++g) best = fmaxf(best, head_score_lane<E, LPR, IDX>(qp[g], qn[g], ka, kb));
     if (c == 0 && n < maxN && n != nskip) out[n] = (n < nb) ? best : -INFINITY;
+  }
+}
+
+// ============================================================== block score on the matrix cores
+//
+// With 16-bit min/max index rows the scores of one (sequence, KV head) are a
+// small dense contraction: S[n, h] = [kmin_n | kmax_n] . [q-_h | q+_h] over the
+// 2D channels of the row pair, q- = min(q, 0) against kmin and q+ = max(q, 0)
+// against kmax (for each channel one of the two products is an exact zero,
+// and products of 16-bit values are exact in fp32).  A wave takes 16
+// consecutive logical blocks as the 16 rows of the MFMA A operand, read
+// straight from the index rows (lane l: block l % 16, channels
+// 32 st + 8 (l / 16) .. + 8 of step st), and the G query heads of the group as
+// the first G columns of B (the other columns are zero).  A block's group
+// score is the max over those G columns of its output row.  Each output
+// element depends on its own A row and B column only, so a block scores the
+// same bits wherever it sits in a tile.
+
+// Lane l's B operand: column l % 16 (head j*G + l % 16 when l % 16 < G) at
+// channels 32 st + 8 (l / 16) .. + 8 of [q- | q+] (16-bit sign masks, exact).
+template <typename DT, int D, int G>
+__device__ inline void score_query_operand(const void* __restrict__ q, size_t head0, int lane,
+                                           uint4 (&qB)[2 * D / 32]) {
+  using St = typename DT::storage;
+  const int r = lane & 15, kg = lane >> 4;
+#pragma unroll
+  for (int st = 0; st < 2 * D / 32; ++st) {
+    const int k0 = 32 * st + 8 * kg;
+    const bool pos = k0 >= D;            // the q+ half pairs with kmax
+    uint4 w = r < G ? load16(static_cast<const St*>(q) + (head0 + r) * D + (pos ? k0 - D : k0))
+                    : make_uint4(0, 0, 0, 0);
+    auto keep = [pos](uint32_t x) {
+      const uint32_t neg = ((x >> 15) & 0x00010001u) * 0xFFFFu;   // per 16-bit half: sign set
+      return x & (pos ? ~neg : neg);
+    };
+    qB[st] = make_uint4(keep(w.x), keep(w.y), keep(w.z), keep(w.w));
+  }
+}
+
+// Group score of the tile's rows 4 (l / 16) + i from the accumulators: the max
+// over the G head columns of each row (aligned groups of G lanes).
+template <int G>
+__device__ inline void group_max_columns(f32x4_v& acc) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) acc[i] = group_reduce<G, OpMax>(acc[i]);
+}
+
+// MEAN: the append also refreshes a mean-key index (its registers are kept
+// out of the instances that have none to refresh).
+template <typename DT, int D, int G, int WAVES, bool APPEND, bool MEAN = false>
+__global__ __launch_bounds__(WAVES * kWave) void block_score_mfma_kernel(
+    const void* __restrict__ q, const void* __restrict__ kmeta,
+    const int32_t* __restrict__ block_table, const int32_t* __restrict__ seq_lens, int Hq,
+    int Hkv, int maxN, float* __restrict__ scores, AppendArgs ap) {
+  static_assert(G >= 1 && G <= 8, "the group fills 1..8 of the 16 B columns");
+  using St = typename DT::storage;
+  constexpr int KS = 2 * D / 32;              // MFMA steps over a row pair
+  const int lane = threadIdx.x & (kWave - 1);
+  const int r = lane & 15, kg = lane >> 4;
+  const int j = blockIdx.y, b = blockIdx.z;
+  const size_t head0 = (size_t)b * Hq + (size_t)j * G;
+  float* out = scores + ((size_t)b * Hkv + j) * maxN;
+  int nskip = -1;
+  if constexpr (APPEND) {
+    // the first workgroup of each (b, j) row appends the new token (lanes
+    // c < LPR of wave 0) and scores its block from the updated rows, staged in
+    // LDS as row 0 of a tile; the other workgroups skip that block
+    nskip = (seq_lens[b] - 1) / kBlockSize;
+    if (blockIdx.x == 0) {
+      if (threadIdx.x >= kWave) return;                  // wave 0 only
+      constexpr int E = RowGeom<DT, D>::E, LPR = RowGeom<DT, D>::LPR;
+      static_assert(2 * LPR == KS * 4, "row-pair chunks");
+      __shared__ uint4 pair[2 * LPR];                    // kmin chunks, then kmax chunks
+      uint4 qB[KS];
+      score_query_operand<DT, D, G>(q, head0, lane, qB);
+      float mn[E], mx[E], mv[E];
+      if (lane < LPR) {
+        append_lane<DT, D>(ap.k_new, ap.v_new, block_table, seq_lens, Hkv, maxN, j, b, lane,
+                           ap.k_cache, ap.v_cache, ap.kmeta, MEAN ? ap.kmean : nullptr, mn, mx,
+                           mv);
+        pair[lane] = DT::narrow_exact(mn);
+        pair[LPR + lane] = DT::narrow_exact(mx);
+      }
+      // one wave: its LDS writes complete before its later LDS reads
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+      f32x4_v acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int st = 0; st < KS; ++st)
+        acc = mfma_16x16x32<DT>(r == 0 ? pair[4 * st + kg] : make_uint4(0, 0, 0, 0), qB[st], acc);
+      group_max_columns<G>(acc);
+      if (lane == 0) out[nskip] = acc[0];
+      return;
+    }
+  }
+  const int wg = APPEND ? (int)blockIdx.x - 1 : (int)blockIdx.x;
+  const int n0 = (wg * WAVES + (threadIdx.x >> 6)) * 16;
+  if (n0 >= maxN) return;
+  // the table entry is read beside the length (the whole row is readable)
+  const int n = n0 + r;
+  const int pg = n < maxN ? block_table[(size_t)b * maxN + n] : 0;
+  const int nb = (seq_lens[b] + kBlockSize - 1) / kBlockSize;
+  uint4 qB[KS];
+  score_query_operand<DT, D, G>(q, head0, lane, qB);
+  uint4 a[KS];
+  const St* src = static_cast<const St*>(kmeta) + ((size_t)pg * Hkv + j) * 2 * D + 8 * kg;
+#pragma unroll
+  for (int st = 0; st < KS; ++st) a[st] = n < nb ? load16(src + 32 * st) : make_uint4(0, 0, 0, 0);
+  f32x4_v acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int st = 0; st < KS; ++st) acc = mfma_16x16x32<DT>(a[st], qB[st], acc);
+  group_max_columns<G>(acc);
+  if (r == 0) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int m = n0 + 4 * kg + i;
+      if (m < maxN && m != nskip) out[m] = m < nb ? acc[i] : -INFINITY;
+    }
   }
 }
 
@@ -872,6 +995,25 @@ hipError_t launch_block_score(int dtype, int D, int G, int index_kind, const voi
         using DT = decltype(dt);
         constexpr int DD = decltype(d)::value;
         constexpr int GG = decltype(g)::value;
+        if constexpr (!std::is_same<DT, F32>::value) {
+          if (index_kind == kIndexMinMax) {     // 16-bit min/max rows: the matrix cores
+            constexpr int W = KVD_SCORE_MFMA_WAVES;
+            const dim3 grid_m((maxN + 16 * W - 1) / (16 * W) + (append ? 1 : 0), Hkv, B);
+            if (append && kmean)
+              hipLaunchKernelGGL((block_score_mfma_kernel<DT, DD, GG, W, true, true>), grid_m,
+                                 dim3(W * kWave), 0, stream, q, index, block_table, seq_lens, Hq,
+                                 Hkv, maxN, scores, ap);
+            else if (append)
+              hipLaunchKernelGGL((block_score_mfma_kernel<DT, DD, GG, W, true, false>), grid_m,
+                                 dim3(W * kWave), 0, stream, q, index, block_table, seq_lens, Hq,
+                                 Hkv, maxN, scores, ap);
+            else
+              hipLaunchKernelGGL((block_score_mfma_kernel<DT, DD, GG, W, false>), grid_m,
+                                 dim3(W * kWave), 0, stream, q, index, block_table, seq_lens, Hq,
+                                 Hkv, maxN, scores, ap);
+            return hipGetLastError();
+          }
+        }
         constexpr int WAVES = KVD_SCORE_WAVES, STEPS = KVD_SCORE_STEPS;
         constexpr int per_wg = WAVES * STEPS * RowGeom<DT, DD>::TPI;
         // one more workgroup per row does the append
