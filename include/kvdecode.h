@@ -202,6 +202,48 @@ kv_status kv_decode_select(const kv_shape* shape, int32_t index_kind, const void
                            int32_t* sel_count, void* workspace, size_t workspace_bytes,
                            void* stream);
 
+/*
+ * The decode step's append and scores in one launch: kv_decode_select without
+ * its Top-K (Dual-Blade background: the step stores the new pair; KVDrive
+ * §2.2-§2.3: the index scores every block).  Results are bit for bit those of
+ * kv_append_token(shape, k_new, v_new, block_table, seq_lens, k_cache, v_cache,
+ * kmeta, kmean) followed by the scores kv_block_select writes to scores_out
+ * ([B, Hkv, maxN] fp32, -inf for n >= N_b) over index = kmeta
+ * (KV_INDEX_MINMAX) or kmean (KV_INDEX_MEAN, which is then required).  The
+ * selection and attention follow in kv_select_decode_attn.  Arguments,
+ * layouts and errors are those of kv_decode_select; scores_out is required.
+ */
+kv_status kv_decode_score(const kv_shape* shape, int32_t index_kind, const void* q,
+                          const void* k_new, const void* v_new, const int32_t* block_table,
+                          const int32_t* seq_lens, void* k_cache, void* v_cache, void* kmeta,
+                          float* kmean, float* scores_out, void* stream);
+
+/*
+ * Top-K selection and sparse split-K attention in one call (KVDrive §2.3: the
+ * critical blocks are selected, then attention runs over them only).  Results
+ * are bit for bit those of the Top-K of kv_block_select over `scores` (the
+ * same topk_blocks, sink_tokens and local_tokens; written to sel_blocks
+ * [B, Hkv, topk_blocks] and sel_count [B, Hkv]) followed by
+ * kv_paged_decode_attn over that list with sel_stride = topk_blocks and the
+ * same num_splits (part_o [B, Hq, S, D], part_m, part_l [B, Hq, S], merged by
+ * kv_decode_combine).  scores: fp32 [B, Hkv, maxN], e.g. from kv_decode_score
+ * or kv_block_select's scores_out.  For 16-bit K/V with G >= 2, maxN <= 2048
+ * and at most 2048 list positions per eight splits (8 * ceil(topk_blocks /
+ * num_splits)) it is one launch: each workgroup repeats the row's Top-K
+ * itself, keeps the positions of its eight splits in LDS and attends them,
+ * which saves the Top-K launch and the list's round trip through memory;
+ * other calls (longer rows, where the repeated Top-K costs more than the
+ * launch it saves) run the two launches.  Arguments and errors are those of
+ * the two calls (KV_FLAG_HOST_KV pools included).
+ */
+kv_status kv_select_decode_attn(const kv_shape* shape, const float* scores,
+                                const int32_t* block_table, const int32_t* seq_lens,
+                                int32_t topk_blocks, int32_t sink_tokens, int32_t local_tokens,
+                                const void* q, const void* k_cache, const void* v_cache,
+                                float scale, int32_t num_splits, int32_t* sel_blocks,
+                                int32_t* sel_count, float* part_o, float* part_m, float* part_l,
+                                void* stream);
+
 /* Workspace bytes kv_block_score_topk needs when scores_out is NULL (0 otherwise). */
 size_t kv_score_topk_workspace_size(const kv_shape* shape, int32_t topk_blocks);
 
@@ -284,6 +326,14 @@ kv_status kv_block_select_no_alloc(const kv_shape* shape, int32_t index_kind, co
  * at least 2 blocks per split (8 with KV_FLAG_HOST_KV).  Always >= 1.
  */
 int32_t kv_auto_num_splits(const kv_shape* shape, int32_t blocks_per_unit);
+
+/*
+ * Number of splits for kv_select_decode_attn with topk_blocks: where the call
+ * is one launch, eight splits (one workgroup) per compute unit over the
+ * (sequence, KV head) rows, at most 8 * ceil(topk_blocks / 8); elsewhere
+ * kv_auto_num_splits(shape, topk_blocks).  Always >= 1.
+ */
+int32_t kv_auto_select_splits(const kv_shape* shape, int32_t topk_blocks);
 
 /* The same for kv_paged_decode_attn_fp8: about 8 waves per compute unit. */
 int32_t kv_auto_num_splits_fp8(const kv_shape* shape, int32_t blocks_per_unit);

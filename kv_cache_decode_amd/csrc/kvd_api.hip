@@ -286,6 +286,93 @@ kv_status kv_decode_select(const kv_shape* shape, int32_t index_kind, const void
                     "top-k launch");
 }
 
+kv_status kv_decode_score(const kv_shape* shape, int32_t index_kind, const void* q,
+                          const void* k_new, const void* v_new, const int32_t* block_table,
+                          const int32_t* seq_lens, void* k_cache, void* v_cache, void* kmeta,
+                          float* kmean, float* scores_out, void* stream) {
+  kv_status st = check_shape(shape);
+  if (st != KV_OK) return st;
+  if (index_kind != KV_INDEX_MINMAX && index_kind != KV_INDEX_MEAN)
+    return fail(KV_ERR_INVALID_ARG, "index_kind=%d unknown", index_kind);
+  const void* index = index_kind == KV_INDEX_MINMAX ? kmeta : static_cast<const void*>(kmean);
+  if (!index)
+    return fail(KV_ERR_INVALID_ARG, "the index selected by index_kind (%s) is required",
+                index_kind == KV_INDEX_MINMAX ? "kmeta" : "kmean");
+  if (!q || !k_new || !v_new || !block_table || !seq_lens || !k_cache || !v_cache || !scores_out)
+    return fail(KV_ERR_INVALID_ARG,
+                "q, k_new, v_new, block_table, seq_lens, k_cache, v_cache and scores_out are "
+                "required");
+  if (!aligned(q, 16) || !aligned(k_new, 16) || !aligned(v_new, 16) || !aligned(k_cache, 16) ||
+      !aligned(v_cache, 16) || (kmeta && !aligned(kmeta, 16)) || (kmean && !aligned(kmean, 16)))
+    return fail(KV_ERR_ALIGNMENT,
+                "q, k_new, v_new, k_cache, v_cache, kmeta and kmean must be 16-byte aligned");
+  if (!aligned(block_table, 4) || !aligned(seq_lens, 4) || !aligned(scores_out, 4))
+    return fail(KV_ERR_ALIGNMENT, "integer and score arrays must be 4-byte aligned");
+  const int G = shape->num_q_heads / shape->num_kv_heads;
+  return hip_status(kvd::launch_block_score(shape->dtype, shape->head_dim, G, index_kind, q, index,
+                                            block_table, seq_lens, shape->num_seqs,
+                                            shape->num_q_heads, shape->num_kv_heads,
+                                            shape->max_blocks_per_seq, scores_out,
+                                            (hipStream_t)stream, k_new, v_new, k_cache, v_cache,
+                                            kmeta, kmean),
+                    "kv_decode_score launch");
+}
+
+kv_status kv_select_decode_attn(const kv_shape* shape, const float* scores,
+                                const int32_t* block_table, const int32_t* seq_lens,
+                                int32_t topk_blocks, int32_t sink_tokens, int32_t local_tokens,
+                                const void* q, const void* k_cache, const void* v_cache,
+                                float scale, int32_t num_splits, int32_t* sel_blocks,
+                                int32_t* sel_count, float* part_o, float* part_m, float* part_l,
+                                void* stream) {
+  kv_status st = check_shape(shape);
+  if (st != KV_OK) return st;
+  if (topk_blocks < 1) return fail(KV_ERR_INVALID_ARG, "topk_blocks=%d must be >= 1", topk_blocks);
+  if (sink_tokens < 0 || local_tokens < 0)
+    return fail(KV_ERR_INVALID_ARG, "sink_tokens=%d and local_tokens=%d must be >= 0", sink_tokens,
+                local_tokens);
+  const int32_t forced = kv_max_forced_blocks(shape, sink_tokens, local_tokens);
+  if (forced > topk_blocks)
+    return fail(KV_ERR_INVALID_ARG,
+                "sink_tokens=%d and local_tokens=%d can force %d blocks, more than topk_blocks=%d",
+                sink_tokens, local_tokens, forced, topk_blocks);
+  if (shape->max_blocks_per_seq > kvd::kTopkMaxBlocks)
+    return fail(KV_ERR_UNSUPPORTED, "max_blocks_per_seq=%d above the Top-K limit %d",
+                shape->max_blocks_per_seq, kvd::kTopkMaxBlocks);
+  if (num_splits < 1 || num_splits > 65535 * 4)
+    return fail(KV_ERR_INVALID_ARG, "num_splits=%d must be in [1, 262140]", num_splits);
+  if (!scores || !sel_blocks || !sel_count)
+    return fail(KV_ERR_INVALID_ARG, "scores, sel_blocks and sel_count are required");
+  if (!aligned(scores, 4))
+    return fail(KV_ERR_ALIGNMENT, "scores must be 4-byte aligned");
+  if ((st = check_attn_args(q, k_cache, v_cache, block_table, seq_lens, sel_blocks, sel_count,
+                            topk_blocks, scale, part_o, part_m, part_l)) != KV_OK)
+    return st;
+  const int G = shape->num_q_heads / shape->num_kv_heads;
+  hipStream_t s = (hipStream_t)stream;
+  if (kvd::select_attn_fusable(shape->dtype, G, shape->max_blocks_per_seq, topk_blocks,
+                               num_splits))
+    return hip_status(
+        kvd::launch_select_attn(shape->dtype, shape->head_dim, G, scores, topk_blocks, sink_tokens,
+                                local_tokens, sel_blocks, sel_count, q, k_cache, v_cache,
+                                block_table, seq_lens, shape->num_seqs, shape->num_q_heads,
+                                shape->num_kv_heads, shape->max_blocks_per_seq, num_splits, scale,
+                                part_o, part_m, part_l, s),
+        "kv_select_decode_attn launch");
+  // the same two steps as separate launches (same lists, same partials)
+  hipError_t e = kvd::launch_topk(scores, seq_lens, shape->num_seqs, shape->num_kv_heads,
+                                  shape->max_blocks_per_seq, topk_blocks, sink_tokens,
+                                  local_tokens, sel_blocks, sel_count, s);
+  if (e != hipSuccess) return hip_status(e, "kv_select_decode_attn top-k launch");
+  return hip_status(
+      kvd::launch_paged_attn(shape->dtype, shape->head_dim, G, 0, q, k_cache, v_cache, nullptr,
+                             block_table, seq_lens, sel_blocks, sel_count, topk_blocks, nullptr, 0,
+                             shape->num_seqs, shape->num_q_heads, shape->num_kv_heads,
+                             shape->max_blocks_per_seq, num_splits, scale, part_o, part_m, part_l,
+                             nullptr, s, 0, nullptr, nullptr, nullptr),
+      "kv_select_decode_attn attention launch");
+}
+
 kv_status kv_append_token(const kv_shape* shape, const void* k_new, const void* v_new,
                           const int32_t* block_table, const int32_t* seq_lens, void* k_cache,
                           void* v_cache, void* kmeta, float* kmean, void* stream) {
@@ -484,6 +571,19 @@ int32_t kv_auto_num_splits(const kv_shape* shape, int32_t blocks_per_unit) {
   if (!shape) return 1;
   return auto_splits(shape, blocks_per_unit,
                      mfma_path(shape) ? KVD_SPLIT_WAVES_PER_CU : KVD_SPLIT_WAVES_PER_CU_VALU);
+}
+
+int32_t kv_auto_select_splits(const kv_shape* shape, int32_t topk_blocks) {
+  if (!shape || check_shape(shape) != KV_OK || topk_blocks < 1) return 1;
+  const int G = shape->num_q_heads / shape->num_kv_heads;
+  // one workgroup of kSelAttnWaves splits per compute unit
+  const long units = (long)shape->num_seqs * shape->num_kv_heads;
+  const long wgs = std::max<long>(1, kvd::device_cu_count() / units);
+  const long cap = ((long)topk_blocks + kvd::kSelAttnWaves - 1) / kvd::kSelAttnWaves;
+  const int32_t s = (int32_t)(kvd::kSelAttnWaves * std::min(wgs, cap));
+  if (kvd::select_attn_fusable(shape->dtype, G, shape->max_blocks_per_seq, topk_blocks, s))
+    return s;
+  return kv_auto_num_splits(shape, topk_blocks);
 }
 
 int32_t kv_auto_num_splits_fp8(const kv_shape* shape, int32_t blocks_per_unit) {

@@ -18,6 +18,7 @@
 #include "kvd_device.hpp"
 #include "kvd_dispatch.hpp"
 #include "kvd_launch.hpp"
+#include "kvd_topk.hpp"
 
 // Launch-shape knobs (build macros): waves (= splits) per workgroup, and a
 // lower bound on waves per SIMD for the MFMA kernel (0 = the compiler's
@@ -612,8 +613,12 @@ __device__ inline int qk_channel(int st, int grp) {
 // cold page's codes sit in the first registers of the 16-bit page buffer, and
 // its K codes are read in the 16-bit layout (the 8 channels of each QK step,
 // as 4 or 8 code bytes), so both tiers share q's B operand.
-template <typename DT, int D, int G, int WAVES, bool SPARSE, int KVQ, int COLD = 0, bool FETCH = false>
-__global__ __launch_bounds__(WAVES * kWave) KVD_MFMA_OCCUPANCY_T(COLD) void paged_attn_mfma_kernel(
+// Split s of (sequence b, KV head j) by the calling wave: the body of
+// paged_attn_mfma_kernel, and of the fused select + attention kernel, which
+// passes its list (LDS_LIST: the list count and a pointer that indexes the
+// list by position) instead of sel / sel_count.
+template <typename DT, int D, int G, bool SPARSE, int KVQ, int COLD, bool FETCH, bool LDS_LIST>
+__device__ __forceinline__ void mfma_attn_split(
     const void* __restrict__ q, const void* __restrict__ k_cache, const void* __restrict__ v_cache,
     const float* __restrict__ kv_scales, const int32_t* __restrict__ block_table,
     const int32_t* __restrict__ seq_lens, const int32_t* __restrict__ sel,
@@ -622,30 +627,29 @@ __global__ __launch_bounds__(WAVES * kWave) KVD_MFMA_OCCUPANCY_T(COLD) void page
     float* __restrict__ part_o,
     float* __restrict__ part_m, float* __restrict__ part_l, float* __restrict__ block_lse,
     const void* __restrict__ k_cold, const void* __restrict__ v_cold,
-    const uint8_t* __restrict__ page_tier, FetchArgs fa) {
+    const uint8_t* __restrict__ page_tier, const FetchArgs& fa, const uint32_t* fetched, int s,
+    int j, int b, int list_count, const int32_t* list, int list_first) {
   static_assert(G >= 2 && G <= 8, "the group fills 2..8 of the 16 MFMA rows");
   static_assert(COLD == 0 || KVQ == 0, "tiered pools pair 16-bit hot pages with code pages");
   static_assert(!FETCH || (SPARSE && COLD == 0), "the fused fetch serves cached lists");
+  static_assert(!LDS_LIST || (SPARSE && !FETCH && COLD == 0), "a given list is a plain selection");
   using St = typename DT::storage;
   using Ops = MfmaOps<DT>;
   constexpr int KS = D / 32;   // QK steps of 32 channels
   constexpr int NT = D / 16;   // PV tiles of 16 output channels
   constexpr int NDW = D / 32;  // dwords of V per lane and token (D/16 channels)
   const int lane = threadIdx.x & (kWave - 1);
-  const int s = blockIdx.x * WAVES + (threadIdx.x >> 6);
-  const int j = blockIdx.y, b = blockIdx.z;
-  [[maybe_unused]] const uint32_t* fetched = nullptr;
-  if constexpr (FETCH) fetched = fetched_slot_bits<WAVES * kWave>(fa, b, j, Hkv, sel_stride, num_slots);
   if (s >= S) return;
   const int col = lane & 15, grp = lane >> 4;
 
   const int L = seq_lens[b];
   const int nb = (L + kBlockSize - 1) / kBlockSize;
-  const ListHead pre = SPARSE ? list_head(sel, sel_slots, (size_t)b * Hkv + j, sel_stride, S, s, lane)
-                             : ListHead{};
-  const int n_list = SPARSE ? sel_count[(size_t)b * Hkv + j] : nb;
+  const ListHead pre = (SPARSE && !LDS_LIST)
+                           ? list_head(sel, sel_slots, (size_t)b * Hkv + j, sel_stride, S, s, lane)
+                           : ListHead{};
+  const int n_list = LDS_LIST ? list_count : (SPARSE ? sel_count[(size_t)b * Hkv + j] : nb);
   const int chunk = (n_list + S - 1) / S;
-  const bool pre_ok = SPARSE && pre.chunk == chunk;
+  const bool pre_ok = SPARSE && !LDS_LIST && pre.chunk == chunk;
   const int p0 = min(s * chunk, n_list);
   const int p1 = min(p0 + chunk, n_list);
   const size_t row0 = (size_t)b * Hq + (size_t)j * G;
@@ -719,7 +723,7 @@ __global__ __launch_bounds__(WAVES * kWave) KVD_MFMA_OCCUPANCY_T(COLD) void page
                                   kv_bytes<DT, COLD>((size_t)j * kBlockSize * D +
                                                      (size_t)(4 * grp) * D + 2 * NDW * col)
                             : nullptr;
-  const int32_t* sel_row = SPARSE ? sel + ((size_t)b * Hkv + j) * sel_stride : nullptr;
+  const int32_t* sel_row = LDS_LIST ? list : (SPARSE ? sel + ((size_t)b * Hkv + j) * sel_stride : nullptr);
   const int32_t* slots_row = (SPARSE && sel_slots) ? sel_slots + ((size_t)b * Hkv + j) * sel_stride
                                                    : nullptr;
   const int32_t* bt_row = block_table ? block_table + (size_t)b * maxN : nullptr;
@@ -730,7 +734,9 @@ __global__ __launch_bounds__(WAVES * kWave) KVD_MFMA_OCCUPANCY_T(COLD) void page
     float my_sk = 1.0f, my_sv = 1.0f;
     if (lane < cnt) {
       const bool use_pre = pre_ok && base == p0;
-      const int n = SPARSE ? (use_pre ? pre.n : sel_row[base + lane]) : base + lane;
+      // a given list holds positions list_first.. (the caller's share of it)
+      const int n = SPARSE ? (use_pre ? pre.n : sel_row[base + lane - (LDS_LIST ? list_first : 0)])
+                           : base + lane;
       // cached list: the block sits in slot sel_slots[.] of cache page b*C + slot
       const int slot = slots_row ? (use_pre ? pre.slot : slots_row[base + lane]) : 0;
       my_page = slots_row ? b * num_slots + slot : bt_row[n];
@@ -1061,6 +1067,74 @@ __global__ __launch_bounds__(WAVES * kWave) KVD_MFMA_OCCUPANCY_T(COLD) void page
     part_m[(row0 + col) * PS + s] = m * kLn2;
     part_l[(row0 + col) * PS + s] = lsum;
   }
+}
+
+template <typename DT, int D, int G, int WAVES, bool SPARSE, int KVQ, int COLD = 0, bool FETCH = false>
+__global__ __launch_bounds__(WAVES * kWave) KVD_MFMA_OCCUPANCY_T(COLD) void paged_attn_mfma_kernel(
+    const void* __restrict__ q, const void* __restrict__ k_cache, const void* __restrict__ v_cache,
+    const float* __restrict__ kv_scales, const int32_t* __restrict__ block_table,
+    const int32_t* __restrict__ seq_lens, const int32_t* __restrict__ sel,
+    const int32_t* __restrict__ sel_count, int sel_stride, const int32_t* __restrict__ sel_slots,
+    int num_slots, int Hq, int Hkv, int maxN, int S, int PS, float qscale,
+    float* __restrict__ part_o,
+    float* __restrict__ part_m, float* __restrict__ part_l, float* __restrict__ block_lse,
+    const void* __restrict__ k_cold, const void* __restrict__ v_cold,
+    const uint8_t* __restrict__ page_tier, FetchArgs fa) {
+  const int s = blockIdx.x * WAVES + (threadIdx.x >> 6);
+  const int j = blockIdx.y, b = blockIdx.z;
+  [[maybe_unused]] const uint32_t* fetched = nullptr;
+  if constexpr (FETCH) fetched = fetched_slot_bits<WAVES * kWave>(fa, b, j, Hkv, sel_stride, num_slots);
+  mfma_attn_split<DT, D, G, SPARSE, KVQ, COLD, FETCH, false>(
+      q, k_cache, v_cache, kv_scales, block_table, seq_lens, sel, sel_count, sel_stride, sel_slots,
+      num_slots, Hq, Hkv, maxN, S, PS, qscale, part_o, part_m, part_l, block_lse, k_cold, v_cold,
+      page_tier, fa, fetched, s, j, b, 0, nullptr, 0);
+}
+
+// ============================================================== select + attention in one launch
+//
+// KVDrive §2.3 selects the critical blocks, then computes attention over them.
+// Here the Top-K and the sparse attention of a (sequence, KV head) row share
+// one launch: each workgroup of kSelAttnWaves waves takes that many
+// consecutive splits of the row's selected list.  It first runs the row's
+// Top-K itself (topk_row: the Top-K launch's algorithm, so the list is the
+// same bit for bit; the workgroups of a row repeat it side by side), keeps
+// the list positions of its own splits in LDS, and then each wave attends its
+// split from that list (mfma_attn_split: the attention launch's code and
+// partition, so the partials are the same bit for bit).  Workgroup 0 of each
+// row writes the list and its count.  This saves the Top-K launch's fixed
+// cost and the list's round trip through memory; it pays while the repeated
+// Top-K is short (rows of at most kSelAttnMaxBlocks blocks) and each compute
+// unit holds about one such workgroup (kv_auto_select_splits).
+
+template <typename DT, int D, int G, int EPT>
+__global__ __launch_bounds__(kSelAttnWaves * kWave) KVD_MFMA_OCCUPANCY void select_attn_mfma_kernel(
+    const float* __restrict__ scores, int K, int sink, int local, int32_t* __restrict__ sel,
+    int32_t* __restrict__ sel_count, const void* __restrict__ q,
+    const void* __restrict__ k_cache, const void* __restrict__ v_cache,
+    const int32_t* __restrict__ block_table, const int32_t* __restrict__ seq_lens, int Hq,
+    int Hkv, int maxN, int S, float qscale, float* __restrict__ part_o,
+    float* __restrict__ part_m, float* __restrict__ part_l) {
+  constexpr int W = kSelAttnWaves, NT = W * kWave;
+  __shared__ TopkSmem<NT> sm;
+  __shared__ int32_t lst[kSelAttnListMax];
+  const int j = blockIdx.y, b = blockIdx.z;
+  const size_t u = (size_t)b * Hkv + j;
+  const int L = seq_lens[b];
+  const int keff = min(K, (L + kBlockSize - 1) / kBlockSize);
+  const int chunk = (keff + S - 1) / S;        // the attention launch's partition
+  const int first = min((int)blockIdx.x * W * chunk, keff);
+  const int last = min(first + W * chunk, keff);
+  int32_t* out = blockIdx.x == 0 ? sel + u * K : nullptr;
+  topk_row<NT, EPT>(scores + u * maxN, maxN, L, K, sink, local, out, sel_count + u, sm,
+                    [&](int pos, int n) {
+                      if (pos >= first && pos < last) lst[pos - first] = n;
+                      if (out) out[pos] = n;
+                    });
+  __syncthreads();
+  mfma_attn_split<DT, D, G, true, 0, 0, false, true>(
+      q, k_cache, v_cache, nullptr, block_table, seq_lens, nullptr, nullptr, K, nullptr, 0, Hq,
+      Hkv, maxN, S, S, qscale, part_o, part_m, part_l, nullptr, nullptr, nullptr, nullptr,
+      FetchArgs{}, nullptr, (int)blockIdx.x * W + (int)(threadIdx.x >> 6), j, b, keff, lst, first);
 }
 
 // ============================================================== combine
@@ -1452,6 +1526,41 @@ hipError_t launch_combine(int D, const float* part_o, const float* part_m, const
   else if (S <= 8 * SLOTS) go(std::integral_constant<int, 8>{});
   else go(std::integral_constant<int, 0>{});
   return hipGetLastError();
+}
+
+bool select_attn_fusable(int dtype, int G, int maxN, int K, int S) {
+  const long per_wg = (long)kSelAttnWaves * ((K + S - 1) / S);   // list positions per workgroup
+  return dtype != 0 && G >= 2 && maxN <= kSelAttnMaxBlocks && per_wg <= kSelAttnListMax;
+}
+
+hipError_t launch_select_attn(int dtype, int D, int G, const float* scores, int K, int sink,
+                              int local, int32_t* sel, int32_t* sel_count, const void* q,
+                              const void* k_cache, const void* v_cache,
+                              const int32_t* block_table, const int32_t* seq_lens, int B, int Hq,
+                              int Hkv, int maxN, int S, float scale, float* part_o, float* part_m,
+                              float* part_l, hipStream_t stream) {
+  if (!select_attn_fusable(dtype, G, maxN, K, S)) return hipErrorInvalidValue;
+  constexpr int NT = kSelAttnWaves * kWave;
+  const dim3 grid((S + kSelAttnWaves - 1) / kSelAttnWaves, Hkv, B);
+  const float qscale = scale * kLog2e;
+  static_assert(kSelAttnMaxBlocks <= NT * 4, "one Top-K instance of 4 keys per thread");
+  return with_dtype(dtype, [&](auto dt) {
+    return with_dim(D, [&](auto d) {
+      return with_group(G, [&](auto g) {
+        using DT = decltype(dt);
+        constexpr int DD = decltype(d)::value, GG = decltype(g)::value;
+        if constexpr (!std::is_same_v<DT, F32> && GG >= 2) {
+          hipLaunchKernelGGL((select_attn_mfma_kernel<DT, DD, GG, 4>), grid, dim3(NT), 0, stream,
+                             scores, K, sink, local, sel, sel_count, q, k_cache, v_cache,
+                             block_table, seq_lens, Hq, Hkv, maxN, S, qscale, part_o, part_m,
+                             part_l);
+          return hipGetLastError();
+        } else {
+          return hipErrorInvalidValue;
+        }
+      });
+    });
+  });
 }
 
 }  // namespace kvd

@@ -149,8 +149,29 @@ inline int cu_count() {
 
 inline int device_cu_count() { return cu_count(); }
 
-// Largest maxN the Top-K kernel keeps in registers (1024 threads x 32 keys).
+// Largest maxN of the Top-K (1024 threads x 64 keys; past 32 keys per thread
+// part of them live in scratch memory).
 constexpr int kTopkMaxBlocks = 65536;
+
+// Top-K + sparse attention in one launch: waves (= splits) per workgroup, the
+// list positions a workgroup keeps in LDS, and the longest row it takes (every
+// workgroup of a row repeats the row's Top-K; past 2048 blocks that costs more
+// than the Top-K launch it saves).
+constexpr int kSelAttnWaves = 8;
+constexpr int kSelAttnListMax = 2048;
+constexpr int kSelAttnMaxBlocks = 2048;
+
+// Whether launch_select_attn takes this call (16-bit keys, G >= 2, maxN <=
+// kSelAttnMaxBlocks, the workgroup's share of the list fits in LDS); other
+// calls run the Top-K and attention launches, with the same results.
+bool select_attn_fusable(int dtype, int G, int maxN, int K, int S);
+
+hipError_t launch_select_attn(int dtype, int D, int G, const float* scores, int K, int sink,
+                              int local, int32_t* sel, int32_t* sel_count, const void* q,
+                              const void* k_cache, const void* v_cache,
+                              const int32_t* block_table, const int32_t* seq_lens, int B, int Hq,
+                              int Hkv, int maxN, int S, float scale, float* part_o, float* part_m,
+                              float* part_l, hipStream_t stream);
 
 
 }  // namespace kvd

@@ -27,9 +27,10 @@ DTYPE_CODES = {"f32": KV_F32, "f16": KV_F16, "bf16": KV_BF16}
 # every symbol the header declares
 EXPORTS = (
     "kv_block_meta_build", "kv_block_mean_build", "kv_append_token", "kv_decode_select",
+    "kv_decode_score", "kv_select_decode_attn",
     "kv_score_topk_workspace_size", "kv_block_score_topk", "kv_max_forced_blocks",
     "kv_block_select", "kv_block_select_no_alloc", "kv_auto_num_splits",
-    "kv_auto_num_splits_fp8",
+    "kv_auto_select_splits", "kv_auto_num_splits_fp8",
     "kv_auto_num_splits_tiered", "kv_paged_decode_attn", "kv_decode_combine",
     "kv_quantize_pages_fp8", "kv_paged_decode_attn_fp8", "kv_quantize_pages_int4",
     "kv_paged_decode_attn_int4", "kv_paged_decode_attn_tiered",
@@ -92,10 +93,14 @@ def _load() -> ctypes.CDLL:
         "kv_decode_select": (I32, [S, I32, P, P, P, P, P, P, P, P, P, I32, I32, I32, P, P, P, P,
                                    SZ, P]),
         "kv_block_select": (I32, [S, I32, P, P, P, P, I32, I32, I32, P, P, P, P, SZ, P]),
+        "kv_decode_score": (I32, [S, I32, P, P, P, P, P, P, P, P, P, P, P]),
+        "kv_select_decode_attn": (I32, [S, P, P, P, I32, I32, I32, P, P, P, F, I32, P, P, P, P, P,
+                                        P]),
         "kv_block_select_no_alloc": (I32, [S, I32, P, P, P, P, I32, I32, I32, P, P, P]),
         "kv_score_topk_workspace_size": (SZ, [S, I32]),
         "kv_block_score_topk": (I32, [S, P, P, P, P, I32, P, P, P, P, SZ, P]),
         "kv_auto_num_splits": (I32, [S, I32]),
+        "kv_auto_select_splits": (I32, [S, I32]),
         "kv_auto_num_splits_fp8": (I32, [S, I32]),
         "kv_auto_num_splits_tiered": (I32, [S, I32]),
         "kv_paged_decode_attn": (I32, [S, P, P, P, P, P, P, P, I32, F, I32, P, P, P, P]),
@@ -267,6 +272,38 @@ def kv_decode_select(shape: KVShape, index_kind: int, q: Buf, k_new: Buf, v_new:
                                  _stream(stream)))
 
 
+def kv_decode_score(shape: KVShape, index_kind: int, q: Buf, k_new: Buf, v_new: Buf,
+                    block_table: Buf, seq_lens: Buf, k_cache: Buf, v_cache: Buf, kmeta: Buf,
+                    kmean: Buf, scores_out: Buf, stream=None) -> None:
+    L = _Lay(shape)
+    _check(_lib.kv_decode_score(ctypes.byref(shape), index_kind, _p(q, L.q, "q"),
+                                _p(k_new, L.token, "k_new"), _p(v_new, L.token, "v_new"),
+                                _p(block_table, L.table, "block_table", True),
+                                _p(seq_lens, L.lens, "seq_lens", True),
+                                _p(k_cache, L.pool, "k_cache"), _p(v_cache, L.pool, "v_cache"),
+                                _p(kmeta, L.kmeta, "kmeta"), _p(kmean, L.kmean, "kmean"),
+                                _p(scores_out, L.scores, "scores_out"), _stream(stream)))
+
+
+def kv_select_decode_attn(shape: KVShape, scores: Buf, block_table: Buf, seq_lens: Buf,
+                          topk_blocks: int, sink_tokens: int, local_tokens: int, q: Buf,
+                          k_cache: Buf, v_cache: Buf, scale: float, num_splits: int,
+                          sel_blocks: Buf, sel_count: Buf, part_o: Buf, part_m: Buf,
+                          part_l: Buf, stream=None) -> None:
+    L = _Lay(shape)
+    po, pm = L.parts(num_splits)
+    _check(_lib.kv_select_decode_attn(ctypes.byref(shape), _p(scores, L.scores, "scores"),
+                                      _p(block_table, L.table, "block_table", True),
+                                      _p(seq_lens, L.lens, "seq_lens", True), topk_blocks,
+                                      sink_tokens, local_tokens, _p(q, L.q, "q"),
+                                      _p(k_cache, L.pool, "k_cache"),
+                                      _p(v_cache, L.pool, "v_cache"), scale, num_splits,
+                                      _p(sel_blocks, L.sel(topk_blocks), "sel_blocks", True),
+                                      _p(sel_count, L.rows, "sel_count", True),
+                                      _p(part_o, po, "part_o"), _p(part_m, pm, "part_m"),
+                                      _p(part_l, pm, "part_l"), _stream(stream)))
+
+
 def kv_score_topk_workspace_size(shape: KVShape, topk_blocks: int) -> int:
     return int(_lib.kv_score_topk_workspace_size(ctypes.byref(shape), topk_blocks))
 
@@ -331,6 +368,10 @@ def kv_block_select_no_alloc(shape: KVShape, index_kind: int, q: Buf, index: Buf
 
 def kv_auto_num_splits(shape: KVShape, blocks_per_unit: int) -> int:
     return int(_lib.kv_auto_num_splits(ctypes.byref(shape), blocks_per_unit))
+
+
+def kv_auto_select_splits(shape: KVShape, topk_blocks: int) -> int:
+    return int(_lib.kv_auto_select_splits(ctypes.byref(shape), topk_blocks))
 
 
 def kv_paged_decode_attn(shape: KVShape, q: Buf, k_cache: Buf, v_cache: Buf, block_table: Buf,

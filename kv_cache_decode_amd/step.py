@@ -184,6 +184,27 @@ class DeviceWorkload:
                             self.kmeta if meta else None, self.kmean, k, sink_tokens,
                             local_tokens, self.scores, self.sel, self.sel_count, None, 0, stream)
 
+    def decode_score(self, index: str = "minmax", k_new=None, v_new=None, meta: bool = True,
+                     stream=None):
+        """kv_decode_score: append (as append()) and the scores of select(), no Top-K."""
+        kind = kd.KV_INDEX_MEAN if index == "mean" else kd.KV_INDEX_MINMAX
+        kd.kv_decode_score(self.shape, kind, self.q, self.last_k if k_new is None else k_new,
+                           self.last_v if v_new is None else v_new, self.block_table,
+                           self.seq_lens, self.k_cache, self.v_cache,
+                           self.kmeta if meta else None, self.kmean, self.scores, stream)
+
+    def select_attention(self, k: int, num_splits: Optional[int] = None, sink_tokens: int = 0,
+                         local_tokens: int = 0, stream=None):
+        """kv_select_decode_attn over self.scores: the Top-K (to self.sel /
+        self.sel_count) and the sparse attention partials, in one call."""
+        self._sel_buffers(k)
+        S = num_splits or kd.kv_auto_select_splits(self.shape, k)
+        po, pm, pl = self.partials(S)
+        kd.kv_select_decode_attn(self.shape, self.scores, self.block_table, self.seq_lens, k,
+                                 sink_tokens, local_tokens, self.q, self.k_cache, self.v_cache,
+                                 self.scale, S, self.sel, self.sel_count, po, pm, pl, stream)
+        return S
+
     def attention(self, sparse: bool, num_splits: Optional[int] = None, stream=None):
         S = num_splits or self.auto_splits(sparse)
         po, pm, pl = self.partials(S)

@@ -180,6 +180,28 @@ def test_auto_splits_bounds():
     assert kd.kv_auto_num_splits(host, 256) <= 256 // 8
 
 
+def test_auto_select_splits():
+    """One eight-split workgroup per compute unit (256 here, the MI355X count the
+    library assumes without a device) where kv_select_decode_attn is one launch;
+    the attention rule elsewhere."""
+    s32k = shape(num_seqs=4, num_kv_heads=8, num_q_heads=32, max_blocks_per_seq=2048,
+                 num_pages=8192)
+    assert kd.kv_auto_select_splits(s32k, 128) == 64          # 32 rows -> 8 workgroups each
+    assert kd.kv_auto_select_splits(s32k, 20) == 24           # at most 8 * ceil(K / 8)
+    two = shape(num_seqs=2, num_kv_heads=8, num_q_heads=32, max_blocks_per_seq=2048,
+                num_pages=4096)
+    assert kd.kv_auto_select_splits(two, 128) == 128
+    many = shape(num_seqs=64, num_kv_heads=8, num_q_heads=32, max_blocks_per_seq=64,
+                 num_pages=4096)
+    assert kd.kv_auto_select_splits(many, 16) == 8            # at least one workgroup
+    for off in (dict(max_blocks_per_seq=8192, num_pages=8192),   # rows too long to fuse
+                dict(dtype="f32"), dict(num_q_heads=8)):          # vector path
+        o = shape(**{**dict(num_seqs=1, num_kv_heads=8, num_q_heads=32, max_blocks_per_seq=2048,
+                            num_pages=2048), **off})
+        assert kd.kv_auto_select_splits(o, 256) == kd.kv_auto_num_splits(o, 256)
+    assert kd.kv_auto_select_splits(s32k, 0) == 1
+
+
 def test_one_hip_runtime_per_process():
     """The binding loads after torch, so only torch's HIP runtime is mapped."""
     import torch  # noqa: F401
