@@ -11,12 +11,15 @@ One step = one pass over every stage of the path on that input:
 The metric is KV GB/s (algorithmic bytes of the step / step time, and the same
 per stage) and decode steps/s; the dominant kernel (dense attention) is also
 reported against the 8 TB/s HBM peak.  Inputs are resident in HBM before the
-timed region.  Four copies of the workload are rotated so that no step can be
-served from the 256 MB last-level cache by the step before it.
+timed region.  Twelve copies of the workload are rotated, and every HIP graph
+steps through each copy once, so no step is served from the 256 MB last-level
+cache by the steps before it (a sparse decode step reads ~53 MB at 128k: twelve
+copies hold ~640 MB).
 
 Also in the same run: the zero-copy variant (K/V pools in mapped pinned host
 memory; its roofline is the measured host-to-device copy bandwidth), and the
-fp64 oracle timed on the host cores on the same workload (cpu_baseline).
+fp64 oracle timed on the host cores on every named workload (cpu_baseline; its
+value is the 128k workload's).
 
 The dominant kernel is also reported against two read ceilings measured in the
 same run by kernels that compute nothing: a plain stream read of 1 GiB, and
@@ -46,8 +49,9 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBPS = 8000.0
-GRAPH_STEPS = 8          # decode steps captured per HIP graph (cycling over the copies)
-GRAPH_MIN_REPLAYS = 25   # decode-step figures: median over >= 25 x 8 = 200 timed steps
+GRAPH_STEPS = 8          # fewest decode steps captured per HIP graph (each graph steps
+                         # through every workload copy once, so len(copies) when larger)
+GRAPH_MIN_REPLAYS = 25   # decode-step figures: median over >= 25 replays (>= 200 timed steps)
 GRAPH_WARM_REPLAYS = 3   # ... after >= 24 untimed ones
 STREAM_PROBE_BYTES = 1 << 30
 WORKLOAD = "llama3.1_8b_gqa_b1_128k_bf16"
@@ -156,9 +160,9 @@ def measured_traffic():
 # ---------------------------------------------------------------- GPU part
 
 def graph_step_us(fn, copies, args):
-    """Time per step of fn, replayed from one HIP graph that holds GRAPH_STEPS
-    steps cycling over the workload copies (one host launch per GRAPH_STEPS
-    steps, so a short step is not timed at the host's graph launch rate): the
+    """Time per step of fn, replayed from one HIP graph that holds one step per
+    workload copy (at least GRAPH_STEPS; one host launch per graph, so a short
+    step is not timed at the host's graph launch rate): the
     median over at least GRAPH_MIN_REPLAYS replays, each bracketed by its own
     events.  Raises RuntimeError where a call cannot be captured."""
     import torch
@@ -168,12 +172,13 @@ def graph_step_us(fn, copies, args):
         for c in copies:
             fn(c)
     torch.cuda.current_stream().wait_stream(side)
+    steps = max(GRAPH_STEPS, len(copies))
     g_ = torch.cuda.CUDAGraph()
     with torch.cuda.graph(g_):
-        for i in range(GRAPH_STEPS):
+        for i in range(steps):
             fn(copies[i % len(copies)])
-    reps = max(GRAPH_MIN_REPLAYS, args.steps // GRAPH_STEPS)
-    for _ in range(max(GRAPH_WARM_REPLAYS, args.warmup // GRAPH_STEPS)):
+    reps = max(GRAPH_MIN_REPLAYS, args.steps // steps)
+    for _ in range(max(GRAPH_WARM_REPLAYS, args.warmup // steps)):
         g_.replay()
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
           for _ in range(reps)]
@@ -184,7 +189,7 @@ def graph_step_us(fn, copies, args):
         b.record()
     torch.cuda.synchronize()
     del g_
-    return float(np.median([a.elapsed_time(b) for a, b in ev])) * 1e3 / GRAPH_STEPS
+    return float(np.median([a.elapsed_time(b) for a, b in ev])) * 1e3 / steps
 
 
 def run_gpu(args, spec, data):
@@ -199,6 +204,7 @@ def run_gpu(args, spec, data):
     torch.cuda.synchronize()
     from kv_cache_decode_amd import kvdecode as kd
     s_sparse = kd.kv_auto_num_splits(copies[0].shape, k)
+    s_sel = kd.kv_auto_select_splits(copies[0].shape, k)
     s_dense = kd.kv_auto_num_splits(copies[0].shape, spec.max_blocks)
     stages = ["meta_build", "append_select", "sparse_attn", "sparse_combine", "dense_attn",
               "dense_combine"]
@@ -238,7 +244,7 @@ def run_gpu(args, spec, data):
             ms_, _ = time_loop(lambda i: fn(copies[i % len(copies)]))
             return ms_ * 1e3 / args.steps
 
-    res = {"s_sparse": s_sparse, "s_dense": s_dense}
+    res = {"s_sparse": s_sparse, "s_sel": s_sel, "s_dense": s_dense}
     if not args.only_variants:
         for i in range(args.warmup):
             step(copies[i % len(copies)])
@@ -264,10 +270,10 @@ def run_gpu(args, spec, data):
 
         ceilings = time_read_ceilings(copies, s_dense, time_loop, args.steps)
 
-        # whole-step timing: HIP graphs of GRAPH_STEPS consecutive steps cycling
+        # whole-step timing: HIP graphs of one step per copy (>= GRAPH_STEPS) cycling
         # over the workload copies (so each graph launch's fixed cost of a few us
         # is spread over several steps, as a decode loop that captures its
-        # layers would), replayed args.steps // GRAPH_STEPS times, plus one graph
+        # layers would), replayed args.steps // per times, plus one graph
         # of the remaining steps: exactly args.steps steps between the events
         launch = "hip_graph"
         try:
@@ -285,7 +291,7 @@ def run_gpu(args, spec, data):
                         step(copies[i % len(copies)])
                 return g
 
-            per = GRAPH_STEPS
+            per = max(GRAPH_STEPS, len(copies))
             full_g = capture(per)
             tail = args.steps % per
             tail_g = capture(tail) if tail else None
@@ -305,10 +311,17 @@ def run_gpu(args, spec, data):
             launch = "eager"
             total_ms, wall = time_loop(lambda i: step(copies[i % len(copies)]))
         # the per-token decode steps on their own, each one HIP graph per copy:
-        # sparse = append + score/Top-K (one call) + sparse attention + merge,
-        # dense  = append + dense attention + merge; and the sparse step with
-        # the append, score and Top-K as three separate calls, for comparison
+        # sparse = append + score (one call), Top-K + sparse attention (one
+        #          call: one launch for rows of <= 2048 blocks, else two) + merge,
+        # dense  = append + dense attention + merge; and for comparison the
+        # sparse step as append + score + Top-K (one call), sparse attention,
+        # merge, and with the append, score and Top-K as three separate calls
         def decode_sparse(c):
+            c.decode_score()
+            c.select_attention(k, s_sel)
+            c.combine(s_sel)
+
+        def decode_sparse_select(c):
             c.decode_select(k)
             c.attention(sparse=True, num_splits=s_sparse)
             c.combine(s_sparse)
@@ -325,11 +338,14 @@ def run_gpu(args, spec, data):
             c.combine(s_dense)
 
         decode_us = {"sparse": graph_us(decode_sparse), "dense": graph_us(decode_dense),
+                     "sparse_decode_select": graph_us(decode_sparse_select),
                      "sparse_unfused": graph_us(decode_sparse_unfused)}
+        dense_graph_us = graph_us(lambda c: c.attention(sparse=False, num_splits=s_dense))
         res.update({
             "total_ms": total_ms, "wall_s": wall, "stage_ms": per_stage_ms,
             "decode_us": decode_us, "launch": launch,
             "dense_attn_loop_us": dense_loop_ms * 1e3 / args.steps,
+            "dense_attn_graph_us": dense_graph_us,
             "ceilings": ceilings,
             "eager_ms_per_step": eager_ms / args.steps,
         })
@@ -484,7 +500,7 @@ def time_variants(args, copies, k, s_sparse, time_loop, graph_us):
     return variants
 
 
-def run_other_workload(args, name):
+def run_other_workload(args, name, cpu_out=None):
     """Kernel-level figures of another named workload (steps replayed from HIP
     graphs over rotated copies): dense attention GB/s, and the sparse decode
     path."""
@@ -513,8 +529,24 @@ def run_other_workload(args, name):
             torch.cuda.synchronize()
             return t0.elapsed_time(t1) * 1e3 / reps
 
+    def eager(fn):
+        """Back-to-back launches between two events on the launch stream: the
+        timer of the headline roofline, so every workload's dense figure is
+        taken the same way."""
+        for i in range(4):
+            fn(copies[i % len(copies)])
+        torch.cuda.synchronize()
+        t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        t0.record()
+        for i in range(args.steps):
+            fn(copies[i % len(copies)])
+        t1.record()
+        torch.cuda.synchronize()
+        return t0.elapsed_time(t1) * 1e3 / args.steps
+
     s_dense = kd.kv_auto_num_splits(copies[0].shape, spec.max_blocks)
-    dense_us = loop(lambda c: c.attention(sparse=False, num_splits=s_dense))
+    dense_us = eager(lambda c: c.attention(sparse=False, num_splits=s_dense))
+    dense_graph_us = loop(lambda c: c.attention(sparse=False, num_splits=s_dense))
     k = spec.topk_blocks
     s_sp = kd.kv_auto_num_splits(copies[0].shape, k) if k else 1
     sb = stage_bytes(spec, k or 1, s_sp, s_dense)
@@ -522,6 +554,9 @@ def run_other_workload(args, name):
     dense_comb_us = loop(lambda c: c.combine(s_dense))
     res = {"dense_attn_us": dense_us, "dense_attn_gbps": gbps("dense_attn", dense_us),
            "dense_frac_of_hbm_peak": gbps("dense_attn", dense_us) / HBM_PEAK_GBPS,
+           "dense_attn_timing": f"{args.steps} back-to-back launches between two HIP events "
+                                f"over {len(copies)} rotated copies",
+           "dense_attn_graph_us": dense_graph_us,
            "dense_combine_us": dense_comb_us,
            "dense_combine_gbps": gbps("dense_combine", dense_comb_us),
            "splits_dense": s_dense, "dtype": spec.dtype, "group": spec.group}
@@ -533,10 +568,16 @@ def run_other_workload(args, name):
         res["score_topk_us"] = loop(lambda c: c.score_topk(k))
         res["sparse_attn_us"] = loop(lambda c: c.attention(sparse=True, num_splits=s_sp))
         res["sparse_combine_us"] = loop(lambda c: c.combine(s_sp))
-        res["sparse_decode_us"] = loop(lambda c: (c.decode_select(k),
-                                                  c.decode(sparse=True, num_splits=s_sp)))
+        s_sel = kd.kv_auto_select_splits(copies[0].shape, k)
+        # the sparse decode step as in the headline record: append + score, Top-K
+        # + sparse attention, merge; and as append + score + Top-K, attention, merge
+        res["sparse_decode_us"] = loop(lambda c: (c.decode_score(), c.select_attention(k, s_sel),
+                                                  c.combine(s_sel)))
         res["sparse_decode_steps_per_s"] = 1e6 / res["sparse_decode_us"]
+        res["sparse_decode_select_us"] = loop(lambda c: (c.decode_select(k),
+                                                         c.decode(sparse=True, num_splits=s_sp)))
         res["splits_sparse"] = s_sp
+        res["splits_select"] = s_sel
         res["stage_gbps"] = {name: gbps(name, res[f"{name}_us"])
                              for name in ("meta_build", "score_topk", "sparse_attn",
                                           "sparse_combine")}
@@ -547,6 +588,9 @@ def run_other_workload(args, name):
         c.close()
     del copies
     torch.cuda.empty_cache()
+    if cpu_out is not None:            # the oracle on the same arrays
+        log(f"[bench] oracle on {name}")
+        cpu_out[name] = oracle_steps(spec, data, CPU_STAGES[name], 3, args.cpu_seconds_other)
     return res
 
 
@@ -831,16 +875,26 @@ def cpu_model() -> str:
     return "unknown"
 
 
-def run_cpu_baseline(spec, data, step_bytes: int, min_reps: int, budget_s: float):
-    """The fp64 oracle on the host cores: whole steps of the timed workload
-    (meta build, Quest scores, Top-K, sparse and dense attention), at least
-    min_reps of them and more until about budget_s seconds have been spent;
-    each stage timed on its own within the step, medians reported."""
+# the stages of each named workload's oracle step (its configuration's list:
+# the OPT-shaped batch is a dense configuration, the host-KV one a sparse step)
+CPU_STAGES = {
+    "tiny_mha_d64_1k_f32": ("meta_build", "score_topk", "sparse_attn", "dense_attn"),
+    "opt6.7b_mha_b32_544_f16": ("dense_attn",),
+    "llama3.1_8b_gqa_b4_32k_bf16": ("meta_build", "score_topk", "sparse_attn", "dense_attn"),
+    WORKLOAD: ("meta_build", "score_topk", "sparse_attn", "dense_attn"),
+    HOSTKV_WORKLOAD: ("meta_build", "score_topk", "sparse_attn"),
+}
+
+
+def oracle_steps(spec, data, stages, min_reps: int, budget_s: float) -> dict:
+    """The fp64 oracle on the host cores: whole steps of one workload (the given
+    stages in order), at least min_reps of them and more until about budget_s
+    seconds have been spent; each stage timed on its own, medians reported."""
     import oracle
 
     q, kp, vp = data.q64(), data.k64(), data.v64()
     bt, sl = data.block_table, data.seq_lens
-    bs, k = spec.block_size, spec.topk_blocks
+    bs, k = spec.block_size, spec.topk_blocks or 1
     ids, val = [], []
     for b in range(spec.num_seqs):
         for n in range(spec.blocks(b)):
@@ -848,39 +902,81 @@ def run_cpu_baseline(spec, data, step_bytes: int, min_reps: int, budget_s: float
             val.append(min(bs, spec.seq_lens[b] - n * bs))
     ids, val = np.array(ids, np.int32), np.array(val, np.int32)
     scale = 1.0 / np.sqrt(spec.head_dim)
-    stages = {"meta_build": [], "score_topk": [], "sparse_attn": [], "dense_attn": []}
+    times = {st: [] for st in stages}
     steps = []
     start = time.perf_counter()
     while len(steps) < min_reps or (time.perf_counter() - start < budget_s and len(steps) < 200):
-        t0 = time.perf_counter()
-        km = oracle.block_meta(kp, ids, val)
-        t1 = time.perf_counter()
-        hs = oracle.head_scores(q, km, bt, sl, bs)
-        gs = oracle.group_scores(hs, spec.num_kv_heads)
-        sel, cnt = oracle.topk(gs, sl, bs, k)
-        t2 = time.perf_counter()
-        oracle.attention(q, kp, vp, bt, sl, scale, sel, cnt)
-        t3 = time.perf_counter()
-        oracle.attention(q, kp, vp, bt, sl, scale)
-        t4 = time.perf_counter()
-        for name, dt in zip(stages, (t1 - t0, t2 - t1, t3 - t2, t4 - t3)):
-            stages[name].append(dt)
-        steps.append(t4 - t0)
+        km = sel = cnt = None
+        t_step = 0.0
+        for st in stages:
+            t0 = time.perf_counter()
+            if st == "meta_build":
+                km = oracle.block_meta(kp, ids, val)
+            elif st == "score_topk":
+                hs = oracle.head_scores(q, km, bt, sl, bs)
+                sel, cnt = oracle.topk(oracle.group_scores(hs, spec.num_kv_heads), sl, bs, k)
+            elif st == "sparse_attn":
+                oracle.attention(q, kp, vp, bt, sl, scale, sel, cnt)
+            else:
+                oracle.attention(q, kp, vp, bt, sl, scale)
+            dt = time.perf_counter() - t0
+            times[st].append(dt)
+            t_step += dt
+        steps.append(t_step)
     t = float(np.median(steps))
     sb = stage_bytes(spec, k, 1, 1)
-    stage_s = {name: float(np.median(v)) for name, v in stages.items()}
+    step_bytes = sum(sb[st] for st in stages)
+    stage_s = {st: float(np.median(v)) for st, v in times.items()}
     return {
-        "value": step_bytes / t / 1e9,
+        "stages": list(stages),
+        "step_s": t,
+        "steps_per_s": 1.0 / t,
+        "gbps": step_bytes / t / 1e9,
+        "step_bytes": step_bytes,
+        "steps_timed": len(steps),
+        "seconds": float(sum(steps)),
+        "stage_s": stage_s,
+        "stage_gbps": {st: sb[st] / v / 1e9 for st, v in stage_s.items()},
+    }
+
+
+def run_cpu_baseline(args, spec, data, other_cpu=None) -> dict:
+    """The oracle timed on every named workload; `value` is the 128k step's GB/s
+    on the same algorithmic-byte definition as the GPU figures.  other_cpu:
+    figures already taken on workloads generated for the GPU legs."""
+    import oracle
+    from kv_cache_decode_amd import workload as wl
+
+    per = dict(other_cpu or {})
+    for name, stages in CPU_STAGES.items():
+        if name in per:
+            continue
+        log(f"[bench] oracle on {name}")
+        if name == WORKLOAD:
+            per[name] = oracle_steps(spec, data, stages, args.cpu_reps, args.cpu_seconds)
+        elif name == HOSTKV_WORKLOAD:
+            # the same shapes as the 128k workload (only the seed differs) and the
+            # oracle reads host memory either way: its step over the 128k arrays
+            per[name] = oracle_steps(spec, data, stages, 3, args.cpu_seconds_other)
+            per[name]["arrays"] = f"{spec.name} (same shapes)"
+        else:
+            other = wl.WORKLOADS[name]
+            per[name] = oracle_steps(other, wl.generate(other), stages, 3, args.cpu_seconds_other)
+    main = per[WORKLOAD]
+    return {
+        "value": main["gbps"],
         "unit": "GB/s",
         "cores": oracle.num_threads(),
         "kind": "oracle",
-        "sample": f"{len(steps)} full steps of {spec.name} (meta build, scores, Top-K, sparse "
-                  f"and dense attention; the append is not part of the oracle step) in fp64, "
-                  f"{sum(steps):.1f} s in all; median step {t:.3f} s",
-        "step_s": t,
-        "steps_per_s": 1.0 / t,
-        "stage_s": stage_s,
-        "stage_gbps": {name: sb[name] / v / 1e9 for name, v in stage_s.items()},
+        "sample": f"{main['steps_timed']} full steps of {spec.name} (meta build, scores, Top-K, "
+                  f"sparse and dense attention; the append and the merges are not part of the "
+                  f"oracle step) in fp64, {main['seconds']:.1f} s in all; median step "
+                  f"{main['step_s']:.3f} s; the other workloads' steps in per_config",
+        "step_s": main["step_s"],
+        "steps_per_s": main["steps_per_s"],
+        "stage_s": main["stage_s"],
+        "stage_gbps": main["stage_gbps"],
+        "per_config": per,
         "host": {"cpu_model": cpu_model(), "logical_cpus": os.cpu_count(),
                  "affinity": len(os.sched_getaffinity(0))},
     }
@@ -962,11 +1058,15 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--copies", type=int, default=4)
+    ap.add_argument("--copies", type=int, default=12,
+                    help="workload copies rotated by the timed loops and graphs")
     ap.add_argument("--zc-reps", type=int, default=5)
     ap.add_argument("--cpu-reps", type=int, default=5, help="fewest oracle steps timed")
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
-                    help="oracle steps are added until about this much host time is spent")
+                    help="oracle steps of the 128k workload are added until about this much "
+                         "host time is spent")
+    ap.add_argument("--cpu-seconds-other", type=float, default=4.0,
+                    help="the same for each other named workload")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-zero-copy", action="store_true")
     ap.add_argument("--no-other-workloads", action="store_true")
@@ -1020,6 +1120,7 @@ def main():
     sb = {s_: sb_all[s_] for s_ in ("meta_build", "sparse_attn", "sparse_combine", "dense_attn",
                                     "dense_combine")}
     sb["append_select"] = sb_all["append"] + sb_all["score_topk"]
+    sb_sel = stage_bytes(spec, spec.topk_blocks, g["s_sel"], g["s_dense"])
     step_bytes = int(sum(sb.values()))
     ms = g["total_ms"] / args.steps
     st = g["stage_ms"]
@@ -1029,11 +1130,11 @@ def main():
     dense_gbps = sb["dense_attn"] / (dense_us * 1e-6) / 1e9
     traffic = measured_traffic()
 
-    others = {}
+    others, other_cpu = {}, ({} if not args.no_cpu_baseline else None)
     if not args.no_other_workloads:
         for name in OTHER_WORKLOADS:
             log(f"[bench] {name}")
-            others[name] = run_other_workload(args, name)
+            others[name] = run_other_workload(args, name, other_cpu)
 
     zc = None
     if not args.no_zero_copy:
@@ -1042,7 +1143,7 @@ def main():
     cpu = None
     if not args.no_cpu_baseline:
         log("[bench] CPU baseline (oracle)")
-        cpu = run_cpu_baseline(spec, data, step_bytes, args.cpu_reps, args.cpu_seconds)
+        cpu = run_cpu_baseline(args, spec, data, other_cpu)
 
     rec = {
         "metric": "KV GB/s streamed by decode attention (% of HBM peak) + decode steps/sec",
@@ -1055,7 +1156,7 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "f32",
+        "dtype": "bf16",
         "arithmetic": "K/V and q in their bf16 storage type as matrix-core operands (products "
                       "exact in fp32); fp32 sums, softmax, Quest scores and merge",
         "data": "synthetic",
@@ -1069,20 +1170,31 @@ def main():
                     "attn + combine + dense attn + combine",
             "launch": g["launch"],
             "step_timing": f"all timed steps between two events, as replays of HIP graphs of "
-                           f"{GRAPH_STEPS} steps cycling over the workload copies",
+                           f"{max(GRAPH_STEPS, args.copies)} steps cycling over the "
+                           f"{args.copies} workload copies",
         },
         "eager_ms_per_step": g["eager_ms_per_step"],
         "frac_of_hbm_peak": step_bytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBPS,
         # one decode step of this layer, timed on its own as a HIP graph replay
         "decode_steps_per_s": {"sparse": 1e6 / g["decode_us"]["sparse"],
                                "dense": 1e6 / g["decode_us"]["dense"],
+                               "sparse_decode_select": 1e6 / g["decode_us"]["sparse_decode_select"],
                                "sparse_unfused": 1e6 / g["decode_us"]["sparse_unfused"],
                                "full_step": 1e3 / ms},
         "decode_step_us": g["decode_us"],
+        "decode_step_calls": {
+            "sparse": "kv_decode_score + kv_select_decode_attn + kv_decode_combine "
+                      f"({g['s_sel']} splits)",
+            "sparse_decode_select": "kv_decode_select + kv_paged_decode_attn + kv_decode_combine "
+                                    f"({g['s_sparse']} splits)",
+            "sparse_unfused": "kv_append_token + kv_block_score_topk + kv_paged_decode_attn + "
+                              "kv_decode_combine",
+            "dense": "kv_append_token + kv_paged_decode_attn + kv_decode_combine"},
         "decode_step_timing": f"median per step over >= {GRAPH_MIN_REPLAYS} replays of a "
-                              f"{GRAPH_STEPS}-step HIP graph, each between its own events",
+                              f"{max(GRAPH_STEPS, args.copies)}-step HIP graph over "
+                              f"{args.copies} workload copies, each between its own events",
         "decode_step_gbps": {
-            "sparse": (sb["append_select"] + sb["sparse_attn"] + sb["sparse_combine"])
+            "sparse": (sb["append_select"] + sb_sel["sparse_attn"] + sb_sel["sparse_combine"])
                       / (g["decode_us"]["sparse"] * 1e-6) / 1e9,
             "dense": (sb_all["append"] + sb["dense_attn"] + sb["dense_combine"])
                      / (g["decode_us"]["dense"] * 1e-6) / 1e9},
@@ -1091,7 +1203,7 @@ def main():
         "stage_us": stage_us,
         "stage_gbps": stage_gbps,
         "roofline": {
-            "kernel": "paged_attn_kernel (dense)",
+            "kernel": "paged_attn_mfma_kernel (dense)",
             "bound": "hbm",
             "achieved": dense_gbps,
             "peak": HBM_PEAK_GBPS,
@@ -1101,6 +1213,7 @@ def main():
             "algorithmic_bytes_per_launch": sb["dense_attn"],
             "avg_launch_us": dense_us,
             "timing": f"{args.steps} back-to-back launches between two HIP events",
+            "avg_launch_us_graph": g["dense_attn_graph_us"],
             # measured in the same run by kernels that read and compute nothing
             "read_ceilings": g["ceilings"],
             "frac_of_stream_read": dense_gbps / g["ceilings"]["stream_read"]["gbps"],
