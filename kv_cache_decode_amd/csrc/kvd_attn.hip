@@ -32,9 +32,10 @@
 #endif
 #if KVD_MFMA_WAVES_PER_EU > 0
 #define KVD_MFMA_OCCUPANCY __attribute__((amdgpu_waves_per_eu(KVD_MFMA_WAVES_PER_EU)))
-// tiered instances carry both page paths
+// tiered instances carry both page paths; 3 waves per SIMD caps them at 168
+// VGPRs (registers go in granules of 8, so 169 would leave room for 2 waves)
 #ifndef KVD_MFMA_TIER_WAVES_PER_EU
-#define KVD_MFMA_TIER_WAVES_PER_EU 2
+#define KVD_MFMA_TIER_WAVES_PER_EU 3
 #endif
 #define KVD_MFMA_OCCUPANCY_T(cold) \
   __attribute__((amdgpu_waves_per_eu((cold) ? KVD_MFMA_TIER_WAVES_PER_EU : KVD_MFMA_WAVES_PER_EU)))
@@ -403,8 +404,8 @@ __global__ __launch_bounds__(WAVES * kWave) void paged_attn_kernel(
 //   S^T[16 tok x 16] = K[16 tok x D] . Q^T[D x 16]       v_mfma_f32_16x16x32 (D/32 steps)
 //   O[16 x D]       += P[16 x 16 tok] . V[16 tok x D]     v_mfma_f32_16x16x16 (D/16 tiles)
 //
-// with the G heads padded to the 16 MFMA rows (rows >= G are zero queries and
-// are never written out).  Lane l = 16*grp + col:
+// with the G heads padded to the 16 MFMA columns of S^T (columns >= G are zero
+// queries) and to the 16 rows of O.  Lane l = 16*grp + col:
 //   * K is the A operand read straight from the page: lane l holds token col,
 //     channels 8*(4*st + grp) .. +8 of step st;
 //   * Q^T is the B operand, loaded once: head col, the same channels;
@@ -418,10 +419,13 @@ __global__ __launch_bounds__(WAVES * kWave) void paged_attn_kernel(
 // The softmax state of head col lives in every lane of that column; the rows
 // of O are rescaled only when some head's running max grows.  P is fed to the
 // 16-bit product as a hi + lo pair (p = hi + lo exactly up to 2^-17 relative),
-// so the weights keep close to fp32 precision.
+// so the weights keep close to fp32 precision: rows h < G of P carry hi, rows
+// G + h (otherwise padding) carry lo, and the two row sums of O are added after
+// the last page, so both halves cost one product per tile.
 
 typedef _Float16 f16x4_v __attribute__((ext_vector_type(4)));
 typedef _Float16 f16x2_v __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2_v __attribute__((ext_vector_type(2)));
 typedef short s16x4_v __attribute__((ext_vector_type(4)));
 
 template <typename DT>
@@ -437,8 +441,7 @@ struct MfmaOps<BF16> {
                                                      __builtin_bit_cast(s16x4_v, b), c, 0, 0, 0);
   }
   __device__ static inline uint32_t pack(float lo, float hi) {  // round to nearest even
-    return (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)lo) |
-           ((uint32_t)__builtin_bit_cast(uint16_t, (__bf16)hi) << 16);
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2_v{lo, hi}, bf16x2_v));
   }
   __device__ static inline float lo(uint32_t w) { return __uint_as_float(w << 16); }
   __device__ static inline float hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
@@ -454,8 +457,7 @@ struct MfmaOps<F16> {
                                                  __builtin_bit_cast(f16x4_v, b), c, 0, 0, 0);
   }
   __device__ static inline uint32_t pack(float lo, float hi) {
-    return (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)lo) |
-           ((uint32_t)__builtin_bit_cast(uint16_t, (_Float16)hi) << 16);
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2_v{lo, hi}, f16x2_v));
   }
   __device__ static inline float lo(uint32_t w) {
     return (float)__builtin_bit_cast(_Float16, (uint16_t)(w & 0xffffu));
@@ -464,6 +466,33 @@ struct MfmaOps<F16> {
     return (float)__builtin_bit_cast(_Float16, (uint16_t)(w >> 16));
   }
 };
+
+// The P.V operand A of a page with P = phi + plo (the weights' 16-bit high
+// part and its rounding residue), for G heads in the 16 MFMA rows: rows h < G
+// take phi of head h (the lane's own), rows G + h the residue plo of head h,
+// moved up G lanes within each 16-lane row.  One 16x16x16 product per output
+// tile then takes both halves; rows h and G + h are added once, after the
+// split's last page (add_residue_rows).  Rows from 2G on carry finite values
+// nothing reads.
+template <int G>
+__device__ inline uint2 pv_rows_hi_lo(const uint2& phi, const uint2& plo, int col) {
+  static_assert(2 * G <= 16, "phi and plo rows share the 16 MFMA rows");
+  const uint32_t sx = dpp_u32<0x110 + G>(plo.x), sy = dpp_u32<0x110 + G>(plo.y);   // row_shr:G
+  return make_uint2(col < G ? phi.x : sx, col < G ? phi.y : sy);
+}
+// Row r of an MFMA output tile sits in element r % 4 of lane group r / 4: add
+// row G + h into row h (G = 2: the same lanes; G = 4 / 8: 16 / 32 lanes on).
+template <int G>
+__device__ inline void add_residue_rows(f32x4_v& t) {
+  static_assert(G == 2 || G == 4 || G == 8, "the dispatched group sizes");
+  if constexpr (G == 2) {
+    t[0] += t[2];
+    t[1] += t[3];
+  } else {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) t[i] += (G == 4) ? xor16(t[i]) : xor32(t[i]);
+  }
+}
 
 // Four E4M3 codes (one dword) as four 16-bit values (two dwords), exact.
 template <typename DT>
@@ -558,13 +587,18 @@ __device__ constexpr uint32_t pair_sel(int d) {
 // the channel pairs (0, 4), (1, 5), (2, 6), (3, 7): nibbles c and c + 4 sit
 // 16 bits apart, so each word is one shift and one and-or.  q's B operand
 // takes the same channel order (int4_q_order).
+// The nibbles at bits 0-3 and 16-19 of x as one word of two 16-bit operands:
+// (nibble ^ 8) | kExp in each half, as one and + xor (kExp has no bits under
+// the mask, so its or and the xor with 8 fold into one constant).
+template <typename DT>
+__device__ inline uint32_t int4_word(uint32_t x) {
+  using W = Int4Words<DT>;
+  return W::fix((x & 0x000F000Fu) ^ (W::kExp | 0x00080008u));
+}
 template <typename DT>
 __device__ inline uint4 int4_k_words(uint32_t w) {
-  const uint32_t x = w ^ 0x88888888u;
-  using W = Int4Words<DT>;
-  return make_uint4(W::fix((x & 0x000F000Fu) | W::kExp), W::fix(((x >> 4) & 0x000F000Fu) | W::kExp),
-                    W::fix(((x >> 8) & 0x000F000Fu) | W::kExp),
-                    W::fix(((x >> 12) & 0x000F000Fu) | W::kExp));
+  return make_uint4(int4_word<DT>(w), int4_word<DT>(w >> 4), int4_word<DT>(w >> 8),
+                    int4_word<DT>(w >> 12));
 }
 // Eight consecutive 16-bit q values (channel pairs (0, 1) .. (6, 7)) in the
 // order of int4_k_words.
@@ -579,17 +613,14 @@ __device__ inline uint4 int4_q_order(const uint4& q) {
 // channel 2k and vB[2k+1] channel 2k+1 of tokens (0, 1) in .x and (2, 3) in .y.
 template <typename DT, int NDW>
 __device__ inline void int4_v_operands(const uint32_t (&v)[4], uint2 (&vB)[2 * NDW]) {
-  using W = Int4Words<DT>;
-  const uint32_t x0 = v[0] ^ 0x88888888u, x1 = v[1] ^ 0x88888888u;
-  const uint32_t x2 = v[2] ^ 0x88888888u, x3 = v[3] ^ 0x88888888u;
 #pragma unroll
   for (int k = 0; k < NDW; ++k) {
-    const uint32_t t01 = __builtin_amdgcn_perm(x1, x0, pair_sel(k));
-    const uint32_t t23 = __builtin_amdgcn_perm(x3, x2, pair_sel(k));
-    vB[2 * k].x = W::fix((t01 & 0x000F000Fu) | W::kExp);
-    vB[2 * k].y = W::fix((t23 & 0x000F000Fu) | W::kExp);
-    vB[2 * k + 1].x = W::fix(((t01 >> 4) & 0x000F000Fu) | W::kExp);
-    vB[2 * k + 1].y = W::fix(((t23 >> 4) & 0x000F000Fu) | W::kExp);
+    const uint32_t t01 = __builtin_amdgcn_perm(v[1], v[0], pair_sel(k));
+    const uint32_t t23 = __builtin_amdgcn_perm(v[3], v[2], pair_sel(k));
+    vB[2 * k].x = int4_word<DT>(t01);
+    vB[2 * k].y = int4_word<DT>(t23);
+    vB[2 * k + 1].x = int4_word<DT>(t01 >> 4);
+    vB[2 * k + 1].y = int4_word<DT>(t23 >> 4);
   }
 }
 
@@ -956,10 +987,12 @@ __device__ __forceinline__ void mfma_attn_split(
       const float zs = qscale * sk;
       float z[4];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) z[i] = (4 * grp + i < valid) ? sacc[i] * zs : -INFINITY;
-      float bm = fmaxf(fmaxf(z[0], z[1]), fmaxf(z[2], z[3]));
-      bm = fmaxf(bm, xor16(bm));
-      bm = fmaxf(bm, xor32(bm));
+      for (int i = 0; i < 4; ++i) z[i] = sacc[i] * zs;
+      if (valid < kBlockSize) {   // wave-uniform: only a sequence's last page is partial
+#pragma unroll
+        for (int i = 0; i < 4; ++i) z[i] = (4 * grp + i < valid) ? z[i] : -INFINITY;
+      }
+      const float bm = rows_max(fmaxf(fmaxf(z[0], z[1]), fmaxf(z[2], z[3])));
       if (__ballot(col < G && bm > m)) {  // wave-uniform
         const float mn = fmaxf(m, bm);
         const float alpha = fast_exp2(m - mn);
@@ -967,7 +1000,7 @@ __device__ __forceinline__ void mfma_attn_split(
         lsum *= alpha;
         float ar[4];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) ar[i] = __shfl(alpha, 4 * grp + i, kWave);
+        for (int i = 0; i < 4; ++i) ar[i] = __shfl(alpha, (4 * grp + i) & (G - 1), kWave);
 #pragma unroll
         for (int n = 0; n < NT; ++n)
 #pragma unroll
@@ -1019,14 +1052,12 @@ __device__ __forceinline__ void mfma_attn_split(
       }
       // (INT4 operands of slots past the sequence end are finite and meet
       // weights of exactly 0)
+      const uint2 pa = pv_rows_hi_lo<G>(phi, plo, col);
 #pragma unroll
-      for (int n = 0; n < NT; ++n) o[n] = Ops::pv(phi, vB[n], o[n]);
-#pragma unroll
-      for (int n = 0; n < NT; ++n) o[n] = Ops::pv(plo, vB[n], o[n]);
+      for (int n = 0; n < NT; ++n) o[n] = Ops::pv(pa, vB[n], o[n]);
       if constexpr (kInt4Off) {
         const uint2 ones = make_uint2(0x3F803F80u, 0x3F803F80u);   // bf16 1.0 pairs
-        vcorr = Ops::pv(phi, ones, vcorr);
-        vcorr = Ops::pv(plo, ones, vcorr);
+        vcorr = Ops::pv(pa, ones, vcorr);
         if ((it & 7) == 7) fold_vcorr();
       }
 
@@ -1046,6 +1077,8 @@ __device__ __forceinline__ void mfma_attn_split(
   }
 
   if constexpr (kInt4Off) fold_vcorr();
+#pragma unroll
+  for (int n = 0; n < NT; ++n) add_residue_rows<G>(o[n]);
   // totals per head (the four k-groups of a column saw disjoint tokens)
   lsum += xor16(lsum);
   lsum += xor32(lsum);

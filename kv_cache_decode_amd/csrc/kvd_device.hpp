@@ -228,6 +228,20 @@ __device__ inline float xor16(float v) {
 }
 __device__ inline float xor32(float v) { return __shfl_xor(v, 32, kWave); }
 
+// Max over lanes l, l ^ 16, l ^ 32 and l ^ 48 (one lane of each 16-lane row)
+// with gfx950's row-swap permutes, which stay in the VALU (no LDS round trip):
+// permlane16_swap of a register with itself returns, per lane, its own value
+// and that of lane l ^ 16 (in one order or the other); permlane32_swap the same
+// for l ^ 32.  Every lane of the wave must be active.
+__device__ inline float rows_max(float v) {
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false,
+                                                  false);
+  v = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false,
+                                                  false);
+  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+
 struct OpSum {
   __device__ static inline float apply(float a, float b) { return a + b; }
 };
