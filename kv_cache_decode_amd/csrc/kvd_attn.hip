@@ -477,7 +477,9 @@ struct MfmaOps<F16> {
 template <int G>
 __device__ inline uint2 pv_rows_hi_lo(const uint2& phi, const uint2& plo, int col) {
   static_assert(2 * G <= 16, "phi and plo rows share the 16 MFMA rows");
-  const uint32_t sx = dpp_u32<0x110 + G>(plo.x), sy = dpp_u32<0x110 + G>(plo.y);   // row_shr:G
+  // row_shr:G; lanes col < G keep phi, so what the shift leaves there is unused
+  const uint32_t sx = (uint32_t)__builtin_amdgcn_mov_dpp((int)plo.x, 0x110 + G, 0xF, 0xF, true);
+  const uint32_t sy = (uint32_t)__builtin_amdgcn_mov_dpp((int)plo.y, 0x110 + G, 0xF, 0xF, true);
   return make_uint2(col < G ? phi.x : sx, col < G ? phi.y : sy);
 }
 // Row r of an MFMA output tile sits in element r % 4 of lane group r / 4: add
@@ -558,26 +560,6 @@ struct Int4Words<F16> {
     return __builtin_bit_cast(uint32_t, v);
   }
 };
-// Eight (or, from the low 16 bits, four) INT4 codes as 16-bit words of
-// channel pairs through fp32, exact: the tiered kernel's cold pages, where the
-// registers of the offset bookkeeping below are not to spare.
-template <typename DT>
-__device__ inline uint32_t pack16_exact(float a, float b);
-template <>
-__device__ inline uint32_t pack16_exact<BF16>(float a, float b) {
-  return __builtin_amdgcn_perm(__float_as_uint(b), __float_as_uint(a), 0x07060302u);
-}
-template <>
-__device__ inline uint32_t pack16_exact<F16>(float a, float b) {
-  return F16::pack2(a, b);
-}
-template <typename DT, int NDW>
-__device__ inline void int4_exact_words(uint32_t w, uint32_t (&r)[NDW]) {
-#pragma unroll
-  for (int k = 0; k < NDW; ++k)
-    r[k] = pack16_exact<DT>((float)int4_code(w, 2 * k), (float)int4_code(w, 2 * k + 1));
-}
-
 // perm selector: byte d of src1 into byte 0, byte d of src0 into byte 2, zeros
 // elsewhere
 __device__ constexpr uint32_t pair_sel(int d) {
@@ -637,13 +619,20 @@ __device__ inline int qk_channel(int st, int grp) {
                   : (KVQ == 4 ? D / 4 * grp + 8 * st : 8 * (4 * st + grp));
 }
 
+// The raw page registers of format F (0: 16-bit rows, 8: E4M3, 4: INT4).
+template <int F, typename R16, typename R8, typename R4>
+struct PageRegsOf {
+  using type = typename std::conditional<F == 8, R8,
+                                         typename std::conditional<F == 4, R4, R16>::type>::type;
+};
+
 // Tiered pools (COLD = 8 or 4, with KVQ = 0): page p is read from the 16-bit
 // pools when page_tier[p] == 0 (hot) and from the code pools k_cold / v_cold
-// in format COLD when page_tier[p] != 0 (cold, scales in kv_scales).  The tier
-// is uniform per page, so each page takes one branch for the whole wave.  A
-// cold page's codes sit in the first registers of the 16-bit page buffer, and
-// its K codes are read in the 16-bit layout (the 8 channels of each QK step,
-// as 4 or 8 code bytes), so both tiers share q's B operand.
+// in format COLD when page_tier[p] != 0 (cold, scales in kv_scales).  Each
+// group of 64 list positions runs its hot pages, then its cold pages, in two
+// loops, each compiled for one page format: a cold page is read and decoded
+// exactly as a code-page call reads its pages (its own lane layout, and a
+// second copy of q's B operand in that layout).
 // Split s of (sequence b, KV head j) by the calling wave: the body of
 // paged_attn_mfma_kernel, and of the fused select + attention kernel, which
 // passes its list (LDS_LIST: the list count and a pointer that indexes the
@@ -685,23 +674,31 @@ __device__ __forceinline__ void mfma_attn_split(
   const int p1 = min(p0 + chunk, n_list);
   const size_t row0 = (size_t)b * Hq + (size_t)j * G;
 
-  uint4 qB[KS];
+  // q's B operand for pages of format F (0: 16-bit rows, 8: E4M3, 4: INT4), in
+  // the channel order that format's K loads give each lane
+  using FmtP = std::integral_constant<int, KVQ>;    // the pools k_cache / v_cache
+  using FmtC = std::integral_constant<int, COLD>;   // tiered calls' cold pools
+  auto load_qB = [&](uint4 (&qb)[KS], auto fmt) {
+    constexpr int F = decltype(fmt)::value;
 #pragma unroll
-  for (int st = 0; st < KS; ++st)
-    qB[st] = col < G ? load16(static_cast<const St*>(q) + (row0 + col) * D + qk_channel<KVQ, D>(st, grp))
-                     : make_uint4(0, 0, 0, 0);
+    for (int st = 0; st < KS; ++st)
+      qb[st] = col < G ? load16(static_cast<const St*>(q) + (row0 + col) * D + qk_channel<F, D>(st, grp))
+                       : make_uint4(0, 0, 0, 0);
+    if constexpr (F == 4) {
+#pragma unroll
+      for (int st = 0; st < KS; ++st) qb[st] = int4_q_order(qb[st]);
+    }
+  };
+  uint4 qB[KS], qBc[KS];
+  load_qB(qB, FmtP{});
+  if constexpr (COLD != 0) load_qB(qBc, FmtC{});
   // bf16 INT4 pages give operands of code + 136 (Int4Words): a page's logit
-  // sums start at -136 * sum_c q_c of their head (the lane's column), and
-  // vcorr accumulates P times a row of ones (each head's summed weights)
-  // beside o, so o - 136 * vcorr is the sum over the codes.  vcorr is folded
-  // into o every eight pages, which keeps o's magnitude (and so its rounding)
-  // near that of the true sum.  (The tiered kernel decodes its cold pages
-  // exactly through fp32 instead: it has no registers to spare.)
-  if constexpr (KVQ == 4) {
-#pragma unroll
-    for (int st = 0; st < KS; ++st) qB[st] = int4_q_order(qB[st]);
-  }
-  constexpr bool kInt4Off = std::is_same<DT, BF16>::value && KVQ == 4;
+  // sums start at -136 * sum_c q_c of their head (the lane's column; the sum is
+  // the same in any channel order), and vcorr accumulates P times a row of
+  // ones (each head's summed weights) beside o, so o - 136 * vcorr is the sum
+  // over the codes.  vcorr is folded into o every eight pages, which keeps o's
+  // magnitude (and so its rounding) near that of the true sum.
+  constexpr bool kInt4Off = std::is_same<DT, BF16>::value && (KVQ == 4 || COLD == 4);
   float qcorr = 0.0f;
   if constexpr (kInt4Off) {
     float t = 0.0f;
@@ -728,12 +725,20 @@ __device__ __forceinline__ void mfma_attn_split(
     vcorr = f32x4_v{0.f, 0.f, 0.f, 0.f};
   };
 
-  // byte addressing (code pages: fewer bytes per channel)
-  constexpr int KCH = KVQ == 8 ? 16 : (KVQ == 4 ? D / 4 : 8);   // K channels a lane starts at, per grp
-  const size_t page_stride = kv_bytes<DT, KVQ>((size_t)Hkv * kBlockSize * D);
-  const size_t k_lane = kv_bytes<DT, KVQ>((size_t)j * kBlockSize * D + (size_t)col * D + KCH * grp);
-  const size_t v_lane = kv_bytes<DT, KVQ>((size_t)j * kBlockSize * D + (size_t)(4 * grp) * D +
-                                          2 * NDW * col);
+  // byte addressing per page format (code pages: fewer bytes per channel): the
+  // lane's K and V offsets inside a page of KV head j, and the page stride
+  struct Lanes {
+    size_t k, v, stride;
+  };
+  auto lanes = [&](auto fmt) {
+    constexpr int F = decltype(fmt)::value;
+    constexpr int KCH = F == 8 ? 16 : (F == 4 ? D / 4 : 8);   // K channels a lane starts at, per grp
+    return Lanes{kv_bytes<DT, F>((size_t)j * kBlockSize * D + (size_t)col * D + KCH * grp),
+                 kv_bytes<DT, F>((size_t)j * kBlockSize * D + (size_t)(4 * grp) * D + 2 * NDW * col),
+                 kv_bytes<DT, F>((size_t)Hkv * kBlockSize * D)};
+  };
+  const Lanes lp = lanes(FmtP{});
+  const size_t page_stride = lp.stride, k_lane = lp.k, v_lane = lp.v;
   const uint8_t* kb = static_cast<const uint8_t*>(k_cache) + k_lane;
   const uint8_t* vb = static_cast<const uint8_t*>(v_cache) + v_lane;
   // fused fetch: the pools a fetched block is read from, and the cache pages
@@ -742,18 +747,11 @@ __device__ __forceinline__ void mfma_attn_split(
   const uint8_t* vbp = FETCH ? static_cast<const uint8_t*>(fa.v_pool) + v_lane : nullptr;
   uint8_t* kbw = FETCH ? static_cast<uint8_t*>(const_cast<void*>(k_cache)) + k_lane : nullptr;
   uint8_t* vbw = FETCH ? static_cast<uint8_t*>(const_cast<void*>(v_cache)) + v_lane : nullptr;
-  // the cold pools of tiered calls (K in the 16-bit lane layout: channel 8*grp
-  // of step 0, steps 32 channels apart)
-  constexpr int KCHC = 8;
-  const size_t page_stride_c = kv_bytes<DT, COLD>((size_t)Hkv * kBlockSize * D);
-  const uint8_t* kbc = COLD ? static_cast<const uint8_t*>(k_cold) +
-                                  kv_bytes<DT, COLD>((size_t)j * kBlockSize * D + (size_t)col * D +
-                                                     KCHC * grp)
-                            : nullptr;
-  const uint8_t* vbc = COLD ? static_cast<const uint8_t*>(v_cold) +
-                                  kv_bytes<DT, COLD>((size_t)j * kBlockSize * D +
-                                                     (size_t)(4 * grp) * D + 2 * NDW * col)
-                            : nullptr;
+  // the cold pools of tiered calls, in the code format's own lane layout
+  const Lanes lc = lanes(FmtC{});
+  const size_t page_stride_c = lc.stride;
+  const uint8_t* kbc = COLD ? static_cast<const uint8_t*>(k_cold) + lc.k : nullptr;
+  const uint8_t* vbc = COLD ? static_cast<const uint8_t*>(v_cold) + lc.v : nullptr;
   const int32_t* sel_row = LDS_LIST ? list : (SPARSE ? sel + ((size_t)b * Hkv + j) * sel_stride : nullptr);
   const int32_t* slots_row = (SPARSE && sel_slots) ? sel_slots + ((size_t)b * Hkv + j) * sel_stride
                                                    : nullptr;
@@ -805,44 +803,16 @@ __device__ __forceinline__ void mfma_attn_split(
       uint32_t k[KS];
       uint32_t v[4];
     };
-    using PageRegs = typename std::conditional<
-        KVQ == 8, PageRegs8, typename std::conditional<KVQ == 4, PageRegs4, PageRegs16>::type>::type;
-    auto load_page = [&](PageRegs& r, int idx) {
-      if constexpr (COLD != 0) {
-        if (readlane(my_tier, idx)) {          // a cold page: codes into the first registers
-          const size_t offc = (size_t)readlane(my_page, idx) * page_stride_c;
-          if constexpr (COLD == 4) {
-#pragma unroll
-            for (int st = 0; st < KS; ++st) r.k[st].x = load4_stream(kbc + offc + 16 * st);
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-              if constexpr (NDW == 4) r.v[i].w[0] = load4_stream(vbc + offc + (size_t)i * (D / 2));
-              else r.v[i].w[0] = load2_stream(vbc + offc + (size_t)i * (D / 2));
-            }
-          } else {
-#pragma unroll
-            for (int st = 0; st < KS; ++st) {
-              const uint2 t = load8_stream(kbc + offc + 32 * st);
-              r.k[st].x = t.x;
-              r.k[st].y = t.y;
-            }
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-              if constexpr (NDW / 2 == 2) {
-                const uint2 t = load8_stream(vbc + offc + (size_t)i * D);
-                r.v[i].w[0] = t.x;
-                r.v[i].w[1] = t.y;
-              } else {
-                r.v[i].w[0] = load4_stream(vbc + offc + (size_t)i * D);
-              }
-            }
-          }
-          return;
-        }
-      }
-      const uint8_t* kb_ = kb;
-      const uint8_t* vb_ = vb;
-      size_t off = (size_t)readlane(my_page, idx) * page_stride;
+    using PageRegs = typename PageRegsOf<KVQ, PageRegs16, PageRegs8, PageRegs4>::type;
+    // fmt (std::integral_constant<int, F>): the format of page idx, known at
+    // compile time in each page loop; a tiered call's cold pages (F = COLD)
+    // come from the cold pools
+    auto load_page = [&](auto& r, int idx, auto fmt) {
+      constexpr int F = decltype(fmt)::value;
+      constexpr bool kCold = COLD != 0 && F == COLD;
+      const uint8_t* kb_ = kCold ? kbc : kb;
+      const uint8_t* vb_ = kCold ? vbc : vb;
+      size_t off = (size_t)readlane(my_page, idx) * (kCold ? page_stride_c : page_stride);
       if constexpr (FETCH) {
         const int pp = readlane(my_pool, idx);   // wave-uniform
         if (pp >= 0) {
@@ -851,7 +821,7 @@ __device__ __forceinline__ void mfma_attn_split(
           off = (size_t)pp * page_stride;
         }
       }
-      if constexpr (KVQ == 4) {
+      if constexpr (F == 4) {
         if constexpr (KS == 4) {
           const uint4 t = load16_stream(kb_ + off);
           r.k[0] = t.x; r.k[1] = t.y; r.k[2] = t.z; r.k[3] = t.w;
@@ -864,7 +834,7 @@ __device__ __forceinline__ void mfma_attn_split(
           if constexpr (NDW == 4) r.v[i] = load4_stream(vb_ + off + (size_t)i * (D / 2));
           else r.v[i] = load2_stream(vb_ + off + (size_t)i * (D / 2));
         }
-      } else if constexpr (KVQ == 8) {
+      } else if constexpr (F == 8) {
 #pragma unroll
         for (int sp = 0; sp < KS / 2; ++sp) r.k[sp] = load16_stream(kb_ + off + 64 * sp);
 #pragma unroll
@@ -886,7 +856,7 @@ __device__ __forceinline__ void mfma_attn_split(
     };
     // fused fetch: a page read from the pool goes to its cache page, from the
     // same registers and lane offsets it was loaded with
-    auto store_page = [&](const PageRegs& r, size_t off) {
+    auto store_page = [&](const auto& r, size_t off) {
       if constexpr (KVQ == 4) {
         if constexpr (KS == 4) store16(kbw + off, make_uint4(r.k[0], r.k[1], r.k[2], r.k[3]));
         else store8(kbw + off, make_uint2(r.k[0], r.k[1]));
@@ -911,26 +881,25 @@ __device__ __forceinline__ void mfma_attn_split(
       }
     };
     // one page of compute; `cur` holds page `it` of the group
-    auto process = [&](const PageRegs& cur, int it) {
+    auto process = [&](const auto& cur, int it, auto fmt) {
+      constexpr int F = decltype(fmt)::value;
+      constexpr bool kCold = COLD != 0 && F == COLD;
       if constexpr (FETCH) {
         if (readlane(my_pool, it) >= 0) store_page(cur, (size_t)readlane(my_page, it) * page_stride);
       }
       const int valid = readlane(my_valid, it);
-      const bool cold = COLD != 0 && readlane(my_tier, it) != 0;   // wave-uniform
-      const float sk = (KVQ || cold) ? readlane_f(my_sk, it) : 1.0f;
-      const float sv = (KVQ || cold) ? readlane_f(my_sv, it) : 1.0f;
+      const float sk = F ? readlane_f(my_sk, it) : 1.0f;
+      const float sv = F ? readlane_f(my_sv, it) : 1.0f;
 
       // 16-bit operands of the page: K words kA, and V rows vr that become the
       // P.V operands below (INT4 V codes are decoded straight into them there,
       // after the softmax, when fewer registers are live)
       uint4 kA[KS];
       RowWords<NDW> vr[4];
-      bool v_int4 = false;
-      if constexpr (KVQ == 4) {
+      if constexpr (F == 4) {
 #pragma unroll
         for (int st = 0; st < KS; ++st) kA[st] = int4_k_words<DT>(cur.k[st]);
-        v_int4 = true;
-      } else if constexpr (KVQ == 8) {
+      } else if constexpr (F == 8) {
 #pragma unroll
         for (int sp = 0; sp < KS / 2; ++sp) {
           const uint2 a0 = fp8x4_to_16<DT>(cur.k[sp].x), a1 = fp8x4_to_16<DT>(cur.k[sp].y);
@@ -946,31 +915,6 @@ __device__ __forceinline__ void mfma_attn_split(
             vr[i].w[2 * k] = t.x;
             vr[i].w[2 * k + 1] = t.y;
           }
-      } else if (cold) {                      // tiered call, a cold page's codes
-        if constexpr (COLD == 4) {
-#pragma unroll
-          for (int st = 0; st < KS; ++st) {
-            uint32_t t[4];
-            int4_exact_words<DT, 4>(cur.k[st].x, t);
-            kA[st] = make_uint4(t[0], t[1], t[2], t[3]);
-          }
-#pragma unroll
-          for (int i = 0; i < 4; ++i) int4_exact_words<DT, NDW>(cur.v[i].w[0], vr[i].w);
-        } else if constexpr (COLD == 8) {
-#pragma unroll
-          for (int st = 0; st < KS; ++st) {
-            const uint2 a0 = fp8x4_to_16<DT>(cur.k[st].x), a1 = fp8x4_to_16<DT>(cur.k[st].y);
-            kA[st] = make_uint4(a0.x, a0.y, a1.x, a1.y);
-          }
-#pragma unroll
-          for (int i = 0; i < 4; ++i)
-#pragma unroll
-            for (int k = 0; k < NDW / 2; ++k) {
-              const uint2 t = fp8x4_to_16<DT>(cur.v[i].w[k]);
-              vr[i].w[2 * k] = t.x;
-              vr[i].w[2 * k + 1] = t.y;
-            }
-        }
       } else {
 #pragma unroll
         for (int st = 0; st < KS; ++st) kA[st] = cur.k[st];
@@ -979,11 +923,11 @@ __device__ __forceinline__ void mfma_attn_split(
       }
 
       f32x4_v sacc = {0.f, 0.f, 0.f, 0.f};
-      if constexpr (kInt4Off) {
+      if constexpr (kInt4Off && F == 4) {
         sacc = f32x4_v{qcorr, qcorr, qcorr, qcorr};
       }
 #pragma unroll
-      for (int st = 0; st < KS; ++st) sacc = Ops::qk(kA[st], qB[st], sacc);
+      for (int st = 0; st < KS; ++st) sacc = Ops::qk(kA[st], kCold ? qBc[st] : qB[st], sacc);
       const float zs = qscale * sk;
       float z[4];
 #pragma unroll
@@ -993,7 +937,7 @@ __device__ __forceinline__ void mfma_attn_split(
         for (int i = 0; i < 4; ++i) z[i] = (4 * grp + i < valid) ? z[i] : -INFINITY;
       }
       const float bm = rows_max(fmaxf(fmaxf(z[0], z[1]), fmaxf(z[2], z[3])));
-      if (__ballot(col < G && bm > m)) {  // wave-uniform
+      if (__builtin_amdgcn_ballot_w64(col < G && bm > m)) {  // wave-uniform
         const float mn = fmaxf(m, bm);
         const float alpha = fast_exp2(m - mn);
         m = mn;
@@ -1005,7 +949,7 @@ __device__ __forceinline__ void mfma_attn_split(
         for (int n = 0; n < NT; ++n)
 #pragma unroll
           for (int i = 0; i < 4; ++i) o[n][i] *= ar[i];
-        if constexpr (kInt4Off) {
+        if constexpr (kInt4Off) {   // (vcorr is zero between the INT4 pages of a tiered call)
 #pragma unroll
           for (int i = 0; i < 4; ++i) vcorr[i] *= ar[i];
         }
@@ -1021,7 +965,7 @@ __device__ __forceinline__ void mfma_attn_split(
         if (grp == 0 && col < G)
           block_lse[(row0 + col) * sel_stride + base + it] = (m + __log2f(ps)) * kLn2;
       }
-      if (KVQ != 0 || cold) {    // the page's V scale rides on its weights
+      if constexpr (F != 0) {    // the page's V scale rides on its weights
 #pragma unroll
         for (int i = 0; i < 4; ++i) p[i] *= sv;
       }
@@ -1032,8 +976,8 @@ __device__ __forceinline__ void mfma_attn_split(
       plo.y = Ops::pack(p[2] - Ops::lo(phi.y), p[3] - Ops::hi(phi.y));
 
       uint2 vB[NT];
-      if (v_int4) {
-        if constexpr (KVQ == 4) int4_v_operands<DT, NDW>(cur.v, vB);
+      if constexpr (F == 4) {
+        int4_v_operands<DT, NDW>(cur.v, vB);
       } else {
         if (valid < kBlockSize) {  // slots past the sequence end may hold anything
 #pragma unroll
@@ -1055,7 +999,7 @@ __device__ __forceinline__ void mfma_attn_split(
       const uint2 pa = pv_rows_hi_lo<G>(phi, plo, col);
 #pragma unroll
       for (int n = 0; n < NT; ++n) o[n] = Ops::pv(pa, vB[n], o[n]);
-      if constexpr (kInt4Off) {
+      if constexpr (kInt4Off && F == 4) {
         const uint2 ones = make_uint2(0x3F803F80u, 0x3F803F80u);   // bf16 1.0 pairs
         vcorr = Ops::pv(pa, ones, vcorr);
         if ((it & 7) == 7) fold_vcorr();
@@ -1066,14 +1010,41 @@ __device__ __forceinline__ void mfma_attn_split(
     // peeled off so every load in the loop is unconditional.  (With a
     // conditional prefetch the compiler waited for every outstanding load, the
     // prefetch included, before using a page.)
-    PageRegs cur, nxt;
-    load_page(cur, 0);
-    for (int it = 0; it + 1 < cnt; ++it) {
-      load_page(nxt, it + 1);
-      process(cur, it);
-      cur = nxt;
+    if constexpr (COLD != 0) {
+      // Tiered calls: the group's hot pages, then its cold pages, each in a
+      // loop of its own, so a loop carries one page path and the two paths'
+      // registers are not live at once.  The masks are wave-uniform.
+      const uint64_t live = cnt >= kWave ? ~0ull : ((1ull << cnt) - 1ull);
+      const uint64_t cold_mask = __builtin_amdgcn_ballot_w64(my_tier != 0) & live;
+      auto run = [&](uint64_t mask, auto fmt) {
+        if (mask == 0) return;
+        using Regs = typename PageRegsOf<decltype(fmt)::value, PageRegs16, PageRegs8, PageRegs4>::type;
+        int idx = __builtin_ctzll(mask);
+        mask &= mask - 1;
+        Regs cur, nxt;
+        load_page(cur, idx, fmt);
+        while (mask != 0) {
+          const int nx = __builtin_ctzll(mask);
+          mask &= mask - 1;
+          load_page(nxt, nx, fmt);
+          process(cur, idx, fmt);
+          cur = nxt;
+          idx = nx;
+        }
+        process(cur, idx, fmt);
+      };
+      run(live & ~cold_mask, std::integral_constant<int, 0>{});
+      run(cold_mask, FmtC{});
+    } else {
+      PageRegs cur, nxt;
+      load_page(cur, 0, FmtP{});
+      for (int it = 0; it + 1 < cnt; ++it) {
+        load_page(nxt, it + 1, FmtP{});
+        process(cur, it, FmtP{});
+        cur = nxt;
+      }
+      process(cur, cnt - 1, FmtP{});
     }
-    process(cur, cnt - 1);
   }
 
   if constexpr (kInt4Off) fold_vcorr();
