@@ -880,6 +880,27 @@ __device__ __forceinline__ void mfma_attn_split(
         for (int i = 0; i < 4; ++i) r.v[i].store(vbw + off + kv_bytes<DT, 0>((size_t)i * D));
       }
     };
+    // raise the running max of each head to the page's (or pair's) max bm where
+    // it grows, rescaling the sums (the test is wave-uniform)
+    auto grow_max = [&](float bm) {
+      if (__builtin_amdgcn_ballot_w64(col < G && bm > m)) {
+        const float mn = fmaxf(m, bm);
+        const float alpha = fast_exp2(m - mn);
+        m = mn;
+        lsum *= alpha;
+        float ar[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) ar[i] = __shfl(alpha, (4 * grp + i) & (G - 1), kWave);
+#pragma unroll
+        for (int n = 0; n < NT; ++n)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) o[n][i] *= ar[i];
+        if constexpr (kInt4Off) {   // (vcorr is zero between the INT4 pages of a tiered call)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) vcorr[i] *= ar[i];
+        }
+      }
+    };
     // one page of compute; `cur` holds page `it` of the group
     auto process = [&](const auto& cur, int it, auto fmt) {
       constexpr int F = decltype(fmt)::value;
@@ -936,24 +957,7 @@ __device__ __forceinline__ void mfma_attn_split(
 #pragma unroll
         for (int i = 0; i < 4; ++i) z[i] = (4 * grp + i < valid) ? z[i] : -INFINITY;
       }
-      const float bm = rows_max(fmaxf(fmaxf(z[0], z[1]), fmaxf(z[2], z[3])));
-      if (__builtin_amdgcn_ballot_w64(col < G && bm > m)) {  // wave-uniform
-        const float mn = fmaxf(m, bm);
-        const float alpha = fast_exp2(m - mn);
-        m = mn;
-        lsum *= alpha;
-        float ar[4];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) ar[i] = __shfl(alpha, (4 * grp + i) & (G - 1), kWave);
-#pragma unroll
-        for (int n = 0; n < NT; ++n)
-#pragma unroll
-          for (int i = 0; i < 4; ++i) o[n][i] *= ar[i];
-        if constexpr (kInt4Off) {   // (vcorr is zero between the INT4 pages of a tiered call)
-#pragma unroll
-          for (int i = 0; i < 4; ++i) vcorr[i] *= ar[i];
-        }
-      }
+      grow_max(rows_max(fmaxf(fmaxf(z[0], z[1]), fmaxf(z[2], z[3]))));
       float p[4];
 #pragma unroll
       for (int i = 0; i < 4; ++i) p[i] = fast_exp2(z[i] - m);
@@ -1006,6 +1010,135 @@ __device__ __forceinline__ void mfma_attn_split(
       }
 
     };
+    // Two INT4 pages (ia, ib) of the pools at once.  The P.V products take the
+    // 32 tokens of both pages per 16x16x32 product: in lane group g, k slots
+    // 0-3 hold page a's tokens 4g..4g+3 and slots 4-7 page b's, in P's operand
+    // (rows h < G: hi, rows G + h: lo, as pv_rows_hi_lo) and in V's alike.
+    // That is half the products of one page at a time, and the running max is
+    // raised once per pair.
+    // K operand words of QK step st, and the P.V B operands (vB[n]: output
+    // tile n), of a code page of format F (8 or 4); V rows of tokens past a
+    // partial page's end are zeroed first (E4M3 slots there may hold NaN codes;
+    // INT4 codes are always finite and meet weights of exactly 0)
+    auto code_k_words = [&](const auto& cur, int st, auto fmt) -> uint4 {
+      if constexpr (decltype(fmt)::value == 4) {
+        return int4_k_words<DT>(cur.k[st]);
+      } else {
+        const uint4 w = cur.k[st >> 1];
+        const uint2 a0 = fp8x4_to_16<DT>((st & 1) ? w.z : w.x);
+        const uint2 a1 = fp8x4_to_16<DT>((st & 1) ? w.w : w.y);
+        return make_uint4(a0.x, a0.y, a1.x, a1.y);
+      }
+    };
+    auto code_v_operands = [&](const auto& cur, int valid, uint2 (&vB)[NT], auto fmt) {
+      if constexpr (decltype(fmt)::value == 4) {
+        int4_v_operands<DT, NDW>(cur.v, vB);
+      } else {
+        RowWords<NDW> vr[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+          for (int k = 0; k < NDW / 2; ++k) {
+            const uint2 t = fp8x4_to_16<DT>(cur.v[i][k]);
+            vr[i].w[2 * k] = t.x;
+            vr[i].w[2 * k + 1] = t.y;
+          }
+        if (valid < kBlockSize) {
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            if (4 * grp + i >= valid)
+#pragma unroll
+              for (int k = 0; k < NDW; ++k) vr[i].w[k] = 0u;
+        }
+#pragma unroll
+        for (int k = 0; k < NDW; ++k) {
+          vB[2 * k].x = __builtin_amdgcn_perm(vr[1].w[k], vr[0].w[k], 0x05040100u);
+          vB[2 * k].y = __builtin_amdgcn_perm(vr[3].w[k], vr[2].w[k], 0x05040100u);
+          vB[2 * k + 1].x = __builtin_amdgcn_perm(vr[1].w[k], vr[0].w[k], 0x07060302u);
+          vB[2 * k + 1].y = __builtin_amdgcn_perm(vr[3].w[k], vr[2].w[k], 0x07060302u);
+        }
+      }
+    };
+    auto process2 = [&](const auto& ca, const auto& cb, int ia, int ib, auto fmt) {
+      constexpr int F = decltype(fmt)::value;
+      static_assert(F == 4 || F == 8, "pairs of code pages");
+      constexpr bool kCold = COLD != 0 && F == COLD;
+      if constexpr (FETCH) {   // pages read from the pool go to their cache pages
+        if (readlane(my_pool, ia) >= 0) store_page(ca, (size_t)readlane(my_page, ia) * page_stride);
+        if (readlane(my_pool, ib) >= 0) store_page(cb, (size_t)readlane(my_page, ib) * page_stride);
+      }
+      const int vla = readlane(my_valid, ia), vlb = readlane(my_valid, ib);
+      const float zsa = qscale * readlane_f(my_sk, ia), zsb = qscale * readlane_f(my_sk, ib);
+      const float sva = readlane_f(my_sv, ia), svb = readlane_f(my_sv, ib);
+      f32x4_v sa = {0.f, 0.f, 0.f, 0.f}, sb = {0.f, 0.f, 0.f, 0.f};
+      if constexpr (kInt4Off && F == 4) {
+        sa = f32x4_v{qcorr, qcorr, qcorr, qcorr};
+        sb = sa;
+      }
+#pragma unroll
+      for (int st = 0; st < KS; ++st) {
+        sa = Ops::qk(code_k_words(ca, st, fmt), kCold ? qBc[st] : qB[st], sa);
+        sb = Ops::qk(code_k_words(cb, st, fmt), kCold ? qBc[st] : qB[st], sb);
+      }
+      float z[8];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        z[i] = sa[i] * zsa;
+        z[4 + i] = sb[i] * zsb;
+      }
+      if (vla < kBlockSize) {   // wave-uniform: partial last pages only
+#pragma unroll
+        for (int i = 0; i < 4; ++i) z[i] = (4 * grp + i < vla) ? z[i] : -INFINITY;
+      }
+      if (vlb < kBlockSize) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) z[4 + i] = (4 * grp + i < vlb) ? z[4 + i] : -INFINITY;
+      }
+      grow_max(rows_max(fmaxf(fmaxf(fmaxf(z[0], z[1]), fmaxf(z[2], z[3])),
+                              fmaxf(fmaxf(z[4], z[5]), fmaxf(z[6], z[7])))));
+      float p[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) p[i] = fast_exp2(z[i] - m);
+      const float psa = (p[0] + p[1]) + (p[2] + p[3]), psb = (p[4] + p[5]) + (p[6] + p[7]);
+      lsum += psa + psb;
+      if (SPARSE && block_lse) {   // ln of each page's summed exp-logits per head; lists only
+        float ta = psa, tb = psb;
+        ta += xor16(ta);
+        ta += xor32(ta);
+        tb += xor16(tb);
+        tb += xor32(tb);
+        if (grp == 0 && col < G) {
+          block_lse[(row0 + col) * sel_stride + base + ia] = (m + __log2f(ta)) * kLn2;
+          block_lse[(row0 + col) * sel_stride + base + ib] = (m + __log2f(tb)) * kLn2;
+        }
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {   // each page's V scale rides on its weights
+        p[i] *= sva;
+        p[4 + i] *= svb;
+      }
+      uint2 ph[2], pl[2];
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        ph[h].x = Ops::pack(p[4 * h], p[4 * h + 1]);
+        ph[h].y = Ops::pack(p[4 * h + 2], p[4 * h + 3]);
+        pl[h].x = Ops::pack(p[4 * h] - Ops::lo(ph[h].x), p[4 * h + 1] - Ops::hi(ph[h].x));
+        pl[h].y = Ops::pack(p[4 * h + 2] - Ops::lo(ph[h].y), p[4 * h + 3] - Ops::hi(ph[h].y));
+      }
+      const uint2 xa = pv_rows_hi_lo<G>(ph[0], pl[0], col), xb = pv_rows_hi_lo<G>(ph[1], pl[1], col);
+      const uint4 pa = make_uint4(xa.x, xa.y, xb.x, xb.y);
+      uint2 va[NT], vb2[NT];
+      code_v_operands(ca, vla, va, fmt);
+      code_v_operands(cb, vlb, vb2, fmt);
+#pragma unroll
+      for (int n = 0; n < NT; ++n)
+        o[n] = mfma_16x16x32<DT>(pa, make_uint4(va[n].x, va[n].y, vb2[n].x, vb2[n].y), o[n]);
+      if constexpr (kInt4Off && F == 4) {
+        const uint4 ones = make_uint4(0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u);
+        vcorr = mfma_16x16x32<DT>(pa, ones, vcorr);
+        if ((ib & 7) == 7) fold_vcorr();
+      }
+    };
     // page it+1 loads while page it is computed; the group's last page is
     // peeled off so every load in the loop is unconditional.  (With a
     // conditional prefetch the compiler waited for every outstanding load, the
@@ -1035,6 +1168,37 @@ __device__ __forceinline__ void mfma_attn_split(
       };
       run(live & ~cold_mask, std::integral_constant<int, 0>{});
       run(cold_mask, FmtC{});
+    } else if constexpr (KVQ == 4) {
+      // INT4 pools: pages two at a time (process2), the next pair loading
+      // while the current one is computed; an odd last page takes process.
+      // (FP8 pools measured slower in pairs, 48.9 against 47.9 us for the 128k
+      // dense call: their decode leaves fewer registers and instructions to
+      // save.)
+      // (Two register sets used in turn, two pairs per trip, measured slower
+      // for INT4 pages: the compiler then needs more registers than three
+      // waves per SIMD allow.  Tiered calls keep one page at a time: their
+      // instances carry both page paths and have no registers to spare.  The
+      // fused-fetch instances pair pages too, so a fetch inside the attention
+      // gives the same sums as the fetch before it.)
+      PageRegs ra, rb, na, nb;
+      int it = 0;
+      if (cnt >= 2) {
+        load_page(ra, 0, FmtP{});
+        load_page(rb, 1, FmtP{});
+        for (; it + 3 < cnt; it += 2) {
+          load_page(na, it + 2, FmtP{});
+          load_page(nb, it + 3, FmtP{});
+          process2(ra, rb, it, it + 1, FmtP{});
+          ra = na;
+          rb = nb;
+        }
+        if (it + 2 < cnt) load_page(na, it + 2, FmtP{});
+        process2(ra, rb, it, it + 1, FmtP{});
+        it += 2;
+      } else {
+        load_page(na, 0, FmtP{});
+      }
+      if (it < cnt) process(na, it, FmtP{});
     } else {
       PageRegs cur, nxt;
       load_page(cur, 0, FmtP{});
