@@ -28,6 +28,11 @@
  *   kv_decode_combine     log-sum-exp merge of the split partials
  *   kv_append_token       store the new token's K/V and fold it into its page's meta
  *   kv_decode_select      kv_append_token followed by kv_block_select, in two launches
+ *   kv_decode_score       kv_decode_select's append + score launch, without the Top-K
+ *   kv_select_decode_attn the Top-K and the sparse attention over it, one launch for
+ *                         rows of up to 2048 blocks (kv_auto_select_splits)
+ *   kv_block_select_no_alloc  kv_block_select with its scores in a library-owned
+ *                         device array, for callers that cannot allocate
  *   kv_check_tables       device-side check of the block table, lengths and selection
  *
  * The method is the select -> fetch -> compute decode step of the KVDrive paper

@@ -404,6 +404,9 @@ __global__ __launch_bounds__(WAVES * kWave) void paged_attn_kernel(
 //   S^T[16 tok x 16] = K[16 tok x D] . Q^T[D x 16]       v_mfma_f32_16x16x32 (D/32 steps)
 //   O[16 x D]       += P[16 x 16 tok] . V[16 tok x D]     v_mfma_f32_16x16x16 (D/16 tiles)
 //
+// (INT4 pages go two at a time, with one v_mfma_f32_16x16x32 per tile over the
+// 32 tokens of both pages: see process2.)
+//
 // with the G heads padded to the 16 MFMA columns of S^T (columns >= G are zero
 // queries) and to the 16 rows of O.  Lane l = 16*grp + col:
 //   * K is the A operand read straight from the page: lane l holds token col,
