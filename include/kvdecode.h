@@ -233,9 +233,9 @@ kv_status kv_decode_score(const kv_shape* shape, int32_t index_kind, const void*
  * same num_splits (part_o [B, Hq, S, D], part_m, part_l [B, Hq, S], merged by
  * kv_decode_combine).  scores: fp32 [B, Hkv, maxN], e.g. from kv_decode_score
  * or kv_block_select's scores_out.  For 16-bit K/V with G >= 2, maxN <= 2048
- * and at most 2048 list positions per eight splits (8 * ceil(topk_blocks /
+ * and at most 2048 list positions per four splits (4 * ceil(topk_blocks /
  * num_splits)) it is one launch: each workgroup repeats the row's Top-K
- * itself, keeps the positions of its eight splits in LDS and attends them,
+ * itself, keeps the positions of its four splits in LDS and attends them,
  * which saves the Top-K launch and the list's round trip through memory;
  * other calls (longer rows, where the repeated Top-K costs more than the
  * launch it saves) run the two launches.  Arguments and errors are those of
@@ -334,8 +334,8 @@ int32_t kv_auto_num_splits(const kv_shape* shape, int32_t blocks_per_unit);
 
 /*
  * Number of splits for kv_select_decode_attn with topk_blocks: where the call
- * is one launch, eight splits (one workgroup) per compute unit over the
- * (sequence, KV head) rows, at most 8 * ceil(topk_blocks / 8); elsewhere
+ * is one launch, four splits (one workgroup) per compute unit over the
+ * (sequence, KV head) rows, at most 4 * ceil(topk_blocks / 4); elsewhere
  * kv_auto_num_splits(shape, topk_blocks).  Always >= 1.
  */
 int32_t kv_auto_select_splits(const kv_shape* shape, int32_t topk_blocks);

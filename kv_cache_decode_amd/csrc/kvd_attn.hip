@@ -1714,14 +1714,14 @@ hipError_t launch_select_attn(int dtype, int D, int G, const float* scores, int 
   constexpr int NT = kSelAttnWaves * kWave;
   const dim3 grid((S + kSelAttnWaves - 1) / kSelAttnWaves, Hkv, B);
   const float qscale = scale * kLog2e;
-  static_assert(kSelAttnMaxBlocks <= NT * 4, "one Top-K instance of 4 keys per thread");
+  constexpr int EPT = (kSelAttnMaxBlocks + NT - 1) / NT;   // keys per thread of the row select
   return with_dtype(dtype, [&](auto dt) {
     return with_dim(D, [&](auto d) {
       return with_group(G, [&](auto g) {
         using DT = decltype(dt);
         constexpr int DD = decltype(d)::value, GG = decltype(g)::value;
         if constexpr (!std::is_same_v<DT, F32> && GG >= 2) {
-          hipLaunchKernelGGL((select_attn_mfma_kernel<DT, DD, GG, 4>), grid, dim3(NT), 0, stream,
+          hipLaunchKernelGGL((select_attn_mfma_kernel<DT, DD, GG, EPT>), grid, dim3(NT), 0, stream,
                              scores, K, sink, local, sel, sel_count, q, k_cache, v_cache,
                              block_table, seq_lens, Hq, Hkv, maxN, S, qscale, part_o, part_m,
                              part_l);

@@ -157,7 +157,10 @@ constexpr int kTopkMaxBlocks = 65536;
 // list positions a workgroup keeps in LDS, and the longest row it takes (every
 // workgroup of a row repeats the row's Top-K; past 2048 blocks that costs more
 // than the Top-K launch it saves).
-constexpr int kSelAttnWaves = 8;
+#ifndef KVD_SEL_ATTN_WAVES
+#define KVD_SEL_ATTN_WAVES 4   // a multiple of 4 (the row select's scans)
+#endif
+constexpr int kSelAttnWaves = KVD_SEL_ATTN_WAVES;
 constexpr int kSelAttnListMax = 2048;
 constexpr int kSelAttnMaxBlocks = 2048;
 

@@ -181,19 +181,19 @@ def test_auto_splits_bounds():
 
 
 def test_auto_select_splits():
-    """One eight-split workgroup per compute unit (256 here, the MI355X count the
+    """One four-split workgroup per compute unit (256 here, the MI355X count the
     library assumes without a device) where kv_select_decode_attn is one launch;
     the attention rule elsewhere."""
     s32k = shape(num_seqs=4, num_kv_heads=8, num_q_heads=32, max_blocks_per_seq=2048,
                  num_pages=8192)
-    assert kd.kv_auto_select_splits(s32k, 128) == 64          # 32 rows -> 8 workgroups each
-    assert kd.kv_auto_select_splits(s32k, 20) == 24           # at most 8 * ceil(K / 8)
+    assert kd.kv_auto_select_splits(s32k, 128) == 32          # 32 rows -> 8 workgroups each
+    assert kd.kv_auto_select_splits(s32k, 18) == 20           # at most 4 * ceil(K / 4)
     two = shape(num_seqs=2, num_kv_heads=8, num_q_heads=32, max_blocks_per_seq=2048,
                 num_pages=4096)
-    assert kd.kv_auto_select_splits(two, 128) == 128
+    assert kd.kv_auto_select_splits(two, 128) == 64
     many = shape(num_seqs=64, num_kv_heads=8, num_q_heads=32, max_blocks_per_seq=64,
                  num_pages=4096)
-    assert kd.kv_auto_select_splits(many, 16) == 8            # at least one workgroup
+    assert kd.kv_auto_select_splits(many, 16) == 4            # at least one workgroup
     for off in (dict(max_blocks_per_seq=8192, num_pages=8192),   # rows too long to fuse
                 dict(dtype="f32"), dict(num_q_heads=8)):          # vector path
         o = shape(**{**dict(num_seqs=1, num_kv_heads=8, num_q_heads=32, max_blocks_per_seq=2048,

@@ -64,7 +64,7 @@ for dtype in ("bf16", "f16"):
 @pytest.mark.parametrize("dtype,D,G,seed", GRID, ids=[f"{d}-D{D}-G{G}" for d, D, G, _ in GRID])
 def test_fused_equals_topk_then_attention(gpu, dtype, D, G, seed):
     """Ragged lengths (1, 15, 17, 543, 1300 tokens), K below and above N_b, split
-    counts that are not multiples of the workgroup's eight and exceed the list,
+    counts that are not multiples of the workgroup's four and exceed the list,
     with and without 4 + 64 forced tokens."""
     data = mk(5, 2 * G, 2, D, (1300, 1, 15, 17, 543), dtype, seed, extra_pages=2,
               planted_frac=0.1)
