@@ -390,6 +390,55 @@ def test_decode_select_argument_checks():
     expect(kd.KV_ERR_WORKSPACE, call(scores_out=None))
 
 
+def test_decode_score_argument_checks():
+    s = shape()
+    f = kd.kv_decode_score
+
+    def call(**kw):
+        args = dict(index_kind=kd.KV_INDEX_MINMAX, q=A16, k_new=A16, v_new=A16, block_table=A16,
+                    seq_lens=A16, k_cache=A16, v_cache=A16, kmeta=A16, kmean=None,
+                    scores_out=A16)
+        args.update(kw)
+        return lambda stream: f(s, stream=stream, **args)
+
+    expect(kd.KV_ERR_INVALID_ARG, call(kmeta=None))                       # the chosen index
+    expect(kd.KV_ERR_INVALID_ARG, call(index_kind=kd.KV_INDEX_MEAN))       # kmean missing
+    expect(kd.KV_ERR_INVALID_ARG, call(index_kind=5))
+    expect(kd.KV_ERR_INVALID_ARG, call(k_new=None))
+    expect(kd.KV_ERR_INVALID_ARG, call(scores_out=None))                  # always required
+    expect(kd.KV_ERR_ALIGNMENT, call(v_new=A4))
+    expect(kd.KV_ERR_ALIGNMENT, call(index_kind=kd.KV_INDEX_MEAN, kmean=A4))
+    expect(kd.KV_ERR_ALIGNMENT, call(scores_out=ODD))
+    expect(kd.KV_ERR_ALIGNMENT, call(block_table=ODD))
+
+
+def test_select_decode_attn_argument_checks():
+    """The Top-K + attention call validates as the two calls it stands for, in
+    either of its forms (one launch for rows of up to 2048 blocks, else two)."""
+    def call(s, **kw):
+        args = dict(scores=A16, block_table=A16, seq_lens=A16, topk_blocks=2, sink_tokens=0,
+                    local_tokens=0, q=A16, k_cache=A16, v_cache=A16, scale=0.1, num_splits=2,
+                    sel_blocks=A16, sel_count=A16, part_o=A16, part_m=A16, part_l=A16)
+        args.update(kw)
+        return lambda stream: kd.kv_select_decode_attn(s, stream=stream, **args)
+
+    for s in (shape(), shape(max_blocks_per_seq=4096, num_pages=4096)):
+        expect(kd.KV_ERR_INVALID_ARG, call(s, topk_blocks=0))
+        expect(kd.KV_ERR_INVALID_ARG, call(s, sink_tokens=64, local_tokens=64))  # forces > K
+        expect(kd.KV_ERR_INVALID_ARG, call(s, sink_tokens=-1))
+        expect(kd.KV_ERR_INVALID_ARG, call(s, num_splits=0))
+        expect(kd.KV_ERR_INVALID_ARG, call(s, scores=None))
+        expect(kd.KV_ERR_INVALID_ARG, call(s, sel_blocks=None))
+        expect(kd.KV_ERR_INVALID_ARG, call(s, q=None))
+        expect(kd.KV_ERR_INVALID_ARG, call(s, part_m=None))
+        expect(kd.KV_ERR_INVALID_ARG, call(s, scale=float("nan")))
+        expect(kd.KV_ERR_ALIGNMENT, call(s, scores=ODD))
+        expect(kd.KV_ERR_ALIGNMENT, call(s, k_cache=A4))
+        expect(kd.KV_ERR_ALIGNMENT, call(s, part_o=A4))
+        expect(kd.KV_ERR_ALIGNMENT, call(s, sel_count=ODD))
+    expect(kd.KV_ERR_UNSUPPORTED, call(shape(max_blocks_per_seq=65537, num_pages=65537)))
+
+
 def test_int4_argument_checks():
     s = shape()
     qz = kd.kv_quantize_pages_int4
