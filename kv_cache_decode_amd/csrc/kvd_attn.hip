@@ -499,22 +499,22 @@ __device__ inline void add_residue_rows(f32x4_v& t) {
   }
 }
 
-// Four E4M3 codes (one dword) as four 16-bit values (two dwords), exact.
+// Four E4M3 codes (one dword) as four 16-bit values (two dwords), exact:
+// gfx950's scaled conversion with scale 1 turns two codes straight into a
+// 16-bit pair (word_sel picks codes 0-1 or 2-3).  Every E4M3 value is exact in
+// bf16 and in f16 (an in-bounds probe compared all non-NaN codes with the
+// fp32 route on the GPU).
 template <typename DT>
 __device__ inline uint2 fp8x4_to_16(uint32_t w);
 template <>
 __device__ inline uint2 fp8x4_to_16<BF16>(uint32_t w) {
-  const f32x2_v a = __builtin_amdgcn_cvt_pk_f32_fp8((int)w, false);
-  const f32x2_v b = __builtin_amdgcn_cvt_pk_f32_fp8((int)w, true);
-  // the bf16 of an exactly representable fp32 is its high half
-  return make_uint2(__builtin_amdgcn_perm(__float_as_uint(a.y), __float_as_uint(a.x), 0x07060302u),
-                    __builtin_amdgcn_perm(__float_as_uint(b.y), __float_as_uint(b.x), 0x07060302u));
+  return make_uint2(__builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, false)),
+                    __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, true)));
 }
 template <>
 __device__ inline uint2 fp8x4_to_16<F16>(uint32_t w) {
-  const f32x2_v a = __builtin_amdgcn_cvt_pk_f32_fp8((int)w, false);
-  const f32x2_v b = __builtin_amdgcn_cvt_pk_f32_fp8((int)w, true);
-  return make_uint2(F16::pack2(a.x, a.y), F16::pack2(b.x, b.y));
+  return make_uint2(__builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w, 1.0f, false)),
+                    __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w, 1.0f, true)));
 }
 
 // NDW dwords (2*NDW 16-bit channels) of one token row, as one vector load.
