@@ -1174,9 +1174,8 @@ __device__ __forceinline__ void mfma_attn_split(
     } else if constexpr (KVQ == 4) {
       // INT4 pools: pages two at a time (process2), the next pair loading
       // while the current one is computed; an odd last page takes process.
-      // (FP8 pools measured slower in pairs, 48.9 against 47.9 us for the 128k
-      // dense call: their decode leaves fewer registers and instructions to
-      // save.)
+      // (FP8 pools measured slower in pairs, 48.1 against 46.5 us for the 128k
+      // dense call, also with their two-codes-per-instruction conversion.)
       // (Two register sets used in turn, two pairs per trip, measured slower
       // for INT4 pages: the compiler then needs more registers than three
       // waves per SIMD allow.  Tiered calls keep one page at a time: their
