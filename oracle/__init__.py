@@ -20,6 +20,8 @@ Functions (each computed as oracle.c states it):
 * ``block_lse``       ln sum exp(logits) of each attended block          (KVDrive §5.1)
 * ``slot_mass``       eviction mass of each cache slot after a step
 * ``cache_plan``      one step of the GPU block cache: hits, misses, victims
+* ``tier_plan``       one step of the hot/cold tier policy: page heat, demotions,
+                      promotions  (tiered-offload blog, page replacement; KVDrive §11)
 * ``attention``       softmax decode attention, dense or over selected blocks
                       (Dual-Blade background; KVDrive §2.3 step 3)
 * ``attention_splits``  the same on each contiguous chunk of the block list
@@ -83,6 +85,10 @@ def _load():
     lib.oracle_cache_plan.argtypes = [_I, _I, _int, _int, _int, _int, _int, _I, _I, _F, _I, _I,
                                       _I, _I]
     lib.oracle_cache_plan.restype = None
+    lib.oracle_tier_plan.argtypes = [_I, _I, _int, _I, _I, _int, _int, _int, _int,
+                                     ctypes.c_float, ctypes.c_float, ctypes.c_float, _int, _int,
+                                     _int, _F, _U8, _I, _I, _I, _I, _I]
+    lib.oracle_tier_plan.restype = None
     lib.oracle_topk.argtypes = [_D, _I, _int, _int, _int, _int, _int, _I, _I]
     lib.oracle_attention.argtypes = [_D, _D, _D, _I, _I, _I, _I, _int, _int, _int, _int, _int,
                                      _int, _int, ctypes.c_double, _D, _D]
@@ -300,6 +306,35 @@ def cache_plan(sel, sel_count, slot_block, block_slot, slot_mass_):
                               mass.ctypes.data_as(ctypes.POINTER(ctypes.c_float)), _pi(sel_slots),
                               _pi(fb), _pi(fs), _pi(fc))
     return sb, bs_, sel_slots, fb, fs, fc
+
+
+def tier_plan(sel, sel_count, block_table, seq_lens, block_size: int, decay: float,
+              hot_above: float, cold_below: float, recent: int, cooldown: int, step: int,
+              heat, tier, stamp):
+    """One step of the tier policy; returns (heat, tier, stamp, demote, demote_count,
+    promote, promote_count) with the page state updated (inputs are not modified).
+
+    heat float32 [P], tier uint8 [P] (0 hot, 1 cold), stamp int32 [P];
+    demote / promote int32 [B, maxN] in block order, -1 padded."""
+    sl_, cnt = _i32(sel), _i32(sel_count)
+    bt, sl = _i32(block_table), _i32(seq_lens)
+    h = np.array(heat, dtype=np.float32, copy=True)
+    t = np.array(tier, dtype=np.uint8, copy=True)
+    st = np.array(stamp, dtype=np.int32, copy=True)
+    B, Hkv, stride = sl_.shape
+    maxN = bt.shape[1]
+    # filled with a value the oracle never writes, so that a row it leaves unset shows
+    dem = np.full((B, maxN), np.iinfo(np.int32).max, np.int32)
+    pro = np.full((B, maxN), np.iinfo(np.int32).max, np.int32)
+    dc = np.full(B, -7, np.int32)
+    pc = np.full(B, -7, np.int32)
+    _load().oracle_tier_plan(_pi(sl_), _pi(cnt), stride, _pi(bt), _pi(sl), B, Hkv, maxN,
+                             block_size, float(decay), float(hot_above), float(cold_below),
+                             recent, cooldown, step,
+                             h.ctypes.data_as(ctypes.POINTER(ctypes.c_float)),
+                             t.ctypes.data_as(ctypes.POINTER(ctypes.c_uint8)), _pi(st),
+                             _pi(dem), _pi(dc), _pi(pro), _pi(pc))
+    return h, t, st, dem, dc, pro, pc
 
 
 def group_scores(head_scores_, num_kv_heads: int) -> np.ndarray:

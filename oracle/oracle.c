@@ -73,7 +73,17 @@
  *    slot first); the missing blocks, in list order, take the reused slots in
  *    increasing slot order.  The mass of a slot is the attention weight its block
  *    received in the latest step, summed over the block's tokens, max over
- *    the query heads of the group; 0 for a block the step did not attend.
+ *    the query heads of the group; 0 for a block the step did not attend;
+ *  - tier plan (the tiered-offload blog, "page replacement": pages move to a
+ *    slower tier when cold, and a hysteresis cooldown keeps a page just moved
+ *    down from coming straight back; KVDrive §11: hot blocks keep high
+ *    precision, cold blocks are quantised): each page in use has a heat
+ *    h <- decay * h + (1 - decay) * hit, where hit = 1 when any KV head of its
+ *    sequence selected its block in the step; a hot page that does not hold
+ *    one of the sequence's last `recent` tokens turns cold when h < cold_below;
+ *    a cold page turns hot when it holds a recent token, or when h > hot_above
+ *    and at least `cooldown` steps have passed since it turned cold.  Heat is
+ *    kept and compared in fp32, the precision in which the kernel decides.
  */
 #include <math.h>
 #include <stdint.h>
@@ -722,6 +732,59 @@ void oracle_cache_plan(const int32_t* sel, const int32_t* sel_count, int sel_str
   }
   free(in_use);
   free(cand);
+}
+
+/*
+ * Tier plan: one decode step's update of every page in use (see the reading
+ * above).  Page p = block_table[b, n], n < N_b, is hit when block n is in
+ * sel[b, j, 0..sel_count[b, j]) for some KV head j (row stride sel_stride),
+ * and recent when it holds one of the last `recent` tokens of sequence b.
+ * heat [P] (fp32), tier [P] (0 hot, 1 cold) and stamp [P] (the step at which
+ * the page last turned cold) are updated in place; pages no sequence
+ * references keep their state; each page is referenced by at most one
+ * (sequence, block).  demote / promote [B, maxN] receive, per sequence and in
+ * block order, the pages that turned cold / hot (-1 after the last), and
+ * demote_count / promote_count [B] their numbers.
+ */
+void oracle_tier_plan(const int32_t* sel, const int32_t* sel_count, int sel_stride,
+                      const int32_t* block_table, const int32_t* seq_lens, int B, int Hkv,
+                      int maxN, int bs, float decay, float hot_above, float cold_below,
+                      int recent, int cooldown, int step, float* heat, uint8_t* tier,
+                      int32_t* stamp, int32_t* demote, int32_t* demote_count, int32_t* promote,
+                      int32_t* promote_count) {
+  for (int b = 0; b < B; ++b) {
+    const i64 L = seq_lens[b];
+    const i64 N = ceil_div(L, bs);
+    int32_t* dem = demote + (i64)b * maxN;
+    int32_t* pro = promote + (i64)b * maxN;
+    for (int n = 0; n < maxN; ++n) { dem[n] = -1; pro[n] = -1; }
+    int nd = 0, np = 0;
+    for (i64 n = 0; n < N; ++n) {
+      int hit = 0;
+      for (int j = 0; j < Hkv && !hit; ++j) {
+        const i64 u = (i64)b * Hkv + j;
+        for (int pos = 0; pos < sel_count[u]; ++pos)
+          if (sel[u * sel_stride + pos] == n) { hit = 1; break; }
+      }
+      /* the block holds tokens n*bs .. n*bs + bs - 1; the recent ones are L - recent .. L - 1 */
+      const int is_recent = recent > 0 && n * bs + bs - 1 >= L - recent;
+      const i64 p = block_table[(i64)b * maxN + n];
+      const float h = hit ? fmaf(decay, heat[p], 1.0f - decay) : decay * heat[p];
+      heat[p] = h;
+      if (tier[p] == 0) {
+        if (!is_recent && h < cold_below) {
+          tier[p] = 1;
+          stamp[p] = step;
+          dem[nd++] = (int32_t)p;
+        }
+      } else if (is_recent || (h > hot_above && (i64)step - stamp[p] >= cooldown)) {
+        tier[p] = 0;
+        pro[np++] = (int32_t)p;
+      }
+    }
+    demote_count[b] = nd;
+    promote_count[b] = np;
+  }
 }
 
 /*

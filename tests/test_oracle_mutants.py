@@ -70,6 +70,18 @@ MUTANTS = [
     ("block_lse_reads_past_the_end", "for (int s = 0; s < bs && n * bs + s < L; ++s) {", "for (int s = 0; s < bs; ++s) {", 0),
     ("slot_mass_sums_heads", "if (w > best) best = w;", "best += w;", 0),
     ("combine_lse_drops_max", "if (lse) lse[r] = M + log(wsum);", "if (lse) lse[r] = log(wsum);", 0),
+    ("tier_cooldown_strict", "(i64)step - stamp[p] >= cooldown", "(i64)step - stamp[p] > cooldown", 0),
+    ("tier_hit_only_first_head", "for (int j = 0; j < Hkv && !hit; ++j)", "for (int j = 0; j < 1 && !hit; ++j)", 0),
+    ("tier_recent_off_by_one", "n * bs + bs - 1 >= L - recent", "n * bs + bs - 1 > L - recent", 0),
+    ("tier_decay_swapped", "fmaf(decay, heat[p], 1.0f - decay) : decay * heat[p]",
+     "fmaf(1.0f - decay, heat[p], decay) : (1.0f - decay) * heat[p]", 0),
+    ("tier_cold_below_inclusive", "!is_recent && h < cold_below", "!is_recent && h <= cold_below", 0),
+    ("tier_hot_above_inclusive", "(h > hot_above &&", "(h >= hot_above &&", 0),
+    ("tier_stamp_not_set", "stamp[p] = step;\n", "", 0),
+    ("tier_recent_not_promoted", "} else if (is_recent || (h > hot_above", "} else if ((h > hot_above", 0),
+    ("tier_recent_demoted", "if (!is_recent && h < cold_below)", "if (h < cold_below)", 0),
+    ("tier_lists_not_cleared", "for (int n = 0; n < maxN; ++n) { dem[n] = -1; pro[n] = -1; }", "", 0),
+    ("tier_miss_keeps_heat", ": decay * heat[p];", ": heat[p];", 0),
 ]
 
 

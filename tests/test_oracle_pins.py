@@ -929,3 +929,181 @@ def test_slot_mass_is_the_attention_weight_of_each_block():
             assert m[0, j, slots[0, j, pos]] == pytest.approx(w[:, pos].max(), rel=1e-14)
         untouched = set(range(6)) - set(slots[0, j, :cnt[0, j]].tolist())
         assert all(m[0, j, c] == 0 for c in untouched)
+
+
+# ---------------------------------------------------------------- tier plan
+# tiered-offload blog page, page replacement (heat, hysteresis cooldown);
+# KVDrive §11 (hot blocks at full precision, cold blocks quantised)
+
+TIER = os.path.join(os.path.dirname(__file__), "golden", "tier_plan.json")
+
+
+def _sel_rows(rows, stride):
+    B, Hkv = len(rows), len(rows[0])
+    sel = np.full((B, Hkv, stride), -1, np.int32)
+    cnt = np.zeros((B, Hkv), np.int32)
+    for b in range(B):
+        for j in range(Hkv):
+            sel[b, j, :len(rows[b][j])] = rows[b][j]
+            cnt[b, j] = len(rows[b][j])
+    return sel, cnt
+
+
+def test_tier_plan_golden():
+    with open(TIER) as f:
+        g = json.load(f)
+    bt = np.array(g["block_table"], np.int32)
+    heat = np.array(g["initial"]["heat"], np.float32)
+    tier = np.array(g["initial"]["tier"], np.uint8)
+    stamp = np.array(g["initial"]["stamp"], np.int32)
+    for st in g["steps"]:
+        sel, cnt = _sel_rows(st["sel"], g["sel_stride"])
+        heat, tier, stamp, dem, dc, pro, pc = oracle.tier_plan(
+            sel, cnt, bt, np.array(st["seq_lens"], np.int32), g["block_size"], g["decay"],
+            g["hot_above"], g["cold_below"], g["recent"], g["cooldown"], st["step"],
+            heat, tier, stamp)
+        assert heat.tolist() == st["heat"], st["why"]
+        assert tier.tolist() == st["tier"], st["why"]
+        assert stamp.tolist() == st["stamp"], st["why"]
+        for b in range(bt.shape[0]):
+            assert dem[b, :dc[b]].tolist() == st["demote"][b], st["why"]
+            assert pro[b, :pc[b]].tolist() == st["promote"][b], st["why"]
+            assert np.all(dem[b, dc[b]:] == -1) and np.all(pro[b, pc[b]:] == -1)
+
+
+def _one_page_plan(hit, heat, tier, stamp, step, decay=0.5, hot_above=0.6, cold_below=0.2,
+                   recent=0, cooldown=0, L=8, bs=4):
+    """One sequence of two blocks on pages 0 and 1; block 0 is hit when ``hit``."""
+    sel = np.array([[[0 if hit else -1]]], np.int32)
+    cnt = np.array([[1 if hit else 0]], np.int32)
+    bt = np.array([[0, 1]], np.int32)
+    return oracle.tier_plan(sel, cnt, bt, np.array([L], np.int32), bs, decay, hot_above,
+                            cold_below, recent, cooldown, step,
+                            np.array([heat, 0.5], np.float32), np.array([tier, 0], np.uint8),
+                            np.array([stamp, 0], np.int32))
+
+
+@pytest.mark.parametrize("decay", [0.75, 0.9, 0.125])
+def test_tier_heat_follows_the_geometric_closed_form(decay):
+    """n hits from h0 give 1 - decay^n (1 - h0); n misses then give decay^n times that."""
+    h0, h = 0.3, np.float32(0.3)
+    for n in range(1, 13):
+        out = _one_page_plan(True, h, 0, 0, n, decay=decay, hot_above=2.0, cold_below=-1.0)
+        h = out[0][0]
+        assert out[0][1] == np.float32(np.float32(decay) * np.float32(0.5))  # block 1 missed
+        assert abs(float(h) - (1 - decay ** n * (1 - h0))) < 1e-6
+    top = float(h)
+    for n in range(1, 13):
+        h = _one_page_plan(False, h, 0, 0, 12 + n, decay=decay, hot_above=2.0, cold_below=-1.0)[0][0]
+        assert abs(float(h) - decay ** n * top) < 1e-6
+
+
+def test_tier_thresholds_are_strict():
+    # a hot page whose heat lands exactly on cold_below stays hot; one ulp above demotes it
+    out = _one_page_plan(False, 0.5, 0, 0, 1, cold_below=0.25)
+    assert out[0][0] == 0.25 and out[1][0] == 0 and out[4][0] == 0
+    # (block 1 holds the recent tokens, so that page 0 alone can move)
+    out = _one_page_plan(False, 0.5, 0, 0, 1, recent=4,
+                         cold_below=float(np.nextafter(np.float32(0.25), 1)))
+    assert out[1][0] == 1 and out[3][0, 0] == 0 and out[4][0] == 1 and out[2][0] == 1
+    # a cold page whose heat lands exactly on hot_above stays cold; one ulp below promotes it
+    out = _one_page_plan(True, 0.5, 1, 0, 5, hot_above=0.75)
+    assert out[0][0] == 0.75 and out[1][0] == 1 and out[6][0] == 0
+    out = _one_page_plan(True, 0.5, 1, 0, 5, hot_above=float(np.nextafter(np.float32(0.75), 0)))
+    assert out[1][0] == 0 and out[5][0, 0] == 0 and out[6][0] == 1
+
+
+@pytest.mark.parametrize("cooldown", [0, 1, 4])
+def test_tier_cooldown_counts_steps_since_demotion(cooldown):
+    # demoted at step 10; hit at every later step; promoted exactly at step 10 + cooldown
+    out = _one_page_plan(False, 0.25, 0, 0, 10, cooldown=cooldown)
+    h, t, st = out[0][0], out[1][0], out[2][0]
+    assert t == 1 and st == 10
+    for step in range(11, 20):
+        h = np.float32(0.99)
+        out = _one_page_plan(True, h, t, st, step, cooldown=cooldown)
+        t = out[1][0]
+        assert t == (0 if step >= 10 + cooldown else 1), step
+        if t == 0:
+            break
+    assert t == 0
+
+
+def test_tier_hit_counts_once_over_the_kv_heads():
+    bt = np.array([[0, 1, 2]], np.int32)
+    L = np.array([12], np.int32)
+    base = (np.full(3, 0.5, np.float32), np.zeros(3, np.uint8), np.zeros(3, np.int32))
+    outs = []
+    for rows in ([[1], []], [[], [1]], [[1], [1]], [[0, 1, 2], [1]]):
+        sel, cnt = _sel_rows([rows], 3)
+        outs.append(oracle.tier_plan(sel, cnt, bt, L, 4, 0.5, 0.6, 0.2, 0, 0, 1, *base)[0])
+    for o in outs:
+        assert o[1] == 0.75
+    assert outs[3][0] == 0.75 and outs[0][0] == 0.25
+
+
+def _token_recent(n, bs, L, recent):
+    return any(L - recent <= t < L for t in range(n * bs, (n + 1) * bs))
+
+
+@pytest.mark.parametrize("seed", range(4))
+def test_tier_plan_invariants_over_many_steps(seed):
+    """Each step's transitions satisfy the policy's conditions, checked token by token."""
+    rng = np.random.default_rng(900 + seed)
+    B, Hkv, bs, maxN, K = 3, 2, 4, 12, 5
+    P = B * maxN + 5
+    perm = rng.permutation(P).astype(np.int32)
+    bt = perm[:B * maxN].reshape(B, maxN)
+    heat = rng.random(P).astype(np.float32)
+    tier = rng.integers(0, 2, P).astype(np.uint8)
+    stamp = rng.integers(0, 3, P).astype(np.int32)
+    lens = rng.integers(1, bs * maxN - 12, B)
+    decay, hot_above, cold_below = 0.8, 0.55, 0.3
+    recent = [0, 1, bs - 1, bs, bs + 1][seed % 5]
+    cooldown = 2
+    for step in range(3, 40):
+        lens = np.minimum(lens + rng.integers(0, 3, B), bs * maxN)
+        sel = np.full((B, Hkv, K), -1, np.int32)
+        cnt = np.zeros((B, Hkv), np.int32)
+        for b in range(B):
+            N = -(-int(lens[b]) // bs)
+            for j in range(Hkv):
+                c = int(rng.integers(0, min(K, N) + 1))
+                sel[b, j, :c] = np.sort(rng.choice(N, c, replace=False))
+                cnt[b, j] = c
+        h1, t1, s1, dem, dc, pro, pc = oracle.tier_plan(sel, cnt, bt, lens.astype(np.int32), bs,
+                                                        decay, hot_above, cold_below, recent,
+                                                        cooldown, step, heat, tier, stamp)
+        seen = set()
+        for b in range(B):
+            L = int(lens[b])
+            N = -(-L // bs)
+            hits = {int(x) for j in range(Hkv) for x in sel[b, j, :cnt[b, j]]}
+            moved_down, moved_up = [], []
+            for n in range(N):
+                p = int(bt[b, n])
+                seen.add(p)
+                rec = _token_recent(n, bs, L, recent)
+                assert (h1[p] > decay * heat[p] - 1e-6) if n in hits else (h1[p] <= heat[p])
+                if rec:
+                    assert t1[p] == 0
+                if tier[p] == 0 and t1[p] == 1:
+                    assert not rec and h1[p] < cold_below and s1[p] == step
+                    moved_down.append(p)
+                elif tier[p] == 1 and t1[p] == 0:
+                    assert rec or (h1[p] > hot_above and step - stamp[p] >= cooldown)
+                    assert s1[p] == stamp[p]
+                    moved_up.append(p)
+                elif t1[p] == 0:
+                    assert rec or h1[p] >= cold_below
+                    assert s1[p] == stamp[p]
+                else:
+                    assert not rec and (h1[p] <= hot_above or step - stamp[p] < cooldown)
+                    assert s1[p] == stamp[p]
+            assert dem[b, :dc[b]].tolist() == moved_down
+            assert pro[b, :pc[b]].tolist() == moved_up
+            assert np.all(dem[b, dc[b]:] == -1) and np.all(pro[b, pc[b]:] == -1)
+        rest = [p for p in range(P) if p not in seen]
+        assert np.array_equal(h1[rest], heat[rest]) and np.array_equal(t1[rest], tier[rest])
+        assert np.array_equal(s1[rest], stamp[rest])
+        heat, tier, stamp = h1, t1, s1
