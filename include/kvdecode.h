@@ -15,6 +15,8 @@
  *   kv_paged_decode_attn_tiered decode attention over hot 16-bit and cold code pages
  *   kv_paged_decode_attn_tiered_split the same as a hot launch and a cold launch
  *                         over the block lists split by tier
+ *   kv_tier_plan          hot/cold tier policy: page heat from the step's selection,
+ *                         demotions and promotions with a cooldown
  *   kv_cache_plan         GPU block cache: hits, misses and lookahead eviction
  *   kv_cache_fetch        copy only the missing blocks into their cache slots
  *   kv_cached_decode_attn decode attention over the cached blocks, with each
@@ -396,8 +398,11 @@ kv_status kv_decode_combine(const kv_shape* shape, int32_t num_splits, const flo
  *                    saturated to +-448;  0 for s >= v.
  * The codes are a deterministic function of the stored values.  K/V keep the
  * layout of the source pools with one byte per channel.  Pages not listed are
- * not touched; ids as in kv_block_meta_build.  The block index (kmeta, kmean)
- * is built from the high-precision keys and is not affected.
+ * not touched; ids as in kv_block_meta_build, except that a negative id is a
+ * skipped entry (so a -1-padded list such as kv_tier_plan's demote rows can be
+ * passed whole).  page_valid_tokens may be NULL: every listed page is full
+ * (v = bs).  The block index (kmeta, kmean) is built from the high-precision
+ * keys and is not affected.
  */
 kv_status kv_quantize_pages_fp8(const kv_shape* shape, const void* k_cache, const void* v_cache,
                                 const int32_t* page_ids, const int32_t* page_valid_tokens,
@@ -434,8 +439,9 @@ kv_status kv_paged_decode_attn_fp8(const kv_shape* shape, const void* q, const u
  *   X4[p, j, s, c / 2] holds n of channel c in bits 4 * (c mod 2) .. +3, as
  *                   4-bit two's complement (the even channel in the low nibble).
  * The value a code stands for is n * scale.  fp16 and bf16 pools only
- * (KV_ERR_UNSUPPORTED for fp32).  Pages not listed are not touched; the block
- * index is not affected.
+ * (KV_ERR_UNSUPPORTED for fp32).  Pages not listed are not touched; negative
+ * ids are skipped and a NULL page_valid_tokens means full pages, as for
+ * kv_quantize_pages_fp8; the block index is not affected.
  */
 kv_status kv_quantize_pages_int4(const kv_shape* shape, const void* k_cache, const void* v_cache,
                                  const int32_t* page_ids, const int32_t* page_valid_tokens,
@@ -511,6 +517,50 @@ kv_status kv_paged_decode_attn_tiered_split(
     const int32_t* sel_blocks, const int32_t* sel_count, int32_t sel_stride, float scale,
     int32_t num_splits_hot, int32_t num_splits_cold, float* part_o, float* part_m,
     float* part_l, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Hot/cold tier policy, one decode step (the tiered-offload blog, page
+ * replacement: pages whose heat has fallen move down a tier, and a cooldown
+ * after a demotion keeps a page from moving straight back up; KVDrive §11:
+ * hot blocks keep full precision, cold blocks are stored quantised).  For each
+ * sequence b and block n < N_b = ceil(seq_lens[b] / bs), page p =
+ * block_table[b, n]:
+ *   hit  = n is in sel_blocks[b, j, 0..sel_count[b, j]) for some KV head j
+ *          (row stride sel_stride; the lists of kv_block_select or
+ *          kv_select_decode_attn)
+ *   page_heat[p] = hit ? fma(decay, h, 1 - decay) : decay * h      (fp32, h the
+ *          heat before the call)
+ *   recent = the block holds one of the last recent_tokens tokens of b
+ *   a hot page (page_tier[p] == 0) that is not recent turns cold when
+ *     page_heat[p] < cold_below: page_tier[p] = 1, page_stamp[p] = step;
+ *   a cold page (page_tier[p] != 0) turns hot (page_tier[p] = 0) when it is
+ *     recent, or when page_heat[p] > hot_above and
+ *     step - page_stamp[p] >= cooldown_steps.
+ * demote / promote [B, maxN] receive, per sequence and in block order, the
+ * pages that turned cold / hot, -1 after the last; demote_count /
+ * promote_count [B] their numbers.  page_heat (fp32), page_tier (uint8, the
+ * array kv_paged_decode_attn_tiered reads) and page_stamp (int32) are [P] and
+ * are updated in place; pages that no sequence references, and block_table
+ * entries outside [0, P), are left alone.  Each page may be referenced by at
+ * most one (sequence, block), as in any block table of distinct pages.
+ * recent_tokens >= 1 keeps the page being appended to hot (kv_append_token
+ * writes the 16-bit pools), so every demoted page is full: passing the demote
+ * rows whole (B * maxN ids) to kv_quantize_pages_fp8 / _int4 with
+ * page_valid_tokens NULL writes their cold codes; do that on the same stream
+ * before the next tiered attention call reads page_tier.  A promoted page is
+ * read from the 16-bit pools again, which this library never frees.
+ * Errors: KV_ERR_INVALID_ARG for a NULL array, sel_stride < 1, decay outside
+ * [0, 1], a NaN threshold, recent_tokens < 1, cooldown_steps < 0 or
+ * max_blocks_per_seq > 262144; KV_ERR_ALIGNMENT for an int32 / fp32 array
+ * that is not 4-byte aligned.  All arrays are device memory.
+ */
+kv_status kv_tier_plan(const kv_shape* shape, const int32_t* sel_blocks, const int32_t* sel_count,
+                       int32_t sel_stride, const int32_t* block_table, const int32_t* seq_lens,
+                       float decay, float hot_above, float cold_below, int32_t recent_tokens,
+                       int32_t cooldown_steps, int32_t step, float* page_heat,
+                       uint8_t* page_tier, int32_t* page_stamp, int32_t* demote,
+                       int32_t* demote_count, int32_t* promote, int32_t* promote_count,
+                       void* stream);
 
 /*
  * GPU-resident block cache with lookahead eviction (KVDrive §5.1: a window of

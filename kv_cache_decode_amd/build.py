@@ -19,7 +19,7 @@ BUILD_DIR = os.path.join(HERE, "_build")
 ARCH = os.environ.get("KVD_OFFLOAD_ARCH", "gfx950")
 
 SOURCES = ["kvd_index.hip", "kvd_attn.hip", "kvd_quant.hip", "kvd_cache.hip", "kvd_probe.hip", "kvd_check.hip",
-           "kvd_api.hip"]
+           "kvd_tier.hip", "kvd_api.hip"]
 COMMON = ["-std=c++17", "-O3", "-fPIC", f"--offload-arch={ARCH}", "-Wall", "-Wno-unused-result",
           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
 

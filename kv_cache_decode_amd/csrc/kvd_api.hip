@@ -619,16 +619,16 @@ kv_status quantize_common(const kv_shape* shape, int fmt, const void* k_cache, c
     return fail(KV_ERR_UNSUPPORTED, "%s: INT4 pages are made from fp16 or bf16 pools", name);
   if (num_page_ids < 0) return fail(KV_ERR_INVALID_ARG, "num_page_ids=%d < 0", num_page_ids);
   if (num_page_ids == 0) return ok();
-  if (!k_cache || !v_cache || !page_ids || !page_valid_tokens || !k_codes || !v_codes || !kv_scales)
+  if (!k_cache || !v_cache || !page_ids || !k_codes || !v_codes || !kv_scales)
     return fail(KV_ERR_INVALID_ARG,
-                "%s: k_cache, v_cache, page_ids, page_valid_tokens, the code pools and kv_scales "
-                "are required", name);
+                "%s: k_cache, v_cache, page_ids, the code pools and kv_scales are required", name);
   if ((long)num_page_ids * shape->num_kv_heads > 0x7fffffffL)
     return fail(KV_ERR_INVALID_ARG, "num_page_ids * num_kv_heads overflows int32");
   if (!aligned(k_cache, 16) || !aligned(v_cache, 16) || !aligned(k_codes, 16) ||
       !aligned(v_codes, 16))
     return fail(KV_ERR_ALIGNMENT, "k_cache, v_cache and the code pools must be 16-byte aligned");
-  if (!aligned(page_ids, 4) || !aligned(page_valid_tokens, 4) || !aligned(kv_scales, 8))
+  if (!aligned(page_ids, 4) || (page_valid_tokens && !aligned(page_valid_tokens, 4)) ||
+      !aligned(kv_scales, 8))
     return fail(KV_ERR_ALIGNMENT,
                 "page_ids and page_valid_tokens must be 4-byte aligned, kv_scales 8-byte aligned");
   std::string what = std::string(name) + " launch";
@@ -835,6 +835,46 @@ kv_status kv_cache_plan(const kv_shape* shape, int32_t num_slots, const int32_t*
                                            sel_slots, fetch_block, fetch_slot, fetch_count,
                                            (hipStream_t)stream),
                     "kv_cache_plan launch");
+}
+
+kv_status kv_tier_plan(const kv_shape* shape, const int32_t* sel_blocks, const int32_t* sel_count,
+                       int32_t sel_stride, const int32_t* block_table, const int32_t* seq_lens,
+                       float decay, float hot_above, float cold_below, int32_t recent_tokens,
+                       int32_t cooldown_steps, int32_t step, float* page_heat,
+                       uint8_t* page_tier, int32_t* page_stamp, int32_t* demote,
+                       int32_t* demote_count, int32_t* promote, int32_t* promote_count,
+                       void* stream) {
+  kv_status st = check_shape(shape);
+  if (st != KV_OK) return st;
+  if (shape->max_blocks_per_seq > kvd::kTierPlanMaxBlocks)
+    return fail(KV_ERR_INVALID_ARG, "kv_tier_plan: max_blocks_per_seq=%d exceeds %d",
+                shape->max_blocks_per_seq, kvd::kTierPlanMaxBlocks);
+  if (sel_stride < 1) return fail(KV_ERR_INVALID_ARG, "sel_stride=%d must be >= 1", sel_stride);
+  if (!(decay >= 0.0f && decay <= 1.0f))
+    return fail(KV_ERR_INVALID_ARG, "decay=%g must be in [0, 1]", (double)decay);
+  if (hot_above != hot_above || cold_below != cold_below)
+    return fail(KV_ERR_INVALID_ARG, "hot_above and cold_below must not be NaN");
+  if (recent_tokens < 1)
+    return fail(KV_ERR_INVALID_ARG,
+                "recent_tokens=%d must be >= 1 (the page being appended to stays hot)",
+                recent_tokens);
+  if (cooldown_steps < 0)
+    return fail(KV_ERR_INVALID_ARG, "cooldown_steps=%d must be >= 0", cooldown_steps);
+  if (!sel_blocks || !sel_count || !block_table || !seq_lens || !page_heat || !page_tier ||
+      !page_stamp || !demote || !demote_count || !promote || !promote_count)
+    return fail(KV_ERR_INVALID_ARG, "every array of kv_tier_plan is required");
+  const void* ptrs[] = {sel_blocks, sel_count, block_table, seq_lens, page_heat, page_stamp,
+                        demote, demote_count, promote, promote_count};
+  for (const void* p : ptrs)
+    if (!aligned(p, 4))
+      return fail(KV_ERR_ALIGNMENT, "kv_tier_plan: arrays other than page_tier must be 4-byte aligned");
+  const kvd::TierPolicy pol{decay, hot_above, cold_below, recent_tokens, cooldown_steps};
+  return hip_status(kvd::launch_tier_plan(sel_blocks, sel_count, sel_stride, block_table,
+                                          seq_lens, shape->num_seqs, shape->num_kv_heads,
+                                          shape->max_blocks_per_seq, shape->num_pages, pol, step,
+                                          page_heat, page_tier, page_stamp, demote, demote_count,
+                                          promote, promote_count, (hipStream_t)stream),
+                    "kv_tier_plan launch");
 }
 
 }  // extern "C"

@@ -86,6 +86,19 @@ hipError_t launch_tier_lists(const int32_t* sel, const int32_t* sel_count, int s
                              int32_t* hot, int32_t* hot_count, int32_t* cold, int32_t* cold_count,
                              uint8_t* flags, int32_t* chunk_cold, hipStream_t stream);
 
+// Hot/cold tier policy of kv_tier_plan.
+struct TierPolicy {
+  float decay, hot_above, cold_below;
+  int recent, cooldown;
+};
+constexpr int kTierPlanMaxBlocks = 1 << 18;       // the hit bitmap: 32 KiB of LDS
+
+hipError_t launch_tier_plan(const int32_t* sel, const int32_t* sel_count, int sel_stride,
+                            const int32_t* block_table, const int32_t* seq_lens, int B, int Hkv,
+                            int maxN, int num_pages, const TierPolicy& pol, int step, float* heat,
+                            uint8_t* tier, int32_t* stamp, int32_t* demote, int32_t* demote_count,
+                            int32_t* promote, int32_t* promote_count, hipStream_t stream);
+
 hipError_t launch_cache_plan(const int32_t* sel, const int32_t* sel_count, int sel_stride, int B,
                              int Hkv, int maxN, int C, int32_t* slot_block, int32_t* block_slot,
                              const float* slot_mass, int32_t* sel_slots, int32_t* fetch_block,

@@ -67,8 +67,10 @@ __global__ __launch_bounds__(WAVES * kWave) void quantize_kernel(
     if (u >= units) continue;                      // the whole unit's lanes skip together
     const int i = (int)(u / Hkv);
     const int j = (int)(u - (long)i * Hkv);
-    const size_t tile = (size_t)page_ids[i] * Hkv + j;
-    const int nv = valid_tokens[i];
+    const int pid = page_ids[i];
+    if (pid < 0) continue;                         // a skipped list entry (unit-uniform)
+    const size_t tile = (size_t)pid * Hkv + j;
+    const int nv = valid_tokens ? valid_tokens[i] : kBlockSize;
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
       const St* src = static_cast<const St*>(t ? v_cache : k_cache) + tile * kBlockSize * D +

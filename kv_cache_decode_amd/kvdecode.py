@@ -34,7 +34,8 @@ EXPORTS = (
     "kv_auto_num_splits_tiered", "kv_paged_decode_attn", "kv_decode_combine",
     "kv_quantize_pages_fp8", "kv_paged_decode_attn_fp8", "kv_quantize_pages_int4",
     "kv_paged_decode_attn_int4", "kv_paged_decode_attn_tiered",
-    "kv_tiered_split_workspace_size", "kv_paged_decode_attn_tiered_split", "kv_cache_plan",
+    "kv_tiered_split_workspace_size", "kv_paged_decode_attn_tiered_split", "kv_tier_plan",
+    "kv_cache_plan",
     "kv_cache_fetch", "kv_cache_fetch_codes", "kv_cached_decode_attn_codes",
     "kv_cached_decode_attn_fetch", "kv_cached_decode_attn_fetch_codes",
     "kv_cached_decode_attn", "kv_cache_slot_mass", "kv_check_tables", "kv_probe_stream_read",
@@ -114,6 +115,8 @@ def _load() -> ctypes.CDLL:
         "kv_tiered_split_workspace_size": (SZ, [S, I32]),
         "kv_paged_decode_attn_tiered_split": (I32, [S, P, P, P, P, P, P, I32, P, P, P, P, P, I32,
                                                     F, I32, I32, P, P, P, P, SZ, P]),
+        "kv_tier_plan": (I32, [S, P, P, I32, P, P, F, F, F, I32, I32, I32, P, P, P, P, P, P, P,
+                               P]),
         "kv_cache_plan": (I32, [S, I32, P, P, I32, P, P, P, P, P, P, P, P]),
         "kv_cache_fetch": (I32, [S, I32, P, P, P, P, P, P, I32, P, P, P]),
         "kv_cached_decode_attn": (I32, [S, I32, P, P, P, P, P, P, P, I32, F, I32, P, P, P, P, P]),
@@ -471,6 +474,18 @@ def kv_paged_decode_attn_tiered_split(shape: KVShape, q: Buf, k_cache: Buf, v_ca
         _p(kv_scales), cold_format, _p(page_tier), _p(block_table), _p(seq_lens),
         _p(sel_blocks), _p(sel_count), sel_stride, scale, num_splits_hot, num_splits_cold,
         _p(part_o), _p(part_m), _p(part_l), _p(workspace), workspace_bytes, _stream(stream)))
+
+
+def kv_tier_plan(shape: KVShape, sel_blocks: Buf, sel_count: Buf, sel_stride: int,
+                 block_table: Buf, seq_lens: Buf, decay: float, hot_above: float,
+                 cold_below: float, recent_tokens: int, cooldown_steps: int, step: int,
+                 page_heat: Buf, page_tier: Buf, page_stamp: Buf, demote: Buf, demote_count: Buf,
+                 promote: Buf, promote_count: Buf, stream=None) -> None:
+    _check(_lib.kv_tier_plan(ctypes.byref(shape), _p(sel_blocks), _p(sel_count), sel_stride,
+                             _p(block_table), _p(seq_lens), decay, hot_above, cold_below,
+                             recent_tokens, cooldown_steps, step, _p(page_heat), _p(page_tier),
+                             _p(page_stamp), _p(demote), _p(demote_count), _p(promote),
+                             _p(promote_count), _stream(stream)))
 
 
 def kv_cache_plan(shape: KVShape, num_slots: int, sel_blocks: Buf, sel_count: Buf,

@@ -337,6 +337,45 @@ class DeviceWorkload:
         self.combine(S, stream)
         return S
 
+    # ------------------------------------------------------------ tier policy
+    def tier_init(self, tier=None, heat: float = 0.0):
+        """State of the hot/cold tier policy: per page heat (fp32), tier (uint8,
+        0 hot; ``tier`` gives the initial one, default all hot) and the step of
+        its last demotion, and the [B, maxN] demote / promote lists."""
+        P = self.shape.num_pages
+        B, maxN = self.spec.num_seqs, self.spec.max_blocks
+        dev = self.device
+        self.page_heat = torch.full((P,), heat, dtype=torch.float32, device=dev)
+        self.page_tier = (torch.zeros(P, dtype=torch.uint8, device=dev) if tier is None else
+                          torch.as_tensor(np.asarray(tier, np.uint8)).to(dev))
+        self.page_stamp = torch.zeros(P, dtype=torch.int32, device=dev)
+        self.demote = torch.empty((B, maxN), dtype=torch.int32, device=dev)
+        self.promote = torch.empty_like(self.demote)
+        self.demote_count = torch.empty(B, dtype=torch.int32, device=dev)
+        self.promote_count = torch.empty_like(self.demote_count)
+
+    def tier_step(self, step: int, cold: Optional[str] = None, decay: float = 0.875,
+                  hot_above: float = 0.5, cold_below: float = 0.125, recent_tokens: int = 64,
+                  cooldown_steps: int = 8, stream=None):
+        """kv_tier_plan over the current selection; with ``cold`` ("fp8" or
+        "int4", after quantize_fp8 / quantize_int4) the demoted pages' codes are
+        then written into that code pool (the demote rows passed whole, full
+        pages), on the same stream and without a host sync."""
+        kd.kv_tier_plan(self.shape, self.sel, self.sel_count, self.topk, self.block_table,
+                        self.seq_lens, decay, hot_above, cold_below, recent_tokens,
+                        cooldown_steps, step, self.page_heat, self.page_tier, self.page_stamp,
+                        self.demote, self.demote_count, self.promote, self.promote_count,
+                        stream)
+        n = int(self.demote.numel())
+        if cold == "fp8":
+            kd.kv_quantize_pages_fp8(self.shape, self.k_cache, self.v_cache, self.demote, None, n,
+                                     self.k8, self.v8, self.kv_scales, stream)
+        elif cold == "int4":
+            kd.kv_quantize_pages_int4(self.shape, self.k_cache, self.v_cache, self.demote, None,
+                                      n, self.k4, self.v4, self.kv_scales4, stream)
+        elif cold is not None:
+            raise ValueError(f"cold={cold!r}: 'fp8', 'int4' or None")
+
     # ------------------------------------------------------------ GPU block cache
     def cache_init(self, num_slots: int, k: int, codes: Optional[str] = None):
         """Cache pools [B * C, Hkv, bs, D] and an empty directory for lists of k

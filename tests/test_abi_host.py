@@ -304,6 +304,9 @@ def test_fp8_argument_checks():
     expect(kd.KV_ERR_ALIGNMENT, lambda stream: qz(s, A16, A16, A16, A16, 3, A4, A16, A16, stream=stream))
     expect(kd.KV_ERR_ALIGNMENT, lambda stream: qz(s, A16, A16, A16, A16, 3, A16, A16, A4 + 2, stream=stream))
     qz(s, None, None, None, None, 0, None, None, None, stream=0)     # nothing to do: OK
+    # page_valid_tokens may be NULL (full pages): the next missing array still fails
+    expect(kd.KV_ERR_INVALID_ARG, lambda stream: qz(s, A16, A16, A16, None, 3, A16, A16, None, stream=stream))
+    expect(kd.KV_ERR_ALIGNMENT, lambda stream: qz(s, A16, A16, A16, None, 3, A4, A16, A16, stream=stream))
     at = kd.kv_paged_decode_attn_fp8
 
     def call(scales=A16 + 8, k8=A16, **kw):
@@ -616,3 +619,30 @@ def test_binding_refuses_host_and_strided_tensors():
         kd.kv_block_score_topk(s, q, A16, A16, A16, 4, A16, A16, A16)
     with pytest.raises(ValueError, match="contiguous"):
         kd.kv_block_score_topk(s, q.transpose(0, 1), A16, A16, A16, 4, A16, A16, A16)
+
+
+def test_tier_plan_argument_checks():
+    s = shape()
+
+    def call(shp=s, **kw):
+        args = dict(sel_blocks=A16, sel_count=A16, sel_stride=4, block_table=A16, seq_lens=A16,
+                    decay=0.5, hot_above=0.6, cold_below=0.2, recent_tokens=16,
+                    cooldown_steps=2, step=3, page_heat=A16, page_tier=A16, page_stamp=A16,
+                    demote=A16, demote_count=A16, promote=A16, promote_count=A16)
+        args.update(kw)
+        return lambda stream: kd.kv_tier_plan(shp, stream=stream, **args)
+
+    expect(kd.KV_ERR_INVALID_ARG, call(sel_stride=0))
+    expect(kd.KV_ERR_INVALID_ARG, call(decay=1.5))
+    expect(kd.KV_ERR_INVALID_ARG, call(decay=-0.1))
+    expect(kd.KV_ERR_INVALID_ARG, call(decay=float("nan")))
+    expect(kd.KV_ERR_INVALID_ARG, call(hot_above=float("nan")))
+    expect(kd.KV_ERR_INVALID_ARG, call(cold_below=float("nan")))
+    expect(kd.KV_ERR_INVALID_ARG, call(recent_tokens=0))       # the appended page stays hot
+    expect(kd.KV_ERR_INVALID_ARG, call(cooldown_steps=-1))
+    for name in ("sel_blocks", "sel_count", "block_table", "seq_lens", "page_heat", "page_tier",
+                 "page_stamp", "demote", "demote_count", "promote", "promote_count"):
+        expect(kd.KV_ERR_INVALID_ARG, call(**{name: None}))
+    for name in ("sel_blocks", "page_heat", "page_stamp", "demote", "promote_count"):
+        expect(kd.KV_ERR_ALIGNMENT, call(**{name: ODD}))
+    expect(kd.KV_ERR_INVALID_ARG, call(shp=shape(max_blocks_per_seq=262145, num_pages=262145)))
