@@ -468,6 +468,102 @@ def time_codes(args, copies, k, time_loop, graph_us, fmt: str):
     res["tiered_dense_bytes"], res["tiered_cold_fraction"] = tiered_bytes(spec, data.block_table,
                                                                           tier_np, fmt, s_tier)
     res["tiered_splits"] = s_tier
+    if fmt == "int4":
+        res["tier_policy"] = time_tier_policy(args, copies[0], k)
+    return res
+
+
+TIER_POLICY = {"decay": 0.875, "hot_above": 0.5, "cold_below": 0.125, "recent_tokens": 64,
+               "cooldown_steps": 8}
+
+
+def time_tier_policy(args, dw, k):
+    """The hot/cold tier policy over a CACHE_STEPS-step decode trajectory (the
+    AR(1) queries of the block cache's trajectory), INT4 cold pages in HBM.  A
+    step is: score + Top-K, kv_tier_plan (page heat from the step's selection,
+    demotions and promotions), the INT4 codes of the demoted pages, tiered
+    sparse attention and the merge.  Every page starts hot with heat 0, so the
+    first step demotes every page outside the selection and the recent tokens.
+    The trajectory runs twice more from that state, counting the pages that
+    move, then is captured as one HIP graph (step numbers going on) whose
+    replays give the step time; kv_tier_plan alone is timed as a graph of
+    GRAPH_STEPS calls."""
+    import torch
+    from kv_cache_decode_amd import kvdecode as kd
+    from kv_cache_decode_amd import workload as wl
+    from kv_cache_decode_amd.step import storage_tensor
+
+    spec, data = dw.spec, dw.data
+    q0 = dw.q
+    qs = [storage_tensor(q, spec.dtype).to(dw.device)
+          for q in wl.query_trajectory(data, CACHE_STEPS, CACHE_RHO, seed=21)]
+    S = kd.kv_auto_num_splits_tiered(dw.shape, k)
+    dw.tier_init()
+    step_no = [0]
+
+    def step(q, counts=None):
+        dw.q = q
+        dw.score_topk(k)
+        dw.tier_step(step_no[0], cold="int4", **TIER_POLICY)
+        dw.attention_tiered(True, "int4", dw.page_tier, S)
+        dw.combine(S)
+        step_no[0] += 1
+        if counts is not None:
+            counts.append(torch.stack([dw.demote_count.sum(), dw.promote_count.sum()]))
+
+    first, moved = [], []
+    for q in qs:                                 # from all hot: the first step demotes
+        step(q, first)
+    for _ in range(2):                           # the same trajectory again, counted
+        for q in qs:
+            step(q, moved)
+    torch.cuda.synchronize()
+    moved = torch.stack(moved).cpu().numpy().astype(np.int64)
+    first = torch.stack(first).cpu().numpy().astype(np.int64)
+    hot = float((dw.page_tier[:spec.used_pages] == 0).float().mean())
+
+    res = {"steps": CACHE_STEPS, "rho": CACHE_RHO, "topk_blocks": k, "splits": S,
+           "cold": "int4", "policy": dict(TIER_POLICY),
+           "first_step_demoted_pages": int(first[0, 0]),
+           "demoted_pages_per_step": float(moved[:, 0].mean()),
+           "promoted_pages_per_step": float(moved[:, 1].mean()),
+           "hot_page_fraction_after": hot}
+    try:
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            for q in qs:
+                step(q)
+        torch.cuda.current_stream().wait_stream(side)
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for q in qs:
+                step(q)
+        for _ in range(GRAPH_WARM_REPLAYS):
+            g.replay()
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(GRAPH_MIN_REPLAYS)]
+        torch.cuda.synchronize()
+        for a, b in ev:
+            a.record()
+            g.replay()
+            b.record()
+        torch.cuda.synchronize()
+        del g
+        res["step_us"] = float(np.median([a.elapsed_time(b) for a, b in ev])) * 1e3 / len(qs)
+        res["timing"] = "HIP graph of the trajectory, median of replays"
+        res["tier_plan_us"] = graph_step_us(
+            lambda c: c.tier_step(step_no[0], cold=None, **TIER_POLICY), [dw], args)
+    except RuntimeError as e:
+        log(f"[bench] tier policy graph capture failed ({e}); timing eager launches")
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for q in qs:
+            step(q)
+        torch.cuda.synchronize()
+        res["step_us"] = (time.perf_counter() - t0) * 1e6 / len(qs)
+        res["timing"] = "eager launches (host time included)"
+    dw.q = q0
     return res
 
 
@@ -1039,6 +1135,7 @@ def codes_record(spec, f: dict, fmt: str) -> dict:
             "split_launches_splits": f["tiered_split_splits"],
             "split_launches_gbps": f["tiered_dense_bytes"] / (f["tiered_split_dense_us"] * 1e-6)
             / 1e9},
+        **({"tier_policy": f["tier_policy"]} if "tier_policy" in f else {}),
     }
 
 
@@ -1084,7 +1181,7 @@ def main():
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}, WORLD_SIZE "
-              f"{world}); this build has no multi-GPU path.", file=sys.stderr)
+              f"{world}); the library has no multi-GPU path.", file=sys.stderr)
         sys.exit(2)
     if args.copy_calibration:
         copy_calibration()

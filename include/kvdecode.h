@@ -526,8 +526,9 @@ kv_status kv_paged_decode_attn_tiered_split(
  * sequence b and block n < N_b = ceil(seq_lens[b] / bs), page p =
  * block_table[b, n]:
  *   hit  = n is in sel_blocks[b, j, 0..sel_count[b, j]) for some KV head j
- *          (row stride sel_stride; the lists of kv_block_select or
- *          kv_select_decode_attn)
+ *          (sel_blocks is [B, Hkv, sel_stride] int32 and is read whole, the
+ *          entries past a count included; a count above sel_stride counts as
+ *          sel_stride; the lists of kv_block_select or kv_select_decode_attn)
  *   page_heat[p] = hit ? fma(decay, h, 1 - decay) : decay * h      (fp32, h the
  *          heat before the call)
  *   recent = the block holds one of the last recent_tokens tokens of b
@@ -549,7 +550,8 @@ kv_status kv_paged_decode_attn_tiered_split(
  * page_valid_tokens NULL writes their cold codes; do that on the same stream
  * before the next tiered attention call reads page_tier.  A promoted page is
  * read from the 16-bit pools again, which this library never frees.
- * Errors: KV_ERR_INVALID_ARG for a NULL array, sel_stride < 1, decay outside
+ * Errors: KV_ERR_INVALID_ARG for a NULL array, sel_stride < 1 or
+ * sel_stride * num_kv_heads > 2^30, decay outside
  * [0, 1], a NaN threshold, recent_tokens < 1, cooldown_steps < 0 or
  * max_blocks_per_seq > 262144; KV_ERR_ALIGNMENT for an int32 / fp32 array
  * that is not 4-byte aligned.  All arrays are device memory.

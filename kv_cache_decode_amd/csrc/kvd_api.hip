@@ -849,7 +849,10 @@ kv_status kv_tier_plan(const kv_shape* shape, const int32_t* sel_blocks, const i
   if (shape->max_blocks_per_seq > kvd::kTierPlanMaxBlocks)
     return fail(KV_ERR_INVALID_ARG, "kv_tier_plan: max_blocks_per_seq=%d exceeds %d",
                 shape->max_blocks_per_seq, kvd::kTierPlanMaxBlocks);
-  if (sel_stride < 1) return fail(KV_ERR_INVALID_ARG, "sel_stride=%d must be >= 1", sel_stride);
+  if (sel_stride < 1 || (long)sel_stride * shape->num_kv_heads > (1L << 30))
+    return fail(KV_ERR_INVALID_ARG,
+                "sel_stride=%d must be >= 1, and sel_stride * num_kv_heads at most 2^30",
+                sel_stride);
   if (!(decay >= 0.0f && decay <= 1.0f))
     return fail(KV_ERR_INVALID_ARG, "decay=%g must be in [0, 1]", (double)decay);
   if (hot_above != hot_above || cold_below != cold_below)

@@ -481,11 +481,19 @@ def kv_tier_plan(shape: KVShape, sel_blocks: Buf, sel_count: Buf, sel_stride: in
                  cold_below: float, recent_tokens: int, cooldown_steps: int, step: int,
                  page_heat: Buf, page_tier: Buf, page_stamp: Buf, demote: Buf, demote_count: Buf,
                  promote: Buf, promote_count: Buf, stream=None) -> None:
-    _check(_lib.kv_tier_plan(ctypes.byref(shape), _p(sel_blocks), _p(sel_count), sel_stride,
-                             _p(block_table), _p(seq_lens), decay, hot_above, cold_below,
-                             recent_tokens, cooldown_steps, step, _p(page_heat), _p(page_tier),
-                             _p(page_stamp), _p(demote), _p(demote_count), _p(promote),
-                             _p(promote_count), _stream(stream)))
+    L = _Lay(shape)
+    lists = L.B * L.maxN * 4
+    _check(_lib.kv_tier_plan(ctypes.byref(shape), _p(sel_blocks, L.sel(sel_stride), "sel_blocks", True),
+                             _p(sel_count, L.rows, "sel_count", True), sel_stride,
+                             _p(block_table, L.table, "block_table", True),
+                             _p(seq_lens, L.lens, "seq_lens", True), decay, hot_above, cold_below,
+                             recent_tokens, cooldown_steps, step, _p(page_heat, L.P * 4, "page_heat"),
+                             _p(page_tier, L.P, "page_tier"),
+                             _p(page_stamp, L.P * 4, "page_stamp", True),
+                             _p(demote, lists, "demote", True),
+                             _p(demote_count, L.B * 4, "demote_count", True),
+                             _p(promote, lists, "promote", True),
+                             _p(promote_count, L.B * 4, "promote_count", True), _stream(stream)))
 
 
 def kv_cache_plan(shape: KVShape, num_slots: int, sel_blocks: Buf, sel_count: Buf,

@@ -633,6 +633,8 @@ def test_tier_plan_argument_checks():
         return lambda stream: kd.kv_tier_plan(shp, stream=stream, **args)
 
     expect(kd.KV_ERR_INVALID_ARG, call(sel_stride=0))
+    # the plan reads the [B, Hkv, sel_stride] rows whole: their positions must fit in int32
+    expect(kd.KV_ERR_INVALID_ARG, call(sel_stride=(1 << 30) // s.num_kv_heads + 1))
     expect(kd.KV_ERR_INVALID_ARG, call(decay=1.5))
     expect(kd.KV_ERR_INVALID_ARG, call(decay=-0.1))
     expect(kd.KV_ERR_INVALID_ARG, call(decay=float("nan")))

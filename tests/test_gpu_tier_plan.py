@@ -29,6 +29,8 @@ def dev(a, gpu, dtype=np.int32):
 
 
 def random_lists(rng, lens, Hkv, K):
+    """Random ascending lists; the entries past each count hold block ids too
+    (and -1s), which the plan must ignore: it reads the rows whole."""
     B = len(lens)
     sel = np.full((B, Hkv, K), -1, np.int32)
     cnt = np.zeros((B, Hkv), np.int32)
@@ -38,6 +40,8 @@ def random_lists(rng, lens, Hkv, K):
             c = int(rng.integers(0, min(K, N) + 1))
             if c:
                 sel[b, j, :c] = np.sort(rng.choice(N, c, replace=False))
+            if c < K:
+                sel[b, j, c:] = rng.integers(-1, max(N, 1), K - c)
             cnt[b, j] = c
     return sel, cnt
 
@@ -88,8 +92,9 @@ CASES = [
     (3, 2, 20, 5, (37, 1, 150), 0.8, 0.55, 0.3, 1, 2, False),
     (2, 3, 40, 8, (0, 600), 0.5, 0.75, 0.25, 16, 0, True),      # empty sequence; exact ties
     (4, 8, 130, 24, (17, 2000, 1024, 2063), 0.875, 0.5, 0.125, 17, 3, True),
-    (2, 4, 5000, 300, (79_000, 33_333), 0.9, 0.4, 0.2, 64, 5, False),   # two kernel passes
-    (1, 2, 9000, 64, (143_990,), 0.0, 0.5, 0.5, 100, 1, False),  # decay 0: heat = hit
+    (2, 4, 5000, 300, (79_000, 33_333), 0.9, 0.4, 0.2, 64, 5, False),
+    (1, 2, 9000, 64, (143_990,), 0.0, 0.5, 0.5, 100, 1, False),  # decay 0; two kernel passes
+    (2, 3, 20000, 700, (319_000, 150_001), 0.75, 0.5, 0.25, 40, 2, False),   # three passes
     (2, 1, 300, 300, (4800, 4791), 1.0, 0.5, 0.5, 33, 0, True),  # decay 1: heat frozen
 ]
 
