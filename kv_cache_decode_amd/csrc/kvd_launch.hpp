@@ -91,7 +91,7 @@ struct TierPolicy {
   float decay, hot_above, cold_below;
   int recent, cooldown;
 };
-constexpr int kTierPlanMaxBlocks = 1 << 18;       // the hit bitmap: 32 KiB of LDS
+constexpr int kTierPlanMaxBlocks = 1 << 18;       // blocks per sequence (64 passes of the list compaction)
 
 hipError_t launch_tier_plan(const int32_t* sel, const int32_t* sel_count, int sel_stride,
                             const int32_t* block_table, const int32_t* seq_lens, int B, int Hkv,

@@ -199,6 +199,27 @@ def test_group_score_is_max_over_the_group_and_reduces_for_g1():
     np.testing.assert_array_equal(gs1, hs)
 
 
+
+def test_group_score_is_the_groups_support_function_by_corner_enumeration():
+    """Brute force, independent of the per-head formula: the group score is the
+    largest q_h . x over the group's heads h and over every corner x of the
+    block's [kmin, kmax] box, computed as one library matrix product per block
+    (heads x corners).  With the box taken from numpy's min and max over the
+    block's valid key rows, no part of the oracle enters the expected value."""
+    data = mk(B=2, Hq=8, Hkv=2, D=6, lens=(45, 18), seed=61)
+    q64, k64 = data.q64(), data.k64()
+    hs = oracle.head_scores(q64, full_meta(data), data.block_table, data.seq_lens, 16)
+    gs = oracle.group_scores(hs, 2)                                            # 2 KV heads
+    corners = np.array(list(itertools.product([0, 1], repeat=6)), bool)       # [64, 6]
+    for b in range(2):
+        L = data.spec.seq_lens[b]
+        for j in range(2):
+            for n in range(data.spec.blocks(b)):
+                rows = k64[data.block_table[b, n], j, :min(16, L - 16 * n)]    # valid keys
+                box = np.where(corners, rows.max(axis=0), rows.min(axis=0))    # [64, 6]
+                want = float((q64[b, 4 * j:4 * j + 4] @ box.T).max())
+                assert gs[b, j, n] == pytest.approx(want, rel=1e-13, abs=1e-13)
+
 def test_scores_invariant_under_page_permutation():
     data = mk(B=2, Hq=4, Hkv=2, D=8, lens=(40, 30), seed=19)
     hs0 = oracle.head_scores(data.q64(), full_meta(data), data.block_table, data.seq_lens, 16)
@@ -930,6 +951,34 @@ def test_slot_mass_is_the_attention_weight_of_each_block():
         untouched = set(range(6)) - set(slots[0, j, :cnt[0, j]].tolist())
         assert all(m[0, j, c] == 0 for c in untouched)
 
+
+
+def test_slot_mass_is_the_softmax_mass_of_each_block_over_the_selection():
+    """Independent of the oracle's block LSEs: each head's softmax over the
+    logits of every token of the selected blocks (scipy), summed per block, max
+    over the group's heads, placed at the block's slot; untouched slots 0."""
+    data = mk(B=2, Hq=4, Hkv=2, D=16, lens=(90, 41), seed=62)
+    q64, k64 = data.q64(), data.k64()
+    scale = 0.25
+    sel = np.array([[[0, 2, 5, -1], [1, 3, 4, -1]], [[2, -1, -1, -1], [0, 1, 2, -1]]], np.int32)
+    cnt = np.array([[3, 3], [1, 3]], np.int32)
+    slots = np.array([[[4, 0, 2, -1], [1, 5, 3, -1]], [[3, -1, -1, -1], [2, 0, 1, -1]]], np.int32)
+    bl = oracle.block_lse(q64, k64, data.block_table, data.seq_lens, 16, scale, sel, cnt)
+    _, lse = oracle.attention(q64, k64, data.v64(), data.block_table, data.seq_lens, scale, sel, cnt)
+    m = oracle.slot_mass(bl, lse, cnt, slots, 6)
+    for b in range(2):
+        L = data.spec.seq_lens[b]
+        for j in range(2):
+            blocks = sel[b, j, :cnt[b, j]]
+            sizes = [min(16, L - 16 * n) for n in blocks]
+            K = gather(k64, data, b, j, blocks)                                 # [T, D]
+            want = np.zeros(6)
+            for h in range(2 * j, 2 * j + 2):
+                p = scipy.special.softmax(scale * (K @ q64[b, h]))
+                mass = np.add.reduceat(p, np.cumsum([0] + sizes[:-1]))
+                for pos, slot in enumerate(slots[b, j, :cnt[b, j]]):
+                    want[slot] = max(want[slot], mass[pos])
+            np.testing.assert_allclose(m[b, j], want, rtol=1e-12, atol=0)
 
 # ---------------------------------------------------------------- tier plan
 # tiered-offload blog page, page replacement (heat, hysteresis cooldown);
