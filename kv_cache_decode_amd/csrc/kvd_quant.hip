@@ -37,11 +37,14 @@ __device__ inline void store_codes(uint8_t* dst, const CodeChunk<E>& cc) {
   }
 }
 
-// Lane (us, c) owns channel chunk c (E channels) of unit us of a wave step, as
-// in the index build: a unit is one (page, KV head); a wave step covers
-// 64 / LPR consecutive units.  The lane keeps the unit's 16 rows of its chunk
-// in registers, the LPR lanes of the unit reduce the amax, and every lane then
-// encodes and stores its own chunk.  K and V are done one after the other.
+// One wave per unit, a unit being one (page, KV head): lane (g, c) owns
+// channel chunk c (E channels) of rows g, g + RG, g + 2 RG, ... (RG = 64 / LPR
+// row groups, so one load instruction reads RG whole consecutive rows).  The
+// K and V rows of the unit are requested together; each tensor's amax is
+// reduced over the whole wave, and every lane then encodes and stores its own
+// chunks.  Spreading a unit over all 64 lanes keeps a lane's share of the
+// correctly rounded divisions at 16 / RG rows, which sets how long a wave
+// takes when only a few pages are quantised (the demotions of one decode step).
 constexpr int kFmtFp8 = 8, kFmtInt4 = 4;
 
 template <typename DT, int D, int WAVES, int FMT>
@@ -52,71 +55,85 @@ __global__ __launch_bounds__(WAVES * kWave) void quantize_kernel(
   using G_ = RowGeom<DT, D>;
   using St = typename DT::storage;
   constexpr int E = G_::E, LPR = G_::LPR;
+  constexpr int RG = kWave / LPR;                  // row groups: rows per load instruction
+  constexpr int RPL = kBlockSize / RG;             // rows per lane
   static_assert(FMT == kFmtFp8 || E == 8, "INT4 pages hold 16-bit sources (8 channels per lane)");
   // code bytes per row and per lane chunk
   constexpr int RB = FMT == kFmtFp8 ? D : D / 2, CB = FMT == kFmtFp8 ? E : E / 2;
-  constexpr int UPS = kWave / LPR;
   const int lane = threadIdx.x & (kWave - 1);
-  const int us = lane / LPR, c = lane % LPR;
+  const int g = lane / LPR, c = lane % LPR;
   const long units = (long)n_ids * Hkv;
-  const long steps = (units + UPS - 1) / UPS;
   const long nwaves = (long)gridDim.x * WAVES;
-
-  for (long step = (long)blockIdx.x * WAVES + (threadIdx.x >> 6); step < steps; step += nwaves) {
-    const long u = step * UPS + us;
-    if (u >= units) continue;                      // the whole unit's lanes skip together
-    const int i = (int)(u / Hkv);
-    const int j = (int)(u - (long)i * Hkv);
-    const int pid = page_ids[i];
-    if (pid < 0) continue;                         // a skipped list entry (unit-uniform)
-    const size_t tile = (size_t)pid * Hkv + j;
-    const int nv = valid_tokens ? valid_tokens[i] : kBlockSize;
+  // the wave's units are u0, u0 + nwaves, ...; lane l fetches the page id (and
+  // valid count) of the l-th of the next 64 in one load, and a ballot lists
+  // those with a page: skipped entries (negative ids) then cost no memory
+  // round trip, however long the list
+  for (long ub = (long)blockIdx.x * WAVES + (threadIdx.x >> 6); ub < units; ub += kWave * nwaves) {
+    const long ul = ub + (long)lane * nwaves;
+    const int il = ul < units ? (int)(ul / Hkv) : 0;
+    const int pid_l = ul < units ? page_ids[il] : -1;
+    const int nv_l = (ul < units && valid_tokens) ? valid_tokens[il] : kBlockSize;
+    uint64_t todo = __ballot(pid_l >= 0);
+    while (todo) {
+      const int slot = __builtin_ctzll(todo);      // wave-uniform
+      todo &= todo - 1;
+      const long u = ub + (long)slot * nwaves;
+      const int i = (int)(u / Hkv);
+      const int j = (int)(u - (long)i * Hkv);
+      const int pid = __builtin_amdgcn_readlane(pid_l, slot);
+      const int nv = __builtin_amdgcn_readlane(nv_l, slot);
+      const size_t tile = (size_t)pid * Hkv + j;
+      uint4 w[2][RPL];
 #pragma unroll
-    for (int t = 0; t < 2; ++t) {
-      const St* src = static_cast<const St*>(t ? v_cache : k_cache) + tile * kBlockSize * D +
-                      (size_t)c * E;
-      uint8_t* dst = (t ? v8 : k8) + tile * kBlockSize * RB + (size_t)c * CB;
-      uint4 w[kBlockSize];
+      for (int t = 0; t < 2; ++t) {
+        const St* src = static_cast<const St*>(t ? v_cache : k_cache) + tile * kBlockSize * D +
+                        (size_t)c * E;
 #pragma unroll
-      for (int r = 0; r < kBlockSize; ++r) w[r] = load16_stream(src + (size_t)r * D);
-      float amax = 0.0f;
-#pragma unroll
-      for (int r = 0; r < kBlockSize; ++r) {
-        if (r < nv) {
-          float f[E];
-          DT::widen(w[r], f);
-#pragma unroll
-          for (int e = 0; e < E; ++e) amax = fmaxf(amax, fabsf(f[e]));
-        }
+        for (int k = 0; k < RPL; ++k) w[t][k] = load16_stream(src + (size_t)(k * RG + g) * D);
       }
-      amax = group_reduce<LPR, OpMax>(amax);
-      const float sc = amax > 0.0f ? __fdiv_rn(amax, FMT == kFmtFp8 ? 448.0f : 7.0f) : 1.0f;
 #pragma unroll
-      for (int r = 0; r < kBlockSize; ++r) {
-        if constexpr (FMT == kFmtFp8) {
-          CodeChunk<E> cc;
+      for (int t = 0; t < 2; ++t) {
+        uint8_t* dst = (t ? v8 : k8) + tile * kBlockSize * RB + (size_t)c * CB;
+        float amax = 0.0f;
 #pragma unroll
-          for (int k = 0; k < E / 4; ++k) cc.w[k] = 0u;
-          if (r < nv) {
+        for (int k = 0; k < RPL; ++k) {
+          if (k * RG + g < nv) {
             float f[E];
-            DT::widen(w[r], f);
+            DT::widen(w[t][k], f);
 #pragma unroll
-            for (int e = 0; e < E; ++e)
-              cc.w[e / 4] |= fp8_encode(__fdiv_rn(f[e], sc)) << (8 * (e % 4));
+            for (int e = 0; e < E; ++e) amax = fmaxf(amax, fabsf(f[e]));
           }
-          store_codes<E>(dst + (size_t)r * RB, cc);
-        } else {
-          uint32_t cw = 0u;                  // eight nibbles, channel e in bits 4e..4e+3
-          if (r < nv) {
-            float f[E];
-            DT::widen(w[r], f);
-#pragma unroll
-            for (int e = 0; e < E; ++e) cw |= int4_encode(__fdiv_rn(f[e], sc)) << (4 * e);
-          }
-          *reinterpret_cast<uint32_t*>(dst + (size_t)r * RB) = cw;
         }
+        amax = group_reduce<kWave, OpMax>(amax);
+        const float sc = amax > 0.0f ? __fdiv_rn(amax, FMT == kFmtFp8 ? 448.0f : 7.0f) : 1.0f;
+#pragma unroll
+        for (int k = 0; k < RPL; ++k) {
+          const int r = k * RG + g;
+          if constexpr (FMT == kFmtFp8) {
+            CodeChunk<E> cc;
+#pragma unroll
+            for (int q = 0; q < E / 4; ++q) cc.w[q] = 0u;
+            if (r < nv) {
+              float f[E];
+              DT::widen(w[t][k], f);
+#pragma unroll
+              for (int e = 0; e < E; ++e)
+                cc.w[e / 4] |= fp8_encode(__fdiv_rn(f[e], sc)) << (8 * (e % 4));
+            }
+            store_codes<E>(dst + (size_t)r * RB, cc);
+          } else {
+            uint32_t cw = 0u;                  // eight nibbles, channel e in bits 4e..4e+3
+            if (r < nv) {
+              float f[E];
+              DT::widen(w[t][k], f);
+#pragma unroll
+              for (int e = 0; e < E; ++e) cw |= int4_encode(__fdiv_rn(f[e], sc)) << (4 * e);
+            }
+            *reinterpret_cast<uint32_t*>(dst + (size_t)r * RB) = cw;
+          }
+        }
+        if (lane == 0) scales[tile * 2 + t] = sc;
       }
-      if (c == 0) scales[tile * 2 + t] = sc;
     }
   }
 }
@@ -130,9 +147,8 @@ hipError_t launch_quantize(int fmt, int dtype, int D, const void* k_cache, const
       using DT = decltype(dt);
       constexpr int DD = decltype(d)::value;
       constexpr int WAVES = 4;
-      constexpr int UPS = kWave / RowGeom<DT, DD>::LPR;
-      const long steps = ((long)n_ids * Hkv + UPS - 1) / UPS;
-      const long want = (steps + WAVES - 1) / WAVES;
+      const long units = (long)n_ids * Hkv;          // one wave per unit up to the cap
+      const long want = (units + WAVES - 1) / WAVES;
       const int grid = (int)std::min<long>(want, (long)cu_count() * KVD_QUANT_WGS_PER_CU);
       if (fmt == kFmtFp8) {
         hipLaunchKernelGGL((quantize_kernel<DT, DD, WAVES, kFmtFp8>), dim3(grid),
