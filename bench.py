@@ -485,9 +485,12 @@ def time_tier_policy(args, dw, k):
     sparse attention and the merge.  Every page starts hot with heat 0, so the
     first step demotes every page outside the selection and the recent tokens.
     The trajectory runs twice more from that state, counting the pages that
-    move, then is captured as one HIP graph (step numbers going on) whose
-    replays give the step time; kv_tier_plan alone is timed as a graph of
-    GRAPH_STEPS calls."""
+    move, once more on a side stream, and is then captured as one HIP graph
+    with the next step numbers.  Each timed replay starts from the state the
+    capture followed (heat, tier and stamp restored outside the events), so
+    every replay runs the same continuation of the trajectory; the median
+    replay gives the step time.  kv_tier_plan alone is timed as a graph of
+    GRAPH_STEPS calls (it keeps updating the state it reads)."""
     import torch
     from kv_cache_decode_amd import kvdecode as kd
     from kv_cache_decode_amd import workload as wl
@@ -535,23 +538,30 @@ def time_tier_policy(args, dw, k):
             for q in qs:
                 step(q)
         torch.cuda.current_stream().wait_stream(side)
+        # the step numbers are launch arguments, fixed at capture: every replay
+        # starts from the policy state the capture followed (restored, untimed),
+        # so each one runs the same continuation of the counted trajectory
+        state = [t.clone() for t in (dw.page_heat, dw.page_tier, dw.page_stamp)]
         g = torch.cuda.CUDAGraph()
         with torch.cuda.graph(g):
             for q in qs:
                 step(q)
-        for _ in range(GRAPH_WARM_REPLAYS):
-            g.replay()
-        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-              for _ in range(GRAPH_MIN_REPLAYS)]
-        torch.cuda.synchronize()
-        for a, b in ev:
+        times = []
+        for rep in range(GRAPH_WARM_REPLAYS + GRAPH_MIN_REPLAYS):
+            for t, s0 in zip((dw.page_heat, dw.page_tier, dw.page_stamp), state):
+                t.copy_(s0)
+            a, b_ = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            torch.cuda.synchronize()
             a.record()
             g.replay()
-            b.record()
-        torch.cuda.synchronize()
+            b_.record()
+            torch.cuda.synchronize()
+            if rep >= GRAPH_WARM_REPLAYS:
+                times.append(a.elapsed_time(b_))
         del g
-        res["step_us"] = float(np.median([a.elapsed_time(b) for a, b in ev])) * 1e3 / len(qs)
-        res["timing"] = "HIP graph of the trajectory, median of replays"
+        res["step_us"] = float(np.median(times)) * 1e3 / len(qs)
+        res["timing"] = ("HIP graph of the trajectory, each replay from the same policy state, "
+                         "median of replays")
         res["tier_plan_us"] = graph_step_us(
             lambda c: c.tier_step(step_no[0], cold=None, **TIER_POLICY), [dw], args)
     except RuntimeError as e:
