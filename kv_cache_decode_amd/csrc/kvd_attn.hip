@@ -33,15 +33,25 @@
 #if KVD_MFMA_WAVES_PER_EU > 0
 #define KVD_MFMA_OCCUPANCY __attribute__((amdgpu_waves_per_eu(KVD_MFMA_WAVES_PER_EU)))
 // tiered instances carry both page paths; 3 waves per SIMD caps them at 168
-// VGPRs (registers go in granules of 8, so 169 would leave room for 2 waves)
+// VGPRs (registers go in granules of 8, so 169 would leave room for 2 waves).
+// With INT4 cold pages that cap spills a few dozen bytes to scratch; the
+// selected-list (sparse) instances, which give each compute unit few waves
+// anyway, take 2 waves per SIMD and no spill (the 128k tier-policy step 43.0
+// -> 40.9 us), while the dense ones keep 3 (at 2 they took 63 against 50.5 us).
 #ifndef KVD_MFMA_TIER_WAVES_PER_EU
 #define KVD_MFMA_TIER_WAVES_PER_EU 3
 #endif
-#define KVD_MFMA_OCCUPANCY_T(cold) \
-  __attribute__((amdgpu_waves_per_eu((cold) ? KVD_MFMA_TIER_WAVES_PER_EU : KVD_MFMA_WAVES_PER_EU)))
+#ifndef KVD_MFMA_TIER_INT4_SPARSE_WAVES_PER_EU
+#define KVD_MFMA_TIER_INT4_SPARSE_WAVES_PER_EU 2
+#endif
+#define KVD_MFMA_OCCUPANCY_T(cold, sparse)                                                   \
+  __attribute__((amdgpu_waves_per_eu(                                                      \
+      (cold) ? (((cold) == 4 && (sparse)) ? KVD_MFMA_TIER_INT4_SPARSE_WAVES_PER_EU         \
+                                          : KVD_MFMA_TIER_WAVES_PER_EU)                    \
+             : KVD_MFMA_WAVES_PER_EU)))
 #else
 #define KVD_MFMA_OCCUPANCY
-#define KVD_MFMA_OCCUPANCY_T(cold)
+#define KVD_MFMA_OCCUPANCY_T(cold, sparse)
 #endif
 
 namespace kvd {
@@ -1240,7 +1250,7 @@ __device__ __forceinline__ void mfma_attn_split(
 }
 
 template <typename DT, int D, int G, int WAVES, bool SPARSE, int KVQ, int COLD = 0, bool FETCH = false>
-__global__ __launch_bounds__(WAVES * kWave) KVD_MFMA_OCCUPANCY_T(COLD) void paged_attn_mfma_kernel(
+__global__ __launch_bounds__(WAVES * kWave) KVD_MFMA_OCCUPANCY_T(COLD, SPARSE) void paged_attn_mfma_kernel(
     const void* __restrict__ q, const void* __restrict__ k_cache, const void* __restrict__ v_cache,
     const float* __restrict__ kv_scales, const int32_t* __restrict__ block_table,
     const int32_t* __restrict__ seq_lens, const int32_t* __restrict__ sel,
