@@ -1295,7 +1295,7 @@ __global__ __launch_bounds__(kSelAttnWaves * kWave) KVD_MFMA_OCCUPANCY void sele
     int Hkv, int maxN, int S, float qscale, float* __restrict__ part_o,
     float* __restrict__ part_m, float* __restrict__ part_l) {
   constexpr int W = kSelAttnWaves, NT = W * kWave;
-  __shared__ TopkSmem<NT> sm;
+  __shared__ TopkSmemFor<NT, EPT> sm;
   __shared__ int32_t lst[kSelAttnListMax];
   const int j = blockIdx.y, b = blockIdx.z;
   const size_t u = (size_t)b * Hkv + j;

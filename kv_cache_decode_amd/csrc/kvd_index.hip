@@ -555,7 +555,7 @@ __global__ __launch_bounds__(NT) void topk_kernel(const float* __restrict__ scor
                                                     int Hkv, int maxN, int K, int sink,
                                                     int local, int32_t* __restrict__ sel,
                                                     int32_t* __restrict__ sel_count) {
-  __shared__ TopkSmem<NT> sm;
+  __shared__ TopkSmemFor<NT, EPT> sm;
   const int j = blockIdx.x, b = blockIdx.y;
   const size_t u = (size_t)b * Hkv + j;
   int32_t* out = sel + u * K;

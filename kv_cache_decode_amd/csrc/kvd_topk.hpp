@@ -66,7 +66,16 @@ __device__ inline uint32_t block_exclusive_scan(uint32_t v, uint32_t* buf) {
 // Most keys the rank count after the wide pass resolves (else 8-bit passes go on).
 constexpr int kTopkCandMax = 512;
 
-template <int NT>
+// Keys a thread keeps in registers.  Rows of more than 32 keys per thread
+// (EPT 64: up to 65536 blocks) keep keys 32 .. EPT-1 in LDS instead, one word
+// per thread per key, lane-strided (thread t's key 32 + i at xkeys[i * NT + t],
+// so a wave's accesses fall on distinct banks): at 1024 threads a thread has
+// 128 VGPRs, and 64 keys in registers spilled to scratch memory.
+constexpr int kTopkRegKeys = 32;
+template <int EPT>
+constexpr int topk_lds_keys() { return EPT > kTopkRegKeys ? EPT - kTopkRegKeys : 0; }
+
+template <int NT, int XK = 0>
 struct TopkSmem {
   static constexpr int NW = NT / kWave;
   static_assert(NW % 4 == 0, "wave partials are read 4 at a time");
@@ -83,7 +92,10 @@ struct TopkSmem {
   uint32_t cand_n;
   uint32_t cand_key[kTopkCandMax];
   int32_t cand_idx[kTopkCandMax];
+  alignas(16) uint32_t xkeys[XK > 0 ? XK * NT : 1];
 };
+template <int NT, int EPT>
+using TopkSmemFor = TopkSmem<NT, topk_lds_keys<EPT>()>;
 
 // The selected blocks go to emit(position, block) (positions 0..K_eff-1 of the
 // ascending list); when out is not null, K_eff goes to *count_out and -1 to
@@ -91,31 +103,40 @@ struct TopkSmem {
 template <int NT, int EPT, typename Emit>
 __device__ inline void topk_row(const float* __restrict__ row, int maxN, int L, int K, int sink,
                                 int local, int32_t* __restrict__ out,
-                                int32_t* __restrict__ count_out, TopkSmem<NT>& sm, Emit&& emit) {
+                                int32_t* __restrict__ count_out,
+                                TopkSmemFor<NT, EPT>& sm, Emit&& emit) {
   constexpr int NW = NT / kWave;
   constexpr int FW = (EPT + 31) / 32;   // words of the forced mask
+  constexpr int ER = EPT - topk_lds_keys<EPT>();   // keys held in registers
   auto& hist = sm.hist;
   auto& state = sm.state;
   const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid >> 6;
   const int n0 = tid * EPT;
+  // key r of the thread (r is a compile-time index in every unrolled loop)
+  uint32_t key[ER];
+  uint32_t* xk = sm.xkeys + tid;
+  auto kget = [&](int r) -> uint32_t { return r < ER ? key[r < ER ? r : 0] : xk[(r - ER) * NT]; };
+  auto kset = [&](int r, uint32_t v) {
+    if (r < ER) key[r < ER ? r : 0] = v;
+    else xk[(r - ER) * NT] = v;
+  };
   // the scores are read first: the row is readable up to maxN whatever the
-  // length, so the loads need not wait for it (key[] holds the score bits)
-  uint32_t key[EPT];
+  // length, so the loads need not wait for it (the keys hold the score bits)
   if constexpr (EPT % 4 == 0) {
     // 16-byte loads of the thread's contiguous scores when the row allows it
     if ((reinterpret_cast<uintptr_t>(row) & 15u) == 0 && n0 + EPT <= maxN) {
 #pragma unroll
       for (int r = 0; r < EPT; r += 4) {
         const uint4 v = load16(row + n0 + r);
-        key[r] = v.x; key[r + 1] = v.y; key[r + 2] = v.z; key[r + 3] = v.w;
+        kset(r, v.x); kset(r + 1, v.y); kset(r + 2, v.z); kset(r + 3, v.w);
       }
     } else {
 #pragma unroll
-      for (int r = 0; r < EPT; ++r) key[r] = (n0 + r < maxN) ? __float_as_uint(row[n0 + r]) : 0u;
+      for (int r = 0; r < EPT; ++r) kset(r, (n0 + r < maxN) ? __float_as_uint(row[n0 + r]) : 0u);
     }
   } else {
 #pragma unroll
-    for (int r = 0; r < EPT; ++r) key[r] = (n0 + r < maxN) ? __float_as_uint(row[n0 + r]) : 0u;
+    for (int r = 0; r < EPT; ++r) kset(r, (n0 + r < maxN) ? __float_as_uint(row[n0 + r]) : 0u);
   }
   const int nb = (L + kBlockSize - 1) / kBlockSize;
   const int keff = min(K, nb);
@@ -144,8 +165,8 @@ __device__ inline void topk_row(const float* __restrict__ row, int maxN, int L, 
         nf += (uint32_t)forced;
         live &= !forced;
       }
-      const uint32_t k = live ? score_key(__uint_as_float(key[r])) : 0u;
-      key[r] = k;
+      const uint32_t k = live ? score_key(__uint_as_float(kget(r))) : 0u;
+      kset(r, k);
       kmn = min(kmn, live ? k : 0xFFFFFFFFu);
       kmx = max(kmx, k);
     }
@@ -186,9 +207,10 @@ __device__ inline void topk_row(const float* __restrict__ row, int maxN, int L, 
     uint32_t kmn_pos = 0xFFFFFFFFu, kmx_neg = 0u, npos = 0u;
 #pragma unroll
     for (int r = 0; r < EPT; ++r) {
-      const bool pos = (key[r] >> 31) != 0u;
-      kmn_pos = min(kmn_pos, pos ? key[r] : 0xFFFFFFFFu);
-      kmx_neg = max(kmx_neg, pos ? 0u : key[r]);
+      const uint32_t kr = kget(r);
+      const bool pos = (kr >> 31) != 0u;
+      kmn_pos = min(kmn_pos, pos ? kr : 0xFFFFFFFFu);
+      kmx_neg = max(kmx_neg, pos ? 0u : kr);
       npos += (uint32_t)pos;
     }
     kmn_pos = wave_reduce_u32(kmn_pos, MinU32());
@@ -239,10 +261,16 @@ __device__ inline void topk_row(const float* __restrict__ row, int maxN, int L, 
     // shares the known bits
     if (split) {
 #pragma unroll
-      for (int r = 0; r < EPT; ++r) atomicAdd(&hs[(key[r] >> shift) & dmask], (uint32_t)known(key[r]));
+      for (int r = 0; r < EPT; ++r) {
+        const uint32_t kr = kget(r);
+        atomicAdd(&hs[(kr >> shift) & dmask], (uint32_t)known(kr));
+      }
     } else {
 #pragma unroll
-      for (int r = 0; r < EPT; ++r) atomicAdd(&hs[(key[r] >> shift) & dmask], (uint32_t)(key[r] != 0u));
+      for (int r = 0; r < EPT; ++r) {
+        const uint32_t kr = kget(r);
+        atomicAdd(&hs[(kr >> shift) & dmask], (uint32_t)(kr != 0u));
+      }
     }
     __syncthreads();
     const uint4 v4 = *reinterpret_cast<const uint4*>(&hs[NB - 4 - 4 * tid]);
@@ -268,15 +296,16 @@ __device__ inline void topk_row(const float* __restrict__ row, int maxN, int L, 
       // ascending); the key ranked krem-1 is T
       uint32_t mine = 0u;
 #pragma unroll
-      for (int r = 0; r < EPT; ++r) mine += (uint32_t)known(key[r]);
+      for (int r = 0; r < EPT; ++r) mine += (uint32_t)known(kget(r));
       const uint32_t incl = wave_scan_add_u32(mine);
       uint32_t wbase = 0u;
       if (lane == kWave - 1 && incl != 0u) wbase = atomicAdd(&sm.cand_n, incl);
       uint32_t pos = (uint32_t)__builtin_amdgcn_readlane((int)wbase, kWave - 1) + incl - mine;
 #pragma unroll
       for (int r = 0; r < EPT; ++r) {
-        if (known(key[r])) {
-          sm.cand_key[pos] = key[r];
+        const uint32_t kr = kget(r);
+        if (known(kr)) {
+          sm.cand_key[pos] = kr;
           sm.cand_idx[pos] = n0 + r;
           ++pos;
         }
@@ -321,7 +350,10 @@ __device__ inline void topk_row(const float* __restrict__ row, int maxN, int L, 
 #pragma unroll
     for (int i = lane; i < 256; i += kWave) h[i] = 0u;
 #pragma unroll
-    for (int r = 0; r < EPT; ++r) atomicAdd(&h[(key[r] >> shift) & dmask], (uint32_t)known(key[r]));
+    for (int r = 0; r < EPT; ++r) {
+      const uint32_t kr = kget(r);
+      atomicAdd(&h[(kr >> shift) & dmask], (uint32_t)known(kr));
+    }
     __syncthreads();
     if (wave == 0) {
       // lane L owns digits 255-4L .. 252-4L (descending)
@@ -355,8 +387,9 @@ __device__ inline void topk_row(const float* __restrict__ row, int maxN, int L, 
   uint32_t n_gt = 0, n_eq = 0;
 #pragma unroll
   for (int r = 0; r < EPT; ++r) {
-    n_gt += ((fm[r / 32] >> (r % 32)) & 1u) | (uint32_t)(key[r] > T);
-    n_eq += (uint32_t)(key[r] == T);
+    const uint32_t kr = kget(r);
+    n_gt += ((fm[r / 32] >> (r % 32)) & 1u) | (uint32_t)(kr > T);
+    n_eq += (uint32_t)(kr == T);
   }
   // the scans use their own buffers: with no radix pass, slower waves may
   // still read the partials, and a wide pass's readers the first scan buffer
@@ -371,8 +404,9 @@ __device__ inline void topk_row(const float* __restrict__ row, int maxN, int L, 
   }
 #pragma unroll
   for (int r = 0; r < EPT; ++r) {
-    const bool gt = (((fm[r / 32] >> (r % 32)) & 1u) != 0u) | (key[r] > T);
-    const bool eq = key[r] == T;
+    const uint32_t kr = kget(r);
+    const bool gt = (((fm[r / 32] >> (r % 32)) & 1u) != 0u) | (kr > T);
+    const bool eq = kr == T;
     if (gt | (eq & (eq_before < krem))) emit((int)(gt_before + min(eq_before, krem)), n0 + r);
     gt_before += (uint32_t)gt;
     eq_before += (uint32_t)eq;
