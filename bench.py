@@ -577,6 +577,52 @@ def time_tier_policy(args, dw, k):
     return res
 
 
+LONG_SELECT = dict(num_kv_heads=8, num_q_heads=32, head_dim=128, blocks=65536, topk=256,
+                   seed=6100)
+
+
+def time_long_select(args):
+    """Score + Top-K over a 1M-token layer (one sequence of 65536 blocks, 8 KV
+    heads, G = 4, D = 128, a bf16 min/max index of normal values behind a
+    shuffled block table, Top-K 256): kv_block_score_topk without candidate
+    storage (one workgroup selects each row) and with a workspace that holds
+    it (the two-level select), each graph-timed; the two lists must be equal."""
+    import torch
+    from kv_cache_decode_amd import kvdecode as kd
+    c = LONG_SELECT
+    Hkv, Hq, D, N, K = c["num_kv_heads"], c["num_q_heads"], c["head_dim"], c["blocks"], c["topk"]
+    dev = torch.device("cuda:0")
+    g = torch.Generator(device=dev).manual_seed(c["seed"])
+    shape = kd.make_shape(1, Hq, Hkv, D, N, N, "bf16")
+    q = torch.randn(1, Hq, D, device=dev, generator=g).to(torch.bfloat16)
+    kmeta = torch.randn(N, Hkv, 2, D, device=dev, generator=g).to(torch.bfloat16)
+    table = torch.randperm(N, device=dev, generator=g).to(torch.int32).view(1, N)
+    lens = torch.full((1,), N * 16, device=dev, dtype=torch.int32)
+    scores = torch.empty(1, Hkv, N, device=dev)
+    need = kd.kv_score_topk_workspace_size(shape, K)
+    ws = torch.empty(need, dtype=torch.uint8, device=dev)
+    out = {}
+    for name, w, nw in (("one_level", None, 0), ("two_level", ws, need)):
+        sel = torch.empty(1, Hkv, K, device=dev, dtype=torch.int32)
+        cnt = torch.empty(1, Hkv, device=dev, dtype=torch.int32)
+        call = (lambda _, w=w, nw=nw, sel=sel, cnt=cnt:
+                kd.kv_block_score_topk(shape, q, kmeta, table, lens, K, scores, sel, cnt, w, nw,
+                                       torch.cuda.current_stream()))
+        us = graph_step_us(call, [None], args)
+        torch.cuda.synchronize()
+        out[name] = (us, sel.cpu(), cnt.cpu())
+    same = bool(torch.equal(out["one_level"][1], out["two_level"][1]) and
+                torch.equal(out["one_level"][2], out["two_level"][2]))
+    if not same:
+        raise RuntimeError("two-level and one-level Top-K lists differ")
+    return {"workload": f"1M-token layer: 1 sequence x {N} blocks of 16 tokens, {Hkv} KV heads, "
+                        f"G={Hq // Hkv}, D={D}, bf16 min/max index, Top-K {K}",
+            "score_topk_one_level_us": out["one_level"][0],
+            "score_topk_two_level_us": out["two_level"][0],
+            "workspace_bytes": need, "lists_equal": same,
+            "timing": "kv_block_score_topk per call, median over HIP graph replays"}
+
+
 def time_variants(args, copies, k, s_sparse, time_loop, graph_us):
     import torch
 
@@ -1186,6 +1232,10 @@ def main():
                     help="skip the variant timings (mean-key index, forced tokens, FP8 pages)")
     ap.add_argument("--only-variants", action="store_true",
                     help="run only the variant timings (for profiling them)")
+    ap.add_argument("--no-long-select", action="store_true",
+                    help="skip the score + Top-K timing over a 1M-token layer")
+    ap.add_argument("--only-long-select", action="store_true",
+                    help="run only the score + Top-K timing over a 1M-token layer")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -1209,6 +1259,9 @@ def main():
         return
     if args.only_zero_copy:
         print(json.dumps({"zero_copy": run_zero_copy(args)}), flush=True)
+        return
+    if args.only_long_select:
+        print(json.dumps({"long_select": time_long_select(args)}), flush=True)
         return
     spec = wl.WORKLOADS[WORKLOAD]
     log(f"[bench] generating {spec.name}")
@@ -1243,6 +1296,10 @@ def main():
             log(f"[bench] {name}")
             others[name] = run_other_workload(args, name, other_cpu)
 
+    long_sel = None
+    if not args.no_long_select:
+        log("[bench] score + Top-K over a 1M-token layer")
+        long_sel = time_long_select(args)
     zc = None
     if not args.no_zero_copy:
         log("[bench] zero-copy host-KV variant")
@@ -1330,6 +1387,7 @@ def main():
         "fp8_pages": codes_record(spec, g["fp8"], "fp8") if g.get("fp8") else None,
         "int4_pages": codes_record(spec, g["int4"], "int4") if g.get("int4") else None,
         "other_workloads": others,
+        "long_select": long_sel,
         "zero_copy": zc,
         "cpu_baseline": cpu,
     }

@@ -251,7 +251,14 @@ kv_status kv_select_decode_attn(const kv_shape* shape, const float* scores,
                                 int32_t* sel_count, float* part_o, float* part_m, float* part_l,
                                 void* stream);
 
-/* Workspace bytes kv_block_score_topk needs when scores_out is NULL (0 otherwise). */
+/*
+ * Workspace bytes for kv_block_score_topk, kv_block_select and
+ * kv_decode_select: the scores (B * Hkv * maxN fp32, rounded up to 256 bytes;
+ * the least a call with scores_out NULL accepts) plus, for rows longer than
+ * 16384 blocks where 2 * topk_blocks candidates per 4096-block chunk stay within
+ * 16384 per row, the candidate storage of the two-level select (8 bytes per
+ * candidate slot).  0 for an invalid shape.
+ */
 size_t kv_score_topk_workspace_size(const kv_shape* shape, int32_t topk_blocks);
 
 /*
@@ -265,10 +272,14 @@ size_t kv_score_topk_workspace_size(const kv_shape* shape, int32_t topk_blocks);
  * block index first), written ascending to sel_blocks[b, j, 0..K_eff) with -1
  * after, and K_eff to sel_count[b, j].  sel_blocks has row stride topk_blocks.
  * scores_out (nullable) receives S ([B, Hkv, maxN], -inf for n >= N_b); when it
- * is NULL the scores go to `workspace`, which must hold
- * kv_score_topk_workspace_size() bytes.  topk_blocks >= 1; maxN <= 65536 (a
- * 1M-token context of 16-token blocks; rows past 32768 blocks take a slower
- * instance that keeps part of its keys in scratch memory).
+ * is NULL the scores go to the head of `workspace`, which must hold at least
+ * their bytes (see kv_score_topk_workspace_size).  Long rows (more than 16384
+ * blocks): when the workspace also holds the candidate storage (after the
+ * scores, or from its head when scores_out is given), the select runs in two
+ * launches -- each 4096-block chunk's forced blocks and best topk_blocks
+ * competing blocks, then the select among those -- which return the same
+ * list; otherwise one workgroup per row selects.  topk_blocks >= 1; maxN <=
+ * 65536 (a 1M-token context of 16-token blocks).
  */
 kv_status kv_block_score_topk(const kv_shape* shape, const void* q, const void* kmeta,
                               const int32_t* block_table, const int32_t* seq_lens,
@@ -313,8 +324,10 @@ kv_status kv_block_select(const kv_shape* shape, int32_t index_kind, const void*
  * process ends; its address on the current device is looked up (never
  * allocated) on the first call on that device.  The call itself allocates
  * nothing.  Limit: num_seqs * num_kv_heads * max_blocks_per_seq <= 1048576
- * scores (for example 8 KV heads of 131072 blocks), else KV_ERR_WORKSPACE
- * before any launch.  Every call on one GPU shares that array: calls that
+ * scores (for example 16 sequences of 8 KV heads and 8192 blocks), else
+ * KV_ERR_WORKSPACE before any launch.  Rows longer than 16384 blocks take the
+ * two-level select (see kv_block_score_topk) when its candidates fit in the
+ * array after the scores.  Every call on one GPU shares that array: calls that
  * overlap on one GPU (other streams, other threads) race and may select from
  * each other's scores; calls ordered on one stream do not.  Arguments, checks
  * and errors are otherwise those of kv_block_select.

@@ -96,6 +96,37 @@ size_t scores_bytes(const kv_shape* s) {
   return (size_t)s->num_seqs * s->num_kv_heads * s->max_blocks_per_seq * sizeof(float);
 }
 
+// The scores' part of a Top-K workspace (256-byte rounded), and the candidate
+// storage of the two-level select of long rows (0 where it does not apply).
+size_t scores_region(const kv_shape* s) { return (scores_bytes(s) + 255) & ~(size_t)255; }
+size_t topk_candidates(const kv_shape* s, int32_t topk_blocks) {
+  return kvd::topk_candidate_bytes(s->num_seqs, s->num_kv_heads, s->max_blocks_per_seq,
+                                   topk_blocks);
+}
+
+// Where the scores and the Top-K candidates go: scores_out, else the head of
+// the workspace (at least the scores' bytes, else KV_ERR_WORKSPACE); the
+// candidates after them when the workspace also holds those (with scores_out
+// given: at the head of a workspace that holds them), else nowhere and the
+// select runs in one level.
+kv_status topk_buffers(const kv_shape* shape, int32_t topk_blocks, float* scores_out,
+                       void* workspace, size_t workspace_bytes, float** scores, void** cand) {
+  const size_t sb = scores_region(shape), cb = topk_candidates(shape, topk_blocks);
+  *scores = scores_out;
+  *cand = nullptr;
+  if (!scores_out) {
+    if (!workspace || workspace_bytes < sb)
+      return fail(KV_ERR_WORKSPACE, "workspace of %zu bytes needed (got %zu)", sb,
+                  workspace ? workspace_bytes : (size_t)0);
+    if (!aligned(workspace, 4)) return fail(KV_ERR_ALIGNMENT, "workspace must be 4-byte aligned");
+    *scores = static_cast<float*>(workspace);
+    if (cb && workspace_bytes >= sb + cb) *cand = static_cast<char*>(workspace) + sb;
+  } else if (cb && workspace && workspace_bytes >= cb && aligned(workspace, 4)) {
+    *cand = workspace;
+  }
+  return KV_OK;
+}
+
 // Bytes of one (page, KV head) tile of a code pool; 0 for an unknown format.
 int code_tile_bytes(const kv_shape* shape, int32_t code_format) {
   const int tile = shape->block_size * shape->head_dim;
@@ -261,15 +292,11 @@ kv_status kv_decode_select(const kv_shape* shape, int32_t index_kind, const void
   if (!aligned(block_table, 4) || !aligned(seq_lens, 4) || !aligned(sel_blocks, 4) ||
       !aligned(sel_count, 4) || (scores_out && !aligned(scores_out, 4)))
     return fail(KV_ERR_ALIGNMENT, "integer and score arrays must be 4-byte aligned");
-  float* scores = scores_out;
-  if (!scores) {
-    const size_t need = kv_score_topk_workspace_size(shape, topk_blocks);
-    if (!workspace || workspace_bytes < need)
-      return fail(KV_ERR_WORKSPACE, "workspace of %zu bytes needed (got %zu)", need,
-                  workspace ? workspace_bytes : (size_t)0);
-    if (!aligned(workspace, 4)) return fail(KV_ERR_ALIGNMENT, "workspace must be 4-byte aligned");
-    scores = static_cast<float*>(workspace);
-  }
+  float* scores = nullptr;
+  void* cand = nullptr;
+  if ((st = topk_buffers(shape, topk_blocks, scores_out, workspace, workspace_bytes, &scores,
+                         &cand)) != KV_OK)
+    return st;
   const int G = shape->num_q_heads / shape->num_kv_heads;
   hipStream_t s = (hipStream_t)stream;
   // the scorer's extra workgroups append the token and score its block from the
@@ -282,7 +309,7 @@ kv_status kv_decode_select(const kv_shape* shape, int32_t index_kind, const void
   if (e != hipSuccess) return hip_status(e, "append + block score launch");
   return hip_status(kvd::launch_topk(scores, seq_lens, shape->num_seqs, shape->num_kv_heads,
                                      shape->max_blocks_per_seq, topk_blocks, sink_tokens,
-                                     local_tokens, sel_blocks, sel_count, s),
+                                     local_tokens, sel_blocks, sel_count, s, cand),
                     "top-k launch");
 }
 
@@ -394,9 +421,8 @@ kv_status kv_append_token(const kv_shape* shape, const void* k_new, const void* 
 }
 
 size_t kv_score_topk_workspace_size(const kv_shape* shape, int32_t topk_blocks) {
-  (void)topk_blocks;
   if (check_shape(shape) != KV_OK) return 0;
-  return (scores_bytes(shape) + 255) & ~(size_t)255;
+  return scores_region(shape) + topk_candidates(shape, topk_blocks);
 }
 
 int32_t kv_max_forced_blocks(const kv_shape* shape, int32_t sink_tokens, int32_t local_tokens) {
@@ -448,7 +474,8 @@ kv_status check_select(const kv_shape* shape, int32_t index_kind, const void* q,
 kv_status launch_select(const kv_shape* shape, int32_t index_kind, const void* q,
                         const void* index, const int32_t* block_table, const int32_t* seq_lens,
                         int32_t topk_blocks, int32_t sink_tokens, int32_t local_tokens,
-                        float* scores, int32_t* sel_blocks, int32_t* sel_count, void* stream) {
+                        float* scores, int32_t* sel_blocks, int32_t* sel_count, void* stream,
+                        void* cand) {
   const int G = shape->num_q_heads / shape->num_kv_heads;
   hipStream_t s = (hipStream_t)stream;
   hipError_t e = kvd::launch_block_score(shape->dtype, shape->head_dim, G, index_kind, q, index,
@@ -458,7 +485,7 @@ kv_status launch_select(const kv_shape* shape, int32_t index_kind, const void* q
   if (e != hipSuccess) return hip_status(e, "block score launch");
   return hip_status(kvd::launch_topk(scores, seq_lens, shape->num_seqs, shape->num_kv_heads,
                                      shape->max_blocks_per_seq, topk_blocks, sink_tokens,
-                                     local_tokens, sel_blocks, sel_count, s),
+                                     local_tokens, sel_blocks, sel_count, s, cand),
                     "top-k launch");
 }
 
@@ -503,17 +530,13 @@ kv_status kv_block_select(const kv_shape* shape, int32_t index_kind, const void*
   kv_status st = check_select(shape, index_kind, q, index, block_table, seq_lens, topk_blocks,
                               sink_tokens, local_tokens, scores_out, sel_blocks, sel_count);
   if (st != KV_OK) return st;
-  float* scores = scores_out;
-  if (!scores) {
-    const size_t need = kv_score_topk_workspace_size(shape, topk_blocks);
-    if (!workspace || workspace_bytes < need)
-      return fail(KV_ERR_WORKSPACE, "workspace of %zu bytes needed (got %zu)", need,
-                  workspace ? workspace_bytes : (size_t)0);
-    if (!aligned(workspace, 4)) return fail(KV_ERR_ALIGNMENT, "workspace must be 4-byte aligned");
-    scores = static_cast<float*>(workspace);
-  }
+  float* scores = nullptr;
+  void* cand = nullptr;
+  if ((st = topk_buffers(shape, topk_blocks, scores_out, workspace, workspace_bytes, &scores,
+                         &cand)) != KV_OK)
+    return st;
   return launch_select(shape, index_kind, q, index, block_table, seq_lens, topk_blocks,
-                       sink_tokens, local_tokens, scores, sel_blocks, sel_count, stream);
+                       sink_tokens, local_tokens, scores, sel_blocks, sel_count, stream, cand);
 }
 
 kv_status kv_block_select_no_alloc(const kv_shape* shape, int32_t index_kind, const void* q,
@@ -532,9 +555,15 @@ kv_status kv_block_select_no_alloc(const kv_shape* shape, int32_t index_kind, co
   float* scores = nullptr;
   st = scratch_scores(&scores);
   if (st != KV_OK) return st;
+  // the two-level select's candidates go after the scores when the array
+  // holds both; every candidate slot a call reads is written in that call
+  void* cand = nullptr;
+  const size_t sb = scores_region(shape), cb = topk_candidates(shape, topk_blocks);
+  if (cb && sb + cb <= kNoAllocScores * sizeof(float))
+    cand = reinterpret_cast<char*>(scores) + sb;
   // the score launch writes every one of the n scores, so nothing is cleared
   return launch_select(shape, index_kind, q, index, block_table, seq_lens, topk_blocks,
-                       sink_tokens, local_tokens, scores, sel_blocks, sel_count, stream);
+                       sink_tokens, local_tokens, scores, sel_blocks, sel_count, stream, cand);
 }
 
 kv_status kv_block_score_topk(const kv_shape* shape, const void* q, const void* kmeta,

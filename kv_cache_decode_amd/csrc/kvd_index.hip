@@ -563,6 +563,71 @@ __global__ __launch_bounds__(NT) void topk_kernel(const float* __restrict__ scor
                     [out](int pos, int n) { out[pos] = n; });
 }
 
+// Two-level select of a long row.  topk_chunk_kernel: one workgroup per
+// (chunk of kTopkChunk blocks, KV head, sequence) selects the chunk's forced
+// blocks and its best min(K, #competing) competing blocks -- the one-level
+// select's rule applied to the chunk -- and writes them, ascending, to the
+// chunk's capc candidate slots (the score's key, 0 for a forced block, and
+// the block; block -1 in unused slots).  Every block of the row's Top-K is
+// among its chunk's candidates, and the candidate slots run in ascending
+// block order, so topk_merge_kernel, the select over a row's candidate slots
+// with each slot standing for its block, returns the one-level list exactly.
+
+template <int NT, int EPT>
+__global__ __launch_bounds__(NT) void topk_chunk_kernel(const float* __restrict__ scores,
+                                                          const int32_t* __restrict__ seq_lens,
+                                                          int Hkv, int maxN, int K, int sink,
+                                                          int local, int capc,
+                                                          uint32_t* __restrict__ cand_key,
+                                                          int32_t* __restrict__ cand_block) {
+  static_assert(NT * EPT == kTopkChunk, "one chunk per workgroup");
+  __shared__ TopkSmemFor<NT, EPT> sm;
+  const int c = blockIdx.x, j = blockIdx.y, b = blockIdx.z;
+  const int nch = gridDim.x;
+  const size_t u = (size_t)b * Hkv + j;
+  const int c0 = c * kTopkChunk;
+  const int npos = min(kTopkChunk, maxN - c0);
+  const float* row = scores + u * maxN + c0;
+  uint32_t* ck = cand_key + (u * nch + c) * capc;
+  int32_t* cb = cand_block + (u * nch + c) * capc;
+  const int L = seq_lens[b];
+  // the chunk's K_eff: its forced blocks (the one-level select's token tests,
+  // counted as ranges) plus min(K, its competing blocks)
+  auto keff_of = [&]() {
+    const int nb = (L + kBlockSize - 1) / kBlockSize;
+    const int a = c0, e = min(nb, c0 + npos);
+    if (e <= a) return 0;
+    const int sb = (sink + kBlockSize - 1) / kBlockSize;          // blocks below hold sink tokens
+    const int t = L - local;
+    const int lb = local > 0 ? (t > 0 ? t / kBlockSize : 0) : 0x7fffffff;   // first local block
+    const int competing = max(0, min(e, lb) - max(a, sb));
+    return (e - a) - competing + min(K, competing);
+  };
+  topk_select<NT, EPT, false>(row, npos, L, sink, local, c0, nullptr, keff_of, cb, nullptr, capc,
+                              sm, [&](int pos, int n, uint32_t key) {
+                                ck[pos] = key;
+                                cb[pos] = n;
+                              });
+}
+
+template <int NT, int EPT>
+__global__ __launch_bounds__(NT) void topk_merge_kernel(const uint32_t* __restrict__ cand_key,
+                                                          const int32_t* __restrict__ cand_block,
+                                                          const int32_t* __restrict__ seq_lens,
+                                                          int Hkv, int ncand, int K, int sink,
+                                                          int local, int32_t* __restrict__ sel,
+                                                          int32_t* __restrict__ sel_count) {
+  __shared__ TopkSmemFor<NT, EPT> sm;
+  const int j = blockIdx.x, b = blockIdx.y;
+  const size_t u = (size_t)b * Hkv + j;
+  const int L = seq_lens[b];
+  int32_t* out = sel + u * K;
+  topk_select<NT, EPT, true>(reinterpret_cast<const float*>(cand_key + u * ncand), ncand, L, sink,
+                             local, 0, cand_block + u * ncand,
+                             [&]() { return min(K, (L + kBlockSize - 1) / kBlockSize); }, out,
+                             sel_count + u, K, sm, [&](int pos, int n, uint32_t) { out[pos] = n; });
+}
+
 // ============================================================== launchers
 
 
@@ -677,7 +742,36 @@ hipError_t launch_block_score(int dtype, int D, int G, int index_kind, const voi
 
 hipError_t launch_topk(const float* scores, const int32_t* seq_lens, int B, int Hkv, int maxN,
                        int K, int sink, int local, int32_t* sel, int32_t* sel_count,
-                       hipStream_t stream) {
+                       hipStream_t stream, void* cand) {
+  const int slots = topk_candidates_per_row(maxN, K);
+  if (cand && slots > 0) {
+    // candidate slots per chunk: K + the most blocks the tokens can force
+    const int forced = (sink + kBlockSize - 1) / kBlockSize +
+                       (local > 0 ? (local - 1 + kBlockSize - 1) / kBlockSize + 1 : 0);
+    const int nch = (maxN + kTopkChunk - 1) / kTopkChunk;
+    const int capc = K + min(forced, K);
+    const int ncand = nch * capc;                      // <= slots
+    uint32_t* ck = static_cast<uint32_t*>(cand);
+    int32_t* cb = reinterpret_cast<int32_t*>(ck + (size_t)B * Hkv * slots);
+    constexpr int CT = KVD_TOPK_CHUNK_THREADS;
+    hipLaunchKernelGGL((topk_chunk_kernel<CT, kTopkChunk / CT>), dim3(nch, Hkv, B), dim3(CT), 0,
+                       stream, scores, seq_lens, Hkv, maxN, K, sink, local, capc, ck, cb);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    const dim3 gm(Hkv, B);
+    const int ept = (ncand + 1023) / 1024;
+#define KVD_TOPK_MERGE(N)                                                                      \
+  hipLaunchKernelGGL((topk_merge_kernel<1024, N>), gm, dim3(1024), 0, stream, ck, cb, seq_lens, \
+                     Hkv, ncand, K, sink, local, sel, sel_count)
+    if (ept <= 1) KVD_TOPK_MERGE(1);
+    else if (ept <= 2) KVD_TOPK_MERGE(2);
+    else if (ept <= 4) KVD_TOPK_MERGE(4);
+    else if (ept <= 8) KVD_TOPK_MERGE(8);
+    else if (ept <= 16) KVD_TOPK_MERGE(16);
+    else return hipErrorInvalidValue;
+#undef KVD_TOPK_MERGE
+    return hipGetLastError();
+  }
   const dim3 grid(Hkv, B);
   const int ept = (maxN + 1023) / 1024;
 #define KVD_TOPK(N)                                                                          \

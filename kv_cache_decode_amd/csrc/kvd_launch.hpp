@@ -31,9 +31,12 @@ hipError_t launch_block_score(int dtype, int D, int G, int index_kind, const voi
                               void* v_cache = nullptr, void* kmeta = nullptr,
                               float* kmean = nullptr);
 
+// cand (nullable): candidate storage of topk_candidate_bytes(B, Hkv, maxN, K)
+// bytes; with it, rows longer than kTopkTwoLevelMin blocks take the two-level
+// select where topk_candidates_per_row allows (the same lists either way).
 hipError_t launch_topk(const float* scores, const int32_t* seq_lens, int B, int Hkv, int maxN,
                        int K, int sink, int local, int32_t* sel, int32_t* sel_count,
-                       hipStream_t stream);
+                       hipStream_t stream, void* cand = nullptr);
 
 // kv_scales == nullptr: K/V pools in `dtype`; otherwise E4M3 code pools with
 // fp32 (k, v) scales per (page, KV head)
@@ -163,8 +166,32 @@ inline int cu_count() {
 inline int device_cu_count() { return cu_count(); }
 
 // Largest maxN of the Top-K (1024 threads x 64 keys; past 32 keys per thread
-// part of them live in scratch memory).
+// the keys live in LDS).
 constexpr int kTopkMaxBlocks = 65536;
+
+// Two-level select of long rows: each chunk of kTopkChunk blocks passes its
+// forced blocks and its best K competing blocks (the candidates, in ascending
+// block order), and a second launch selects among a row's candidates.  It is
+// used for rows longer than kTopkTwoLevelMin blocks while a row's candidate
+// slots (chunks x 2K, enough for K + the forced blocks the host check allows)
+// stay within kTopkMaxCandidates.
+#ifndef KVD_TOPK_CHUNK_THREADS
+#define KVD_TOPK_CHUNK_THREADS 1024   // threads of a chunk's workgroup
+#endif
+#ifndef KVD_TOPK_CHUNK
+#define KVD_TOPK_CHUNK 4096           // blocks per chunk
+#endif
+constexpr int kTopkChunk = KVD_TOPK_CHUNK;
+constexpr int kTopkTwoLevelMin = 16384;
+constexpr int kTopkMaxCandidates = 16384;
+inline int topk_candidates_per_row(int maxN, int K) {
+  if (maxN <= kTopkTwoLevelMin || K < 1) return 0;
+  const long slots = (long)((maxN + kTopkChunk - 1) / kTopkChunk) * 2 * K;
+  return slots <= kTopkMaxCandidates ? (int)slots : 0;
+}
+inline size_t topk_candidate_bytes(int B, int Hkv, int maxN, int K) {
+  return (size_t)B * Hkv * topk_candidates_per_row(maxN, K) * 8;   // uint32 key + int32 block
+}
 
 // Top-K + sparse attention in one launch: waves (= splits) per workgroup, the
 // list positions a workgroup keeps in LDS, and the longest row it takes (every

@@ -97,14 +97,23 @@ struct TopkSmem {
 template <int NT, int EPT>
 using TopkSmemFor = TopkSmem<NT, topk_lds_keys<EPT>()>;
 
-// The selected blocks go to emit(position, block) (positions 0..K_eff-1 of the
-// ascending list); when out is not null, K_eff goes to *count_out and -1 to
-// out[K_eff..K).
-template <int NT, int EPT, typename Emit>
-__device__ inline void topk_row(const float* __restrict__ row, int maxN, int L, int K, int sink,
-                                int local, int32_t* __restrict__ out,
-                                int32_t* __restrict__ count_out,
-                                TopkSmemFor<NT, EPT>& sm, Emit&& emit) {
+// Row select over npos positions of `row`.  Without IDX, row holds scores and
+// position p stands for global block nbase + p.  With IDX, row holds keys
+// (score_key values, as emitted by an earlier select) and position p stands
+// for block bidx[p] (-1: no block).  A position is live when its block is in
+// [0, N_b), N_b = ceil(L / bs), and the forced-token tests apply to its block.
+// Ranking is by (key descending, position ascending), so positions must run
+// in ascending block order for the lower-block tie rule.  keff_of() gives
+// K_eff once the loads are issued (it may read only scalars).  The selected
+// blocks go to emit(position in the ascending list, block, key; 0 for a
+// forced block); when out is not null, K_eff goes to *count_out (if not null)
+// and -1 to out[K_eff..out_len).
+template <int NT, int EPT, bool IDX, typename KeffOf, typename Emit>
+__device__ inline void topk_select(const float* __restrict__ row, int npos, int L, int sink,
+                                   int local, int nbase, const int32_t* __restrict__ bidx,
+                                   KeffOf&& keff_of, int32_t* __restrict__ out,
+                                   int32_t* __restrict__ count_out, int out_len,
+                                   TopkSmemFor<NT, EPT>& sm, Emit&& emit) {
   constexpr int NW = NT / kWave;
   constexpr int FW = (EPT + 31) / 32;   // words of the forced mask
   constexpr int ER = EPT - topk_lds_keys<EPT>();   // keys held in registers
@@ -112,6 +121,7 @@ __device__ inline void topk_row(const float* __restrict__ row, int maxN, int L, 
   auto& state = sm.state;
   const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid >> 6;
   const int n0 = tid * EPT;
+  const int maxN = npos;
   // key r of the thread (r is a compile-time index in every unrolled loop)
   uint32_t key[ER];
   uint32_t* xk = sm.xkeys + tid;
@@ -120,8 +130,9 @@ __device__ inline void topk_row(const float* __restrict__ row, int maxN, int L, 
     if (r < ER) key[r < ER ? r : 0] = v;
     else xk[(r - ER) * NT] = v;
   };
-  // the scores are read first: the row is readable up to maxN whatever the
-  // length, so the loads need not wait for it (the keys hold the score bits)
+  // the scores (and block indexes) are read first: the row is readable up to
+  // npos whatever the length, so the loads need not wait for it (the keys hold
+  // the score bits)
   if constexpr (EPT % 4 == 0) {
     // 16-byte loads of the thread's contiguous scores when the row allows it
     if ((reinterpret_cast<uintptr_t>(row) & 15u) == 0 && n0 + EPT <= maxN) {
@@ -138,12 +149,25 @@ __device__ inline void topk_row(const float* __restrict__ row, int maxN, int L, 
 #pragma unroll
     for (int r = 0; r < EPT; ++r) kset(r, (n0 + r < maxN) ? __float_as_uint(row[n0 + r]) : 0u);
   }
+  // the block of each of the thread's positions: with IDX from the index
+  // array, read beside the scores (-1 past npos); else nbase + position (a
+  // position past npos lies past the row, so past N_b)
+  constexpr int EB = IDX ? EPT : 1;
+  int32_t blkr[EB];
+  if constexpr (IDX) {
+#pragma unroll
+    for (int r = 0; r < EPT; ++r) blkr[r] = (n0 + r < maxN) ? bidx[n0 + r] : -1;
+  }
+  auto blk = [&](int r) -> int {
+    if constexpr (IDX) return blkr[r];
+    else return nbase + n0 + r;
+  };
   const int nb = (L + kBlockSize - 1) / kBlockSize;
-  const int keff = min(K, nb);
+  const int keff = keff_of();
   const int local_from = local > 0 ? L - local : 0x7fffffff;  // first forced local token
   if (out) {
-    if (tid == 0) *count_out = max(keff, 0);
-    for (int i = max(keff, 0) + tid; i < K; i += NT) out[i] = -1;
+    if (count_out && tid == 0) *count_out = max(keff, 0);
+    for (int i = max(keff, 0) + tid; i < out_len; i += NT) out[i] = -1;
   }
   if (keff <= 0) return;  // workgroup-uniform
 
@@ -157,15 +181,17 @@ __device__ inline void topk_row(const float* __restrict__ row, int maxN, int L, 
   auto convert = [&](auto with_forcing) {
 #pragma unroll
     for (int r = 0; r < EPT; ++r) {
-      const int n = n0 + r;
-      bool live = n < nb;
+      const int n = blk(r);
+      bool live = (n >= 0) & (n < nb);
       if constexpr (decltype(with_forcing)::value) {
         const bool forced = live & ((n * kBlockSize < sink) | ((n + 1) * kBlockSize > local_from));
         fm[r / 32] |= (uint32_t)forced << (r % 32);
         nf += (uint32_t)forced;
         live &= !forced;
       }
-      const uint32_t k = live ? score_key(__uint_as_float(kget(r))) : 0u;
+      uint32_t k = kget(r);
+      if constexpr (!IDX) k = score_key(__uint_as_float(k));
+      k = live ? k : 0u;
       kset(r, k);
       kmn = min(kmn, live ? k : 0xFFFFFFFFu);
       kmx = max(kmx, k);
@@ -407,10 +433,22 @@ __device__ inline void topk_row(const float* __restrict__ row, int maxN, int L, 
     const uint32_t kr = kget(r);
     const bool gt = (((fm[r / 32] >> (r % 32)) & 1u) != 0u) | (kr > T);
     const bool eq = kr == T;
-    if (gt | (eq & (eq_before < krem))) emit((int)(gt_before + min(eq_before, krem)), n0 + r);
+    if (gt | (eq & (eq_before < krem))) emit((int)(gt_before + min(eq_before, krem)), blk(r), kr);
     gt_before += (uint32_t)gt;
     eq_before += (uint32_t)eq;
   }
+}
+
+// Top-K of one full row of maxN block scores (blocks 0..maxN-1); when out is
+// not null, K_eff goes to *count_out and -1 to out[K_eff..K).
+template <int NT, int EPT, typename Emit>
+__device__ inline void topk_row(const float* __restrict__ row, int maxN, int L, int K, int sink,
+                                int local, int32_t* __restrict__ out,
+                                int32_t* __restrict__ count_out, TopkSmemFor<NT, EPT>& sm,
+                                Emit&& emit) {
+  topk_select<NT, EPT, false>(row, maxN, L, sink, local, 0, nullptr,
+                              [&]() { return min(K, (L + kBlockSize - 1) / kBlockSize); }, out,
+                              count_out, K, sm, [&](int pos, int n, uint32_t) { emit(pos, n); });
 }
 
 }  // namespace kvd

@@ -157,32 +157,45 @@ class DeviceWorkload:
             self.sel_count = torch.empty((B, Hkv), dtype=torch.int32, device=self.device)
             self.topk = k
 
-    def score_topk(self, k: int, stream=None):
+    def topk_workspace(self, k: int):
+        """A workspace of kv_score_topk_workspace_size bytes (with scores_out
+        given, its candidate storage lets long rows take the two-level select)."""
+        need = kd.kv_score_topk_workspace_size(self.shape, k)
+        ws = getattr(self, "_topk_ws", None)
+        if ws is None or ws.numel() < need:
+            ws = self._topk_ws = torch.empty(max(need, 1), dtype=torch.uint8, device=self.device)
+        return ws, need
+
+    def score_topk(self, k: int, stream=None, workspace: bool = False):
         self._sel_buffers(k)
+        ws, need = self.topk_workspace(k) if workspace else (None, 0)
         kd.kv_block_score_topk(self.shape, self.q, self.kmeta, self.block_table, self.seq_lens, k,
-                               self.scores, self.sel, self.sel_count, None, 0, stream)
+                               self.scores, self.sel, self.sel_count, ws, need, stream)
 
     def select(self, k: int, index: str = "minmax", sink_tokens: int = 0, local_tokens: int = 0,
-               stream=None):
-        """kv_block_select over the min/max index ("minmax") or the mean index ("mean")."""
+               stream=None, workspace: bool = False):
+        """kv_block_select over the min/max index ("minmax") or the mean index ("mean");
+        with ``workspace`` the call also gets kv_score_topk_workspace_size bytes."""
         self._sel_buffers(k)
         kind, idx = ((kd.KV_INDEX_MEAN, self.kmean) if index == "mean"
                      else (kd.KV_INDEX_MINMAX, self.kmeta))
+        ws, need = self.topk_workspace(k) if workspace else (None, 0)
         kd.kv_block_select(self.shape, kind, self.q, idx, self.block_table, self.seq_lens, k,
-                           sink_tokens, local_tokens, self.scores, self.sel, self.sel_count, None,
-                           0, stream)
+                           sink_tokens, local_tokens, self.scores, self.sel, self.sel_count, ws,
+                           need, stream)
 
     def decode_select(self, k: int, index: str = "minmax", sink_tokens: int = 0,
                       local_tokens: int = 0, k_new=None, v_new=None, meta: bool = True,
-                      stream=None):
+                      stream=None, workspace: bool = False):
         """kv_decode_select: append (as append()) and select (as select()) in one call."""
         self._sel_buffers(k)
         kind = kd.KV_INDEX_MEAN if index == "mean" else kd.KV_INDEX_MINMAX
+        ws, need = self.topk_workspace(k) if workspace else (None, 0)
         kd.kv_decode_select(self.shape, kind, self.q, self.last_k if k_new is None else k_new,
                             self.last_v if v_new is None else v_new, self.block_table,
                             self.seq_lens, self.k_cache, self.v_cache,
                             self.kmeta if meta else None, self.kmean, k, sink_tokens,
-                            local_tokens, self.scores, self.sel, self.sel_count, None, 0, stream)
+                            local_tokens, self.scores, self.sel, self.sel_count, ws, need, stream)
 
     def decode_score(self, index: str = "minmax", k_new=None, v_new=None, meta: bool = True,
                      stream=None):

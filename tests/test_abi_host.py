@@ -137,6 +137,15 @@ def test_score_topk_argument_checks():
                                                  stream=stream))
     expect(kd.KV_ERR_WORKSPACE, lambda stream: f(s, A16, A16, A16, A16, 2, None, A16, A16, A16,
                                                  need - 4, stream=stream))
+    # long rows: the candidate storage of the two-level select (8 bytes per
+    # slot, 2K slots per 4096-block chunk) while a row's slots stay within 16384
+    def scores_part(sh):
+        return (sh.num_seqs * sh.num_kv_heads * sh.max_blocks_per_seq * 4 + 255) // 256 * 256
+    for n, k, slots in ((16384, 256, 0), (16385, 256, 5 * 512), (65536, 256, 16 * 512),
+                        (65536, 512, 16 * 1024), (65536, 513, 0), (20000, 1, 5 * 2)):
+        sh = shape(max_blocks_per_seq=n, num_pages=n)
+        rows = sh.num_seqs * sh.num_kv_heads
+        assert kd.kv_score_topk_workspace_size(sh, k) == scores_part(sh) + rows * slots * 8, (n, k)
     big = shape(max_blocks_per_seq=65537)
     expect(kd.KV_ERR_UNSUPPORTED, lambda stream: f(big, A16, A16, A16, A16, 2, A16, A16, A16,
                                                    stream=stream))

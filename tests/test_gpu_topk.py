@@ -34,8 +34,9 @@ def scored_workload(rows, G=1, Hkv=2, seed=0, ragged=None):
     q[:, :, 0] = 1.0
     data.q_raw[:] = wl.to_storage(q, "bf16")
     k32 = wl.bf16_bits_to_f32(data.k_raw).copy()
+    nb = data.num_blocks()
     for b, r in enumerate(rows):
-        for n in range(r.shape[1]):
+        for n in range(min(r.shape[1], nb[b])):      # blocks past the sequence have no page
             p = data.block_table[b, n]
             k32[p, :, :, 0] = r[:, n][:, None]
     data.k_raw[:] = wl.to_storage(k32, "bf16")
