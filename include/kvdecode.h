@@ -762,6 +762,20 @@ kv_status kv_probe_gather_read(const kv_shape* shape, const void* k_cache, const
                                int32_t num_splits, uint32_t* sink, void* stream);
 
 /*
+ * Instruction probe behind the bf16 quantizers' E4M3 codes (see
+ * kv_quantize_pages_fp8): every one of the 2^32 fp32 bit patterns goes through
+ * the GPU's fp32 -> E4M3 conversion instruction, in both of its operand
+ * slots, and is compared with the codes' rounding rule (round to nearest
+ * even, subnormals kept, saturating to 448, NaN to 0x7f | sign).  counts
+ * (device, 4 uint64) receives the mismatches per class of input magnitude:
+ * [0] finite below 464 (the only range the quantizers convert), [1] finite
+ * from 464 up, [2] infinity, [3] NaN; first (device, 4 uint32) the smallest
+ * mismatching bit pattern of each class (0xffffffff for none).  Both arrays
+ * are overwritten; the call takes well under a second.
+ */
+kv_status kv_probe_fp8_convert(uint64_t* counts, uint32_t* first, void* stream);
+
+/*
  * Pinned, device-mapped host memory for a zero-copy K/V pool (DirectKV review,
  * core method 4: KV kept in pinned host memory behind a device-visible pointer).
  * *host_ptr is the CPU address, *dev_ptr the address to pass to the kernels.

@@ -1177,6 +1177,15 @@ kv_status kv_probe_gather_read(const kv_shape* shape, const void* k_cache, const
                     "kv_probe_gather_read launch");
 }
 
+kv_status kv_probe_fp8_convert(uint64_t* counts, uint32_t* first, void* stream) {
+  if (!counts || !first) return fail(KV_ERR_INVALID_ARG, "counts and first are required");
+  if (!aligned(counts, 8) || !aligned(first, 4))
+    return fail(KV_ERR_ALIGNMENT, "counts must be 8-byte aligned, first 4-byte aligned");
+  return hip_status(kvd::launch_fp8_convert(reinterpret_cast<unsigned long long*>(counts), first,
+                                            (hipStream_t)stream),
+                    "kv_probe_fp8_convert launch");
+}
+
 kv_status kv_host_alloc(size_t bytes, uint32_t flags, void** host_ptr, void** dev_ptr) {
   if (!host_ptr || !dev_ptr) return fail(KV_ERR_INVALID_ARG, "host_ptr and dev_ptr are required");
   *host_ptr = nullptr;

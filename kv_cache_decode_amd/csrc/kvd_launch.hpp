@@ -139,6 +139,10 @@ hipError_t launch_gather_read(int dtype, int D, const void* k_cache, const void*
 // Words of the stream-read probe's sink (one per workgroup).
 constexpr int kProbeSinkWords = 4096;
 
+// Classes of kv_probe_fp8_convert's counts; the launch writes them all.
+constexpr int kProbeFp8Classes = 4;
+hipError_t launch_fp8_convert(unsigned long long* counts, uint32_t* first, hipStream_t stream);
+
 // Largest cache (slots per sequence and KV head) the plan kernel holds.
 constexpr int kCacheMaxSlots = 8192;
 

@@ -9,6 +9,13 @@
 //                       KV head, sequence) wave the K and V tiles of its pages
 //                       in block-table order, in the matrix-core kernel's lane
 //                       layout, one page ahead
+//
+// And one probe of an instruction the quantizer relies on:
+//
+//   fp8_convert_kernel  every fp32 bit pattern through v_cvt_pk_fp8_f32 (as
+//                       the first operand, and XOR 0x80012345 as the second)
+//                       against fp8_encode, the E4M3 rounding rule the codes
+//                       are defined by; mismatches counted per magnitude class
 #include "kvd_device.hpp"
 #include "kvd_dispatch.hpp"
 #include "kvd_launch.hpp"
@@ -115,6 +122,68 @@ __global__ __launch_bounds__(WAVES * kWave) void gather_read_kernel(
 #pragma unroll
   for (int off = 1; off < kWave; off <<= 1) acc ^= (uint32_t)__shfl_xor((int)acc, off, kWave);
   if (lane == 0) sink[((size_t)b * Hkv + j) * S + s] = acc;
+}
+
+// magnitude classes of an fp32 input: finite below 464 (where the quantizer
+// uses the instruction), finite from 464 up, infinity, NaN
+__device__ inline int fp8_probe_class(uint32_t u) {
+  const uint32_t a = u & 0x7fffffffu;
+  return a < 0x43e80000u ? 0 : a < 0x7f800000u ? 1 : a == 0x7f800000u ? 2 : 3;
+}
+
+__global__ void fp8_convert_init_kernel(unsigned long long* counts, uint32_t* first) {
+  const int i = threadIdx.x;
+  if (i < kProbeFp8Classes) {
+    counts[i] = 0ull;
+    first[i] = 0xffffffffu;
+  }
+}
+
+__global__ __launch_bounds__(kProbeThreads) void fp8_convert_kernel(unsigned long long* counts,
+                                                                   uint32_t* first) {
+  unsigned long long c[kProbeFp8Classes];
+  uint32_t f[kProbeFp8Classes];
+#pragma unroll
+  for (int k = 0; k < kProbeFp8Classes; ++k) {
+    c[k] = 0ull;
+    f[k] = 0xffffffffu;
+  }
+  const uint64_t stride = (uint64_t)gridDim.x * blockDim.x;
+  for (uint64_t i = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x; i < (1ull << 32); i += stride) {
+    const uint32_t u0 = (uint32_t)i, u1 = u0 ^ 0x80012345u;
+    const uint32_t hw = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(__uint_as_float(u0),
+                                                                   __uint_as_float(u1), 0, false);
+    const uint32_t v[2] = {u0, u1};
+#pragma unroll
+    for (int o = 0; o < 2; ++o) {
+      if (((hw >> (8 * o)) & 0xffu) != fp8_encode(__uint_as_float(v[o]))) {
+        const int k = fp8_probe_class(v[o]);
+#pragma unroll
+        for (int q = 0; q < kProbeFp8Classes; ++q) {   // registers stay statically indexed
+          if (q == k) {
+            c[q] += 1ull;
+            f[q] = min(f[q], v[o]);
+          }
+        }
+      }
+    }
+  }
+#pragma unroll
+  for (int k = 0; k < kProbeFp8Classes; ++k) {
+    if (c[k]) {
+      atomicAdd(&counts[k], c[k]);
+      atomicMin(&first[k], f[k]);
+    }
+  }
+}
+
+hipError_t launch_fp8_convert(unsigned long long* counts, uint32_t* first, hipStream_t stream) {
+  hipLaunchKernelGGL(fp8_convert_init_kernel, dim3(1), dim3(kWave), 0, stream, counts, first);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(fp8_convert_kernel, dim3(cu_count() * 8), dim3(kProbeThreads), 0, stream,
+                     counts, first);
+  return hipGetLastError();
 }
 
 hipError_t launch_stream_read(const void* buf, size_t bytes, uint32_t* sink, int sink_words,

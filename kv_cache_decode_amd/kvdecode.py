@@ -39,7 +39,7 @@ EXPORTS = (
     "kv_cache_fetch", "kv_cache_fetch_codes", "kv_cached_decode_attn_codes",
     "kv_cached_decode_attn_fetch", "kv_cached_decode_attn_fetch_codes",
     "kv_cached_decode_attn", "kv_cache_slot_mass", "kv_check_tables", "kv_probe_stream_read",
-    "kv_probe_gather_read", "kv_host_alloc", "kv_host_free",
+    "kv_probe_gather_read", "kv_probe_fp8_convert", "kv_host_alloc", "kv_host_free",
     "kv_status_string", "kv_last_error_message",
 )
 
@@ -131,6 +131,7 @@ def _load() -> ctypes.CDLL:
         "kv_check_tables": (I32, [S, P, P, P, P, I32, P, P]),
         "kv_probe_stream_read": (I32, [P, SZ, P, P]),
         "kv_probe_gather_read": (I32, [S, P, P, P, P, I32, P, P]),
+        "kv_probe_fp8_convert": (I32, [P, P, P]),
         "kv_host_alloc": (I32, [SZ, U32, ctypes.POINTER(P), ctypes.POINTER(P)]),
         "kv_host_free": (I32, [P]),
         "kv_status_string": (ctypes.c_char_p, [I32]),
@@ -608,6 +609,11 @@ def kv_probe_gather_read(shape: KVShape, k_cache: Buf, v_cache: Buf, block_table
                          seq_lens: Buf, num_splits: int, sink: Buf, stream=None) -> None:
     _check(_lib.kv_probe_gather_read(ctypes.byref(shape), _p(k_cache), _p(v_cache),
                                      _p(block_table), _p(seq_lens), num_splits, _p(sink),
+                                     _stream(stream)))
+
+
+def kv_probe_fp8_convert(counts: Buf, first: Buf, stream=None) -> None:
+    _check(_lib.kv_probe_fp8_convert(_p(counts, 32, "counts"), _p(first, 16, "first"),
                                      _stream(stream)))
 
 

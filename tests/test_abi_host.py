@@ -377,6 +377,10 @@ def test_probe_argument_checks():
                                                  stream=stream))
     expect(kd.KV_ERR_UNSUPPORTED, lambda stream: g(shape(dtype="f32"), A16, A16, A16, A16, 2,
                                                    A16, stream=stream))
+    c = kd.kv_probe_fp8_convert
+    expect(kd.KV_ERR_INVALID_ARG, lambda stream: c(None, A16, stream=stream))
+    expect(kd.KV_ERR_INVALID_ARG, lambda stream: c(A16, None, stream=stream))
+    expect(kd.KV_ERR_ALIGNMENT, lambda stream: c(A4, A16, stream=stream))
 
 
 def test_decode_select_argument_checks():

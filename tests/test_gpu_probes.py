@@ -1,4 +1,5 @@
-"""The read-ceiling probes read exactly the bytes they claim (GPU).
+"""The read-ceiling probes read exactly the bytes they claim, and the E4M3
+conversion instruction probe finds no mismatch where the quantizers use it (GPU).
 
 Each probe folds what it loads with XOR, so the XOR of its sink words is the
 XOR of every 32-bit word it read: for the stream probe, the whole buffer; for
@@ -51,3 +52,20 @@ def test_gather_probe_reads_the_dense_pages(gpu, S, D, dtype):
                 want ^= xor_all(data.k_raw[p, j]) ^ xor_all(data.v_raw[p, j])
         assert xor_all(got[:, j, :]) == want, j
     dw.close()
+
+
+def test_fp8_conversion_instruction_matches_the_rounding_rule(gpu):
+    """The bf16 quantizers take E4M3 codes from the conversion instruction for
+    quotients below 464 in magnitude; over all 2^32 fp32 inputs, in both
+    operand slots, it must agree there with the codes' rounding rule.  Above
+    that it need not (it does not saturate), and the quantizers never ask."""
+    counts = torch.full((4,), -1, dtype=torch.int64, device=gpu)
+    first = torch.zeros(4, dtype=torch.int32, device=gpu)
+    kd.kv_probe_fp8_convert(counts, first)
+    torch.cuda.synchronize()
+    c = counts.cpu().numpy()
+    f = first.cpu().numpy().view(np.uint32)
+    print("fp8 conversion mismatches by class (<464, >=464, inf, NaN):", c.tolist(),
+          "first:", [hex(int(x)) for x in f])
+    assert c[0] == 0 and f[0] == 0xFFFFFFFF
+    assert (c >= 0).all()
