@@ -409,8 +409,9 @@ kv_status kv_decode_combine(const kv_shape* shape, int32_t num_splits, const flo
  *   X8[p, j, s, c] = E4M3 code of X[p, j, s, c] / scale (fp32, correctly
  *                    rounded), rounded to nearest with ties to the even code,
  *                    saturated to +-448;  0 for s >= v.
- * The codes are a deterministic function of the stored values.  K/V keep the
- * layout of the source pools with one byte per channel.  Pages not listed are
+ * The codes are a deterministic function of the stored values (amax ignores
+ * NaNs; the code of a NaN value is an E4M3 NaN, 0x7f with either sign bit).
+ * K/V keep the layout of the source pools with one byte per channel.  Pages not listed are
  * not touched; ids as in kv_block_meta_build, except that a negative id is a
  * skipped entry (so a -1-padded list such as kv_tier_plan's demote rows can be
  * passed whole).  page_valid_tokens may be NULL: every listed page is full
@@ -451,7 +452,8 @@ kv_status kv_paged_decode_attn_fp8(const kv_shape* shape, const void* q, const u
  *                   nearest with ties to even, clamped to [-7, 7];  0 for s >= v
  *   X4[p, j, s, c / 2] holds n of channel c in bits 4 * (c mod 2) .. +3, as
  *                   4-bit two's complement (the even channel in the low nibble).
- * The value a code stands for is n * scale.  fp16 and bf16 pools only
+ * The value a code stands for is n * scale; amax ignores NaNs, and the code
+ * of a NaN value is not specified.  fp16 and bf16 pools only
  * (KV_ERR_UNSUPPORTED for fp32).  Pages not listed are not touched; negative
  * ids are skipped and a NULL page_valid_tokens means full pages, as for
  * kv_quantize_pages_fp8; the block index is not affected.
