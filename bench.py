@@ -414,8 +414,20 @@ def time_codes(args, copies, k, time_loop, graph_us, fmt: str):
     # the code-page paths share their own split heuristic
     s_sparse = kd.kv_auto_num_splits_fp8(copies[0].shape, k)
     s_dense = kd.kv_auto_num_splits_fp8(copies[0].shape, copies[0].spec.max_blocks)
-    quantize = (lambda c: c.quantize_fp8(host=False)) if fmt == "fp8" else \
-        (lambda c: c.quantize_int4(host=False))
+    # the quantizer call alone, into code pools allocated once per copy
+    qcall = kd.kv_quantize_pages_fp8 if fmt == "fp8" else kd.kv_quantize_pages_int4
+    qbufs = {}
+
+    def quantize(c):
+        if id(c) not in qbufs:
+            P, Hkv, bs, D = c.data.k_raw.shape
+            row = D if fmt == "fp8" else D // 2
+            kq = torch.zeros((P, Hkv, bs, row), dtype=torch.uint8, device=c.device)
+            qbufs[id(c)] = (kq, torch.zeros_like(kq),
+                            torch.zeros((P, Hkv, 2), dtype=torch.float32, device=c.device))
+        kq, vq, sq = qbufs[id(c)]
+        qcall(c.shape, c.k_cache, c.v_cache, c.page_ids, c.page_valid, int(c.page_ids.numel()),
+              kq, vq, sq)
     attn = (lambda c, sp, S: c.attention_fp8(sparse=sp, num_splits=S)) if fmt == "fp8" else \
         (lambda c, sp, S: c.attention_int4(sparse=sp, num_splits=S))
 
@@ -426,6 +438,7 @@ def time_codes(args, copies, k, time_loop, graph_us, fmt: str):
         return ms_ * 1e3 / args.steps
 
     for c in copies:
+        (c.quantize_fp8 if fmt == "fp8" else c.quantize_int4)(host=False)   # the pools attention reads
         quantize(c)
         c.score_topk(k)
     torch.cuda.synchronize()
