@@ -48,13 +48,31 @@ struct CodeChunk {
   uint32_t w[E / 4];
 };
 
+// Code stores are non-temporal: the pools are written once and read by later
+// steps (over rotated full pools: FP8 150 -> 141 us, INT4 133 -> 121 us).
+#ifndef KVD_QUANT_NT_STORE
+#define KVD_QUANT_NT_STORE 1
+#endif
+
+typedef unsigned int u32x2_sv __attribute__((ext_vector_type(2)));
+
+__device__ inline void store_code_word(uint8_t* dst, uint32_t w) {
+  if constexpr (KVD_QUANT_NT_STORE)
+    __builtin_nontemporal_store(w, reinterpret_cast<unsigned int*>(dst));
+  else
+    *reinterpret_cast<uint32_t*>(dst) = w;
+}
+
 template <int E>
 __device__ inline void store_codes(uint8_t* dst, const CodeChunk<E>& cc) {
   if constexpr (E == 8) {
-    *reinterpret_cast<uint2*>(dst) = make_uint2(cc.w[0], cc.w[1]);
+    if constexpr (KVD_QUANT_NT_STORE)
+      __builtin_nontemporal_store(u32x2_sv{cc.w[0], cc.w[1]}, reinterpret_cast<u32x2_sv*>(dst));
+    else
+      *reinterpret_cast<uint2*>(dst) = make_uint2(cc.w[0], cc.w[1]);
   } else {
     static_assert(E == 4, "4 or 8 channels per chunk");
-    *reinterpret_cast<uint32_t*>(dst) = cc.w[0];
+    store_code_word(dst, cc.w[0]);
   }
 }
 
@@ -217,7 +235,7 @@ __global__ __launch_bounds__(WAVES * kWave) void quantize_kernel(
                 for (int e = 0; e < E; ++e) cw |= int4_encode(__fdiv_rn(f[e], sc)) << (4 * e);
               }
             }
-            *reinterpret_cast<uint32_t*>(dst + (size_t)r * RB) = cw;
+            store_code_word(dst + (size_t)r * RB, cw);
           }
         }
         if (lane == 0) scales[tile * 2 + t] = sc;
