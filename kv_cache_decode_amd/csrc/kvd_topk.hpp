@@ -64,7 +64,10 @@ __device__ inline uint32_t block_exclusive_scan(uint32_t v, uint32_t* buf) {
 // wave): with 16 waves sharing a compute unit's 4 SIMDs, per-key exec-mask
 // branches cost more time than the row's loads.
 // Most keys the rank count after the wide pass resolves (else 8-bit passes go on).
-constexpr int kTopkCandMax = 512;
+#ifndef KVD_TOPK_CAND_MAX
+#define KVD_TOPK_CAND_MAX 512
+#endif
+constexpr int kTopkCandMax = KVD_TOPK_CAND_MAX;
 
 // Keys a thread keeps in registers.  Rows of more than 32 keys per thread
 // (EPT 64: up to 65536 blocks) keep keys 32 .. EPT-1 in LDS instead, one word
