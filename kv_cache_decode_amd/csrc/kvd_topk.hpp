@@ -93,8 +93,10 @@ struct TopkSmem {
   alignas(16) uint32_t scan_d[NW];
   uint32_t state[3];
   uint32_t cand_n;
-  uint32_t cand_key[kTopkCandMax];
-  int32_t cand_idx[kTopkCandMax];
+  // candidates of the rank count, and four key-0 pads after the last one
+  alignas(16) uint32_t cand_key[kTopkCandMax + 4];
+  alignas(16) int32_t cand_idx[kTopkCandMax + 4];
+  uint32_t cand_gt[kTopkCandMax], cand_rank[kTopkCandMax];   // partial counts summed over waves
   alignas(16) uint32_t xkeys[XK > 0 ? XK * NT : 1];
 };
 template <int NT, int EPT>
@@ -323,6 +325,14 @@ __device__ inline void topk_select(const float* __restrict__ row, int npos, int 
       // few keys share the known bits: gather them (one reservation per wave)
       // and rank each against the others by (key descending, index
       // ascending); the key ranked krem-1 is T
+      if (tid < 4) sm.cand_key[nc + tid] = 0u;   // pads: rank below every candidate
+      const bool spread = nc > (uint32_t)kWave;    // more than one wave's candidates
+      if (spread) {
+        for (int i = tid; i < (int)nc; i += NT) {
+          sm.cand_gt[i] = 0u;
+          sm.cand_rank[i] = 0u;
+        }
+      }
       uint32_t mine = 0u;
 #pragma unroll
       for (int r = 0; r < EPT; ++r) mine += (uint32_t)known(kget(r));
@@ -340,24 +350,67 @@ __device__ inline void topk_select(const float* __restrict__ row, int npos, int 
         }
       }
       __syncthreads();
-      // wave w ranks candidates 64w .. 64w+63 (then 64(w+NW) ...), one per
-      // lane, against the others read 64 at a time into registers and
-      // broadcast with readlane
-      for (int cw = wave; cw * kWave < (int)nc; cw += NW) {
+      // candidates are ranked by (key descending, index ascending) against
+      // all others, four at a time: every lane reads the same 16 bytes of keys
+      // and of indexes (an LDS broadcast), so the compares wait on no scalar
+      // round trip; the key-0 pads past nc never count.  Up to 64 candidates
+      // wave 0 ranks them all.  Beyond that, each block of 64 candidates (one
+      // per lane) is compared by NW / blocks waves, each over its own range of
+      // candidates, and the partial counts are summed in LDS.
+      if (spread) {
+        const int nblk = ((int)nc + kWave - 1) / kWave;
+        const int parts = max(1, NW / nblk);
+        const int nc4 = ((int)nc + 3) & ~3;
+        const int len = (((nc4 + parts - 1) / parts) + 3) & ~3;
+        for (int wv = wave; wv < nblk * parts; wv += NW) {
+          const int cb = wv / parts, pt = wv - cb * parts;
+          const int i = cb * kWave + lane;
+          const bool own = i < (int)nc;
+          const uint32_t ki = own ? sm.cand_key[i] : 0u;
+          const int ii = own ? sm.cand_idx[i] : 0;
+          uint32_t gt = 0, rank = 0;
+          const int c1 = min(nc4, (pt + 1) * len);
+#pragma unroll 2
+          for (int c = pt * len; c < c1; c += 4) {
+            const uint4 kc = *reinterpret_cast<const uint4*>(&sm.cand_key[c]);
+            const int4 ic = *reinterpret_cast<const int4*>(&sm.cand_idx[c]);
+            const uint32_t k4[4] = {kc.x, kc.y, kc.z, kc.w};
+            const int i4[4] = {ic.x, ic.y, ic.z, ic.w};
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+              gt += k4[q] > ki;
+              rank += k4[q] > ki || (k4[q] == ki && i4[q] < ii);
+            }
+          }
+          if (own) {
+            atomicAdd(&sm.cand_gt[i], gt);
+            atomicAdd(&sm.cand_rank[i], rank);
+          }
+        }
+        __syncthreads();
+        for (int i = tid; i < (int)nc; i += NT) {
+          if (sm.cand_rank[i] == krem - 1u) {
+            state[0] = sm.cand_key[i];
+            state[1] = krem - sm.cand_gt[i];
+          }
+        }
+      }
+      for (int cw = wave; !spread && cw * kWave < (int)nc; cw += NW) {
         const int i = cw * kWave + lane;
         const bool own = i < (int)nc;
         const uint32_t ki = own ? sm.cand_key[i] : 0u;
         const int ii = own ? sm.cand_idx[i] : 0;
         uint32_t gt = 0, rank = 0;
-        for (int base = 0; base < (int)nc; base += kWave) {
-          const int cnt = min(kWave, (int)nc - base);
-          const int kc_l = (int)sm.cand_key[base + lane];   // base + 63 < kTopkCandMax
-          const int ic_l = sm.cand_idx[base + lane];
-          for (int c2 = 0; c2 < cnt; ++c2) {
-            const uint32_t kc = (uint32_t)__builtin_amdgcn_readlane(kc_l, c2);
-            const int ic = __builtin_amdgcn_readlane(ic_l, c2);
-            gt += kc > ki;
-            rank += kc > ki || (kc == ki && ic < ii);
+#pragma unroll 2
+        for (int c = 0; c < (int)nc; c += 4) {
+          const uint4 kc = *reinterpret_cast<const uint4*>(&sm.cand_key[c]);
+          const int4 ic = *reinterpret_cast<const int4*>(&sm.cand_idx[c]);
+          const uint32_t k4[4] = {kc.x, kc.y, kc.z, kc.w};
+          const int i4[4] = {ic.x, ic.y, ic.z, ic.w};
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            gt += k4[q] > ki;
+            rank += k4[q] > ki || (k4[q] == ki && i4[q] < ii);
           }
         }
         if (own && rank == krem - 1u) {
