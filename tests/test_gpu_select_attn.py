@@ -135,3 +135,35 @@ def test_decode_score_equals_decode_select(gpu, dtype, G, index):
         assert torch.equal(A.scores, B.scores), ("scores", i)
     A.close()
     B.close()
+
+
+def test_fused_select_with_many_tied_candidates(gpu):
+    """Exact scores where hundreds of blocks share the K-th score, so more than
+    64 keys reach the rank count, which then spreads over the workgroup's waves
+    (in the fused kernel's 256-thread select, more candidate blocks than
+    waves).  The fused list and partials equal kv_block_select + attention bit
+    for bit, and the list equals the oracle's rank count."""
+    import oracle
+    from kv_cache_decode_amd.step import DeviceWorkload
+    from test_gpu_topk import scored_workload
+    rng = np.random.default_rng(7777)
+    n = 1800
+    rows = []
+    for h, n_tied in enumerate((300, 420)):
+        r = rng.uniform(-4.0, 4.0, size=n)
+        tied = rng.choice(n, n_tied, replace=False)
+        r[tied] = 4.5
+        rest = np.setdiff1d(np.arange(n), tied)
+        r[rng.choice(rest, 200, replace=False)] = rng.uniform(5.0, 9.0, size=200)
+        rows.append(r.astype(np.float32))
+    data = scored_workload([np.stack(rows)], G=2, Hkv=2, seed=7778)
+    dw = DeviceWorkload(data, device=gpu)
+    dw.meta_build()
+    for k in (256, 300, 450, 650):
+        for S in (4, 8):
+            fused_vs_separate(dw, data, k, S)
+            gs = dw.scores.cpu().numpy().astype(np.float64)
+            rsel, rcnt = oracle.select(gs, data.seq_lens, 16, k)
+            np.testing.assert_array_equal(dw.sel_count.cpu().numpy(), rcnt)
+            np.testing.assert_array_equal(dw.sel.cpu().numpy()[:, :, :k], rsel)
+    dw.close()
